@@ -1,0 +1,149 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: argument validation,
+// variant choice, workspace, launches. No exception crosses the interface.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+int64_t max_chunks(int64_t N, int64_t T) { return (T + KDA_CHUNK - 1) / KDA_CHUNK + N; }
+
+struct Layout {
+    size_t chunk_off, order, recs, total;
+};
+
+Layout split_layout(int64_t N, int64_t T, int64_t H) {
+    Layout L;
+    L.chunk_off = 0;
+    L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
+    L.recs = L.order + align_up(sizeof(int32_t) * (size_t)N);
+    L.total = L.recs + (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
+    return L;
+}
+
+// Shape limits: grid sizes stay far below 2^31 blocks and token-head offsets fit int64.
+bool shape_ok(int64_t N, int64_t T, int64_t H) {
+    if (N < 1 || T < 0 || H < 1) return false;
+    if (max_chunks(N, T) * H > (int64_t)1 << 30) return false;
+    if (N * H * 8 > (int64_t)1 << 30) return false;
+    return true;
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+int resolve_variant(int v) { return v == KDA_VARIANT_AUTO ? KDA_VARIANT_SPLIT : v; }
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_version(void) { return "kda-mi355x 0.1.0 (gfx950)"; }
+
+const char *kda_status_string(int s) {
+    switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "a size is out of range";
+    case KDA_ERR_UNSUPPORTED: return "unsupported argument (head_dim must be 128; scale finite; known variant)";
+    case KDA_ERR_ALLOC: return "workspace allocation failed or caller workspace too small";
+    case KDA_ERR_LAUNCH: return "kernel launch failed";
+    case KDA_ERR_DEVICE: return "HIP device error";
+    case KDA_ERR_ALIAS: return "final_state partially overlaps initial_state";
+    default: return "unknown status";
+    }
+}
+
+int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads) {
+    (void)num_seqs;
+    (void)total_tokens;
+    (void)num_heads;
+    return resolve_variant(KDA_VARIANT_AUTO);
+}
+
+size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                           int32_t variant) {
+    if (!shape_ok(num_seqs, total_tokens, num_heads)) return 0;
+    const int v = variant == KDA_VARIANT_AUTO
+                      ? kda_select_variant(num_seqs, total_tokens, num_heads)
+                      : variant;
+    if (v != KDA_VARIANT_SPLIT) return 0;
+    return split_layout(num_seqs, total_tokens, num_heads).total;
+}
+
+int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+               float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+               int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+               float *final_state, void *stream, const kda_options *opt) {
+    // ---- host-side validation, before anything is enqueued
+    if (opt && opt->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    const int variant = opt ? opt->variant : KDA_VARIANT_AUTO;
+    if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED)
+        return KDA_ERR_UNSUPPORTED;
+    if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+    if (!shape_ok(num_seqs, total_tokens, num_heads)) return KDA_ERR_SHAPE;
+    if (!cu_seqlens && num_seqs != 1) return KDA_ERR_SHAPE;
+    if (!out && total_tokens > 0) return KDA_ERR_NULL;
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta)) return KDA_ERR_NULL;
+    const size_t state_bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    if (initial_state && final_state && (const void *)initial_state != (const void *)final_state &&
+        overlaps(initial_state, state_bytes, final_state, state_bytes))
+        return KDA_ERR_ALIAS;
+
+    const int chosen = variant == KDA_VARIANT_AUTO
+                           ? kda_select_variant(num_seqs, total_tokens, num_heads)
+                           : variant;
+    if (chosen == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;   // not built yet
+
+    hipStream_t st = (hipStream_t)stream;
+    const int N = num_seqs, T = total_tokens, H = num_heads;
+    const Layout lay = split_layout(N, T, H);
+
+    char *ws = nullptr;
+    bool owned = false;
+    if (opt && opt->workspace) {
+        if (opt->workspace_bytes < lay.total) return KDA_ERR_ALLOC;
+        ws = (char *)opt->workspace;
+    } else {
+        if (hipMallocAsync((void **)&ws, lay.total, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return KDA_ERR_ALLOC;
+        }
+        owned = true;
+    }
+    int32_t *chunk_off = (int32_t *)(ws + lay.chunk_off);
+    int32_t *order = (int32_t *)(ws + lay.order);
+    char *recs = ws + lay.recs;
+
+    int rc = KDA_OK;
+    if (kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, st) != hipSuccess ||
+        kda::launch_prep((const uint16_t *)q, (const uint16_t *)k, g, beta, cu_seqlens, N, T, H,
+                         scale, chunk_off, recs, max_chunks(N, T), st) != hipSuccess ||
+        kda::launch_recur(recs, (const uint16_t *)v, cu_seqlens, chunk_off, order, N, T, H,
+                          initial_state, out, final_state, 4, st) != hipSuccess)
+        rc = KDA_ERR_LAUNCH;
+    if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
+    return rc;
+}
+
+int kda_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+            float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+            int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+            float *final_state, void *stream) {
+    return kda_fwd_ex(q, k, v, g, beta, scale, cu_seqlens, num_seqs, total_tokens, num_heads,
+                      head_dim, initial_state, out, final_state, stream, nullptr);
+}
+
+}  // extern "C"

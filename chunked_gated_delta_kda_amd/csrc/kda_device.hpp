@@ -1,0 +1,380 @@
+// kda_device.hpp -- device building blocks of the gfx950 KDA forward.
+//
+// Chunked form of the recurrence (per sequence and head; chunk of n <= 16
+// tokens, G_r = in-chunk cumulative clamped log-decay per key channel,
+// K+ = K.e^{G}, K- = K.e^{-G}, Q+ = scale.Q.e^{G}, K~ = K.e^{G_C - G}):
+//
+//   A   = Diag(beta) . strict_lower(K+ K-^T)          16x16
+//   T   = (I + A)^{-1} = (I - A)(I + A^2)(I + A^4)(I + A^8)   (A^16 = 0)
+//   W   = T Diag(beta) K+ ,  U = T Diag(beta) V       16x128
+//   Vn  = U - W S                                     true per-token writes
+//   O   = Q+ S + incl_lower(Q+ K-^T) Vn               outputs of the chunk
+//   S  <- Diag(e^{G_C}) S + K~^T Vn                   next chunk's state
+//
+// The 16-token chunking, the strictly lower 16x16 matrix whose inverse is a
+// Neumann series folded by repeated squaring, and the -5 bound that keeps
+// every e^{+-G} inside the floating-point range all follow the description of
+// FlashKDA's kernels (smzdm.com, "KDA 内核到底难在哪"). The rest is this
+// library's own derivation from the per-token recurrence.
+//
+// Matrix products run on v_mfma_f32_16x16x32_bf16. Operand layouts (verified
+// on gfx950): A-operand lane l holds row l%16, k-slots 8*(l/16)+i (i<8);
+// B-operand lane l holds column l%16, the same k-slots; the 16x16 fp32
+// result ("D layout") has lane l holding rows 4*(l/16)+j (j<4), column l%16.
+// A contraction only needs A and B to agree on which logical k each slot
+// carries, so every product below relabels slots freely:
+//  * "hi/lo folding": slots 8g+j carry (k = 4g+j, hi part) and 8g+4+j carry
+//    (k = 4g+j, lo part) of a split-bf16 operand x = hi + lo, so one MFMA
+//    over a D-layout operand gives x_hi.y + x_lo.y or y.(x_hi + x_lo).
+//  * "state permutation": for the 128-deep products against the state, slot
+//    8g+j of k-block kb is key channel 32kb+4g+j and slot 8g+4+j is
+//    32kb+16+4g+j. With that labelling the fp32 state, kept in D layout as
+//    eight 16-row blocks, converts in registers to the B operand of W.S and
+//    Q+.S without any data exchange between lanes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int D = 128;             // head dimension (key and value)
+constexpr int C = 16;              // chunk length
+constexpr float LOWER_BOUND = -5.0f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- primitives
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// e^x through the hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+
+// x = hi + lo with hi = bf16(x) (round to nearest even) and lo = bf16(x - hi).
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    hi = __builtin_convertvector(x, bf16x4);
+    f32x4 h = __builtin_convertvector(hi, f32x4);
+    lo = __builtin_convertvector(x - h, bf16x4);
+}
+
+__device__ __forceinline__ void split2(f32x2 x, bf16x2 &hi, bf16x2 &lo) {
+    hi = __builtin_convertvector(x, bf16x2);
+    f32x2 h = __builtin_convertvector(hi, f32x2);
+    lo = __builtin_convertvector(x - h, bf16x2);
+}
+
+// Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8). Return a
+// logical index such that consecutive logical indices share an XCD (and its L2).
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+    const int per = nb >> 3, rem = nb & 7;
+    const int x = b & 7, i = b >> 3;
+    return x * per + (x < rem ? x : rem) + i;
+}
+
+// ---------------------------------------------------------------- chunk record
+// Everything the recurrence needs from one (chunk, head), in per-lane order so
+// that each lane of a wave reads contiguous 8/16-byte pieces. Offsets in bytes.
+struct Rec {
+    static constexpr int WN = 0;       // bf16 [4 kb][64 lanes][8]: -W, state-permuted A operand
+    static constexpr int QH = 4096;    // bf16 [4][64][8]: Q+ hi, state-permuted A operand
+    static constexpr int QL = 8192;    // bf16 [4][64][8]: Q+ lo
+    static constexpr int KTH = 12288;  // bf16 [8 blocks][64][4]: K~[4g+j][16b + l%16] hi
+    static constexpr int KTL = 16384;  // bf16 [8 blocks][64][4]: K~ lo
+    static constexpr int PH = 20480;   // bf16 [64][4]: P[l%16][4g+j] hi (causal, diagonal kept)
+    static constexpr int PL = 20992;   // bf16 [64][4]: P lo
+    static constexpr int TB = 21504;   // bf16 [64][8]: (T Diag(beta))[l%16][4g+j] hi | lo
+    static constexpr int EG = 22528;   // f32 [128]: e^{G_C} per key channel
+    static constexpr int BYTES = 23040;
+};
+
+// LDS scratch of one chunk prep (one wave).
+struct alignas(16) PrepLds {
+    static constexpr int ROW = 136;    // bf16 per padded token row (128 + 8: spreads banks)
+    __bf16 kp[16 * ROW];               // K+ (single bf16)
+    __bf16 kmh[16 * ROW];              // K- hi
+    __bf16 kml[16 * ROW];              // K- lo
+    __bf16 qph[16 * ROW];              // Q+ hi
+    __bf16 qpl[16 * ROW];              // Q+ lo
+    __bf16 kpt[D * 16];                // K+ transposed: [channel][token]
+    float ktt[D * 16];                 // K~ transposed (fp32; split when stored)
+};
+
+// 16x16 product N.M, given N^T and M in D layout, split-bf16 on both sides
+// (error ~ |N||M| 2^-16). Result in D layout.
+__device__ __forceinline__ f32x4 mm16(f32x4 Nt, f32x4 M) {
+    bf16x4 nh, nl, mh, ml;
+    split4(Nt, nh, nl);
+    split4(M, mh, ml);
+    const bf16x4 z = {};
+    const bf16x8 b = cat(mh, ml);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma(cat(nh, nh), b, acc);
+    acc = mfma(cat(nl, z), b, acc);
+    return acc;
+}
+
+// Identity plus/minus a D-layout matrix.
+__device__ __forceinline__ f32x4 eye_plus(f32x4 M, int lane, float sign) {
+    const int col = lane & 15, r0 = 4 * (lane >> 4);
+    f32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = sign * M[j] + ((r0 + j) == col ? 1.f : 0.f);
+    return o;
+}
+
+// ---------------------------------------------------------------- chunk prep
+// One wave turns one (chunk, head) of raw inputs into a chunk record.
+//   q, k: bf16 bits [T, H, 128]; g: fp32 [T, H, 128]; beta: fp32 [T, H]
+//   t0: first token of the chunk; nc: its length (1..16); rows past nc are
+//   treated as k = q = 0, g = 0, beta = 0, which adds nothing.
+// `rec` may point to global memory or LDS.
+__device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
+                                           const uint16_t *__restrict__ k,
+                                           const float *__restrict__ g,
+                                           const float *__restrict__ beta, int64_t t0, int nc,
+                                           int h, int H, float scale, PrepLds &L, char *rec) {
+    const int l = threadIdx.x & 63;
+    const int c0 = 2 * l;            // this lane's two key channels (channel-major phase)
+    const int r = l & 15, gq = l >> 4;
+
+    // ---- phase 0: gates and scaled operands, lane = channel pair, loop over tokens
+    float G0[C], G1[C];
+    uint32_t qv[C], kv[C];
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        f32x2 gt = {0.f, 0.f};
+        uint32_t qq = 0, kk = 0;
+        if (t < nc) {
+            const int64_t row = (t0 + t) * (int64_t)H + h;
+            gt = *(const f32x2 *)(g + row * D + c0);
+            qq = *(const uint32_t *)(q + row * D + c0);
+            kk = *(const uint32_t *)(k + row * D + c0);
+        }
+        acc0 += fmaxf(gt.x, LOWER_BOUND);
+        acc1 += fmaxf(gt.y, LOWER_BOUND);
+        G0[t] = acc0;
+        G1[t] = acc1;
+        qv[t] = qq;
+        kv[t] = kk;
+    }
+    // padded rows carry g = 0, so acc is G at the last real token
+    const float eC0 = exp_e(acc0), eC1 = exp_e(acc1);
+    *(f32x2 *)(rec + Rec::EG + c0 * 4) = f32x2{eC0, eC1};
+
+#pragma unroll
+    for (int t = 0; t < C; t += 2) {
+        float kpT[2][2], ktT[2][2];   // [token pair][channel]
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = t + u;
+            const float ep0 = exp_e(G0[tt]), ep1 = exp_e(G1[tt]);
+            const float en0 = exp_e(-G0[tt]), en1 = exp_e(-G1[tt]);
+            const float k0 = bf_lo(kv[tt]), k1 = bf_hi(kv[tt]);
+            const float q0 = bf_lo(qv[tt]), q1 = bf_hi(qv[tt]);
+            const f32x2 kp = {k0 * ep0, k1 * ep1};
+            const f32x2 km = {k0 * en0, k1 * en1};
+            const f32x2 qp = {scale * q0 * ep0, scale * q1 * ep1};
+            *(bf16x2 *)&L.kp[tt * PrepLds::ROW + c0] = __builtin_convertvector(kp, bf16x2);
+            bf16x2 hi, lo;
+            split2(km, hi, lo);
+            *(bf16x2 *)&L.kmh[tt * PrepLds::ROW + c0] = hi;
+            *(bf16x2 *)&L.kml[tt * PrepLds::ROW + c0] = lo;
+            split2(qp, hi, lo);
+            *(bf16x2 *)&L.qph[tt * PrepLds::ROW + c0] = hi;
+            *(bf16x2 *)&L.qpl[tt * PrepLds::ROW + c0] = lo;
+            kpT[u][0] = kp.x;
+            kpT[u][1] = kp.y;
+            ktT[u][0] = km.x * eC0;      // K~ = K e^{G_C - G}
+            ktT[u][1] = km.y * eC1;
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            *(bf16x2 *)&L.kpt[(c0 + ch) * 16 + t] =
+                __builtin_convertvector((f32x2{kpT[0][ch], kpT[1][ch]}), bf16x2);
+            *(f32x2 *)&L.ktt[(c0 + ch) * 16 + t] = f32x2{ktT[0][ch], ktT[1][ch]};
+        }
+    }
+    // beta of token r (this lane's column) and of tokens 4g+j (this lane's rows)
+    float br = 0.f;
+    f32x4 bj = {0.f, 0.f, 0.f, 0.f};
+    if (r < nc) br = beta[(t0 + r) * (int64_t)H + h];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (4 * gq + j < nc) bj[j] = beta[(t0 + 4 * gq + j) * (int64_t)H + h];
+    __syncthreads();
+
+    // ---- phase 1: K+K-^T (both orientations) and the causal Q+K-^T, 128-deep
+    f32x4 akk = {0.f, 0.f, 0.f, 0.f}, akt = akk, pt = akk;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int off = r * PrepLds::ROW + 32 * kb + 8 * gq;
+        const bf16x8 kp = *(const bf16x8 *)&L.kp[off];
+        const bf16x8 kmh = *(const bf16x8 *)&L.kmh[off];
+        const bf16x8 kml = *(const bf16x8 *)&L.kml[off];
+        const bf16x8 qph = *(const bf16x8 *)&L.qph[off];
+        const bf16x8 qpl = *(const bf16x8 *)&L.qpl[off];
+        akk = mfma(kp, kmh, akk);   // (K+K-^T)[4g+j][r]
+        akt = mfma(kmh, kp, akt);   // (K+K-^T)[r][4g+j]
+        pt = mfma(kmh, qph, pt);    // (Q+K-^T)[r][4g+j], split 3-term
+        pt = mfma(kmh, qpl, pt);
+        pt = mfma(kml, qph, pt);
+    }
+    f32x4 Am, At, Pm;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * gq + j;
+        Am[j] = (r < row) ? bj[j] * akk[j] : 0.f;   // A[row][r]
+        At[j] = (row < r) ? br * akt[j] : 0.f;       // A^T[row][r] = A[r][row]
+        Pm[j] = (row <= r) ? pt[j] : 0.f;            // P[r][row]
+    }
+    {
+        bf16x4 ph, pl;
+        split4(Pm, ph, pl);
+        *(bf16x4 *)(rec + Rec::PH + l * 8) = ph;
+        *(bf16x4 *)(rec + Rec::PL + l * 8) = pl;
+    }
+
+    // ---- phase 2: T^T = (I + A^T)^{-1} = (I - X)(I + X^2)(I + X^4)(I + X^8), X = A^T
+    const f32x4 X2 = mm16(Am, At);
+    const f32x4 A2 = mm16(At, Am);
+    const f32x4 X4 = mm16(A2, X2);
+    const f32x4 A4 = mm16(X2, A2);
+    const f32x4 X8 = mm16(A4, X4);
+    const f32x4 R1 = mm16(eye_plus(A4, l, 1.f), eye_plus(X8, l, 1.f));
+    const f32x4 R2 = mm16(eye_plus(A2, l, 1.f), R1);
+    const f32x4 Tt = mm16(eye_plus(Am, l, -1.f), R2);   // Tt[j] = T[r][4g+j]
+    bf16x8 tb;
+    {
+        bf16x4 hi, lo;
+        split4(Tt * bj, hi, lo);                       // (T Diag(beta))[r][4g+j]
+        tb = cat(hi, lo);
+        *(bf16x8 *)(rec + Rec::TB + l * 16) = tb;
+    }
+
+    // ---- phase 3: W^T = K+^T (T Diag(beta))^T, one 16-row key block at a time
+    f32x4 Wt[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bf16x4 a = *(const bf16x4 *)&L.kpt[(16 * b + r) * 16 + 4 * gq];
+        Wt[b] = mfma(cat(a, a), tb, f32x4{0.f, 0.f, 0.f, 0.f});   // W[r][16b+4g+j]
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x4 a = __builtin_convertvector(-Wt[2 * kb], bf16x4);
+        const bf16x4 b = __builtin_convertvector(-Wt[2 * kb + 1], bf16x4);
+        *(bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16) = cat(a, b);
+        const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
+        *(bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16) =
+            cat(*(const bf16x4 *)&L.qph[o], *(const bf16x4 *)&L.qph[o + 16]);
+        *(bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16) =
+            cat(*(const bf16x4 *)&L.qpl[o], *(const bf16x4 *)&L.qpl[o + 16]);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        bf16x4 hi, lo;
+        split4(*(const f32x4 *)&L.ktt[(16 * b + r) * 16 + 4 * gq], hi, lo);
+        *(bf16x4 *)(rec + Rec::KTH + b * 512 + l * 8) = hi;
+        *(bf16x4 *)(rec + Rec::KTL + b * 512 + l * 8) = lo;
+    }
+}
+
+// ---------------------------------------------------------------- recurrence
+// Inputs of one chunk step for one wave (a 16-column slice of the state).
+struct StepIn {
+    bf16x8 wn[4], qh[4], ql[4];
+    bf16x4 kth[8], ktl[8];
+    bf16x4 ph, pl;
+    bf16x8 tb;
+    f32x4 eg[8];
+    bf16x4 v;     // V[4g+j][col], zero past the chunk end
+};
+
+__device__ __forceinline__ void load_step(StepIn &s, const char *__restrict__ rec,
+                                          const uint16_t *__restrict__ vsrc, int64_t vstride,
+                                          int nc) {
+    const int l = threadIdx.x & 63, gq = l >> 4;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        s.wn[kb] = *(const bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16);
+        s.qh[kb] = *(const bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16);
+        s.ql[kb] = *(const bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16);
+    }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        s.kth[b] = *(const bf16x4 *)(rec + Rec::KTH + b * 512 + l * 8);
+        s.ktl[b] = *(const bf16x4 *)(rec + Rec::KTL + b * 512 + l * 8);
+        s.eg[b] = *(const f32x4 *)(rec + Rec::EG + (16 * b + 4 * gq) * 4);
+    }
+    s.ph = *(const bf16x4 *)(rec + Rec::PH + l * 8);
+    s.pl = *(const bf16x4 *)(rec + Rec::PL + l * 8);
+    s.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
+    // vsrc points at V[t0][h][col], vstride = H*128 elements between tokens
+    uint16_t vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vv[j] = (4 * gq + j < nc) ? vsrc[(4 * gq + j) * vstride] : 0;
+    s.v = __builtin_bit_cast(bf16x4, (ushort4{vv[0], vv[1], vv[2], vv[3]}));
+}
+
+// One chunk of the recurrence on a 16-column state slice S (D layout, 8 key
+// blocks). Returns the chunk's outputs O[4g+j][col] (scale already folded in).
+__device__ __forceinline__ f32x4 recur_step(const StepIn &s, f32x4 (&S)[8]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const bf16x4 z4 = {};
+    // state as B operand, split hi/lo, permuted key labelling
+    bf16x8 sh[4], sl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x4 h0, l0, h1, l1;
+        split4(S[2 * kb], h0, l0);
+        split4(S[2 * kb + 1], h1, l1);
+        sh[kb] = cat(h0, h1);
+        sl[kb] = cat(l0, l1);
+    }
+    // U = (T Diag(beta)) V, then Vn = U - W S  (two accumulators to shorten the chain)
+    f32x4 va = mfma(s.tb, cat(s.v, s.v), zero);
+    f32x4 vb = zero;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        va = mfma(s.wn[kb], sh[kb], va);
+        vb = mfma(s.wn[kb], sl[kb], vb);
+    }
+    const f32x4 vn = va + vb;
+    // O = Q+ S (3-term split) ...
+    f32x4 o = zero;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        o = mfma(s.qh[kb], sh[kb], o);
+        o = mfma(s.qh[kb], sl[kb], o);
+        o = mfma(s.ql[kb], sh[kb], o);
+    }
+    // ... + P Vn
+    bf16x4 vh, vl;
+    split4(vn, vh, vl);
+    const bf16x8 vs = cat(vh, vl);
+    o = mfma(cat(s.ph, s.ph), vs, o);
+    o = mfma(cat(s.pl, z4), vs, o);
+    // S <- Diag(e^{G_C}) S + K~^T Vn  (K~ split: hi.(Vh + Vl) + lo.Vh)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        S[b] = mfma(cat(s.kth[b], s.kth[b]), vs, S[b] * s.eg[b]);
+        S[b] = mfma(cat(s.ktl[b], z4), vs, S[b]);
+    }
+    return o;
+}
+
+}  // namespace kda

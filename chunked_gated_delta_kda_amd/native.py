@@ -1,0 +1,68 @@
+"""ctypes binding of libkda.so (include/kda.h). Argument marshalling only.
+
+Loading fails loudly when the library has not been built; there is no other
+compute path.
+"""
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_OK = 0
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
+          4: "KDA_ERR_ALLOC", 5: "KDA_ERR_LAUNCH", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_ALIAS"}
+VARIANTS = {"auto": 0, "split": 1, "fused": 2}
+
+#: every symbol include/kda.h declares
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
+           "kda_status_string", "kda_version")
+
+
+class KdaOptions(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libkda.so; raises if it is missing (build it with chunked_gated_delta_kda_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python -m chunked_gated_delta_kda_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    fwd_args = [vp, vp, vp, f32p, f32p, ctypes.c_float, vp, i32, i32, i32, i32, f32p, f32p, f32p, vp]
+    lib.kda_fwd.argtypes = fwd_args
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(KdaOptions)]
+    lib.kda_fwd_ex.restype = ctypes.c_int
+    lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.kda_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_select_variant.argtypes = [i32, i32, i32]
+    lib.kda_select_variant.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().kda_status_string(status).decode()
+
+
+def check(status):
+    if status != KDA_OK:
+        raise KdaError(status, status_string(status))

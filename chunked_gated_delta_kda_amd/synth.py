@@ -177,3 +177,28 @@ def parity(got, ref):
 
 def passes(m, rel=GATE_REL_L2, mx=GATE_MAX_ABS_RMS):
     return m["finite"] and m["rel_l2"] <= rel and m["max_abs_rms"] <= mx
+
+
+# ----------------------------------------------------------------------------- device upload
+def to_device(w, device="cuda"):
+    """Copy a workload's host arrays to device tensors (bf16 bits are reinterpreted, not converted)."""
+    import torch
+
+    def bf16(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+
+    d = {"q": bf16(w.q), "k": bf16(w.k), "v": bf16(w.v),
+         "g": torch.from_numpy(w.g).to(device), "beta": torch.from_numpy(w.beta).to(device),
+         "cu_seqlens": torch.from_numpy(w.cu_seqlens.astype(np.int32)).to(device),
+         "initial_state": None if w.initial_state is None else torch.from_numpy(w.initial_state).to(device),
+         "scale": w.scale}
+    return d
+
+
+def oracle_inputs(w):
+    """The same inputs as float64 host arrays (exact upcast), for the oracle."""
+    return dict(q=w.q_f32().astype(np.float64), k=w.k_f32().astype(np.float64),
+                v=w.v_f32().astype(np.float64), g=w.g.astype(np.float64),
+                beta=w.beta.astype(np.float64), scale=float(w.scale),
+                cu_seqlens=w.cu_seqlens.astype(np.int64),
+                initial_state=None if w.initial_state is None else w.initial_state.astype(np.float64))

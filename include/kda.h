@@ -1,0 +1,116 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward library.
+ *
+ * Operation (per sequence n and head h, tokens t of that sequence in order):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp(max(g_t, -5))) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * with S_0 = initial_state[n,h] (zeros when NULL) and final_state[n,h] = S_last.
+ * This is the gated delta rule with one decay per key channel that the
+ * FlashKDA articles describe (smzdm.com, "KDA 内核到底难在哪": per-channel
+ * decay over a fixed-size recurrent state, log-decay bounded below by
+ * lower_bound = -5, 16-token chunks); variable-length batches are packed
+ * through cu_seqlens (nerdleveltech.com, summary and "FLA" sections); only
+ * head dimension K = V = 128 is supported (same article, requirements).
+ *
+ * All pointers except `opt` are DEVICE pointers on the current HIP device.
+ * The caller owns every buffer; the library keeps no pointer after return.
+ * Calls are asynchronous: work is enqueued on `stream` (NULL = the default
+ * stream) and the call returns without synchronising. Errors found on the
+ * host are returned before anything is enqueued; no C++ exception crosses
+ * this interface.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128
+#define KDA_CHUNK 16
+#define KDA_LOWER_BOUND (-5.0f)
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL                              */
+    KDA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, too big  */
+    KDA_ERR_UNSUPPORTED = 3, /* head_dim != 128, unknown variant, non-finite scale      */
+    KDA_ERR_ALLOC = 4,       /* workspace allocation failed or caller workspace too small */
+    KDA_ERR_LAUNCH = 5,      /* a kernel launch failed                                  */
+    KDA_ERR_DEVICE = 6,      /* no usable gfx950 device, or a HIP runtime call failed   */
+    KDA_ERR_ALIAS = 7        /* final_state partially overlaps initial_state            */
+} kda_status;
+
+typedef enum kda_variant {
+    KDA_VARIANT_AUTO = 0,  /* library picks by shape                                   */
+    KDA_VARIANT_SPLIT = 1, /* chunk-parallel prep kernel + sequential recurrence kernel */
+    KDA_VARIANT_FUSED = 2  /* one kernel: prep produced on chip, feeding the recurrence */
+} kda_variant;
+
+typedef struct kda_options {
+    int32_t variant;        /* kda_variant                                              */
+    int32_t reserved;       /* must be 0                                                */
+    void *workspace;        /* device scratch for the split variant, or NULL: then the  */
+                            /* library allocates it stream-ordered on `stream`          */
+    size_t workspace_bytes; /* size of `workspace`; see kda_workspace_bytes()           */
+} kda_options;
+
+/*
+ * kda_fwd -- KDA forward (prefill) over a packed batch.
+ *
+ *   q, k        bf16 [total_tokens, num_heads, 128], contiguous (token-major)
+ *   v           bf16 [total_tokens, num_heads, 128]
+ *   g           fp32 [total_tokens, num_heads, 128]: natural-log decay per key
+ *               channel (expected <= 0); values below -5 act as -5
+ *   beta        fp32 [total_tokens, num_heads]: write strength per token and head
+ *   scale       output scale (e.g. 1/sqrt(128)); must be finite
+ *   cu_seqlens  int32 [num_seqs+1], 0 = c_0 <= c_1 <= ... <= c_N = total_tokens
+ *               (sequence n owns tokens [c_n, c_{n+1})); NULL means one
+ *               sequence of total_tokens tokens (then num_seqs must be 1).
+ *               Monotonicity and c_N = total_tokens are preconditions that are
+ *               not checked: violating them is undefined behaviour.
+ *   num_seqs    N >= 1;  total_tokens T >= 0;  num_heads H >= 1;  head_dim == 128
+ *   initial_state  fp32 [N, H, 128(key), 128(value)] or NULL (zeros)
+ *   out         fp32 [T, H, 128]: o_t (written for every token)
+ *   final_state fp32 [N, H, 128, 128] or NULL (not written). It may be the
+ *               same pointer as initial_state (updated in place) but must not
+ *               otherwise overlap it.
+ *   stream      hipStream_t or NULL
+ *
+ * Returns KDA_OK or a kda_status code. Inputs are not modified.
+ */
+int kda_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,
+            float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+            int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+            float *final_state, void *stream);
+
+/* kda_fwd with options (variant choice, caller-provided workspace). opt may be NULL. */
+int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+               float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+               int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+               float *final_state, void *stream, const kda_options *opt);
+
+/* Bytes of device workspace kda_fwd_ex needs for this shape and variant
+ * (0 for a variant that needs none). Returns 0 for invalid shapes too. */
+size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                           int32_t variant);
+
+/* The variant KDA_VARIANT_AUTO resolves to for this shape. */
+int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
+
+/* Static, NUL-terminated description of a status code. */
+const char *kda_status_string(int status);
+
+/* Static version string. */
+const char *kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

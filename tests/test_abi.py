@@ -1,0 +1,77 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from chunked_gated_delta_kda_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(kda_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(native.LIB_PATH):
+        pytest.skip("libkda.so not built")
+    return native.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(native.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert b"gfx950" in lib.kda_version()
+    for s in range(8):
+        assert lib.kda_status_string(s)
+    assert lib.kda_status_string(99) == b"unknown status"
+
+
+P = ctypes.c_void_p(16)   # never dereferenced: every call below fails validation first
+
+
+def call(lib, **over):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.088, cu=P, N=1, T=16, H=2, D=128, s0=None,
+             out=P, fin=P, opt=None)
+    a.update(over)
+    opt = ctypes.byref(a["opt"]) if a["opt"] is not None else None
+    return lib.kda_fwd_ex(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], a["N"],
+                          a["T"], a["H"], a["D"], a["s0"], a["out"], a["fin"], None, opt)
+
+
+def test_validation_errors(lib):
+    assert call(lib, D=64) == 3                       # KDA_ERR_UNSUPPORTED
+    assert call(lib, scale=float("nan")) == 3
+    assert call(lib, scale=float("inf")) == 3
+    assert call(lib, N=0) == 2                        # KDA_ERR_SHAPE
+    assert call(lib, T=-1) == 2
+    assert call(lib, H=0) == 2
+    assert call(lib, cu=None, N=2) == 2
+    assert call(lib, q=None) == 1                     # KDA_ERR_NULL
+    assert call(lib, beta=None) == 1
+    assert call(lib, out=None) == 1
+    assert call(lib, opt=native.KdaOptions(7, 0, None, 0)) == 3
+    assert call(lib, opt=native.KdaOptions(0, 1, None, 0)) == 3
+    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10)
+    assert call(lib, opt=small) == 4                  # KDA_ERR_ALLOC: workspace too small
+    # final_state partially overlapping initial_state
+    assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + 64)) == 7
+
+
+def test_workspace_bytes(lib):
+    assert lib.kda_workspace_bytes(0, 16, 1, 1) == 0
+    b = lib.kda_workspace_bytes(1, 8192, 32, 1)
+    assert b >= (8192 // 16) * 32 * 23040
+    assert lib.kda_select_variant(1, 8192, 32) in (1, 2)
