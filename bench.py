@@ -1,0 +1,234 @@
+#!/usr/bin/env python3
+"""KDA forward (prefill) benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--variant auto]
+
+A step is one kda_fwd call over the whole synthetic workload (chunk map,
+chunk prep and the sequential recurrence: every kernel of the path) with the
+inputs already resident in device memory. W untimed steps, then exactly K
+timed steps bracketed by device synchronisation. Prints one JSON line.
+
+Per-kernel durations come from HIP events that the library records on its
+own stream between its kernels (kda_options.stage_events), over the same
+timed steps. The CPU baseline is the fp64 oracle on the host cores, timed in
+the same run on the same inputs; it also provides the parity check printed
+with the result.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from chunked_gated_delta_kda_amd import synth  # noqa: E402
+
+METRIC = "KDA prefill fwd tokens/s + % bf16 MFMA peak, 1 MI355X (T=8192, dk=dv=128)"
+HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+FLOP_PER_TOKEN_HEAD = 121856      # chunked method at C=16: 6 d^2 + 2C(3d + 2d) + 12 C^2, d = 128
+STATE_BYTES = 128 * 128 * 4       # one (sequence, head) state, fp32
+# algorithmic bytes per token-head that each kernel must move (inputs it reads,
+# outputs it writes); together they are q,k,v bf16 + g fp32 + beta fp32 + o fp32 = 1796 B
+KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796}
+KERNELS = {"split": ["chunk_map", "prep", "recur"], "fused": ["chunk_map", "fused"]}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch loaded (libkda.so binds to the same one)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def array(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            arr[i] = e.value
+            self.made.append(e.value)
+        return arr
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(out.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_gated_delta_kda_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources for this workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, threads, gpu_o, gpu_f):
+    import oracle
+    inp = synth.oracle_inputs(w)
+    pairs = [(n, h) for n in range(w.N) for h in range(w.H)]
+    t0 = time.perf_counter()
+    ro, rf = oracle.kda_forward(**inp, pairs=pairs, threads=threads)
+    dt = time.perf_counter() - t0
+    par_o = synth.parity(gpu_o, ro)
+    par_f = synth.parity(gpu_f, rf)
+    return dt, par_o, par_f
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(synth.CONFIGS),
+                    help="workload (default 2: fixed-length prefill T=8192, H=32)")
+    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating config {args.config}: {synth.CONFIGS[args.config]['name']}")
+    w = synth.config_workload(args.config)
+    d = synth.to_device(w, dev)
+    N, T, H = w.N, w.T, w.H
+    variant = args.variant if args.variant != "auto" else kda.select_variant(N, T, H)
+    out = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
+    fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+    nws = kda.workspace_bytes(N, T, H, variant)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+
+    names = KERNELS[variant]
+    ev = HipEvents()
+    n_ev = len(names) + 1
+    step_events = [ev.array(n_ev) for _ in range(args.steps)]
+
+    def step(events=None):
+        kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["cu_seqlens"],
+                d["initial_state"], variant=variant, out=out, final_state=fin, workspace=ws,
+                stage_events=events)
+
+    log(f"[bench] variant={variant} warmup={args.warmup} steps={args.steps}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(step_events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = {nm: float(np.mean([ev.ms(e[j], e[j + 1]) for e in step_events]))
+               for j, nm in enumerate(names)}
+    ev.close()
+    log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms): {kern_ms}")
+
+    TH = T * H
+    states = N * H * STATE_BYTES * ((1 if w.initial_state is not None else 0) + 1)
+    alg_bytes_total = TH * 1796 + states
+    alg_flops = TH * FLOP_PER_TOKEN_HEAD
+    step_s = ms_per_step / 1e3
+    tokens_per_s = T / step_s
+
+    def kernel_alg_bytes(nm):
+        if nm == "chunk_map":
+            return 4 * (N + 1)
+        b = TH * KERNEL_BYTES_PER_TOKEN_HEAD[nm]
+        if nm in ("recur", "fused"):
+            b += states
+        return b
+
+    dom = max((nm for nm in names if nm != "chunk_map"), key=lambda nm: kern_ms[nm])
+    dom_s = kern_ms[dom] / 1e3
+    achieved = kernel_alg_bytes(dom) / dom_s / 1e9
+    workload = f"config{args.config}"
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dom, workload)}
+
+    res = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta)",
+           "config": {"workload": f"{synth.CONFIGS[args.config]['name']} (config {args.config})",
+                      "num_seqs": N, "total_tokens": T, "num_heads": H, "dk": 128, "dv": 128,
+                      "chunk": 16, "variant": variant, "initial_state": w.initial_state is not None},
+           "tflops": round(alg_flops / step_s / 1e12, 2),
+           "mfma_bf16_peak_frac": round(alg_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "path_hbm_frac": round(alg_bytes_total / step_s / 1e9 / HBM_PEAK_GBS, 4),
+           "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+           "roofline": roofline, "cpu_baseline": None}
+
+    if not args.no_cpu_baseline:
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        threads = args.cpu_threads or min(16, cores)
+        log(f"[bench] oracle on the host: {N * H} chains, {threads} threads")
+        o_np, f_np = out.cpu().numpy(), fin.cpu().numpy()
+        dt, po, pf = cpu_baseline(w, threads, o_np, f_np)
+        res["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole workload ({N * H} (sequence, head) chains, "
+                                         f"{TH} token-heads), fp64 token loop, {dt:.2f} s wall"}
+        res["parity"] = {"o": {k: po[k] for k in ("rel_l2", "max_abs_rms")},
+                         "final_state": {k: pf[k] for k in ("rel_l2", "max_abs_rms")},
+                         "pass": synth.passes(po) and synth.passes(pf)}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

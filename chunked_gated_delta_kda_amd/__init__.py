@@ -34,7 +34,7 @@ def _ptr(t):
 
 def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         output_final_state=True, *, variant="auto", out=None, final_state=None,
-        workspace=None, stream=None):
+        workspace=None, stream=None, stage_events=None):
     """KDA forward on the current HIP device.
 
     q, k, v: bf16 [T, H, 128]; g: fp32 [T, H, 128] (log-decay, clamped at -5);
@@ -82,7 +82,10 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     opt = native.KdaOptions(var, 0, ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0)
+                            workspace.numel() if workspace is not None else 0, None)
+    if stage_events is not None:   # profiling: a ctypes array of hipEvent_t handles
+        opt.n_stage_events = len(stage_events)
+        opt.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     rc = lib.kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(cu_seqlens),
                         N, T, H, Dk, _ptr(initial_state), _ptr(out), _ptr(final_state),

@@ -24,6 +24,9 @@ SOURCES = ["kda_api.cpp", "kda_split.hip"]
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Werror",
           "-Wno-unused-command-line-argument",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in VGPRs: the state is also touched by VALU every chunk,
+          # and the AGPR form costs a copy per element each way
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I" + INCLUDE, "-I" + CSRC]
 
 
@@ -48,20 +51,27 @@ def _filter(err):
     return "\n".join(x for x in err.splitlines() if "packed-fp32-ops" not in x)
 
 
-def build(verbose=False, extra=()):
+def build(verbose=False, extra=(), out=None):
     os.makedirs(BUILD_DIR, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{_filter(r.stderr)}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(LIB)
-    return LIB
+        print(lib)
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True, extra=tuple(sys.argv[1:]))
+    args = sys.argv[1:]
+    out = None
+    if "-o" in args:
+        i = args.index("-o")
+        out = os.path.abspath(args[i + 1])
+        del args[i:i + 2]
+    build(verbose=True, extra=tuple(args), out=out)

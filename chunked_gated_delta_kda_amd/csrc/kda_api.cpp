@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "kda.h"
@@ -44,6 +45,21 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 int resolve_variant(int v) { return v == KDA_VARIANT_AUTO ? KDA_VARIANT_SPLIT : v; }
+
+// Waves per recurrence block (each wave owns 16 value columns). Few (sequence, head)
+// chains: one wave per block spreads the chains over more CUs; many chains: four
+// waves per block share each chunk record through one LDS ring. KDA_RECUR_WAVES
+// (1, 2 or 4) overrides the choice, for tuning.
+int recur_waves(int64_t N, int64_t H) {
+    if (const char *e = std::getenv("KDA_RECUR_WAVES")) {
+        const int w = std::atoi(e);
+        if (w == 1 || w == 2 || w == 4) return w;
+    }
+    const int64_t chains = N * H;
+    if (chains * 8 <= 512) return 1;
+    if (chains * 4 <= 1024) return 2;
+    return 4;
+}
 
 }  // namespace
 
@@ -87,7 +103,9 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
                float *final_state, void *stream, const kda_options *opt) {
     // ---- host-side validation, before anything is enqueued
-    if (opt && opt->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    const int n_ev = opt ? opt->n_stage_events : 0;
+    if (n_ev != 0 && (n_ev < 2 || n_ev > KDA_MAX_STAGE_EVENTS || !opt->stage_events))
+        return KDA_ERR_UNSUPPORTED;
     const int variant = opt ? opt->variant : KDA_VARIANT_AUTO;
     if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED)
         return KDA_ERR_UNSUPPORTED;
@@ -127,12 +145,26 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     int32_t *order = (int32_t *)(ws + lay.order);
     char *recs = ws + lay.recs;
 
+    // stage events (profiling only): slot i after kernel i, trailing slots after the last
+    void **ev = n_ev ? opt->stage_events : nullptr;
+    int ev_next = 0;
+    auto mark = [&](bool last) -> bool {
+        if (!ev) return true;
+        do {
+            if (ev_next < n_ev && hipEventRecord((hipEvent_t)ev[ev_next++], st) != hipSuccess)
+                return false;
+        } while (last && ev_next < n_ev);
+        return true;
+    };
+
     int rc = KDA_OK;
-    if (kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, st) != hipSuccess ||
+    if (!mark(false) ||
+        kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, st) != hipSuccess || !mark(false) ||
         kda::launch_prep((const uint16_t *)q, (const uint16_t *)k, g, beta, cu_seqlens, N, T, H,
-                         scale, chunk_off, recs, max_chunks(N, T), st) != hipSuccess ||
+                         scale, chunk_off, recs, max_chunks(N, T), st) != hipSuccess || !mark(false) ||
         kda::launch_recur(recs, (const uint16_t *)v, cu_seqlens, chunk_off, order, N, T, H,
-                          initial_state, out, final_state, 4, st) != hipSuccess)
+                          initial_state, out, final_state, recur_waves(N, H), st) != hipSuccess ||
+        !mark(true))
         rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;

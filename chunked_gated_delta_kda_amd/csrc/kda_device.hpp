@@ -43,6 +43,15 @@ constexpr int C = 16;              // chunk length
 constexpr float LOWER_BOUND = -5.0f;
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Precision recipe of the state products (compile-time): whether the state's
+// bf16 lo part enters W.S and Q+.S (1) or only its hi part (0).
+#ifndef KDA_SPLIT_S_WS
+#define KDA_SPLIT_S_WS 1
+#endif
+#ifndef KDA_SPLIT_S_QS
+#define KDA_SPLIT_S_QS 1
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -64,17 +73,31 @@ __device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 
 // e^x through the hardware base-2 exponential (v_exp_f32).
 __device__ __forceinline__ float exp_e(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 
-// x = hi + lo with hi = bf16(x) (round to nearest even) and lo = bf16(x - hi).
-__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
-    hi = __builtin_convertvector(x, bf16x4);
-    f32x4 h = __builtin_convertvector(hi, f32x4);
-    lo = __builtin_convertvector(x - h, bf16x4);
+// Two floats to packed bf16 (round to nearest even): one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{a, b}), bf16x2));
 }
 
+// x = hi + lo with hi = bf16(x) (round to nearest even) and lo = bf16(x - hi);
+// 3 VALU operations per element (pack-convert, unpack, subtract, pack-convert).
 __device__ __forceinline__ void split2(f32x2 x, bf16x2 &hi, bf16x2 &lo) {
-    hi = __builtin_convertvector(x, bf16x2);
-    f32x2 h = __builtin_convertvector(hi, f32x2);
-    lo = __builtin_convertvector(x - h, bf16x2);
+    const uint32_t h = pack2(x.x, x.y);
+    const float h0 = __uint_as_float(h << 16), h1 = __uint_as_float(h & 0xffff0000u);
+    hi = __builtin_bit_cast(bf16x2, h);
+    lo = __builtin_bit_cast(bf16x2, pack2(x.x - h0, x.y - h1));
+}
+
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+    bf16x2 h0, l0, h1, l1;
+    split2(f32x2{x[0], x[1]}, h0, l0);
+    split2(f32x2{x[2], x[3]}, h1, l1);
+    hi = __builtin_shufflevector(h0, h1, 0, 1, 2, 3);
+    lo = __builtin_shufflevector(l0, l1, 0, 1, 2, 3);
+}
+
+// Round four floats to bf16.
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    return __builtin_bit_cast(bf16x4, (uint2{pack2(x[0], x[1]), pack2(x[2], x[3])}));
 }
 
 // Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8). Return a
@@ -98,7 +121,8 @@ struct Rec {
     static constexpr int PL = 20992;   // bf16 [64][4]: P lo
     static constexpr int TB = 21504;   // bf16 [64][8]: (T Diag(beta))[l%16][4g+j] hi | lo
     static constexpr int EG = 22528;   // f32 [128]: e^{G_C} per key channel
-    static constexpr int BYTES = 23040;
+    static constexpr int USED = 23040;
+    static constexpr int BYTES = 23552; // padded to whole 1 KiB wave loads (64 lanes x 16 B)
 };
 
 // LDS scratch of one chunk prep (one wave).
@@ -189,7 +213,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
             const f32x2 kp = {k0 * ep0, k1 * ep1};
             const f32x2 km = {k0 * en0, k1 * en1};
             const f32x2 qp = {scale * q0 * ep0, scale * q1 * ep1};
-            *(bf16x2 *)&L.kp[tt * PrepLds::ROW + c0] = __builtin_convertvector(kp, bf16x2);
+            *(uint32_t *)&L.kp[tt * PrepLds::ROW + c0] = pack2(kp.x, kp.y);
             bf16x2 hi, lo;
             split2(km, hi, lo);
             *(bf16x2 *)&L.kmh[tt * PrepLds::ROW + c0] = hi;
@@ -204,8 +228,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            *(bf16x2 *)&L.kpt[(c0 + ch) * 16 + t] =
-                __builtin_convertvector((f32x2{kpT[0][ch], kpT[1][ch]}), bf16x2);
+            *(uint32_t *)&L.kpt[(c0 + ch) * 16 + t] = pack2(kpT[0][ch], kpT[1][ch]);
             *(f32x2 *)&L.ktt[(c0 + ch) * 16 + t] = f32x2{ktT[0][ch], ktT[1][ch]};
         }
     }
@@ -275,8 +298,8 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const bf16x4 a = __builtin_convertvector(-Wt[2 * kb], bf16x4);
-        const bf16x4 b = __builtin_convertvector(-Wt[2 * kb + 1], bf16x4);
+        const bf16x4 a = to_bf16x4(-Wt[2 * kb]);
+        const bf16x4 b = to_bf16x4(-Wt[2 * kb + 1]);
         *(bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16) = cat(a, b);
         const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
         *(bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16) =
@@ -304,10 +327,11 @@ struct StepIn {
     bf16x4 v;     // V[4g+j][col], zero past the chunk end
 };
 
-__device__ __forceinline__ void load_step(StepIn &s, const char *__restrict__ rec,
-                                          const uint16_t *__restrict__ vsrc, int64_t vstride,
-                                          int nc) {
-    const int l = threadIdx.x & 63, gq = l >> 4;
+// Read one wave's step inputs from a chunk record (LDS or global) and from a
+// V tile laid out [16 tokens][vcols] bf16, this wave's columns starting at vcol0.
+__device__ __forceinline__ void read_step(StepIn &s, const char *rec, const uint16_t *vtile,
+                                          int vcols, int vcol0) {
+    const int l = threadIdx.x & 63, gq = l >> 4, c = l & 15;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         s.wn[kb] = *(const bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16);
@@ -323,10 +347,9 @@ __device__ __forceinline__ void load_step(StepIn &s, const char *__restrict__ re
     s.ph = *(const bf16x4 *)(rec + Rec::PH + l * 8);
     s.pl = *(const bf16x4 *)(rec + Rec::PL + l * 8);
     s.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
-    // vsrc points at V[t0][h][col], vstride = H*128 elements between tokens
     uint16_t vv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) vv[j] = (4 * gq + j < nc) ? vsrc[(4 * gq + j) * vstride] : 0;
+    for (int j = 0; j < 4; ++j) vv[j] = vtile[(4 * gq + j) * vcols + vcol0 + c];
     s.v = __builtin_bit_cast(bf16x4, (ushort4{vv[0], vv[1], vv[2], vv[3]}));
 }
 
@@ -335,39 +358,56 @@ __device__ __forceinline__ void load_step(StepIn &s, const char *__restrict__ re
 __device__ __forceinline__ f32x4 recur_step(const StepIn &s, f32x4 (&S)[8]) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const bf16x4 z4 = {};
-    // state as B operand, split hi/lo, permuted key labelling
+    // state as B operand, permuted key labelling: hi part first (it gates W.S)
     bf16x8 sh[4], sl[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        bf16x4 h0, l0, h1, l1;
-        split4(S[2 * kb], h0, l0);
-        split4(S[2 * kb + 1], h1, l1);
-        sh[kb] = cat(h0, h1);
-        sl[kb] = cat(l0, l1);
-    }
+    for (int kb = 0; kb < 4; ++kb)
+        sh[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
     // U = (T Diag(beta)) V, then Vn = U - W S  (two accumulators to shorten the chain)
     f32x4 va = mfma(s.tb, cat(s.v, s.v), zero);
     f32x4 vb = zero;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        va = mfma(s.wn[kb], sh[kb], va);
-        vb = mfma(s.wn[kb], sl[kb], vb);
+        if (kb & 1) vb = mfma(s.wn[kb], sh[kb], vb);
+        else va = mfma(s.wn[kb], sh[kb], va);
+    }
+    if (KDA_SPLIT_S_WS || KDA_SPLIT_S_QS) {
+        // lo part: x - float(hi), rounded
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const f32x4 a = S[2 * kb], b = S[2 * kb + 1];
+            const uint2 h0 = __builtin_bit_cast(uint2, __builtin_shufflevector(sh[kb], sh[kb], 0, 1, 2, 3));
+            const uint2 h1 = __builtin_bit_cast(uint2, __builtin_shufflevector(sh[kb], sh[kb], 4, 5, 6, 7));
+            const uint32_t l0 = pack2(a[0] - __uint_as_float(h0.x << 16), a[1] - __uint_as_float(h0.x & 0xffff0000u));
+            const uint32_t l1 = pack2(a[2] - __uint_as_float(h0.y << 16), a[3] - __uint_as_float(h0.y & 0xffff0000u));
+            const uint32_t l2 = pack2(b[0] - __uint_as_float(h1.x << 16), b[1] - __uint_as_float(h1.x & 0xffff0000u));
+            const uint32_t l3 = pack2(b[2] - __uint_as_float(h1.y << 16), b[3] - __uint_as_float(h1.y & 0xffff0000u));
+            sl[kb] = __builtin_bit_cast(bf16x8, (uint4{l0, l1, l2, l3}));
+        }
+    }
+    if (KDA_SPLIT_S_WS) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            if (kb & 1) vb = mfma(s.wn[kb], sl[kb], vb);
+            else va = mfma(s.wn[kb], sl[kb], va);
+        }
     }
     const f32x4 vn = va + vb;
-    // O = Q+ S (3-term split) ...
-    f32x4 o = zero;
+    // O = Q+ S (Q+ split hi/lo; two accumulators keep the dependent chains short) ...
+    f32x4 oa = zero, ob = zero;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        o = mfma(s.qh[kb], sh[kb], o);
-        o = mfma(s.qh[kb], sl[kb], o);
-        o = mfma(s.ql[kb], sh[kb], o);
+        oa = mfma(s.qh[kb], sh[kb], oa);
+        if (KDA_SPLIT_S_QS) ob = mfma(s.qh[kb], sl[kb], ob);
+        oa = mfma(s.ql[kb], sh[kb], oa);
     }
     // ... + P Vn
     bf16x4 vh, vl;
     split4(vn, vh, vl);
     const bf16x8 vs = cat(vh, vl);
-    o = mfma(cat(s.ph, s.ph), vs, o);
-    o = mfma(cat(s.pl, z4), vs, o);
+    ob = mfma(cat(s.ph, s.ph), vs, ob);
+    ob = mfma(cat(s.pl, z4), vs, ob);
+    const f32x4 o = oa + ob;
     // S <- Diag(e^{G_C}) S + K~^T Vn  (K~ split: hi.(Vh + Vl) + lo.Vh)
 #pragma unroll
     for (int b = 0; b < 8; ++b) {

@@ -6,7 +6,7 @@
 
 namespace kda {
 
-constexpr int REC_BYTES = 23040;   // bytes of one chunk record (Rec::BYTES)
+constexpr int REC_BYTES = 23552;   // bytes of one chunk record (Rec::BYTES)
 
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
                             hipStream_t st);

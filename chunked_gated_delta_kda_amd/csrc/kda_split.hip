@@ -93,14 +93,78 @@ __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q
 }
 
 // ---------------------------------------------------------------- recurrence
-// NW waves per block, one 16-column state slice each; block covers 16*NW
-// value columns of one (sequence, head). Blocks of one (sequence, head) are
-// given consecutive logical ids, and xcd_remap keeps them on one XCD.
+// NW waves per block, one 16-column state slice each; a block covers 16*NW
+// value columns of one (sequence, head). Chunk records and the block's V tile
+// stream through an NSLOT-deep LDS ring filled by direct global->LDS loads
+// (no registers held while in flight), NSLOT-1 chunks ahead of the compute.
+// Blocks of one (sequence, head) get consecutive logical ids; xcd_remap keeps
+// them on one XCD so they share the record reads in L2.
 template <int NW>
+struct Ring {
+    static constexpr int REC_LOADS = Rec::BYTES / 1024;              // 1 KiB wave loads
+    static constexpr int VCOLS = 16 * NW;                            // value columns per block
+    static constexpr int V_BYTES = 16 * VCOLS * 2;                   // [16 tokens][VCOLS] bf16
+    static constexpr int V_LOADS = (V_BYTES + 1023) / 1024;
+    static constexpr int V_LANE = 16;                                // bytes per lane
+    static constexpr int V_LPR = VCOLS * 2 / V_LANE;                 // lanes per token row
+    static constexpr int V_ACTIVE = V_BYTES / V_LOADS / V_LANE;      // lanes with data per load
+    static constexpr int LOADS = REC_LOADS + V_LOADS;
+    static constexpr int SLOT = Rec::BYTES + V_LOADS * 1024;
+    static constexpr int loads_of(int w) { return (LOADS - w + NW - 1) / NW; }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]; others left open
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+#define KDA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Issue this wave's share of the loads of one chunk (record + V tile) into an LDS slot.
+template <int NW>
+__device__ __forceinline__ void ring_fill(char *slot, const char *rec, const uint16_t *v,
+                                          int64_t t0, int nc, int h, int H, int vcol0) {
+    using R = Ring<NW>;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < R::LOADS; ++i) {
+        if (i % NW != w) continue;
+        if (i < R::REC_LOADS) {
+            __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
+                                             KDA_LDS(slot + i * 1024), 16, 0, 0);
+        } else {
+            const int j = i - R::REC_LOADS;
+            const int row = j * (64 / R::V_LPR) + l / R::V_LPR;
+            const int col = vcol0 + (l % R::V_LPR) * (R::V_LANE / 2);
+            const int64_t t = t0 + (row < nc ? row : nc - 1);   // rows past the end: finite filler
+            if (R::V_ACTIVE == 64 || l < R::V_ACTIVE)
+                __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + col),
+                                                 KDA_LDS(slot + Rec::BYTES + j * 1024), R::V_LANE, 0, 0);
+        }
+    }
+}
+
+template <int NW, int NSLOT>
+__device__ __forceinline__ void ring_wait(int w) {
+    // own loads of the chunk about to be consumed are done once at most the
+    // loads of the NSLOT-2 younger chunks are still outstanding
+    using R = Ring<NW>;
+    if (w == 0) wait_vmcnt<(NSLOT - 2) * R::loads_of(0)>();
+    else if (NW > 1 && w == NW - 1) wait_vmcnt<(NSLOT - 2) * R::loads_of(NW > 1 ? NW - 1 : 0)>();
+    else wait_vmcnt<(NSLOT - 2) * R::loads_of(NW > 2 ? 1 : 0)>();
+}
+
+template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * NW) void recur_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+    using R = Ring<NW>;
+    static_assert(NSLOT >= 2, "ring needs two slots");
+    static_assert(R::loads_of(0) - R::loads_of(NW - 1) <= 1, "unbalanced ring loads");
+    extern __shared__ __attribute__((aligned(16))) char ring[];
     constexpr int PARTS = D / (16 * NW);
     const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int part = bid % PARTS;
@@ -108,36 +172,50 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     const int h = sh % H;
     const int n = order[sh / H];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
-    const int col = (part * NW + w) * 16 + c;
+    const int vcol0 = part * R::VCOLS;            // first value column of this block
+    const int col = vcol0 + w * 16 + c;           // this lane's value column
     const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
     const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
-    const int64_t HD = (int64_t)H * D;
 
     f32x4 S[8];
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (s0) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+        for (int b = 0; b < 8; ++b)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            S[b][j] = s0 ? s0[sbase + (int64_t)(16 * b + 4 * gq + j) * D] : 0.f;
+            for (int j = 0; j < 4; ++j) S[b][j] = s0[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+    } else {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) S[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    if (ci0 < ci1) {
-        StepIn cur, nxt;
-        load_step(cur, recs + ((int64_t)ci0 * H + h) * Rec::BYTES, v + (bos * H + h) * D + col,
-                  HD, (int)min<int64_t>(C, eos - bos));
-        for (int ci = ci0; ci < ci1; ++ci) {
-            const int64_t t0 = bos + (int64_t)C * (ci - ci0);
+    const int nch = ci1 - ci0;
+    // every chunk index past the end is clamped to the last chunk (a harmless reload
+    // into a slot nobody reads) so that each wave issues the same loads per step
+    auto fill = [&](int it) {
+        const int k = it < nch ? it : nch - 1;
+        const int64_t t0 = bos + (int64_t)C * k;
+        ring_fill<NW>(ring + (it % NSLOT) * R::SLOT, recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES,
+                      v, t0, (int)min<int64_t>(C, eos - t0), h, H, vcol0);
+    };
+    if (nch > 0) {
+#pragma unroll
+        for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        for (int it = 0; it < nch; ++it) {
+            ring_wait<NW, NSLOT>(w);
+            __builtin_amdgcn_s_barrier();         // all waves: slot it ready, slot it-1 released
+            __builtin_amdgcn_sched_barrier(0);
+            fill(it + NSLOT - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const char *slot = ring + (it % NSLOT) * R::SLOT;
+            StepIn st;
+            read_step(st, slot, (const uint16_t *)(slot + Rec::BYTES), R::VCOLS, w * 16);
+            const f32x4 o = recur_step(st, S);
+            const int64_t t0 = bos + (int64_t)C * it;
             const int nc = (int)min<int64_t>(C, eos - t0);
-            if (ci + 1 < ci1) {
-                const int64_t t1 = t0 + C;
-                load_step(nxt, recs + ((int64_t)(ci + 1) * H + h) * Rec::BYTES,
-                          v + (t1 * H + h) * D + col, HD, (int)min<int64_t>(C, eos - t1));
-            }
-            const f32x4 o = recur_step(cur, S);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
-            cur = nxt;
         }
     }
     if (sfin) {
@@ -166,27 +244,34 @@ hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, con
     return hipGetLastError();
 }
 
+template <int NW, int NSLOT>
+static hipError_t launch_recur_t(const char *recs, const uint16_t *v, const int32_t *cu,
+                                 const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                 int H, const float *s0, float *out, float *sfin, hipStream_t st) {
+    const size_t lds = (size_t)NSLOT * Ring<NW>::SLOT;
+    auto kern = recur_kernel<NW, NSLOT>;
+    static bool attr_set = false;   // raising the dynamic LDS limit is per-kernel, idempotent
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, recs, v, cu,
+                       chunk_off, order, N, T, H, s0, out, sfin);
+    return hipGetLastError();
+}
+
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
-    const int64_t sh = (int64_t)N * H;
     switch (waves) {
-    case 1:
-        hipLaunchKernelGGL(recur_kernel<1>, dim3((unsigned)(sh * 8)), dim3(64), 0, st, recs, v, cu,
-                           chunk_off, order, N, T, H, s0, out, sfin);
-        break;
-    case 2:
-        hipLaunchKernelGGL(recur_kernel<2>, dim3((unsigned)(sh * 4)), dim3(128), 0, st, recs, v,
-                           cu, chunk_off, order, N, T, H, s0, out, sfin);
-        break;
-    case 4:
-        hipLaunchKernelGGL(recur_kernel<4>, dim3((unsigned)(sh * 2)), dim3(256), 0, st, recs, v,
-                           cu, chunk_off, order, N, T, H, s0, out, sfin);
-        break;
-    default:
-        return hipErrorInvalidValue;
+    case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 4: return launch_recur_t<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace kda

@@ -7,7 +7,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkda.so")
+# KDA_LIB points at an alternative build of the same library (tuning experiments)
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(PKG, "libkda.so")
 
 KDA_OK = 0
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
@@ -20,8 +21,9 @@ EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
 
 
 class KdaOptions(ctypes.Structure):
-    _fields_ = [("variant", ctypes.c_int32), ("reserved", ctypes.c_int32),
-                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+    _fields_ = [("variant", ctypes.c_int32), ("n_stage_events", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class KdaError(RuntimeError):
@@ -40,6 +42,12 @@ def load_library(path=LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run `python -m chunked_gated_delta_kda_amd.build`")
+    # Load torch's HIP runtime first: libkda.so then binds to that same runtime
+    # (same SONAME), so torch streams and events are valid handles for the library.
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the library also works without torch
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
     fwd_args = [vp, vp, vp, f32p, f32p, ctypes.c_float, vp, i32, i32, i32, i32, f32p, f32p, f32p, vp]

@@ -52,12 +52,18 @@ typedef enum kda_variant {
     KDA_VARIANT_FUSED = 2  /* one kernel: prep produced on chip, feeding the recurrence */
 } kda_variant;
 
+#define KDA_MAX_STAGE_EVENTS 8
+
 typedef struct kda_options {
     int32_t variant;        /* kda_variant                                              */
-    int32_t reserved;       /* must be 0                                                */
+    int32_t n_stage_events; /* 0, or the length of stage_events (2..KDA_MAX_STAGE_EVENTS) */
     void *workspace;        /* device scratch for the split variant, or NULL: then the  */
                             /* library allocates it stream-ordered on `stream`          */
     size_t workspace_bytes; /* size of `workspace`; see kda_workspace_bytes()           */
+    void **stage_events;    /* profiling: hipEvent_t[n_stage_events], caller-created.   */
+                            /* [0] is recorded on `stream` before the first kernel,     */
+                            /* [i] after kernel i; slots past the last kernel are       */
+                            /* recorded after it too. NULL = no events.                 */
 } kda_options;
 
 /*

@@ -62,9 +62,10 @@ def test_validation_errors(lib):
     assert call(lib, q=None) == 1                     # KDA_ERR_NULL
     assert call(lib, beta=None) == 1
     assert call(lib, out=None) == 1
-    assert call(lib, opt=native.KdaOptions(7, 0, None, 0)) == 3
-    assert call(lib, opt=native.KdaOptions(0, 1, None, 0)) == 3
-    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10)
+    assert call(lib, opt=native.KdaOptions(7, 0, None, 0, None)) == 3
+    assert call(lib, opt=native.KdaOptions(0, 1, None, 0, None)) == 3      # 1 stage event
+    assert call(lib, opt=native.KdaOptions(0, 4, None, 0, None)) == 3      # events NULL
+    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10, None)
     assert call(lib, opt=small) == 4                  # KDA_ERR_ALLOC: workspace too small
     # final_state partially overlapping initial_state
     assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + 64)) == 7
@@ -73,5 +74,5 @@ def test_validation_errors(lib):
 def test_workspace_bytes(lib):
     assert lib.kda_workspace_bytes(0, 16, 1, 1) == 0
     b = lib.kda_workspace_bytes(1, 8192, 32, 1)
-    assert b >= (8192 // 16) * 32 * 23040
+    assert b >= (8192 // 16) * 32 * 23552
     assert lib.kda_select_variant(1, 8192, 32) in (1, 2)
