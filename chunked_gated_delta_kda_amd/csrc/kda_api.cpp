@@ -18,16 +18,21 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 int64_t max_chunks(int64_t N, int64_t T) { return (T + KDA_CHUNK - 1) / KDA_CHUNK + N; }
 
+// Workspace: chunk offsets [N+1], sequence order [N], an error word, and (split
+// variant only) one chunk record per (chunk, head).
 struct Layout {
-    size_t chunk_off, order, recs, total;
+    size_t chunk_off, order, err, recs, total;
 };
 
-Layout split_layout(int64_t N, int64_t T, int64_t H) {
+Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant) {
     Layout L;
     L.chunk_off = 0;
     L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
-    L.recs = L.order + align_up(sizeof(int32_t) * (size_t)N);
-    L.total = L.recs + (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
+    L.err = L.order + align_up(sizeof(int32_t) * (size_t)N);
+    L.recs = L.err + ALIGN;
+    L.total = L.recs;
+    if (variant == KDA_VARIANT_SPLIT)
+        L.total += (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
     return L;
 }
 
@@ -44,14 +49,13 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     return pa < pb + nb && pb < pa + na;
 }
 
-int resolve_variant(int v) { return v == KDA_VARIANT_AUTO ? KDA_VARIANT_SPLIT : v; }
 
 // Waves per recurrence block (each wave owns 16 value columns). Few (sequence, head)
 // chains: one wave per block spreads the chains over more CUs; many chains: four
 // waves per block share each chunk record through one LDS ring. KDA_RECUR_WAVES
 // (1, 2 or 4) overrides the choice, for tuning.
-int recur_waves(int64_t N, int64_t H) {
-    if (const char *e = std::getenv("KDA_RECUR_WAVES")) {
+int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
+    if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
         if (w == 1 || w == 2 || w == 4) return w;
     }
@@ -85,7 +89,11 @@ int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads
     (void)num_seqs;
     (void)total_tokens;
     (void)num_heads;
-    return resolve_variant(KDA_VARIANT_AUTO);
+    if (const char *e = std::getenv("KDA_VARIANT")) {
+        if (!std::strcmp(e, "split")) return KDA_VARIANT_SPLIT;
+        if (!std::strcmp(e, "fused")) return KDA_VARIANT_FUSED;
+    }
+    return KDA_VARIANT_SPLIT;
 }
 
 size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
@@ -94,8 +102,7 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    if (v != KDA_VARIANT_SPLIT) return 0;
-    return split_layout(num_seqs, total_tokens, num_heads).total;
+    return ws_layout(num_seqs, total_tokens, num_heads, v).total;
 }
 
 int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -123,11 +130,9 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int chosen = variant == KDA_VARIANT_AUTO
                            ? kda_select_variant(num_seqs, total_tokens, num_heads)
                            : variant;
-    if (chosen == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;   // not built yet
-
     hipStream_t st = (hipStream_t)stream;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    const Layout lay = split_layout(N, T, H);
+    const Layout lay = ws_layout(N, T, H, chosen);
 
     char *ws = nullptr;
     bool owned = false;
@@ -143,6 +148,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     }
     int32_t *chunk_off = (int32_t *)(ws + lay.chunk_off);
     int32_t *order = (int32_t *)(ws + lay.order);
+    int32_t *err = (int32_t *)(ws + lay.err);
     char *recs = ws + lay.recs;
 
     // stage events (profiling only): slot i after kernel i, trailing slots after the last
@@ -158,14 +164,22 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     };
 
     int rc = KDA_OK;
-    if (!mark(false) ||
-        kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, st) != hipSuccess || !mark(false) ||
-        kda::launch_prep((const uint16_t *)q, (const uint16_t *)k, g, beta, cu_seqlens, N, T, H,
-                         scale, chunk_off, recs, max_chunks(N, T), st) != hipSuccess || !mark(false) ||
-        kda::launch_recur(recs, (const uint16_t *)v, cu_seqlens, chunk_off, order, N, T, H,
-                          initial_state, out, final_state, recur_waves(N, H), st) != hipSuccess ||
-        !mark(true))
-        rc = KDA_ERR_LAUNCH;
+    bool ok = mark(false) &&
+              kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, st) == hipSuccess &&
+              mark(false);
+    if (ok && chosen == KDA_VARIANT_SPLIT) {
+        ok = kda::launch_prep((const uint16_t *)q, (const uint16_t *)k, g, beta, cu_seqlens, N, T,
+                              H, scale, chunk_off, recs, max_chunks(N, T), st) == hipSuccess &&
+             mark(false) &&
+             kda::launch_recur(recs, (const uint16_t *)v, cu_seqlens, chunk_off, order, N, T, H,
+                               initial_state, out, final_state, recur_waves(N, H), st) == hipSuccess;
+    } else if (ok) {
+        ok = kda::launch_fused((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g,
+                               beta, cu_seqlens, order, N, T, H, scale, initial_state, out,
+                               final_state, err, recur_waves(N, H, "KDA_FUSED_WAVES"),
+                               st) == hipSuccess;
+    }
+    if (!ok || !mark(true)) rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;
 }

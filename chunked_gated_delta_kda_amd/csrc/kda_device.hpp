@@ -151,6 +151,16 @@ __device__ __forceinline__ f32x4 mm16(f32x4 Nt, f32x4 M) {
     return acc;
 }
 
+// Orders one wave's LDS writes before its later LDS reads of other lanes' data.
+// A wave's LDS operations execute in issue order, so this only has to stop the
+// compiler from moving memory operations across it; it is not a workgroup
+// barrier (other waves may be anywhere).
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Identity plus/minus a D-layout matrix.
 __device__ __forceinline__ f32x4 eye_plus(f32x4 M, int lane, float sign) {
     const int col = lane & 15, r0 = 4 * (lane >> 4);
@@ -239,7 +249,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         if (4 * gq + j < nc) bj[j] = beta[(t0 + 4 * gq + j) * (int64_t)H + h];
-    __syncthreads();
+    wave_sync();
 
     // ---- phase 1: K+K-^T (both orientations) and the causal Q+K-^T, 128-deep
     f32x4 akk = {0.f, 0.f, 0.f, 0.f}, akt = akk, pt = akk;
@@ -327,11 +337,9 @@ struct StepIn {
     bf16x4 v;     // V[4g+j][col], zero past the chunk end
 };
 
-// Read one wave's step inputs from a chunk record (LDS or global) and from a
-// V tile laid out [16 tokens][vcols] bf16, this wave's columns starting at vcol0.
-__device__ __forceinline__ void read_step(StepIn &s, const char *rec, const uint16_t *vtile,
-                                          int vcols, int vcol0) {
-    const int l = threadIdx.x & 63, gq = l >> 4, c = l & 15;
+// Read one wave's step inputs from a chunk record (LDS or global).
+__device__ __forceinline__ void read_rec(StepIn &s, const char *rec) {
+    const int l = threadIdx.x & 63, gq = l >> 4;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         s.wn[kb] = *(const bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16);
@@ -347,6 +355,12 @@ __device__ __forceinline__ void read_step(StepIn &s, const char *rec, const uint
     s.ph = *(const bf16x4 *)(rec + Rec::PH + l * 8);
     s.pl = *(const bf16x4 *)(rec + Rec::PL + l * 8);
     s.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
+}
+
+// ... and this lane's V values from a tile laid out [16 tokens][vcols] bf16, the
+// wave's columns starting at vcol0.
+__device__ __forceinline__ void read_vtile(StepIn &s, const uint16_t *vtile, int vcols, int vcol0) {
+    const int l = threadIdx.x & 63, gq = l >> 4, c = l & 15;
     uint16_t vv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) vv[j] = vtile[(4 * gq + j) * vcols + vcol0 + c];

@@ -9,7 +9,7 @@ namespace kda {
 constexpr int REC_BYTES = 23552;   // bytes of one chunk record (Rec::BYTES)
 
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            hipStream_t st);
+                            int32_t *err, hipStream_t st);
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
@@ -18,5 +18,10 @@ hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, con
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st);
+
+hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                        const float *beta, const int32_t *cu, const int32_t *order, int N, int T,
+                        int H, float scale, const float *s0, float *out, float *sfin, int *err,
+                        int waves, hipStream_t st);
 
 }  // namespace kda

@@ -23,7 +23,8 @@ constexpr int ORDER_MAX = 2048;
 __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *__restrict__ cu,
                                                                  int N, int T,
                                                                  int32_t *__restrict__ chunk_off,
-                                                                 int32_t *__restrict__ order) {
+                                                                 int32_t *__restrict__ order,
+                                                                 int32_t *__restrict__ err) {
     __shared__ int32_t part[MAP_THREADS];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
@@ -49,7 +50,10 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
         if (tid == MAP_THREADS - 1) carry += part[tid];
         __syncthreads();
     }
-    if (tid == 0) chunk_off[0] = 0;
+    if (tid == 0) {
+        chunk_off[0] = 0;
+        *err = 0;
+    }
     if (N <= ORDER_MAX) {
         for (int n = tid; n < N; n += MAP_THREADS) {
             const int32_t ln = cu ? cu[n + 1] - cu[n] : T;
@@ -209,7 +213,8 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
             __builtin_amdgcn_sched_barrier(0);
             const char *slot = ring + (it % NSLOT) * R::SLOT;
             StepIn st;
-            read_step(st, slot, (const uint16_t *)(slot + Rec::BYTES), R::VCOLS, w * 16);
+            read_rec(st, slot);
+            read_vtile(st, (const uint16_t *)(slot + Rec::BYTES), R::VCOLS, w * 16);
             const f32x4 o = recur_step(st, S);
             const int64_t t0 = bos + (int64_t)C * it;
             const int nc = (int)min<int64_t>(C, eos - t0);
@@ -228,9 +233,9 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            hipStream_t st) {
+                            int32_t *err, hipStream_t st) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(MAP_THREADS), 0, st, cu, N, T, chunk_off,
-                       order);
+                       order, err);
     return hipGetLastError();
 }
 

@@ -74,3 +74,10 @@ def status_string(status):
 def check(status):
     if status != KDA_OK:
         raise KdaError(status, status_string(status))
+
+
+def error_word_offset(num_seqs):
+    """Byte offset of the device error word inside a kda_fwd_ex workspace (nonzero after
+    a call means a fused-kernel wait gave up and the outputs are not valid)."""
+    a = lambda x: (x + 255) // 256 * 256
+    return a(4 * (num_seqs + 1)) + a(4 * num_seqs)

@@ -8,11 +8,17 @@ from chunked_gated_delta_kda_amd import synth
 def run_gpu(w, variant="auto", **kw):
     import torch
     import chunked_gated_delta_kda_amd as kda
+    from chunked_gated_delta_kda_amd import native
 
     d = synth.to_device(w)
+    nbytes = kda.workspace_bytes(w.N, w.T, w.H, variant)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     o, fin = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["cu_seqlens"],
-                     d["initial_state"], variant=variant, **kw)
+                     d["initial_state"], variant=variant, workspace=ws, **kw)
     torch.cuda.synchronize()
+    off = native.error_word_offset(w.N)
+    err = int(ws[off:off + 4].view(torch.int32).item())
+    assert err == 0, f"device error word set ({err})"
     return o.cpu().numpy(), fin.cpu().numpy()
 
 
