@@ -104,6 +104,51 @@ def measured_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def ingest_pmc(fetch_csv, write_csv, workload, command):
+    """Turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch) into
+    profiles/traffic.json. Each counter is scaled by the ratio of true bytes to counted
+    bytes for the plain device copy that --copy-calibration runs in the same process
+    (the largest copy dispatch moves the same known number of bytes each way)."""
+    import collections
+    import csv
+    import re
+
+    def load(path, counter):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                per[r["Kernel_Name"]].append(float(r["Counter_Value"]) * 1024.0)
+        return per
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    if not copy:
+        raise SystemExit("no copy kernel in the counter run (use --copy-calibration)")
+    true_bytes = max(max(fetch[copy[0]]), max(write[copy[0]]))   # read == written for a copy
+    f_scale = true_bytes / max(fetch[copy[0]])
+    w_scale = true_bytes / max(write[copy[0]])
+    out = {"workload": workload, "command": command, "fetch_scale": f_scale, "write_scale": w_scale,
+           "calibration_bytes": true_bytes, "kernels": {}}
+    for name in fetch:
+        m = re.search(r"kda::(\w+?)_kernel", name)
+        if not m or name not in write:
+            continue
+        fb = float(np.median(fetch[name])) * f_scale
+        wb = float(np.median(write[name])) * w_scale
+        out["kernels"][m.group(1)] = {"workload": workload, "source_hash": kernel_source_hash(),
+                                      "fetch_bytes": fb, "write_bytes": wb,
+                                      "bytes_per_launch": fb + wb}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    prev = {}
+    if os.path.exists(TRAFFIC_FILE):
+        prev = json.load(open(TRAFFIC_FILE)).get("kernels", {})
+    prev.update(out["kernels"])
+    out["kernels"] = prev
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(w, threads, gpu_o, gpu_f):
     import oracle
     inp = synth.oracle_inputs(w)
@@ -126,7 +171,17 @@ def main():
     ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (3 times) after the timed steps, "
+                         "as the reference kernel for HBM byte counters")
+    ap.add_argument("--ingest-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 counter runs and exit")
+    ap.add_argument("--pmc-command", default="", help="command line recorded with --ingest-pmc")
     args = ap.parse_args()
+
+    if args.ingest_pmc:
+        ingest_pmc(*args.ingest_pmc, f"config{args.config}", args.pmc_command)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path (asked for --gpus "
@@ -173,6 +228,14 @@ def main():
     kern_ms = {nm: float(np.mean([ev.ms(e[j], e[j + 1]) for e in step_events]))
                for j, nm in enumerate(names)}
     ev.close()
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: 3 x {nbytes} bytes read + written")
     log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms): {kern_ms}")
 
     TH = T * H
