@@ -25,7 +25,10 @@
 // carries, so every product below relabels slots freely:
 //  * "hi/lo folding": slots 8g+j carry (k = 4g+j, hi part) and 8g+4+j carry
 //    (k = 4g+j, lo part) of a split-bf16 operand x = hi + lo, so one MFMA
-//    over a D-layout operand gives x_hi.y + x_lo.y or y.(x_hi + x_lo).
+//    over a D-layout operand gives x_hi.y + x_lo.y or y.(x_hi + x_lo). With
+//    A = [a_hi | a_lo] and B = [b_hi | b_hi] then [b_lo | 0], two MFMAs give the
+//    three-term product a_hi.b_hi + a_lo.b_hi + a_hi.b_lo, and the B operands
+//    are built once per chunk for every A that meets them.
 //  * "state permutation": for the 128-deep products against the state, slot
 //    8g+j of k-block kb is key channel 32kb+4g+j and slot 8g+4+j is
 //    32kb+16+4g+j. With that labelling the fp32 state, kept in D layout as
@@ -115,10 +118,8 @@ struct Rec {
     static constexpr int WN = 0;       // bf16 [4 kb][64 lanes][8]: -W, state-permuted A operand
     static constexpr int QH = 4096;    // bf16 [4][64][8]: Q+ hi, state-permuted A operand
     static constexpr int QL = 8192;    // bf16 [4][64][8]: Q+ lo
-    static constexpr int KTH = 12288;  // bf16 [8 blocks][64][4]: K~[4g+j][16b + l%16] hi
-    static constexpr int KTL = 16384;  // bf16 [8 blocks][64][4]: K~ lo
-    static constexpr int PH = 20480;   // bf16 [64][4]: P[l%16][4g+j] hi (causal, diagonal kept)
-    static constexpr int PL = 20992;   // bf16 [64][4]: P lo
+    static constexpr int KT = 12288;   // bf16 [8 blocks][64][8]: K~[4g+j][16b + l%16] hi(4) | lo(4)
+    static constexpr int PP = 20480;   // bf16 [64][8]: P[l%16][4g+j] hi(4) | lo(4) (causal, diagonal kept)
     static constexpr int TB = 21504;   // bf16 [64][8]: (T Diag(beta))[l%16][4g+j] hi | lo
     static constexpr int EG = 22528;   // f32 [128]: e^{G_C} per key channel
     static constexpr int USED = 23040;
@@ -278,8 +279,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     {
         bf16x4 ph, pl;
         split4(Pm, ph, pl);
-        *(bf16x4 *)(rec + Rec::PH + l * 8) = ph;
-        *(bf16x4 *)(rec + Rec::PL + l * 8) = pl;
+        *(bf16x8 *)(rec + Rec::PP + l * 16) = cat(ph, pl);
     }
 
     // ---- phase 2: T^T = (I + A^T)^{-1} = (I - X)(I + X^2)(I + X^4)(I + X^8), X = A^T
@@ -321,8 +321,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     for (int b = 0; b < 8; ++b) {
         bf16x4 hi, lo;
         split4(*(const f32x4 *)&L.ktt[(16 * b + r) * 16 + 4 * gq], hi, lo);
-        *(bf16x4 *)(rec + Rec::KTH + b * 512 + l * 8) = hi;
-        *(bf16x4 *)(rec + Rec::KTL + b * 512 + l * 8) = lo;
+        *(bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16) = cat(hi, lo);
     }
 }
 
@@ -330,8 +329,8 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
 // Inputs of one chunk step for one wave (a 16-column slice of the state).
 struct StepIn {
     bf16x8 wn[4], qh[4], ql[4];
-    bf16x4 kth[8], ktl[8];
-    bf16x4 ph, pl;
+    bf16x8 kt[8];     // K~ hi | lo, per key block
+    bf16x8 pp;        // P hi | lo
     bf16x8 tb;
     f32x4 eg[8];
     bf16x4 v;     // V[4g+j][col], zero past the chunk end
@@ -348,12 +347,10 @@ __device__ __forceinline__ void read_rec(StepIn &s, const char *rec) {
     }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        s.kth[b] = *(const bf16x4 *)(rec + Rec::KTH + b * 512 + l * 8);
-        s.ktl[b] = *(const bf16x4 *)(rec + Rec::KTL + b * 512 + l * 8);
+        s.kt[b] = *(const bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16);
         s.eg[b] = *(const f32x4 *)(rec + Rec::EG + (16 * b + 4 * gq) * 4);
     }
-    s.ph = *(const bf16x4 *)(rec + Rec::PH + l * 8);
-    s.pl = *(const bf16x4 *)(rec + Rec::PL + l * 8);
+    s.pp = *(const bf16x8 *)(rec + Rec::PP + l * 16);
     s.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
 }
 
@@ -415,18 +412,18 @@ __device__ __forceinline__ f32x4 recur_step(const StepIn &s, f32x4 (&S)[8]) {
         if (KDA_SPLIT_S_QS) ob = mfma(s.qh[kb], sl[kb], ob);
         oa = mfma(s.ql[kb], sh[kb], oa);
     }
-    // ... + P Vn
+    // ... + P Vn  (three-term split through the shared B operands)
     bf16x4 vh, vl;
     split4(vn, vh, vl);
-    const bf16x8 vs = cat(vh, vl);
-    ob = mfma(cat(s.ph, s.ph), vs, ob);
-    ob = mfma(cat(s.pl, z4), vs, ob);
+    const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
+    ob = mfma(s.pp, vhh, ob);
+    ob = mfma(s.pp, vl0, ob);
     const f32x4 o = oa + ob;
-    // S <- Diag(e^{G_C}) S + K~^T Vn  (K~ split: hi.(Vh + Vl) + lo.Vh)
+    // S <- Diag(e^{G_C}) S + K~^T Vn
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        S[b] = mfma(cat(s.kth[b], s.kth[b]), vs, S[b] * s.eg[b]);
-        S[b] = mfma(cat(s.ktl[b], z4), vs, S[b]);
+        S[b] = mfma(s.kt[b], vhh, S[b] * s.eg[b]);
+        S[b] = mfma(s.kt[b], vl0, S[b]);
     }
     return o;
 }

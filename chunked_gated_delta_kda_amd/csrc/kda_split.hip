@@ -124,6 +124,14 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// vmcnt(N) and lgkmcnt(0) together: own global loads up to the N youngest, and
+// every own LDS access, complete
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
 #define KDA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Issue this wave's share of the loads of one chunk (record + V tile) into an LDS slot.
@@ -231,6 +239,375 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     }
 }
 
+// ---------------------------------------------------------------- paired recurrence
+// NW 16-column slices per block, two waves per slice. The chain wave (w < NW)
+// runs only the state chain: V_new = U - W S (state hi part), S <- D S + K~^T V_new;
+// each chunk it publishes the pre-update state (fp32) and V_new (hi|lo) to LDS.
+// The output wave (w >= NW) runs one chunk behind, off the chain: it splits the
+// published state into hi/lo and forms O = Q+ S + P V_new. One barrier per chunk
+// (the ring's); snapshots are double-buffered by chunk parity; the output wave
+// reads its record pieces (Q+, P) of chunk it while slot it is still held and
+// keeps them in registers for one chunk.
+template <int NW>
+struct PairLayout {
+    static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
+};
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+    using R = Ring<NW>;         // record loads and the V tile of NW slices
+    constexpr int LOADS = R::REC_LOADS + R::V_LOADS;
+    constexpr int SLOT = Rec::BYTES + R::V_LOADS * 1024;
+    static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    char *snaps = ring + NSLOT * SLOT;
+
+    constexpr int PARTS = D / (16 * NW);
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int part = bid % PARTS;
+    const int sh = bid / PARTS;
+    const int h = sh % H;
+    const int n = order[sh / H];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
+    const bool chain = w < NW;
+    const bool loader = w == 2 * NW;     // issues every ring load; computes nothing
+    const int slice = chain ? w : (loader ? 0 : w - NW);
+    const int vcol0 = part * R::VCOLS;
+    const int col = vcol0 + slice * 16 + c;
+    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
+    const int nch = ci1 - ci0;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+
+    // ring fill, issued by the loader wave alone (the vector-memory pipe is busy for
+    // most of a chunk's worth of time; no compute wave waits on it)
+    auto fill = [&](int it) {
+        const int k = it < nch ? it : nch - 1;
+        const int64_t t0 = bos + (int64_t)C * k;
+        const int nc = (int)min<int64_t>(C, eos - t0);
+        char *slot = ring + (it % NSLOT) * SLOT;
+        const char *rec = recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            if (i < R::REC_LOADS) {
+                __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
+                                                 KDA_LDS(slot + i * 1024), 16, 0, 0);
+            } else {
+                const int j = i - R::REC_LOADS;
+                const int row = j * (64 / R::V_LPR) + l / R::V_LPR;
+                const int cc = vcol0 + (l % R::V_LPR) * (R::V_LANE / 2);
+                const int64_t t = t0 + (row < nc ? row : nc - 1);
+                if (R::V_ACTIVE == 64 || l < R::V_ACTIVE)
+                    __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
+                                                     KDA_LDS(slot + Rec::BYTES + j * 1024), 16, 0, 0);
+            }
+        }
+    };
+
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const bf16x4 z4 = {};
+    f32x4 S[8];
+    if (chain) {
+        if (s0) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[b][j] = s0[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = zero;
+        }
+    }
+    bf16x8 qh[4], ql[4];
+    bf16x8 pp;
+
+    // output wave: O of chunk it from snapshot it and the held Q+/P pieces
+    auto emit = [&](int it) {
+        const char *snap = snaps + ((it & 1) * NW + slice) * PairLayout<NW>::SNAP;
+        bf16x8 shi[4], slo[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const f32x4 a = *(const f32x4 *)(snap + ((2 * kb) * 64 + l) * 16);
+            const f32x4 b = *(const f32x4 *)(snap + ((2 * kb + 1) * 64 + l) * 16);
+            bf16x4 ah, al, bh, bl;
+            split4(a, ah, al);
+            split4(b, bh, bl);
+            shi[kb] = cat(ah, bh);
+            slo[kb] = cat(al, bl);
+        }
+        const bf16x8 vs = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);   // V_new hi | lo
+        const bf16x4 vh = __builtin_shufflevector(vs, vs, 0, 1, 2, 3);
+        const bf16x4 vl = __builtin_shufflevector(vs, vs, 4, 5, 6, 7);
+        f32x4 oa = zero, ob = zero;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            oa = mfma(qh[kb], shi[kb], oa);
+            ob = mfma(qh[kb], slo[kb], ob);
+            oa = mfma(ql[kb], shi[kb], oa);
+        }
+        ob = mfma(pp, cat(vh, vh), ob);
+        ob = mfma(pp, cat(vl, z4), ob);
+        const f32x4 o = oa + ob;
+        const int64_t t0 = bos + (int64_t)C * it;
+        const int nc = (int)min<int64_t>(C, eos - t0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
+    };
+
+    if (nch > 0) {
+        if (loader) {
+#pragma unroll
+            for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        }
+        for (int it = 0; it < nch; ++it) {
+            // the loader's loads of chunk it are complete once at most those of the
+            // NSLOT-2 younger chunks remain outstanding
+            if (loader) wait_vmcnt<(NSLOT - 2) * LOADS>();
+            __builtin_amdgcn_s_barrier();      // slot it ready; slot it-1 and snapshot it-2 released
+            __builtin_amdgcn_sched_barrier(0);
+            const char *slot = ring + (it % NSLOT) * SLOT;
+            if (loader) {
+                fill(it + NSLOT - 1);
+            } else if (chain) {
+                StepIn st;
+                read_rec(st, slot);
+                read_vtile(st, (const uint16_t *)(slot + Rec::BYTES), R::VCOLS, slice * 16);
+                char *snap = snaps + ((it & 1) * NW + slice) * PairLayout<NW>::SNAP;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
+                bf16x8 shi[4];
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
+                f32x4 va = mfma(st.tb, cat(st.v, st.v), zero), vb = zero;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    if (kb & 1) vb = mfma(st.wn[kb], shi[kb], vb);
+                    else va = mfma(st.wn[kb], shi[kb], va);
+                }
+                bf16x4 vh, vl;
+                split4(va + vb, vh, vl);
+                *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
+                const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
+#pragma unroll
+                for (int b = 0; b < 8; ++b) {
+                    S[b] = mfma(st.kt[b], vhh, S[b] * st.eg[b]);
+                    S[b] = mfma(st.kt[b], vl0, S[b]);
+                }
+            } else {
+                if (it > 0) emit(it - 1);
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    qh[kb] = *(const bf16x8 *)(slot + Rec::QH + kb * 1024 + l * 16);
+                    ql[kb] = *(const bf16x8 *)(slot + Rec::QL + kb * 1024 + l * 16);
+                }
+                pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        if (!chain && !loader) emit(nch - 1);
+    }
+    if (chain && sfin) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sfin[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+    }
+}
+
+// ---------------------------------------------------------------- key-split recurrence
+// For few (sequence, head) chains: one block of 4 waves per (sequence, head,
+// 16-column slice), wave w owning key rows [32w, 32w+32) of the slice's state
+// (exactly k-block w of the state permutation, so its two 16-row blocks are the
+// B operand of its share of W.S). Per chunk, one barrier:
+//   before it: each wave computes its partial -W_w S_w (wave 0 adds U) and
+//     publishes it in LDS; waits for its own ring loads of the next chunk;
+//   after it: every wave sums the four partials in the same order (identical
+//     V_new everywhere), issues the ring load NSLOT chunks ahead, forms its
+//     partial of Q+S (wave 0 adds P V_new), publishes it, updates its own state
+//     rows; one wave (rotating) reduces and stores the previous chunk's output.
+// Partial buffers are double-buffered by chunk parity; all record pieces a wave
+// needs are read into registers before the barrier that releases their slot.
+constexpr int DK_WAVES = 4;
+#ifndef KDA_DK_NSLOT
+#define KDA_DK_NSLOT 4   // ring depth of the key-split recurrence (chunks in flight + 1)
+#endif
+
+template <int NSLOT>
+struct DkLayout {
+    static constexpr int SLOT = Rec::BYTES + 1024;                 // record + V tile (512 B used)
+    static constexpr int REC_LOADS = Rec::BYTES / 1024;            // 23
+    static constexpr int LOADS = REC_LOADS + 1;                    // + V tile
+    static constexpr int PER_WAVE = LOADS / DK_WAVES;              // 6
+    static constexpr int XCH = NSLOT * SLOT;                       // f32x4 [2][4][64]
+    static constexpr int XO = XCH + 2 * DK_WAVES * 64 * 16;        // f32x4 [2][4][64]
+    static constexpr int BYTES = XO + 2 * DK_WAVES * 64 * 16;
+};
+
+template <int NSLOT>
+__device__ __forceinline__ void dk_fill(char *slot, const char *rec, const uint16_t *v, int64_t t0,
+                                        int nc, int h, int H, int col0) {
+    using L = DkLayout<NSLOT>;
+    static_assert(L::LOADS % DK_WAVES == 0, "unbalanced ring loads");
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+    for (int u = 0; u < L::PER_WAVE; ++u) {
+        const int i = u * DK_WAVES + w;
+        if (i < L::REC_LOADS) {
+            __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
+                                             KDA_LDS(slot + i * 1024), 16, 0, 0);
+        } else if (l < 32) {
+            // V tile [16 tokens][16 columns] bf16: lane l -> token l/2, columns 8*(l%2)..+7
+            const int row = l >> 1;
+            const int64_t t = t0 + (row < nc ? row : nc - 1);
+            __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + col0 + (l & 1) * 8),
+                                             KDA_LDS(slot + Rec::BYTES), 16, 0, 0);
+        }
+    }
+}
+
+template <int NSLOT>
+__global__ __launch_bounds__(64 * DK_WAVES) void recur_dk_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+    using L = DkLayout<NSLOT>;
+    static_assert(NSLOT >= 2, "ring needs two slots");
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    f32x4 *xch = (f32x4 *)(ring + L::XCH);
+    f32x4 *xo = (f32x4 *)(ring + L::XO);
+
+    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int tile = bid % 8;
+    const int sh = bid / 8;
+    const int h = sh % H;
+    const int n = order[sh / H];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
+    const int col0 = tile * 16, col = col0 + c;
+    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
+    const int nch = ci1 - ci0;
+
+    // this wave's state rows: blocks 2w and 2w+1 (key rows 32w + 4g + j and 32w + 16 + 4g + j)
+    f32x4 S0, S1;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (s0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            S0[j] = s0[sbase + (int64_t)(32 * w + 4 * gq + j) * D];
+            S1[j] = s0[sbase + (int64_t)(32 * w + 16 + 4 * gq + j) * D];
+        }
+    } else {
+        S0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        S1 = S0;
+    }
+
+    auto fill = [&](int it) {
+        const int k = it < nch ? it : nch - 1;
+        const int64_t t0 = bos + (int64_t)C * k;
+        dk_fill<NSLOT>(ring + (it % NSLOT) * L::SLOT, recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES,
+                       v, t0, (int)min<int64_t>(C, eos - t0), h, H, col0);
+    };
+    // reduce the four output partials of chunk it (published before the barrier of it+1)
+    auto emit = [&](int it) {
+        const f32x4 *xp = xo + (it & 1) * DK_WAVES * 64;
+        const f32x4 o = ((xp[l] + xp[64 + l]) + xp[128 + l]) + xp[192 + l];
+        const int64_t t0 = bos + (int64_t)C * it;
+        const int nc = (int)min<int64_t>(C, eos - t0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
+    };
+
+    if (nch > 0) {
+#pragma unroll
+        for (int it = 0; it < NSLOT; ++it) fill(it);
+        wait_vmcnt<(NSLOT - 1) * L::PER_WAVE>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const bf16x4 z4 = {};
+        for (int it = 0; it < nch; ++it) {
+            const char *slot = ring + (it % NSLOT) * L::SLOT;
+            // ---- record pieces of this wave (all read before the barrier)
+            const bf16x8 wn = *(const bf16x8 *)(slot + Rec::WN + w * 1024 + l * 16);
+            const bf16x8 qh = *(const bf16x8 *)(slot + Rec::QH + w * 1024 + l * 16);
+            const bf16x8 ql = *(const bf16x8 *)(slot + Rec::QL + w * 1024 + l * 16);
+            const bf16x8 kt0 = *(const bf16x8 *)(slot + Rec::KT + (2 * w) * 1024 + l * 16);
+            const bf16x8 kt1 = *(const bf16x8 *)(slot + Rec::KT + (2 * w + 1) * 1024 + l * 16);
+            const f32x4 eg0 = *(const f32x4 *)(slot + Rec::EG + (32 * w + 4 * gq) * 4);
+            const f32x4 eg1 = *(const f32x4 *)(slot + Rec::EG + (32 * w + 16 + 4 * gq) * 4);
+            bf16x8 tb = {}, vdup = {}, pp = {};
+            if (w == 0) {
+                tb = *(const bf16x8 *)(slot + Rec::TB + l * 16);
+                pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
+                const uint16_t *vt = (const uint16_t *)(slot + Rec::BYTES);
+                const bf16x4 vv = __builtin_bit_cast(
+                    bf16x4, (ushort4{vt[(4 * gq) * 16 + c], vt[(4 * gq + 1) * 16 + c],
+                                     vt[(4 * gq + 2) * 16 + c], vt[(4 * gq + 3) * 16 + c]}));
+                vdup = cat(vv, vv);
+            }
+            // ---- partial V_new: (wave 0: U) - W_w S_w
+            const bf16x8 shi = cat(to_bf16x4(S0), to_bf16x4(S1));
+            f32x4 part = w == 0 ? mfma(tb, vdup, zero) : zero;
+            part = mfma(wn, shi, part);
+            bf16x8 slo;
+            {
+                const uint2 h0 = __builtin_bit_cast(uint2, __builtin_shufflevector(shi, shi, 0, 1, 2, 3));
+                const uint2 h1 = __builtin_bit_cast(uint2, __builtin_shufflevector(shi, shi, 4, 5, 6, 7));
+                const uint32_t l0 = pack2(S0[0] - __uint_as_float(h0.x << 16), S0[1] - __uint_as_float(h0.x & 0xffff0000u));
+                const uint32_t l1 = pack2(S0[2] - __uint_as_float(h0.y << 16), S0[3] - __uint_as_float(h0.y & 0xffff0000u));
+                const uint32_t l2 = pack2(S1[0] - __uint_as_float(h1.x << 16), S1[1] - __uint_as_float(h1.x & 0xffff0000u));
+                const uint32_t l3 = pack2(S1[2] - __uint_as_float(h1.y << 16), S1[3] - __uint_as_float(h1.y & 0xffff0000u));
+                slo = __builtin_bit_cast(bf16x8, (uint4{l0, l1, l2, l3}));
+            }
+            if (KDA_SPLIT_S_WS) part = mfma(wn, slo, part);
+            xch[((it & 1) * DK_WAVES + w) * 64 + l] = part;
+            // own loads of chunk it+1 landed, own reads of this slot done (it is refilled next)
+            wait_vmcnt_lgkm0<(NSLOT - 2) * L::PER_WAVE>();
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            fill(it + NSLOT);                           // slot of chunk it is released
+            __builtin_amdgcn_sched_barrier(0);
+            // ---- V_new (same summation order in every wave)
+            const f32x4 *xp = xch + (it & 1) * DK_WAVES * 64;
+            const f32x4 vn = ((xp[l] + xp[64 + l]) + xp[128 + l]) + xp[192 + l];
+            bf16x4 vh, vl;
+            split4(vn, vh, vl);
+            const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
+            // ---- partial outputs
+            f32x4 oa = mfma(qh, shi, zero);
+            f32x4 ob = KDA_SPLIT_S_QS ? mfma(qh, slo, zero) : zero;
+            oa = mfma(ql, shi, oa);
+            if (w == 0) {
+                ob = mfma(pp, vhh, ob);
+                ob = mfma(pp, vl0, ob);
+            }
+            xo[((it & 1) * DK_WAVES + w) * 64 + l] = oa + ob;
+            if (it > 0 && w == ((it - 1) & (DK_WAVES - 1))) emit(it - 1);
+            // ---- state update of this wave's rows
+            S0 = mfma(kt0, vhh, S0 * eg0);
+            S1 = mfma(kt1, vhh, S1 * eg1);
+            S0 = mfma(kt0, vl0, S0);
+            S1 = mfma(kt1, vl0, S1);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);             // own LDS writes done
+        __builtin_amdgcn_s_barrier();
+        if (w == ((nch - 1) & (DK_WAVES - 1))) emit(nch - 1);
+    }
+    if (sfin) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sfin[sbase + (int64_t)(32 * w + 4 * gq + j) * D] = S0[j];
+            sfin[sbase + (int64_t)(32 * w + 16 + 4 * gq + j) * D] = S1[j];
+        }
+    }
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
                             int32_t *err, hipStream_t st) {
@@ -268,10 +645,55 @@ static hipError_t launch_recur_t(const char *recs, const uint16_t *v, const int3
     return hipGetLastError();
 }
 
+template <int NSLOT>
+static hipError_t launch_recur_dk(const char *recs, const uint16_t *v, const int32_t *cu,
+                                  const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                  int H, const float *s0, float *out, float *sfin, hipStream_t st) {
+    const size_t lds = (size_t)DkLayout<NSLOT>::BYTES;
+    auto kern = recur_dk_kernel<NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t blocks = (int64_t)N * H * 8;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DK_WAVES), lds, st, recs, v, cu,
+                       chunk_off, order, N, T, H, s0, out, sfin);
+    return hipGetLastError();
+}
+
+template <int NW, int NSLOT>
+static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const int32_t *cu,
+                                    const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                    int H, const float *s0, float *out, float *sfin,
+                                    hipStream_t st) {
+    constexpr int SLOT = Rec::BYTES + Ring<NW>::V_LOADS * 1024;
+    const size_t lds = (size_t)NSLOT * SLOT + 2 * NW * PairLayout<NW>::SNAP;
+    static_assert((size_t)NSLOT * SLOT + 2 * NW * PairLayout<NW>::SNAP <= 160 * 1024, "LDS");
+    auto kern = recur_pair_kernel<NW, NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(128 * NW + 64), lds, st, recs, v, cu,
+                       chunk_off, order, N, T, H, s0, out, sfin);
+    return hipGetLastError();
+}
+
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
+    case 101: return launch_recur_pair<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 102: return launch_recur_pair<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 104: return launch_recur_pair<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 4: return launch_recur_t<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
