@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -66,6 +67,19 @@ int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (chains <= 16) return 101;
     if (chains <= 256) return 102;
     return 104;
+}
+
+// Consumer waves per block of the fused kernel (1, 2 or 4; 16 value columns each).
+// KDA_FUSED_WAVES overrides the choice, for tuning.
+int fused_waves(int64_t N, int64_t H) {
+    if (const char *e = std::getenv("KDA_FUSED_WAVES")) {
+        const int w = std::atoi(e);
+        if (w == 1 || w == 2 || w == 4) return w;
+    }
+    const int64_t chains = N * H;
+    if (chains * 8 <= 512) return 1;
+    if (chains * 4 <= 1024) return 2;
+    return 4;
 }
 
 }  // namespace
@@ -179,10 +193,16 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     } else if (ok) {
         ok = kda::launch_fused((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g,
                                beta, cu_seqlens, order, N, T, H, scale, initial_state, out,
-                               final_state, err, recur_waves(N, H, "KDA_FUSED_WAVES"),
-                               st) == hipSuccess;
+                               final_state, err, fused_waves(N, H), st) == hipSuccess;
     }
-    if (!ok || !mark(true)) rc = KDA_ERR_LAUNCH;
+    if (!ok || !mark(true)) {
+        rc = KDA_ERR_LAUNCH;
+        if (std::getenv("KDA_DEBUG")) {
+            const hipError_t e = hipGetLastError();
+            std::fprintf(stderr, "kda_fwd: launch failed (variant %d): %s\n", chosen,
+                         hipGetErrorString(e));
+        }
+    }
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;
 }

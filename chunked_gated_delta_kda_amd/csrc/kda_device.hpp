@@ -129,13 +129,16 @@ struct Rec {
 // LDS scratch of one chunk prep (one wave).
 struct alignas(16) PrepLds {
     static constexpr int ROW = 136;    // bf16 per padded token row (128 + 8: spreads banks)
+    static constexpr int CROW = 20;    // bf16 per channel row of a transposed tile (16 + 4):
+                                       // 40-byte rows keep 8-byte accesses conflict-light
     __bf16 kp[16 * ROW];               // K+ (single bf16)
     __bf16 kmh[16 * ROW];              // K- hi
     __bf16 kml[16 * ROW];              // K- lo
     __bf16 qph[16 * ROW];              // Q+ hi
     __bf16 qpl[16 * ROW];              // Q+ lo
-    __bf16 kpt[D * 16];                // K+ transposed: [channel][token]
-    float ktt[D * 16];                 // K~ transposed (fp32; split when stored)
+    __bf16 kpt[D * CROW];              // K+ transposed: [channel][token]
+    __bf16 kth[D * CROW];              // K~ hi, transposed
+    __bf16 ktl[D * CROW];              // K~ lo, transposed
 };
 
 // 16x16 product N.M, given N^T and M in D layout, split-bf16 on both sides
@@ -187,6 +190,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     const int r = l & 15, gq = l >> 4;
 
     // ---- phase 0: gates and scaled operands, lane = channel pair, loop over tokens
+    // G is kept in base-2 units (log2 e folded into the running sum)
     float G0[C], G1[C];
     uint32_t qv[C], kv[C];
     float acc0 = 0.f, acc1 = 0.f;
@@ -200,25 +204,28 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
             qq = *(const uint32_t *)(q + row * D + c0);
             kk = *(const uint32_t *)(k + row * D + c0);
         }
-        acc0 += fmaxf(gt.x, LOWER_BOUND);
-        acc1 += fmaxf(gt.y, LOWER_BOUND);
+        acc0 = __builtin_fmaf(fmaxf(gt.x, LOWER_BOUND), LOG2E, acc0);
+        acc1 = __builtin_fmaf(fmaxf(gt.y, LOWER_BOUND), LOG2E, acc1);
         G0[t] = acc0;
         G1[t] = acc1;
         qv[t] = qq;
         kv[t] = kk;
     }
     // padded rows carry g = 0, so acc is G at the last real token
-    const float eC0 = exp_e(acc0), eC1 = exp_e(acc1);
+    const float eC0 = __builtin_amdgcn_exp2f(acc0), eC1 = __builtin_amdgcn_exp2f(acc1);
     *(f32x2 *)(rec + Rec::EG + c0 * 4) = f32x2{eC0, eC1};
 
+    // per-channel token rows of K+ and K~ (hi, lo), packed two tokens per dword,
+    // written to the transposed tiles with wide stores after the loop
+    uint32_t kpT[2][8], khT[2][8], klT[2][8];
 #pragma unroll
     for (int t = 0; t < C; t += 2) {
-        float kpT[2][2], ktT[2][2];   // [token pair][channel]
+        float kpv[2][2], ktv[2][2];   // [token of pair][channel]
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int tt = t + u;
-            const float ep0 = exp_e(G0[tt]), ep1 = exp_e(G1[tt]);
-            const float en0 = exp_e(-G0[tt]), en1 = exp_e(-G1[tt]);
+            const float ep0 = __builtin_amdgcn_exp2f(G0[tt]), ep1 = __builtin_amdgcn_exp2f(G1[tt]);
+            const float en0 = __builtin_amdgcn_exp2f(-G0[tt]), en1 = __builtin_amdgcn_exp2f(-G1[tt]);
             const float k0 = bf_lo(kv[tt]), k1 = bf_hi(kv[tt]);
             const float q0 = bf_lo(qv[tt]), q1 = bf_hi(qv[tt]);
             const f32x2 kp = {k0 * ep0, k1 * ep1};
@@ -232,15 +239,28 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
             split2(qp, hi, lo);
             *(bf16x2 *)&L.qph[tt * PrepLds::ROW + c0] = hi;
             *(bf16x2 *)&L.qpl[tt * PrepLds::ROW + c0] = lo;
-            kpT[u][0] = kp.x;
-            kpT[u][1] = kp.y;
-            ktT[u][0] = km.x * eC0;      // K~ = K e^{G_C - G}
-            ktT[u][1] = km.y * eC1;
+            kpv[u][0] = kp.x;
+            kpv[u][1] = kp.y;
+            ktv[u][0] = km.x * eC0;      // K~ = K e^{G_C - G}
+            ktv[u][1] = km.y * eC1;
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
-            *(uint32_t *)&L.kpt[(c0 + ch) * 16 + t] = pack2(kpT[0][ch], kpT[1][ch]);
-            *(f32x2 *)&L.ktt[(c0 + ch) * 16 + t] = f32x2{ktT[0][ch], ktT[1][ch]};
+            kpT[ch][t / 2] = pack2(kpv[0][ch], kpv[1][ch]);
+            bf16x2 hi, lo;
+            split2(f32x2{ktv[0][ch], ktv[1][ch]}, hi, lo);
+            khT[ch][t / 2] = __builtin_bit_cast(uint32_t, hi);
+            klT[ch][t / 2] = __builtin_bit_cast(uint32_t, lo);
+        }
+    }
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const int o = (c0 + ch) * PrepLds::CROW;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            *(uint2 *)&L.kpt[o + 4 * e] = uint2{kpT[ch][2 * e], kpT[ch][2 * e + 1]};
+            *(uint2 *)&L.kth[o + 4 * e] = uint2{khT[ch][2 * e], khT[ch][2 * e + 1]};
+            *(uint2 *)&L.ktl[o + 4 * e] = uint2{klT[ch][2 * e], klT[ch][2 * e + 1]};
         }
     }
     // beta of token r (this lane's column) and of tokens 4g+j (this lane's rows)
@@ -303,7 +323,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     f32x4 Wt[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        const bf16x4 a = *(const bf16x4 *)&L.kpt[(16 * b + r) * 16 + 4 * gq];
+        const bf16x4 a = *(const bf16x4 *)&L.kpt[(16 * b + r) * PrepLds::CROW + 4 * gq];
         Wt[b] = mfma(cat(a, a), tb, f32x4{0.f, 0.f, 0.f, 0.f});   // W[r][16b+4g+j]
     }
 #pragma unroll
@@ -319,9 +339,9 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        bf16x4 hi, lo;
-        split4(*(const f32x4 *)&L.ktt[(16 * b + r) * 16 + 4 * gq], hi, lo);
-        *(bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16) = cat(hi, lo);
+        const int o = (16 * b + r) * PrepLds::CROW + 4 * gq;
+        *(bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16) =
+            cat(*(const bf16x4 *)&L.kth[o], *(const bf16x4 *)&L.ktl[o]);
     }
 }
 

@@ -177,9 +177,9 @@ static hipError_t launch_fused_t(const uint16_t *q, const uint16_t *k, const uin
     auto kern = fused_kernel<NW, NP, NSLOT>;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                LY::BYTES) != hipSuccess)
-            return hipErrorInvalidValue;
+        const hipError_t e = hipFuncSetAttribute(
+            (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
+        if (e != hipSuccess) return e;
         attr_set = true;
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
