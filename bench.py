@@ -9,8 +9,13 @@ inputs already resident in device memory. W untimed steps, then exactly K
 timed steps bracketed by device synchronisation. Prints one JSON line.
 
 Per-kernel durations come from HIP events that the library records on its
-own stream between its kernels (kda_options.stage_events), over the same
-timed steps. The CPU baseline is the fp64 oracle on the host cores, timed in
+stream before its first kernel launch and after each launch
+(kda_options.stage_events), in every EVENT_EVERY-th of the timed steps (each
+record costs about a microsecond of device time); kda_launch_plan names the
+launches. When the recurrence leaves CUs idle, the split variant cuts the chunk
+range into segments and prepares segment s+1 inside the launch that runs the
+recurrence of segment s: then a kernel kind has several launches per step, and
+its time is their sum. The CPU baseline is the fp64 oracle on the host cores, timed in
 the same run on the same inputs; it also provides the parity check printed
 with the result.
 """
@@ -37,7 +42,8 @@ STATE_BYTES = 128 * 128 * 4       # one (sequence, head) state, fp32
 # algorithmic bytes per token-head that each kernel must move (inputs it reads,
 # outputs it writes); together they are q,k,v bf16 + g fp32 + beta fp32 + o fp32 = 1796 B
 KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796}
-KERNELS = {"split": ["chunk_map", "prep", "recur"], "fused": ["chunk_map", "fused"]}
+EVENT_EVERY = 4                   # timed steps per step that records kernel events
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -50,7 +56,7 @@ class HipEvents:
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so.7")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -60,9 +66,11 @@ class HipEvents:
         arr = (ctypes.c_void_p * n)()
         for i in range(n):
             e = ctypes.c_void_p()
-            rc = self.hip.hipEventCreate(ctypes.byref(e))
+            # timing-only events: no system-scope fence (cache writeback) at each record;
+            # they are read after a full device synchronisation
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), HIP_EVENT_DISABLE_SYSTEM_FENCE)
             if rc != 0:
-                raise RuntimeError(f"hipEventCreate failed ({rc})")
+                raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
             arr[i] = e.value
             self.made.append(e.value)
         return arr
@@ -129,15 +137,20 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
     w_scale = true_bytes / max(write[copy[0]])
     out = {"workload": workload, "command": command, "fetch_scale": f_scale, "write_scale": w_scale,
            "calibration_bytes": true_bytes, "kernels": {}}
+    kinds = collections.defaultdict(lambda: ([], []))
     for name in fetch:
-        m = re.search(r"kda::(\w+?)_kernel", name)
+        m = re.search(r"kda::(chunk_map|prep|recur|fused)\w*_kernel", name)
         if not m or name not in write:
             continue
-        fb = float(np.median(fetch[name])) * f_scale
-        wb = float(np.median(write[name])) * w_scale
-        out["kernels"][m.group(1)] = {"workload": workload, "source_hash": kernel_source_hash(),
-                                      "fetch_bytes": fb, "write_bytes": wb,
-                                      "bytes_per_launch": fb + wb}
+        kinds[m.group(1)][0].extend(fetch[name])
+        kinds[m.group(1)][1].extend(write[name])
+    for kind, (fl, wl) in kinds.items():
+        # mean over dispatches: segment launches of one kind cover different chunk ranges
+        fb = float(np.mean(fl)) * f_scale
+        wb = float(np.mean(wl)) * w_scale
+        out["kernels"][kind] = {"workload": workload, "source_hash": kernel_source_hash(),
+                                "fetch_bytes": fb, "write_bytes": wb, "dispatches": len(fl),
+                                "bytes_per_launch": fb + wb}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     prev = {}
     if os.path.exists(TRAFFIC_FILE):
@@ -205,10 +218,13 @@ def main():
     nws = kda.workspace_bytes(N, T, H, variant)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
-    names = KERNELS[variant]
+    from chunked_gated_delta_kda_amd import native
+    launch_info = native.launch_plan(N, T, H, variant)
+    plan = [p[0] for p in launch_info]
+    names = list(dict.fromkeys(plan))            # kinds, first-launch order
     ev = HipEvents()
-    n_ev = len(names) + 1
-    step_events = [ev.array(n_ev) for _ in range(args.steps)]
+    n_ev = len(plan) + 1
+    step_events = [ev.array(n_ev) if i % EVENT_EVERY == 0 else None for i in range(args.steps)]
 
     def step(events=None):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["cu_seqlens"],
@@ -225,8 +241,11 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = {nm: float(np.mean([ev.ms(e[j], e[j + 1]) for e in step_events]))
-               for j, nm in enumerate(names)}
+    kern_ms = {nm: 0.0 for nm in names}
+    sampled = [e for e in step_events if e is not None]
+    for j, nm in enumerate(plan):
+        kern_ms[nm] += float(np.mean([ev.ms(e[j], e[j + 1]) for e in sampled]))
+    launches = {nm: plan.count(nm) for nm in names}
     ev.close()
     if args.copy_calibration:
         nbytes = args.copy_calibration << 20
@@ -236,7 +255,8 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: 3 x {nbytes} bytes read + written")
-    log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms): {kern_ms}")
+    log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms summed over launches): {kern_ms}; "
+        f"launches {launches}")
 
     TH = T * H
     states = N * H * STATE_BYTES * ((1 if w.initial_state is not None else 0) + 1)
@@ -245,21 +265,44 @@ def main():
     step_s = ms_per_step / 1e3
     tokens_per_s = T / step_s
 
-    def kernel_alg_bytes(nm):
-        if nm == "chunk_map":
-            return 4 * (N + 1)
-        b = TH * KERNEL_BYTES_PER_TOKEN_HEAD[nm]
-        if nm in ("recur", "fused"):
+    # token counts per global chunk range, from the sequence lengths
+    chunk_tokens = np.concatenate([np.minimum(16, L - 16 * np.arange((L + 15) // 16))
+                                   for L in w.lengths] + [np.zeros(0, np.int64)]).astype(np.int64)
+    csum = np.concatenate([[0], np.cumsum(chunk_tokens)])
+    n_ch = len(chunk_tokens)
+
+    def tokens_in(r):
+        a, b = min(r[0], n_ch), min(r[1], n_ch)
+        return int(csum[b] - csum[a]) if b > a else 0
+
+    def launch_alg_bytes(kind, prep_r, recur_r):
+        """Bytes the algorithm must move in one launch: inputs read and outputs written
+        for the token-heads it prepares and runs; the batch's initial and final states
+        are counted once per step, with the last recurrence launch."""
+        if kind == "chunk_map":
+            return 4 * (N + 1) + 8 * N
+        if kind == "fused":
+            return TH * KERNEL_BYTES_PER_TOKEN_HEAD["fused"] + states
+        b = (tokens_in(prep_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["prep"]
+             + tokens_in(recur_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["recur"])
+        if recur_r[1] >= n_ch and recur_r[1] > recur_r[0]:
             b += states
         return b
 
+    kind_bytes = {nm: 0 for nm in names}
+    for kind, pr, rr in launch_info:
+        kind_bytes[kind] += launch_alg_bytes(kind, pr, rr)
+
     dom = max((nm for nm in names if nm != "chunk_map"), key=lambda nm: kern_ms[nm])
     dom_s = kern_ms[dom] / 1e3
-    achieved = kernel_alg_bytes(dom) / dom_s / 1e9
+    achieved = kind_bytes[dom] / dom_s / 1e9
     workload = f"config{args.config}"
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dom, workload)}
+                "traffic": measured_traffic(dom, workload),
+                "alg_bytes_per_launch": int(kind_bytes[dom] / launches[dom]),
+                "launches_per_step": launches[dom],
+                "avg_launch_ms": round(kern_ms[dom] / launches[dom], 5)}
 
     res = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -272,6 +315,7 @@ def main():
            "mfma_bf16_peak_frac": round(alg_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "path_hbm_frac": round(alg_bytes_total / step_s / 1e9 / HBM_PEAK_GBS, 4),
            "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+           "kernel_launches": launches,
            "roofline": roofline, "cpu_baseline": None}
 
     if not args.no_cpu_baseline:

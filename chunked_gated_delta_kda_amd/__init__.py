@@ -82,7 +82,7 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     opt = native.KdaOptions(var, 0, ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0, None)
+                            workspace.numel() if workspace is not None else 0, None, 0)
     if stage_events is not None:   # profiling: a ctypes array of hipEvent_t handles
         opt.n_stage_events = len(stage_events)
         opt.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))

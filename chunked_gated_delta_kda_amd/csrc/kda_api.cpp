@@ -14,26 +14,32 @@
 namespace {
 
 constexpr size_t ALIGN = 256;
+constexpr int KDA_MAX_SEGMENTS = 8;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 int64_t max_chunks(int64_t N, int64_t T) { return (T + KDA_CHUNK - 1) / KDA_CHUNK + N; }
 
 // Workspace: chunk offsets [N+1], sequence order [N], an error word, and (split
-// variant only) one chunk record per (chunk, head).
+// variant only) a state carry buffer [N, H, 128, 128] fp32 when the chunk range is
+// cut into segments, followed by one chunk record per (chunk, head).
 struct Layout {
-    size_t chunk_off, order, err, recs, total;
+    size_t chunk_off, order, err, carry, recs, total;
 };
 
-Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant) {
+Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments) {
     Layout L;
     L.chunk_off = 0;
     L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
     L.err = L.order + align_up(sizeof(int32_t) * (size_t)N);
-    L.recs = L.err + ALIGN;
+    L.carry = L.err + ALIGN;
+    L.recs = L.carry;
     L.total = L.recs;
-    if (variant == KDA_VARIANT_SPLIT)
-        L.total += (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
+    if (variant == KDA_VARIANT_SPLIT) {
+        if (segments > 1)
+            L.recs = L.carry + (size_t)N * H * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+        L.total = L.recs + (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
+    }
     return L;
 }
 
@@ -67,6 +73,21 @@ int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (chains <= 16) return 101;
     if (chains <= 256) return 102;
     return 104;
+}
+
+// Number of chunk-range segments of the split variant. With S > 1 the launches are
+// prep(segment 0), then recurrence(s) fused with prep(s+1) for s < S-1, then
+// recurrence(S-1): the prep of later segments runs on the CUs the recurrence leaves
+// idle, which pays when the recurrence has fewer blocks than the chip has CUs. 1 for
+// the non-paired recurrence forms. KDA_SEGMENTS (1..KDA_MAX_SEGMENTS) overrides.
+int split_segments(int64_t N, int64_t H, int waves) {
+    if (waves < 100) return 1;
+    if (const char *e = std::getenv("KDA_SEGMENTS")) {
+        const int s = std::atoi(e);
+        if (s >= 1 && s <= KDA_MAX_SEGMENTS) return s;
+    }
+    const int64_t blocks = N * H * (8 / (waves - 100));
+    return blocks < 256 ? 4 : 1;
 }
 
 // Consumer waves per block of the fused kernel (1, 2 or 4; 16 value columns each).
@@ -113,13 +134,40 @@ int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads
     return KDA_VARIANT_SPLIT;
 }
 
+int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                        int32_t variant, kda_launch_info *info, int32_t max_launches) {
+    if (!shape_ok(num_seqs, total_tokens, num_heads)) return 0;
+    const int v = variant == KDA_VARIANT_AUTO
+                      ? kda_select_variant(num_seqs, total_tokens, num_heads)
+                      : variant;
+    const int32_t M = (int32_t)max_chunks(num_seqs, total_tokens);
+    kda_launch_info plan[2 + KDA_MAX_SEGMENTS];
+    int n = 0;
+    plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0};
+    if (v == KDA_VARIANT_SPLIT) {
+        const int segs = split_segments(num_seqs, num_heads, recur_waves(num_seqs, num_heads));
+        auto bound = [&](int sg) { return (int32_t)((int64_t)M * sg / segs); };
+        plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0};
+        for (int sg = 0; sg + 1 < segs; ++sg)
+            plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1)};
+        plan[n++] = {KDA_KERNEL_RECUR, 0, 0, bound(segs - 1), M};
+    } else {
+        plan[n++] = {KDA_KERNEL_FUSED, 0, M, 0, M};
+    }
+    for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
+    return n;
+}
+
 size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                            int32_t variant) {
     if (!shape_ok(num_seqs, total_tokens, num_heads)) return 0;
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    return ws_layout(num_seqs, total_tokens, num_heads, v).total;
+    const int segs = v == KDA_VARIANT_SPLIT
+                         ? split_segments(num_seqs, num_heads, recur_waves(num_seqs, num_heads))
+                         : 1;
+    return ws_layout(num_seqs, total_tokens, num_heads, v, segs).total;
 }
 
 int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -130,6 +178,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int n_ev = opt ? opt->n_stage_events : 0;
     if (n_ev != 0 && (n_ev < 2 || n_ev > KDA_MAX_STAGE_EVENTS || !opt->stage_events))
         return KDA_ERR_UNSUPPORTED;
+    if (opt && opt->reserved != 0) return KDA_ERR_UNSUPPORTED;
     const int variant = opt ? opt->variant : KDA_VARIANT_AUTO;
     if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED)
         return KDA_ERR_UNSUPPORTED;
@@ -149,7 +198,9 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                            : variant;
     hipStream_t st = (hipStream_t)stream;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    const Layout lay = ws_layout(N, T, H, chosen);
+    const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, H) : fused_waves(N, H);
+    const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, H, waves) : 1;
+    const Layout lay = ws_layout(N, T, H, chosen, segs);
 
     char *ws = nullptr;
     bool owned = false;
@@ -168,34 +219,42 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     int32_t *err = (int32_t *)(ws + lay.err);
     char *recs = ws + lay.recs;
 
-    // stage events (profiling only): slot i after kernel i, trailing slots after the last
+    // profiling events: [0] before the first kernel launch, [i] after the i-th (all on
+    // the caller's stream, where every kernel runs in order)
     void **ev = n_ev ? opt->stage_events : nullptr;
-    int ev_next = 0;
-    auto mark = [&](bool last) -> bool {
-        if (!ev) return true;
-        do {
-            if (ev_next < n_ev && hipEventRecord((hipEvent_t)ev[ev_next++], st) != hipSuccess)
-                return false;
-        } while (last && ev_next < n_ev);
+    int kidx = 0;
+    auto around = [&](hipStream_t s, auto &&launch) -> bool {
+        if (ev && kidx == 0 && hipEventRecord((hipEvent_t)ev[0], s) != hipSuccess) return false;
+        if (launch() != hipSuccess) return false;
+        ++kidx;
+        if (ev && kidx < n_ev && hipEventRecord((hipEvent_t)ev[kidx], s) != hipSuccess) return false;
         return true;
     };
 
-    int rc = KDA_OK;
-    bool ok = mark(false) &&
-              kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, st) == hipSuccess &&
-              mark(false);
+    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
+    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
-        ok = kda::launch_prep((const uint16_t *)q, (const uint16_t *)k, g, beta, cu_seqlens, N, T,
-                              H, scale, chunk_off, recs, max_chunks(N, T), st) == hipSuccess &&
-             mark(false) &&
-             kda::launch_recur(recs, (const uint16_t *)v, cu_seqlens, chunk_off, order, N, T, H,
-                               initial_state, out, final_state, recur_waves(N, H), st) == hipSuccess;
+        const int64_t M = max_chunks(N, T);
+        if (segs == 1) {
+            ok = around(st, [&] { return kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, 0, M, st); }) &&
+                 around(st, [&] { return kda::launch_recur(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st); });
+        } else {
+            kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cu_seqlens, chunk_off, order,
+                                 N, T, H, initial_state, out, final_state,
+                                 final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0};
+            auto bound = [&](int sg) { return M * sg / segs; };
+            ok = around(st, [&] { return kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, 0, bound(1), st); });
+            for (int sg = 0; ok && sg + 1 < segs; ++sg) {
+                a.cbeg = bound(sg), a.cend = bound(sg + 1), a.pbeg = bound(sg + 1), a.pend = bound(sg + 2);
+                ok = around(st, [&] { return kda::launch_recur_prep(a, waves, st); });
+            }
+            ok = ok && around(st, [&] { return kda::launch_recur_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, a.carry, waves, (int)bound(segs - 1), (int)M, st); });
+        }
     } else if (ok) {
-        ok = kda::launch_fused((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g,
-                               beta, cu_seqlens, order, N, T, H, scale, initial_state, out,
-                               final_state, err, fused_waves(N, H), st) == hipSuccess;
+        ok = around(st, [&] { return kda::launch_fused(q16, k16, v16, g, beta, cu_seqlens, order, N, T, H, scale, initial_state, out, final_state, err, waves, st); });
     }
-    if (!ok || !mark(true)) {
+    int rc = KDA_OK;
+    if (!ok) {
         rc = KDA_ERR_LAUNCH;
         if (std::getenv("KDA_DEBUG")) {
             const hipError_t e = hipGetLastError();

@@ -13,7 +13,29 @@ hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off,
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
-                       const int32_t *chunk_off, char *recs, int64_t max_chunks, hipStream_t st);
+                       const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                       hipStream_t st);
+
+// paired recurrence over the global chunk range [cbeg, cend); waves in {101, 102, 104}
+hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
+                              const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
+                              const float *s0, float *out, float *sfin, float *carry, int waves,
+                              int cbeg, int cend, hipStream_t st);
+
+// One launch: paired recurrence over chunks [cbeg, cend) plus the records of
+// chunks [pbeg, pend) (the next range), prepared on the CUs the recurrence leaves idle.
+struct RecurPrepArgs {
+    char *recs;
+    const uint16_t *q, *k, *v;
+    const float *g, *beta;
+    float scale;
+    const int32_t *cu, *chunk_off, *order;
+    int N, T, H;
+    const float *s0;
+    float *out, *sfin, *carry;
+    int64_t cbeg, cend, pbeg, pend;
+};
+hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,

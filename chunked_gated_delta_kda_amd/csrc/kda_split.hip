@@ -72,17 +72,12 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
 // ---------------------------------------------------------------- prep
 // One wave per (chunk, head). Grid: max_chunks * H blocks of 64 threads; blocks
 // past the real chunk count exit.
-__global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q,
-                                                  const uint16_t *__restrict__ k,
-                                                  const float *__restrict__ g,
-                                                  const float *__restrict__ beta,
-                                                  const int32_t *__restrict__ cu, int N, int T,
-                                                  int H, float scale,
-                                                  const int32_t *__restrict__ chunk_off,
-                                                  char *__restrict__ recs) {
-    __shared__ PrepLds L;
-    const int ci = blockIdx.x / H, h = blockIdx.x % H;
-    if (ci >= chunk_off[N]) return;
+// Record of chunk ci (global index), head h.
+__device__ __forceinline__ void prep_one(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                         const float *__restrict__ g, const float *__restrict__ beta,
+                                         const int32_t *__restrict__ cu, int N, int T, int H,
+                                         float scale, const int32_t *__restrict__ chunk_off,
+                                         char *__restrict__ recs, int ci, int h, PrepLds &L) {
     // sequence owning chunk ci: largest n with chunk_off[n] <= ci
     int lo = 0, hi = N - 1;
     while (lo < hi) {
@@ -94,6 +89,20 @@ __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q
     const int64_t t0 = bos + (int64_t)C * (ci - chunk_off[n]);
     const int nc = (int)min<int64_t>(C, eos - t0);
     prep_chunk(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * Rec::BYTES);
+}
+
+__global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q,
+                                                  const uint16_t *__restrict__ k,
+                                                  const float *__restrict__ g,
+                                                  const float *__restrict__ beta,
+                                                  const int32_t *__restrict__ cu, int N, int T,
+                                                  int H, float scale,
+                                                  const int32_t *__restrict__ chunk_off,
+                                                  char *__restrict__ recs, int cbeg) {
+    __shared__ PrepLds L;
+    const int ci = cbeg + (int)(blockIdx.x / H), h = blockIdx.x % H;
+    if (ci >= chunk_off[N]) return;
+    prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
 }
 
 // ---------------------------------------------------------------- recurrence
@@ -253,20 +262,25 @@ struct PairLayout {
     static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
 };
 
+// A launch covers the global chunk range [cbeg, cend) (launches over consecutive
+// ranges, in order on one stream, cover a batch). A sequence's state enters from
+// initial_state (or zeros) at its first chunk and from `carry` otherwise, and
+// leaves to final_state after its last chunk and to `carry` otherwise (carry may
+// be final_state itself). Sequences without chunks copy initial to final state
+// in the launch that starts at chunk 0.
 template <int NW, int NSLOT>
-__global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
-    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+__device__ __forceinline__ void recur_pair_block(
+    int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+    const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
+    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
     using R = Ring<NW>;         // record loads and the V tile of NW slices
     constexpr int LOADS = R::REC_LOADS + R::V_LOADS;
     constexpr int SLOT = Rec::BYTES + R::V_LOADS * 1024;
     static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
-    extern __shared__ __attribute__((aligned(16))) char ring[];
     char *snaps = ring + NSLOT * SLOT;
 
     constexpr int PARTS = D / (16 * NW);
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int part = bid % PARTS;
     const int sh = bid / PARTS;
     const int h = sh % H;
@@ -277,10 +291,27 @@ __global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
     const int slice = chain ? w : (loader ? 0 : w - NW);
     const int vcol0 = part * R::VCOLS;
     const int col = vcol0 + slice * 16 + c;
-    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
-    const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
-    const int nch = ci1 - ci0;
+    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
+    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;      // this launch's chunks of the sequence
+    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (ci0 >= ci1) {
+        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
+                    sfin[o] = s0 ? s0[o] : 0.f;
+                }
+        }
+        return;
+    }
+    const int nch = ci1 - ci0;
+    const int64_t bos = seq_bos + (int64_t)C * (ci0 - seq_c0);   // first token of this launch's part
+    const float *sin = ci0 == seq_c0 ? s0 : carry;
+    float *sout = ci1 == seq_c1 ? sfin : carry;
 
     // ring fill, issued by the loader wave alone (the vector-memory pipe is busy for
     // most of a chunk's worth of time; no compute wave waits on it)
@@ -311,11 +342,11 @@ __global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
     const bf16x4 z4 = {};
     f32x4 S[8];
     if (chain) {
-        if (s0) {
+        if (sin) {
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) S[b][j] = s0[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
         } else {
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = zero;
@@ -358,7 +389,7 @@ __global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
             if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
     };
 
-    if (nch > 0) {
+    {
         if (loader) {
 #pragma unroll
             for (int it = 0; it < NSLOT - 1; ++it) fill(it);
@@ -411,12 +442,62 @@ __global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
         __builtin_amdgcn_s_barrier();
         if (!chain && !loader) emit(nch - 1);
     }
-    if (chain && sfin) {
+    if (chain && sout) {
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sfin[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+            for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
     }
+}
+
+template <int NW, int NSLOT>
+struct PairLds {
+    static constexpr int BYTES = NSLOT * (Rec::BYTES + Ring<NW>::V_LOADS * 1024) + 2 * NW * PairLayout<NW>::SNAP;
+};
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x), ring, recs, v, cu, chunk_off,
+                                order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+}
+
+// ---------------------------------------------------------------- recurrence + next prep
+// One launch that runs the paired recurrence over the chunk range [cbeg, cend) in
+// blocks [0, RB) and prepares the records of the next range [pbeg, pend) in the
+// remaining blocks, PREP_WAVES chunk-heads per block (one per wave). Workgroups
+// are dispatched in index order and the LDS request admits one block per CU, so
+// the recurrence blocks take their CUs first and the prep blocks fill the CUs
+// the recurrence leaves idle, instead of waiting for the recurrence to finish.
+template <int NW>
+struct RecurPrep {
+    static constexpr int PREP_WAVES = 2 * NW + 1 < 4 ? 2 * NW + 1 : 4;
+};
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(128 * NW + 64) void recur_prep_kernel(
+    const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    if ((int)blockIdx.x < RB) {
+        recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off,
+                                    order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+        return;
+    }
+    constexpr int PW = RecurPrep<NW>::PREP_WAVES;
+    const int w = threadIdx.x >> 6;
+    if (w >= PW) return;
+    const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
+    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
+    if (ci >= pend || ci >= chunk_off[N]) return;
+    prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
+             *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
 
 // ---------------------------------------------------------------- key-split recurrence
@@ -618,11 +699,12 @@ hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off,
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
-                       const int32_t *chunk_off, char *recs, int64_t max_chunks, hipStream_t st) {
-    const int64_t blocks = max_chunks * H;
+                       const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                       hipStream_t st) {
+    const int64_t blocks = (cend - cbeg) * H;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N,
-                       T, H, scale, chunk_off, recs);
+                       T, H, scale, chunk_off, recs, (int)cbeg);
     return hipGetLastError();
 }
 
@@ -667,32 +749,79 @@ static hipError_t launch_recur_dk(const char *recs, const uint16_t *v, const int
 template <int NW, int NSLOT>
 static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const int32_t *cu,
                                     const int32_t *chunk_off, const int32_t *order, int N, int T,
-                                    int H, const float *s0, float *out, float *sfin,
-                                    hipStream_t st) {
-    constexpr int SLOT = Rec::BYTES + Ring<NW>::V_LOADS * 1024;
-    const size_t lds = (size_t)NSLOT * SLOT + 2 * NW * PairLayout<NW>::SNAP;
-    static_assert((size_t)NSLOT * SLOT + 2 * NW * PairLayout<NW>::SNAP <= 160 * 1024, "LDS");
+                                    int H, const float *s0, float *out, float *sfin, float *carry,
+                                    int cbeg, int cend, hipStream_t st) {
+    constexpr int lds = PairLds<NW, NSLOT>::BYTES;
+    static_assert(lds <= 160 * 1024, "LDS");
     auto kern = recur_pair_kernel<NW, NSLOT>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
+                                lds) != hipSuccess)
             return hipErrorInvalidValue;
         attr_set = true;
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(128 * NW + 64), lds, st, recs, v, cu,
-                       chunk_off, order, N, T, H, s0, out, sfin);
+                       chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
     return hipGetLastError();
+}
+
+template <int NW, int NSLOT>
+static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
+    constexpr int PW = RecurPrep<NW>::PREP_WAVES;
+    constexpr int pair = PairLds<NW, NSLOT>::BYTES;
+    constexpr int prep = PW * (int)sizeof(PrepLds);
+    constexpr int lds = pair > prep ? pair : prep;
+    // more than 80 KiB: never two blocks on one CU (the prep blocks must not share
+    // a CU with a recurrence block)
+    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
+    auto kern = recur_prep_kernel<NW, NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
+    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
+    if (pb < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(128 * NW + 64), lds, st, a.recs, a.v,
+                       a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry,
+                       (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale, a.recs,
+                       (int)a.pbeg, (int)a.pend);
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
+    switch (waves) {
+    case 101: return launch_recur_prep_t<1, 4>(a, st);
+    case 102: return launch_recur_prep_t<2, 4>(a, st);
+    case 104: return launch_recur_prep_t<4, 3>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
+                              const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
+                              const float *s0, float *out, float *sfin, float *carry, int waves,
+                              int cbeg, int cend, hipStream_t st) {
+    switch (waves) {
+    case 101: return launch_recur_pair<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 102: return launch_recur_pair<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 104: return launch_recur_pair<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: return launch_recur_pair<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 102: return launch_recur_pair<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 104: return launch_recur_pair<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 101: case 102: case 104:
+        return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
+                                  waves, 0, 1 << 30, st);
     case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);

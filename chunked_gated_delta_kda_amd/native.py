@@ -17,13 +17,19 @@ VARIANTS = {"auto": 0, "split": 1, "fused": 2}
 
 #: every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
-           "kda_status_string", "kda_version")
+           "kda_launch_plan", "kda_status_string", "kda_version")
+KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep"}
 
 
 class KdaOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("n_stage_events", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p))]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("reserved", ctypes.c_int32)]
+
+
+class KdaLaunchInfo(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("prep_begin", ctypes.c_int32), ("prep_end", ctypes.c_int32),
+                ("recur_begin", ctypes.c_int32), ("recur_end", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -59,6 +65,8 @@ def load_library(path=LIB_PATH):
     lib.kda_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_select_variant.argtypes = [i32, i32, i32]
     lib.kda_select_variant.restype = ctypes.c_int
+    lib.kda_launch_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(KdaLaunchInfo), i32]
+    lib.kda_launch_plan.restype = ctypes.c_int32
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -81,3 +89,13 @@ def error_word_offset(num_seqs):
     a call means a fused-kernel wait gave up and the outputs are not valid)."""
     a = lambda x: (x + 255) // 256 * 256
     return a(4 * (num_seqs + 1)) + a(4 * num_seqs)
+
+
+def launch_plan(num_seqs, total_tokens, num_heads, variant="auto"):
+    """Kernel launches one kda_fwd_ex call makes for this shape, in order: a list of
+    (kind name, (prep_begin, prep_end), (recur_begin, recur_end)) in chunk indices."""
+    lib = load_library()
+    info = (KdaLaunchInfo * 64)()
+    n = lib.kda_launch_plan(num_seqs, total_tokens, num_heads, VARIANTS[variant], info, 64)
+    return [(KERNEL_KINDS[x.kind], (x.prep_begin, x.prep_end), (x.recur_begin, x.recur_end))
+            for x in info[:n]]

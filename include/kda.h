@@ -52,18 +52,27 @@ typedef enum kda_variant {
     KDA_VARIANT_FUSED = 2  /* one kernel: prep produced on chip, feeding the recurrence */
 } kda_variant;
 
-#define KDA_MAX_STAGE_EVENTS 8
+#define KDA_MAX_STAGE_EVENTS 64
+
+/* Kernel kinds reported by kda_launch_plan (profiling). */
+#define KDA_KERNEL_CHUNK_MAP 0
+#define KDA_KERNEL_PREP 1
+#define KDA_KERNEL_RECUR 2
+#define KDA_KERNEL_FUSED 3
+#define KDA_KERNEL_RECUR_PREP 4   /* recurrence over one chunk range + prep of the next */
 
 typedef struct kda_options {
     int32_t variant;        /* kda_variant                                              */
     int32_t n_stage_events; /* 0, or the length of stage_events (2..KDA_MAX_STAGE_EVENTS) */
-    void *workspace;        /* device scratch for the split variant, or NULL: then the  */
-                            /* library allocates it stream-ordered on `stream`          */
+    void *workspace;        /* device scratch, or NULL: then the library allocates it   */
+                            /* stream-ordered on `stream`                               */
     size_t workspace_bytes; /* size of `workspace`; see kda_workspace_bytes()           */
     void **stage_events;    /* profiling: hipEvent_t[n_stage_events], caller-created.   */
-                            /* [0] is recorded on `stream` before the first kernel,     */
-                            /* [i] after kernel i; slots past the last kernel are       */
-                            /* recorded after it too. NULL = no events.                 */
+                            /* [0] is recorded on `stream` before the first kernel      */
+                            /* launch and [i] after the i-th (kda_launch_plan lists     */
+                            /* them); slots past the last launch are left untouched.   */
+                            /* NULL = no events.                                        */
+    int32_t reserved;       /* must be 0                                                */
 } kda_options;
 
 /*
@@ -108,6 +117,24 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
 
 /* The variant KDA_VARIANT_AUTO resolves to for this shape. */
 int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
+
+/* One kernel launch of a kda_fwd_ex call: its KDA_KERNEL_* kind and the global
+ * chunk ranges [begin, end) whose records it prepares and whose recurrence it runs
+ * (chunks are numbered sequence by sequence; a range may extend past the last
+ * chunk; an empty range is 0, 0). */
+typedef struct kda_launch_info {
+    int32_t kind;
+    int32_t prep_begin, prep_end;
+    int32_t recur_begin, recur_end;
+} kda_launch_info;
+
+/* The kernel launches (in order) a kda_fwd_ex call with this shape and variant makes:
+ * writes up to max_launches entries to info (may be NULL) and returns the count
+ * (0 for an invalid shape). When the recurrence of a shape leaves CUs idle,
+ * the split variant cuts the chunk range into segments and prepares the records
+ * of segment s+1 inside the launch that runs the recurrence of segment s. */
+int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+                        int32_t variant, kda_launch_info *info, int32_t max_launches);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);

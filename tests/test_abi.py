@@ -62,10 +62,11 @@ def test_validation_errors(lib):
     assert call(lib, q=None) == 1                     # KDA_ERR_NULL
     assert call(lib, beta=None) == 1
     assert call(lib, out=None) == 1
-    assert call(lib, opt=native.KdaOptions(7, 0, None, 0, None)) == 3
-    assert call(lib, opt=native.KdaOptions(0, 1, None, 0, None)) == 3      # 1 stage event
-    assert call(lib, opt=native.KdaOptions(0, 4, None, 0, None)) == 3      # events NULL
-    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10, None)
+    assert call(lib, opt=native.KdaOptions(7, 0, None, 0, None, 0)) == 3
+    assert call(lib, opt=native.KdaOptions(0, 1, None, 0, None, 0)) == 3      # 1 stage event
+    assert call(lib, opt=native.KdaOptions(0, 4, None, 0, None, 0)) == 3      # events NULL
+    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10, None, 0)
+    assert call(lib, opt=native.KdaOptions(0, 0, None, 0, None, 1)) == 3   # reserved != 0
     assert call(lib, opt=small) == 4                  # KDA_ERR_ALLOC: workspace too small
     # final_state partially overlapping initial_state
     assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + 64)) == 7
@@ -76,3 +77,27 @@ def test_workspace_bytes(lib):
     b = lib.kda_workspace_bytes(1, 8192, 32, 1)
     assert b >= (8192 // 16) * 32 * 23552
     assert lib.kda_select_variant(1, 8192, 32) in (1, 2)
+
+
+def test_launch_plan():
+    from chunked_gated_delta_kda_amd import native as nat
+    for N, T, H in ((1, 8192, 32), (1, 65536, 8), (8, 8192, 16), (64, 100000, 32)):
+        plan = nat.launch_plan(N, T, H, "split")
+        kinds = [p[0] for p in plan]
+        assert kinds[:2] == ["chunk_map", "prep"] and kinds[-1] == "recur"
+        assert set(kinds[2:-1]) <= {"recur_prep"}
+        M = (T + 15) // 16 + N
+        # the prep ranges and the recurrence ranges each tile [0, M) in order, and a
+        # range's records are prepared in an earlier launch than its recurrence
+        preps = [p[1] for p in plan[1:] if p[1] != (0, 0)]
+        recs = [p[2] for p in plan[1:] if p[2] != (0, 0)]
+        for ranges in (preps, recs):
+            assert ranges[0][0] == 0 and ranges[-1][1] == M
+            assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
+        for i, p in enumerate(plan):
+            if p[2] != (0, 0):
+                lo, hi = p[2]
+                covered = [q[1] for q in plan[:i] if q[1] != (0, 0)]
+                assert any(a <= lo for a, _ in covered) and max(b for _, b in covered) >= hi
+    assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
+    assert nat.launch_plan(0, 16, 1, "split") == []
