@@ -59,20 +59,19 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 
 // Recurrence block shape. 1, 2 or 4: waves per block, each owning 16 value columns
 // (many chains: four waves share each chunk record through one LDS ring). 0: the
-// key-split form, four waves per 16-column slice. 101, 102, 104: the paired form
-// (1, 2 or 4 slices per block, a chain wave and an output wave per slice).
+// key-split form, four waves per 16-column slice. 101, 102: the paired form (1 or 2
+// slices per block, a chain wave and two output waves per slice, one loader wave).
 // KDA_RECUR_WAVES overrides the choice, for tuning.
 int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102 || w == 104) return w;
+        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102) return w;
     }
     // measured on MI355X (bench.py configs): the paired form wins everywhere; one slice
-    // per block when chains are very few, two up to 256 chains, four beyond
+    // per block when chains are very few, two otherwise
     const int64_t chains = N * H;
     if (chains <= 16) return 101;
-    if (chains <= 256) return 102;
-    return 104;
+    return 102;
 }
 
 // Number of chunk-range segments of the split variant. With S > 1 the launches are

@@ -249,17 +249,31 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 }
 
 // ---------------------------------------------------------------- paired recurrence
-// NW 16-column slices per block, two waves per slice. The chain wave (w < NW)
-// runs only the state chain: V_new = U - W S (state hi part), S <- D S + K~^T V_new;
-// each chunk it publishes the pre-update state (fp32) and V_new (hi|lo) to LDS.
-// The output wave (w >= NW) runs one chunk behind, off the chain: it splits the
-// published state into hi/lo and forms O = Q+ S + P V_new. One barrier per chunk
-// (the ring's); snapshots are double-buffered by chunk parity; the output wave
-// reads its record pieces (Q+, P) of chunk it while slot it is still held and
-// keeps them in registers for one chunk.
+// NW 16-column slices per block; per slice one chain wave and two output waves.
+// The chain wave (w < NW) runs only the state chain: V_new = U - W S (state hi
+// part), S <- D S + K~^T V_new; each chunk it publishes the pre-update state
+// (fp32) and V_new (hi|lo) in a snapshot. Output wave parity p (chunks m with
+// m % 2 == p) forms O = Q+ S + P V_new of its chunk off the chain, in two halves
+// over the two chunks after it (key blocks 0-3, then 4-7 and P V_new), so that
+// each output wave does half a chunk of work per chunk. One barrier per chunk
+// (the ring's); snapshots rotate through three buffers. A dedicated loader wave
+// issues every ring load.
+// Waves w and w+4 of a block share a SIMD (and its matrix unit), so the roles are
+// placed to keep each chain wave's SIMD free of output work:
+//   NW = 1: chain 0 | output p0 | output p1 | loader
+//   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | loader | idle |
+//           output (slice 0, p1), (slice 1, p1)
+// (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
 template <int NW>
 struct PairLayout {
+    static_assert(NW == 1 || NW == 2, "one or two slices per block");
     static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
+    static constexpr int SNAPS = 3;                      // snapshot buffers per slice
+    static constexpr int WAVES = NW == 1 ? 4 : 8;
+    static constexpr int LOADER = NW == 1 ? 3 : 4;
+    static constexpr int IDLE = NW == 1 ? -1 : 5;
+    // output wave of slice s, parity p
+    __device__ static constexpr int out_wave(int s, int p) { return NW == 1 ? 1 + p : (p ? 6 : 2) + s; }
 };
 
 // A launch covers the global chunk range [cbeg, cend) (launches over consecutive
@@ -275,8 +289,10 @@ __device__ __forceinline__ void recur_pair_block(
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
     float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
     using R = Ring<NW>;         // record loads and the V tile of NW slices
+    using PL = PairLayout<NW>;
     constexpr int LOADS = R::REC_LOADS + R::V_LOADS;
     constexpr int SLOT = Rec::BYTES + R::V_LOADS * 1024;
+    static_assert(NSLOT >= 3, "the chain reads one chunk ahead of the one it computes");
     static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
     char *snaps = ring + NSLOT * SLOT;
 
@@ -287,8 +303,10 @@ __device__ __forceinline__ void recur_pair_block(
     const int n = order[sh / H];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
     const bool chain = w < NW;
-    const bool loader = w == 2 * NW;     // issues every ring load; computes nothing
-    const int slice = chain ? w : (loader ? 0 : w - NW);
+    const bool loader = w == PL::LOADER;     // issues every ring load; computes nothing
+    const bool idle = w == PL::IDLE;
+    const int parity = (w == PL::out_wave(0, 1) || w == PL::out_wave(NW - 1, 1)) ? 1 : 0;
+    const int slice = chain ? w : ((loader || idle) ? 0 : (w == PL::out_wave(0, parity) ? 0 : 1));
     const int vcol0 = part * R::VCOLS;
     const int col = vcol0 + slice * 16 + c;
     const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
@@ -312,36 +330,61 @@ __device__ __forceinline__ void recur_pair_block(
     const int64_t bos = seq_bos + (int64_t)C * (ci0 - seq_c0);   // first token of this launch's part
     const float *sin = ci0 == seq_c0 ? s0 : carry;
     float *sout = ci1 == seq_c1 ? sfin : carry;
-
-    // ring fill, issued by the loader wave alone (the vector-memory pipe is busy for
-    // most of a chunk's worth of time; no compute wave waits on it)
-    auto fill = [&](int it) {
-        const int k = it < nch ? it : nch - 1;
-        const int64_t t0 = bos + (int64_t)C * k;
-        const int nc = (int)min<int64_t>(C, eos - t0);
-        char *slot = ring + (it % NSLOT) * SLOT;
-        const char *rec = recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES;
-#pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            if (i < R::REC_LOADS) {
-                __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
-                                                 KDA_LDS(slot + i * 1024), 16, 0, 0);
-            } else {
-                const int j = i - R::REC_LOADS;
-                const int row = j * (64 / R::V_LPR) + l / R::V_LPR;
-                const int cc = vcol0 + (l % R::V_LPR) * (R::V_LANE / 2);
-                const int64_t t = t0 + (row < nc ? row : nc - 1);
-                if (R::V_ACTIVE == 64 || l < R::V_ACTIVE)
-                    __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
-                                                     KDA_LDS(slot + Rec::BYTES + j * 1024), 16, 0, 0);
-            }
-        }
+    auto snap_of = [&](int it) { return snaps + ((it % PL::SNAPS) * NW + slice) * PL::SNAP; };
+    auto sync = [] {
+        __builtin_amdgcn_s_barrier();      // slots it, it+1 ready; slot it-1 released
+        __builtin_amdgcn_sched_barrier(0);
     };
-
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     const bf16x4 z4 = {};
-    f32x4 S[8];
+
+    if (loader) {
+        // ring fill (the vector-memory pipe is busy for most of a chunk's worth of
+        // time; no compute wave waits on it)
+        auto fill = [&](int it) {
+            const int k = it < nch ? it : nch - 1;
+            const int64_t t0 = bos + (int64_t)C * k;
+            const int nc = (int)min<int64_t>(C, eos - t0);
+            char *slot = ring + (it % NSLOT) * SLOT;
+            const char *rec = recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES;
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                if (i < R::REC_LOADS) {
+                    __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
+                                                     KDA_LDS(slot + i * 1024), 16, 0, 0);
+                } else {
+                    const int j = i - R::REC_LOADS;
+                    const int row = j * (64 / R::V_LPR) + l / R::V_LPR;
+                    const int cc = vcol0 + (l % R::V_LPR) * (R::V_LANE / 2);
+                    const int64_t t = t0 + (row < nc ? row : nc - 1);
+                    if (R::V_ACTIVE == 64 || l < R::V_ACTIVE)
+                        __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
+                                                         KDA_LDS(slot + Rec::BYTES + j * 1024), 16, 0, 0);
+                }
+            }
+        };
+#pragma unroll
+        for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        for (int it = 0; it < nch; ++it) {
+            // chunks it and it+1 have landed once at most the loads of the NSLOT-3
+            // younger chunks remain outstanding
+            wait_vmcnt<(NSLOT - 3) * LOADS>();
+            sync();
+            fill(it + NSLOT - 1);
+        }
+        sync();
+        sync();
+        wait_vmcnt<0>();     // no ring write still in flight when the wave ends
+        return;
+    }
+
+    if (idle) {
+        for (int it = 0; it < nch + 2; ++it) sync();
+        return;
+    }
+
     if (chain) {
+        f32x4 S[8];
         if (sin) {
 #pragma unroll
             for (int b = 0; b < 8; ++b)
@@ -351,112 +394,153 @@ __device__ __forceinline__ void recur_pair_block(
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = zero;
         }
+        // inputs of one chunk, read from its ring slot one chunk ahead of use
+        struct ChainIn {
+            bf16x8 wn[4], kt[8], tb;
+            bf16x4 v;
+        };
+        auto chain_read = [&](ChainIn &x, int it) {
+            const char *slot = ring + (it % NSLOT) * SLOT;
+            x.tb = *(const bf16x8 *)(slot + Rec::TB + l * 16);
+            const uint16_t *vt = (const uint16_t *)(slot + Rec::BYTES);
+            uint16_t vv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[j] = vt[(4 * gq + j) * R::VCOLS + slice * 16 + c];
+            x.v = __builtin_bit_cast(bf16x4, (ushort4{vv[0], vv[1], vv[2], vv[3]}));
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) x.wn[kb] = *(const bf16x8 *)(slot + Rec::WN + kb * 1024 + l * 16);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) x.kt[b] = *(const bf16x8 *)(slot + Rec::KT + b * 1024 + l * 16);
+        };
+        // state decay of chunk it, read at the end of the step before (it is used last;
+        // the read completes while the wave waits at the barrier)
+        f32x4 eg[8];
+        auto read_eg = [&](int it) {
+            const char *slot = ring + (it % NSLOT) * SLOT;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) eg[b] = *(const f32x4 *)(slot + Rec::EG + (16 * b + 4 * gq) * 4);
+        };
+        // one chunk: publish S (pre-update) and V_new, then update S
+        auto chain_step = [&](const ChainIn &x, int it) {
+            char *snap = snap_of(it);
+            bf16x8 shi[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
+            f32x4 va = mfma(x.wn[0], shi[0], zero), vb = mfma(x.wn[1], shi[1], zero);
+            va = mfma(x.wn[2], shi[2], va);
+            vb = mfma(x.wn[3], shi[3], vb);
+            va = mfma(x.tb, cat(x.v, x.v), va);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
+            bf16x4 vh, vl;
+            split4(va + vb, vh, vl);
+            *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
+            const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
+            // two passes over each half of the key blocks so that no MFMA waits on
+            // the one just before it
+#pragma unroll
+            for (int hb = 0; hb < 8; hb += 4) {
+                f32x4 tmp[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) tmp[b] = mfma(x.kt[hb + b], vhh, S[hb + b] * eg[hb + b]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) S[hb + b] = mfma(x.kt[hb + b], vl0, tmp[b]);
+            }
+            if (it + 1 < nch) read_eg(it + 1);   // slot it+1 stays valid through the next step
+        };
+        ChainIn A, B;
+        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
+            sync();
+            if (it == 0) {
+                chain_read(A, 0);
+                read_eg(0);
+            }
+            if (it + 1 < nch) chain_read(B, it + 1);
+            chain_step(A, it);
+            if (it + 1 < nch) {
+                sync();
+                if (it + 2 < nch) chain_read(A, it + 2);
+                chain_step(B, it + 1);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
+        sync();
+        sync();
+        if (sout) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+        }
+        return;
     }
-    bf16x8 qh[4], ql[4];
-    bf16x8 pp;
 
-    // output wave: O of chunk it from snapshot it and the held Q+/P pieces
-    auto emit = [&](int it) {
-        const char *snap = snaps + ((it & 1) * NW + slice) * PairLayout<NW>::SNAP;
-        bf16x8 shi[4], slo[4];
+    // ---- output wave of parity `parity`
+    bf16x8 qh[4], ql[4], pp;      // Q+ (hi, lo) and P of the chunk in flight
+    f32x4 oa = zero, ob = zero;   // its partial output after the first half
+    auto read_q = [&](int it) {
+        const char *slot = ring + (it % NSLOT) * SLOT;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            qh[kb] = *(const bf16x8 *)(slot + Rec::QH + kb * 1024 + l * 16);
+            ql[kb] = *(const bf16x8 *)(slot + Rec::QL + kb * 1024 + l * 16);
+        }
+        pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
+    };
+    // Q+ S over key blocks kb0, kb0+1 of chunk m's snapshot, into oa/ob
+    auto half_qs = [&](int m, int kb0) {
+        const char *snap = snap_of(m);
+#pragma unroll
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
             const f32x4 a = *(const f32x4 *)(snap + ((2 * kb) * 64 + l) * 16);
             const f32x4 b = *(const f32x4 *)(snap + ((2 * kb + 1) * 64 + l) * 16);
             bf16x4 ah, al, bh, bl;
             split4(a, ah, al);
             split4(b, bh, bl);
-            shi[kb] = cat(ah, bh);
-            slo[kb] = cat(al, bl);
+            const bf16x8 shi = cat(ah, bh), slo = cat(al, bl);
+            oa = mfma(qh[kb], shi, oa);
+            ob = mfma(qh[kb], slo, ob);
+            oa = mfma(ql[kb], shi, oa);
         }
+    };
+    auto finish = [&](int m) {
+        const char *snap = snap_of(m);
         const bf16x8 vs = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);   // V_new hi | lo
+        half_qs(m, 2);
         const bf16x4 vh = __builtin_shufflevector(vs, vs, 0, 1, 2, 3);
         const bf16x4 vl = __builtin_shufflevector(vs, vs, 4, 5, 6, 7);
-        f32x4 oa = zero, ob = zero;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            oa = mfma(qh[kb], shi[kb], oa);
-            ob = mfma(qh[kb], slo[kb], ob);
-            oa = mfma(ql[kb], shi[kb], oa);
-        }
         ob = mfma(pp, cat(vh, vh), ob);
         ob = mfma(pp, cat(vl, z4), ob);
         const f32x4 o = oa + ob;
-        const int64_t t0 = bos + (int64_t)C * it;
+        const int64_t t0 = bos + (int64_t)C * m;
         const int nc = (int)min<int64_t>(C, eos - t0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
     };
-
-    {
-        if (loader) {
-#pragma unroll
-            for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+    for (int it = 0; it < nch + 2; ++it) {
+        sync();
+        // exactly one of chunks it-1, it-2 has this wave's parity
+        if (it >= 2 && it - 2 < nch && ((it - 2) & 1) == parity) finish(it - 2);
+        if (it >= 1 && it - 1 < nch && ((it - 1) & 1) == parity) {
+            oa = zero;
+            ob = zero;
+            half_qs(it - 1, 0);
         }
-        for (int it = 0; it < nch; ++it) {
-            // the loader's loads of chunk it are complete once at most those of the
-            // NSLOT-2 younger chunks remain outstanding
-            if (loader) wait_vmcnt<(NSLOT - 2) * LOADS>();
-            __builtin_amdgcn_s_barrier();      // slot it ready; slot it-1 and snapshot it-2 released
-            __builtin_amdgcn_sched_barrier(0);
-            const char *slot = ring + (it % NSLOT) * SLOT;
-            if (loader) {
-                fill(it + NSLOT - 1);
-            } else if (chain) {
-                StepIn st;
-                read_rec(st, slot);
-                read_vtile(st, (const uint16_t *)(slot + Rec::BYTES), R::VCOLS, slice * 16);
-                char *snap = snaps + ((it & 1) * NW + slice) * PairLayout<NW>::SNAP;
-#pragma unroll
-                for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
-                bf16x8 shi[4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
-                f32x4 va = mfma(st.tb, cat(st.v, st.v), zero), vb = zero;
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    if (kb & 1) vb = mfma(st.wn[kb], shi[kb], vb);
-                    else va = mfma(st.wn[kb], shi[kb], va);
-                }
-                bf16x4 vh, vl;
-                split4(va + vb, vh, vl);
-                *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
-                const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
-#pragma unroll
-                for (int b = 0; b < 8; ++b) {
-                    S[b] = mfma(st.kt[b], vhh, S[b] * st.eg[b]);
-                    S[b] = mfma(st.kt[b], vl0, S[b]);
-                }
-            } else {
-                if (it > 0) emit(it - 1);
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    qh[kb] = *(const bf16x8 *)(slot + Rec::QH + kb * 1024 + l * 16);
-                    ql[kb] = *(const bf16x8 *)(slot + Rec::QL + kb * 1024 + l * 16);
-                }
-                pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
-            }
-        }
+        if (it < nch && (it & 1) == parity) read_q(it);   // slot it is refilled after the next barrier
         __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_s_barrier();
-        if (!chain && !loader) emit(nch - 1);
-    }
-    if (chain && sout) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
     }
 }
 
 template <int NW, int NSLOT>
 struct PairLds {
-    static constexpr int BYTES = NSLOT * (Rec::BYTES + Ring<NW>::V_LOADS * 1024) + 2 * NW * PairLayout<NW>::SNAP;
+    static constexpr int BYTES = NSLOT * (Rec::BYTES + Ring<NW>::V_LOADS * 1024) +
+                                 PairLayout<NW>::SNAPS * NW * PairLayout<NW>::SNAP;
 };
 
+
 template <int NW, int NSLOT>
-__global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
@@ -474,11 +558,11 @@ __global__ __launch_bounds__(128 * NW + 64) void recur_pair_kernel(
 // the recurrence leaves idle, instead of waiting for the recurrence to finish.
 template <int NW>
 struct RecurPrep {
-    static constexpr int PREP_WAVES = 2 * NW + 1 < 4 ? 2 * NW + 1 : 4;
+    static constexpr int PREP_WAVES = PairLayout<NW>::WAVES < 4 ? PairLayout<NW>::WAVES : 4;
 };
 
 template <int NW, int NSLOT>
-__global__ __launch_bounds__(128 * NW + 64) void recur_prep_kernel(
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_prep_kernel(
     const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
@@ -762,8 +846,8 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
         attr_set = true;
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(128 * NW + 64), lds, st, recs, v, cu,
-                       chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
     return hipGetLastError();
 }
 
@@ -787,7 +871,7 @@ static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
     const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
     if (pb < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(128 * NW + 64), lds, st, a.recs, a.v,
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
                        a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry,
                        (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale, a.recs,
                        (int)a.pbeg, (int)a.pend);
@@ -798,7 +882,6 @@ hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) 
     switch (waves) {
     case 101: return launch_recur_prep_t<1, 4>(a, st);
     case 102: return launch_recur_prep_t<2, 4>(a, st);
-    case 104: return launch_recur_prep_t<4, 3>(a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -810,7 +893,6 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
     switch (waves) {
     case 101: return launch_recur_pair<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
     case 102: return launch_recur_pair<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 104: return launch_recur_pair<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -819,7 +901,7 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: case 102: case 104:
+    case 101: case 102:
         return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
                                   waves, 0, 1 << 30, st);
     case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
