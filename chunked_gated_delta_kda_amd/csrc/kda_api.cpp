@@ -65,7 +65,7 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102) return w;
+        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102 || w == 201 || w == 202) return w;
     }
     // measured on MI355X (bench.py configs): the paired form wins everywhere; one slice
     // per block when chains are very few, two otherwise
@@ -85,7 +85,7 @@ int split_segments(int64_t N, int64_t H, int waves) {
         const int s = std::atoi(e);
         if (s >= 1 && s <= KDA_MAX_SEGMENTS) return s;
     }
-    const int64_t blocks = N * H * (8 / (waves - 100));
+    const int64_t blocks = N * H * (8 / (waves % 100));
     return blocks < 256 ? 4 : 1;
 }
 

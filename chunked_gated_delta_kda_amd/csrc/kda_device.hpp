@@ -115,16 +115,26 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
 // Everything the recurrence needs from one (chunk, head), in per-lane order so
 // that each lane of a wave reads contiguous 8/16-byte pieces. Offsets in bytes.
 struct Rec {
+    // pieces the state chain reads, first (one contiguous run of whole 1 KiB loads)
     static constexpr int WN = 0;       // bf16 [4 kb][64 lanes][8]: -W, state-permuted A operand
-    static constexpr int QH = 4096;    // bf16 [4][64][8]: Q+ hi, state-permuted A operand
-    static constexpr int QL = 8192;    // bf16 [4][64][8]: Q+ lo
-    static constexpr int KT = 12288;   // bf16 [8 blocks][64][8]: K~[4g+j][16b + l%16] hi(4) | lo(4)
-    static constexpr int PP = 20480;   // bf16 [64][8]: P[l%16][4g+j] hi(4) | lo(4) (causal, diagonal kept)
-    static constexpr int TB = 21504;   // bf16 [64][8]: (T Diag(beta))[l%16][4g+j] hi | lo
-    static constexpr int EG = 22528;   // f32 [128]: e^{G_C} per key channel
-    static constexpr int USED = 23040;
-    static constexpr int BYTES = 23552; // padded to whole 1 KiB wave loads (64 lanes x 16 B)
+    static constexpr int KT = 4096;    // bf16 [8 blocks][64][8]: K~[4g+j][16b + l%16] hi(4) | lo(4)
+    static constexpr int TB = 12288;   // bf16 [64][8]: (T Diag(beta))[l%16][4g+j] hi | lo
+    static constexpr int EGP = 13312;  // f32 [128]: e^{G_C}, lane-permuted (egp_index): 8 B per lane
+    static constexpr int EG = 13824;   // f32 [128]: e^{G_C} per key channel
+    static constexpr int CHAIN = 14336;
+    // pieces the output reads
+    static constexpr int QH = 14336;   // bf16 [4][64][8]: Q+ hi, state-permuted A operand
+    static constexpr int QL = 18432;   // bf16 [4][64][8]: Q+ lo
+    static constexpr int PP = 22528;   // bf16 [64][8]: P[l%16][4g+j] hi(4) | lo(4) (causal, diagonal kept)
+    static constexpr int BYTES = 23552; // whole 1 KiB wave loads (64 lanes x 16 B)
 };
+static_assert(Rec::CHAIN % 1024 == 0 && Rec::BYTES % 1024 == 0, "record pieces in whole wave loads");
+// Position of key channel r in the lane-permuted decay vector: lane (c, g) of the
+// MFMA D layout holds, as two floats, the decays of rows 16*(c/2) + 4g + 2*(c%2) + i
+// (i = 0, 1), so that row 16b + 4g + j sits in lane 2b + j/2 of row group g.
+__host__ __device__ constexpr int egp_index(int r) {
+    return ((((r & 15) >> 2) * 16 + 2 * (r >> 4) + ((r & 3) >> 1)) * 2) + (r & 1);
+}
 
 // LDS scratch of one chunk prep (one wave).
 struct alignas(16) PrepLds {
@@ -214,6 +224,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     // padded rows carry g = 0, so acc is G at the last real token
     const float eC0 = __builtin_amdgcn_exp2f(acc0), eC1 = __builtin_amdgcn_exp2f(acc1);
     *(f32x2 *)(rec + Rec::EG + c0 * 4) = f32x2{eC0, eC1};
+    *(f32x2 *)(rec + Rec::EGP + egp_index(c0) * 4) = f32x2{eC0, eC1};   // c0 even: one pair
 
     // per-channel token rows of K+ and K~ (hi, lo), packed two tokens per dword,
     // written to the transposed tiles with wide stores after the loop

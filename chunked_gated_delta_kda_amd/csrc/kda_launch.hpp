@@ -16,7 +16,7 @@ hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, con
                        const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
                        hipStream_t st);
 
-// paired recurrence over the global chunk range [cbeg, cend); waves in {101, 102}
+// paired recurrence over the global chunk range [cbeg, cend); waves in {101, 102, 201, 202}
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
                               const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                               const float *s0, float *out, float *sfin, float *carry, int waves,

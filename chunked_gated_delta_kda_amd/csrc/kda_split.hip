@@ -248,6 +248,20 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     }
 }
 
+// x broadcast from lane N of each 16-lane row to the whole row
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N,
+                                                              0xf, 0xf, true));
+}
+// state block B (rows 16B + 4g + j) times its decay; e = this lane's pair of the
+// lane-permuted decay vector
+template <int B>
+__device__ __forceinline__ f32x4 decay_block(f32x4 s, f32x2 e) {
+    return f32x4{s[0] * row_bcast<2 * B>(e[0]), s[1] * row_bcast<2 * B>(e[1]),
+                 s[2] * row_bcast<2 * B + 1>(e[0]), s[3] * row_bcast<2 * B + 1>(e[1])};
+}
+
 // ---------------------------------------------------------------- paired recurrence
 // NW 16-column slices per block; per slice one chain wave and two output waves.
 // The chain wave (w < NW) runs only the state chain: V_new = U - W S (state hi
@@ -264,6 +278,9 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 //   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | loader | idle |
 //           output (slice 0, p1), (slice 1, p1)
 // (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
+#ifndef KDA_PAIR_NSLOT
+#define KDA_PAIR_NSLOT 4   // ring depth of the paired recurrence (chunks)
+#endif
 template <int NW>
 struct PairLayout {
     static_assert(NW == 1 || NW == 2, "one or two slices per block");
@@ -288,10 +305,11 @@ __device__ __forceinline__ void recur_pair_block(
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
     float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
-    using R = Ring<NW>;         // record loads and the V tile of NW slices
+    using R = Ring<NW>;         // V tile geometry of NW slices
     using PL = PairLayout<NW>;
-    constexpr int LOADS = R::REC_LOADS + R::V_LOADS;
-    constexpr int SLOT = Rec::BYTES + R::V_LOADS * 1024;
+    constexpr int REC_LOADS = Rec::CHAIN / 1024;       // the chain's part of the record
+    constexpr int LOADS = REC_LOADS + R::V_LOADS;
+    constexpr int SLOT = Rec::CHAIN + R::V_LOADS * 1024;
     static_assert(NSLOT >= 3, "the chain reads one chunk ahead of the one it computes");
     static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
     char *snaps = ring + NSLOT * SLOT;
@@ -349,17 +367,17 @@ __device__ __forceinline__ void recur_pair_block(
             const char *rec = recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES;
 #pragma unroll
             for (int i = 0; i < LOADS; ++i) {
-                if (i < R::REC_LOADS) {
+                if (i < REC_LOADS) {
                     __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
                                                      KDA_LDS(slot + i * 1024), 16, 0, 0);
                 } else {
-                    const int j = i - R::REC_LOADS;
+                    const int j = i - REC_LOADS;
                     const int row = j * (64 / R::V_LPR) + l / R::V_LPR;
                     const int cc = vcol0 + (l % R::V_LPR) * (R::V_LANE / 2);
                     const int64_t t = t0 + (row < nc ? row : nc - 1);
                     if (R::V_ACTIVE == 64 || l < R::V_ACTIVE)
                         __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
-                                                         KDA_LDS(slot + Rec::BYTES + j * 1024), 16, 0, 0);
+                                                         KDA_LDS(slot + Rec::CHAIN + j * 1024), 16, 0, 0);
                 }
             }
         };
@@ -397,28 +415,20 @@ __device__ __forceinline__ void recur_pair_block(
         // inputs of one chunk, read from its ring slot one chunk ahead of use
         struct ChainIn {
             bf16x8 wn[4], kt[8], tb;
-            bf16x4 v;
+            f32x2 e;             // lane-permuted state decay
+            uint16_t vv[4];      // V[4g+j][col], combined only where used
         };
         auto chain_read = [&](ChainIn &x, int it) {
             const char *slot = ring + (it % NSLOT) * SLOT;
             x.tb = *(const bf16x8 *)(slot + Rec::TB + l * 16);
-            const uint16_t *vt = (const uint16_t *)(slot + Rec::BYTES);
-            uint16_t vv[4];
+            const uint16_t *vt = (const uint16_t *)(slot + Rec::CHAIN);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vv[j] = vt[(4 * gq + j) * R::VCOLS + slice * 16 + c];
-            x.v = __builtin_bit_cast(bf16x4, (ushort4{vv[0], vv[1], vv[2], vv[3]}));
+            for (int j = 0; j < 4; ++j) x.vv[j] = vt[(4 * gq + j) * R::VCOLS + slice * 16 + c];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) x.wn[kb] = *(const bf16x8 *)(slot + Rec::WN + kb * 1024 + l * 16);
 #pragma unroll
             for (int b = 0; b < 8; ++b) x.kt[b] = *(const bf16x8 *)(slot + Rec::KT + b * 1024 + l * 16);
-        };
-        // state decay of chunk it, read at the end of the step before (it is used last;
-        // the read completes while the wave waits at the barrier)
-        f32x4 eg[8];
-        auto read_eg = [&](int it) {
-            const char *slot = ring + (it % NSLOT) * SLOT;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) eg[b] = *(const f32x4 *)(slot + Rec::EG + (16 * b + 4 * gq) * 4);
+            x.e = *(const f32x2 *)(slot + Rec::EGP + l * 8);
         };
         // one chunk: publish S (pre-update) and V_new, then update S
         auto chain_step = [&](const ChainIn &x, int it) {
@@ -426,14 +436,29 @@ __device__ __forceinline__ void recur_pair_block(
             bf16x8 shi[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
-            f32x4 va = mfma(x.wn[0], shi[0], zero), vb = mfma(x.wn[1], shi[1], zero);
-            va = mfma(x.wn[2], shi[2], va);
-            vb = mfma(x.wn[3], shi[3], vb);
-            va = mfma(x.tb, cat(x.v, x.v), va);
+            // combine the V values here, not where they were read (the compiler would
+            // otherwise do it at the read and wait for the read to land)
+            uint32_t v0 = x.vv[0], v1 = x.vv[1], v2 = x.vv[2], v3 = x.vv[3];
+            asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+            const bf16x4 vin = __builtin_bit_cast(bf16x4, (uint2{v0 | (v1 << 16), v2 | (v3 << 16)}));
+            // U - W S over four independent accumulators (plus T Diag(beta) V)
+            f32x4 a0 = mfma(x.wn[0], shi[0], zero), a1 = mfma(x.wn[1], shi[1], zero);
+            f32x4 a2 = mfma(x.wn[2], shi[2], zero), a3 = mfma(x.wn[3], shi[3], zero);
+            const f32x4 u = mfma(x.tb, cat(vin, vin), zero);
+            // the decayed state, formed while the products above run
+            f32x4 Sd[8];
+            Sd[0] = decay_block<0>(S[0], x.e);
+            Sd[1] = decay_block<1>(S[1], x.e);
+            Sd[2] = decay_block<2>(S[2], x.e);
+            Sd[3] = decay_block<3>(S[3], x.e);
+            Sd[4] = decay_block<4>(S[4], x.e);
+            Sd[5] = decay_block<5>(S[5], x.e);
+            Sd[6] = decay_block<6>(S[6], x.e);
+            Sd[7] = decay_block<7>(S[7], x.e);
 #pragma unroll
             for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
             bf16x4 vh, vl;
-            split4(va + vb, vh, vl);
+            split4((a0 + a1) + (a2 + a3) + u, vh, vl);
             *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
             const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
             // two passes over each half of the key blocks so that no MFMA waits on
@@ -442,26 +467,35 @@ __device__ __forceinline__ void recur_pair_block(
             for (int hb = 0; hb < 8; hb += 4) {
                 f32x4 tmp[4];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) tmp[b] = mfma(x.kt[hb + b], vhh, S[hb + b] * eg[hb + b]);
+                for (int b = 0; b < 4; ++b) tmp[b] = mfma(x.kt[hb + b], vhh, Sd[hb + b]);
 #pragma unroll
                 for (int b = 0; b < 4; ++b) S[hb + b] = mfma(x.kt[hb + b], vl0, tmp[b]);
             }
-            if (it + 1 < nch) read_eg(it + 1);   // slot it+1 stays valid through the next step
         };
-        ChainIn A, B;
-        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
+
+        // After each barrier every LDS access of the wave issued before it (a chunk
+        // ago) is waited for explicitly: the LDS counter completes in order and
+        // counts at most 15, so waits placed per use after the next chunk's reads
+        // have been issued would also wait for those.
+        auto sync_chain = [&] {
             sync();
-            if (it == 0) {
-                chain_read(A, 0);
-                read_eg(0);
-            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        };
+        // the first chunk's inputs are read (and waited for) before the loop, so that
+        // every step starts with its inputs complete
+        ChainIn A, B;
+        sync();
+        chain_read(A, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
             if (it + 1 < nch) chain_read(B, it + 1);
             chain_step(A, it);
-            if (it + 1 < nch) {
-                sync();
-                if (it + 2 < nch) chain_read(A, it + 2);
-                chain_step(B, it + 1);
-            }
+            if (it + 1 >= nch) break;
+            sync_chain();
+            if (it + 2 < nch) chain_read(A, it + 2);
+            chain_step(B, it + 1);
+            if (it + 2 >= nch) break;
+            sync_chain();
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
         sync();
@@ -475,20 +509,23 @@ __device__ __forceinline__ void recur_pair_block(
         return;
     }
 
-    // ---- output wave of parity `parity`
-    bf16x8 qh[4], ql[4], pp;      // Q+ (hi, lo) and P of the chunk in flight
-    f32x4 oa = zero, ob = zero;   // its partial output after the first half
-    auto read_q = [&](int it) {
-        const char *slot = ring + (it % NSLOT) * SLOT;
+    // ---- output wave: chunks m = parity, parity + 2, ...; the first half of chunk
+    // m's output after barrier m+1, the rest after barrier m+2. Its Q+ and P pieces
+    // come straight from global memory into registers, four chunks ahead.
+    struct OutIn {
+        bf16x8 qh[4], ql[4], pp;
+    };
+    auto load = [&](OutIn &x, int m) {
+        const char *rec = recs + ((int64_t)(ci0 + m) * H + h) * Rec::BYTES;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            qh[kb] = *(const bf16x8 *)(slot + Rec::QH + kb * 1024 + l * 16);
-            ql[kb] = *(const bf16x8 *)(slot + Rec::QL + kb * 1024 + l * 16);
+            x.qh[kb] = *(const bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16);
+            x.ql[kb] = *(const bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16);
         }
-        pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
+        x.pp = *(const bf16x8 *)(rec + Rec::PP + l * 16);
     };
-    // Q+ S over key blocks kb0, kb0+1 of chunk m's snapshot, into oa/ob
-    auto half_qs = [&](int m, int kb0) {
+    f32x4 oa = zero, ob = zero;
+    auto half_qs = [&](const OutIn &x, int m, int kb0) {
         const char *snap = snap_of(m);
 #pragma unroll
         for (int kb = kb0; kb < kb0 + 2; ++kb) {
@@ -498,43 +535,57 @@ __device__ __forceinline__ void recur_pair_block(
             split4(a, ah, al);
             split4(b, bh, bl);
             const bf16x8 shi = cat(ah, bh), slo = cat(al, bl);
-            oa = mfma(qh[kb], shi, oa);
-            ob = mfma(qh[kb], slo, ob);
-            oa = mfma(ql[kb], shi, oa);
+            oa = mfma(x.qh[kb], shi, oa);
+            ob = mfma(x.qh[kb], slo, ob);
+            oa = mfma(x.ql[kb], shi, oa);
         }
     };
-    auto finish = [&](int m) {
+    auto first = [&](const OutIn &x, int m) {
+        oa = zero;
+        ob = zero;
+        half_qs(x, m, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // snapshot reads done before the next barrier
+    };
+    auto finish = [&](const OutIn &x, int m) {
         const char *snap = snap_of(m);
         const bf16x8 vs = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);   // V_new hi | lo
-        half_qs(m, 2);
+        half_qs(x, m, 2);
         const bf16x4 vh = __builtin_shufflevector(vs, vs, 0, 1, 2, 3);
         const bf16x4 vl = __builtin_shufflevector(vs, vs, 4, 5, 6, 7);
-        ob = mfma(pp, cat(vh, vh), ob);
-        ob = mfma(pp, cat(vl, z4), ob);
+        ob = mfma(x.pp, cat(vh, vh), ob);
+        ob = mfma(x.pp, cat(vl, z4), ob);
         const f32x4 o = oa + ob;
         const int64_t t0 = bos + (int64_t)C * m;
         const int nc = (int)min<int64_t>(C, eos - t0);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
-    };
-    for (int it = 0; it < nch + 2; ++it) {
-        sync();
-        // exactly one of chunks it-1, it-2 has this wave's parity
-        if (it >= 2 && it - 2 < nch && ((it - 2) & 1) == parity) finish(it - 2);
-        if (it >= 1 && it - 1 < nch && ((it - 1) & 1) == parity) {
-            oa = zero;
-            ob = zero;
-            half_qs(it - 1, 0);
-        }
-        if (it < nch && (it & 1) == parity) read_q(it);   // slot it is refilled after the next barrier
         __builtin_amdgcn_s_waitcnt(0xc07f);
+    };
+    OutIn X, Y;                      // chunks m = parity + 4i and parity + 4i + 2
+    if (parity < nch) load(X, parity);
+    if (parity + 2 < nch) load(Y, parity + 2);
+    int nb = 0;
+    for (; nb < parity + 1; ++nb) sync();
+    for (int m = parity; m < nch; m += 4) {
+        sync(); ++nb;
+        first(X, m);
+        sync(); ++nb;
+        finish(X, m);
+        if (m + 4 < nch) load(X, m + 4);
+        if (m + 2 >= nch) break;
+        sync(); ++nb;
+        first(Y, m + 2);
+        sync(); ++nb;
+        finish(Y, m + 2);
+        if (m + 6 < nch) load(Y, m + 6);
     }
+    for (; nb < nch + 2; ++nb) sync();
 }
 
 template <int NW, int NSLOT>
 struct PairLds {
-    static constexpr int BYTES = NSLOT * (Rec::BYTES + Ring<NW>::V_LOADS * 1024) +
+    static constexpr int BYTES = NSLOT * (Rec::CHAIN + Ring<NW>::V_LOADS * 1024) +
                                  PairLayout<NW>::SNAPS * NW * PairLayout<NW>::SNAP;
 };
 
@@ -575,6 +626,290 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_prep_kernel(
         return;
     }
     constexpr int PW = RecurPrep<NW>::PREP_WAVES;
+    const int w = threadIdx.x >> 6;
+    if (w >= PW) return;
+    const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
+    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
+    if (ci >= pend || ci >= chunk_off[N]) return;
+    prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
+             *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
+}
+
+// ---------------------------------------------------------------- direct-load paired recurrence
+// The paired recurrence without an LDS ring: every wave loads its own record
+// pieces from global memory (L2) straight into registers, one or two chunks
+// ahead of use, so that record traffic neither passes through LDS nor waits on
+// the LDS-DMA path (whose per-CU rate is a fraction of what plain vector loads
+// reach). LDS holds only the state snapshots the chain wave hands to the output
+// waves. The state decay arrives lane-permuted (two floats per lane) and is
+// broadcast within each 16-lane row by DPP inside the multiply.
+//   NW = 1: chain | output p0 | output p1
+//   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | idle, idle |
+//           output (slice 0, p1), (slice 1, p1)
+// (waves w and w+4 share a SIMD: each chain wave's partner does nothing.)
+template <int NW>
+struct DirectLayout {
+    static_assert(NW == 1 || NW == 2, "one or two slices per block");
+    static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
+    static constexpr int SNAPS = 3;
+    static constexpr int WAVES = NW == 1 ? 3 : 8;
+    static constexpr int BYTES = SNAPS * NW * SNAP;
+};
+
+template <int NW>
+__device__ __forceinline__ void recur_direct_block(
+    int bid, char *lds, const char *__restrict__ recs, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+    const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
+    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    using DL = DirectLayout<NW>;
+    constexpr int PARTS = D / (16 * NW);
+    const int part = bid % PARTS;
+    const int sh = bid / PARTS;
+    const int h = sh % H;
+    const int n = order[sh / H];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
+    const bool chain = w < NW;
+    const bool idle = NW == 2 && (w == 4 || w == 5);
+    const int parity = NW == 1 ? (w == 2) : (w >= 6);
+    const int slice = chain ? w : (NW == 1 ? 0 : (w & 1));
+    const int col = part * 16 * NW + slice * 16 + c;
+    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
+    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;      // this launch's chunks of the sequence
+    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (ci0 >= ci1) {
+        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
+                    sfin[o] = s0 ? s0[o] : 0.f;
+                }
+        }
+        return;
+    }
+    const int nch = ci1 - ci0;
+    const int64_t bos = seq_bos + (int64_t)C * (ci0 - seq_c0);
+    const float *sin = ci0 == seq_c0 ? s0 : carry;
+    float *sout = ci1 == seq_c1 ? sfin : carry;
+    auto snap_of = [&](int it) { return lds + ((it % DL::SNAPS) * NW + slice) * DL::SNAP; };
+    auto rec_of = [&](int k) { return recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES; };
+    auto sync = [] {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const bf16x4 z4 = {};
+
+    if (idle) {
+        for (int it = 0; it < nch + 2; ++it) sync();
+        return;
+    }
+
+    if (chain) {
+        f32x4 S[8];
+        if (sin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = zero;
+        }
+        struct ChainIn {
+            bf16x8 wn[4], kt[8], tb;
+            f32x2 e;             // lane-permuted state decay
+            uint16_t vv[4];      // V[4g+j][col]; rows past the chunk end repeat its last
+                                 // row (finite, and T Diag(beta) is zero there)
+        };
+        auto load = [&](ChainIn &x, int k) {
+            const char *rec = rec_of(k);
+            x.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) x.wn[kb] = *(const bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16);
+            const int64_t t0 = bos + (int64_t)C * k;
+            const int nc = (int)min<int64_t>(C, eos - t0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * gq + j < nc ? 4 * gq + j : nc - 1;
+                x.vv[j] = v[((t0 + t) * H + h) * D + col];
+            }
+#pragma unroll
+            for (int b = 0; b < 8; ++b) x.kt[b] = *(const bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16);
+            x.e = *(const f32x2 *)(rec + Rec::EGP + l * 8);
+        };
+        auto step = [&](const ChainIn &x, int it) {
+            char *snap = snap_of(it);
+            bf16x8 shi[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
+            const bf16x4 vin = __builtin_bit_cast(
+                bf16x4, (uint2{x.vv[0] | ((uint32_t)x.vv[1] << 16), x.vv[2] | ((uint32_t)x.vv[3] << 16)}));
+            // U - W S over four independent accumulators (plus T Diag(beta) V)
+            f32x4 a0 = mfma(x.wn[0], shi[0], zero), a1 = mfma(x.wn[1], shi[1], zero);
+            f32x4 a2 = mfma(x.wn[2], shi[2], zero), a3 = mfma(x.wn[3], shi[3], zero);
+            const f32x4 u = mfma(x.tb, cat(vin, vin), zero);
+            // the decayed state, formed while the products above run
+            f32x4 Sd[8];
+            Sd[0] = decay_block<0>(S[0], x.e);
+            Sd[1] = decay_block<1>(S[1], x.e);
+            Sd[2] = decay_block<2>(S[2], x.e);
+            Sd[3] = decay_block<3>(S[3], x.e);
+            Sd[4] = decay_block<4>(S[4], x.e);
+            Sd[5] = decay_block<5>(S[5], x.e);
+            Sd[6] = decay_block<6>(S[6], x.e);
+            Sd[7] = decay_block<7>(S[7], x.e);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
+            bf16x4 vh, vl;
+            split4((a0 + a1) + (a2 + a3) + u, vh, vl);
+            *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
+            const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
+#pragma unroll
+            for (int hb = 0; hb < 8; hb += 4) {
+                f32x4 tmp[4];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) tmp[b] = mfma(x.kt[hb + b], vhh, Sd[hb + b]);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) S[hb + b] = mfma(x.kt[hb + b], vl0, tmp[b]);
+            }
+        };
+        ChainIn A, B;
+        load(A, 0);
+        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
+            sync();
+            if (it + 1 < nch) load(B, it + 1);
+            step(A, it);
+            if (it + 1 >= nch) break;
+            sync();
+            if (it + 2 < nch) load(A, it + 2);
+            step(B, it + 1);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
+        sync();
+        sync();
+        if (sout) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+        }
+        return;
+    }
+
+    // ---- output wave: chunks m = parity, parity + 2, ...; the first half of chunk
+    // m's output after barrier m+1, the rest after barrier m+2
+    struct OutIn {
+        bf16x8 qh[4], ql[4], pp;
+    };
+    auto load = [&](OutIn &x, int m) {
+        const char *rec = rec_of(m);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            x.qh[kb] = *(const bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16);
+            x.ql[kb] = *(const bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16);
+        }
+        x.pp = *(const bf16x8 *)(rec + Rec::PP + l * 16);
+    };
+    f32x4 oa = zero, ob = zero;
+    auto half_qs = [&](const OutIn &x, int m, int kb0) {
+        const char *snap = snap_of(m);
+#pragma unroll
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
+            const f32x4 a = *(const f32x4 *)(snap + ((2 * kb) * 64 + l) * 16);
+            const f32x4 b = *(const f32x4 *)(snap + ((2 * kb + 1) * 64 + l) * 16);
+            bf16x4 ah, al, bh, bl;
+            split4(a, ah, al);
+            split4(b, bh, bl);
+            const bf16x8 shi = cat(ah, bh), slo = cat(al, bl);
+            oa = mfma(x.qh[kb], shi, oa);
+            ob = mfma(x.qh[kb], slo, ob);
+            oa = mfma(x.ql[kb], shi, oa);
+        }
+    };
+    auto first = [&](const OutIn &x, int m) {
+        oa = zero;
+        ob = zero;
+        half_qs(x, m, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // snapshot reads done before the next barrier
+    };
+    auto finish = [&](const OutIn &x, int m) {
+        const char *snap = snap_of(m);
+        const bf16x8 vs = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);   // V_new hi | lo
+        half_qs(x, m, 2);
+        const bf16x4 vh = __builtin_shufflevector(vs, vs, 0, 1, 2, 3);
+        const bf16x4 vl = __builtin_shufflevector(vs, vs, 4, 5, 6, 7);
+        ob = mfma(x.pp, cat(vh, vh), ob);
+        ob = mfma(x.pp, cat(vl, z4), ob);
+        const f32x4 o = oa + ob;
+        const int64_t t0 = bos + (int64_t)C * m;
+        const int nc = (int)min<int64_t>(C, eos - t0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    };
+    OutIn X, Y;                      // chunks m = parity + 4i and parity + 4i + 2
+    if (parity < nch) load(X, parity);
+    if (parity + 2 < nch) load(Y, parity + 2);
+    int nb = 0;
+    for (; nb < parity + 1; ++nb) sync();
+    for (int m = parity; m < nch; m += 4) {
+        sync(); ++nb;
+        first(X, m);
+        sync(); ++nb;
+        finish(X, m);
+        if (m + 4 < nch) load(X, m + 4);
+        if (m + 2 >= nch) break;
+        sync(); ++nb;
+        first(Y, m + 2);
+        sync(); ++nb;
+        finish(Y, m + 2);
+        if (m + 6 < nch) load(Y, m + 6);
+    }
+    for (; nb < nch + 2; ++nb) sync();
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    recur_direct_block<NW>(xcd_remap(blockIdx.x, gridDim.x), lds, recs, v, cu, chunk_off, order, N,
+                           T, H, s0, out, sfin, carry, cbeg, cend);
+}
+
+// recurrence over [cbeg, cend) in blocks [0, RB), prep of [pbeg, pend) in the rest
+// (the LDS request, above half a CU's, keeps prep blocks off the recurrence's CUs)
+template <int NW>
+struct DirectPrep {
+    static constexpr int PREP_WAVES = DirectLayout<NW>::WAVES < 4 ? DirectLayout<NW>::WAVES : 4;
+    static constexpr int PREP_BYTES = PREP_WAVES * (int)sizeof(PrepLds);
+    static constexpr int LDS = (DirectLayout<NW>::BYTES > PREP_BYTES ? DirectLayout<NW>::BYTES : PREP_BYTES) >
+                                       80 * 1024
+                                   ? (DirectLayout<NW>::BYTES > PREP_BYTES ? DirectLayout<NW>::BYTES : PREP_BYTES)
+                                   : 80 * 1024 + 1024;
+};
+
+template <int NW>
+__global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_prep_kernel(
+    const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    if ((int)blockIdx.x < RB) {
+        recur_direct_block<NW>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off, order, N,
+                               T, H, s0, out, sfin, carry, cbeg, cend);
+        return;
+    }
+    constexpr int PW = DirectPrep<NW>::PREP_WAVES;
     const int w = threadIdx.x >> 6;
     if (w >= PW) return;
     const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
@@ -878,12 +1213,47 @@ static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
-    switch (waves) {
-    case 101: return launch_recur_prep_t<1, 4>(a, st);
-    case 102: return launch_recur_prep_t<2, 4>(a, st);
-    default: return hipErrorInvalidValue;
+template <int NW>
+static hipError_t launch_recur_direct(const char *recs, const uint16_t *v, const int32_t *cu,
+                                      const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                      int H, const float *s0, float *out, float *sfin, float *carry,
+                                      int cbeg, int cend, hipStream_t st) {
+    constexpr int lds = DirectLayout<NW>::BYTES;
+    auto kern = recur_direct_kernel<NW>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
     }
+    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_recur_direct_prep(const RecurPrepArgs &a, hipStream_t st) {
+    constexpr int PW = DirectPrep<NW>::PREP_WAVES;
+    constexpr int lds = DirectPrep<NW>::LDS;
+    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
+    auto kern = recur_direct_prep_kernel<NW>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
+    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
+    if (pb < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
+                       a.recs, a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin,
+                       a.carry, (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
+                       a.recs, (int)a.pbeg, (int)a.pend);
+    return hipGetLastError();
 }
 
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
@@ -891,8 +1261,20 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
                               const float *s0, float *out, float *sfin, float *carry, int waves,
                               int cbeg, int cend, hipStream_t st) {
     switch (waves) {
-    case 101: return launch_recur_pair<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 102: return launch_recur_pair<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 101: return launch_recur_pair<1, KDA_PAIR_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 102: return launch_recur_pair<2, KDA_PAIR_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
+    switch (waves) {
+    case 101: return launch_recur_prep_t<1, KDA_PAIR_NSLOT>(a, st);
+    case 102: return launch_recur_prep_t<2, KDA_PAIR_NSLOT>(a, st);
+    case 201: return launch_recur_direct_prep<1>(a, st);
+    case 202: return launch_recur_direct_prep<2>(a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -901,7 +1283,7 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: case 102:
+    case 101: case 102: case 201: case 202:
         return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
                                   waves, 0, 1 << 30, st);
     case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
