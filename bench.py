@@ -139,11 +139,14 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
            "calibration_bytes": true_bytes, "kernels": {}}
     kinds = collections.defaultdict(lambda: ([], []))
     for name in fetch:
-        m = re.search(r"kda::(chunk_map|prep|recur|fused)\w*_kernel", name)
+        m = re.search(r"kda::(\w+?)_kernel", name)
         if not m or name not in write:
             continue
-        kinds[m.group(1)][0].extend(fetch[name])
-        kinds[m.group(1)][1].extend(write[name])
+        base = m.group(1)      # e.g. prep, recur_pair, recur_prep, fused, chunk_map
+        kind = ("recur_prep" if base.startswith("recur") and base.endswith("_prep") else
+                "recur" if base.startswith("recur") else base)
+        kinds[kind][0].extend(fetch[name])
+        kinds[kind][1].extend(write[name])
     for kind, (fl, wl) in kinds.items():
         # mean over dispatches: segment launches of one kind cover different chunk ranges
         fb = float(np.mean(fl)) * f_scale
