@@ -224,6 +224,7 @@ def main():
     from chunked_gated_delta_kda_amd import native
     launch_info = native.launch_plan(N, T, H, variant)
     plan = [p[0] for p in launch_info]
+    chunk_len = launch_info[0][3]
     names = list(dict.fromkeys(plan))            # kinds, first-launch order
     ev = HipEvents()
     n_ev = len(plan) + 1
@@ -269,7 +270,8 @@ def main():
     tokens_per_s = T / step_s
 
     # token counts per global chunk range, from the sequence lengths
-    chunk_tokens = np.concatenate([np.minimum(16, L - 16 * np.arange((L + 15) // 16))
+    cl = chunk_len
+    chunk_tokens = np.concatenate([np.minimum(cl, L - cl * np.arange((L + cl - 1) // cl))
                                    for L in w.lengths] + [np.zeros(0, np.int64)]).astype(np.int64)
     csum = np.concatenate([[0], np.cumsum(chunk_tokens)])
     n_ch = len(chunk_tokens)
@@ -293,7 +295,7 @@ def main():
         return b
 
     kind_bytes = {nm: 0 for nm in names}
-    for kind, pr, rr in launch_info:
+    for kind, pr, rr, _ in launch_info:
         kind_bytes[kind] += launch_alg_bytes(kind, pr, rr)
 
     dom = max((nm for nm in names if nm != "chunk_map"), key=lambda nm: kern_ms[nm])
@@ -313,7 +315,7 @@ def main():
            "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta)",
            "config": {"workload": f"{synth.CONFIGS[args.config]['name']} (config {args.config})",
                       "num_seqs": N, "total_tokens": T, "num_heads": H, "dk": 128, "dv": 128,
-                      "chunk": 16, "variant": variant, "initial_state": w.initial_state is not None},
+                      "chunk": chunk_len, "variant": variant, "initial_state": w.initial_state is not None},
            "tflops": round(alg_flops / step_s / 1e12, 2),
            "mfma_bf16_peak_frac": round(alg_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "path_hbm_frac": round(alg_bytes_total / step_s / 1e9 / HBM_PEAK_GBS, 4),

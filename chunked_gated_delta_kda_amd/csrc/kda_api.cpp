@@ -18,7 +18,12 @@ constexpr int KDA_MAX_SEGMENTS = 8;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-int64_t max_chunks(int64_t N, int64_t T) { return (T + KDA_CHUNK - 1) / KDA_CHUNK + N; }
+// chunks of cl tokens: an upper bound over any split of T tokens into N sequences
+int64_t max_chunks(int64_t N, int64_t T, int cl = KDA_CHUNK) { return (T + cl - 1) / cl + N; }
+
+// The recurrence forms 301/302 consume 32-token chunk records; all others 16-token ones.
+int chunk_len(int waves) { return waves >= 300 ? 32 : KDA_CHUNK; }
+size_t rec_bytes(int waves) { return waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES; }
 
 // Workspace: chunk offsets [N+1], sequence order [N], an error word, and (split
 // variant only) a state carry buffer [N, H, 128, 128] fp32 when the chunk range is
@@ -27,7 +32,7 @@ struct Layout {
     size_t chunk_off, order, err, carry, recs, total;
 };
 
-Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments) {
+Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves) {
     Layout L;
     L.chunk_off = 0;
     L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
@@ -38,7 +43,7 @@ Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments) {
     if (variant == KDA_VARIANT_SPLIT) {
         if (segments > 1)
             L.recs = L.carry + (size_t)N * H * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
-        L.total = L.recs + (size_t)max_chunks(N, T) * (size_t)H * (size_t)kda::REC_BYTES;
+        L.total = L.recs + (size_t)max_chunks(N, T, chunk_len(waves)) * (size_t)H * rec_bytes(waves);
     }
     return L;
 }
@@ -65,7 +70,9 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102 || w == 201 || w == 202) return w;
+        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102 || w == 201 || w == 202 || w == 301 ||
+            w == 302)
+            return w;
     }
     // measured on MI355X (bench.py configs): the paired form wins everywhere; one slice
     // per block when chains are very few, two otherwise
@@ -139,19 +146,21 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    const int32_t M = (int32_t)max_chunks(num_seqs, total_tokens);
+    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
+    const int cl = v == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
+    const int32_t M = (int32_t)max_chunks(num_seqs, total_tokens, cl);
     kda_launch_info plan[2 + KDA_MAX_SEGMENTS];
     int n = 0;
-    plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0};
+    plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
-        const int segs = split_segments(num_seqs, num_heads, recur_waves(num_seqs, num_heads));
+        const int segs = split_segments(num_seqs, num_heads, waves);
         auto bound = [&](int sg) { return (int32_t)((int64_t)M * sg / segs); };
-        plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0};
+        plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0, cl};
         for (int sg = 0; sg + 1 < segs; ++sg)
-            plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1)};
-        plan[n++] = {KDA_KERNEL_RECUR, 0, 0, bound(segs - 1), M};
+            plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1), cl};
+        plan[n++] = {KDA_KERNEL_RECUR, 0, 0, bound(segs - 1), M, cl};
     } else {
-        plan[n++] = {KDA_KERNEL_FUSED, 0, M, 0, M};
+        plan[n++] = {KDA_KERNEL_FUSED, 0, M, 0, M, cl};
     }
     for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
     return n;
@@ -163,10 +172,9 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    const int segs = v == KDA_VARIANT_SPLIT
-                         ? split_segments(num_seqs, num_heads, recur_waves(num_seqs, num_heads))
-                         : 1;
-    return ws_layout(num_seqs, total_tokens, num_heads, v, segs).total;
+    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
+    const int segs = v == KDA_VARIANT_SPLIT ? split_segments(num_seqs, num_heads, waves) : 1;
+    return ws_layout(num_seqs, total_tokens, num_heads, v, segs, waves).total;
 }
 
 int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -199,7 +207,9 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int N = num_seqs, T = total_tokens, H = num_heads;
     const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, H) : fused_waves(N, H);
     const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, H, waves) : 1;
-    const Layout lay = ws_layout(N, T, H, chosen, segs);
+    const Layout lay = ws_layout(N, T, H, chosen, segs, waves);
+    const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
+    const bool c32 = cl == 32;
 
     char *ws = nullptr;
     bool owned = false;
@@ -231,23 +241,34 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     };
 
     const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
-    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, st); });
+    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, cl, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
-        const int64_t M = max_chunks(N, T);
+        const int64_t M = max_chunks(N, T, cl);
+        auto prep = [&](int64_t b, int64_t e) {
+            return c32 ? kda::launch_prep32(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, b, e, st)
+                       : kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, b, e, st);
+        };
+        auto recur_range = [&](float *carry, int b, int e) {
+            return c32 ? kda::launch_recur32_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
+                       : kda::launch_recur_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
+        };
         if (segs == 1) {
-            ok = around(st, [&] { return kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, 0, M, st); }) &&
-                 around(st, [&] { return kda::launch_recur(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st); });
+            ok = around(st, [&] { return prep(0, M); }) &&
+                 around(st, [&] {
+                     return waves >= 100 ? recur_range(final_state, 0, 1 << 30)
+                                         : kda::launch_recur(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st);
+                 });
         } else {
             kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cu_seqlens, chunk_off, order,
                                  N, T, H, initial_state, out, final_state,
                                  final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0};
             auto bound = [&](int sg) { return M * sg / segs; };
-            ok = around(st, [&] { return kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, 0, bound(1), st); });
+            ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
                 a.cbeg = bound(sg), a.cend = bound(sg + 1), a.pbeg = bound(sg + 1), a.pend = bound(sg + 2);
-                ok = around(st, [&] { return kda::launch_recur_prep(a, waves, st); });
+                ok = around(st, [&] { return c32 ? kda::launch_recur32_prep(a, waves, st) : kda::launch_recur_prep(a, waves, st); });
             }
-            ok = ok && around(st, [&] { return kda::launch_recur_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, a.carry, waves, (int)bound(segs - 1), (int)M, st); });
+            ok = ok && around(st, [&] { return recur_range(a.carry, (int)bound(segs - 1), (int)M); });
         }
     } else if (ok) {
         ok = around(st, [&] { return kda::launch_fused(q16, k16, v16, g, beta, cu_seqlens, order, N, T, H, scale, initial_state, out, final_state, err, waves, st); });

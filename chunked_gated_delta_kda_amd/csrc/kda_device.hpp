@@ -136,6 +136,34 @@ __host__ __device__ constexpr int egp_index(int r) {
     return ((((r & 15) >> 2) * 16 + 2 * (r >> 4) + ((r & 3) >> 1)) * 2) + (r & 1);
 }
 
+// x broadcast from lane N of each 16-lane row to the whole row
+template <int N>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N,
+                                                              0xf, 0xf, true));
+}
+// state block B (rows 16B + 4g + j) times its decay; e = this lane's pair of the
+// lane-permuted decay vector
+template <int B>
+__device__ __forceinline__ f32x4 decay_block(f32x4 s, f32x2 e) {
+    return f32x4{s[0] * row_bcast<2 * B>(e[0]), s[1] * row_bcast<2 * B>(e[1]),
+                 s[2] * row_bcast<2 * B + 1>(e[0]), s[3] * row_bcast<2 * B + 1>(e[1])};
+}
+
+// decay_block with a block index that is a constant only after unrolling
+__device__ __forceinline__ f32x4 decay_any(int b, f32x4 s, f32x2 e) {
+    switch (b) {
+    case 0: return decay_block<0>(s, e);
+    case 1: return decay_block<1>(s, e);
+    case 2: return decay_block<2>(s, e);
+    case 3: return decay_block<3>(s, e);
+    case 4: return decay_block<4>(s, e);
+    case 5: return decay_block<5>(s, e);
+    case 6: return decay_block<6>(s, e);
+    default: return decay_block<7>(s, e);
+    }
+}
+
 // LDS scratch of one chunk prep (one wave).
 struct alignas(16) PrepLds {
     static constexpr int ROW = 136;    // bf16 per padded token row (128 + 8: spreads banks)
@@ -149,6 +177,7 @@ struct alignas(16) PrepLds {
     __bf16 kpt[D * CROW];              // K+ transposed: [channel][token]
     __bf16 kth[D * CROW];              // K~ hi, transposed
     __bf16 ktl[D * CROW];              // K~ lo, transposed
+    float egs[D];                      // lane-permutation scratch (32-token records)
 };
 
 // 16x16 product N.M, given N^T and M in D layout, split-bf16 on both sides
@@ -190,11 +219,21 @@ __device__ __forceinline__ f32x4 eye_plus(f32x4 M, int lane, float sign) {
 //   t0: first token of the chunk; nc: its length (1..16); rows past nc are
 //   treated as k = q = 0, g = 0, beta = 0, which adds nothing.
 // `rec` may point to global memory or LDS.
-__device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
-                                           const uint16_t *__restrict__ k,
-                                           const float *__restrict__ g,
-                                           const float *__restrict__ beta, int64_t t0, int nc,
-                                           int h, int H, float scale, PrepLds &L, char *rec) {
+// For the two 16-token halves of a 32-token chunk (prep_chunk32):
+//   KTS: K~ is further scaled per key channel by kts (this lane's channel pair): the
+//        first half's K~ then refers to the end of the 32-token chunk;
+//   SB:  W and Q+ are scaled per key channel by the lane-permuted vector ega: the
+//        second half's W and Q+ then refer to the start of the 32-token chunk. The
+//        scaled -W (hi) and Q+ (hi, lo) MFMA operands are also returned in wn_o,
+//        qh_o, ql_o.
+template <bool KTS, bool SB>
+__device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
+                                             const uint16_t *__restrict__ k,
+                                             const float *__restrict__ g,
+                                             const float *__restrict__ beta, int64_t t0, int nc,
+                                             int h, int H, float scale, PrepLds &L, char *rec,
+                                             f32x2 kts, f32x2 ega, bf16x8 (&wn_o)[4],
+                                             bf16x8 (&qh_o)[4], bf16x8 (&ql_o)[4], f32x2 &ec_o) {
     const int l = threadIdx.x & 63;
     const int c0 = 2 * l;            // this lane's two key channels (channel-major phase)
     const int r = l & 15, gq = l >> 4;
@@ -223,6 +262,7 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     }
     // padded rows carry g = 0, so acc is G at the last real token
     const float eC0 = __builtin_amdgcn_exp2f(acc0), eC1 = __builtin_amdgcn_exp2f(acc1);
+    ec_o = f32x2{eC0, eC1};
     *(f32x2 *)(rec + Rec::EG + c0 * 4) = f32x2{eC0, eC1};
     *(f32x2 *)(rec + Rec::EGP + egp_index(c0) * 4) = f32x2{eC0, eC1};   // c0 even: one pair
 
@@ -252,8 +292,8 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
             *(bf16x2 *)&L.qpl[tt * PrepLds::ROW + c0] = lo;
             kpv[u][0] = kp.x;
             kpv[u][1] = kp.y;
-            ktv[u][0] = km.x * eC0;      // K~ = K e^{G_C - G}
-            ktv[u][1] = km.y * eC1;
+            ktv[u][0] = km.x * (KTS ? eC0 * kts.x : eC0);      // K~ = K e^{G_C - G}
+            ktv[u][1] = km.y * (KTS ? eC1 * kts.y : eC1);
         }
 #pragma unroll
         for (int ch = 0; ch < 2; ++ch) {
@@ -336,17 +376,38 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
     for (int b = 0; b < 8; ++b) {
         const bf16x4 a = *(const bf16x4 *)&L.kpt[(16 * b + r) * PrepLds::CROW + 4 * gq];
         Wt[b] = mfma(cat(a, a), tb, f32x4{0.f, 0.f, 0.f, 0.f});   // W[r][16b+4g+j]
+        if (SB) Wt[b] = decay_any(b, Wt[b], ega);
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         const bf16x4 a = to_bf16x4(-Wt[2 * kb]);
         const bf16x4 b = to_bf16x4(-Wt[2 * kb + 1]);
-        *(bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16) = cat(a, b);
+        const bf16x8 wn = cat(a, b);
+        *(bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16) = wn;
         const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
-        *(bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16) =
-            cat(*(const bf16x4 *)&L.qph[o], *(const bf16x4 *)&L.qph[o + 16]);
-        *(bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16) =
-            cat(*(const bf16x4 *)&L.qpl[o], *(const bf16x4 *)&L.qpl[o + 16]);
+        bf16x8 qh = cat(*(const bf16x4 *)&L.qph[o], *(const bf16x4 *)&L.qph[o + 16]);
+        bf16x8 ql = cat(*(const bf16x4 *)&L.qpl[o], *(const bf16x4 *)&L.qpl[o + 16]);
+        if (SB) {
+            // channels 32kb + 4g + j and 32kb + 16 + 4g + j: rows of key blocks 2kb, 2kb+1
+            f32x4 x0, x1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x0[j] = (float)qh[j] + (float)ql[j];
+                x1[j] = (float)qh[4 + j] + (float)ql[4 + j];
+            }
+            x0 = decay_any(2 * kb, x0, ega);
+            x1 = decay_any(2 * kb + 1, x1, ega);
+            bf16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            qh = cat(h0, h1);
+            ql = cat(l0, l1);
+            wn_o[kb] = wn;
+            qh_o[kb] = qh;
+            ql_o[kb] = ql;
+        }
+        *(bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16) = qh;
+        *(bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16) = ql;
     }
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -354,6 +415,105 @@ __device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
         *(bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16) =
             cat(*(const bf16x4 *)&L.kth[o], *(const bf16x4 *)&L.ktl[o]);
     }
+}
+
+__device__ __forceinline__ void prep_chunk(const uint16_t *__restrict__ q,
+                                           const uint16_t *__restrict__ k,
+                                           const float *__restrict__ g,
+                                           const float *__restrict__ beta, int64_t t0, int nc,
+                                           int h, int H, float scale, PrepLds &L, char *rec) {
+    bf16x8 unused[4];
+    f32x2 ec;
+    prep_chunk_t<false, false>(q, k, g, beta, t0, nc, h, H, scale, L, rec, f32x2{1.f, 1.f},
+                               f32x2{1.f, 1.f}, unused, unused, unused, ec);
+}
+
+// ---------------------------------------------------------------- 32-token chunk record
+// A 32-token chunk as two 16-token halves a, b with the block form of the chunked
+// method (T of the whole chunk is block lower triangular with T_aa, T_bb on the
+// diagonal and -T_bb A_ba T_aa below). With D_a = Diag(e^{G_a}) the first half's
+// decay, the recurrence step over the chunk is
+//   V_a = U_a - W_a S
+//   V_b = U_b - (W_b D_a) S - M V_a,            M = W_b K~_a^T = (W_b D_a) K-_a^T
+//   O_a = Q+_a S + P_aa V_a
+//   O_b = (Q+_b D_a) S + P_ba V_a + P_bb V_b,   P_ba = (Q+_b D_a) K-_a^T
+//   S  <- D_a D_b S + (K~_a D_b)^T V_a + K~_b^T V_b
+// where every quantity with a subscript is the 16-token one of its half (gates
+// cumulated from the start of that half). All scale factors are at most 1 except
+// K-_a, whose range is that of a 16-token chunk.
+struct Rec32 {
+    static constexpr int A = 0;                    // Rec of half a (K~ scaled by D_b)
+    static constexpr int B = Rec::BYTES;           // Rec of half b (W, Q+ scaled by D_a)
+    static constexpr int X = 2 * Rec::BYTES;       // cross terms:
+    static constexpr int MN = X;                   //   -M, A operand [b row][a tokens] hi | lo
+    static constexpr int EGP = X + 1024;           //   e^{G_a + G_b}, lane-permuted
+    static constexpr int PX = X + 2048;            //   P_ba hi | lo
+    static constexpr int BYTES = X + 3072;
+};
+
+__device__ __forceinline__ void prep_chunk32(const uint16_t *__restrict__ q,
+                                             const uint16_t *__restrict__ k,
+                                             const float *__restrict__ g,
+                                             const float *__restrict__ beta, int64_t t0, int nc,
+                                             int h, int H, float scale, PrepLds &L, char *rec) {
+    const int l = threadIdx.x & 63, c0 = 2 * l, r = l & 15, gq = l >> 4;
+    const int nca = nc < C ? nc : C, ncb = nc > C ? nc - C : 0;
+    // gate total of the second half on this lane's channel pair (base 2): all loads
+    // issued at once (rows past the end reread a real row and are masked)
+    float gb0 = 0.f, gb1 = 0.f;
+    {
+        f32x2 x[C];
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+            const int tt = t < ncb ? t : 0;
+            x[t] = *(const f32x2 *)(g + ((t0 + (ncb > 0 ? C : 0) + tt) * (int64_t)H + h) * D + c0);
+        }
+#pragma unroll
+        for (int t = 0; t < C; ++t) {
+            gb0 = __builtin_fmaf(t < ncb ? fmaxf(x[t].x, LOWER_BOUND) : 0.f, LOG2E, gb0);
+            gb1 = __builtin_fmaf(t < ncb ? fmaxf(x[t].y, LOWER_BOUND) : 0.f, LOG2E, gb1);
+        }
+    }
+    const f32x2 eb = {__builtin_amdgcn_exp2f(gb0), __builtin_amdgcn_exp2f(gb1)};
+
+    bf16x8 unused[4];
+    f32x2 ea;   // e^{G_a} on this lane's channel pair
+    prep_chunk_t<true, false>(q, k, g, beta, t0, nca, h, H, scale, L, rec + Rec32::A, eb,
+                              f32x2{1.f, 1.f}, unused, unused, unused, ea);
+    *(f32x2 *)(rec + Rec32::EGP + egp_index(c0) * 4) = f32x2{ea.x * eb.x, ea.y * eb.y};
+    // K-_a as an MFMA operand (row = token of a, k-slots = keys in the state permutation)
+    bf16x8 kah[4], kal[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
+        kah[kb] = cat(*(const bf16x4 *)&L.kmh[o], *(const bf16x4 *)&L.kmh[o + 16]);
+        kal[kb] = cat(*(const bf16x4 *)&L.kml[o], *(const bf16x4 *)&L.kml[o + 16]);
+    }
+    // e^{G_a} lane-permuted, through LDS
+    *(f32x2 *)&L.egs[egp_index(c0)] = ea;
+    wave_sync();
+    const f32x2 ega = *(const f32x2 *)&L.egs[2 * l];
+    wave_sync();
+    bf16x8 wnb[4], qhb[4], qlb[4];
+    f32x2 eb_unused;
+    prep_chunk_t<false, true>(q, k, g, beta, t0 + C, ncb, h, H, scale, L, rec + Rec32::B,
+                              f32x2{1.f, 1.f}, ega, wnb, qhb, qlb, eb_unused);
+    // cross terms, transposed products so that the result lands in A-operand layout
+    // (row = token of b, k-slots = tokens of a):  -M^T = K-_a (-W'_b)^T,  P_ba^T = K-_a Q'_b^T
+    f32x4 mt = {0.f, 0.f, 0.f, 0.f}, pt = mt;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        mt = mfma(kah[kb], wnb[kb], mt);
+        mt = mfma(kal[kb], wnb[kb], mt);
+        pt = mfma(kah[kb], qhb[kb], pt);
+        pt = mfma(kah[kb], qlb[kb], pt);
+        pt = mfma(kal[kb], qhb[kb], pt);
+    }
+    bf16x4 hi, lo;
+    split4(mt, hi, lo);
+    *(bf16x8 *)(rec + Rec32::MN + l * 16) = cat(hi, lo);
+    split4(pt, hi, lo);
+    *(bf16x8 *)(rec + Rec32::PX + l * 16) = cat(hi, lo);
 }
 
 // ---------------------------------------------------------------- recurrence

@@ -6,10 +6,18 @@
 
 namespace kda {
 
-constexpr int REC_BYTES = 23552;   // bytes of one chunk record (Rec::BYTES)
+constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
+constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
 
+// chunk offsets of cl-token chunks (cl = 16 or 32), longest-first order, error word reset
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            int32_t *err, hipStream_t st);
+                            int32_t *err, int cl, hipStream_t st);
+
+// 32-token records of chunks [cbeg, cend)
+hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+                         const int32_t *cu, int N, int T, int H, float scale,
+                         const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                         hipStream_t st);
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
@@ -36,6 +44,13 @@ struct RecurPrepArgs {
     int64_t cbeg, cend, pbeg, pend;
 };
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
+// 32-token forms (waves 301: one slice per block, 302: two): recurrence over [cbeg, cend),
+// alone or with the prep of [pbeg, pend) on the idle CUs
+hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
+                                const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                int H, const float *s0, float *out, float *sfin, float *carry,
+                                int waves, int cbeg, int cend, hipStream_t st);
+hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,

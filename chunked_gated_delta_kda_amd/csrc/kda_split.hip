@@ -12,9 +12,15 @@
 namespace kda {
 
 static_assert(Rec::BYTES == REC_BYTES, "record size mismatch");
+static_assert(Rec32::BYTES == REC32_BYTES, "record size mismatch");
+
+// Write-only sink for the output rows of a partial chunk: the output waves store
+// every row unconditionally (rows past the chunk end go here), which keeps their
+// stores out of branches so that the waits for their in-flight loads stay exact.
+__device__ float store_sink[64];
 
 // ---------------------------------------------------------------- chunk map
-// One workgroup. chunk_off[n] = number of 16-token chunks before sequence n
+// One workgroup. chunk_off[n] = number of cl-token chunks before sequence n
 // (chunk_off[N] = total); order[] lists sequences longest first (ties by
 // index) when N <= ORDER_MAX, else in input order.
 constexpr int MAP_THREADS = 256;
@@ -24,7 +30,8 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
                                                                  int N, int T,
                                                                  int32_t *__restrict__ chunk_off,
                                                                  int32_t *__restrict__ order,
-                                                                 int32_t *__restrict__ err) {
+                                                                 int32_t *__restrict__ err,
+                                                                 int cl) {
     __shared__ int32_t part[MAP_THREADS];
     __shared__ int32_t carry;
     const int tid = threadIdx.x;
@@ -35,7 +42,7 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
         int32_t c = 0;
         if (n < N) {
             const int32_t len = cu ? cu[n + 1] - cu[n] : T;
-            c = (len + C - 1) / C;
+            c = (len + cl - 1) / cl;
         }
         part[tid] = c;
         __syncthreads();
@@ -248,19 +255,6 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     }
 }
 
-// x broadcast from lane N of each 16-lane row to the whole row
-template <int N>
-__device__ __forceinline__ float row_bcast(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N,
-                                                              0xf, 0xf, true));
-}
-// state block B (rows 16B + 4g + j) times its decay; e = this lane's pair of the
-// lane-permuted decay vector
-template <int B>
-__device__ __forceinline__ f32x4 decay_block(f32x4 s, f32x2 e) {
-    return f32x4{s[0] * row_bcast<2 * B>(e[0]), s[1] * row_bcast<2 * B>(e[1]),
-                 s[2] * row_bcast<2 * B + 1>(e[0]), s[3] * row_bcast<2 * B + 1>(e[1])};
-}
 
 // ---------------------------------------------------------------- paired recurrence
 // NW 16-column slices per block; per slice one chain wave and two output waves.
@@ -281,6 +275,7 @@ __device__ __forceinline__ f32x4 decay_block(f32x4 s, f32x2 e) {
 #ifndef KDA_PAIR_NSLOT
 #define KDA_PAIR_NSLOT 4   // ring depth of the paired recurrence (chunks)
 #endif
+
 template <int NW>
 struct PairLayout {
     static_assert(NW == 1 || NW == 2, "one or two slices per block");
@@ -358,7 +353,8 @@ __device__ __forceinline__ void recur_pair_block(
 
     if (loader) {
         // ring fill (the vector-memory pipe is busy for most of a chunk's worth of
-        // time; no compute wave waits on it)
+        // time; no compute wave waits on it). Sharing the loads with the idle wave,
+        // one loading wave on each chain wave's SIMD, measured slower.
         auto fill = [&](int it) {
             const int k = it < nch ? it : nch - 1;
             const int64_t t0 = bos + (int64_t)C * k;
@@ -558,13 +554,18 @@ __device__ __forceinline__ void recur_pair_block(
         const int64_t t0 = bos + (int64_t)C * m;
         const int nc = (int)min<int64_t>(C, eos - t0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
+        for (int j = 0; j < 4; ++j) {
+            float *dst = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : store_sink + l;
+            *dst = o[j];
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);
     };
     OutIn X, Y;                      // chunks m = parity + 4i and parity + 4i + 2
-    if (parity < nch) load(X, parity);
-    if (parity + 2 < nch) load(Y, parity + 2);
+    // loads are issued unconditionally (past the end they repeat the last chunk), so
+    // that the compiler can count them exactly in its waits
+    auto cl = [&](int m) { return m < nch ? m : nch - 1; };
+    load(X, cl(parity));
+    load(Y, cl(parity + 2));
     int nb = 0;
     for (; nb < parity + 1; ++nb) sync();
     for (int m = parity; m < nch; m += 4) {
@@ -572,13 +573,13 @@ __device__ __forceinline__ void recur_pair_block(
         first(X, m);
         sync(); ++nb;
         finish(X, m);
-        if (m + 4 < nch) load(X, m + 4);
+        load(X, cl(m + 4));
         if (m + 2 >= nch) break;
         sync(); ++nb;
         first(Y, m + 2);
         sync(); ++nb;
         finish(Y, m + 2);
-        if (m + 6 < nch) load(Y, m + 6);
+        load(Y, cl(m + 6));
     }
     for (; nb < nch + 2; ++nb) sync();
 }
@@ -849,13 +850,18 @@ __device__ __forceinline__ void recur_direct_block(
         const int64_t t0 = bos + (int64_t)C * m;
         const int nc = (int)min<int64_t>(C, eos - t0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
+        for (int j = 0; j < 4; ++j) {
+            float *dst = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : store_sink + l;
+            *dst = o[j];
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);
     };
     OutIn X, Y;                      // chunks m = parity + 4i and parity + 4i + 2
-    if (parity < nch) load(X, parity);
-    if (parity + 2 < nch) load(Y, parity + 2);
+    // loads are issued unconditionally (past the end they repeat the last chunk), so
+    // that the compiler can count them exactly in its waits
+    auto cl = [&](int m) { return m < nch ? m : nch - 1; };
+    load(X, cl(parity));
+    load(Y, cl(parity + 2));
     int nb = 0;
     for (; nb < parity + 1; ++nb) sync();
     for (int m = parity; m < nch; m += 4) {
@@ -863,13 +869,13 @@ __device__ __forceinline__ void recur_direct_block(
         first(X, m);
         sync(); ++nb;
         finish(X, m);
-        if (m + 4 < nch) load(X, m + 4);
+        load(X, cl(m + 4));
         if (m + 2 >= nch) break;
         sync(); ++nb;
         first(Y, m + 2);
         sync(); ++nb;
         finish(Y, m + 2);
-        if (m + 6 < nch) load(Y, m + 6);
+        load(Y, cl(m + 6));
     }
     for (; nb < nch + 2; ++nb) sync();
 }
@@ -917,6 +923,434 @@ __global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_pre
     if (ci >= pend || ci >= chunk_off[N]) return;
     prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
              *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
+}
+
+// ---------------------------------------------------------------- 32-token paired recurrence
+// The paired form (chain, two output waves per slice, loader) over 32-token chunks
+// built from two 16-token halves (Rec32). Per chunk step the chain wave converts
+// and decays the state once and publishes one snapshot for 32 tokens; the ring
+// carries both halves' chain pieces, the cross term -M and the decay of the whole
+// chunk, and the block's 32-row V tile.
+constexpr int C32 = 32;
+
+template <int NW>
+struct Pair32 {
+    static constexpr int VCOLS = 16 * NW;
+    static constexpr int V_LPR = VCOLS * 2 / 16;                  // lanes per V row (16 B each)
+    static constexpr int V_RPL = 64 / V_LPR;                      // V rows per wave load
+    static constexpr int V_LOADS = C32 / V_RPL;
+    static constexpr int SA = 0;                                  // slot: half a's chain pieces
+    static constexpr int SB = Rec::CHAIN;                         //       half b's chain pieces
+    static constexpr int SX = 2 * Rec::CHAIN;                     //       -M, decay (Rec32 X..X+2048)
+    static constexpr int SV = SX + 2048;                          //       V tile [32][VCOLS]
+    static constexpr int SLOT = SV + V_LOADS * 1024;
+    static constexpr int LOADS = 2 * (Rec::CHAIN / 1024) + 2 + V_LOADS;
+    static constexpr int SNAP = 64 * 32 * 4 + 2 * 64 * 16;        // state + V_new of both halves
+    static constexpr int SNAPS = 3;
+    static_assert(V_RPL * V_LOADS == C32, "V tile geometry");
+};
+#ifndef KDA_PAIR32_NSLOT1
+#define KDA_PAIR32_NSLOT1 4
+#endif
+#ifndef KDA_PAIR32_NSLOT2
+#define KDA_PAIR32_NSLOT2 3
+#endif
+
+template <int NW, int NSLOT>
+struct Pair32Lds {
+    static constexpr int BYTES = NSLOT * Pair32<NW>::SLOT + Pair32<NW>::SNAPS * NW * Pair32<NW>::SNAP;
+    static_assert(BYTES <= 160 * 1024, "LDS");
+};
+
+template <int NW, int NSLOT>
+__device__ __forceinline__ void recur_pair32_block(
+    int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
+    const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
+    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    using P = Pair32<NW>;
+    using PL = PairLayout<NW>;     // wave roles
+    constexpr int LOADS = P::LOADS;
+    constexpr int SLOT = P::SLOT;
+    static_assert(NSLOT >= 3, "the chain reads one chunk ahead of the one it computes");
+    static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
+    char *snaps = ring + NSLOT * SLOT;
+
+    constexpr int PARTS = D / (16 * NW);
+    const int part = bid % PARTS;
+    const int sh = bid / PARTS;
+    const int h = sh % H;
+    const int n = order[sh / H];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
+    const bool chain = w < NW;
+    const bool loader = w == PL::LOADER;
+    const bool idle = w == PL::IDLE;
+    const int parity = (w == PL::out_wave(0, 1) || w == PL::out_wave(NW - 1, 1)) ? 1 : 0;
+    const int slice = chain ? w : ((loader || idle) ? 0 : (w == PL::out_wave(0, parity) ? 0 : 1));
+    const int vcol0 = part * P::VCOLS;
+    const int col = vcol0 + slice * 16 + c;
+    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
+    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;
+    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (ci0 >= ci1) {
+        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
+                    sfin[o] = s0 ? s0[o] : 0.f;
+                }
+        }
+        return;
+    }
+    const int nch = ci1 - ci0;
+    const int64_t bos = seq_bos + (int64_t)C32 * (ci0 - seq_c0);
+    const float *sin = ci0 == seq_c0 ? s0 : carry;
+    float *sout = ci1 == seq_c1 ? sfin : carry;
+    auto snap_of = [&](int it) { return snaps + ((it % P::SNAPS) * NW + slice) * P::SNAP; };
+    auto rec_of = [&](int k) { return recs + ((int64_t)(ci0 + k) * H + h) * Rec32::BYTES; };
+    auto sync = [] {
+        __builtin_amdgcn_s_barrier();      // slots it, it+1 ready; slot it-1 released
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const bf16x4 z4 = {};
+
+    if (loader) {
+        auto fill = [&](int it) {
+            const int k = it < nch ? it : nch - 1;
+            const int64_t t0 = bos + (int64_t)C32 * k;
+            const int nc = (int)min<int64_t>(C32, eos - t0);
+            char *slot = ring + (it % NSLOT) * SLOT;
+            const char *rec = rec_of(k);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                constexpr int NA = Rec::CHAIN / 1024;
+                const char *src;
+                int dst;
+                if (i < NA) {
+                    src = rec + Rec32::A + i * 1024;
+                    dst = P::SA + i * 1024;
+                } else if (i < 2 * NA) {
+                    src = rec + Rec32::B + (i - NA) * 1024;
+                    dst = P::SB + (i - NA) * 1024;
+                } else if (i < 2 * NA + 2) {
+                    src = rec + Rec32::X + (i - 2 * NA) * 1024;
+                    dst = P::SX + (i - 2 * NA) * 1024;
+                } else {
+                    const int j = i - 2 * NA - 2;
+                    const int row = j * P::V_RPL + l / P::V_LPR;
+                    const int cc = vcol0 + (l % P::V_LPR) * 8;
+                    const int64_t t = t0 + (row < nc ? row : nc - 1);
+                    __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
+                                                     KDA_LDS(slot + P::SV + j * 1024), 16, 0, 0);
+                    continue;
+                }
+                __builtin_amdgcn_global_load_lds((const void *)(src + l * 16), KDA_LDS(slot + dst), 16, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        for (int it = 0; it < nch; ++it) {
+            wait_vmcnt<(NSLOT - 3) * LOADS>();      // chunks it and it+1 have landed
+            sync();
+            fill(it + NSLOT - 1);
+        }
+        sync();
+        sync();
+        wait_vmcnt<0>();
+        return;
+    }
+
+    if (idle) {
+        for (int it = 0; it < nch + 2; ++it) sync();
+        return;
+    }
+
+    if (chain) {
+        f32x4 S[8];
+        if (sin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = zero;
+        }
+        struct ChainIn {
+            bf16x8 wna[4], wnb[4], tba, tbb, mn;
+            f32x2 e;                          // lane-permuted decay of the whole chunk
+            uint16_t va[4], vb[4];            // V of the two halves, rows 4g+j
+        };
+        auto chain_read = [&](ChainIn &x, int it) {
+            const char *slot = ring + (it % NSLOT) * SLOT;
+            x.tba = *(const bf16x8 *)(slot + P::SA + Rec::TB + l * 16);
+            x.tbb = *(const bf16x8 *)(slot + P::SB + Rec::TB + l * 16);
+            x.mn = *(const bf16x8 *)(slot + P::SX + (Rec32::MN - Rec32::X) + l * 16);
+            x.e = *(const f32x2 *)(slot + P::SX + (Rec32::EGP - Rec32::X) + l * 8);
+            const uint16_t *vt = (const uint16_t *)(slot + P::SV);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x.va[j] = vt[(4 * gq + j) * P::VCOLS + slice * 16 + c];
+                x.vb[j] = vt[(C + 4 * gq + j) * P::VCOLS + slice * 16 + c];
+            }
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                x.wna[kb] = *(const bf16x8 *)(slot + P::SA + Rec::WN + kb * 1024 + l * 16);
+                x.wnb[kb] = *(const bf16x8 *)(slot + P::SB + Rec::WN + kb * 1024 + l * 16);
+            }
+        };
+        auto vcat = [](const uint16_t (&vv)[4]) {
+            uint32_t v0 = vv[0], v1 = vv[1], v2 = vv[2], v3 = vv[3];
+            asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+            return __builtin_bit_cast(bf16x4, (uint2{v0 | (v1 << 16), v2 | (v3 << 16)}));
+        };
+        auto chain_step = [&](const ChainIn &x, int it) {
+            char *snap = snap_of(it);
+            const char *slot = ring + (it % NSLOT) * SLOT;
+            // K~ pieces, read now and used last
+            bf16x8 kta[8], ktb[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                kta[b] = *(const bf16x8 *)(slot + P::SA + Rec::KT + b * 1024 + l * 16);
+                ktb[b] = *(const bf16x8 *)(slot + P::SB + Rec::KT + b * 1024 + l * 16);
+            }
+            bf16x8 shi[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
+            const bf16x4 vina = vcat(x.va), vinb = vcat(x.vb);
+            // U_a - W_a S and U_b - W'_b S
+            f32x4 a0 = mfma(x.wna[0], shi[0], zero), a1 = mfma(x.wna[1], shi[1], zero);
+            f32x4 b0 = mfma(x.wnb[0], shi[0], zero), b1 = mfma(x.wnb[1], shi[1], zero);
+            a0 = mfma(x.wna[2], shi[2], a0);
+            a1 = mfma(x.wna[3], shi[3], a1);
+            b0 = mfma(x.wnb[2], shi[2], b0);
+            b1 = mfma(x.wnb[3], shi[3], b1);
+            a0 = mfma(x.tba, cat(vina, vina), a0);
+            b0 = mfma(x.tbb, cat(vinb, vinb), b0);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
+            bf16x4 vah, val;
+            split4(a0 + a1, vah, val);
+            *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vah, val);
+            // V_b = (U_b - W'_b S) - M V_a
+            f32x4 y = mfma(x.mn, cat(vah, vah), b0 + b1);
+            y = mfma(x.mn, cat(val, z4), y);
+            bf16x4 vbh, vbl;
+            split4(y, vbh, vbl);
+            *(bf16x8 *)(snap + 9 * 64 * 16 + l * 16) = cat(vbh, vbl);
+            S[0] = decay_block<0>(S[0], x.e);
+            S[1] = decay_block<1>(S[1], x.e);
+            S[2] = decay_block<2>(S[2], x.e);
+            S[3] = decay_block<3>(S[3], x.e);
+            S[4] = decay_block<4>(S[4], x.e);
+            S[5] = decay_block<5>(S[5], x.e);
+            S[6] = decay_block<6>(S[6], x.e);
+            S[7] = decay_block<7>(S[7], x.e);
+            const bf16x8 vahh = cat(vah, vah), val0 = cat(val, z4);
+            const bf16x8 vbhh = cat(vbh, vbh), vbl0 = cat(vbl, z4);
+            // four passes over the 8 key blocks: no MFMA waits on the one before it
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = mfma(kta[b], vahh, S[b]);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = mfma(kta[b], val0, S[b]);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = mfma(ktb[b], vbhh, S[b]);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = mfma(ktb[b], vbl0, S[b]);
+        };
+        auto sync_chain = [&] {
+            sync();
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        };
+        ChainIn A, B;
+        sync();
+        chain_read(A, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        for (int it = 0; it < nch; it += 2) {
+            if (it + 1 < nch) chain_read(B, it + 1);
+            chain_step(A, it);
+            if (it + 1 >= nch) break;
+            sync_chain();
+            if (it + 2 < nch) chain_read(A, it + 2);
+            chain_step(B, it + 1);
+            if (it + 2 >= nch) break;
+            sync_chain();
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        sync();
+        sync();
+        if (sout) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+        }
+        return;
+    }
+
+    // ---- output wave: 32-token chunks m = parity, parity + 2, ...
+    struct OutIn {
+        bf16x8 qha[4], qla[4], qhb[4], qlb[4], ppa, ppb, ppx;
+    };
+    auto load = [&](OutIn &x, int m) {
+        const char *rec = rec_of(m);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            x.qha[kb] = *(const bf16x8 *)(rec + Rec32::A + Rec::QH + kb * 1024 + l * 16);
+            x.qla[kb] = *(const bf16x8 *)(rec + Rec32::A + Rec::QL + kb * 1024 + l * 16);
+            x.qhb[kb] = *(const bf16x8 *)(rec + Rec32::B + Rec::QH + kb * 1024 + l * 16);
+            x.qlb[kb] = *(const bf16x8 *)(rec + Rec32::B + Rec::QL + kb * 1024 + l * 16);
+        }
+        x.ppa = *(const bf16x8 *)(rec + Rec32::A + Rec::PP + l * 16);
+        x.ppb = *(const bf16x8 *)(rec + Rec32::B + Rec::PP + l * 16);
+        x.ppx = *(const bf16x8 *)(rec + Rec32::PX + l * 16);
+    };
+    f32x4 oaa = zero, oba = zero, oab = zero, obb = zero;
+    auto half_qs = [&](const OutIn &x, int m, int kb0) {
+        const char *snap = snap_of(m);
+#pragma unroll
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
+            const f32x4 a = *(const f32x4 *)(snap + ((2 * kb) * 64 + l) * 16);
+            const f32x4 b = *(const f32x4 *)(snap + ((2 * kb + 1) * 64 + l) * 16);
+            bf16x4 ah, al, bh, bl;
+            split4(a, ah, al);
+            split4(b, bh, bl);
+            const bf16x8 shi = cat(ah, bh), slo = cat(al, bl);
+            oaa = mfma(x.qha[kb], shi, oaa);
+            oba = mfma(x.qha[kb], slo, oba);
+            oaa = mfma(x.qla[kb], shi, oaa);
+            oab = mfma(x.qhb[kb], shi, oab);
+            obb = mfma(x.qhb[kb], slo, obb);
+            oab = mfma(x.qlb[kb], shi, oab);
+        }
+    };
+    auto first = [&](const OutIn &x, int m) {
+        oaa = zero;
+        oba = zero;
+        oab = zero;
+        obb = zero;
+        half_qs(x, m, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    };
+    auto finish = [&](const OutIn &x, int m) {
+        const char *snap = snap_of(m);
+        const bf16x8 vsa = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);
+        const bf16x8 vsb = *(const bf16x8 *)(snap + 9 * 64 * 16 + l * 16);
+        half_qs(x, m, 2);
+        const bf16x4 vah = __builtin_shufflevector(vsa, vsa, 0, 1, 2, 3);
+        const bf16x4 val = __builtin_shufflevector(vsa, vsa, 4, 5, 6, 7);
+        const bf16x4 vbh = __builtin_shufflevector(vsb, vsb, 0, 1, 2, 3);
+        const bf16x4 vbl = __builtin_shufflevector(vsb, vsb, 4, 5, 6, 7);
+        oba = mfma(x.ppa, cat(vah, vah), oba);
+        oba = mfma(x.ppa, cat(val, z4), oba);
+        obb = mfma(x.ppx, cat(vah, vah), obb);
+        obb = mfma(x.ppx, cat(val, z4), obb);
+        obb = mfma(x.ppb, cat(vbh, vbh), obb);
+        obb = mfma(x.ppb, cat(vbl, z4), obb);
+        const f32x4 oa = oaa + oba, ob = oab + obb;
+        const int64_t t0 = bos + (int64_t)C32 * m;
+        const int nc = (int)min<int64_t>(C32, eos - t0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *da = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : store_sink + l;
+            float *db = C + 4 * gq + j < nc ? out + ((t0 + C + 4 * gq + j) * H + h) * D + col : store_sink + l;
+            *da = oa[j];
+            *db = ob[j];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    };
+    OutIn X, Y;
+    // loads are issued unconditionally (past the end they repeat the last chunk), so
+    // that the compiler can count them exactly in its waits
+    auto cl = [&](int m) { return m < nch ? m : nch - 1; };
+    load(X, cl(parity));
+    load(Y, cl(parity + 2));
+    int nb = 0;
+    for (; nb < parity + 1; ++nb) sync();
+    for (int m = parity; m < nch; m += 4) {
+        sync(); ++nb;
+        first(X, m);
+        sync(); ++nb;
+        finish(X, m);
+        load(X, cl(m + 4));
+        if (m + 2 >= nch) break;
+        sync(); ++nb;
+        first(Y, m + 2);
+        sync(); ++nb;
+        finish(Y, m + 2);
+        load(Y, cl(m + 6));
+    }
+    for (; nb < nch + 2; ++nb) sync();
+}
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair32_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x), ring, recs, v, cu, chunk_off,
+                                  order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+}
+
+// 32-token record of chunk ci (global index), head h
+__device__ __forceinline__ void prep32_one(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                           const float *__restrict__ g, const float *__restrict__ beta,
+                                           const int32_t *__restrict__ cu, int N, int T, int H,
+                                           float scale, const int32_t *__restrict__ chunk_off,
+                                           char *__restrict__ recs, int ci, int h, PrepLds &L) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= ci) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int64_t t0 = bos + (int64_t)C32 * (ci - chunk_off[n]);
+    const int nc = (int)min<int64_t>(C32, eos - t0);
+    prep_chunk32(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * Rec32::BYTES);
+}
+
+__global__ __launch_bounds__(64) void prep32_kernel(const uint16_t *__restrict__ q,
+                                                    const uint16_t *__restrict__ k,
+                                                    const float *__restrict__ g,
+                                                    const float *__restrict__ beta,
+                                                    const int32_t *__restrict__ cu, int N, int T,
+                                                    int H, float scale,
+                                                    const int32_t *__restrict__ chunk_off,
+                                                    char *__restrict__ recs, int cbeg) {
+    __shared__ PrepLds L;
+    const int ci = cbeg + (int)(blockIdx.x / H), h = blockIdx.x % H;
+    if (ci >= chunk_off[N]) return;
+    prep32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
+}
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur32_prep_kernel(
+    const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    if ((int)blockIdx.x < RB) {
+        recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off,
+                                      order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+        return;
+    }
+    constexpr int PW = RecurPrep<NW>::PREP_WAVES;
+    const int w = threadIdx.x >> 6;
+    if (w >= PW) return;
+    const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
+    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
+    if (ci >= pend || ci >= chunk_off[N]) return;
+    prep32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
+               *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
 
 // ---------------------------------------------------------------- key-split recurrence
@@ -1110,9 +1544,9 @@ __global__ __launch_bounds__(64 * DK_WAVES) void recur_dk_kernel(
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            int32_t *err, hipStream_t st) {
+                            int32_t *err, int cl, hipStream_t st) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(MAP_THREADS), 0, st, cu, N, T, chunk_off,
-                       order, err);
+                       order, err, cl);
     return hipGetLastError();
 }
 
@@ -1254,6 +1688,81 @@ static hipError_t launch_recur_direct_prep(const RecurPrepArgs &a, hipStream_t s
                        a.carry, (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
                        a.recs, (int)a.pbeg, (int)a.pend);
     return hipGetLastError();
+}
+
+hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+                         const int32_t *cu, int N, int T, int H, float scale,
+                         const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                         hipStream_t st) {
+    const int64_t blocks = (cend - cbeg) * H;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL(prep32_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N,
+                       T, H, scale, chunk_off, recs, (int)cbeg);
+    return hipGetLastError();
+}
+
+template <int NW, int NSLOT>
+static hipError_t launch_recur_pair32(const char *recs, const uint16_t *v, const int32_t *cu,
+                                      const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                      int H, const float *s0, float *out, float *sfin, float *carry,
+                                      int cbeg, int cend, hipStream_t st) {
+    constexpr int lds = Pair32Lds<NW, NSLOT>::BYTES;
+    auto kern = recur_pair32_kernel<NW, NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+    return hipGetLastError();
+}
+
+template <int NW, int NSLOT>
+static hipError_t launch_recur32_prep_t(const RecurPrepArgs &a, hipStream_t st) {
+    constexpr int PW = RecurPrep<NW>::PREP_WAVES;
+    constexpr int pair = Pair32Lds<NW, NSLOT>::BYTES;
+    constexpr int prep = PW * (int)sizeof(PrepLds);
+    constexpr int lds = pair > prep ? pair : prep;
+    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
+    auto kern = recur32_prep_kernel<NW, NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds) != hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
+    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
+    if (pb < 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * PairLayout<NW>::WAVES), lds, st,
+                       a.recs, a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin,
+                       a.carry, (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
+                       a.recs, (int)a.pbeg, (int)a.pend);
+    return hipGetLastError();
+}
+
+hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
+                                const int32_t *chunk_off, const int32_t *order, int N, int T,
+                                int H, const float *s0, float *out, float *sfin, float *carry,
+                                int waves, int cbeg, int cend, hipStream_t st) {
+    switch (waves) {
+    case 301: return launch_recur_pair32<1, KDA_PAIR32_NSLOT1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 302: return launch_recur_pair32<2, KDA_PAIR32_NSLOT2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
+    switch (waves) {
+    case 301: return launch_recur32_prep_t<1, KDA_PAIR32_NSLOT1>(a, st);
+    case 302: return launch_recur32_prep_t<2, KDA_PAIR32_NSLOT2>(a, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,

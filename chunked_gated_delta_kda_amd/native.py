@@ -29,7 +29,8 @@ class KdaOptions(ctypes.Structure):
 
 class KdaLaunchInfo(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("prep_begin", ctypes.c_int32), ("prep_end", ctypes.c_int32),
-                ("recur_begin", ctypes.c_int32), ("recur_end", ctypes.c_int32)]
+                ("recur_begin", ctypes.c_int32), ("recur_end", ctypes.c_int32),
+                ("chunk_len", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -93,9 +94,10 @@ def error_word_offset(num_seqs):
 
 def launch_plan(num_seqs, total_tokens, num_heads, variant="auto"):
     """Kernel launches one kda_fwd_ex call makes for this shape, in order: a list of
-    (kind name, (prep_begin, prep_end), (recur_begin, recur_end)) in chunk indices."""
+    (kind name, (prep_begin, prep_end), (recur_begin, recur_end), chunk_len), ranges in
+    chunk indices of chunk_len tokens."""
     lib = load_library()
     info = (KdaLaunchInfo * 64)()
     n = lib.kda_launch_plan(num_seqs, total_tokens, num_heads, VARIANTS[variant], info, 64)
-    return [(KERNEL_KINDS[x.kind], (x.prep_begin, x.prep_end), (x.recur_begin, x.recur_end))
+    return [(KERNEL_KINDS[x.kind], (x.prep_begin, x.prep_end), (x.recur_begin, x.recur_end), x.chunk_len)
             for x in info[:n]]

@@ -120,12 +120,13 @@ int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads
 
 /* One kernel launch of a kda_fwd_ex call: its KDA_KERNEL_* kind and the global
  * chunk ranges [begin, end) whose records it prepares and whose recurrence it runs
- * (chunks are numbered sequence by sequence; a range may extend past the last
- * chunk; an empty range is 0, 0). */
+ * (chunks of chunk_len tokens, numbered sequence by sequence; a range may extend
+ * past the last chunk; an empty range is 0, 0). */
 typedef struct kda_launch_info {
     int32_t kind;
     int32_t prep_begin, prep_end;
     int32_t recur_begin, recur_end;
+    int32_t chunk_len;          /* tokens per chunk of these ranges (16 or 32) */
 } kda_launch_info;
 
 /* The kernel launches (in order) a kda_fwd_ex call with this shape and variant makes:

@@ -86,7 +86,9 @@ def test_launch_plan():
         kinds = [p[0] for p in plan]
         assert kinds[:2] == ["chunk_map", "prep"] and kinds[-1] == "recur"
         assert set(kinds[2:-1]) <= {"recur_prep"}
-        M = (T + 15) // 16 + N
+        cl = plan[0][3]
+        assert cl in (16, 32) and all(p[3] == cl for p in plan)
+        M = (T + cl - 1) // cl + N
         # the prep ranges and the recurrence ranges each tile [0, M) in order, and a
         # range's records are prepared in an earlier launch than its recurrence
         preps = [p[1] for p in plan[1:] if p[1] != (0, 0)]
