@@ -103,9 +103,11 @@ int fused_waves(int64_t N, int64_t H) {
         const int w = std::atoi(e);
         if (w == 1 || w == 2 || w == 4) return w;
     }
+    // measured on MI355X: 2 chains (config 1) 1 or 2 slices per block tie; 128 chains
+    // (config 3): 4 slices 0.22 ms, 2 slices 0.34 ms, 1 slice 0.66 ms
     const int64_t chains = N * H;
-    if (chains * 8 <= 512) return 1;
-    if (chains * 4 <= 1024) return 2;
+    if (chains <= 16) return 1;
+    if (chains <= 64) return 2;
     return 4;
 }
 
