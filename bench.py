@@ -2,6 +2,7 @@
 """KDA forward (prefill) benchmark on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--variant auto]
+    python bench.py --decode 256 [--heads 32]     # decode step (kda_decode) instead
 
 A step is one kda_fwd call over the whole synthetic workload (chunk map,
 chunk prep and the sequential recurrence: every kernel of the path) with the
@@ -18,6 +19,10 @@ recurrence of segment s: then a kernel kind has several launches per step, and
 its time is their sum. The CPU baseline is the fp64 oracle on the host cores, timed in
 the same run on the same inputs; it also provides the parity check printed
 with the result.
+
+With --decode N a step is one kda_decode call: one token for each of N sequences,
+the fp32 state updated in place, as in a decode loop; that mode prints its own
+JSON line (decode tokens/s, roofline against HBM for the state traffic).
 """
 import argparse
 import ctypes
@@ -41,7 +46,9 @@ FLOP_PER_TOKEN_HEAD = 121856      # chunked method at C=16: 6 d^2 + 2C(3d + 2d) 
 STATE_BYTES = 128 * 128 * 4       # one (sequence, head) state, fp32
 # algorithmic bytes per token-head that each kernel must move (inputs it reads,
 # outputs it writes); together they are q,k,v bf16 + g fp32 + beta fp32 + o fp32 = 1796 B
-KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796}
+KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796,
+                               "recurrent": 1796}
+DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128, fp32 state)"
 EVENT_EVERY = 4                   # timed steps per step that records kernel events
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -88,11 +95,17 @@ class HipEvents:
         self.made = []
 
 
-def kernel_source_hash():
+# the sources each kernel kind is built and launched from
+_COMMON_SOURCES = ("kda_api.cpp", "kda_launch.hpp")
+KIND_SOURCES = {"recurrent": _COMMON_SOURCES + ("kda_recurrent.hip",)}
+_CHUNKED_SOURCES = _COMMON_SOURCES + ("kda_device.hpp", "kda_split.hip", "kda_fused.hip")
+
+
+def kernel_source_hash(kind):
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_gated_delta_kda_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(KIND_SOURCES.get(kind, _CHUNKED_SOURCES)):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -107,7 +120,7 @@ def measured_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     rec = t.get("kernels", {}).get(kernel)
-    if not rec or rec.get("source_hash") != kernel_source_hash() or rec.get("workload") != workload:
+    if not rec or rec.get("source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -139,11 +152,12 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
            "calibration_bytes": true_bytes, "kernels": {}}
     kinds = collections.defaultdict(lambda: ([], []))
     for name in fetch:
-        m = re.search(r"kda::(\w+?)_kernel", name)
+        m = re.search(r"kda::(?:\(anonymous namespace\)::)?(\w+?)_kernel", name)
         if not m or name not in write:
             continue
         base = m.group(1)      # e.g. prep, recur_pair, recur_prep, fused, chunk_map
-        kind = ("recur_prep" if base.startswith("recur") and base.endswith("_prep") else
+        kind = ("recurrent" if base == "recurrent" else
+                "recur_prep" if base.startswith("recur") and base.endswith("_prep") else
                 "recur" if base.startswith("recur") else base)
         kinds[kind][0].extend(fetch[name])
         kinds[kind][1].extend(write[name])
@@ -151,7 +165,8 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
         # mean over dispatches: segment launches of one kind cover different chunk ranges
         fb = float(np.mean(fl)) * f_scale
         wb = float(np.mean(wl)) * w_scale
-        out["kernels"][kind] = {"workload": workload, "source_hash": kernel_source_hash(),
+        out["kernels"][kind] = {"workload": workload, "source_hash": kernel_source_hash(kind),
+                                "command": command, "fetch_scale": f_scale, "write_scale": w_scale,
                                 "fetch_bytes": fb, "write_bytes": wb, "dispatches": len(fl),
                                 "bytes_per_launch": fb + wb}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -177,6 +192,94 @@ def cpu_baseline(w, threads, gpu_o, gpu_f):
     return dt, par_o, par_f
 
 
+def copy_calibration(args, dev):
+    """A plain device copy of known size: the reference for the HBM byte counters."""
+    import torch
+
+    if not args.copy_calibration:
+        return
+    nbytes = args.copy_calibration << 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 3 x {nbytes} bytes read + written")
+
+
+def bench_decode(args, dev):
+    """Decode step: N sequences, one token each, state updated in place every step."""
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+
+    N, H = args.decode, args.heads
+    log(f"[bench] decode: {N} sequences x {H} heads")
+    w = synth.make_workload([1] * N, H, 1000 + N, with_initial_state=True)
+    w.initial_state *= np.float32(3.0)     # a state of the size a long prefill leaves (RMS ~0.06)
+    d = synth.to_device(w, dev)
+    q, k, v, g, beta = d["q"], d["k"], d["v"], d["g"], d["beta"]
+    # parity of one step from the drawn state (written to a separate buffer)
+    o1, s1 = kda.decode(q, k, v, g, beta, w.scale, d["initial_state"],
+                        state_out=torch.empty_like(d["initial_state"]))
+    torch.cuda.synchronize()
+    o1, s1 = o1.cpu().numpy(), s1.cpu().numpy()
+    state = d["initial_state"].clone()
+    out = torch.empty((N, H, 128), dtype=torch.float32, device=dev)
+
+    def step():
+        kda.decode(q, k, v, g, beta, w.scale, state, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    copy_calibration(args, dev)
+    alg_bytes = N * H * (2 * STATE_BYTES + 1796)
+    achieved = alg_bytes / (launch_ms / 1e3) / 1e9
+    res = {"metric": DECODE_METRIC, "value": round(N / (ms_per_step / 1e3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta/state)",
+           "config": {"workload": f"decode step, {N} sequences x {H} heads", "num_seqs": N,
+                      "num_heads": H, "dk": 128, "dv": 128},
+           "roofline": {"bound": "hbm", "kernel": "recurrent", "achieved": round(achieved, 1),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("recurrent", f"decode{N}x{H}"),
+                        "alg_bytes_per_launch": alg_bytes, "launches_per_step": 1,
+                        "avg_launch_ms": round(launch_ms, 5)},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        import oracle
+        inp = synth.oracle_inputs(w)
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:  # pragma: no cover
+            cores = os.cpu_count() or 1
+        threads = args.cpu_threads or min(16, cores)
+        t0 = time.perf_counter()
+        ro, rf = oracle.kda_forward(**inp, threads=threads)
+        dt = time.perf_counter() - t0
+        po, pf = synth.parity(o1, ro), synth.parity(s1, rf)
+        res["cpu_baseline"] = {"value": round(N / dt, 1), "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"one decode step of the whole batch ({N * H} (sequence, head) "
+                                         f"states), fp64, {dt:.3f} s wall"}
+        res["parity"] = {"o": {k: po[k] for k in ("rel_l2", "max_abs_rms")},
+                         "final_state": {k: pf[k] for k in ("rel_l2", "max_abs_rms")},
+                         "pass": synth.passes(po) and synth.passes(pf)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,7 +287,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=sorted(synth.CONFIGS),
                     help="workload (default 2: fixed-length prefill T=8192, H=32)")
-    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused"])
+    ap.add_argument("--variant", default="auto", choices=["auto", "split", "fused", "recurrent"])
+    ap.add_argument("--decode", type=int, default=0, metavar="N",
+                    help="benchmark the decode step over N sequences instead of a prefill config")
+    ap.add_argument("--heads", type=int, default=32, help="heads of the --decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -196,7 +302,8 @@ def main():
     args = ap.parse_args()
 
     if args.ingest_pmc:
-        ingest_pmc(*args.ingest_pmc, f"config{args.config}", args.pmc_command)
+        workload = f"decode{args.decode}x{args.heads}" if args.decode else f"config{args.config}"
+        ingest_pmc(*args.ingest_pmc, workload, args.pmc_command)
         return
 
     if args.gpus != 1:
@@ -211,6 +318,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.decode:
+        bench_decode(args, dev)
+        return
     log(f"[bench] generating config {args.config}: {synth.CONFIGS[args.config]['name']}")
     w = synth.config_workload(args.config)
     d = synth.to_device(w, dev)
@@ -251,14 +361,7 @@ def main():
         kern_ms[nm] += float(np.mean([ev.ms(e[j], e[j + 1]) for e in sampled]))
     launches = {nm: plan.count(nm) for nm in names}
     ev.close()
-    if args.copy_calibration:
-        nbytes = args.copy_calibration << 20
-        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"[bench] copy calibration: 3 x {nbytes} bytes read + written")
+    copy_calibration(args, dev)
     log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms summed over launches): {kern_ms}; "
         f"launches {launches}")
 
@@ -286,8 +389,8 @@ def main():
         are counted once per step, with the last recurrence launch."""
         if kind == "chunk_map":
             return 4 * (N + 1) + 8 * N
-        if kind == "fused":
-            return TH * KERNEL_BYTES_PER_TOKEN_HEAD["fused"] + states
+        if kind in ("fused", "recurrent"):
+            return TH * KERNEL_BYTES_PER_TOKEN_HEAD[kind] + states
         b = (tokens_in(prep_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["prep"]
              + tokens_in(recur_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["recur"])
         if recur_r[1] >= n_ch and recur_r[1] > recur_r[0]:

@@ -9,7 +9,7 @@ import math
 
 from . import native
 
-__all__ = ["fwd", "workspace_bytes", "select_variant", "version", "native"]
+__all__ = ["fwd", "decode", "workspace_bytes", "select_variant", "version", "native"]
 
 HEAD_DIM = 128
 
@@ -92,3 +92,47 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
                         ctypes.c_void_p(st.cuda_stream), ctypes.byref(opt))
     native.check(rc)
     return out, final_state
+
+
+def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inplace", stream=None):
+    """One recurrence step per sequence (decode) on the current HIP device.
+
+    q, k, v: bf16 [N, H, 128] (one token per sequence); g: fp32 [N, H, 128];
+    beta: fp32 [N, H]; state: fp32 [N, H, 128, 128] or None (zeros).
+    state_out: "inplace" (update ``state``; a new tensor when state is None), None
+    (state not written), or an fp32 [N, H, 128, 128] tensor.
+    Returns (o fp32 [N, H, 128], the updated state or None).
+    """
+    import torch
+
+    lib = native.load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda.decode needs device tensors")
+    N, H, Dk = q.shape
+    if Dk != HEAD_DIM:
+        raise ValueError("head_dim must be 128")
+    for name, t, dt, shape in (("q", q, torch.bfloat16, (N, H, Dk)), ("k", k, torch.bfloat16, (N, H, Dk)),
+                               ("v", v, torch.bfloat16, (N, H, Dk)), ("g", g, torch.float32, (N, H, Dk)),
+                               ("beta", beta, torch.float32, (N, H))):
+        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name}: expected contiguous {dt} {shape} on {dev}, "
+                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    sshape = (N, H, Dk, Dk)
+    for name, t in (("state", state), ("state_out", state_out)):
+        if isinstance(t, torch.Tensor) and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+                                            or not t.is_contiguous() or t.device != dev):
+            raise ValueError(f"{name}: expected contiguous fp32 {sshape} on {dev}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((N, H, Dk), dtype=torch.float32, device=dev)
+    if isinstance(state_out, str):
+        if state_out != "inplace":
+            raise ValueError('state_out: "inplace", None or a tensor')
+        state_out = state if state is not None else torch.empty(sshape, dtype=torch.float32, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), N, H, Dk,
+                        _ptr(state), _ptr(state_out), _ptr(out), ctypes.c_void_p(st.cuda_stream))
+    native.check(rc)
+    return out, state_out

@@ -33,7 +33,8 @@ struct Layout {
 };
 
 Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves) {
-    Layout L;
+    Layout L{};
+    if (variant == KDA_VARIANT_RECURRENT) return L;  // reads cu_seqlens directly, no workspace
     L.chunk_off = 0;
     L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
     L.err = L.order + align_up(sizeof(int32_t) * (size_t)N);
@@ -133,13 +134,19 @@ const char *kda_status_string(int s) {
 }
 
 int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads) {
-    (void)num_seqs;
-    (void)total_tokens;
     (void)num_heads;
     if (const char *e = std::getenv("KDA_VARIANT")) {
         if (!std::strcmp(e, "split")) return KDA_VARIANT_SPLIT;
         if (!std::strcmp(e, "fused")) return KDA_VARIANT_FUSED;
+        if (!std::strcmp(e, "recurrent")) return KDA_VARIANT_RECURRENT;
     }
+    // The token loop costs ~1.2 us per token of the longest sequence (plus ~12 us); the
+    // split variant at least ~34 us, and ~2 us per (sequence, head) chain when the
+    // sequences are short (measured on MI355X, 32 heads). The host cannot see the
+    // lengths, only T and N; with T <= max(16, 2N) even the most skewed split of the
+    // T tokens keeps the token loop ahead of the split variant's time.
+    if ((int64_t)total_tokens <= 16 || (int64_t)total_tokens <= 2 * (int64_t)num_seqs)
+        return KDA_VARIANT_RECURRENT;
     return KDA_VARIANT_SPLIT;
 }
 
@@ -154,6 +161,11 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     const int32_t M = (int32_t)max_chunks(num_seqs, total_tokens, cl);
     kda_launch_info plan[2 + KDA_MAX_SEGMENTS];
     int n = 0;
+    if (v == KDA_VARIANT_RECURRENT) {
+        plan[n++] = {KDA_KERNEL_RECURRENT, 0, 0, 0, 0, 1};
+        for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
+        return n;
+    }
     plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, num_heads, waves);
@@ -190,7 +202,8 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
         return KDA_ERR_UNSUPPORTED;
     if (opt && opt->reserved != 0) return KDA_ERR_UNSUPPORTED;
     const int variant = opt ? opt->variant : KDA_VARIANT_AUTO;
-    if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED)
+    if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED &&
+        variant != KDA_VARIANT_RECURRENT)
         return KDA_ERR_UNSUPPORTED;
     if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
@@ -214,6 +227,28 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
     const bool c32 = cl == 32;
 
+    // profiling events: [0] before the first kernel launch, [i] after the i-th (all on
+    // the caller's stream, where every kernel runs in order)
+    void **ev = n_ev ? opt->stage_events : nullptr;
+    int kidx = 0;
+    auto around = [&](hipStream_t s, auto &&launch) -> bool {
+        if (ev && kidx == 0 && hipEventRecord((hipEvent_t)ev[0], s) != hipSuccess) return false;
+        if (launch() != hipSuccess) return false;
+        ++kidx;
+        if (ev && kidx < n_ev && hipEventRecord((hipEvent_t)ev[kidx], s) != hipSuccess) return false;
+        return true;
+    };
+    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
+
+    if (chosen == KDA_VARIANT_RECURRENT) {
+        const int dvt = kda::recurrent_tile((int64_t)N * H);
+        const bool ok = around(st, [&] {
+            return kda::launch_recurrent(q16, k16, v16, g, beta, scale, cu_seqlens, N, T, H, false, initial_state,
+                                         out, final_state, dvt, st);
+        });
+        return ok ? KDA_OK : KDA_ERR_LAUNCH;
+    }
+
     char *ws = nullptr;
     bool owned = false;
     if (opt && opt->workspace) {
@@ -231,19 +266,6 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     int32_t *err = (int32_t *)(ws + lay.err);
     char *recs = ws + lay.recs;
 
-    // profiling events: [0] before the first kernel launch, [i] after the i-th (all on
-    // the caller's stream, where every kernel runs in order)
-    void **ev = n_ev ? opt->stage_events : nullptr;
-    int kidx = 0;
-    auto around = [&](hipStream_t s, auto &&launch) -> bool {
-        if (ev && kidx == 0 && hipEventRecord((hipEvent_t)ev[0], s) != hipSuccess) return false;
-        if (launch() != hipSuccess) return false;
-        ++kidx;
-        if (ev && kidx < n_ev && hipEventRecord((hipEvent_t)ev[kidx], s) != hipSuccess) return false;
-        return true;
-    };
-
-    const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
     bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, cl, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
@@ -295,6 +317,26 @@ int kda_fwd(const void *q, const void *k, const void *v, const float *g, const f
             float *final_state, void *stream) {
     return kda_fwd_ex(q, k, v, g, beta, scale, cu_seqlens, num_seqs, total_tokens, num_heads,
                       head_dim, initial_state, out, final_state, stream, nullptr);
+}
+
+int kda_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
+               float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+               const float *state_in, float *state_out, float *out, void *stream) {
+    if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+    if (!shape_ok(num_seqs, num_seqs, num_heads)) return KDA_ERR_SHAPE;
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
+    const size_t state_bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    if (state_in && state_out && (const void *)state_in != (const void *)state_out &&
+        overlaps(state_in, state_bytes, state_out, state_bytes))
+        return KDA_ERR_ALIAS;
+    hipStream_t st = (hipStream_t)stream;
+    const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads);
+    if (kda::launch_recurrent((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale,
+                              nullptr, num_seqs, num_seqs, num_heads, true, state_in, out, state_out, dvt,
+                              st) != hipSuccess)
+        return KDA_ERR_LAUNCH;
+    return KDA_OK;
 }
 
 }  // extern "C"

@@ -56,6 +56,15 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st);
 
+// Token-by-token recurrence: one block per (sequence, head, tile of dvt value columns),
+// dvt in {128, 64, 32}. one_token_per_seq: sequence n is token n (decode step, cu unused).
+hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                            const float *beta, float scale, const int32_t *cu, int N, int T, int H,
+                            bool one_token_per_seq, const float *s0, float *out, float *sfin, int dvt,
+                            hipStream_t st);
+// value-column tile of launch_recurrent for this many (sequence, head) chains
+int recurrent_tile(int64_t chains);
+
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                         const float *beta, const int32_t *cu, const int32_t *order, int N, int T,
                         int H, float scale, const float *s0, float *out, float *sfin, int *err,

@@ -1,0 +1,245 @@
+// kda_recurrent.hip -- token-by-token KDA recurrence on gfx950: the decode step
+// (one token per sequence, state in and out) and the recurrent variant of the
+// forward pass (any cu_seqlens, one token after another).
+//
+// One token of the recurrence (smzdm.com, "KDA 内核到底难在哪": per-channel decay
+// over a fixed-size state; nerdleveltech.com, section "سياق Kimi Linear": a decode
+// step costs the same at any context length because the state does not grow) is, with
+// e = exp(max(g, -5)) per key row i and value column j:
+//
+//   S1[i][j] = e_i S[i][j]                     (decay)
+//   u_j      = sum_i k_i S1[i][j]              (what the state predicts for k)
+//   d_j      = beta (v_j - u_j)                (delta-rule correction)
+//   S'[i][j] = S1[i][j] + k_i d_j              (= (I - beta k k^T) S1 + beta k v^T)
+//   o_j      = scale sum_i q_i S'[i][j] = scale (sum_i q_i S1[i][j] + (q.k) d_j)
+//
+// so a step reads and writes the 64 KiB fp32 state once and needs two reductions
+// over the key index (u and sum_i q_i S1) plus q.k. The work per step is a few
+// flops per state element: the decode step is bound by HBM traffic of the state.
+//
+// Block = 256 threads = one (sequence, head, tile of DVT value columns). Thread
+// (cg, rg) owns columns [4cg, 4cg+4) of the tile for key rows rg + RG*m: a wave's
+// float4 load covers 64/CG consecutive rows of the tile, so state traffic is
+// coalesced in whole rows (DVT = 128: 1 KiB per wave instruction). The state tile
+// lives in registers for the whole sequence. Per token: q, k and the decay are
+// staged in LDS (double-buffered: one barrier), the column reductions go through
+// lane shuffles inside a wave and an LDS exchange across the four waves (second
+// barrier), then every thread updates its rows. The next token's inputs are
+// loaded while the current token computes.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "kda.h"
+#include "kda_launch.hpp"
+
+namespace kda {
+namespace {
+
+constexpr int D = KDA_HEAD_DIM;
+constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
+constexpr float LB = KDA_LOWER_BOUND;
+constexpr float LOG2E_R = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// The state is read once and written once per call: nontemporal accesses keep it
+// from evicting reusable lines (measured on MI355X, decode of 256 sequences x 32
+// heads: 0.193 ms against 0.215 ms with ordinary loads and stores).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_state(const float *p) {
+    const f32x4v x = __builtin_nontemporal_load((const f32x4v *)p);
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_state(float *p, float4 x) {
+    const f32x4v y = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(y, (f32x4v *)p);
+}
+
+template <int DVT>
+struct Tile {
+    static constexpr int CG = DVT / 4;  // column groups (float4) per tile
+    static constexpr int RG = NT / CG;  // row groups
+    static constexpr int RPT = D / RG;  // key rows per thread
+    static constexpr int TILES = D / DVT;
+    static_assert(CG <= 64 && 64 % CG == 0, "a wave holds whole row groups");
+};
+
+// Inputs of one token for this thread: q, k, g of key row `tid` (threads < 128),
+// and v (4 columns) and beta for every thread.
+struct TokIn {
+    float q, k, g;
+    uint2 v;
+    float beta;
+};
+
+__device__ __forceinline__ TokIn load_token(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                            const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                            const float *__restrict__ beta, int64_t th, int tid, int col) {
+    TokIn r;
+    const int64_t o = th * D;
+    const int row = tid & (D - 1);  // threads >= 128 load a row they do not use: keeps the loads unconditional
+    r.q = __uint_as_float((uint32_t)q[o + row] << 16);
+    r.k = __uint_as_float((uint32_t)k[o + row] << 16);
+    r.g = g[o + row];
+    r.v = *(const uint2 *)(v + o + col);
+    r.beta = beta[th];
+    return r;
+}
+
+template <int DVT>
+__global__ __launch_bounds__(NT) void recurrent_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
+    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin) {
+    using TL = Tile<DVT>;
+    __shared__ float sq[2][D], sk[2][D], se[2][D];
+    __shared__ float sqk[2][2];
+    __shared__ float4 red[NWAVE][2][TL::CG];
+
+    const int tile = blockIdx.x % TL::TILES;
+    const int nh = blockIdx.x / TL::TILES;
+    const int h = nh % H, n = nh / H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % TL::CG, rg = tid / TL::CG;
+    const int col = tile * DVT + cg * 4;
+
+    // tokens of sequence n, clamped to [0, T] so that malformed cu_seqlens cannot
+    // send an access out of bounds
+    int t0, t1;
+    if (one_token_per_seq) {
+        t0 = n, t1 = n + 1;
+    } else if (cu) {
+        t0 = min(max(cu[n], 0), T);
+        t1 = min(max(cu[n + 1], t0), T);
+    } else {
+        t0 = 0, t1 = T;
+    }
+
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    float4 st[TL::RPT];
+#pragma unroll
+    for (int m = 0; m < TL::RPT; ++m)
+        st[m] = s0 ? load_state(s0 + sbase + (int64_t)(rg + TL::RG * m) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+
+    TokIn cur{};
+    if (t0 < t1) cur = load_token(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
+    for (int t = t0; t < t1; ++t) {
+        const int buf = (t - t0) & 1;
+        const int64_t th = (int64_t)t * H + h;
+        // stage q, k and the decay of this token; q.k per wave
+        if (tid < D) {
+            sq[buf][tid] = cur.q;
+            sk[buf][tid] = cur.k;
+            se[buf][tid] = __builtin_amdgcn_exp2f(fmaxf(cur.g, LB) * LOG2E_R);
+            float p = cur.q * cur.k;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off);
+            if (lane == 0) sqk[buf][wave] = p;
+        }
+        const uint2 vb = cur.v;
+        const float bt = cur.beta;
+        // next token's inputs (the last token reloads itself: loads stay unconditional)
+        const int tn = t + 1 < t1 ? t + 1 : t;
+        cur = load_token(q, k, v, g, beta, (int64_t)tn * H + h, tid, col);
+        __syncthreads();
+
+        // decay, and this thread's part of u = S1^T k and w = S1^T q
+        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
+#pragma unroll
+        for (int m = 0; m < TL::RPT; ++m) {
+            const int r = rg + TL::RG * m;
+            const float e = se[buf][r], kr = sk[buf][r], qr = sq[buf][r];
+            st[m].x *= e, st[m].y *= e, st[m].z *= e, st[m].w *= e;
+            u.x = fmaf(kr, st[m].x, u.x), u.y = fmaf(kr, st[m].y, u.y);
+            u.z = fmaf(kr, st[m].z, u.z), u.w = fmaf(kr, st[m].w, u.w);
+            w.x = fmaf(qr, st[m].x, w.x), w.y = fmaf(qr, st[m].y, w.y);
+            w.z = fmaf(qr, st[m].z, w.z), w.w = fmaf(qr, st[m].w, w.w);
+        }
+        // sum over the row groups of this wave (lanes that differ in the rg bits)
+#pragma unroll
+        for (int off = TL::CG; off < 64; off <<= 1) {
+            u.x += __shfl_xor(u.x, off), u.y += __shfl_xor(u.y, off);
+            u.z += __shfl_xor(u.z, off), u.w += __shfl_xor(u.w, off);
+            w.x += __shfl_xor(w.x, off), w.y += __shfl_xor(w.y, off);
+            w.z += __shfl_xor(w.z, off), w.w += __shfl_xor(w.w, off);
+        }
+        if (lane < TL::CG) {
+            red[wave][0][lane] = u;
+            red[wave][1][lane] = w;
+        }
+        __syncthreads();
+        u = red[0][0][cg], w = red[0][1][cg];
+#pragma unroll
+        for (int x = 1; x < NWAVE; ++x) {
+            const float4 a = red[x][0][cg], b = red[x][1][cg];
+            u.x += a.x, u.y += a.y, u.z += a.z, u.w += a.w;
+            w.x += b.x, w.y += b.y, w.z += b.z, w.w += b.w;
+        }
+        const float qk = sqk[buf][0] + sqk[buf][1];
+        float4 dl;
+        dl.x = bt * (bf16_lo(vb.x) - u.x), dl.y = bt * (bf16_hi(vb.x) - u.y);
+        dl.z = bt * (bf16_lo(vb.y) - u.z), dl.w = bt * (bf16_hi(vb.y) - u.w);
+#pragma unroll
+        for (int m = 0; m < TL::RPT; ++m) {
+            const float kr = sk[buf][rg + TL::RG * m];
+            st[m].x = fmaf(kr, dl.x, st[m].x), st[m].y = fmaf(kr, dl.y, st[m].y);
+            st[m].z = fmaf(kr, dl.z, st[m].z), st[m].w = fmaf(kr, dl.w, st[m].w);
+        }
+        if (rg == 0) {
+            float4 o;
+            o.x = scale * fmaf(qk, dl.x, w.x), o.y = scale * fmaf(qk, dl.y, w.y);
+            o.z = scale * fmaf(qk, dl.z, w.z), o.w = scale * fmaf(qk, dl.w, w.w);
+            *(float4 *)(out + th * D + col) = o;
+        }
+    }
+    if (sfin) {
+#pragma unroll
+        for (int m = 0; m < TL::RPT; ++m) store_state(sfin + sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+    }
+}
+
+}  // namespace
+
+int recurrent_tile(int64_t chains) {
+    // KDA_RECURRENT_TILE (128, 64 or 32) overrides the choice, for tuning
+    if (const char *e = std::getenv("KDA_RECURRENT_TILE")) {
+        const int t = std::atoi(e);
+        if (t == 128 || t == 64 || t == 32) return t;
+    }
+    // measured on MI355X (decode, 32 heads; GB/s of state traffic): 256 sequences:
+    // 128 columns 5,625, 64 columns 5,646, 32 columns 5,345; 1024 sequences: 5,452,
+    // 5,516, 5,240. Below 1024 chains the narrow tile gives more blocks.
+    if (chains >= 1024) return 64;
+    return 32;
+}
+
+hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                            const float *beta, float scale, const int32_t *cu, int N, int T, int H,
+                            bool one_token_per_seq, const float *s0, float *out, float *sfin, int dvt,
+                            hipStream_t st) {
+    const int64_t chains = (int64_t)N * H;
+    const dim3 block(NT);
+    switch (dvt) {
+    case 128:
+        hipLaunchKernelGGL(recurrent_kernel<128>, dim3((unsigned)(chains * Tile<128>::TILES)), block, 0, st,
+                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
+        break;
+    case 64:
+        hipLaunchKernelGGL(recurrent_kernel<64>, dim3((unsigned)(chains * Tile<64>::TILES)), block, 0, st,
+                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
+        break;
+    case 32:
+        hipLaunchKernelGGL(recurrent_kernel<32>, dim3((unsigned)(chains * Tile<32>::TILES)), block, 0, st,
+                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kda

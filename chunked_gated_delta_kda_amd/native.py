@@ -13,12 +13,12 @@ LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(PKG, "libkda.so")
 KDA_OK = 0
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
           4: "KDA_ERR_ALLOC", 5: "KDA_ERR_LAUNCH", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_ALIAS"}
-VARIANTS = {"auto": 0, "split": 1, "fused": 2}
+VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 
 #: every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
-           "kda_launch_plan", "kda_status_string", "kda_version")
-KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep"}
+           "kda_launch_plan", "kda_decode", "kda_status_string", "kda_version")
+KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent"}
 
 
 class KdaOptions(ctypes.Structure):
@@ -68,6 +68,8 @@ def load_library(path=LIB_PATH):
     lib.kda_select_variant.restype = ctypes.c_int
     lib.kda_launch_plan.argtypes = [i32, i32, i32, i32, ctypes.POINTER(KdaLaunchInfo), i32]
     lib.kda_launch_plan.restype = ctypes.c_int32
+    lib.kda_decode.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, i32, i32, i32, f32p, f32p, f32p, vp]
+    lib.kda_decode.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

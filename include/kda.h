@@ -49,7 +49,8 @@ typedef enum kda_status {
 typedef enum kda_variant {
     KDA_VARIANT_AUTO = 0,  /* library picks by shape                                   */
     KDA_VARIANT_SPLIT = 1, /* chunk-parallel prep kernel + sequential recurrence kernel */
-    KDA_VARIANT_FUSED = 2  /* one kernel: prep produced on chip, feeding the recurrence */
+    KDA_VARIANT_FUSED = 2, /* one kernel: prep produced on chip, feeding the recurrence */
+    KDA_VARIANT_RECURRENT = 3 /* token by token, no chunking: for sequences of a few tokens */
 } kda_variant;
 
 #define KDA_MAX_STAGE_EVENTS 64
@@ -60,6 +61,7 @@ typedef enum kda_variant {
 #define KDA_KERNEL_RECUR 2
 #define KDA_KERNEL_FUSED 3
 #define KDA_KERNEL_RECUR_PREP 4   /* recurrence over one chunk range + prep of the next */
+#define KDA_KERNEL_RECURRENT 5    /* token-by-token recurrence (no chunk ranges)          */
 
 typedef struct kda_options {
     int32_t variant;        /* kda_variant                                              */
@@ -136,6 +138,36 @@ typedef struct kda_launch_info {
  * of segment s+1 inside the launch that runs the recurrence of segment s. */
 int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                         int32_t variant, kda_launch_info *info, int32_t max_launches);
+
+/*
+ * kda_decode -- one recurrence step per sequence: the decode step that continues
+ * from a prefill's final_state. Sequence n has exactly one token, at row n of the
+ * token-major inputs, so the operation is that of kda_fwd with cu_seqlens =
+ * [0, 1, ..., N] (same formula as at the top of this file). A step costs the same
+ * at any context length because the state has a fixed size (nerdleveltech.com,
+ * section "سياق Kimi Linear", on Kimi Linear's decoding; smzdm.com, "KDA 内核到底难在哪",
+ * on the fixed-size state): its cost is one read and one write of the fp32 state,
+ * 64 KiB each per (sequence, head).
+ *
+ *   q, k, v     bf16 [num_seqs, num_heads, 128]
+ *   g           fp32 [num_seqs, num_heads, 128] natural-log decay; below -5 acts as -5
+ *   beta        fp32 [num_seqs, num_heads]
+ *   scale       finite output scale
+ *   num_seqs N >= 1;  num_heads H >= 1;  head_dim == 128
+ *   state_in    fp32 [N, H, 128(key), 128(value)] or NULL (zeros)
+ *   state_out   fp32 [N, H, 128, 128] or NULL (not written); may be the same
+ *               pointer as state_in (updated in place) but must not otherwise
+ *               overlap it
+ *   out         fp32 [N, H, 128]
+ *   stream      hipStream_t or NULL
+ *
+ * Needs no workspace and allocates nothing. Returns KDA_OK or a kda_status code
+ * (host-side checks, before anything is enqueued; KDA_ERR_LAUNCH if the launch
+ * fails). Inputs are not modified (except state_in when it is state_out).
+ */
+int kda_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
+               float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+               const float *state_in, float *state_out, float *out, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);

@@ -72,11 +72,30 @@ def test_validation_errors(lib):
     assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + 64)) == 7
 
 
+def decode_call(lib, **over):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.088, N=4, H=2, D=128, s_in=None, s_out=P, out=P)
+    a.update(over)
+    return lib.kda_decode(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["N"], a["H"],
+                          a["D"], a["s_in"], a["s_out"], a["out"], None)
+
+
+def test_decode_validation_errors(lib):
+    assert decode_call(lib, D=64) == 3
+    assert decode_call(lib, scale=float("nan")) == 3
+    assert decode_call(lib, N=0) == 2
+    assert decode_call(lib, H=0) == 2
+    assert decode_call(lib, q=None) == 1
+    assert decode_call(lib, g=None) == 1
+    assert decode_call(lib, out=None) == 1
+    assert decode_call(lib, s_in=ctypes.c_void_p(4096), s_out=ctypes.c_void_p(4096 + 64)) == 7
+
+
 def test_workspace_bytes(lib):
     assert lib.kda_workspace_bytes(0, 16, 1, 1) == 0
     b = lib.kda_workspace_bytes(1, 8192, 32, 1)
     assert b >= (8192 // 16) * 32 * 23552
-    assert lib.kda_select_variant(1, 8192, 32) in (1, 2)
+    assert lib.kda_select_variant(1, 8192, 32) in (1, 2, 3)
+    assert lib.kda_workspace_bytes(1, 8192, 32, 3) == 0    # the recurrent variant needs none
 
 
 def test_launch_plan():
@@ -103,3 +122,4 @@ def test_launch_plan():
                 assert any(a <= lo for a, _ in covered) and max(b for _, b in covered) >= hi
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []
+    assert [p[0] for p in nat.launch_plan(8, 8192, 16, "recurrent")] == ["recurrent"]

@@ -13,7 +13,7 @@ from kda_check import compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["split", "fused"]
+VARIANTS = ["split", "fused", "recurrent"]
 
 
 def _say(*a):
