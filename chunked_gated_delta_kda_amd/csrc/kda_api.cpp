@@ -63,23 +63,30 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 
-// Recurrence block shape. 1, 2 or 4: waves per block, each owning 16 value columns
-// (many chains: four waves share each chunk record through one LDS ring). 0: the
-// key-split form, four waves per 16-column slice. 101, 102: the paired form (1 or 2
-// slices per block, a chain wave and two output waves per slice, one loader wave).
+// Recurrence block shape. 9: per chain, paired or eight-wave (below). 1, 2, 4 or 8:
+// waves per block, each owning 16 value columns
+// and forming its own outputs; the block's waves share each chunk record through one
+// LDS ring (3 chunks deep for 4 waves, 2 for 8; 42 and 83 are the other depths). 0:
+// the key-split form, four waves per 16-column slice. 101, 102: the paired form (1 or
+// 2 slices per block, a chain wave and two output waves per slice, one loader wave).
 // KDA_RECUR_WAVES overrides the choice, for tuning.
 int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 101 || w == 102 || w == 201 || w == 202 || w == 301 ||
-            w == 302)
+        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 42 || w == 8 || w == 83 || w == 9 || w == 101 ||
+            w == 102 || w == 201 || w == 202 || w == 301 || w == 302)
             return w;
     }
-    // measured on MI355X (bench.py configs): the paired form wins everywhere; one slice
-    // per block when chains are very few, two otherwise
+    // measured on MI355X (ms; paired 102 | eight-wave 8): 128 chains (8 x 1024 tokens,
+    // 16 heads) 0.181 | 0.205; 192 chains 0.476 | 0.478; 512 chains of 2048 tokens
+    // 1.23 | 1.00; 8192 chains of 64 tokens 1.18 | 0.72; but 384 chains of skewed
+    // lengths (12 sequences, 32768 tokens, 32 heads) 1.29 | 2.43, where the longest
+    // chain sets the end time. From 192 chains the hybrid (9) picks per chain on the
+    // device: paired for chains longer than a CU's balanced share, eight-wave otherwise.
     const int64_t chains = N * H;
     if (chains <= 16) return 101;
-    return 102;
+    if (chains < 192) return 102;
+    return 9;
 }
 
 // Number of chunk-range segments of the split variant. With S > 1 the launches are

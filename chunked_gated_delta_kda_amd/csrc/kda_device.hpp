@@ -103,12 +103,25 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
     return __builtin_bit_cast(bf16x4, (uint2{pack2(x[0], x[1]), pack2(x[2], x[3])}));
 }
 
-// Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8). Return a
-// logical index such that consecutive logical indices share an XCD (and its L2).
-__device__ __forceinline__ int xcd_remap(int b, int nb) {
-    const int per = nb >> 3, rem = nb & 7;
-    const int x = b & 7, i = b >> 3;
-    return x * per + (x < rem ? x : rem) + i;
+// Blocks are handed to the 8 XCDs round-robin (block b -> XCD b % 8), in increasing
+// b. The logical index is chain * parts + part (parts blocks per (sequence, head)
+// chain, chains in priority order, longest sequence first). Chains are dealt to the
+// XCDs in turn, eight at a time: the first chains spread over the whole chip and start
+// first, and the blocks of one chain share an XCD (and its L2, where they all read
+// that chain's records). A chain-contiguous range per XCD would instead pile the
+// longest chains onto one XCD's CUs.
+__device__ __forceinline__ int xcd_remap(int b, int nb, int parts) {
+    const int chains = nb / parts;
+    const int full = chains >> 3;                // complete groups of eight chains
+    const int g = b / (8 * parts);
+    if (g < full) {
+        const int j = b - g * 8 * parts;
+        return ((g << 3) + (j & 7)) * parts + (j >> 3);
+    }
+    const int r = chains - (full << 3);          // chains of the last group (1..7)
+    if (r <= 0 || b >= nb) return b;
+    const int j = b - full * 8 * parts;
+    return ((full << 3) + j % r) * parts + j / r;
 }
 
 // ---------------------------------------------------------------- chunk record

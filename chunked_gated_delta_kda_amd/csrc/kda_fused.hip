@@ -64,7 +64,7 @@ __global__ __launch_bounds__(64 * (NW + NP)) void fused_kernel(
     int *failed = done + NSLOT;
 
     constexpr int PARTS = D / (16 * NW);
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bid = xcd_remap(blockIdx.x, gridDim.x, PARTS);
     const int part = bid % PARTS;
     const int sh = bid / PARTS;
     const int h = sh % H;

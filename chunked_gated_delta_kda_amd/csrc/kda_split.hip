@@ -118,7 +118,7 @@ __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q
 // stream through an NSLOT-deep LDS ring filled by direct global->LDS loads
 // (no registers held while in flight), NSLOT-1 chunks ahead of the compute.
 // Blocks of one (sequence, head) get consecutive logical ids; xcd_remap keeps
-// them on one XCD so they share the record reads in L2.
+// them on one XCD so they share the record reads in L2, and deals chains to XCDs in turn.
 template <int NW>
 struct Ring {
     static constexpr int REC_LOADS = Rec::BYTES / 1024;              // 1 KiB wave loads
@@ -151,7 +151,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 #define KDA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Issue this wave's share of the loads of one chunk (record + V tile) into an LDS slot.
-template <int NW>
+// (NSLOT only makes each ring shape its own specialization: clang's host pass rejects a
+// second instantiation of this device template from another kernel specialization.)
+template <int NW, int NSLOT>
 __device__ __forceinline__ void ring_fill(char *slot, const char *rec, const uint16_t *v,
                                           int64_t t0, int nc, int h, int H, int vcol0) {
     using R = Ring<NW>;
@@ -174,27 +176,42 @@ __device__ __forceinline__ void ring_fill(char *slot, const char *rec, const uin
     }
 }
 
+// Loads of a sequence's chunk `it` (of nch) into its ring slot. Every chunk index past
+// the end is clamped to the last chunk (a harmless reload into a slot nobody reads) so
+// that each wave issues the same loads per step.
 template <int NW, int NSLOT>
+__device__ __forceinline__ void ring_fill_chunk(char *ring, int it, int nch, int64_t bos, int64_t eos, int ci0,
+                                                const char *recs, const uint16_t *v, int h, int H, int vcol0) {
+    const int k = it < nch ? it : nch - 1;
+    const int64_t t0 = bos + (int64_t)C * k;
+    ring_fill<NW, NSLOT>(ring + (it % NSLOT) * Ring<NW>::SLOT, recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES, v, t0,
+                  (int)min<int64_t>(C, eos - t0), h, H, vcol0);
+}
+
+template <int NW, int NSLOT, int W = 0>
 __device__ __forceinline__ void ring_wait(int w) {
     // own loads of the chunk about to be consumed are done once at most the
-    // loads of the NSLOT-2 younger chunks are still outstanding
+    // loads of the NSLOT-2 younger chunks are still outstanding (wave W issues
+    // loads_of(W) loads per chunk; w is uniform across the wave)
     using R = Ring<NW>;
-    if (w == 0) wait_vmcnt<(NSLOT - 2) * R::loads_of(0)>();
-    else if (NW > 1 && w == NW - 1) wait_vmcnt<(NSLOT - 2) * R::loads_of(NW > 1 ? NW - 1 : 0)>();
-    else wait_vmcnt<(NSLOT - 2) * R::loads_of(NW > 2 ? 1 : 0)>();
+    if constexpr (W + 1 < NW) {
+        if (w != W) {
+            ring_wait<NW, NSLOT, W + 1>(w);
+            return;
+        }
+    }
+    wait_vmcnt<(NSLOT - 2) * R::loads_of(W)>();
 }
 
 template <int NW, int NSLOT>
-__global__ __launch_bounds__(64 * NW) void recur_kernel(
-    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+__device__ __forceinline__ void recur_ring_block(
+    int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
+    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
+    int N, int T, int H, const float *s0, float *__restrict__ out, float *sfin) {
     using R = Ring<NW>;
     static_assert(NSLOT >= 2, "ring needs two slots");
     static_assert(R::loads_of(0) - R::loads_of(NW - 1) <= 1, "unbalanced ring loads");
-    extern __shared__ __attribute__((aligned(16))) char ring[];
     constexpr int PARTS = D / (16 * NW);
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
     const int part = bid % PARTS;
     const int sh = bid / PARTS;
     const int h = sh % H;
@@ -218,22 +235,15 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     }
 
     const int nch = ci1 - ci0;
-    // every chunk index past the end is clamped to the last chunk (a harmless reload
-    // into a slot nobody reads) so that each wave issues the same loads per step
-    auto fill = [&](int it) {
-        const int k = it < nch ? it : nch - 1;
-        const int64_t t0 = bos + (int64_t)C * k;
-        ring_fill<NW>(ring + (it % NSLOT) * R::SLOT, recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES,
-                      v, t0, (int)min<int64_t>(C, eos - t0), h, H, vcol0);
-    };
     if (nch > 0) {
 #pragma unroll
-        for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        for (int it = 0; it < NSLOT - 1; ++it)
+            ring_fill_chunk<NW, NSLOT>(ring, it, nch, bos, eos, ci0, recs, v, h, H, vcol0);
         for (int it = 0; it < nch; ++it) {
             ring_wait<NW, NSLOT>(w);
             __builtin_amdgcn_s_barrier();         // all waves: slot it ready, slot it-1 released
             __builtin_amdgcn_sched_barrier(0);
-            fill(it + NSLOT - 1);
+            ring_fill_chunk<NW, NSLOT>(ring, it + NSLOT - 1, nch, bos, eos, ci0, recs, v, h, H, vcol0);
             __builtin_amdgcn_sched_barrier(0);
             const char *slot = ring + (it % NSLOT) * R::SLOT;
             StepIn st;
@@ -253,6 +263,16 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) sfin[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
     }
+}
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * NW) void recur_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    recur_ring_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
+                                order, N, T, H, s0, out, sfin);
 }
 
 
@@ -597,8 +617,46 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair_kernel(
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
-    recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x), ring, recs, v, cu, chunk_off,
+    recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
                                 order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+}
+
+// ---------------------------------------------------------------- per-chain choice of shape
+// Many chains of unequal length: the paired form has the lowest latency per chunk but
+// holds a CU per 32 columns of one chain; the eight-wave ring form (one block per
+// chain, each wave forming its own outputs) moves more chain-chunks per CU but takes
+// ~3x longer per chunk. The chains that set the end time are those longer than the
+// balanced share of a CU, (all chains' chunks) / 256 CUs: they get four paired blocks
+// (two 16-column slices each), every other chain one eight-wave block. Sequences come
+// longest first, so the long chains are the first L of the order and their blocks are
+// dispatched first. The grid is sized for the case where every chain is long; blocks
+// past the ones in use exit at the end of the grid (spare blocks interleaved with
+// working ones were measured to halve the working blocks' throughput).
+constexpr int HYBRID_RING = 4;   // ring depth of the eight-wave blocks (fits in the paired block's LDS)
+
+template <int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<2>::WAVES) void recur_hybrid_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin) {
+    static_assert(PairLayout<2>::WAVES == 8, "both shapes run eight waves");
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int64_t share = ((int64_t)chunk_off[N] * H + 255) / 256;
+    int nlong = 0;   // sequences with more chunks than the share (the same count in every block)
+    for (int base = 0; base < N; base += 64 * PairLayout<2>::WAVES) {
+        const int s = base + (int)threadIdx.x;
+        nlong += __syncthreads_count(s < N && chunk_off[s + 1] - chunk_off[s] > share);
+    }
+    const int L = nlong * H;              // long chains: the first L in chain order
+    const int NH = N * H;
+    const int b = blockIdx.x;
+    if (b < 4 * L) {
+        recur_pair_block<2, NSLOT>(xcd_remap(b, 4 * L, 4), lds, recs, v, cu, chunk_off, order, N, T, H, s0, out,
+                                   sfin, sfin, 0, 1 << 30);
+    } else if (b < 4 * L + (NH - L)) {
+        recur_ring_block<8, HYBRID_RING>(L + xcd_remap(b - 4 * L, NH - L, 1), lds, recs, v, cu, chunk_off, order,
+                                         N, T, H, s0, out, sfin);
+    }
 }
 
 // ---------------------------------------------------------------- recurrence + next prep
@@ -622,7 +680,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_prep_kernel(
     const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
-        recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off,
+        recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
                                     order, N, T, H, s0, out, sfin, carry, cbeg, cend);
         return;
     }
@@ -886,7 +944,7 @@ __global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_ker
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    recur_direct_block<NW>(xcd_remap(blockIdx.x, gridDim.x), lds, recs, v, cu, chunk_off, order, N,
+    recur_direct_block<NW>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), lds, recs, v, cu, chunk_off, order, N,
                            T, H, s0, out, sfin, carry, cbeg, cend);
 }
 
@@ -911,7 +969,7 @@ __global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_pre
     const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
-        recur_direct_block<NW>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off, order, N,
+        recur_direct_block<NW>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off, order, N,
                                T, H, s0, out, sfin, carry, cbeg, cend);
         return;
     }
@@ -1294,7 +1352,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair32_kerne
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
-    recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x), ring, recs, v, cu, chunk_off,
+    recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
                                   order, N, T, H, s0, out, sfin, carry, cbeg, cend);
 }
 
@@ -1339,7 +1397,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur32_prep_kerne
     const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
-        recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB), lds, recs_in, v, cu, chunk_off,
+        recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
                                       order, N, T, H, s0, out, sfin, carry, cbeg, cend);
         return;
     }
@@ -1415,7 +1473,7 @@ __global__ __launch_bounds__(64 * DK_WAVES) void recur_dk_kernel(
     f32x4 *xch = (f32x4 *)(ring + L::XCH);
     f32x4 *xo = (f32x4 *)(ring + L::XO);
 
-    const int bid = xcd_remap(blockIdx.x, gridDim.x);
+    const int bid = xcd_remap(blockIdx.x, gridDim.x, 8);
     const int tile = bid % 8;
     const int sh = bid / 8;
     const int h = sh % H;
@@ -1620,6 +1678,27 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
     return hipGetLastError();
 }
 
+static hipError_t launch_recur_hybrid(const char *recs, const uint16_t *v, const int32_t *cu,
+                                      const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
+                                      const float *s0, float *out, float *sfin, hipStream_t st) {
+    constexpr int pair = PairLds<2, KDA_PAIR_NSLOT>::BYTES;
+    constexpr int ring = HYBRID_RING * Ring<8>::SLOT;
+    constexpr int lds = pair > ring ? pair : ring;
+    static_assert(lds <= 160 * 1024, "LDS");
+    auto kern = recur_hybrid_kernel<KDA_PAIR_NSLOT>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
+            hipSuccess)
+            return hipErrorInvalidValue;
+        attr_set = true;
+    }
+    const int64_t blocks = (int64_t)N * H * 4;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<2>::WAVES), lds, st, recs, v, cu,
+                       chunk_off, order, N, T, H, s0, out, sfin);
+    return hipGetLastError();
+}
+
 template <int NW, int NSLOT>
 static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     constexpr int PW = RecurPrep<NW>::PREP_WAVES;
@@ -1799,6 +1878,10 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
     case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 4: return launch_recur_t<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 42: return launch_recur_t<4, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 8: return launch_recur_t<8, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 83: return launch_recur_t<8, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
+    case 9: return launch_recur_hybrid(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     default: return hipErrorInvalidValue;
     }
 }

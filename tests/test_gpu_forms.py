@@ -17,7 +17,7 @@ from kda_check import compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-FORMS = [0, 1, 2, 4, 101, 102, 201, 202, 301, 302]
+FORMS = [0, 1, 2, 4, 42, 8, 83, 9, 101, 102, 201, 202, 301, 302]
 SEGMENTS = [1, 2, 3, 8]
 LENGTHS = [70, 0, 300, 16, 1, 129]
 
