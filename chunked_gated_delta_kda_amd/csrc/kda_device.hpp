@@ -178,19 +178,25 @@ __device__ __forceinline__ f32x4 decay_any(int b, f32x4 s, f32x2 e) {
 }
 
 // LDS scratch of one chunk prep (one wave).
+// Unpadded tiles with XOR-swizzled placement (25 KiB: six prep waves fit on a CU).
+// Token-row tiles [16 tokens][128 channels]: the 16-byte unit u of row r sits at unit
+// u ^ r, so the 16 rows read by one MFMA operand load fall in distinct banks. The
+// transposed tile [128 channels][16 tokens]: the 8-byte piece e of channel row c sits
+// at piece e ^ ((c >> 2) & 3). No access crosses a unit (or a piece).
 struct alignas(16) PrepLds {
-    static constexpr int ROW = 136;    // bf16 per padded token row (128 + 8: spreads banks)
-    static constexpr int CROW = 20;    // bf16 per channel row of a transposed tile (16 + 4):
-                                       // 40-byte rows keep 8-byte accesses conflict-light
-    __bf16 kp[16 * ROW];               // K+ (single bf16)
-    __bf16 kmh[16 * ROW];              // K- hi
-    __bf16 kml[16 * ROW];              // K- lo
-    __bf16 qph[16 * ROW];              // Q+ hi
-    __bf16 qpl[16 * ROW];              // Q+ lo
-    __bf16 kpt[D * CROW];              // K+ transposed: [channel][token]
-    __bf16 kth[D * CROW];              // K~ hi, transposed
-    __bf16 ktl[D * CROW];              // K~ lo, transposed
+    __bf16 kp[16 * D];                 // K+ (single bf16)
+    __bf16 kmh[16 * D];                // K- hi
+    __bf16 kml[16 * D];                // K- lo
+    __bf16 qph[16 * D];                // Q+ hi
+    __bf16 qpl[16 * D];                // Q+ lo
+    __bf16 kpt[D * C];                 // K+ transposed: [channel][token]
     float egs[D];                      // lane-permutation scratch (32-token records)
+    // bf16 index of (token row r, channel c) in a token-row tile
+    __device__ static constexpr int at(int r, int c) { return r * D + ((((c >> 3) ^ r) & 15) << 3) + (c & 7); }
+    // bf16 index of (channel c, token t) in the transposed tile
+    __device__ static constexpr int at_t(int c, int t) {
+        return c * C + ((((t >> 2) ^ (c >> 2)) & 3) << 2) + (t & 3);
+    }
 };
 
 // 16x16 product N.M, given N^T and M in D layout, split-bf16 on both sides
@@ -295,14 +301,15 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
             const f32x2 kp = {k0 * ep0, k1 * ep1};
             const f32x2 km = {k0 * en0, k1 * en1};
             const f32x2 qp = {scale * q0 * ep0, scale * q1 * ep1};
-            *(uint32_t *)&L.kp[tt * PrepLds::ROW + c0] = pack2(kp.x, kp.y);
+            const int rc = PrepLds::at(tt, c0);
+            *(uint32_t *)&L.kp[rc] = pack2(kp.x, kp.y);
             bf16x2 hi, lo;
             split2(km, hi, lo);
-            *(bf16x2 *)&L.kmh[tt * PrepLds::ROW + c0] = hi;
-            *(bf16x2 *)&L.kml[tt * PrepLds::ROW + c0] = lo;
+            *(bf16x2 *)&L.kmh[rc] = hi;
+            *(bf16x2 *)&L.kml[rc] = lo;
             split2(qp, hi, lo);
-            *(bf16x2 *)&L.qph[tt * PrepLds::ROW + c0] = hi;
-            *(bf16x2 *)&L.qpl[tt * PrepLds::ROW + c0] = lo;
+            *(bf16x2 *)&L.qph[rc] = hi;
+            *(bf16x2 *)&L.qpl[rc] = lo;
             kpv[u][0] = kp.x;
             kpv[u][1] = kp.y;
             ktv[u][0] = km.x * (KTS ? eC0 * kts.x : eC0);      // K~ = K e^{G_C - G}
@@ -317,14 +324,16 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
             klT[ch][t / 2] = __builtin_bit_cast(uint32_t, lo);
         }
     }
+    // K+ transposed into LDS (the A operand of W^T); K~ (hi | lo) straight into the
+    // record: channel c, tokens 4e..4e+3 is recurrence lane 16e + c % 16 of key block c / 16
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
-        const int o = (c0 + ch) * PrepLds::CROW;
+        const int c = c0 + ch;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            *(uint2 *)&L.kpt[o + 4 * e] = uint2{kpT[ch][2 * e], kpT[ch][2 * e + 1]};
-            *(uint2 *)&L.kth[o + 4 * e] = uint2{khT[ch][2 * e], khT[ch][2 * e + 1]};
-            *(uint2 *)&L.ktl[o + 4 * e] = uint2{klT[ch][2 * e], klT[ch][2 * e + 1]};
+            *(uint2 *)&L.kpt[PrepLds::at_t(c, 4 * e)] = uint2{kpT[ch][2 * e], kpT[ch][2 * e + 1]};
+            *(uint4 *)(rec + Rec::KT + (c >> 4) * 1024 + (16 * e + (c & 15)) * 16) =
+                uint4{khT[ch][2 * e], khT[ch][2 * e + 1], klT[ch][2 * e], klT[ch][2 * e + 1]};
         }
     }
     // beta of token r (this lane's column) and of tokens 4g+j (this lane's rows)
@@ -340,7 +349,7 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
     f32x4 akk = {0.f, 0.f, 0.f, 0.f}, akt = akk, pt = akk;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const int off = r * PrepLds::ROW + 32 * kb + 8 * gq;
+        const int off = PrepLds::at(r, 32 * kb + 8 * gq);
         const bf16x8 kp = *(const bf16x8 *)&L.kp[off];
         const bf16x8 kmh = *(const bf16x8 *)&L.kmh[off];
         const bf16x8 kml = *(const bf16x8 *)&L.kml[off];
@@ -387,7 +396,7 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
     f32x4 Wt[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
-        const bf16x4 a = *(const bf16x4 *)&L.kpt[(16 * b + r) * PrepLds::CROW + 4 * gq];
+        const bf16x4 a = *(const bf16x4 *)&L.kpt[PrepLds::at_t(16 * b + r, 4 * gq)];
         Wt[b] = mfma(cat(a, a), tb, f32x4{0.f, 0.f, 0.f, 0.f});   // W[r][16b+4g+j]
         if (SB) Wt[b] = decay_any(b, Wt[b], ega);
     }
@@ -397,9 +406,9 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
         const bf16x4 b = to_bf16x4(-Wt[2 * kb + 1]);
         const bf16x8 wn = cat(a, b);
         *(bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16) = wn;
-        const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
-        bf16x8 qh = cat(*(const bf16x4 *)&L.qph[o], *(const bf16x4 *)&L.qph[o + 16]);
-        bf16x8 ql = cat(*(const bf16x4 *)&L.qpl[o], *(const bf16x4 *)&L.qpl[o + 16]);
+        const int o0 = PrepLds::at(r, 32 * kb + 4 * gq), o1 = PrepLds::at(r, 32 * kb + 16 + 4 * gq);
+        bf16x8 qh = cat(*(const bf16x4 *)&L.qph[o0], *(const bf16x4 *)&L.qph[o1]);
+        bf16x8 ql = cat(*(const bf16x4 *)&L.qpl[o0], *(const bf16x4 *)&L.qpl[o1]);
         if (SB) {
             // channels 32kb + 4g + j and 32kb + 16 + 4g + j: rows of key blocks 2kb, 2kb+1
             f32x4 x0, x1;
@@ -421,12 +430,6 @@ __device__ __forceinline__ void prep_chunk_t(const uint16_t *__restrict__ q,
         }
         *(bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16) = qh;
         *(bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16) = ql;
-    }
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const int o = (16 * b + r) * PrepLds::CROW + 4 * gq;
-        *(bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16) =
-            cat(*(const bf16x4 *)&L.kth[o], *(const bf16x4 *)&L.ktl[o]);
     }
 }
 
@@ -498,9 +501,9 @@ __device__ __forceinline__ void prep_chunk32(const uint16_t *__restrict__ q,
     bf16x8 kah[4], kal[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        const int o = r * PrepLds::ROW + 32 * kb + 4 * gq;
-        kah[kb] = cat(*(const bf16x4 *)&L.kmh[o], *(const bf16x4 *)&L.kmh[o + 16]);
-        kal[kb] = cat(*(const bf16x4 *)&L.kml[o], *(const bf16x4 *)&L.kml[o + 16]);
+        const int o0 = PrepLds::at(r, 32 * kb + 4 * gq), o1 = PrepLds::at(r, 32 * kb + 16 + 4 * gq);
+        kah[kb] = cat(*(const bf16x4 *)&L.kmh[o0], *(const bf16x4 *)&L.kmh[o1]);
+        kal[kb] = cat(*(const bf16x4 *)&L.kml[o0], *(const bf16x4 *)&L.kml[o1]);
     }
     // e^{G_a} lane-permuted, through LDS
     *(f32x2 *)&L.egs[egp_index(c0)] = ea;
