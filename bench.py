@@ -48,7 +48,7 @@ STATE_BYTES = 128 * 128 * 4       # one (sequence, head) state, fp32
 # outputs it writes); together they are q,k,v bf16 + g fp32 + beta fp32 + o fp32 = 1796 B
 KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796,
                                "recurrent": 1796}
-DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128, fp32 state)"
+DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128)"
 EVENT_EVERY = 4                   # timed steps per step that records kernel events
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -119,7 +119,7 @@ def measured_traffic(kernel, workload):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = t.get("kernels", {}).get(kernel)
+    rec = t.get("kernels", {}).get(f"{kernel}@{workload}")
     if not rec or rec.get("source_hash") != kernel_source_hash(kernel) or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
@@ -165,7 +165,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
         # mean over dispatches: segment launches of one kind cover different chunk ranges
         fb = float(np.mean(fl)) * f_scale
         wb = float(np.mean(wl)) * w_scale
-        out["kernels"][kind] = {"workload": workload, "source_hash": kernel_source_hash(kind),
+        out["kernels"][f"{kind}@{workload}"] = {"workload": workload, "source_hash": kernel_source_hash(kind),
                                 "command": command, "fetch_scale": f_scale, "write_scale": w_scale,
                                 "fetch_bytes": fb, "write_bytes": wb, "dispatches": len(fl),
                                 "bytes_per_launch": fb + wb}
@@ -213,17 +213,23 @@ def bench_decode(args, dev):
     import chunked_gated_delta_kda_amd as kda
 
     N, H = args.decode, args.heads
-    log(f"[bench] decode: {N} sequences x {H} heads")
+    bf16 = args.state_dtype == "bf16"
+    log(f"[bench] decode: {N} sequences x {H} heads, {args.state_dtype} state")
     w = synth.make_workload([1] * N, H, 1000 + N, with_initial_state=True)
     w.initial_state *= np.float32(3.0)     # a state of the size a long prefill leaves (RMS ~0.06)
+    if bf16:   # the drawn state rounded to bf16; the oracle starts from the same values
+        bits = synth.bf16_bits(w.initial_state)
+        w.initial_state = synth.bf16_to_f32(bits)
+        s0 = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
     d = synth.to_device(w, dev)
+    if not bf16:
+        s0 = d["initial_state"]
     q, k, v, g, beta = d["q"], d["k"], d["v"], d["g"], d["beta"]
     # parity of one step from the drawn state (written to a separate buffer)
-    o1, s1 = kda.decode(q, k, v, g, beta, w.scale, d["initial_state"],
-                        state_out=torch.empty_like(d["initial_state"]))
+    o1, s1 = kda.decode(q, k, v, g, beta, w.scale, s0, state_out=torch.empty_like(s0))
     torch.cuda.synchronize()
-    o1, s1 = o1.cpu().numpy(), s1.cpu().numpy()
-    state = d["initial_state"].clone()
+    o1, s1 = o1.cpu().numpy(), s1.float().cpu().numpy()
+    state = s0.clone()
     out = torch.empty((N, H, 128), dtype=torch.float32, device=dev)
 
     def step():
@@ -244,17 +250,17 @@ def bench_decode(args, dev):
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     copy_calibration(args, dev)
-    alg_bytes = N * H * (2 * STATE_BYTES + 1796)
+    alg_bytes = N * H * (2 * STATE_BYTES // (2 if bf16 else 1) + 1796)
     achieved = alg_bytes / (launch_ms / 1e3) / 1e9
     res = {"metric": DECODE_METRIC, "value": round(N / (ms_per_step / 1e3), 1), "unit": "tokens/s",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
-           "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta/state)",
-           "config": {"workload": f"decode step, {N} sequences x {H} heads", "num_seqs": N,
-                      "num_heads": H, "dk": 128, "dv": 128},
+           "data": f"synthetic (seeded; bf16 q/k/v, fp32 g/beta, {args.state_dtype} state)",
+           "config": {"workload": f"decode step, {N} sequences x {H} heads, {args.state_dtype} state", "num_seqs": N,
+                      "num_heads": H, "dk": 128, "dv": 128, "state_dtype": args.state_dtype},
            "roofline": {"bound": "hbm", "kernel": "recurrent", "achieved": round(achieved, 1),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("recurrent", f"decode{N}x{H}"),
+                        "traffic": measured_traffic("recurrent", f"decode{N}x{H}" + ("bf16" if bf16 else "")),
                         "alg_bytes_per_launch": alg_bytes, "launches_per_step": 1,
                         "avg_launch_ms": round(launch_ms, 5)},
            "cpu_baseline": None}
@@ -269,14 +275,16 @@ def bench_decode(args, dev):
         t0 = time.perf_counter()
         ro, rf = oracle.kda_forward(**inp, threads=threads)
         dt = time.perf_counter() - t0
-        po, pf = synth.parity(o1, ro), synth.parity(s1, rf)
+        po = synth.parity(o1, ro)
+        pf = synth.parity_bf16(s1, rf) if bf16 else synth.parity(s1, rf)
         res["cpu_baseline"] = {"value": round(N / dt, 1), "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"one decode step of the whole batch ({N * H} (sequence, head) "
                                          f"states), fp64, {dt:.3f} s wall"}
+        fkeys = ("rel_l2", "max_abs_rms") + (("max_err_over_bf16_bound",) if bf16 else ())
         res["parity"] = {"o": {k: po[k] for k in ("rel_l2", "max_abs_rms")},
-                         "final_state": {k: pf[k] for k in ("rel_l2", "max_abs_rms")},
-                         "pass": synth.passes(po) and synth.passes(pf)}
+                         "final_state": {k: pf[k] for k in fkeys},
+                         "pass": synth.passes(po) and (synth.passes_bf16(pf) if bf16 else synth.passes(pf))}
     print(json.dumps(res), flush=True)
 
 
@@ -291,6 +299,8 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="benchmark the decode step over N sequences instead of a prefill config")
     ap.add_argument("--heads", type=int, default=32, help="heads of the --decode workload")
+    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
+                    help="state element type in HBM for --decode (bf16: the BF16-state form)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -302,7 +312,8 @@ def main():
     args = ap.parse_args()
 
     if args.ingest_pmc:
-        workload = f"decode{args.decode}x{args.heads}" if args.decode else f"config{args.config}"
+        workload = (f"decode{args.decode}x{args.heads}" + ("bf16" if args.state_dtype == "bf16" else "")
+                    if args.decode else f"config{args.config}")
         ingest_pmc(*args.ingest_pmc, workload, args.pmc_command)
         return
 

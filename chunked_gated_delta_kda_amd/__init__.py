@@ -94,13 +94,16 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
     return out, final_state
 
 
-def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inplace", stream=None):
+def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inplace", state_dtype=None,
+           stream=None):
     """One recurrence step per sequence (decode) on the current HIP device.
 
     q, k, v: bf16 [N, H, 128] (one token per sequence); g: fp32 [N, H, 128];
-    beta: fp32 [N, H]; state: fp32 [N, H, 128, 128] or None (zeros).
-    state_out: "inplace" (update ``state``; a new tensor when state is None), None
-    (state not written), or an fp32 [N, H, 128, 128] tensor.
+    beta: fp32 [N, H]; state: [N, H, 128, 128] fp32 or bf16 (the BF16-state form), or
+    None (zeros). state_out: "inplace" (update ``state``; a new tensor when state is
+    None), None (state not written), or a tensor of the state's dtype.
+    state_dtype: torch.float32 or torch.bfloat16; by default the dtype of ``state``
+    (or of ``state_out``), else float32.
     Returns (o fp32 [N, H, 128], the updated state or None).
     """
     import torch
@@ -118,11 +121,17 @@ def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inp
         if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
             raise ValueError(f"{name}: expected contiguous {dt} {shape} on {dev}, "
                              f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+    if state_dtype is None:
+        state_dtype = (state.dtype if state is not None else
+                       state_out.dtype if isinstance(state_out, torch.Tensor) else torch.float32)
+    codes = {torch.float32: native.STATE_DTYPES["f32"], torch.bfloat16: native.STATE_DTYPES["bf16"]}
+    if state_dtype not in codes:
+        raise ValueError("state_dtype: torch.float32 or torch.bfloat16")
     sshape = (N, H, Dk, Dk)
     for name, t in (("state", state), ("state_out", state_out)):
-        if isinstance(t, torch.Tensor) and (t.dtype != torch.float32 or tuple(t.shape) != sshape
+        if isinstance(t, torch.Tensor) and (t.dtype != state_dtype or tuple(t.shape) != sshape
                                             or not t.is_contiguous() or t.device != dev):
-            raise ValueError(f"{name}: expected contiguous fp32 {sshape} on {dev}")
+            raise ValueError(f"{name}: expected contiguous {state_dtype} {sshape} on {dev}")
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     if out is None:
@@ -130,9 +139,10 @@ def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inp
     if isinstance(state_out, str):
         if state_out != "inplace":
             raise ValueError('state_out: "inplace", None or a tensor')
-        state_out = state if state is not None else torch.empty(sshape, dtype=torch.float32, device=dev)
+        state_out = state if state is not None else torch.empty(sshape, dtype=state_dtype, device=dev)
     st = stream if stream is not None else torch.cuda.current_stream(dev)
-    rc = lib.kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), N, H, Dk,
-                        _ptr(state), _ptr(state_out), _ptr(out), ctypes.c_void_p(st.cuda_stream))
+    rc = lib.kda_decode_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), N, H, Dk,
+                           _ptr(state), _ptr(state_out), _ptr(out), ctypes.c_void_p(st.cuda_stream),
+                           codes[state_dtype])
     native.check(rc)
     return out, state_out

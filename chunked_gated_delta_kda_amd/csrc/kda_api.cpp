@@ -251,7 +251,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
         const int dvt = kda::recurrent_tile((int64_t)N * H);
         const bool ok = around(st, [&] {
             return kda::launch_recurrent(q16, k16, v16, g, beta, scale, cu_seqlens, N, T, H, false, initial_state,
-                                         out, final_state, dvt, st);
+                                         out, final_state, false, dvt, st);
         });
         return ok ? KDA_OK : KDA_ERR_LAUNCH;
     }
@@ -329,19 +329,28 @@ int kda_fwd(const void *q, const void *k, const void *v, const float *g, const f
 int kda_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,
                float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                const float *state_in, float *state_out, float *out, void *stream) {
+    return kda_decode_ex(q, k, v, g, beta, scale, num_seqs, num_heads, head_dim, state_in, state_out, out, stream,
+                         KDA_STATE_F32);
+}
+
+int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                  const void *state_in, void *state_out, float *out, void *stream, int32_t state_dtype) {
     if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
+    if (state_dtype != KDA_STATE_F32 && state_dtype != KDA_STATE_BF16) return KDA_ERR_UNSUPPORTED;
     if (!shape_ok(num_seqs, num_seqs, num_heads)) return KDA_ERR_SHAPE;
     if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_NULL;
-    const size_t state_bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    const size_t state_bytes =
+        (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * (state_dtype == KDA_STATE_BF16 ? 2 : 4);
     if (state_in && state_out && (const void *)state_in != (const void *)state_out &&
         overlaps(state_in, state_bytes, state_out, state_bytes))
         return KDA_ERR_ALIAS;
     hipStream_t st = (hipStream_t)stream;
     const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads);
     if (kda::launch_recurrent((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale,
-                              nullptr, num_seqs, num_seqs, num_heads, true, state_in, out, state_out, dvt,
-                              st) != hipSuccess)
+                              nullptr, num_seqs, num_seqs, num_heads, true, state_in, out, state_out,
+                              state_dtype == KDA_STATE_BF16, dvt, st) != hipSuccess)
         return KDA_ERR_LAUNCH;
     return KDA_OK;
 }

@@ -48,15 +48,37 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 
 // The state is read once and written once per call: nontemporal accesses keep it
 // from evicting reusable lines (measured on MI355X, decode of 256 sequences x 32
-// heads: 0.193 ms against 0.215 ms with ordinary loads and stores).
+// heads: 0.193 ms against 0.215 ms with ordinary loads and stores). In HBM it is fp32,
+// or bf16 (the BF16-state form: stored in bf16, updated in fp32 registers; smzdm.com,
+// "KDA 内核到底难在哪" and "反转二"), which halves the decode step's traffic.
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 load_state(const float *p) {
-    const f32x4v x = __builtin_nontemporal_load((const f32x4v *)p);
-    return make_float4(x[0], x[1], x[2], x[3]);
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
-__device__ __forceinline__ void store_state(float *p, float4 x) {
-    const f32x4v y = {x.x, x.y, x.z, x.w};
-    __builtin_nontemporal_store(y, (f32x4v *)p);
+
+template <bool BF16S>
+__device__ __forceinline__ float4 load_state(const void *base, int64_t i) {
+    if constexpr (BF16S) {
+        const u32x2v x = __builtin_nontemporal_load((const u32x2v *)((const uint16_t *)base + i));
+        return make_float4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]));
+    } else {
+        const f32x4v x = __builtin_nontemporal_load((const f32x4v *)((const float *)base + i));
+        return make_float4(x[0], x[1], x[2], x[3]);
+    }
+}
+template <bool BF16S>
+__device__ __forceinline__ void store_state(void *base, int64_t i, float4 x) {
+    if constexpr (BF16S) {
+        const u32x2v y = {bf16_rne(x.x) | (bf16_rne(x.y) << 16), bf16_rne(x.z) | (bf16_rne(x.w) << 16)};
+        __builtin_nontemporal_store(y, (u32x2v *)((uint16_t *)base + i));
+    } else {
+        const f32x4v y = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(y, (f32x4v *)((float *)base + i));
+    }
 }
 
 template <int DVT>
@@ -90,11 +112,11 @@ __device__ __forceinline__ TokIn load_token(const uint16_t *__restrict__ q, cons
     return r;
 }
 
-template <int DVT>
+template <int DVT, bool BF16S>
 __global__ __launch_bounds__(NT) void recurrent_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
-    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin) {
+    int N, int T, int H, int one_token_per_seq, const void *s0, float *__restrict__ out, void *sfin) {
     using TL = Tile<DVT>;
     __shared__ float sq[2][D], sk[2][D], se[2][D];
     __shared__ float sqk[2][2];
@@ -123,7 +145,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     float4 st[TL::RPT];
 #pragma unroll
     for (int m = 0; m < TL::RPT; ++m)
-        st[m] = s0 ? load_state(s0 + sbase + (int64_t)(rg + TL::RG * m) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+        st[m] = s0 ? load_state<BF16S>(s0, sbase + (int64_t)(rg + TL::RG * m) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
 
     TokIn cur{};
     if (t0 < t1) cur = load_token(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
@@ -198,7 +220,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     }
     if (sfin) {
 #pragma unroll
-        for (int m = 0; m < TL::RPT; ++m) store_state(sfin + sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+        for (int m = 0; m < TL::RPT; ++m) store_state<BF16S>(sfin, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
     }
 }
 
@@ -217,28 +239,34 @@ int recurrent_tile(int64_t chains) {
     return 32;
 }
 
+template <int DVT, bool BF16S>
+static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                        float scale, const int32_t *cu, int N, int T, int H, bool one_token_per_seq, const void *s0,
+                        float *out, void *sfin, hipStream_t st) {
+    const int64_t blocks = (int64_t)N * H * Tile<DVT>::TILES;
+    hipLaunchKernelGGL((recurrent_kernel<DVT, BF16S>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
+                       scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
+}
+
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                             const float *beta, float scale, const int32_t *cu, int N, int T, int H,
-                            bool one_token_per_seq, const float *s0, float *out, float *sfin, int dvt,
-                            hipStream_t st) {
-    const int64_t chains = (int64_t)N * H;
-    const dim3 block(NT);
+                            bool one_token_per_seq, const void *s0, float *out, void *sfin, bool bf16_state,
+                            int dvt, hipStream_t st) {
+#define KDA_TILE_CASE(W)                                                                                     \
+    case W:                                                                                                  \
+        if (bf16_state)                                                                                      \
+            launch_tile<W, true>(q, k, v, g, beta, scale, cu, N, T, H, one_token_per_seq, s0, out, sfin, st); \
+        else                                                                                                 \
+            launch_tile<W, false>(q, k, v, g, beta, scale, cu, N, T, H, one_token_per_seq, s0, out, sfin, st); \
+        break;
     switch (dvt) {
-    case 128:
-        hipLaunchKernelGGL(recurrent_kernel<128>, dim3((unsigned)(chains * Tile<128>::TILES)), block, 0, st,
-                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
-        break;
-    case 64:
-        hipLaunchKernelGGL(recurrent_kernel<64>, dim3((unsigned)(chains * Tile<64>::TILES)), block, 0, st,
-                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
-        break;
-    case 32:
-        hipLaunchKernelGGL(recurrent_kernel<32>, dim3((unsigned)(chains * Tile<32>::TILES)), block, 0, st,
-                           q, k, v, g, beta, scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
-        break;
+        KDA_TILE_CASE(128)
+        KDA_TILE_CASE(64)
+        KDA_TILE_CASE(32)
     default:
         return hipErrorInvalidValue;
     }
+#undef KDA_TILE_CASE
     return hipGetLastError();
 }
 

@@ -17,7 +17,8 @@ VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 
 #: every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
-           "kda_launch_plan", "kda_decode", "kda_status_string", "kda_version")
+           "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_status_string", "kda_version")
+STATE_DTYPES = {"f32": 0, "bf16": 1}
 KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent"}
 
 
@@ -70,6 +71,8 @@ def load_library(path=LIB_PATH):
     lib.kda_launch_plan.restype = ctypes.c_int32
     lib.kda_decode.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, i32, i32, i32, f32p, f32p, f32p, vp]
     lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode_ex.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, i32, i32, i32, vp, vp, f32p, vp, i32]
+    lib.kda_decode_ex.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

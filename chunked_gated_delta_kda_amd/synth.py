@@ -179,6 +179,28 @@ def passes(m, rel=GATE_REL_L2, mx=GATE_MAX_ABS_RMS):
     return m["finite"] and m["rel_l2"] <= rel and m["max_abs_rms"] <= mx
 
 
+#: A result stored in bf16 is at best the rounding of the exact value (error up to half a
+#: bf16 ulp, 2^-9 |x|): on top of the relative-L2 gate, every element must lie within one
+#: bf16 ulp (bounded by 2^-7 |ref|) of the fp64 reference, with an absolute allowance of
+#: 1e-4 RMS for the fp32 arithmetic before the rounding.
+GATE_BF16_ULP = 2.0 ** -7
+GATE_BF16_ABS_RMS = 1e-4
+
+
+def parity_bf16(got, ref):
+    """``parity`` plus the largest elementwise error in units of the bf16 bound."""
+    m = parity(got, ref)
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bound = GATE_BF16_ULP * np.abs(ref) + GATE_BF16_ABS_RMS * m["rms"]
+    m["max_err_over_bf16_bound"] = float(np.max(np.abs(got - ref) / bound)) if ref.size and m["finite"] else 0.0
+    return m
+
+
+def passes_bf16(m, rel=GATE_REL_L2):
+    return m["finite"] and m["rel_l2"] <= rel and m["max_err_over_bf16_bound"] <= 1.0
+
+
 # ----------------------------------------------------------------------------- device upload
 def to_device(w, device="cuda"):
     """Copy a workload's host arrays to device tensors (bf16 bits are reinterpreted, not converted)."""

@@ -169,6 +169,22 @@ int kda_decode(const void *q, const void *k, const void *v, const float *g, cons
                float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                const float *state_in, float *state_out, float *out, void *stream);
 
+/* State element types of kda_decode_ex. */
+#define KDA_STATE_F32 0
+#define KDA_STATE_BF16 1
+
+/*
+ * kda_decode_ex -- kda_decode with the state held in HBM as fp32 (KDA_STATE_F32, the
+ * same as kda_decode) or as bf16 (KDA_STATE_BF16): the BF16-state form, where the state
+ * is stored in bf16 and updated in fp32 (smzdm.com, "KDA 内核到底难在哪" and "反转二").
+ * state_in and state_out are then bf16 [N, H, 128, 128] (state_out rounded to nearest
+ * even), which halves the step's HBM traffic. Other arguments, aliasing rules and
+ * errors as kda_decode; an unknown state_dtype returns KDA_ERR_UNSUPPORTED.
+ */
+int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                  float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                  const void *state_in, void *state_out, float *out, void *stream, int32_t state_dtype);
+
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);
 

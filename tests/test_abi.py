@@ -90,6 +90,18 @@ def test_decode_validation_errors(lib):
     assert decode_call(lib, s_in=ctypes.c_void_p(4096), s_out=ctypes.c_void_p(4096 + 64)) == 7
 
 
+def test_decode_ex_validation_errors(lib):
+    def call_ex(dtype, s_in=None, s_out=P, N=4, D=128):
+        return lib.kda_decode_ex(P, P, P, P, P, 0.088, N, 2, D, s_in, s_out, P, None, dtype)
+    assert call_ex(2) == 3                                       # unknown state dtype
+    assert call_ex(-1) == 3
+    assert call_ex(1, D=64) == 3
+    assert call_ex(1, N=0) == 2
+    # bf16 states are half as long: these two overlap by 64 bytes only as bf16
+    n_bf16 = 4 * 2 * 128 * 128 * 2
+    assert call_ex(1, s_in=ctypes.c_void_p(4096), s_out=ctypes.c_void_p(4096 + n_bf16 - 64)) == 7
+
+
 def test_workspace_bytes(lib):
     assert lib.kda_workspace_bytes(0, 16, 1, 1) == 0
     b = lib.kda_workspace_bytes(1, 8192, 32, 1)

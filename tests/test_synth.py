@@ -55,3 +55,19 @@ def test_parity_metric():
     assert not synth.passes(synth.parity(np.array([np.nan, 0, 0, 0]), ref))
     z = synth.parity(np.zeros(3), np.zeros(3))
     assert synth.passes(z)
+
+
+def test_bf16_result_gate():
+    """The bf16 gate accepts the round-to-nearest of the reference and rejects an element
+    two bf16 ulps away."""
+    rng = np.random.default_rng(3)
+    ref = rng.standard_normal(4096) * np.exp(rng.uniform(-6, 3, 4096))
+    rounded = synth.bf16_to_f32(synth.bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    m = synth.parity_bf16(rounded, ref)
+    assert synth.passes_bf16(m) and m["max_err_over_bf16_bound"] <= 0.51
+    # the same rounding fails the fp32 max-abs gate once large elements dominate
+    bad = rounded.copy()
+    i = int(np.argmax(np.abs(ref)))
+    e = int(np.floor(np.log2(abs(ref[i]))))
+    bad[i] += 2 * 2.0 ** (e - 7) * np.sign(ref[i])
+    assert not synth.passes_bf16(synth.parity_bf16(bad, ref))
