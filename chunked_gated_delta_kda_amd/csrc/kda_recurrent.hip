@@ -52,7 +52,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x 
 // or bf16 (the BF16-state form: stored in bf16, updated in fp32 registers; smzdm.com,
 // "KDA 内核到底难在哪" and "反转二"), which halves the decode step's traffic.
 typedef float f32x4v __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 
 // fp32 -> bf16, round to nearest even (finite inputs)
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
@@ -60,54 +60,70 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <bool BF16S>
-__device__ __forceinline__ float4 load_state(const void *base, int64_t i) {
+// CPT consecutive value columns of one key row: fp32 (CPT = 4: one 16-byte access) or
+// bf16 (CPT = 8: one 16-byte access)
+template <bool BF16S, int CPT>
+__device__ __forceinline__ void load_state(const void *base, int64_t i, float (&x)[CPT]) {
     if constexpr (BF16S) {
-        const u32x2v x = __builtin_nontemporal_load((const u32x2v *)((const uint16_t *)base + i));
-        return make_float4(bf16_lo(x[0]), bf16_hi(x[0]), bf16_lo(x[1]), bf16_hi(x[1]));
+        static_assert(CPT == 8, "bf16 state: 8 columns per access");
+        const u32x4v y = __builtin_nontemporal_load((const u32x4v *)((const uint16_t *)base + i));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[2 * j] = bf16_lo(y[j]), x[2 * j + 1] = bf16_hi(y[j]);
     } else {
-        const f32x4v x = __builtin_nontemporal_load((const f32x4v *)((const float *)base + i));
-        return make_float4(x[0], x[1], x[2], x[3]);
+        static_assert(CPT == 4, "fp32 state: 4 columns per access");
+        const f32x4v y = __builtin_nontemporal_load((const f32x4v *)((const float *)base + i));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = y[j];
     }
 }
-template <bool BF16S>
-__device__ __forceinline__ void store_state(void *base, int64_t i, float4 x) {
+template <bool BF16S, int CPT>
+__device__ __forceinline__ void store_state(void *base, int64_t i, const float (&x)[CPT]) {
     if constexpr (BF16S) {
-        const u32x2v y = {bf16_rne(x.x) | (bf16_rne(x.y) << 16), bf16_rne(x.z) | (bf16_rne(x.w) << 16)};
-        __builtin_nontemporal_store(y, (u32x2v *)((uint16_t *)base + i));
+        u32x4v y;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y[j] = bf16_rne(x[2 * j]) | (bf16_rne(x[2 * j + 1]) << 16);
+        __builtin_nontemporal_store(y, (u32x4v *)((uint16_t *)base + i));
     } else {
-        const f32x4v y = {x.x, x.y, x.z, x.w};
+        const f32x4v y = {x[0], x[1], x[2], x[3]};
         __builtin_nontemporal_store(y, (f32x4v *)((float *)base + i));
     }
 }
 
-template <int DVT>
+template <int DVT, int CPT>
 struct Tile {
-    static constexpr int CG = DVT / 4;  // column groups (float4) per tile
-    static constexpr int RG = NT / CG;  // row groups
-    static constexpr int RPT = D / RG;  // key rows per thread
+    static constexpr int CG = DVT / CPT;  // column groups per tile
+    static constexpr int RG = NT / CG;    // row groups
+    static constexpr int RPT = D / RG;    // key rows per thread
     static constexpr int TILES = D / DVT;
     static_assert(CG <= 64 && 64 % CG == 0, "a wave holds whole row groups");
 };
 
 // Inputs of one token for this thread: q, k, g of key row `tid` (threads < 128),
-// and v (4 columns) and beta for every thread.
+// and v (CPT columns, bf16) and beta for every thread.
+template <int CPT>
 struct TokIn {
     float q, k, g;
-    uint2 v;
+    uint32_t v[CPT / 2];
     float beta;
 };
 
-__device__ __forceinline__ TokIn load_token(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                            const uint16_t *__restrict__ v, const float *__restrict__ g,
-                                            const float *__restrict__ beta, int64_t th, int tid, int col) {
-    TokIn r;
+template <int CPT>
+__device__ __forceinline__ TokIn<CPT> load_token(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                 const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                                 const float *__restrict__ beta, int64_t th, int tid, int col) {
+    TokIn<CPT> r;
     const int64_t o = th * D;
     const int row = tid & (D - 1);  // threads >= 128 load a row they do not use: keeps the loads unconditional
     r.q = __uint_as_float((uint32_t)q[o + row] << 16);
     r.k = __uint_as_float((uint32_t)k[o + row] << 16);
     r.g = g[o + row];
-    r.v = *(const uint2 *)(v + o + col);
+    if constexpr (CPT == 8) {
+        const uint4 x = *(const uint4 *)(v + o + col);
+        r.v[0] = x.x, r.v[1] = x.y, r.v[2] = x.z, r.v[3] = x.w;
+    } else {
+        const uint2 x = *(const uint2 *)(v + o + col);
+        r.v[0] = x.x, r.v[1] = x.y;
+    }
     r.beta = beta[th];
     return r;
 }
@@ -117,17 +133,18 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
     int N, int T, int H, int one_token_per_seq, const void *s0, float *__restrict__ out, void *sfin) {
-    using TL = Tile<DVT>;
+    constexpr int CPT = BF16S ? 8 : 4;
+    using TL = Tile<DVT, CPT>;
     __shared__ float sq[2][D], sk[2][D], se[2][D];
     __shared__ float sqk[2][2];
-    __shared__ float4 red[NWAVE][2][TL::CG];
+    __shared__ float red[NWAVE][2][TL::CG][CPT];
 
     const int tile = blockIdx.x % TL::TILES;
     const int nh = blockIdx.x / TL::TILES;
     const int h = nh % H, n = nh / H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % TL::CG, rg = tid / TL::CG;
-    const int col = tile * DVT + cg * 4;
+    const int col = tile * DVT + cg * CPT;
 
     // tokens of sequence n, clamped to [0, T] so that malformed cu_seqlens cannot
     // send an access out of bounds
@@ -142,13 +159,19 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     }
 
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
-    float4 st[TL::RPT];
+    float st[TL::RPT][CPT];
 #pragma unroll
-    for (int m = 0; m < TL::RPT; ++m)
-        st[m] = s0 ? load_state<BF16S>(s0, sbase + (int64_t)(rg + TL::RG * m) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m = 0; m < TL::RPT; ++m) {
+        if (s0) {
+            load_state<BF16S, CPT>(s0, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) st[m][j] = 0.f;
+        }
+    }
 
-    TokIn cur{};
-    if (t0 < t1) cur = load_token(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
+    TokIn<CPT> cur{};
+    if (t0 < t1) cur = load_token<CPT>(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
     for (int t = t0; t < t1; ++t) {
         const int buf = (t - t0) & 1;
         const int64_t th = (int64_t)t * H + h;
@@ -162,65 +185,71 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
             for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off);
             if (lane == 0) sqk[buf][wave] = p;
         }
-        const uint2 vb = cur.v;
+        float vv[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT / 2; ++j) vv[2 * j] = bf16_lo(cur.v[j]), vv[2 * j + 1] = bf16_hi(cur.v[j]);
         const float bt = cur.beta;
         // next token's inputs (the last token reloads itself: loads stay unconditional)
         const int tn = t + 1 < t1 ? t + 1 : t;
-        cur = load_token(q, k, v, g, beta, (int64_t)tn * H + h, tid, col);
+        cur = load_token<CPT>(q, k, v, g, beta, (int64_t)tn * H + h, tid, col);
         __syncthreads();
 
         // decay, and this thread's part of u = S1^T k and w = S1^T q
-        float4 u = make_float4(0.f, 0.f, 0.f, 0.f), w = u;
+        float u[CPT], w[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) u[j] = 0.f, w[j] = 0.f;
 #pragma unroll
         for (int m = 0; m < TL::RPT; ++m) {
             const int r = rg + TL::RG * m;
             const float e = se[buf][r], kr = sk[buf][r], qr = sq[buf][r];
-            st[m].x *= e, st[m].y *= e, st[m].z *= e, st[m].w *= e;
-            u.x = fmaf(kr, st[m].x, u.x), u.y = fmaf(kr, st[m].y, u.y);
-            u.z = fmaf(kr, st[m].z, u.z), u.w = fmaf(kr, st[m].w, u.w);
-            w.x = fmaf(qr, st[m].x, w.x), w.y = fmaf(qr, st[m].y, w.y);
-            w.z = fmaf(qr, st[m].z, w.z), w.w = fmaf(qr, st[m].w, w.w);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) {
+                st[m][j] *= e;
+                u[j] = fmaf(kr, st[m][j], u[j]);
+                w[j] = fmaf(qr, st[m][j], w[j]);
+            }
         }
         // sum over the row groups of this wave (lanes that differ in the rg bits)
 #pragma unroll
         for (int off = TL::CG; off < 64; off <<= 1) {
-            u.x += __shfl_xor(u.x, off), u.y += __shfl_xor(u.y, off);
-            u.z += __shfl_xor(u.z, off), u.w += __shfl_xor(u.w, off);
-            w.x += __shfl_xor(w.x, off), w.y += __shfl_xor(w.y, off);
-            w.z += __shfl_xor(w.z, off), w.w += __shfl_xor(w.w, off);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) u[j] += __shfl_xor(u[j], off), w[j] += __shfl_xor(w[j], off);
         }
         if (lane < TL::CG) {
-            red[wave][0][lane] = u;
-            red[wave][1][lane] = w;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) red[wave][0][lane][j] = u[j], red[wave][1][lane][j] = w[j];
         }
         __syncthreads();
-        u = red[0][0][cg], w = red[0][1][cg];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) u[j] = red[0][0][cg][j], w[j] = red[0][1][cg][j];
 #pragma unroll
         for (int x = 1; x < NWAVE; ++x) {
-            const float4 a = red[x][0][cg], b = red[x][1][cg];
-            u.x += a.x, u.y += a.y, u.z += a.z, u.w += a.w;
-            w.x += b.x, w.y += b.y, w.z += b.z, w.w += b.w;
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) u[j] += red[x][0][cg][j], w[j] += red[x][1][cg][j];
         }
         const float qk = sqk[buf][0] + sqk[buf][1];
-        float4 dl;
-        dl.x = bt * (bf16_lo(vb.x) - u.x), dl.y = bt * (bf16_hi(vb.x) - u.y);
-        dl.z = bt * (bf16_lo(vb.y) - u.z), dl.w = bt * (bf16_hi(vb.y) - u.w);
+        float dl[CPT];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) dl[j] = bt * (vv[j] - u[j]);
 #pragma unroll
         for (int m = 0; m < TL::RPT; ++m) {
             const float kr = sk[buf][rg + TL::RG * m];
-            st[m].x = fmaf(kr, dl.x, st[m].x), st[m].y = fmaf(kr, dl.y, st[m].y);
-            st[m].z = fmaf(kr, dl.z, st[m].z), st[m].w = fmaf(kr, dl.w, st[m].w);
+#pragma unroll
+            for (int j = 0; j < CPT; ++j) st[m][j] = fmaf(kr, dl[j], st[m][j]);
         }
         if (rg == 0) {
-            float4 o;
-            o.x = scale * fmaf(qk, dl.x, w.x), o.y = scale * fmaf(qk, dl.y, w.y);
-            o.z = scale * fmaf(qk, dl.z, w.z), o.w = scale * fmaf(qk, dl.w, w.w);
-            *(float4 *)(out + th * D + col) = o;
+#pragma unroll
+            for (int j = 0; j < CPT; j += 4) {
+                float4 o;
+                o.x = scale * fmaf(qk, dl[j], w[j]), o.y = scale * fmaf(qk, dl[j + 1], w[j + 1]);
+                o.z = scale * fmaf(qk, dl[j + 2], w[j + 2]), o.w = scale * fmaf(qk, dl[j + 3], w[j + 3]);
+                *(float4 *)(out + th * D + col + j) = o;
+            }
         }
     }
     if (sfin) {
 #pragma unroll
-        for (int m = 0; m < TL::RPT; ++m) store_state<BF16S>(sfin, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+        for (int m = 0; m < TL::RPT; ++m) store_state<BF16S, CPT>(sfin, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
     }
 }
 
@@ -243,7 +272,7 @@ template <int DVT, bool BF16S>
 static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                         float scale, const int32_t *cu, int N, int T, int H, bool one_token_per_seq, const void *s0,
                         float *out, void *sfin, hipStream_t st) {
-    const int64_t blocks = (int64_t)N * H * Tile<DVT>::TILES;
+    const int64_t blocks = (int64_t)N * H * (D / DVT);
     hipLaunchKernelGGL((recurrent_kernel<DVT, BF16S>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
                        scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
 }

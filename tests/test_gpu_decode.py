@@ -137,7 +137,7 @@ def _bf16_state(a):
 
 
 @pytest.mark.parametrize("N,H", [(7, 3), (300, 4)])
-@pytest.mark.parametrize("tile", [None, "128"])
+@pytest.mark.parametrize("tile", [None, "128", "32"])
 def test_decode_bf16_state(N, H, tile, monkeypatch):
     """BF16-state form: the oracle starts from the same bf16 state values (exact in fp64)."""
     import torch
