@@ -94,15 +94,23 @@ int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
 // recurrence(S-1): the prep of later segments runs on the CUs the recurrence leaves
 // idle, which pays when the recurrence has fewer blocks than the chip has CUs. 1 for
 // the non-paired recurrence forms. KDA_SEGMENTS (1..KDA_MAX_SEGMENTS) overrides.
-int split_segments(int64_t N, int64_t H, int waves) {
+int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     if (waves < 100) return 1;
     if (const char *e = std::getenv("KDA_SEGMENTS")) {
         const int s = std::atoi(e);
         if (s >= 1 && s <= KDA_MAX_SEGMENTS) return s;
     }
-    // measured on MI355X (config 2, 128 blocks): 3 segments 0.442 ms, 4 0.439, 6 0.435, 8 0.441
     const int64_t blocks = N * H * (8 / (waves % 100));
-    return blocks < 256 ? 6 : 1;
+    if (blocks >= 256) return 1;
+    // S segments hide (1 - 1/S) of the prep (~7 ns per chunk-head on the whole chip)
+    // and add S - 1 launches (~5 us each): S = sqrt(prep / 5 us), i.e. sqrt(chunk-heads
+    // / 500), at most 6. Measured on MI355X (ms for 1 | 2 | 3 | 6 segments): 256 tokens x
+    // 2 heads 0.024 | 0.028 | 0.032 | 0.051; 4096 x 8 0.160 | 0.159 | 0.160 | 0.170;
+    // 4096 x 32 0.229 | 0.218 | 0.216 | 0.228; 8192 x 32: 3 0.442, 4 0.439, 6 0.435,
+    // 8 0.441; 65536 x 8: 4 2.308, 6 2.305, 8 2.321.
+    const double chunk_heads = (double)max_chunks(N, T) * (double)H;
+    const int s = (int)std::lround(std::sqrt(chunk_heads / 500.0));
+    return s < 1 ? 1 : s > 6 ? 6 : s;
 }
 
 // Consumer waves per block of the fused kernel (1, 2 or 4; 16 value columns each).
@@ -175,7 +183,7 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     }
     plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
-        const int segs = split_segments(num_seqs, num_heads, waves);
+        const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
         auto bound = [&](int sg) { return (int32_t)((int64_t)M * sg / segs); };
         plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0, cl};
         for (int sg = 0; sg + 1 < segs; ++sg)
@@ -195,7 +203,7 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
     const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
-    const int segs = v == KDA_VARIANT_SPLIT ? split_segments(num_seqs, num_heads, waves) : 1;
+    const int segs = v == KDA_VARIANT_SPLIT ? split_segments(num_seqs, total_tokens, num_heads, waves) : 1;
     return ws_layout(num_seqs, total_tokens, num_heads, v, segs, waves).total;
 }
 
@@ -229,7 +237,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     hipStream_t st = (hipStream_t)stream;
     const int N = num_seqs, T = total_tokens, H = num_heads;
     const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, H) : fused_waves(N, H);
-    const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, H, waves) : 1;
+    const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, T, H, waves) : 1;
     const Layout lay = ws_layout(N, T, H, chosen, segs, waves);
     const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
     const bool c32 = cl == 32;
