@@ -25,11 +25,12 @@ int64_t max_chunks(int64_t N, int64_t T, int cl = KDA_CHUNK) { return (T + cl - 
 int chunk_len(int waves) { return waves >= 300 ? 32 : KDA_CHUNK; }
 size_t rec_bytes(int waves) { return waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES; }
 
-// Workspace: chunk offsets [N+1], sequence order [N], an error word, and (split
-// variant only) a state carry buffer [N, H, 128, 128] fp32 when the chunk range is
-// cut into segments, followed by one chunk record per (chunk, head).
+// Workspace: chunk offsets [N+1], sequence order [N], an error word, the sanitised
+// sequence offsets [N+1], and (split variant only) a state carry buffer [N, H, 128, 128]
+// fp32 when the chunk range is cut into segments, followed by one chunk record per
+// (chunk, head).
 struct Layout {
-    size_t chunk_off, order, err, carry, recs, total;
+    size_t chunk_off, order, err, cu, carry, recs, total;
 };
 
 Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves) {
@@ -38,7 +39,8 @@ Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int
     L.chunk_off = 0;
     L.order = align_up(sizeof(int32_t) * (size_t)(N + 1));
     L.err = L.order + align_up(sizeof(int32_t) * (size_t)N);
-    L.carry = L.err + ALIGN;
+    L.cu = L.err + ALIGN;
+    L.carry = L.cu + align_up(sizeof(int32_t) * (size_t)(N + 1));
     L.recs = L.carry;
     L.total = L.recs;
     if (variant == KDA_VARIANT_SPLIT) {
@@ -279,27 +281,28 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     int32_t *chunk_off = (int32_t *)(ws + lay.chunk_off);
     int32_t *order = (int32_t *)(ws + lay.order);
     int32_t *err = (int32_t *)(ws + lay.err);
+    int32_t *cus = (int32_t *)(ws + lay.cu);   // sanitised cu_seqlens, written by the chunk map
     char *recs = ws + lay.recs;
 
-    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, chunk_off, order, err, cl, st); });
+    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, cl, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
         auto prep = [&](int64_t b, int64_t e) {
-            return c32 ? kda::launch_prep32(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, b, e, st)
-                       : kda::launch_prep(q16, k16, g, beta, cu_seqlens, N, T, H, scale, chunk_off, recs, b, e, st);
+            return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, st)
+                       : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, st);
         };
         auto recur_range = [&](float *carry, int b, int e) {
-            return c32 ? kda::launch_recur32_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
-                       : kda::launch_recur_range(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
+            return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
+                       : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
         if (segs == 1) {
             ok = around(st, [&] { return prep(0, M); }) &&
                  around(st, [&] {
                      return waves >= 100 ? recur_range(final_state, 0, 1 << 30)
-                                         : kda::launch_recur(recs, v16, cu_seqlens, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st);
+                                         : kda::launch_recur(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st);
                  });
         } else {
-            kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cu_seqlens, chunk_off, order,
+            kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cus, chunk_off, order,
                                  N, T, H, initial_state, out, final_state,
                                  final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0};
             auto bound = [&](int sg) { return M * sg / segs; };
@@ -311,7 +314,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             ok = ok && around(st, [&] { return recur_range(a.carry, (int)bound(segs - 1), (int)M); });
         }
     } else if (ok) {
-        ok = around(st, [&] { return kda::launch_fused(q16, k16, v16, g, beta, cu_seqlens, order, N, T, H, scale, initial_state, out, final_state, err, waves, st); });
+        ok = around(st, [&] { return kda::launch_fused(q16, k16, v16, g, beta, cus, order, N, T, H, scale, initial_state, out, final_state, err, waves, st); });
     }
     int rc = KDA_OK;
     if (!ok) {

@@ -9,9 +9,11 @@ namespace kda {
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
 constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
 
-// chunk offsets of cl-token chunks (cl = 16 or 32), longest-first order, error word reset
-hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            int32_t *err, int cl, hipStream_t st);
+// sanitised sequence offsets cu_safe[N+1] (ordered, inside [0, T]; the error word gets
+// 2 when cu was malformed, else 0), chunk offsets of cl-token chunks (cl = 16 or 32),
+// longest-first order. Later kernels take cu_safe as their cu.
+hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, int32_t *chunk_off,
+                            int32_t *order, int32_t *err, int cl, hipStream_t st);
 
 // 32-token records of chunks [cbeg, cend)
 hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,

@@ -20,14 +20,22 @@ static_assert(Rec32::BYTES == REC32_BYTES, "record size mismatch");
 __device__ float store_sink[64];
 
 // ---------------------------------------------------------------- chunk map
-// One workgroup. chunk_off[n] = number of cl-token chunks before sequence n
-// (chunk_off[N] = total); order[] lists sequences longest first (ties by
-// index) when N <= ORDER_MAX, else in input order.
+// One workgroup. First the sequence offsets are sanitised into cu_safe[N+1]: each
+// offset clamped to [0, T] and raised to the largest offset before it, so that the
+// ranges are ordered, inside [0, T], and add up to at most T tokens; every later
+// kernel reads cu_safe, so malformed cu_seqlens cannot send an access outside the
+// inputs, the outputs or the workspace (whose record area is sized for T tokens).
+// The error word is set to ERR_CU_SEQLENS when the offsets were not 0 = c_0 <= c_1
+// <= ... <= c_N = T. Then chunk_off[n] = number of cl-token chunks before sequence n
+// (chunk_off[N] = total), and order[] lists sequences longest first (ties by index)
+// when N <= ORDER_MAX, else in input order.
 constexpr int MAP_THREADS = 256;
 constexpr int ORDER_MAX = 2048;
+constexpr int ERR_CU_SEQLENS = 2;   // (bit 0 is the fused kernel's wait timeout)
 
 __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *__restrict__ cu,
                                                                  int N, int T,
+                                                                 int32_t *__restrict__ cu_safe,
                                                                  int32_t *__restrict__ chunk_off,
                                                                  int32_t *__restrict__ order,
                                                                  int32_t *__restrict__ err,
@@ -37,13 +45,39 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
     const int tid = threadIdx.x;
     if (tid == 0) carry = 0;
     __syncthreads();
+    // sanitised offsets: running maximum of the clamped offsets (inclusive scan)
+    int bad = 0;
+    for (int base = 0; base <= N; base += MAP_THREADS) {
+        const int n = base + tid;
+        int32_t x = 0;
+        if (n <= N) {
+            const int32_t raw = cu ? cu[n] : (n == 0 ? 0 : T);
+            x = min(max(raw, 0), T);
+            if (n == 0) bad |= raw != 0;
+            else bad |= raw < (cu ? cu[n - 1] : 0);
+            if (n == N) bad |= raw != T;
+        }
+        part[tid] = x;
+        __syncthreads();
+        for (int s = 1; s < MAP_THREADS; s <<= 1) {
+            const int32_t y = tid >= s ? part[tid - s] : 0;
+            __syncthreads();
+            part[tid] = max(part[tid], y);
+            __syncthreads();
+        }
+        if (n <= N) cu_safe[n] = max(carry, part[tid]);
+        __syncthreads();
+        if (tid == MAP_THREADS - 1) carry = max(carry, part[tid]);
+        __syncthreads();
+    }
+    bad = __syncthreads_or(bad);
+    // chunk counts of the sanitised ranges, exclusive scan into chunk_off
+    if (tid == 0) carry = 0;
+    __syncthreads();
     for (int base = 0; base < N; base += MAP_THREADS) {
         const int n = base + tid;
         int32_t c = 0;
-        if (n < N) {
-            const int32_t len = cu ? cu[n + 1] - cu[n] : T;
-            c = (len + cl - 1) / cl;
-        }
+        if (n < N) c = (cu_safe[n + 1] - cu_safe[n] + cl - 1) / cl;
         part[tid] = c;
         __syncthreads();
         for (int s = 1; s < MAP_THREADS; s <<= 1) {   // inclusive Hillis-Steele scan
@@ -59,14 +93,14 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
     }
     if (tid == 0) {
         chunk_off[0] = 0;
-        *err = 0;
+        *err = bad ? ERR_CU_SEQLENS : 0;
     }
     if (N <= ORDER_MAX) {
         for (int n = tid; n < N; n += MAP_THREADS) {
-            const int32_t ln = cu ? cu[n + 1] - cu[n] : T;
+            const int32_t ln = cu_safe[n + 1] - cu_safe[n];
             int rank = 0;
             for (int m = 0; m < N; ++m) {
-                const int32_t lm = cu ? cu[m + 1] - cu[m] : T;
+                const int32_t lm = cu_safe[m + 1] - cu_safe[m];
                 rank += (lm > ln) || (lm == ln && m < n);
             }
             order[rank] = n;
@@ -1601,9 +1635,9 @@ __global__ __launch_bounds__(64 * DK_WAVES) void recur_dk_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *chunk_off, int32_t *order,
-                            int32_t *err, int cl, hipStream_t st) {
-    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(MAP_THREADS), 0, st, cu, N, T, chunk_off,
+hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, int32_t *chunk_off,
+                            int32_t *order, int32_t *err, int cl, hipStream_t st) {
+    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(MAP_THREADS), 0, st, cu, N, T, cu_safe, chunk_off,
                        order, err, cl);
     return hipGetLastError();
 }

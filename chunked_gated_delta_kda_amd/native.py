@@ -91,8 +91,10 @@ def check(status):
 
 
 def error_word_offset(num_seqs):
-    """Byte offset of the device error word inside a kda_fwd_ex workspace (nonzero after
-    a call means a fused-kernel wait gave up and the outputs are not valid)."""
+    """Byte offset of the device error word inside a kda_fwd_ex workspace. After a call
+    it holds 0, or bit 0 (1): a fused-kernel wait gave up and the outputs are not valid,
+    or bit 1 (2): cu_seqlens was not 0 = c_0 <= ... <= c_N = T (the offsets were clamped
+    to [0, T] and made non-decreasing before use)."""
     a = lambda x: (x + 255) // 256 * 256
     return a(4 * (num_seqs + 1)) + a(4 * num_seqs)
 

@@ -89,8 +89,12 @@ typedef struct kda_options {
  *   cu_seqlens  int32 [num_seqs+1], 0 = c_0 <= c_1 <= ... <= c_N = total_tokens
  *               (sequence n owns tokens [c_n, c_{n+1})); NULL means one
  *               sequence of total_tokens tokens (then num_seqs must be 1).
- *               Monotonicity and c_N = total_tokens are preconditions that are
- *               not checked: violating them is undefined behaviour.
+ *               Monotonicity and c_N = total_tokens are preconditions checked on
+ *               the device: malformed offsets are clamped to [0, T] and made
+ *               non-decreasing before any kernel uses them (every access stays in
+ *               bounds; rows outside the resulting ranges are not written), and the
+ *               workspace's error word (see kda_workspace_bytes) is set to 2. The
+ *               recurrent variant clamps each sequence's range the same way.
  *   num_seqs    N >= 1;  total_tokens T >= 0;  num_heads H >= 1;  head_dim == 128
  *   initial_state  fp32 [N, H, 128(key), 128(value)] or NULL (zeros)
  *   out         fp32 [T, H, 128]: o_t (written for every token)
@@ -113,7 +117,11 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                float *final_state, void *stream, const kda_options *opt);
 
 /* Bytes of device workspace kda_fwd_ex needs for this shape and variant
- * (0 for a variant that needs none). Returns 0 for invalid shapes too. */
+ * (0 for a variant that needs none). Returns 0 for invalid shapes too.
+ * The workspace begins with int32 chunk offsets [N+1] and a sequence order [N],
+ * each padded to a multiple of 256 bytes, followed by an int32 error word that a
+ * call leaves at 0, or with bit 0 set (the fused variant's hand-off wait gave up:
+ * outputs invalid) or bit 1 set (malformed cu_seqlens, see kda_fwd). */
 size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                            int32_t variant);
 
