@@ -33,6 +33,25 @@ constexpr int MAP_THREADS = 256;
 constexpr int ORDER_MAX = 2048;
 constexpr int ERR_CU_SEQLENS = 2;   // (bit 0 is the fused kernel's wait timeout)
 
+// Inclusive scan over the workgroup (MAP_THREADS threads): shuffles within each wave,
+// then one exchange of the wave totals through LDS. op is max or +; both treat 0 as
+// the identity for the non-negative values scanned here.
+template <bool MAX>
+__device__ __forceinline__ int32_t block_scan(int32_t v, int32_t *wsum) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(v, off);
+        if (lane >= off) v = MAX ? max(v, y) : v + y;
+    }
+    if (lane == 63) wsum[w] = v;
+    __syncthreads();
+    int32_t pre = 0;
+    for (int i = 0; i < w; ++i) pre = MAX ? max(pre, wsum[i]) : pre + wsum[i];
+    __syncthreads();   // wsum free for the next scan
+    return MAX ? max(pre, v) : pre + v;
+}
+
 __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *__restrict__ cu,
                                                                  int N, int T,
                                                                  int32_t *__restrict__ cu_safe,
@@ -40,13 +59,14 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
                                                                  int32_t *__restrict__ order,
                                                                  int32_t *__restrict__ err,
                                                                  int cl) {
-    __shared__ int32_t part[MAP_THREADS];
-    __shared__ int32_t carry;
+    __shared__ int32_t wsum[MAP_THREADS / 64];
+    __shared__ int32_t last;   // the scan's last value: the carry into the next MAP_THREADS
+    __shared__ int32_t lcs[ORDER_MAX + 1];   // the sanitised offsets again, for N <= ORDER_MAX
     const int tid = threadIdx.x;
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    // sanitised offsets: running maximum of the clamped offsets (inclusive scan)
+    const bool in_lds = N <= ORDER_MAX;
+    // sanitised offsets: running maximum of the clamped offsets
     int bad = 0;
+    int32_t carry = 0;   // the same in every thread
     for (int base = 0; base <= N; base += MAP_THREADS) {
         const int n = base + tid;
         int32_t x = 0;
@@ -57,50 +77,40 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
             else bad |= raw < (cu ? cu[n - 1] : 0);
             if (n == N) bad |= raw != T;
         }
-        part[tid] = x;
-        __syncthreads();
-        for (int s = 1; s < MAP_THREADS; s <<= 1) {
-            const int32_t y = tid >= s ? part[tid - s] : 0;
-            __syncthreads();
-            part[tid] = max(part[tid], y);
-            __syncthreads();
+        const int32_t m = max(carry, block_scan<true>(x, wsum));
+        if (n <= N) {
+            cu_safe[n] = m;
+            if (in_lds) lcs[n] = m;
         }
-        if (n <= N) cu_safe[n] = max(carry, part[tid]);
+        if (tid == MAP_THREADS - 1) last = m;
         __syncthreads();
-        if (tid == MAP_THREADS - 1) carry = max(carry, part[tid]);
+        carry = last;
         __syncthreads();
     }
     bad = __syncthreads_or(bad);
-    // chunk counts of the sanitised ranges, exclusive scan into chunk_off
-    if (tid == 0) carry = 0;
-    __syncthreads();
+    // chunk counts of the sanitised ranges (written by this workgroup above)
+    const int32_t *cs = in_lds ? lcs : cu_safe;
+    carry = 0;
     for (int base = 0; base < N; base += MAP_THREADS) {
         const int n = base + tid;
-        int32_t c = 0;
-        if (n < N) c = (cu_safe[n + 1] - cu_safe[n] + cl - 1) / cl;
-        part[tid] = c;
+        const int32_t c = n < N ? (cs[n + 1] - cs[n] + cl - 1) / cl : 0;
+        const int32_t incl = carry + block_scan<false>(c, wsum);
+        if (n < N) chunk_off[n + 1] = incl;
+        if (tid == MAP_THREADS - 1) last = incl;
         __syncthreads();
-        for (int s = 1; s < MAP_THREADS; s <<= 1) {   // inclusive Hillis-Steele scan
-            const int32_t x = tid >= s ? part[tid - s] : 0;
-            __syncthreads();
-            part[tid] += x;
-            __syncthreads();
-        }
-        if (n < N) chunk_off[n + 1] = carry + part[tid];
-        __syncthreads();
-        if (tid == MAP_THREADS - 1) carry += part[tid];
+        carry = last;
         __syncthreads();
     }
     if (tid == 0) {
         chunk_off[0] = 0;
         *err = bad ? ERR_CU_SEQLENS : 0;
     }
-    if (N <= ORDER_MAX) {
+    if (in_lds) {
         for (int n = tid; n < N; n += MAP_THREADS) {
-            const int32_t ln = cu_safe[n + 1] - cu_safe[n];
+            const int32_t ln = lcs[n + 1] - lcs[n];
             int rank = 0;
             for (int m = 0; m < N; ++m) {
-                const int32_t lm = cu_safe[m + 1] - cu_safe[m];
+                const int32_t lm = lcs[m + 1] - lcs[m];
                 rank += (lm > ln) || (lm == ln && m < n);
             }
             order[rank] = n;

@@ -111,3 +111,20 @@ def test_full_config_sampled(cfg, variant):
     ok, mo, mf = compare(w, o, f, ro, rf, pairs=pairs)
     _say(f"  o {mo}\n  S {mf}")
     assert ok
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("N,maxlen", [(700, 40), (2100, 8)])
+def test_many_sequences(N, maxlen, variant):
+    """More sequences than the chunk map's 256 threads (its scans carry across passes),
+    and past 2048 sequences (no longest-first ranking); with 2 heads the split variant
+    runs the per-chain hybrid over 1,400 and 4,200 chains. Every chain is compared."""
+    rng = np.random.Generator(np.random.PCG64(N))
+    lengths = rng.integers(0, maxlen + 1, size=N)
+    w = synth.make_workload(lengths, 2, N, with_initial_state=True, clamp_frac=0.1)
+    _say(f"[parity] many sequences N={N} T={w.T} variant={variant}")
+    o, f = run_gpu(w, variant)
+    ro, rf = run_oracle(w)
+    ok, mo, mf = compare(w, o, f, ro, rf)
+    _say(f"  o {mo}\n  S {mf}")
+    assert ok
