@@ -20,6 +20,10 @@ its time is their sum. The CPU baseline is the fp64 oracle on the host cores, ti
 the same run on the same inputs; it also provides the parity check printed
 with the result.
 
+After the timed steps, COLD_STEPS more steps run each after a 512 MiB device write that
+evicts the L2s and the last-level cache; their median (HIP events around the call) is
+reported as "cold".
+
 With --decode N a step is one kda_decode call: one token for each of N sequences,
 the fp32 state updated in place, as in a decode loop; that mode prints its own
 JSON line (decode tokens/s, roofline against HBM for the state traffic).
@@ -50,6 +54,8 @@ KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "f
                                "recurrent": 1796}
 DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128)"
 EVENT_EVERY = 4                   # timed steps per step that records kernel events
+COLD_STEPS = 20                   # extra steps timed after a cache-evicting device write each
+COLD_FLUSH_BYTES = 512 << 20      # > the 256 MB last-level cache (MALL) plus the L2s
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -372,6 +378,19 @@ def main():
         kern_ms[nm] += float(np.mean([ev.ms(e[j], e[j + 1]) for e in sampled]))
     launches = {nm: plan.count(nm) for nm in names}
     ev.close()
+    # cold caches: each step after a 512 MiB write that evicts L2 and MALL (HIP events around
+    # the call only, on the stream the library uses)
+    flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(COLD_STEPS):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
     copy_calibration(args, dev)
     log(f"[bench] {ms_per_step:.4f} ms/step; kernels (ms summed over launches): {kern_ms}; "
         f"launches {launches}")
@@ -434,6 +453,8 @@ def main():
            "mfma_bf16_peak_frac": round(alg_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "path_hbm_frac": round(alg_bytes_total / step_s / 1e9 / HBM_PEAK_GBS, 4),
            "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
+           "cold": {"ms_per_step_median": round(float(np.median(cold)), 5), "steps": COLD_STEPS,
+                    "flush_bytes_before_each": COLD_FLUSH_BYTES},
            "kernel_launches": launches,
            "roofline": roofline, "cpu_baseline": None}
 

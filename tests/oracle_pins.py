@@ -186,6 +186,41 @@ def check_scalar_gate_is_gated_deltanet(fwd):
     assert np.max(np.abs(o_pc[:, 0] - wrong)) > 1e-3
 
 
+def check_g_zero_is_deltanet(fwd):
+    """g = 0: no decay, and KDA is the plain delta rule (DeltaNet),
+    S_t = S_{t-1} + b k (v - S_{t-1}^T k)^T, o_t = scale S_t^T q_t."""
+    rng = np.random.default_rng(23)
+    dk, dv, T = 6, 5, 30
+    q, k, v, _, b = _rand(rng, T, 1, dk, dv)
+    g = np.zeros((T, 1, dk))
+    s0 = rng.standard_normal((1, 1, dk, dv))
+    o, fin = fwd(q, k, v, g, b, 0.4, None, s0)
+    S = s0[0, 0].copy()
+    for t in range(T):
+        kt = k[t, 0]
+        S = S + b[t, 0] * np.outer(kt, v[t, 0] - S.T @ kt)
+        np.testing.assert_allclose(o[t, 0], 0.4 * S.T @ q[t, 0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(fin[0, 0], S, rtol=1e-11, atol=1e-12)
+
+
+def check_non_expansive(fwd):
+    """With b ||k||^2 in [0, 2] and g <= 0 the step matrix (I - b k k^T) Diag(e^g) has
+    spectral norm <= 1, so ||S_t||_2 <= ||S_{t-1}||_2 + b_t ||k_t|| ||v_t|| along a chain
+    (checked on every prefix of one sequence, with keys of norm up to sqrt(2))."""
+    rng = np.random.default_rng(29)
+    dk, dv, T = 8, 6, 24
+    q, k, v, g, b = _rand(rng, T, 1, dk, dv)
+    k = k * rng.uniform(0.2, math.sqrt(2.0), size=(T, 1, 1))
+    s0 = 3.0 * rng.standard_normal((1, 1, dk, dv))
+    prev = np.linalg.norm(s0[0, 0], 2)
+    for t in range(1, T + 1):
+        _, fin = fwd(q[:t], k[:t], v[:t], g[:t], b[:t], 1.0, None, s0)
+        cur = np.linalg.norm(fin[0, 0], 2)
+        bound = prev + b[t - 1, 0] * np.linalg.norm(k[t - 1, 0]) * np.linalg.norm(v[t - 1, 0])
+        assert cur <= bound + 1e-12, (t, cur, bound)
+        prev = cur
+
+
 def check_resume_and_packing(fwd):
     """Splitting a sequence and chaining final -> initial state, and packing sequences with
     cu_seqlens, both reproduce the single run."""
@@ -246,5 +281,5 @@ def check_clamp(fwd):
 
 ALL_CHECKS = [check_golden, check_single_token, check_beta_zero,
               check_orthogonal_keys_linear_attention, check_unit_write_readback, check_matrix_form,
-              check_chunked_forms, check_scalar_gate_is_gated_deltanet, check_resume_and_packing,
-              check_linearity_and_heads, check_clamp]
+              check_chunked_forms, check_scalar_gate_is_gated_deltanet, check_g_zero_is_deltanet,
+              check_non_expansive, check_resume_and_packing, check_linearity_and_heads, check_clamp]
