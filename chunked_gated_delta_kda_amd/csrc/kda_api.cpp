@@ -115,6 +115,32 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     return s < 1 ? 1 : s > 6 ? 6 : s;
 }
 
+// First chunk of segment sg of S over M chunks (segment_bound(M, S, S) = M). Segment
+// sizes grow geometrically by a ratio r: the first segment's prep runs alone, so a small
+// first segment shortens it, while each later prep (work per chunk ~ the chain count)
+// must still fit under the previous segment's recurrence (time per chunk independent of
+// the chain count). r = min(2, 1 + 8 / chains); measured on MI355X (ms for r = 1, 1.3,
+// 1.6, 2): 8192 tokens x 32 heads 0.433, 0.428, 0.435, 0.454; 65536 x 8 2.307, 2.293,
+// 2.280, 2.277. KDA_SEGMENT_RATIO overrides r, for tuning.
+double segment_ratio(int64_t chains) {
+    if (const char *e = std::getenv("KDA_SEGMENT_RATIO")) {
+        const double r = std::atof(e);
+        if (r >= 1.0 && r <= 4.0) return r;
+    }
+    const double r = 1.0 + 8.0 / (double)(chains > 0 ? chains : 1);
+    return r > 2.0 ? 2.0 : r;
+}
+int64_t segment_bound(int64_t M, int sg, int S, int64_t chains) {
+    if (sg <= 0) return 0;
+    if (sg >= S) return M;
+    const double r = segment_ratio(chains);
+    const double f = r == 1.0 ? (double)sg / S : (std::pow(r, sg) - 1.0) / (std::pow(r, S) - 1.0);
+    int64_t b = (int64_t)std::llround(f * (double)M);
+    // strictly increasing where M allows it
+    const int64_t lo = segment_bound(M, sg - 1, S, chains) + (M >= S ? 1 : 0), hi = M - (M >= S ? S - sg : 0);
+    return b < lo ? lo : b > hi ? hi : b;
+}
+
 // Consumer waves per block of the fused kernel (1, 2 or 4; 16 value columns each).
 // KDA_FUSED_WAVES overrides the choice, for tuning.
 int fused_waves(int64_t N, int64_t H) {
@@ -186,7 +212,7 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
-        auto bound = [&](int sg) { return (int32_t)((int64_t)M * sg / segs); };
+        auto bound = [&](int sg) { return (int32_t)segment_bound(M, sg, segs, (int64_t)num_seqs * num_heads); };
         plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0, cl};
         for (int sg = 0; sg + 1 < segs; ++sg)
             plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1), cl};
@@ -305,7 +331,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cus, chunk_off, order,
                                  N, T, H, initial_state, out, final_state,
                                  final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0};
-            auto bound = [&](int sg) { return M * sg / segs; };
+            auto bound = [&](int sg) { return segment_bound(M, sg, segs, (int64_t)N * H); };
             ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
                 a.cbeg = bound(sg), a.cend = bound(sg + 1), a.pbeg = bound(sg + 1), a.pend = bound(sg + 2);
