@@ -336,9 +336,11 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 //   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | loader | idle |
 //           output (slice 0, p1), (slice 1, p1)
 // (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
-#ifndef KDA_PAIR_NSLOT
-#define KDA_PAIR_NSLOT 4   // ring depth of the paired recurrence (chunks)
-#endif
+// Ring depth (chunks) of the paired recurrence. Measured on MI355X (ms per call, ring of
+// 4 | 5 | 6): one slice per block, 65536 tokens x 8 heads 2.275 | 2.174 | 2.168; two
+// slices per block, 8192 x 32 0.430 | 0.437 | 0.440 and 8 x 1024 x 16 0.187 | 0.190 | 0.191.
+template <int NW>
+constexpr int pair_nslot() { return NW == 1 ? 5 : 4; }
 
 template <int NW>
 struct PairLayout {
@@ -1725,11 +1727,11 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
 static hipError_t launch_recur_hybrid(const char *recs, const uint16_t *v, const int32_t *cu,
                                       const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                                       const float *s0, float *out, float *sfin, hipStream_t st) {
-    constexpr int pair = PairLds<2, KDA_PAIR_NSLOT>::BYTES;
+    constexpr int pair = PairLds<2, pair_nslot<2>()>::BYTES;
     constexpr int ring = HYBRID_RING * Ring<8>::SLOT;
     constexpr int lds = pair > ring ? pair : ring;
     static_assert(lds <= 160 * 1024, "LDS");
-    auto kern = recur_hybrid_kernel<KDA_PAIR_NSLOT>;
+    auto kern = recur_hybrid_kernel<pair_nslot<2>()>;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
@@ -1893,8 +1895,8 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
                               const float *s0, float *out, float *sfin, float *carry, int waves,
                               int cbeg, int cend, hipStream_t st) {
     switch (waves) {
-    case 101: return launch_recur_pair<1, KDA_PAIR_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 102: return launch_recur_pair<2, KDA_PAIR_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 101: return launch_recur_pair<1, pair_nslot<1>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 102: return launch_recur_pair<2, pair_nslot<2>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
     case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
     case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
     default: return hipErrorInvalidValue;
@@ -1903,8 +1905,8 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
 
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: return launch_recur_prep_t<1, KDA_PAIR_NSLOT>(a, st);
-    case 102: return launch_recur_prep_t<2, KDA_PAIR_NSLOT>(a, st);
+    case 101: return launch_recur_prep_t<1, pair_nslot<1>()>(a, st);
+    case 102: return launch_recur_prep_t<2, pair_nslot<2>()>(a, st);
     case 201: return launch_recur_direct_prep<1>(a, st);
     case 202: return launch_recur_direct_prep<2>(a, st);
     default: return hipErrorInvalidValue;
