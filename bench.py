@@ -402,16 +402,19 @@ def main():
     step_s = ms_per_step / 1e3
     tokens_per_s = T / step_s
 
-    # token counts per global chunk range, from the sequence lengths
+    # token counts per segment (a fraction of every sequence's chunks), from the lengths
     cl = chunk_len
-    chunk_tokens = np.concatenate([np.minimum(cl, L - cl * np.arange((L + cl - 1) // cl))
-                                   for L in w.lengths] + [np.zeros(0, np.int64)]).astype(np.int64)
-    csum = np.concatenate([[0], np.cumsum(chunk_tokens)])
-    n_ch = len(chunk_tokens)
+    seg_one = native.SEGMENT_ONE
+    seq_csum = [np.concatenate([[0], np.cumsum(np.minimum(cl, L - cl * np.arange((L + cl - 1) // cl)))])
+                for L in w.lengths]
 
     def tokens_in(r):
-        a, b = min(r[0], n_ch), min(r[1], n_ch)
-        return int(csum[b] - csum[a]) if b > a else 0
+        t = 0
+        for cs in seq_csum:
+            c = len(cs) - 1
+            a, b = c * r[0] // seg_one, c * r[1] // seg_one
+            t += int(cs[b] - cs[a]) if b > a else 0
+        return t
 
     def launch_alg_bytes(kind, prep_r, recur_r):
         """Bytes the algorithm must move in one launch: inputs read and outputs written
@@ -423,7 +426,7 @@ def main():
             return TH * KERNEL_BYTES_PER_TOKEN_HEAD[kind] + states
         b = (tokens_in(prep_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["prep"]
              + tokens_in(recur_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["recur"])
-        if recur_r[1] >= n_ch and recur_r[1] > recur_r[0]:
+        if recur_r[1] == seg_one and recur_r[1] > recur_r[0]:
             b += states
         return b
 

@@ -15,6 +15,7 @@ namespace {
 
 constexpr size_t ALIGN = 256;
 constexpr int KDA_MAX_SEGMENTS = 8;
+static_assert(KDA_SEGMENT_ONE == kda::SEG_ONE, "segment fraction unit");
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -115,13 +116,14 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     return s < 1 ? 1 : s > 6 ? 6 : s;
 }
 
-// First chunk of segment sg of S over M chunks (segment_bound(M, S, S) = M). Segment
-// sizes grow geometrically by a ratio r: the first segment's prep runs alone, so a small
-// first segment shortens it, while each later prep (work per chunk ~ the chain count)
-// must still fit under the previous segment's recurrence (time per chunk independent of
-// the chain count). r = min(2, 1 + 8 / chains); measured on MI355X (ms for r = 1, 1.3,
-// 1.6, 2): 8192 tokens x 32 heads 0.433, 0.428, 0.435, 0.454; 65536 x 8 2.307, 2.293,
-// 2.280, 2.277. KDA_SEGMENT_RATIO overrides r, for tuning.
+// Start of segment sg of S, as a fraction of every sequence's chunks in units of
+// 1/SEG_ONE (segment_frac(S, S) = SEG_ONE). Segment sizes grow geometrically by a ratio
+// r: the first segment's prep runs alone, so a small first segment shortens it, while
+// each later prep (work per chunk ~ the chain count) must still fit under the previous
+// segment's recurrence (time per chunk independent of the chain count).
+// r = min(2, 1 + 8 / chains); measured on MI355X (ms for r = 1, 1.3, 1.6, 2): 8192 tokens x
+// 32 heads 0.433, 0.428, 0.435, 0.454; 65536 x 8 2.307, 2.293, 2.280, 2.277.
+// KDA_SEGMENT_RATIO overrides r, for tuning.
 double segment_ratio(int64_t chains) {
     if (const char *e = std::getenv("KDA_SEGMENT_RATIO")) {
         const double r = std::atof(e);
@@ -130,15 +132,12 @@ double segment_ratio(int64_t chains) {
     const double r = 1.0 + 8.0 / (double)(chains > 0 ? chains : 1);
     return r > 2.0 ? 2.0 : r;
 }
-int64_t segment_bound(int64_t M, int sg, int S, int64_t chains) {
+int segment_frac(int sg, int S, int64_t chains) {
     if (sg <= 0) return 0;
-    if (sg >= S) return M;
+    if (sg >= S) return kda::SEG_ONE;
     const double r = segment_ratio(chains);
     const double f = r == 1.0 ? (double)sg / S : (std::pow(r, sg) - 1.0) / (std::pow(r, S) - 1.0);
-    int64_t b = (int64_t)std::llround(f * (double)M);
-    // strictly increasing where M allows it
-    const int64_t lo = segment_bound(M, sg - 1, S, chains) + (M >= S ? 1 : 0), hi = M - (M >= S ? S - sg : 0);
-    return b < lo ? lo : b > hi ? hi : b;
+    return (int)std::lround(f * kda::SEG_ONE);
 }
 
 // Consumer waves per block of the fused kernel (1, 2 or 4; 16 value columns each).
@@ -201,7 +200,6 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
                       : variant;
     const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
     const int cl = v == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
-    const int32_t M = (int32_t)max_chunks(num_seqs, total_tokens, cl);
     kda_launch_info plan[2 + KDA_MAX_SEGMENTS];
     int n = 0;
     if (v == KDA_VARIANT_RECURRENT) {
@@ -212,13 +210,13 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
-        auto bound = [&](int sg) { return (int32_t)segment_bound(M, sg, segs, (int64_t)num_seqs * num_heads); };
+        auto bound = [&](int sg) { return (int32_t)segment_frac(sg, segs, (int64_t)num_seqs * num_heads); };
         plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0, cl};
         for (int sg = 0; sg + 1 < segs; ++sg)
             plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1), cl};
-        plan[n++] = {KDA_KERNEL_RECUR, 0, 0, bound(segs - 1), M, cl};
+        plan[n++] = {KDA_KERNEL_RECUR, 0, 0, bound(segs - 1), KDA_SEGMENT_ONE, cl};
     } else {
-        plan[n++] = {KDA_KERNEL_FUSED, 0, M, 0, M, cl};
+        plan[n++] = {KDA_KERNEL_FUSED, 0, KDA_SEGMENT_ONE, 0, KDA_SEGMENT_ONE, cl};
     }
     for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
     return n;
@@ -313,31 +311,31 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, cl, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
-        auto prep = [&](int64_t b, int64_t e) {
-            return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, st)
-                       : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, st);
+        auto prep = [&](int b, int e) {
+            return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st)
+                       : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
         };
         auto recur_range = [&](float *carry, int b, int e) {
             return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
                        : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
         if (segs == 1) {
-            ok = around(st, [&] { return prep(0, M); }) &&
+            ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
                  around(st, [&] {
-                     return waves >= 100 ? recur_range(final_state, 0, 1 << 30)
+                     return waves >= 100 ? recur_range(final_state, 0, kda::SEG_ONE)
                                          : kda::launch_recur(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st);
                  });
         } else {
             kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cus, chunk_off, order,
                                  N, T, H, initial_state, out, final_state,
-                                 final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0};
-            auto bound = [&](int sg) { return segment_bound(M, sg, segs, (int64_t)N * H); };
+                                 final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0, M};
+            auto bound = [&](int sg) { return segment_frac(sg, segs, (int64_t)N * H); };
             ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
-                a.cbeg = bound(sg), a.cend = bound(sg + 1), a.pbeg = bound(sg + 1), a.pend = bound(sg + 2);
+                a.fb = bound(sg), a.fe = bound(sg + 1), a.pb = bound(sg + 1), a.pe = bound(sg + 2);
                 ok = around(st, [&] { return c32 ? kda::launch_recur32_prep(a, waves, st) : kda::launch_recur_prep(a, waves, st); });
             }
-            ok = ok && around(st, [&] { return recur_range(a.carry, (int)bound(segs - 1), (int)M); });
+            ok = ok && around(st, [&] { return recur_range(a.carry, bound(segs - 1), kda::SEG_ONE); });
         }
     } else if (ok) {
         ok = around(st, [&] { return kda::launch_fused(q16, k16, v16, g, beta, cus, order, N, T, H, scale, initial_state, out, final_state, err, waves, st); });

@@ -9,31 +9,45 @@ namespace kda {
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
 constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
 
+// Segments of the split path. A launch over the segment [fb, fe) covers, of every
+// sequence with c chunks, its local chunks [seg_chunk(c, fb), seg_chunk(c, fe)): fb <= fe
+// are fractions of a sequence in units of 1/SEG_ONE, and [0, SEG_ONE) is all of it. So
+// every sequence advances in every launch, however the lengths in a batch are spread.
+constexpr int SEG_ONE = 1 << 16;
+__host__ __device__ inline int seg_chunk(int c, int f) { return (int)(((int64_t)c * f) >> 16); }
+// Upper bound on the chunks of all sequences inside [fb, fe) when they have at most M in all.
+inline int64_t seg_chunks_bound(int64_t M, int N, int fb, int fe) {
+    if (fb == 0 && fe == SEG_ONE) return M;
+    const int64_t b = (M * (int64_t)(fe - fb) + SEG_ONE - 1) / SEG_ONE + N;
+    return b < M ? b : M;
+}
+
 // sanitised sequence offsets cu_safe[N+1] (ordered, inside [0, T]; the error word gets
 // 2 when cu was malformed, else 0), chunk offsets of cl-token chunks (cl = 16 or 32),
 // longest-first order. Later kernels take cu_safe as their cu.
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, int32_t *chunk_off,
                             int32_t *order, int32_t *err, int cl, hipStream_t st);
 
-// 32-token records of chunks [cbeg, cend)
+// Records (16-token chunks; 32-token with prep32) of the segment [fb, fe); M bounds the
+// batch's chunk count.
 hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                          const int32_t *cu, int N, int T, int H, float scale,
-                         const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                         const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
                          hipStream_t st);
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
-                       const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                       const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
                        hipStream_t st);
 
-// paired recurrence over the global chunk range [cbeg, cend); waves in {101, 102, 201, 202}
+// paired recurrence over the segment [fb, fe); waves in {101, 102, 201, 202}
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
                               const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                               const float *s0, float *out, float *sfin, float *carry, int waves,
-                              int cbeg, int cend, hipStream_t st);
+                              int fb, int fe, hipStream_t st);
 
-// One launch: paired recurrence over chunks [cbeg, cend) plus the records of
-// chunks [pbeg, pend) (the next range), prepared on the CUs the recurrence leaves idle.
+// One launch: paired recurrence over the segment [fb, fe) plus the records of the
+// segment [pb, pe) (the next one), prepared on the CUs the recurrence leaves idle.
 struct RecurPrepArgs {
     char *recs;
     const uint16_t *q, *k, *v;
@@ -43,15 +57,16 @@ struct RecurPrepArgs {
     int N, T, H;
     const float *s0;
     float *out, *sfin, *carry;
-    int64_t cbeg, cend, pbeg, pend;
+    int fb, fe, pb, pe;
+    int64_t M;          // bound on the batch's chunk count
 };
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
-// 32-token forms (waves 301: one slice per block, 302: two): recurrence over [cbeg, cend),
-// alone or with the prep of [pbeg, pend) on the idle CUs
+// 32-token forms (waves 301: one slice per block, 302: two): recurrence over the segment
+// [fb, fe), alone or with the prep of [pb, pe) on the idle CUs
 hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
                                 const int32_t *chunk_off, const int32_t *order, int N, int T,
                                 int H, const float *s0, float *out, float *sfin, float *carry,
-                                int waves, int cbeg, int cend, hipStream_t st);
+                                int waves, int fb, int fe, hipStream_t st);
 hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,

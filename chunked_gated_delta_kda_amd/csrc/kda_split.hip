@@ -142,6 +142,23 @@ __device__ __forceinline__ void prep_one(const uint16_t *__restrict__ q, const u
     prep_chunk(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * Rec::BYTES);
 }
 
+// Global index of the idx-th chunk-head (heads fastest, sequences in input order) of the
+// segment [fb, fe), or -1 past its end. The whole range is the global chunk order itself;
+// for a part of it the sequences are walked in turn (segmented launches serve few).
+__device__ __forceinline__ int seg_chunk_of(const int32_t *__restrict__ chunk_off, int N, int H,
+                                            int fb, int fe, int64_t idx, int &h) {
+    h = (int)(idx % H);
+    int64_t c = idx / H;
+    if (fb == 0 && fe == SEG_ONE) return c < chunk_off[N] ? (int)c : -1;
+    for (int n = 0; n < N; ++n) {
+        const int len = chunk_off[n + 1] - chunk_off[n];
+        const int b = seg_chunk(len, fb), e = seg_chunk(len, fe);
+        if (c < e - b) return chunk_off[n] + b + (int)c;
+        c -= e - b;
+    }
+    return -1;
+}
+
 __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q,
                                                   const uint16_t *__restrict__ k,
                                                   const float *__restrict__ g,
@@ -149,10 +166,11 @@ __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q
                                                   const int32_t *__restrict__ cu, int N, int T,
                                                   int H, float scale,
                                                   const int32_t *__restrict__ chunk_off,
-                                                  char *__restrict__ recs, int cbeg) {
+                                                  char *__restrict__ recs, int fb, int fe) {
     __shared__ PrepLds L;
-    const int ci = cbeg + (int)(blockIdx.x / H), h = blockIdx.x % H;
-    if (ci >= chunk_off[N]) return;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, fb, fe, blockIdx.x, h);
+    if (ci < 0) return;
     prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
 }
 
@@ -354,18 +372,18 @@ struct PairLayout {
     __device__ static constexpr int out_wave(int s, int p) { return NW == 1 ? 1 + p : (p ? 6 : 2) + s; }
 };
 
-// A launch covers the global chunk range [cbeg, cend) (launches over consecutive
-// ranges, in order on one stream, cover a batch). A sequence's state enters from
-// initial_state (or zeros) at its first chunk and from `carry` otherwise, and
-// leaves to final_state after its last chunk and to `carry` otherwise (carry may
-// be final_state itself). Sequences without chunks copy initial to final state
-// in the launch that starts at chunk 0.
+// A launch covers the segment [fb, fe) of every sequence (seg_chunk; launches over
+// consecutive segments, in order on one stream, cover a batch). A sequence's state
+// enters from initial_state (or zeros) at its first chunk and from `carry` otherwise,
+// and leaves to final_state after its last chunk and to `carry` otherwise (carry may
+// be final_state itself). Sequences without chunks copy initial to final state in
+// the launch of the first segment.
 template <int NW, int NSLOT>
 __device__ __forceinline__ void recur_pair_block(
     int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
-    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     using R = Ring<NW>;         // V tile geometry of NW slices
     using PL = PairLayout<NW>;
     constexpr int REC_LOADS = Rec::CHAIN / 1024;       // the chain's part of the record
@@ -390,11 +408,11 @@ __device__ __forceinline__ void recur_pair_block(
     const int col = vcol0 + slice * 16 + c;
     const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
     const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
-    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;      // this launch's chunks of the sequence
-    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
+    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);   // this launch's chunks of the sequence
+    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
     if (ci0 >= ci1) {
-        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+        if (seq_c0 == seq_c1 && fb == 0 && chain && sfin) {
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -661,10 +679,10 @@ template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
     recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
-                                order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                                order, N, T, H, s0, out, sfin, carry, fb, fe);
 }
 
 // ---------------------------------------------------------------- per-chain choice of shape
@@ -698,7 +716,7 @@ __global__ __launch_bounds__(64 * PairLayout<2>::WAVES) void recur_hybrid_kernel
     const int b = blockIdx.x;
     if (b < 4 * L) {
         recur_pair_block<2, NSLOT>(xcd_remap(b, 4 * L, 4), lds, recs, v, cu, chunk_off, order, N, T, H, s0, out,
-                                   sfin, sfin, 0, 1 << 30);
+                                   sfin, sfin, 0, SEG_ONE);
     } else if (b < 4 * L + (NH - L)) {
         recur_ring_block<8, HYBRID_RING>(L + xcd_remap(b - 4 * L, NH - L, 1), lds, recs, v, cu, chunk_off, order,
                                          N, T, H, s0, out, sfin);
@@ -706,8 +724,8 @@ __global__ __launch_bounds__(64 * PairLayout<2>::WAVES) void recur_hybrid_kernel
 }
 
 // ---------------------------------------------------------------- recurrence + next prep
-// One launch that runs the paired recurrence over the chunk range [cbeg, cend) in
-// blocks [0, RB) and prepares the records of the next range [pbeg, pend) in the
+// One launch that runs the paired recurrence over the segment [fb, fe) in
+// blocks [0, RB) and prepares the records of the next segment [pb, pe) in the
 // remaining blocks, PREP_WAVES chunk-heads per block (one per wave). Workgroups
 // are dispatched in index order and the LDS request admits one block per CU, so
 // the recurrence blocks take their CUs first and the prep blocks fill the CUs
@@ -721,21 +739,22 @@ template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_prep_kernel(
     const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
         recur_pair_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
-                                    order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                                    order, N, T, H, s0, out, sfin, carry, fb, fe);
         return;
     }
     constexpr int PW = RecurPrep<NW>::PREP_WAVES;
     const int w = threadIdx.x >> 6;
     if (w >= PW) return;
     const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
-    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
-    if (ci >= pend || ci >= chunk_off[N]) return;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
+    if (ci < 0) return;
     prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
              *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
@@ -766,7 +785,7 @@ __device__ __forceinline__ void recur_direct_block(
     int bid, char *lds, const char *__restrict__ recs, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
-    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     using DL = DirectLayout<NW>;
     constexpr int PARTS = D / (16 * NW);
     const int part = bid % PARTS;
@@ -781,11 +800,11 @@ __device__ __forceinline__ void recur_direct_block(
     const int col = part * 16 * NW + slice * 16 + c;
     const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
     const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
-    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;      // this launch's chunks of the sequence
-    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
+    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);   // this launch's chunks of the sequence
+    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
     if (ci0 >= ci1) {
-        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+        if (seq_c0 == seq_c1 && fb == 0 && chain && sfin) {
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -988,13 +1007,13 @@ template <int NW>
 __global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     recur_direct_block<NW>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), lds, recs, v, cu, chunk_off, order, N,
-                           T, H, s0, out, sfin, carry, cbeg, cend);
+                           T, H, s0, out, sfin, carry, fb, fe);
 }
 
-// recurrence over [cbeg, cend) in blocks [0, RB), prep of [pbeg, pend) in the rest
+// recurrence over the segment [fb, fe) in blocks [0, RB), prep of [pb, pe) in the rest
 // (the LDS request, above half a CU's, keeps prep blocks off the recurrence's CUs)
 template <int NW>
 struct DirectPrep {
@@ -1010,21 +1029,22 @@ template <int NW>
 __global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_prep_kernel(
     const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
         recur_direct_block<NW>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off, order, N,
-                               T, H, s0, out, sfin, carry, cbeg, cend);
+                               T, H, s0, out, sfin, carry, fb, fe);
         return;
     }
     constexpr int PW = DirectPrep<NW>::PREP_WAVES;
     const int w = threadIdx.x >> 6;
     if (w >= PW) return;
     const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
-    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
-    if (ci >= pend || ci >= chunk_off[N]) return;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
+    if (ci < 0) return;
     prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
              *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
@@ -1071,7 +1091,7 @@ __device__ __forceinline__ void recur_pair32_block(
     int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
-    float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     using P = Pair32<NW>;
     using PL = PairLayout<NW>;     // wave roles
     constexpr int LOADS = P::LOADS;
@@ -1095,11 +1115,11 @@ __device__ __forceinline__ void recur_pair32_block(
     const int col = vcol0 + slice * 16 + c;
     const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
     const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
-    const int ci0 = seq_c0 > cbeg ? seq_c0 : cbeg;
-    const int ci1 = seq_c1 < cend ? seq_c1 : cend;
+    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);   // this launch's chunks of the sequence
+    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
     if (ci0 >= ci1) {
-        if (seq_c0 == seq_c1 && cbeg == 0 && chain && sfin) {
+        if (seq_c0 == seq_c1 && fb == 0 && chain && sfin) {
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -1396,10 +1416,10 @@ template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair32_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend) {
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
     recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
-                                  order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                                  order, N, T, H, s0, out, sfin, carry, fb, fe);
 }
 
 // 32-token record of chunk ci (global index), head h
@@ -1427,10 +1447,11 @@ __global__ __launch_bounds__(64) void prep32_kernel(const uint16_t *__restrict__
                                                     const int32_t *__restrict__ cu, int N, int T,
                                                     int H, float scale,
                                                     const int32_t *__restrict__ chunk_off,
-                                                    char *__restrict__ recs, int cbeg) {
+                                                    char *__restrict__ recs, int fb, int fe) {
     __shared__ PrepLds L;
-    const int ci = cbeg + (int)(blockIdx.x / H), h = blockIdx.x % H;
-    if (ci >= chunk_off[N]) return;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, fb, fe, blockIdx.x, h);
+    if (ci < 0) return;
     prep32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
 }
 
@@ -1438,21 +1459,22 @@ template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur32_prep_kernel(
     const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int cbeg, int cend, int RB,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pbeg, int pend) {
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
         recur_pair32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
-                                      order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                                      order, N, T, H, s0, out, sfin, carry, fb, fe);
         return;
     }
     constexpr int PW = RecurPrep<NW>::PREP_WAVES;
     const int w = threadIdx.x >> 6;
     if (w >= PW) return;
     const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
-    const int ci = pbeg + (int)(idx / H), h = (int)(idx % H);
-    if (ci >= pend || ci >= chunk_off[N]) return;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
+    if (ci < 0) return;
     prep32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
                *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
@@ -1656,12 +1678,12 @@ hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, i
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
-                       const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                       const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
                        hipStream_t st) {
-    const int64_t blocks = (cend - cbeg) * H;
-    if (blocks <= 0) return hipSuccess;
+    const int64_t blocks = seg_chunks_bound(M, N, fb, fe) * H;
+    if (blocks <= 0 || fe <= fb) return hipSuccess;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N,
-                       T, H, scale, chunk_off, recs, (int)cbeg);
+                       T, H, scale, chunk_off, recs, fb, fe);
     return hipGetLastError();
 }
 
@@ -1707,7 +1729,7 @@ template <int NW, int NSLOT>
 static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const int32_t *cu,
                                     const int32_t *chunk_off, const int32_t *order, int N, int T,
                                     int H, const float *s0, float *out, float *sfin, float *carry,
-                                    int cbeg, int cend, hipStream_t st) {
+                                    int fb, int fe, hipStream_t st) {
     constexpr int lds = PairLds<NW, NSLOT>::BYTES;
     static_assert(lds <= 160 * 1024, "LDS");
     auto kern = recur_pair_kernel<NW, NSLOT>;
@@ -1720,7 +1742,7 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
-                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
     return hipGetLastError();
 }
 
@@ -1763,12 +1785,11 @@ static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
         attr_set = true;
     }
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
-    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
-    if (pb < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
+    const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
                        a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry,
-                       (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale, a.recs,
-                       (int)a.pbeg, (int)a.pend);
+                       a.fb, a.fe, (int)rb, a.q, a.k, a.g, a.beta, a.scale, a.recs,
+                       a.pb, a.pe);
     return hipGetLastError();
 }
 
@@ -1776,7 +1797,7 @@ template <int NW>
 static hipError_t launch_recur_direct(const char *recs, const uint16_t *v, const int32_t *cu,
                                       const int32_t *chunk_off, const int32_t *order, int N, int T,
                                       int H, const float *s0, float *out, float *sfin, float *carry,
-                                      int cbeg, int cend, hipStream_t st) {
+                                      int fb, int fe, hipStream_t st) {
     constexpr int lds = DirectLayout<NW>::BYTES;
     auto kern = recur_direct_kernel<NW>;
     static bool attr_set = false;
@@ -1788,7 +1809,7 @@ static hipError_t launch_recur_direct(const char *recs, const uint16_t *v, const
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
-                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
     return hipGetLastError();
 }
 
@@ -1806,23 +1827,22 @@ static hipError_t launch_recur_direct_prep(const RecurPrepArgs &a, hipStream_t s
         attr_set = true;
     }
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
-    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
-    if (pb < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
+    const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
                        a.recs, a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin,
-                       a.carry, (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
-                       a.recs, (int)a.pbeg, (int)a.pend);
+                       a.carry, a.fb, a.fe, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
+                       a.recs, a.pb, a.pe);
     return hipGetLastError();
 }
 
 hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                          const int32_t *cu, int N, int T, int H, float scale,
-                         const int32_t *chunk_off, char *recs, int64_t cbeg, int64_t cend,
+                         const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
                          hipStream_t st) {
-    const int64_t blocks = (cend - cbeg) * H;
-    if (blocks <= 0) return hipSuccess;
+    const int64_t blocks = seg_chunks_bound(M, N, fb, fe) * H;
+    if (blocks <= 0 || fe <= fb) return hipSuccess;
     hipLaunchKernelGGL(prep32_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N,
-                       T, H, scale, chunk_off, recs, (int)cbeg);
+                       T, H, scale, chunk_off, recs, fb, fe);
     return hipGetLastError();
 }
 
@@ -1830,7 +1850,7 @@ template <int NW, int NSLOT>
 static hipError_t launch_recur_pair32(const char *recs, const uint16_t *v, const int32_t *cu,
                                       const int32_t *chunk_off, const int32_t *order, int N, int T,
                                       int H, const float *s0, float *out, float *sfin, float *carry,
-                                      int cbeg, int cend, hipStream_t st) {
+                                      int fb, int fe, hipStream_t st) {
     constexpr int lds = Pair32Lds<NW, NSLOT>::BYTES;
     auto kern = recur_pair32_kernel<NW, NSLOT>;
     static bool attr_set = false;
@@ -1842,7 +1862,7 @@ static hipError_t launch_recur_pair32(const char *recs, const uint16_t *v, const
     }
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
-                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend);
+                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
     return hipGetLastError();
 }
 
@@ -1862,22 +1882,21 @@ static hipError_t launch_recur32_prep_t(const RecurPrepArgs &a, hipStream_t st) 
         attr_set = true;
     }
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
-    const int64_t pb = ((a.pend - a.pbeg) * a.H + PW - 1) / PW;
-    if (pb < 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pb)), dim3(64 * PairLayout<NW>::WAVES), lds, st,
+    const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st,
                        a.recs, a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin,
-                       a.carry, (int)a.cbeg, (int)a.cend, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
-                       a.recs, (int)a.pbeg, (int)a.pend);
+                       a.carry, a.fb, a.fe, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
+                       a.recs, a.pb, a.pe);
     return hipGetLastError();
 }
 
 hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
                                 const int32_t *chunk_off, const int32_t *order, int N, int T,
                                 int H, const float *s0, float *out, float *sfin, float *carry,
-                                int waves, int cbeg, int cend, hipStream_t st) {
+                                int waves, int fb, int fe, hipStream_t st) {
     switch (waves) {
-    case 301: return launch_recur_pair32<1, KDA_PAIR32_NSLOT1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 302: return launch_recur_pair32<2, KDA_PAIR32_NSLOT2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 301: return launch_recur_pair32<1, KDA_PAIR32_NSLOT1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 302: return launch_recur_pair32<2, KDA_PAIR32_NSLOT2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1893,12 +1912,12 @@ hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
                               const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                               const float *s0, float *out, float *sfin, float *carry, int waves,
-                              int cbeg, int cend, hipStream_t st) {
+                              int fb, int fe, hipStream_t st) {
     switch (waves) {
-    case 101: return launch_recur_pair<1, pair_nslot<1>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 102: return launch_recur_pair<2, pair_nslot<2>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
-    case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, cbeg, cend, st);
+    case 101: return launch_recur_pair<1, pair_nslot<1>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 102: return launch_recur_pair<2, pair_nslot<2>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1919,7 +1938,7 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
     switch (waves) {
     case 101: case 102: case 201: case 202:
         return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
-                                  waves, 0, 1 << 30, st);
+                                  waves, 0, SEG_ONE, st);
     case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);

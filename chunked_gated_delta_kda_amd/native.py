@@ -19,6 +19,7 @@ VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
            "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_status_string", "kda_version")
 STATE_DTYPES = {"f32": 0, "bf16": 1}
+SEGMENT_ONE = 65536   # KDA_SEGMENT_ONE: unit of the launch plan's segment fractions
 KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent"}
 
 
@@ -101,8 +102,9 @@ def error_word_offset(num_seqs):
 
 def launch_plan(num_seqs, total_tokens, num_heads, variant="auto"):
     """Kernel launches one kda_fwd_ex call makes for this shape, in order: a list of
-    (kind name, (prep_begin, prep_end), (recur_begin, recur_end), chunk_len), ranges in
-    chunk indices of chunk_len tokens."""
+    (kind name, (prep_begin, prep_end), (recur_begin, recur_end), chunk_len). A range is
+    a segment: a fraction of every sequence in units of 1/SEGMENT_ONE (of a sequence with
+    c chunks, chunks c*begin//SEGMENT_ONE to c*end//SEGMENT_ONE - 1)."""
     lib = load_library()
     info = (KdaLaunchInfo * 64)()
     n = lib.kda_launch_plan(num_seqs, total_tokens, num_heads, VARIANTS[variant], info, 64)

@@ -128,10 +128,14 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
 /* The variant KDA_VARIANT_AUTO resolves to for this shape. */
 int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
 
-/* One kernel launch of a kda_fwd_ex call: its KDA_KERNEL_* kind and the global
- * chunk ranges [begin, end) whose records it prepares and whose recurrence it runs
- * (chunks of chunk_len tokens, numbered sequence by sequence; a range may extend
- * past the last chunk; an empty range is 0, 0). */
+/* One kernel launch of a kda_fwd_ex call: its KDA_KERNEL_* kind and the segments
+ * [begin, end) whose records it prepares and whose recurrence it runs. A segment is a
+ * fraction of every sequence, in units of 1/KDA_SEGMENT_ONE: of a sequence with c
+ * chunks of chunk_len tokens it holds the chunks floor(c*begin/KDA_SEGMENT_ONE) to
+ * floor(c*end/KDA_SEGMENT_ONE) - 1, so that every sequence advances in every launch.
+ * [0, KDA_SEGMENT_ONE) is the whole batch; an empty range is 0, 0. */
+#define KDA_SEGMENT_ONE 65536
+
 typedef struct kda_launch_info {
     int32_t kind;
     int32_t prep_begin, prep_end;
@@ -142,8 +146,8 @@ typedef struct kda_launch_info {
 /* The kernel launches (in order) a kda_fwd_ex call with this shape and variant makes:
  * writes up to max_launches entries to info (may be NULL) and returns the count
  * (0 for an invalid shape). When the recurrence of a shape leaves CUs idle,
- * the split variant cuts the chunk range into segments and prepares the records
- * of segment s+1 inside the launch that runs the recurrence of segment s. */
+ * the split variant cuts the sequences into segments and prepares the records of
+ * segment s+1 inside the launch that runs the recurrence of segment s. */
 int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                         int32_t variant, kda_launch_info *info, int32_t max_launches);
 

@@ -119,19 +119,28 @@ def test_launch_plan():
         assert set(kinds[2:-1]) <= {"recur_prep"}
         cl = plan[0][3]
         assert cl in (16, 32) and all(p[3] == cl for p in plan)
-        M = (T + cl - 1) // cl + N
-        # the prep ranges and the recurrence ranges each tile [0, M) in order, and a
-        # range's records are prepared in an earlier launch than its recurrence
+        one = nat.SEGMENT_ONE
+        assert f"#define KDA_SEGMENT_ONE {one}" in open(HEADER).read()
+        # the prep segments and the recurrence segments each tile [0, SEGMENT_ONE) in
+        # order, and a segment's records are prepared in an earlier launch than its
+        # recurrence
         preps = [p[1] for p in plan[1:] if p[1] != (0, 0)]
         recs = [p[2] for p in plan[1:] if p[2] != (0, 0)]
         for ranges in (preps, recs):
-            assert ranges[0][0] == 0 and ranges[-1][1] == M
+            assert ranges[0][0] == 0 and ranges[-1][1] == one
             assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
+            assert all(a < b for a, b in ranges)
         for i, p in enumerate(plan):
             if p[2] != (0, 0):
                 lo, hi = p[2]
                 covered = [q[1] for q in plan[:i] if q[1] != (0, 0)]
                 assert any(a <= lo for a, _ in covered) and max(b for _, b in covered) >= hi
+        # of a sequence of any length, the recurrence segments take each chunk once
+        for c in (0, 1, 2, 7, 64, 513, 4096):
+            got = []
+            for lo, hi in recs:
+                got += range(c * lo // one, c * hi // one)
+            assert got == list(range(c))
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "recurrent")] == ["recurrent"]
