@@ -80,19 +80,23 @@ int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
             w == 102 || w == 201 || w == 202 || w == 301 || w == 302)
             return w;
     }
-    // measured on MI355X (ms; paired 102 | eight-wave 8): 128 chains (8 x 1024 tokens,
-    // 16 heads) 0.181 | 0.205; 192 chains 0.476 | 0.478; 512 chains of 2048 tokens
-    // 1.23 | 1.00; 8192 chains of 64 tokens 1.18 | 0.72; but 384 chains of skewed
-    // lengths (12 sequences, 32768 tokens, 32 heads) 1.29 | 2.43, where the longest
-    // chain sets the end time. From 192 chains the hybrid (9) picks per chain on the
-    // device: paired for chains longer than a CU's balanced share, eight-wave otherwise.
+    // Measured on MI355X (ms, best segment count each; one slice per block 101 | two
+    // slices 102), one sequence of 8192 tokens: 20 heads 0.326 | 0.370; 24 heads 0.356 |
+    // 0.384; 28 heads 0.391 | 0.401; 32 heads 0.408 | 0.417; 40 heads 0.673 | 0.460 (101
+    // needs two rounds of blocks from 33 chains). Then (ms; paired 102 | eight-wave 8):
+    // 128 chains (8 x 1024 tokens, 16 heads) 0.181 | 0.205; 192 chains 0.476 | 0.478; 512
+    // chains of 2048 tokens 1.23 | 1.00; 8192 chains of 64 tokens 1.18 | 0.72; but 384
+    // chains of skewed lengths (12 sequences, 32768 tokens, 32 heads) 1.29 | 2.43, where
+    // the longest chain sets the end time. From 192 chains the hybrid (9) picks per chain
+    // on the device: paired for chains longer than a CU's balanced share, eight-wave
+    // otherwise.
     const int64_t chains = N * H;
-    if (chains <= 16) return 101;
+    if (chains <= 32) return 101;
     if (chains < 192) return 102;
     return 9;
 }
 
-// Number of chunk-range segments of the split variant. With S > 1 the launches are
+// Number of segments of the split variant. With S > 1 the launches are
 // prep(segment 0), then recurrence(s) fused with prep(s+1) for s < S-1, then
 // recurrence(S-1): the prep of later segments runs on the CUs the recurrence leaves
 // idle, which pays when the recurrence has fewer blocks than the chip has CUs. 1 for
@@ -103,8 +107,15 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
         const int s = std::atoi(e);
         if (s >= 1 && s <= KDA_MAX_SEGMENTS) return s;
     }
-    const int64_t blocks = N * H * (8 / (waves % 100));
-    if (blocks >= 256) return 1;
+    // The prep of a segment (work ~ the chain count) runs on the CUs the recurrence
+    // leaves idle and must fit under its time: segments only with at least 2.5 idle CUs
+    // per chain. Measured on MI355X (ms, 8192 tokens; unsegmented | segmented): 101 with
+    // 20 heads (96 idle CUs) 0.359 | 0.326, 24 heads (64) 0.371 | 0.356, 28 heads (32)
+    // 0.391 | 0.401; 102 with 32 heads (128) 0.447 | 0.417, 40 heads (96) 0.476 | 0.460,
+    // 48 heads (64) 0.511 | 0.527, 56 heads (32) 0.548 | 0.602.
+    const int64_t chains = N * H;
+    const int64_t blocks = chains * (8 / (waves % 100));
+    if (2 * (256 - blocks) < 5 * chains) return 1;
     // S segments hide (1 - 1/S) of the prep (~7 ns per chunk-head on the whole chip)
     // and add S - 1 launches (~5 us each): S = sqrt(prep / 5 us), i.e. sqrt(chunk-heads
     // / 500), at most 6. Measured on MI355X (ms for 1 | 2 | 3 | 6 segments): 256 tokens x
