@@ -193,12 +193,14 @@ int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads
         if (!std::strcmp(e, "fused")) return KDA_VARIANT_FUSED;
         if (!std::strcmp(e, "recurrent")) return KDA_VARIANT_RECURRENT;
     }
-    // The token loop costs ~1.2 us per token of the longest sequence (plus ~12 us); the
-    // split variant at least ~34 us, and ~2 us per (sequence, head) chain when the
-    // sequences are short (measured on MI355X, 32 heads). The host cannot see the
-    // lengths, only T and N; with T <= max(16, 2N) even the most skewed split of the
-    // T tokens keeps the token loop ahead of the split variant's time.
-    if ((int64_t)total_tokens <= 16 || (int64_t)total_tokens <= 2 * (int64_t)num_seqs)
+    // The token loop costs ~0.9 us per token of the longest sequence (plus ~11 us); the
+    // split variant at least ~17 us (measured on MI355X, 32 heads, ms split | token
+    // loop: 1 sequence of 8 tokens 0.017 | 0.012, of 16 tokens 0.017 | 0.021; 256
+    // sequences of 1 token 0.313 | 0.102, of 8 tokens 0.328 | 0.192, of 16 tokens 0.341
+    // | 0.333). The host cannot see the lengths, only T and N; with T <= max(8, 2N) even
+    // the most skewed split of the T tokens (one sequence of T - N + 1) keeps the token
+    // loop ahead of the split variant.
+    if ((int64_t)total_tokens <= 8 || (int64_t)total_tokens <= 2 * (int64_t)num_seqs)
         return KDA_VARIANT_RECURRENT;
     return KDA_VARIANT_SPLIT;
 }
@@ -293,7 +295,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
 
     if (chosen == KDA_VARIANT_RECURRENT) {
-        const int dvt = kda::recurrent_tile((int64_t)N * H);
+        const int dvt = kda::recurrent_tile((int64_t)N * H, T, N);
         const bool ok = around(st, [&] {
             return kda::launch_recurrent(q16, k16, v16, g, beta, scale, cu_seqlens, N, T, H, false, initial_state,
                                          out, final_state, false, dvt, st);
@@ -393,7 +395,7 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
         overlaps(state_in, state_bytes, state_out, state_bytes))
         return KDA_ERR_ALIAS;
     hipStream_t st = (hipStream_t)stream;
-    const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads);
+    const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads, num_seqs, num_seqs);
     if (kda::launch_recurrent((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale,
                               nullptr, num_seqs, num_seqs, num_heads, true, state_in, out, state_out,
                               state_dtype == KDA_STATE_BF16, dvt, st) != hipSuccess)

@@ -80,8 +80,9 @@ hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t
                             const float *beta, float scale, const int32_t *cu, int N, int T, int H,
                             bool one_token_per_seq, const void *s0, float *out, void *sfin, bool bf16_state,
                             int dvt, hipStream_t st);
-// value-column tile of launch_recurrent for this many (sequence, head) chains
-int recurrent_tile(int64_t chains);
+// value-column tile of launch_recurrent for this many (sequence, head) chains over a
+// batch of `tokens` tokens in `seqs` sequences
+int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs);
 
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                         const float *beta, const int32_t *cu, const int32_t *order, int N, int T,

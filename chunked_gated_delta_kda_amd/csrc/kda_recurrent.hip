@@ -255,17 +255,21 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
 
 }  // namespace
 
-int recurrent_tile(int64_t chains) {
+int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs) {
     // KDA_RECURRENT_TILE (128, 64 or 32) overrides the choice, for tuning
     if (const char *e = std::getenv("KDA_RECURRENT_TILE")) {
         const int t = std::atoi(e);
         if (t == 128 || t == 64 || t == 32) return t;
     }
-    // measured on MI355X (decode, 32 heads; GB/s of state traffic): 256 sequences:
-    // 128 columns 5,625, 64 columns 5,646, 32 columns 5,345; 1024 sequences: 5,452,
-    // 5,516, 5,240. Below 1024 chains the narrow tile gives more blocks.
-    if (chains >= 1024) return 64;
-    return 32;
+    // Measured on MI355X, 32 heads (ms per call for 128 | 64 | 32 columns per block).
+    // One token per sequence (decode): 24 sequences 0.022 | 0.026 | 0.027; 256 sequences
+    // 0.202 | 0.199 | 0.211 (bf16 state 0.125 | 0.126 | 0.181). Several tokens per
+    // sequence: a wider tile shares the per-token work (inputs, barriers, q.k) over more
+    // columns, a narrower one gives more blocks: 1 x 16 tokens 0.025 | 0.022 | 0.020; 8 x
+    // 8 0.017 | 0.015 | 0.021; 64 x 16 0.096 | 0.124 | 0.222; 256 x 8 0.178 | 0.230 | 0.433.
+    if (tokens <= seqs) return chains >= 1024 ? 64 : 128;
+    if (chains >= 1024) return 128;
+    return chains >= 256 ? 64 : 32;
 }
 
 template <int DVT, bool BF16S>
