@@ -1,0 +1,153 @@
+"""GPU invariants at the full workload sizes, where the oracle checks sampled chains only.
+
+Properties of the recurrence that hold at any size, checked on the HIP path
+against itself:
+- resume: running a sequence in two calls, the first call's final state fed to
+  the second as initial state, gives the one-call result (to the parity gate:
+  the split moves chunk boundaries, so rounding differs);
+- packing: a packed varlen batch gives the same per-sequence results as separate
+  calls (to the parity gate);
+- permutation: permuting heads or sequences permutes the outputs, bit for bit
+  (each (sequence, head) chain is computed by the same instructions wherever it
+  is scheduled);
+- linearity: doubling v and the initial state doubles o and the final state
+  (every step is linear in (v, S0) and scaling by 2 is exact in bf16 and fp32
+  alike, so the results agree bit for bit except where a value is subnormal; the
+  test allows 1e-6 of the RMS).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from chunked_gated_delta_kda_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _fwd(d, variant="auto", **kw):
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+
+    args = dict(d)
+    args.update(kw)
+    o, f = kda.fwd(args["q"], args["k"], args["v"], args["g"], args["beta"], args["scale"],
+                   args["cu_seqlens"], args["initial_state"], variant=variant)
+    torch.cuda.synchronize()
+    return o, f
+
+
+def _gate(got, ref):
+    m = synth.parity(got.cpu().numpy(), ref.cpu().numpy())
+    return synth.passes(m), m
+
+
+def test_resume_config4():
+    import torch
+
+    w = synth.config_workload(4)
+    d = synth.to_device(w)
+    T = w.T
+    split = 40001                     # not a chunk multiple: partial chunks on both sides
+    _say(f"[invariants] resume: config 4, T={T}, split at {split}")
+    o, f = _fwd(d)
+    a = {k: (v[:split] if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    b = {k: (v[split:] if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    for x in (a, b):
+        for k in ("q", "k", "v", "g", "beta"):
+            x[k] = x[k].contiguous()
+        x["cu_seqlens"] = None        # one sequence each
+    o1, f1 = _fwd(a)
+    o2, f2 = _fwd(b, initial_state=f1)
+    ok_o, mo = _gate(torch.cat([o1, o2]), o)
+    ok_f, mf = _gate(f2, f)
+    _say(f"  o {mo}\n  S {mf}")
+    assert ok_o and ok_f
+
+
+def test_packing_config3():
+    import torch
+
+    w = synth.config_workload(3)
+    d = synth.to_device(w)
+    _say(f"[invariants] packing: config 3, {w.N} sequences")
+    o, f = _fwd(d)
+    cu = w.cu_seqlens
+    for n in range(w.N):
+        s = {k: (v[cu[n]:cu[n + 1]].contiguous() if k in ("q", "k", "v", "g", "beta") else v)
+             for k, v in d.items()}
+        s["cu_seqlens"] = None
+        s["initial_state"] = d["initial_state"][n:n + 1].contiguous()
+        on, fn = _fwd(s)
+        ok_o, mo = _gate(on, o[cu[n]:cu[n + 1]])
+        ok_f, mf = _gate(fn[0], f[n])
+        assert ok_o and ok_f, (n, mo, mf)
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "recurrent"])
+def test_head_permutation_config2(variant):
+    import torch
+
+    if variant == "recurrent":
+        w = synth.make_workload([2048], 32, 2, name="2048 tokens, 32 heads")   # the token loop is slow on long chains
+    else:
+        w = synth.config_workload(2)
+    d = synth.to_device(w)
+    perm = torch.from_numpy(np.random.Generator(np.random.PCG64(7)).permutation(w.H)).cuda()
+    _say(f"[invariants] head permutation: {w.meta.get('seed')} T={w.T} H={w.H} variant={variant}")
+    o, f = _fwd(d, variant)
+    p = {k: (v[:, perm].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    op, fp = _fwd(p, variant)
+    assert torch.equal(op, o[:, perm])
+    assert torch.equal(fp, f[:, perm])
+
+
+def test_sequence_permutation_config5():
+    import torch
+
+    w = synth.config_workload(5)
+    d = synth.to_device(w)
+    order = list(range(w.N))[::-1]
+    cu = w.cu_seqlens
+    _say(f"[invariants] sequence permutation: config 5, lengths {list(w.lengths)}")
+    o, f = _fwd(d)
+    idx = torch.cat([torch.arange(int(cu[n]), int(cu[n + 1])) for n in order]).cuda()
+    lens = np.array([w.lengths[n] for n in order])
+    cu_p = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    p = {k: (v[idx].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    p["cu_seqlens"] = torch.from_numpy(cu_p).cuda()
+    p["initial_state"] = d["initial_state"][order].contiguous()
+    op, fp = _fwd(p)
+    assert torch.equal(op, o[idx])
+    assert torch.equal(fp, f[order])
+
+
+@pytest.mark.parametrize("variant", ["auto", "fused", "recurrent"])
+def test_linearity_config3(variant):
+    import torch
+
+    w = synth.config_workload(3)
+    d = synth.to_device(w)
+    _say(f"[invariants] linearity: config 3, variant={variant}")
+    o, f = _fwd(d, variant)
+    two = dict(d)
+    two["v"] = (d["v"].float() * 2).to(torch.bfloat16)      # exact: a power of two
+    two["initial_state"] = d["initial_state"] * 2
+    o2, f2 = _fwd(two, variant)
+    for got, ref in ((o2, o * 2), (f2, f * 2)):
+        rms = float(ref.double().pow(2).mean().sqrt())
+        err = float((got - ref).abs().max())
+        exact = float((got != ref).double().mean())
+        _say(f"  max err {err:.3e} (RMS {rms:.3e}), share of inexact values {exact:.2e}")
+        assert err <= 1e-6 * rms
