@@ -295,7 +295,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const uint16_t *q16 = (const uint16_t *)q, *k16 = (const uint16_t *)k, *v16 = (const uint16_t *)v;
 
     if (chosen == KDA_VARIANT_RECURRENT) {
-        const int dvt = kda::recurrent_tile((int64_t)N * H, T, N);
+        const int dvt = kda::recurrent_tile((int64_t)N * H, T, N, false);
         const bool ok = around(st, [&] {
             return kda::launch_recurrent(q16, k16, v16, g, beta, scale, cu_seqlens, N, T, H, false, initial_state,
                                          out, final_state, false, dvt, st);
@@ -395,7 +395,8 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
         overlaps(state_in, state_bytes, state_out, state_bytes))
         return KDA_ERR_ALIAS;
     hipStream_t st = (hipStream_t)stream;
-    const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads, num_seqs, num_seqs);
+    const int dvt = kda::recurrent_tile((int64_t)num_seqs * num_heads, num_seqs, num_seqs,
+                                        state_dtype == KDA_STATE_BF16);
     if (kda::launch_recurrent((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale,
                               nullptr, num_seqs, num_seqs, num_heads, true, state_in, out, state_out,
                               state_dtype == KDA_STATE_BF16, dvt, st) != hipSuccess)

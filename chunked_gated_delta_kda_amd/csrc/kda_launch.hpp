@@ -75,14 +75,14 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
 
 // Token-by-token recurrence: one block per (sequence, head, tile of dvt value columns),
 // dvt in {128, 64, 32}. one_token_per_seq: sequence n is token n (decode step, cu unused).
-// States s0 / sfin are fp32, or bf16 with bf16_state.
+// States s0 / sfin are fp32, or bf16 with bf16_state (one token per sequence only).
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                             const float *beta, float scale, const int32_t *cu, int N, int T, int H,
                             bool one_token_per_seq, const void *s0, float *out, void *sfin, bool bf16_state,
                             int dvt, hipStream_t st);
 // value-column tile of launch_recurrent for this many (sequence, head) chains over a
-// batch of `tokens` tokens in `seqs` sequences
-int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs);
+// batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
+int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                         const float *beta, const int32_t *cu, const int32_t *order, int N, int T,

@@ -60,33 +60,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// CPT consecutive value columns of one key row: fp32 (CPT = 4: one 16-byte access) or
-// bf16 (CPT = 8: one 16-byte access)
-template <bool BF16S, int CPT>
-__device__ __forceinline__ void load_state(const void *base, int64_t i, float (&x)[CPT]) {
-    if constexpr (BF16S) {
-        static_assert(CPT == 8, "bf16 state: 8 columns per access");
-        const u32x4v y = __builtin_nontemporal_load((const u32x4v *)((const uint16_t *)base + i));
+// Four consecutive value columns of one key row of the fp32 state: one 16-byte access.
+__device__ __forceinline__ void load_state(const float *base, int64_t i, float (&x)[4]) {
+    const f32x4v y = __builtin_nontemporal_load((const f32x4v *)(base + i));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[2 * j] = bf16_lo(y[j]), x[2 * j + 1] = bf16_hi(y[j]);
-    } else {
-        static_assert(CPT == 4, "fp32 state: 4 columns per access");
-        const f32x4v y = __builtin_nontemporal_load((const f32x4v *)((const float *)base + i));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = y[j];
-    }
+    for (int j = 0; j < 4; ++j) x[j] = y[j];
 }
-template <bool BF16S, int CPT>
-__device__ __forceinline__ void store_state(void *base, int64_t i, const float (&x)[CPT]) {
-    if constexpr (BF16S) {
-        u32x4v y;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) y[j] = bf16_rne(x[2 * j]) | (bf16_rne(x[2 * j + 1]) << 16);
-        __builtin_nontemporal_store(y, (u32x4v *)((uint16_t *)base + i));
-    } else {
-        const f32x4v y = {x[0], x[1], x[2], x[3]};
-        __builtin_nontemporal_store(y, (f32x4v *)((float *)base + i));
-    }
+__device__ __forceinline__ void store_state(float *base, int64_t i, const float (&x)[4]) {
+    const f32x4v y = {x[0], x[1], x[2], x[3]};
+    __builtin_nontemporal_store(y, (f32x4v *)(base + i));
 }
 
 template <int DVT, int CPT>
@@ -128,12 +110,12 @@ __device__ __forceinline__ TokIn<CPT> load_token(const uint16_t *__restrict__ q,
     return r;
 }
 
-template <int DVT, bool BF16S>
+template <int DVT>
 __global__ __launch_bounds__(NT) void recurrent_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
-    int N, int T, int H, int one_token_per_seq, const void *s0, float *__restrict__ out, void *sfin) {
-    constexpr int CPT = BF16S ? 8 : 4;
+    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin) {
+    constexpr int CPT = 4;
     using TL = Tile<DVT, CPT>;
     __shared__ float sq[2][D], sk[2][D], se[2][D];
     __shared__ float sqk[2][2];
@@ -163,7 +145,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
 #pragma unroll
     for (int m = 0; m < TL::RPT; ++m) {
         if (s0) {
-            load_state<BF16S, CPT>(s0, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+            load_state(s0, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
         } else {
 #pragma unroll
             for (int j = 0; j < CPT; ++j) st[m][j] = 0.f;
@@ -249,13 +231,137 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     }
     if (sfin) {
 #pragma unroll
-        for (int m = 0; m < TL::RPT; ++m) store_state<BF16S, CPT>(sfin, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+        for (int m = 0; m < TL::RPT; ++m) store_state(sfin, sbase + (int64_t)(rg + TL::RG * m) * D, st[m]);
+    }
+}
+
+// The BF16-state decode step (one token per sequence). The state tile stays in
+// registers as it arrives, two bf16 per VGPR, and is widened where it is used: half the
+// registers of the fp32 copy, so a thread keeps twice the rows (and bytes) in flight
+// for the same occupancy. The arithmetic is that of recurrent_kernel on one token.
+// Widening through an opaque instruction: the sums use these, the update widens again in
+// plain code, so the compiler cannot keep the widened tile alive across the barrier in
+// place of the packed one.
+__device__ __forceinline__ float bf16_lo_opaque(uint32_t x) {
+    uint32_t r;
+    asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(x));
+    return __uint_as_float(r);
+}
+__device__ __forceinline__ float bf16_hi_opaque(uint32_t x) {
+    uint32_t r;
+    asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(x));
+    return __uint_as_float(r);
+}
+
+template <int DVT>
+__global__ __launch_bounds__(NT) void decode_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, float scale, int H,
+    const uint16_t *s0, float *__restrict__ out, uint16_t *sfin) {
+    constexpr int CPT = 8;
+    using TL = Tile<DVT, CPT>;
+    __shared__ float sq[D], sk[D], se[D];
+    __shared__ float sqk[2];
+    __shared__ float red[NWAVE][2][TL::CG][CPT];
+
+    const int tile = blockIdx.x % TL::TILES;
+    const int nh = blockIdx.x / TL::TILES;
+    const int h = nh % H, n = nh / H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % TL::CG, rg = tid / TL::CG;
+    const int col = tile * DVT + cg * CPT;
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+
+    u32x4v sp[TL::RPT];
+#pragma unroll
+    for (int m = 0; m < TL::RPT; ++m) {
+        if (s0)
+            sp[m] = __builtin_nontemporal_load((const u32x4v *)(s0 + sbase + (int64_t)(rg + TL::RG * m) * D));
+        else
+            sp[m] = u32x4v{0u, 0u, 0u, 0u};
+    }
+    const int64_t th = (int64_t)n * H + h;
+    const TokIn<CPT> cur = load_token<CPT>(q, k, v, g, beta, th, tid, col);
+    if (tid < D) {
+        sq[tid] = cur.q;
+        sk[tid] = cur.k;
+        se[tid] = __builtin_amdgcn_exp2f(fmaxf(cur.g, LB) * LOG2E_R);
+        float p = cur.q * cur.k;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) p += __shfl_xor(p, off);
+        if (lane == 0) sqk[wave] = p;
+    }
+    float vv[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT / 2; ++j) vv[2 * j] = bf16_lo(cur.v[j]), vv[2 * j + 1] = bf16_hi(cur.v[j]);
+    __syncthreads();
+
+    float u[CPT], w[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) u[j] = 0.f, w[j] = 0.f;
+#pragma unroll
+    for (int m = 0; m < TL::RPT; ++m) {
+        const int r = rg + TL::RG * m;
+        const float e = se[r], kr = sk[r], qr = sq[r];
+#pragma unroll
+        for (int j = 0; j < CPT / 2; ++j) {
+            const float lo = bf16_lo_opaque(sp[m][j]) * e, hi = bf16_hi_opaque(sp[m][j]) * e;
+            u[2 * j] = fmaf(kr, lo, u[2 * j]);
+            w[2 * j] = fmaf(qr, lo, w[2 * j]);
+            u[2 * j + 1] = fmaf(kr, hi, u[2 * j + 1]);
+            w[2 * j + 1] = fmaf(qr, hi, w[2 * j + 1]);
+        }
+    }
+#pragma unroll
+    for (int off = TL::CG; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) u[j] += __shfl_xor(u[j], off), w[j] += __shfl_xor(w[j], off);
+    }
+    if (lane < TL::CG) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) red[wave][0][lane][j] = u[j], red[wave][1][lane][j] = w[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) u[j] = red[0][0][cg][j], w[j] = red[0][1][cg][j];
+#pragma unroll
+    for (int x = 1; x < NWAVE; ++x) {
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) u[j] += red[x][0][cg][j], w[j] += red[x][1][cg][j];
+    }
+    const float qk = sqk[0] + sqk[1];
+    float dl[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) dl[j] = cur.beta * (vv[j] - u[j]);
+    if (sfin) {
+#pragma unroll
+        for (int m = 0; m < TL::RPT; ++m) {
+            const int r = rg + TL::RG * m;
+            const float e = se[r], kr = sk[r];
+            u32x4v y;
+#pragma unroll
+            for (int j = 0; j < CPT / 2; ++j) {
+                const float lo = fmaf(kr, dl[2 * j], bf16_lo(sp[m][j]) * e);
+                const float hi = fmaf(kr, dl[2 * j + 1], bf16_hi(sp[m][j]) * e);
+                y[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+            }
+            __builtin_nontemporal_store(y, (u32x4v *)(sfin + sbase + (int64_t)(rg + TL::RG * m) * D));
+        }
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int j = 0; j < CPT; j += 4) {
+            float4 o;
+            o.x = scale * fmaf(qk, dl[j], w[j]), o.y = scale * fmaf(qk, dl[j + 1], w[j + 1]);
+            o.z = scale * fmaf(qk, dl[j + 2], w[j + 2]), o.w = scale * fmaf(qk, dl[j + 3], w[j + 3]);
+            *(float4 *)(out + th * D + col + j) = o;
+        }
     }
 }
 
 }  // namespace
 
-int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs) {
+int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state) {
     // KDA_RECURRENT_TILE (128, 64 or 32) overrides the choice, for tuning
     if (const char *e = std::getenv("KDA_RECURRENT_TILE")) {
         const int t = std::atoi(e);
@@ -263,11 +369,12 @@ int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs) {
     }
     // Measured on MI355X, 32 heads (ms per call for 128 | 64 | 32 columns per block).
     // One token per sequence (decode): 24 sequences 0.022 | 0.026 | 0.027; 256 sequences
-    // 0.202 | 0.199 | 0.211 (bf16 state 0.125 | 0.126 | 0.181). Several tokens per
-    // sequence: a wider tile shares the per-token work (inputs, barriers, q.k) over more
-    // columns, a narrower one gives more blocks: 1 x 16 tokens 0.025 | 0.022 | 0.020; 8 x
-    // 8 0.017 | 0.015 | 0.021; 64 x 16 0.096 | 0.124 | 0.222; 256 x 8 0.178 | 0.230 | 0.433.
-    if (tokens <= seqs) return chains >= 1024 ? 64 : 128;
+    // 0.202 | 0.199 | 0.211; with the bf16 state (decode_bf16_kernel) 256 sequences 0.101 |
+    // 0.107-0.110, 1024 sequences 0.383 | 0.396. Several tokens per sequence: a wider
+    // tile shares the per-token work (inputs, barriers, q.k) over more columns, a narrower
+    // one gives more blocks: 1 x 16 tokens 0.025 | 0.022 | 0.020; 8 x 8 0.017 | 0.015 |
+    // 0.021; 64 x 16 0.096 | 0.124 | 0.222; 256 x 8 0.178 | 0.230 | 0.433.
+    if (tokens <= seqs) return (chains >= 1024 && !bf16_state) ? 64 : 128;
     if (chains >= 1024) return 128;
     return chains >= 256 ? 64 : 32;
 }
@@ -277,14 +384,19 @@ static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         float scale, const int32_t *cu, int N, int T, int H, bool one_token_per_seq, const void *s0,
                         float *out, void *sfin, hipStream_t st) {
     const int64_t blocks = (int64_t)N * H * (D / DVT);
-    hipLaunchKernelGGL((recurrent_kernel<DVT, BF16S>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
-                       scale, cu, N, T, H, (int)one_token_per_seq, s0, out, sfin);
+    if constexpr (BF16S)
+        hipLaunchKernelGGL((decode_bf16_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
+                           scale, H, (const uint16_t *)s0, out, (uint16_t *)sfin);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
+                           scale, cu, N, T, H, (int)one_token_per_seq, (const float *)s0, out, (float *)sfin);
 }
 
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                             const float *beta, float scale, const int32_t *cu, int N, int T, int H,
                             bool one_token_per_seq, const void *s0, float *out, void *sfin, bool bf16_state,
                             int dvt, hipStream_t st) {
+    if (bf16_state && !one_token_per_seq) return hipErrorInvalidValue;   // the BF16-state form is a decode step
 #define KDA_TILE_CASE(W)                                                                                     \
     case W:                                                                                                  \
         if (bf16_state)                                                                                      \
