@@ -162,7 +162,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
         if not m or name not in write:
             continue
         base = m.group(1)      # e.g. prep, recur_pair, recur_prep, fused, chunk_map
-        kind = ("recurrent" if base == "recurrent" else
+        kind = ("recurrent" if base in ("recurrent", "decode_bf16") else
                 "recur_prep" if base.startswith("recur") and base.endswith("_prep") else
                 "recur" if base.startswith("recur") else base)
         kinds[kind][0].extend(fetch[name])
@@ -180,7 +180,9 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
     if os.path.exists(TRAFFIC_FILE):
         prev = json.load(open(TRAFFIC_FILE)).get("kernels", {})
     prev.update(out["kernels"])
-    out["kernels"] = prev
+    # records taken on sources that have changed since describe kernels that no longer exist
+    out["kernels"] = {k: r for k, r in prev.items()
+                      if r.get("source_hash") == kernel_source_hash(k.split("@")[0])}
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
