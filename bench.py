@@ -162,7 +162,7 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
         if not m or name not in write:
             continue
         base = m.group(1)      # e.g. prep, recur_pair, recur_prep, fused, chunk_map
-        kind = ("recurrent" if base in ("recurrent", "decode_bf16") else
+        kind = ("recurrent" if base in ("recurrent", "decode") else
                 "recur_prep" if base.startswith("recur") and base.endswith("_prep") else
                 "recur" if base.startswith("recur") else base)
         kinds[kind][0].extend(fetch[name])

@@ -30,6 +30,7 @@
 
 #include <cstdint>
 #include <cstdlib>
+#include <type_traits>
 
 #include "kda.h"
 #include "kda_launch.hpp"
@@ -235,13 +236,14 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     }
 }
 
-// The BF16-state decode step (one token per sequence). The state tile stays in
-// registers as it arrives, two bf16 per VGPR, and is widened where it is used: half the
-// registers of the fp32 copy, so a thread keeps twice the rows (and bytes) in flight
-// for the same occupancy. The arithmetic is that of recurrent_kernel on one token.
-// Widening through an opaque instruction: the sums use these, the update widens again in
-// plain code, so the compiler cannot keep the widened tile alive across the barrier in
-// place of the packed one.
+// The decode step (one token per sequence), fp32 or bf16 state. The state tile stays in
+// registers as it arrives (for the bf16 state: two values per VGPR, half the registers of
+// an fp32 copy, so a thread keeps twice the rows and bytes in flight) and is widened
+// where it is used; without the token loop of recurrent_kernel (no next-token prefetch)
+// fewer registers are live. The arithmetic is that of recurrent_kernel on one token.
+// For the bf16 state the sums widen through an opaque instruction and the update widens
+// again in plain code, so the compiler cannot keep a widened tile alive across the
+// barrier in place of the packed one.
 __device__ __forceinline__ float bf16_lo_opaque(uint32_t x) {
     uint32_t r;
     asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(x));
@@ -253,12 +255,14 @@ __device__ __forceinline__ float bf16_hi_opaque(uint32_t x) {
     return __uint_as_float(r);
 }
 
-template <int DVT>
-__global__ __launch_bounds__(NT) void decode_bf16_kernel(
+template <int DVT, bool BF16S>
+__global__ __launch_bounds__(NT) void decode_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, int H,
-    const uint16_t *s0, float *__restrict__ out, uint16_t *sfin) {
-    constexpr int CPT = 8;
+    const void *s0, float *__restrict__ out, void *sfin) {
+    constexpr int CPT = BF16S ? 8 : 4;      // value columns per thread: one 16-byte state access per row
+    using SV = std::conditional_t<BF16S, u32x4v, f32x4v>;
+    using SE = std::conditional_t<BF16S, uint16_t, float>;
     using TL = Tile<DVT, CPT>;
     __shared__ float sq[D], sk[D], se[D];
     __shared__ float sqk[2];
@@ -272,13 +276,13 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(
     const int col = tile * DVT + cg * CPT;
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
 
-    u32x4v sp[TL::RPT];
+    SV sp[TL::RPT];
 #pragma unroll
     for (int m = 0; m < TL::RPT; ++m) {
         if (s0)
-            sp[m] = __builtin_nontemporal_load((const u32x4v *)(s0 + sbase + (int64_t)(rg + TL::RG * m) * D));
+            sp[m] = __builtin_nontemporal_load((const SV *)((const SE *)s0 + sbase + (int64_t)(rg + TL::RG * m) * D));
         else
-            sp[m] = u32x4v{0u, 0u, 0u, 0u};
+            sp[m] = SV{};
     }
     const int64_t th = (int64_t)n * H + h;
     const TokIn<CPT> cur = load_token<CPT>(q, k, v, g, beta, th, tid, col);
@@ -304,12 +308,15 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(
         const int r = rg + TL::RG * m;
         const float e = se[r], kr = sk[r], qr = sq[r];
 #pragma unroll
-        for (int j = 0; j < CPT / 2; ++j) {
-            const float lo = bf16_lo_opaque(sp[m][j]) * e, hi = bf16_hi_opaque(sp[m][j]) * e;
-            u[2 * j] = fmaf(kr, lo, u[2 * j]);
-            w[2 * j] = fmaf(qr, lo, w[2 * j]);
-            u[2 * j + 1] = fmaf(kr, hi, u[2 * j + 1]);
-            w[2 * j + 1] = fmaf(qr, hi, w[2 * j + 1]);
+        for (int j = 0; j < CPT; ++j) {
+            float x;
+            if constexpr (BF16S)
+                x = (j & 1) ? bf16_hi_opaque(sp[m][j >> 1]) : bf16_lo_opaque(sp[m][j >> 1]);
+            else
+                x = sp[m][j];
+            const float s1 = x * e;
+            u[j] = fmaf(kr, s1, u[j]);
+            w[j] = fmaf(qr, s1, w[j]);
         }
     }
 #pragma unroll
@@ -338,14 +345,19 @@ __global__ __launch_bounds__(NT) void decode_bf16_kernel(
         for (int m = 0; m < TL::RPT; ++m) {
             const int r = rg + TL::RG * m;
             const float e = se[r], kr = sk[r];
-            u32x4v y;
+            SV y;
+            if constexpr (BF16S) {
 #pragma unroll
-            for (int j = 0; j < CPT / 2; ++j) {
-                const float lo = fmaf(kr, dl[2 * j], bf16_lo(sp[m][j]) * e);
-                const float hi = fmaf(kr, dl[2 * j + 1], bf16_hi(sp[m][j]) * e);
-                y[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                for (int j = 0; j < CPT / 2; ++j) {
+                    const float lo = fmaf(kr, dl[2 * j], bf16_lo(sp[m][j]) * e);
+                    const float hi = fmaf(kr, dl[2 * j + 1], bf16_hi(sp[m][j]) * e);
+                    y[j] = bf16_rne(lo) | (bf16_rne(hi) << 16);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) y[j] = fmaf(kr, dl[j], sp[m][j] * e);
             }
-            __builtin_nontemporal_store(y, (u32x4v *)(sfin + sbase + (int64_t)(rg + TL::RG * m) * D));
+            __builtin_nontemporal_store(y, (SV *)((SE *)sfin + sbase + (int64_t)(rg + TL::RG * m) * D));
         }
     }
     if (rg == 0) {
@@ -368,13 +380,14 @@ int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state
         if (t == 128 || t == 64 || t == 32) return t;
     }
     // Measured on MI355X, 32 heads (ms per call for 128 | 64 | 32 columns per block).
-    // One token per sequence (decode): 24 sequences 0.022 | 0.026 | 0.027; 256 sequences
-    // 0.202 | 0.199 | 0.211; with the bf16 state (decode_bf16_kernel) 256 sequences 0.101 |
-    // 0.107-0.110, 1024 sequences 0.383 | 0.396. Several tokens per sequence: a wider
+    // One token per sequence (decode_kernel): fp32 state, 24 sequences 0.022 | 0.026 |
+    // 0.027, 256 sequences 0.195 | 0.199 | 0.208, 1024 sequences 0.812 | 0.801 | 0.833;
+    // bf16 state, 256 sequences 0.100 | 0.106, 1024 sequences 0.370 | 0.393. Several
+    // tokens per sequence (recurrent_kernel): a wider
     // tile shares the per-token work (inputs, barriers, q.k) over more columns, a narrower
     // one gives more blocks: 1 x 16 tokens 0.025 | 0.022 | 0.020; 8 x 8 0.017 | 0.015 |
     // 0.021; 64 x 16 0.096 | 0.124 | 0.222; 256 x 8 0.178 | 0.230 | 0.433.
-    if (tokens <= seqs) return (chains >= 1024 && !bf16_state) ? 64 : 128;
+    if (tokens <= seqs) return (chains >= 16384 && !bf16_state) ? 64 : 128;
     if (chains >= 1024) return 128;
     return chains >= 256 ? 64 : 32;
 }
@@ -384,12 +397,12 @@ static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         float scale, const int32_t *cu, int N, int T, int H, bool one_token_per_seq, const void *s0,
                         float *out, void *sfin, hipStream_t st) {
     const int64_t blocks = (int64_t)N * H * (D / DVT);
-    if constexpr (BF16S)
-        hipLaunchKernelGGL((decode_bf16_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
-                           scale, H, (const uint16_t *)s0, out, (uint16_t *)sfin);
-    else
+    if (one_token_per_seq)
+        hipLaunchKernelGGL((decode_kernel<DVT, BF16S>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
+                           scale, H, s0, out, sfin);
+    else if constexpr (!BF16S)
         hipLaunchKernelGGL((recurrent_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
-                           scale, cu, N, T, H, (int)one_token_per_seq, (const float *)s0, out, (float *)sfin);
+                           scale, cu, N, T, H, 0, (const float *)s0, out, (float *)sfin);
 }
 
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
