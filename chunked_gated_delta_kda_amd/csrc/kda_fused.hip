@@ -192,10 +192,14 @@ hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         const float *beta, const int32_t *cu, const int32_t *order, int N, int T,
                         int H, float scale, const float *s0, float *out, float *sfin, int *err,
                         int waves, hipStream_t st) {
+    // three producer waves: measured on MI355X (config 3, four slices per block, ms per
+    // call for 2 | 3 producers and 3 ring slots) 0.206 | 0.164; 3 or 4 producers with 2
+    // slots 0.211 (the consumers wait for the ring); 4 producers and 3 slots do not fit
+    // in LDS
     switch (waves) {
-    case 1: return launch_fused_t<1, 2, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
-    case 2: return launch_fused_t<2, 2, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
-    case 4: return launch_fused_t<4, 2, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
+    case 1: return launch_fused_t<1, 3, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
+    case 2: return launch_fused_t<2, 3, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
+    case 4: return launch_fused_t<4, 3, 3>(q, k, v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, st);
     default: return hipErrorInvalidValue;
     }
 }
