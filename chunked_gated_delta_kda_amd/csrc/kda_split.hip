@@ -355,8 +355,9 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 //           output (slice 0, p1), (slice 1, p1)
 // (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
 // Ring depth (chunks) of the paired recurrence. Measured on MI355X (ms per call, ring of
-// 4 | 5 | 6): one slice per block, 65536 tokens x 8 heads 2.275 | 2.174 | 2.168; two
-// slices per block, 8192 x 32 0.430 | 0.437 | 0.440 and 8 x 1024 x 16 0.187 | 0.190 | 0.191.
+// 4 | 5 | 6): one slice per block, 65536 tokens x 8 heads 2.275 | 2.174 | 2.168, 8192 x 32
+// 0.428 | 0.423 | 0.422; two slices per block, 8192 x 32 0.430 | 0.437 | 0.440 and 8 x
+// 1024 x 16 0.187 | 0.190 | 0.191.
 template <int NW>
 constexpr int pair_nslot() { return NW == 1 ? 5 : 4; }
 
