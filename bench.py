@@ -103,8 +103,33 @@ class HipEvents:
 
 # the sources each kernel kind is built and launched from
 _COMMON_SOURCES = ("kda_api.cpp", "kda_launch.hpp")
-KIND_SOURCES = {"recurrent": _COMMON_SOURCES + ("kda_recurrent.hip",)}
-_CHUNKED_SOURCES = _COMMON_SOURCES + ("kda_device.hpp", "kda_split.hip", "kda_fused.hip")
+KIND_SOURCES = {"recurrent": _COMMON_SOURCES + ("kda_recurrent.hip",),
+                "fused": _COMMON_SOURCES + ("kda_device.hpp", "kda_fused.hip")}
+_CHUNKED_SOURCES = _COMMON_SOURCES + ("kda_device.hpp", "kda_split.hip")
+
+
+def _code_only(text):
+    """C++ source without comments and blank-line/indent differences: a comment edit
+    leaves the kernels, and so the hash, unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # string or character literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(" ".join(line.split()) for line in "".join(out).splitlines() if line.strip())
 
 
 def kernel_source_hash(kind):
@@ -112,8 +137,8 @@ def kernel_source_hash(kind):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_gated_delta_kda_amd", "csrc")
     for f in sorted(KIND_SOURCES.get(kind, _CHUNKED_SOURCES)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
