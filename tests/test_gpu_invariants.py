@@ -151,3 +151,35 @@ def test_linearity_config3(variant):
         exact = float((got != ref).double().mean())
         _say(f"  max err {err:.3e} (RMS {rms:.3e}), share of inexact values {exact:.2e}")
         assert err <= 1e-6 * rms
+
+
+def test_affine_composition_config4():
+    """Context-parallel design check: a segment's chunk chain is affine in its entry
+    state, S_out = M S_in + B, with M the final state of a run from S_in = I with v = 0
+    and B the final state of a run from S_in = 0. Composing the last 41 tokens of config 4
+    this way from the final state of the tokens before reproduces the one-call final state.
+    The decays and the delta rule forget an entry state within tens of tokens (config 4's
+    own gates take M to ~1e-12 over 41 tokens), so g is scaled by 1/100 here and the
+    segment is short: otherwise M is 0 and the check is empty."""
+    import torch
+
+    w = synth.config_workload(4)
+    d = synth.to_device(w)
+    d["g"] = d["g"] * 0.01            # slow decays, so that 41 tokens do not forget the entry state
+    split = w.T - 41
+    _say(f"[invariants] affine composition: config 4 with g / 100, T={w.T}, split at {split}")
+    _, f = _fwd(d)
+    a = {k: (v[:split].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    b = {k: (v[split:].contiguous() if k in ("q", "k", "v", "g", "beta") else v) for k, v in d.items()}
+    a["cu_seqlens"] = b["cu_seqlens"] = None
+    _, f1 = _fwd(a)                                                   # true entry state of b
+    eye = torch.eye(128, device="cuda").expand(1, w.H, 128, 128).contiguous()
+    _, M = _fwd(b, v=torch.zeros_like(b["v"]), initial_state=eye)    # S_out for S_in = I, v = 0
+    _, B = _fwd(b, initial_state=torch.zeros_like(f1))               # S_out for S_in = 0
+    carried = M.double() @ f1.double()
+    # the entry state must matter for the check to mean anything
+    assert float(carried.norm()) > 0.1 * float(B.double().norm())
+    pred = (carried + B.double()).float()
+    ok, mf = _gate(pred, f)
+    _say(f"  carried/B norm {float(carried.norm() / B.double().norm()):.3f}\n  S {mf}")
+    assert ok
