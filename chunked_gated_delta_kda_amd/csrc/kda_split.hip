@@ -265,11 +265,15 @@ __device__ __forceinline__ void ring_wait(int w) {
     wait_vmcnt<(NSLOT - 2) * R::loads_of(W)>();
 }
 
+// Segments [fb, fe) of every sequence as in the paired recurrence below: the state
+// enters from s0 (or zeros) at a sequence's first chunk and from `carry` otherwise, and
+// leaves to sfin after its last chunk and to `carry` otherwise.
 template <int NW, int NSLOT>
 __device__ __forceinline__ void recur_ring_block(
     int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order,
-    int N, int T, int H, const float *s0, float *__restrict__ out, float *sfin) {
+    int N, int T, int H, const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb,
+    int fe) {
     using R = Ring<NW>;
     static_assert(NSLOT >= 2, "ring needs two slots");
     static_assert(R::loads_of(0) - R::loads_of(NW - 1) <= 1, "unbalanced ring loads");
@@ -281,16 +285,23 @@ __device__ __forceinline__ void recur_ring_block(
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
     const int vcol0 = part * R::VCOLS;            // first value column of this block
     const int col = vcol0 + w * 16 + c;           // this lane's value column
-    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
-    const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
+    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
+    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);   // this launch's chunks of the sequence
+    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
+    // a sequence without chunks copies its initial state in the first segment
+    if (ci0 >= ci1 && !(seq_c0 == seq_c1 && fb == 0)) return;
+    const int64_t bos = seq_bos + (int64_t)C * (ci0 - seq_c0);
+    const float *sin = ci0 == seq_c0 ? s0 : carry;
+    float *sout = ci1 == seq_c1 ? sfin : carry;
 
     f32x4 S[8];
     const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
-    if (s0) {
+    if (sin) {
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) S[b][j] = s0[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+            for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
     } else {
 #pragma unroll
         for (int b = 0; b < 8; ++b) S[b] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -319,11 +330,11 @@ __device__ __forceinline__ void recur_ring_block(
                 if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
         }
     }
-    if (sfin) {
+    if (sout) {
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sfin[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+            for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
     }
 }
 
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
     recur_ring_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
-                                order, N, T, H, s0, out, sfin);
+                                order, N, T, H, s0, out, sfin, sfin, 0, SEG_ONE);
 }
 
 
@@ -699,13 +710,36 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair_kernel(
 // working ones were measured to halve the working blocks' throughput).
 constexpr int HYBRID_RING = 4;   // ring depth of the eight-wave blocks (fits in the paired block's LDS)
 
+//
+// Over segments (as the paired recurrence below), blocks from 4 N H on prepare the
+// records of the next segment [pb, pe), HYBRID_PREP_WAVES chunk-heads per block: they
+// are dispatched after every recurrence block and take the CUs that the short chains
+// leave while the long ones run on.
+constexpr int HYBRID_PREP_WAVES = 4;
+
 template <int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<2>::WAVES) void recur_hybrid_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin) {
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
     static_assert(PairLayout<2>::WAVES == 8, "both shapes run eight waves");
     extern __shared__ __attribute__((aligned(16))) char lds[];
+    const int NH = N * H;
+    const int b = blockIdx.x;
+    if (b >= 4 * NH) {
+        constexpr int PW = HYBRID_PREP_WAVES;
+        const int w = threadIdx.x >> 6;
+        if (w >= PW) return;
+        const int64_t idx = (int64_t)(b - 4 * NH) * PW + w;
+        int h;
+        const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
+        if (ci < 0) return;
+        prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
+                 *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
+        return;
+    }
     const int64_t share = ((int64_t)chunk_off[N] * H + 255) / 256;
     int nlong = 0;   // sequences with more chunks than the share (the same count in every block)
     for (int base = 0; base < N; base += 64 * PairLayout<2>::WAVES) {
@@ -713,14 +747,12 @@ __global__ __launch_bounds__(64 * PairLayout<2>::WAVES) void recur_hybrid_kernel
         nlong += __syncthreads_count(s < N && chunk_off[s + 1] - chunk_off[s] > share);
     }
     const int L = nlong * H;              // long chains: the first L in chain order
-    const int NH = N * H;
-    const int b = blockIdx.x;
     if (b < 4 * L) {
         recur_pair_block<2, NSLOT>(xcd_remap(b, 4 * L, 4), lds, recs, v, cu, chunk_off, order, N, T, H, s0, out,
-                                   sfin, sfin, 0, SEG_ONE);
+                                   sfin, carry, fb, fe);
     } else if (b < 4 * L + (NH - L)) {
         recur_ring_block<8, HYBRID_RING>(L + xcd_remap(b - 4 * L, NH - L, 1), lds, recs, v, cu, chunk_off, order,
-                                         N, T, H, s0, out, sfin);
+                                         N, T, H, s0, out, sfin, carry, fb, fe);
     }
 }
 
@@ -1747,13 +1779,15 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
     return hipGetLastError();
 }
 
-static hipError_t launch_recur_hybrid(const char *recs, const uint16_t *v, const int32_t *cu,
-                                      const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
-                                      const float *s0, float *out, float *sfin, hipStream_t st) {
+// a.fb..a.fe: the recurrence's segment; a.pb..a.pe: the segment to prepare (none if equal)
+static hipError_t launch_recur_hybrid(const RecurPrepArgs &a, hipStream_t st) {
     constexpr int pair = PairLds<2, pair_nslot<2>()>::BYTES;
     constexpr int ring = HYBRID_RING * Ring<8>::SLOT;
-    constexpr int lds = pair > ring ? pair : ring;
-    static_assert(lds <= 160 * 1024, "LDS");
+    constexpr int rl = pair > ring ? pair : ring;
+    constexpr int prep = HYBRID_PREP_WAVES * (int)sizeof(PrepLds);
+    constexpr int lds = rl > prep ? rl : prep;
+    // more than 80 KiB: never two blocks on one CU
+    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
     auto kern = recur_hybrid_kernel<pair_nslot<2>()>;
     static bool attr_set = false;
     if (!attr_set) {
@@ -1762,9 +1796,12 @@ static hipError_t launch_recur_hybrid(const char *recs, const uint16_t *v, const
             return hipErrorInvalidValue;
         attr_set = true;
     }
-    const int64_t blocks = (int64_t)N * H * 4;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<2>::WAVES), lds, st, recs, v, cu,
-                       chunk_off, order, N, T, H, s0, out, sfin);
+    constexpr int PW = HYBRID_PREP_WAVES;
+    const int64_t rb = (int64_t)a.N * a.H * 4;
+    const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<2>::WAVES), lds, st, a.recs,
+                       a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry, a.fb, a.fe,
+                       a.q, a.k, a.g, a.beta, a.scale, a.recs, a.pb, a.pe);
     return hipGetLastError();
 }
 
@@ -1919,12 +1956,18 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
     case 102: return launch_recur_pair<2, pair_nslot<2>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 9: {
+        const RecurPrepArgs a{const_cast<char *>(recs), nullptr, nullptr, v, nullptr, nullptr, 0.f, cu, chunk_off,
+                              order, N, T, H, s0, out, sfin, carry, fb, fe, 0, 0, 0};
+        return launch_recur_hybrid(a, st);
+    }
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
     switch (waves) {
+    case 9: return launch_recur_hybrid(a, st);
     case 101: return launch_recur_prep_t<1, pair_nslot<1>()>(a, st);
     case 102: return launch_recur_prep_t<2, pair_nslot<2>()>(a, st);
     case 201: return launch_recur_direct_prep<1>(a, st);
@@ -1937,7 +1980,7 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: case 102: case 201: case 202:
+    case 101: case 102: case 201: case 202: case 9:
         return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
                                   waves, 0, SEG_ONE, st);
     case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
@@ -1947,7 +1990,6 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
     case 42: return launch_recur_t<4, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 8: return launch_recur_t<8, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 83: return launch_recur_t<8, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 9: return launch_recur_hybrid(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     default: return hipErrorInvalidValue;
     }
 }
