@@ -99,24 +99,23 @@ int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
 // Number of segments of the split variant. With S > 1 the launches are
 // prep(segment 0), then recurrence(s) fused with prep(s+1) for s < S-1, then
 // recurrence(S-1): the prep of later segments runs on the CUs the recurrence leaves
-// idle, which pays when the recurrence has fewer blocks than the chip has CUs (or, for
-// the hybrid, when its short chains free CUs early). 1 for the other recurrence forms.
-// KDA_SEGMENTS (1..KDA_MAX_SEGMENTS) overrides.
+// idle, which pays when the recurrence has fewer blocks than the chip has CUs. 1 for
+// the other recurrence forms. KDA_SEGMENTS (1..KDA_MAX_SEGMENTS) overrides (the hybrid
+// form included).
 int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     if (waves < 100 && waves != 9) return 1;
     if (const char *e = std::getenv("KDA_SEGMENTS")) {
         const int s = std::atoi(e);
         if (s >= 1 && s <= KDA_MAX_SEGMENTS) return s;
     }
-    // The hybrid fills the chip from the start, but its short chains finish early and
-    // leave CUs to the next segment's prep while the long chains run on. Measured on
-    // MI355X (ms for 1 | 2 | 3 | 4 segments): 12 skewed sequences of 32768 tokens x 32
-    // heads 1.272 | 1.220 | 1.258 | 1.286; 6 skewed sequences of 22528 tokens x 32 heads
-    // 0.987 | 0.910 | 0.914 | 0.922; 8 x 4096 x 32 1.125 | 1.068 | 1.068 | 1.092; 16 x
-    // 2048 x 32 1.123 | 1.096 | 1.122 | 1.172; 16 x 1024 x 16 0.319 | 0.321 | 0.334 |
-    // 0.344; 256 x 64 x 32 0.804 | 1.870 | 2.463 | 2.816. Two segments once sequences
-    // average 128 chunks (2048 tokens).
-    if (waves == 9) return T >= 2048 * N ? 2 : 1;
+    // The hybrid runs whole: its prep of a next segment waits for every recurrence block
+    // to be dispatched, and the chains below the longest keep the CUs busy for most of a
+    // segment. Measured on MI355X (ms for 1 | 2 | 3 segments, best of 4 alternating
+    // rounds): 12 skewed sequences of 32768 tokens x 32 heads 1.172 | 1.222 | 1.257; 6
+    // skewed sequences of 22528 tokens x 32 heads 0.950 | 0.910 | 0.907; 8 x 4096 x 32
+    // 1.023 | 1.052 | 1.075; 16 x 2048 x 32 1.032 | 1.084 | 1.124; 16 x 1024 x 16 0.263 |
+    // 0.299 | 0.322. KDA_SEGMENTS selects segments for it (parity-tested).
+    if (waves == 9) return 1;
     // The prep of a segment (work ~ the chain count) runs on the CUs the recurrence
     // leaves idle and must fit under its time: segments only with at least 2.5 idle CUs
     // per chain. Measured on MI355X (ms, 8192 tokens; unsegmented | segmented): 101 with

@@ -141,10 +141,8 @@ def test_launch_plan():
             for lo, hi in recs:
                 got += range(c * lo // one, c * hi // one)
             assert got == list(range(c))
-    # the per-chain hybrid (from 192 chains) runs in two segments only when sequences
-    # average at least 2048 tokens
-    assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur_prep", "recur"]
-    assert [p[0] for p in nat.launch_plan(256, 16384, 32, "split")] == ["chunk_map", "prep", "recur"]
+    # the per-chain hybrid (from 192 chains) runs whole by default
+    assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "recurrent")] == ["recurrent"]
