@@ -708,13 +708,11 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_pair_kernel(
 // dispatched first. The grid is sized for the case where every chain is long; blocks
 // past the ones in use exit at the end of the grid (spare blocks interleaved with
 // working ones were measured to halve the working blocks' throughput).
+// Over segments [fb, fe) (as the paired recurrence above; by default the form runs
+// whole), blocks from 4 N H on prepare the records of the next segment [pb, pe),
+// HYBRID_PREP_WAVES chunk-heads per block, as in recur_prep_kernel. They are dispatched
+// after every recurrence block.
 constexpr int HYBRID_RING = 4;   // ring depth of the eight-wave blocks (fits in the paired block's LDS)
-
-//
-// Over segments (as the paired recurrence below), blocks from 4 N H on prepare the
-// records of the next segment [pb, pe), HYBRID_PREP_WAVES chunk-heads per block: they
-// are dispatched after every recurrence block and take the CUs that the short chains
-// leave while the long ones run on.
 constexpr int HYBRID_PREP_WAVES = 4;
 
 template <int NSLOT>
