@@ -175,13 +175,8 @@ static hipError_t launch_fused_t(const uint16_t *q, const uint16_t *k, const uin
                                  hipStream_t st) {
     using LY = FusedLayout<NW, NP, NSLOT>;
     auto kern = fused_kernel<NW, NP, NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(
-            (const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY::BYTES);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (const hipError_t e = ensure_lds_limit((const void *)kern, LY::BYTES, lds_set); e != hipSuccess) return e;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * (NW + NP)), LY::BYTES, st, q, k,
                        v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err);

@@ -4,7 +4,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kda {
+
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once per device
+// (one process may drive several GPUs; concurrent callers may both set it, which is
+// harmless). `done` is the calling launcher's own bit set of devices (64 at most; a
+// device beyond that has the attribute set at every call).
+inline hipError_t ensure_lds_limit(const void *kern, int bytes, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t(1) << dev : 0;
+    if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
 constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)

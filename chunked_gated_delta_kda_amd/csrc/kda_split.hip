@@ -1724,13 +1724,8 @@ static hipError_t launch_recur_t(const char *recs, const uint16_t *v, const int3
                                  int H, const float *s0, float *out, float *sfin, hipStream_t st) {
     const size_t lds = (size_t)NSLOT * Ring<NW>::SLOT;
     auto kern = recur_kernel<NW, NSLOT>;
-    static bool attr_set = false;   // raising the dynamic LDS limit is per-kernel, idempotent
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, (int)lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, recs, v, cu,
                        chunk_off, order, N, T, H, s0, out, sfin);
@@ -1743,13 +1738,8 @@ static hipError_t launch_recur_dk(const char *recs, const uint16_t *v, const int
                                   int H, const float *s0, float *out, float *sfin, hipStream_t st) {
     const size_t lds = (size_t)DkLayout<NSLOT>::BYTES;
     auto kern = recur_dk_kernel<NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, (int)lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DK_WAVES), lds, st, recs, v, cu,
                        chunk_off, order, N, T, H, s0, out, sfin);
@@ -1764,13 +1754,8 @@ static hipError_t launch_recur_pair(const char *recs, const uint16_t *v, const i
     constexpr int lds = PairLds<NW, NSLOT>::BYTES;
     static_assert(lds <= 160 * 1024, "LDS");
     auto kern = recur_pair_kernel<NW, NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
                        recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
@@ -1787,13 +1772,8 @@ static hipError_t launch_recur_hybrid(const RecurPrepArgs &a, hipStream_t st) {
     // more than 80 KiB: never two blocks on one CU
     static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
     auto kern = recur_hybrid_kernel<pair_nslot<2>()>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds) !=
-            hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     constexpr int PW = HYBRID_PREP_WAVES;
     const int64_t rb = (int64_t)a.N * a.H * 4;
     const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
@@ -1813,13 +1793,8 @@ static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     // a CU with a recurrence block)
     static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
     auto kern = recur_prep_kernel<NW, NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
     const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
@@ -1836,13 +1811,8 @@ static hipError_t launch_recur_direct(const char *recs, const uint16_t *v, const
                                       int fb, int fe, hipStream_t st) {
     constexpr int lds = DirectLayout<NW>::BYTES;
     auto kern = recur_direct_kernel<NW>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
                        recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
@@ -1855,13 +1825,8 @@ static hipError_t launch_recur_direct_prep(const RecurPrepArgs &a, hipStream_t s
     constexpr int lds = DirectPrep<NW>::LDS;
     static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
     auto kern = recur_direct_prep_kernel<NW>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
     const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
@@ -1889,13 +1854,8 @@ static hipError_t launch_recur_pair32(const char *recs, const uint16_t *v, const
                                       int fb, int fe, hipStream_t st) {
     constexpr int lds = Pair32Lds<NW, NSLOT>::BYTES;
     auto kern = recur_pair32_kernel<NW, NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st,
                        recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
@@ -1910,13 +1870,8 @@ static hipError_t launch_recur32_prep_t(const RecurPrepArgs &a, hipStream_t st) 
     constexpr int lds = pair > prep ? pair : prep;
     static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
     auto kern = recur32_prep_kernel<NW, NSLOT>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds) != hipSuccess)
-            return hipErrorInvalidValue;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
     const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st,
