@@ -31,10 +31,35 @@ size_t rec_bytes(int waves) { return waves >= 300 ? kda::REC32_BYTES : kda::REC_
 // fp32 when the chunk range is cut into segments, followed by one chunk record per
 // (chunk, head).
 struct Layout {
-    size_t chunk_off, order, err, cu, carry, recs, total;
+    size_t chunk_off, order, err, cu, carry, recs, parts, total;
 };
 
-Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves) {
+constexpr int MAX_PARTS = 16;
+constexpr size_t STATE_BYTES = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
+
+// Parts per sequence of the split variant's recurrence (1: whole sequences; see
+// launch_parts). Pass 1 runs 8 N P H two-slice paired blocks and pass 2 8 N P H one-slice
+// blocks, so P <= 32 / (N H) keeps each pass within one round of the 256 CUs; three
+// passes over a P times shorter chain pay from P = 3. Parts are kept at 256 chunks or
+// more. Measured on MI355X (ms, whole | in P parts; best of 4 alternating rounds): one
+// sequence of 65536 tokens x 8 heads 2.16 | 1.74 (3), 1.41 (4); 32768 x 8 1.09 | 0.76 (4);
+// 65536 x 4 2.08 | 1.26 (4), 0.79 (8). KDA_PARTS (1..MAX_PARTS) overrides, for the
+// 16-token forms.
+int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
+    if (waves >= 300) return 1;
+    if (const char *e = std::getenv("KDA_PARTS")) {
+        const int p = std::atoi(e);
+        if (p >= 1 && p <= MAX_PARTS) return p;
+    }
+    if (waves != 101) return 1;
+    int64_t p = 32 / (N * H);
+    const int64_t by_len = max_chunks(N, T) / 256;
+    if (by_len < p) p = by_len;
+    if (p > MAX_PARTS) p = MAX_PARTS;
+    return p >= 3 ? (int)p : 1;
+}
+
+Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves, int parts = 1) {
     Layout L{};
     if (variant == KDA_VARIANT_RECURRENT) return L;  // reads cu_seqlens directly, no workspace
     L.chunk_off = 0;
@@ -47,7 +72,10 @@ Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int
     if (variant == KDA_VARIANT_SPLIT) {
         if (segments > 1)
             L.recs = L.carry + (size_t)N * H * KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(float);
-        L.total = L.recs + (size_t)max_chunks(N, T, chunk_len(waves)) * (size_t)H * rec_bytes(waves);
+        L.parts = L.recs + align_up((size_t)max_chunks(N, T, chunk_len(waves)) * (size_t)H * rec_bytes(waves));
+        L.total = L.parts;
+        if (parts > 1)   // identity, zero-run, identity-run and entry states; virtual cu, chunk offsets, order
+            L.total += 4 * (size_t)N * parts * H * STATE_BYTES + 3 * align_up(sizeof(int32_t) * (size_t)(N * parts + 1));
     }
     return L;
 }
@@ -233,6 +261,12 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
         auto bound = [&](int sg) { return (int32_t)segment_frac(sg, segs, (int64_t)num_seqs * num_heads); };
+        if (split_parts(num_seqs, total_tokens, num_heads, waves) > 1) {
+            plan[n++] = {KDA_KERNEL_PREP, 0, KDA_SEGMENT_ONE, 0, 0, cl};
+            plan[n++] = {KDA_KERNEL_PARTS, 0, 0, 0, KDA_SEGMENT_ONE, cl};
+            for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
+            return n;
+        }
         plan[n++] = {KDA_KERNEL_PREP, 0, bound(1), 0, 0, cl};
         for (int sg = 0; sg + 1 < segs; ++sg)
             plan[n++] = {KDA_KERNEL_RECUR_PREP, bound(sg + 1), bound(sg + 2), bound(sg), bound(sg + 1), cl};
@@ -252,7 +286,8 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
                       : variant;
     const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
     const int segs = v == KDA_VARIANT_SPLIT ? split_segments(num_seqs, total_tokens, num_heads, waves) : 1;
-    return ws_layout(num_seqs, total_tokens, num_heads, v, segs, waves).total;
+    const int parts = v == KDA_VARIANT_SPLIT ? split_parts(num_seqs, total_tokens, num_heads, waves) : 1;
+    return ws_layout(num_seqs, total_tokens, num_heads, v, segs, waves, parts).total;
 }
 
 int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
@@ -286,7 +321,8 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int N = num_seqs, T = total_tokens, H = num_heads;
     const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, H) : fused_waves(N, H);
     const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, T, H, waves) : 1;
-    const Layout lay = ws_layout(N, T, H, chosen, segs, waves);
+    const int parts = chosen == KDA_VARIANT_SPLIT ? split_parts(N, T, H, waves) : 1;
+    const Layout lay = ws_layout(N, T, H, chosen, segs, waves, parts);
     const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
     const bool c32 = cl == 32;
 
@@ -341,7 +377,21 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
                        : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
-        if (segs == 1) {
+        if (parts > 1) {
+            const int NV = N * parts;
+            const size_t sb = (size_t)NV * H * STATE_BYTES;
+            const size_t ib = align_up(sizeof(int32_t) * (size_t)(NV + 1));
+            char *pw = ws + lay.parts;
+            float *ident = (float *)pw, *rb = (float *)(pw + sb), *ri = (float *)(pw + 2 * sb);
+            float *sin = (float *)(pw + 3 * sb);
+            int32_t *vcu = (int32_t *)(pw + 4 * sb), *vco = (int32_t *)(pw + 4 * sb + ib);
+            int32_t *vorder = (int32_t *)(pw + 4 * sb + 2 * ib);
+            ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
+                 around(st, [&] {
+                     return kda::launch_parts(recs, v16, cus, chunk_off, order, N, T, H, parts, initial_state, out,
+                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, st);
+                 });
+        } else if (segs == 1) {
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
                  around(st, [&] {
                      return waves >= 100 ? recur_range(final_state, 0, kda::SEG_ONE)

@@ -105,4 +105,10 @@ hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int H, float scale, const float *s0, float *out, float *sfin, int *err,
                         int waves, hipStream_t st);
 
+// The recurrence over P parts of every sequence (few long chains); the buffers hold N P H
+// states each (ident, rb, ri, sin) and N P + 1 (vcu, vco) or N P (vorder) entries.
+hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
+                        const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
+                        float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
+                        float *ri, float *sin, hipStream_t st);
 }  // namespace kda

@@ -1947,4 +1947,119 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
     }
 }
 
+// ---------------------------------------------------------------- parts of long sequences
+// A sequence's chain of chunk steps is affine in its entry state: S_out = M S_in + B
+// (every step is linear in the state plus a term from the chunk's v). With few long
+// chains the paired recurrence leaves most CUs idle while each block walks thousands
+// of chunks, so every sequence is cut into P parts of about equal chunk count, each a
+// virtual sequence (contiguous in tokens and records). Pass 1 runs every part twice in
+// one launch, from S_in = 0 (final state B) and from S_in = I (final state M + B); the
+// composition kernel walks the parts of each sequence in order, S_{p+1} = M_p S_p + B_p
+// from the sequence's initial state, and writes each part's entry state and the final
+// state; pass 2 re-runs every part from its entry state and writes the outputs. The
+// chain is then P times shorter for three passes of it, two of them side by side.
+
+// virtual batch: part p of sequence n (at position n of `order`) is virtual sequence n P + p,
+// covering its chunks [seg(c, p/P), seg(c, (p+1)/P)); also fills the identity entry states
+__global__ __launch_bounds__(256) void parts_setup_kernel(const int32_t *cu_safe, const int32_t *chunk_off,
+                                                          const int32_t *order, int N, int P, int32_t *vcu,
+                                                          int32_t *vco, int32_t *vorder, float *ident,
+                                                          int64_t nstates) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = tid; v < (int64_t)N * P; v += nth) {
+        const int n = (int)(v / P), p = (int)(v % P);
+        const int c0 = chunk_off[n], c = chunk_off[n + 1] - c0;
+        const int k = seg_chunk(c, (int)(((int64_t)p * SEG_ONE) / P));
+        vco[v] = c0 + k;
+        vcu[v] = min(cu_safe[n + 1], cu_safe[n] + C * k);
+        vorder[v] = order[n] * P + p;
+        if (v == (int64_t)N * P - 1) {
+            vco[v + 1] = chunk_off[N];
+            vcu[v + 1] = cu_safe[N];
+        }
+    }
+    for (int64_t i = tid; i < nstates * D * D; i += nth) {
+        const int rc = (int)(i % (D * D));
+        ident[i] = rc / D == rc % D ? 1.f : 0.f;
+    }
+}
+
+// pass 1: blocks [0, G/2) run every part from a zero state, blocks [G/2, G) from the identity
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
+    const int32_t *__restrict__ vco, const int32_t *__restrict__ vorder, int NV, int T, int H,
+    const float *ident, float *out, float *rb, float *ri) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    const int RB = (int)(gridDim.x / 2);
+    const bool id = (int)blockIdx.x >= RB;
+    const int b = id ? (int)blockIdx.x - RB : (int)blockIdx.x;
+    recur_pair_block<NW, NSLOT>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
+                                id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE);
+}
+
+// composition over the parts of each sequence, one block per (sequence, head, 16 value
+// columns): the columns of a state evolve independently under M
+__global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, const float *rb, const float *ri,
+                                                            int N, int P, int H, float *sin, float *sfin) {
+    __shared__ float S[D][16];
+    const int cs = blockIdx.x % 8, h = (blockIdx.x / 8) % H, n = blockIdx.x / (8 * H);
+    const int t = threadIdx.x, r = t >> 1, c0 = (t & 1) * 8, col0 = cs * 16;
+    for (int i = t; i < D * 16; i += 256) {
+        const int rr = i / 16, cc = i % 16;
+        S[rr][cc] = s0 ? s0[((int64_t)n * H + h) * D * D + (int64_t)rr * D + col0 + cc] : 0.f;
+    }
+    __syncthreads();
+    for (int p = 0; p < P; ++p) {
+        const int64_t base = (((int64_t)n * P + p) * H + h) * D * D;
+        float acc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = rb[base + (int64_t)r * D + col0 + c0 + j];
+        for (int k = 0; k < D; ++k) {
+            const float m = ri[base + (int64_t)r * D + k] - rb[base + (int64_t)r * D + k];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] = fmaf(m, S[k][c0 + j], acc[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sin[base + (int64_t)r * D + col0 + c0 + j] = S[r][c0 + j];
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 8; ++j) S[r][c0 + j] = acc[j];
+        __syncthreads();
+    }
+    if (sfin) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sfin[((int64_t)n * H + h) * D * D + (int64_t)r * D + col0 + c0 + j] = S[r][c0 + j];
+    }
+}
+
+// setup, pass 1 (two-slice paired blocks: 8 N P H of them), composition, pass 2 (one-slice
+// paired blocks, no state written: the composition wrote the final state)
+hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
+                        const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
+                        float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
+                        float *ri, float *sin, hipStream_t st) {
+    const int NV = N * P;
+    const int64_t ns = (int64_t)NV * H;
+    hipLaunchKernelGGL(parts_setup_kernel, dim3(512), dim3(256), 0, st, cu_safe, chunk_off, order, N, P, vcu, vco,
+                       vorder, ident, ns);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    {
+        constexpr int NW = 2, NS = pair_nslot<2>();
+        constexpr int lds = PairLds<NW, NS>::BYTES;
+        auto kern = recur_parts_kernel<NW, NS>;
+        static std::atomic<uint64_t> lds_set{0};
+        if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
+        const int64_t rbk = (int64_t)NV * H * (D / (16 * NW));
+        hipLaunchKernelGGL(kern, dim3((unsigned)(2 * rbk)), dim3(64 * PairLayout<NW>::WAVES), lds, st, recs, v, vcu,
+                           vco, vorder, NV, T, H, (const float *)ident, out, rb, ri);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), 0, st, s0, (const float *)rb,
+                       (const float *)ri, N, P, H, sin, sfin);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    return launch_recur_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 101, 0, SEG_ONE, st);
+}
+
 }  // namespace kda

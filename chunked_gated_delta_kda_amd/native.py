@@ -20,7 +20,7 @@ EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
            "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_status_string", "kda_version")
 STATE_DTYPES = {"f32": 0, "bf16": 1}
 SEGMENT_ONE = 65536   # KDA_SEGMENT_ONE: unit of the launch plan's segment fractions
-KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent"}
+KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent", 6: "parts"}
 
 
 class KdaOptions(ctypes.Structure):

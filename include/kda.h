@@ -62,6 +62,7 @@ typedef enum kda_variant {
 #define KDA_KERNEL_FUSED 3
 #define KDA_KERNEL_RECUR_PREP 4   /* recurrence over one chunk range + prep of the next */
 #define KDA_KERNEL_RECURRENT 5    /* token-by-token recurrence (no chunk ranges)          */
+#define KDA_KERNEL_PARTS 6        /* recurrence over parts of each sequence: setup, two passes, composition */
 
 typedef struct kda_options {
     int32_t variant;        /* kda_variant                                              */

@@ -112,7 +112,7 @@ def test_workspace_bytes(lib):
 
 def test_launch_plan():
     from chunked_gated_delta_kda_amd import native as nat
-    for N, T, H in ((1, 8192, 32), (1, 65536, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32)):
+    for N, T, H in ((1, 8192, 32), (2, 65536, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32)):
         plan = nat.launch_plan(N, T, H, "split")
         kinds = [p[0] for p in plan]
         assert kinds[:2] == ["chunk_map", "prep"] and kinds[-1] == "recur"
@@ -141,6 +141,11 @@ def test_launch_plan():
             for lo, hi in recs:
                 got += range(c * lo // one, c * hi // one)
             assert got == list(range(c))
+    # few long chains: the recurrence runs over parts of each sequence, in one launch
+    # entry after the prep of all chunks
+    assert [p[0] for p in nat.launch_plan(1, 65536, 8, "split")] == ["chunk_map", "prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 65536, 4, "split")] == ["chunk_map", "prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 2048, 8, "split")] == ["chunk_map", "prep", "recur"]
     # the per-chain hybrid (from 192 chains) runs whole by default
     assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]

@@ -5,7 +5,8 @@ KDA_RECUR_WAVES and KDA_SEGMENTS environment overrides force each of the others
 here, so that every form stays checked against the fp64 oracle on shapes that
 cross segment boundaries inside sequences, hold empty sequences, and carry the
 state between segments through final_state, through the workspace (no final
-state requested), and in place (final_state aliasing initial_state).
+state requested), and in place (final_state aliasing initial_state); and the
+recurrence over parts of every sequence (KDA_PARTS).
 """
 import sys
 
@@ -52,13 +53,28 @@ def test_form_and_segments(workload, form, segments, monkeypatch):
     assert ok
 
 
-@pytest.mark.parametrize("segments", [1, 4])
-def test_no_final_state_and_in_place(workload, segments, monkeypatch):
+@pytest.mark.parametrize("parts", [2, 3, 5, 16])
+def test_parts(workload, parts, monkeypatch):
+    """The recurrence over parts of every sequence (pass 1 from zero and identity entry
+    states, composition, pass 2), forced on the varlen batch: some parts of the short
+    sequences hold no chunks, and the empty sequence passes its initial state through."""
+    monkeypatch.setenv("KDA_PARTS", str(parts))
+    w, (ro, rf) = workload
+    _say(f"[forms] parts={parts} lengths={LENGTHS}")
+    o, f = run_gpu(w, "split")
+    ok, mo, mf = compare(w, o, f, ro, rf)
+    _say(f"  o {mo}\n  S {mf}")
+    assert ok
+
+
+@pytest.mark.parametrize("segments,parts", [(1, 1), (4, 1), (1, 3)])
+def test_no_final_state_and_in_place(workload, segments, parts, monkeypatch):
     import torch
     import chunked_gated_delta_kda_amd as kda
 
-    monkeypatch.setenv("KDA_RECUR_WAVES", "102")
+    monkeypatch.setenv("KDA_RECUR_WAVES", "102" if parts == 1 else "101")
     monkeypatch.setenv("KDA_SEGMENTS", str(segments))
+    monkeypatch.setenv("KDA_PARTS", str(parts))
     w, (ro, rf) = workload
     d = synth.to_device(w)
     _say(f"[forms] no final state, segments={segments}")
