@@ -1985,7 +1985,9 @@ __global__ __launch_bounds__(256) void parts_setup_kernel(const int32_t *cu_safe
     }
 }
 
-// pass 1: blocks [0, G/2) run every part from a zero state, blocks [G/2, G) from the identity
+// pass 1: blocks [0, G/2) run every part from a zero state, blocks [G/2, G) from the identity.
+// Both halves also write outputs (for entry states that are not the true ones) to `out`;
+// pass 2, a later launch on the same stream, overwrites every one of them.
 template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
