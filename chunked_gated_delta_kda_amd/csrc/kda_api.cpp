@@ -40,11 +40,14 @@ constexpr size_t STATE_BYTES = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(floa
 // Parts per sequence of the split variant's recurrence (1: whole sequences; see
 // launch_parts). Pass 1 runs 8 N P H two-slice paired blocks and pass 2 8 N P H one-slice
 // blocks, so P <= 32 / (N H) keeps each pass within one round of the 256 CUs; three
-// passes over a P times shorter chain pay from P = 3. Parts are kept at 256 chunks or
-// more. Measured on MI355X (ms, whole | in P parts; best of 4 alternating rounds): one
-// sequence of 65536 tokens x 8 heads 2.16 | 1.74 (3), 1.41 (4); 32768 x 8 1.09 | 0.76 (4);
-// 65536 x 4 2.08 | 1.26 (4), 0.79 (8). KDA_PARTS (1..MAX_PARTS) overrides, for the
-// 16-token forms.
+// passes over a P times shorter chain pay from P = 3, down to parts of 64 chunks. Measured
+// on MI355X (ms, whole | in P parts; best of 4 alternating rounds), one sequence of T
+// tokens x H heads: 65536 x 8 2.16 | 1.74 (3), 1.41 (4); 32768 x 8 1.09 | 0.76 (4); 16384 x
+// 8 0.551 | 0.481 (3), 0.412 (4); 12288 x 8 0.419 | 0.365 (3); 8192 x 8 0.275 | 0.253 (3),
+// 0.223 (4); 65536 x 4 2.08 | 1.26 (4), 0.79 (8); 8192 x 4 0.269 | 0.201 (4), 0.177 (8);
+// 4096 x 2 0.142 | 0.126 (4), 0.122 (8); two sequences of 16384 x 4 0.554 | 0.418 (4);
+// but 32768 x 16 1.21 | 1.41 (2). KDA_PARTS (1..MAX_PARTS) overrides, for the 16-token
+// forms.
 int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
     if (waves >= 300) return 1;
     if (const char *e = std::getenv("KDA_PARTS")) {
@@ -53,7 +56,7 @@ int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
     }
     if (waves != 101) return 1;
     int64_t p = 32 / (N * H);
-    const int64_t by_len = max_chunks(N, T) / 256;
+    const int64_t by_len = max_chunks(N, T) / 64;
     if (by_len < p) p = by_len;
     if (p > MAX_PARTS) p = MAX_PARTS;
     return p >= 3 ? (int)p : 1;

@@ -145,7 +145,9 @@ def test_launch_plan():
     # entry after the prep of all chunks
     assert [p[0] for p in nat.launch_plan(1, 65536, 8, "split")] == ["chunk_map", "prep", "parts"]
     assert [p[0] for p in nat.launch_plan(1, 65536, 4, "split")] == ["chunk_map", "prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 8192, 8, "split")] == ["chunk_map", "prep", "parts"]
     assert [p[0] for p in nat.launch_plan(1, 2048, 8, "split")] == ["chunk_map", "prep", "recur"]
+    assert [p[0] for p in nat.launch_plan(1, 32768, 16, "split")][-1] != "parts"   # two parts do not pay
     # the per-chain hybrid (from 192 chains) runs whole by default
     assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
