@@ -9,7 +9,7 @@ import math
 
 from . import native
 
-__all__ = ["fwd", "decode", "workspace_bytes", "select_variant", "version", "native"]
+__all__ = ["fwd", "decode", "workspace_bytes", "select_variant", "device_errors", "version", "native"]
 
 HEAD_DIM = 128
 
@@ -23,6 +23,15 @@ def workspace_bytes(num_seqs, total_tokens, num_heads, variant="auto"):
                                                          native.VARIANTS[variant]))
 
 
+def device_errors(clear=True, stream=None):
+    """KDA_DEVERR_* bits raised on the current device since the last clear (synchronises
+    ``stream``, by default torch's current stream)."""
+    import torch
+
+    st = stream if stream is not None else torch.cuda.current_stream()
+    return native.device_errors(st.cuda_stream, clear=clear)
+
+
 def select_variant(num_seqs, total_tokens, num_heads):
     v = native.load_library().kda_select_variant(num_seqs, total_tokens, num_heads)
     return {b: a for a, b in native.VARIANTS.items()}[v]
@@ -32,14 +41,58 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _expect(name, t, dtype, shape, dev):
+    """Raise unless ``t`` is a contiguous ``dtype`` tensor of ``shape`` on ``dev``: the
+    kernels write whole rows through raw pointers, so a wrong buffer must be caught here."""
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name}: expected contiguous {dtype} {tuple(shape)} on {dev}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
+def check_fwd_args(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None, final_state=None):
+    """Every check fwd makes on its tensors before anything is launched (dtype, shape,
+    contiguity, one device); returns (T, H, N)."""
+    import torch
+
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q: expected [T, H, 128]")
+    T, H, Dk = q.shape
+    if Dk != HEAD_DIM:
+        raise ValueError("head_dim must be 128")
+    for name, t, dt, shape in (("q", q, torch.bfloat16, (T, H, Dk)), ("k", k, torch.bfloat16, (T, H, Dk)),
+                               ("v", v, torch.bfloat16, (T, H, Dk)), ("g", g, torch.float32, (T, H, Dk)),
+                               ("beta", beta, torch.float32, (T, H))):
+        _expect(name, t, dt, shape, dev)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1 \
+                or not cu_seqlens.is_contiguous() or cu_seqlens.shape[0] < 2:
+            raise ValueError("cu_seqlens: expected a contiguous int32 vector of N+1 >= 2 offsets on the device")
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = 1
+    if initial_state is not None:
+        _expect("initial_state", initial_state, torch.float32, (N, H, Dk, Dk), dev)
+    if out is not None:
+        _expect("out", out, torch.float32, (T, H, Dk), dev)
+    if final_state is not None:
+        _expect("final_state", final_state, torch.float32, (N, H, Dk, Dk), dev)
+    return T, H, N
+
+
 def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         output_final_state=True, *, variant="auto", out=None, final_state=None,
-        workspace=None, stream=None, stage_events=None):
+        workspace=None, stream=None, stage_events=None, check=False):
     """KDA forward on the current HIP device.
 
     q, k, v: bf16 [T, H, 128]; g: fp32 [T, H, 128] (log-decay, clamped at -5);
     beta: fp32 [T, H]; cu_seqlens: int32 [N+1] on the device or None (one sequence);
-    initial_state: fp32 [N, H, 128, 128] or None.
+    initial_state: fp32 [N, H, 128, 128] or None; out / final_state: caller buffers of the
+    result shapes (fp32, contiguous, on the device) or None.
+    check: clear the device error word before the call and read it after (both
+    synchronise the stream); raise native.KdaDeviceError if the kernels raised a bit
+    (malformed cu_seqlens, a fused hand-off timeout).
     Returns (o fp32 [T, H, 128], final_state fp32 [N, H, 128, 128] or None).
     """
     import torch
@@ -48,34 +101,16 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kda.fwd needs device tensors")
-    T, H, Dk = q.shape
-    if Dk != HEAD_DIM:
-        raise ValueError("head_dim must be 128")
-    for name, t, dt, shape in (("q", q, torch.bfloat16, (T, H, Dk)), ("k", k, torch.bfloat16, (T, H, Dk)),
-                               ("v", v, torch.bfloat16, (T, H, Dk)), ("g", g, torch.float32, (T, H, Dk)),
-                               ("beta", beta, torch.float32, (T, H))):
-        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name}: expected contiguous {dt} {shape} on {dev}, "
-                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1 \
-                or not cu_seqlens.is_contiguous():
-            raise ValueError("cu_seqlens: expected a contiguous int32 vector on the device")
-        N = cu_seqlens.shape[0] - 1
-    else:
-        N = 1
-    if initial_state is not None:
-        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != (N, H, Dk, Dk) \
-                or not initial_state.is_contiguous() or initial_state.device != dev:
-            raise ValueError("initial_state: expected contiguous fp32 [N, H, 128, 128]")
+    T, H, N = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    Dk = HEAD_DIM
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     if out is None:
         out = torch.empty((T, H, Dk), dtype=torch.float32, device=dev)
-    if output_final_state and final_state is None:
-        final_state = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=dev)
     if not output_final_state:
         final_state = None
+    elif final_state is None:
+        final_state = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=dev)
     var = native.VARIANTS[variant]
     if workspace is None:
         nbytes = lib.kda_workspace_bytes(N, T, H, var)
@@ -87,11 +122,44 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         opt.n_stage_events = len(stage_events)
         opt.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
     st = stream if stream is not None else torch.cuda.current_stream(dev)
+    if check:
+        native.device_errors(st.cuda_stream, clear=True)
     rc = lib.kda_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(cu_seqlens),
                         N, T, H, Dk, _ptr(initial_state), _ptr(out), _ptr(final_state),
                         ctypes.c_void_p(st.cuda_stream), ctypes.byref(opt))
     native.check(rc)
+    if check:
+        bits = native.device_errors(st.cuda_stream, clear=True)
+        if bits:
+            raise native.KdaDeviceError(bits)
     return out, final_state
+
+
+def check_decode_args(q, k, v, g, beta, state=None, state_out="inplace", out=None, state_dtype=None):
+    """Every check decode makes on its tensors before the launch; returns (N, H, state dtype)."""
+    import torch
+
+    dev = q.device
+    if q.dim() != 3:
+        raise ValueError("q: expected [N, H, 128]")
+    N, H, Dk = q.shape
+    if Dk != HEAD_DIM:
+        raise ValueError("head_dim must be 128")
+    for name, t, dt, shape in (("q", q, torch.bfloat16, (N, H, Dk)), ("k", k, torch.bfloat16, (N, H, Dk)),
+                               ("v", v, torch.bfloat16, (N, H, Dk)), ("g", g, torch.float32, (N, H, Dk)),
+                               ("beta", beta, torch.float32, (N, H))):
+        _expect(name, t, dt, shape, dev)
+    if state_dtype is None:
+        state_dtype = (state.dtype if state is not None else
+                       state_out.dtype if isinstance(state_out, torch.Tensor) else torch.float32)
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("state_dtype: torch.float32 or torch.bfloat16")
+    for name, t in (("state", state), ("state_out", state_out)):
+        if isinstance(t, torch.Tensor):
+            _expect(name, t, state_dtype, (N, H, Dk, Dk), dev)
+    if out is not None:
+        _expect("out", out, torch.float32, (N, H, Dk), dev)
+    return N, H, state_dtype
 
 
 def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inplace", state_dtype=None,
@@ -112,26 +180,10 @@ def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inp
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kda.decode needs device tensors")
-    N, H, Dk = q.shape
-    if Dk != HEAD_DIM:
-        raise ValueError("head_dim must be 128")
-    for name, t, dt, shape in (("q", q, torch.bfloat16, (N, H, Dk)), ("k", k, torch.bfloat16, (N, H, Dk)),
-                               ("v", v, torch.bfloat16, (N, H, Dk)), ("g", g, torch.float32, (N, H, Dk)),
-                               ("beta", beta, torch.float32, (N, H))):
-        if t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name}: expected contiguous {dt} {shape} on {dev}, "
-                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
-    if state_dtype is None:
-        state_dtype = (state.dtype if state is not None else
-                       state_out.dtype if isinstance(state_out, torch.Tensor) else torch.float32)
+    N, H, state_dtype = check_decode_args(q, k, v, g, beta, state, state_out, out, state_dtype)
+    Dk = HEAD_DIM
     codes = {torch.float32: native.STATE_DTYPES["f32"], torch.bfloat16: native.STATE_DTYPES["bf16"]}
-    if state_dtype not in codes:
-        raise ValueError("state_dtype: torch.float32 or torch.bfloat16")
     sshape = (N, H, Dk, Dk)
-    for name, t in (("state", state), ("state_out", state_out)):
-        if isinstance(t, torch.Tensor) and (t.dtype != state_dtype or tuple(t.shape) != sshape
-                                            or not t.is_contiguous() or t.device != dev):
-            raise ValueError(f"{name}: expected contiguous {state_dtype} {sshape} on {dev}")
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     if out is None:

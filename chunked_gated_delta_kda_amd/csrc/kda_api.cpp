@@ -2,6 +2,7 @@
 // variant choice, workspace, launches. No exception crosses the interface.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -10,6 +11,29 @@
 
 #include "kda.h"
 #include "kda_launch.hpp"
+
+namespace kda {
+
+// Error bits raised on the device by any call on this device (see kda_device_errors).
+__device__ int32_t device_error_bits;
+
+int32_t *device_error_word() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    static std::atomic<int32_t *> cache[64];
+    if (dev < 64) {
+        if (int32_t *p = cache[dev].load(std::memory_order_acquire)) return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(device_error_bits)) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (dev < 64) cache[dev].store((int32_t *)p, std::memory_order_release);
+    return (int32_t *)p;
+}
+
+}  // namespace kda
 
 namespace {
 
@@ -22,7 +46,7 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // chunks of cl tokens: an upper bound over any split of T tokens into N sequences
 int64_t max_chunks(int64_t N, int64_t T, int cl = KDA_CHUNK) { return (T + cl - 1) / cl + N; }
 
-// The recurrence forms 301/302 consume 32-token chunk records; all others 16-token ones.
+// The recurrence form 301 consumes 32-token chunk records; all others 16-token ones.
 int chunk_len(int waves) { return waves >= 300 ? 32 : KDA_CHUNK; }
 size_t rec_bytes(int waves) { return waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES; }
 
@@ -97,19 +121,16 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 }
 
 
-// Recurrence block shape. 9: per chain, paired or eight-wave (below). 1, 2, 4 or 8:
-// waves per block, each owning 16 value columns
-// and forming its own outputs; the block's waves share each chunk record through one
-// LDS ring (3 chunks deep for 4 waves, 2 for 8; 42 and 83 are the other depths). 0:
-// the key-split form, four waves per 16-column slice. 101, 102: the paired form (1 or
-// 2 slices per block, a chain wave and two output waves per slice, one loader wave).
-// KDA_RECUR_WAVES overrides the choice, for tuning.
+// Recurrence block shape. 9: per chain, paired or eight-wave (below). 8: eight waves
+// per block, each owning 16 value columns and forming its own outputs; the block's waves
+// share each chunk record through one LDS ring 2 chunks deep. 101, 102: the paired form
+// (1 or 2 slices per block, a chain wave and two output waves per slice, one loader
+// wave). 301: the paired form over 32-token chunks. KDA_RECUR_WAVES overrides the
+// choice, for tuning.
 int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 0 || w == 1 || w == 2 || w == 4 || w == 42 || w == 8 || w == 83 || w == 9 || w == 101 ||
-            w == 102 || w == 201 || w == 202 || w == 301 || w == 302)
-            return w;
+        if (w == 8 || w == 9 || w == 101 || w == 102 || w == 301) return w;
     }
     // Measured on MI355X (ms, best segment count each; one slice per block 101 | two
     // slices 102), one sequence of 8192 tokens: 20 heads 0.326 | 0.370; 24 heads 0.356 |
@@ -426,6 +447,23 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     }
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;
+}
+
+int kda_device_errors(void *stream, int32_t *bits, int32_t clear) {
+    if (!bits) return KDA_ERR_NULL;
+    int32_t *w = kda::device_error_word();
+    if (!w) return KDA_ERR_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    static const int32_t zero = 0;
+    int32_t got = 0;
+    if (hipMemcpyAsync(&got, w, sizeof(got), hipMemcpyDeviceToHost, st) != hipSuccess ||
+        (clear && hipMemcpyAsync(w, &zero, sizeof(zero), hipMemcpyHostToDevice, st) != hipSuccess) ||
+        hipStreamSynchronize(st) != hipSuccess) {
+        (void)hipGetLastError();
+        return KDA_ERR_DEVICE;
+    }
+    *bits = got;
+    return KDA_OK;
 }
 
 int kda_fwd(const void *q, const void *k, const void *v, const float *g, const float *beta,

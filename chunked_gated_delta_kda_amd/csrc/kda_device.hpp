@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_launch.hpp"
+
 namespace kda {
 
 constexpr int D = 128;             // head dimension (key and value)
@@ -633,6 +635,62 @@ __device__ __forceinline__ f32x4 recur_step(const StepIn &s, f32x4 (&S)[8]) {
         S[b] = mfma(s.kt[b], vl0, S[b]);
     }
     return o;
+}
+
+
+// ---------------------------------------------------------------- shared by the recurrences
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]; others left open
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// vmcnt(N) and lgkmcnt(0) together: own global loads up to the N youngest, and
+// every own LDS access, complete
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+}
+
+#define KDA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Wave roles of the paired recurrence blocks (NW 16-column slices per block): per slice a
+// chain wave and two output waves, one loader wave. Waves w and w+4 of a block share a
+// SIMD (and its matrix unit), so the roles are placed to keep each chain wave's SIMD free
+// of output work:
+//   NW = 1: chain 0 | output p0 | output p1 | loader
+//   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | loader | idle |
+//           output (slice 0, p1), (slice 1, p1)
+// (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
+template <int NW>
+struct PairLayout {
+    static_assert(NW == 1 || NW == 2, "one or two slices per block");
+    static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
+    static constexpr int SNAPS = 3;                      // snapshot buffers per slice
+    static constexpr int WAVES = NW == 1 ? 4 : 8;
+    static constexpr int LOADER = NW == 1 ? 3 : 4;
+    static constexpr int IDLE = NW == 1 ? -1 : 5;
+    // output wave of slice s, parity p
+    __device__ static constexpr int out_wave(int s, int p) { return NW == 1 ? 1 + p : (p ? 6 : 2) + s; }
+};
+
+// Global index of the idx-th chunk-head (heads fastest, sequences in input order) of the
+// segment [fb, fe), or -1 past its end. The whole range is the global chunk order itself;
+// for a part of it the sequences are walked in turn (segmented launches serve few).
+__device__ __forceinline__ int seg_chunk_of(const int32_t *__restrict__ chunk_off, int N, int H,
+                                            int fb, int fe, int64_t idx, int &h) {
+    h = (int)(idx % H);
+    int64_t c = idx / H;
+    if (fb == 0 && fe == SEG_ONE) return c < chunk_off[N] ? (int)c : -1;
+    for (int n = 0; n < N; ++n) {
+        const int len = chunk_off[n + 1] - chunk_off[n];
+        const int b = seg_chunk(len, fb), e = seg_chunk(len, fe);
+        if (c < e - b) return chunk_off[n] + b + (int)c;
+        c -= e - b;
+    }
+    return -1;
 }
 
 }  // namespace kda

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(64 * (NW + NP)) void fused_kernel(
     const float *__restrict__ g, const float *__restrict__ beta, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ order, int N, int T, int H, float scale,
     const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin,
-    int *__restrict__ err) {
+    int *__restrict__ err, int *dev_err) {
     using LY = FusedLayout<NW, NP, NSLOT>;
     static_assert(LY::FLAGS >= (2 * NSLOT + 1) * 4, "flag area too small");
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -156,7 +156,10 @@ __global__ __launch_bounds__(64 * (NW + NP)) void fused_kernel(
         for (int j = 0; j < 4; ++j) vcur[j] = vnxt[j];
     }
     if (!ok || lds_load_acquire(failed)) {
-        if (l == 0) atomicOr(err, 1);
+        if (l == 0) {
+            atomicOr(err, 1);
+            if (dev_err) atomicOr(dev_err, 1);
+        }
         return;
     }
     if (sfin) {
@@ -179,7 +182,7 @@ static hipError_t launch_fused_t(const uint16_t *q, const uint16_t *k, const uin
     if (const hipError_t e = ensure_lds_limit((const void *)kern, LY::BYTES, lds_set); e != hipSuccess) return e;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * (NW + NP)), LY::BYTES, st, q, k,
-                       v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err);
+                       v, g, beta, cu, order, N, T, H, scale, s0, out, sfin, err, device_error_word());
     return hipGetLastError();
 }
 

@@ -22,6 +22,11 @@ inline hipError_t ensure_lds_limit(const void *kern, int bytes, std::atomic<uint
     return e;
 }
 
+// Device error word of the current device: one int32 in device memory that kernels OR
+// their error bits into (KDA_DEVERR_* of kda.h) and that only kda_device_errors clears.
+// Resolved once per device; nullptr if the runtime cannot resolve it (kernels then skip it).
+int32_t *device_error_word();
+
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
 constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
 
@@ -56,7 +61,7 @@ hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, con
                        const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
                        hipStream_t st);
 
-// paired recurrence over the segment [fb, fe); waves in {101, 102, 201, 202}
+// paired recurrence over the segment [fb, fe); waves in {101, 102, 9}
 hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t *cu,
                               const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                               const float *s0, float *out, float *sfin, float *carry, int waves,
@@ -77,7 +82,7 @@ struct RecurPrepArgs {
     int64_t M;          // bound on the batch's chunk count
 };
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
-// 32-token forms (waves 301: one slice per block, 302: two): recurrence over the segment
+// 32-token form (waves 301: one slice per block): recurrence over the segment
 // [fb, fe), alone or with the prep of [pb, pe) on the idle CUs
 hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
                                 const int32_t *chunk_off, const int32_t *order, int N, int T,

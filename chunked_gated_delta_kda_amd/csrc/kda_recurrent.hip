@@ -43,6 +43,7 @@ constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 constexpr float LB = KDA_LOWER_BOUND;
 constexpr float LOG2E_R = 1.4426950408889634f;
+constexpr int32_t ERR_CU_SEQLENS_BIT = KDA_DEVERR_CU_SEQLENS;
 
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -115,12 +116,14 @@ template <int DVT>
 __global__ __launch_bounds__(NT) void recurrent_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
-    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin) {
+    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin,
+    int32_t *dev_err) {
     constexpr int CPT = 4;
     using TL = Tile<DVT, CPT>;
     __shared__ float sq[2][D], sk[2][D], se[2][D];
     __shared__ float sqk[2][2];
     __shared__ float red[NWAVE][2][TL::CG][CPT];
+    __shared__ int32_t cmax[NWAVE][2];
 
     const int tile = blockIdx.x % TL::TILES;
     const int nh = blockIdx.x / TL::TILES;
@@ -129,14 +132,36 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     const int cg = tid % TL::CG, rg = tid / TL::CG;
     const int col = tile * DVT + cg * CPT;
 
-    // tokens of sequence n, clamped to [0, T] so that malformed cu_seqlens cannot
-    // send an access out of bounds
+    // tokens of sequence n. Malformed cu_seqlens are sanitised as the split and fused
+    // variants' chunk map does: every offset clamped to [0, T] and raised to the largest
+    // offset before it (a running maximum, taken here over cu[0..n+1] by the block), so
+    // that the ranges stay ordered, disjoint and inside [0, T]. The blocks of sequence n
+    // check its own offsets and raise the device error bit when they are malformed.
     int t0, t1;
     if (one_token_per_seq) {
         t0 = n, t1 = n + 1;
     } else if (cu) {
-        t0 = min(max(cu[n], 0), T);
-        t1 = min(max(cu[n + 1], t0), T);
+        int32_t m0 = 0, m1 = 0;
+        for (int i = tid; i <= n + 1; i += NT) {
+            const int32_t x = min(max(cu[i], 0), T);
+            if (i <= n) m0 = max(m0, x);
+            m1 = max(m1, x);
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            m0 = max(m0, __shfl_xor(m0, off));
+            m1 = max(m1, __shfl_xor(m1, off));
+        }
+        if (lane == 0) cmax[wave][0] = m0, cmax[wave][1] = m1;
+        __syncthreads();
+        t0 = cmax[0][0], t1 = cmax[0][1];
+#pragma unroll
+        for (int x = 1; x < NWAVE; ++x) t0 = max(t0, cmax[x][0]), t1 = max(t1, cmax[x][1]);
+        if (tid == 0 && dev_err && blockIdx.x % (H * TL::TILES) == 0) {
+            const int32_t a = cu[n], b = cu[n + 1];
+            if ((n == 0 && a != 0) || b < a || a < 0 || b > T || (n == N - 1 && b != T))
+                atomicOr(dev_err, ERR_CU_SEQLENS_BIT);
+        }
     } else {
         t0 = 0, t1 = T;
     }
@@ -402,7 +427,7 @@ static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                            scale, H, s0, out, sfin);
     else if constexpr (!BF16S)
         hipLaunchKernelGGL((recurrent_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
-                           scale, cu, N, T, H, 0, (const float *)s0, out, (float *)sfin);
+                           scale, cu, N, T, H, 0, (const float *)s0, out, (float *)sfin, device_error_word());
 }
 
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

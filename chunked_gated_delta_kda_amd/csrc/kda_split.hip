@@ -26,7 +26,7 @@ __device__ float store_sink[64];
 // kernel reads cu_safe, so malformed cu_seqlens cannot send an access outside the
 // inputs, the outputs or the workspace (whose record area is sized for T tokens).
 // The error word is set to ERR_CU_SEQLENS when the offsets were not 0 = c_0 <= c_1
-// <= ... <= c_N = T. Then chunk_off[n] = number of cl-token chunks before sequence n
+// <= ... <= c_N = T (and the bit is ORed into the device error word). Then chunk_off[n] = number of cl-token chunks before sequence n
 // (chunk_off[N] = total), and order[] lists sequences longest first (ties by index)
 // when N <= ORDER_MAX, else in input order.
 constexpr int MAP_THREADS = 256;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
                                                                  int32_t *__restrict__ chunk_off,
                                                                  int32_t *__restrict__ order,
                                                                  int32_t *__restrict__ err,
-                                                                 int cl) {
+                                                                 int32_t *dev_err, int cl) {
     __shared__ int32_t wsum[MAP_THREADS / 64];
     __shared__ int32_t last;   // the scan's last value: the carry into the next MAP_THREADS
     __shared__ int32_t lcs[ORDER_MAX + 1];   // the sanitised offsets again, for N <= ORDER_MAX
@@ -104,6 +104,7 @@ __global__ __launch_bounds__(MAP_THREADS) void chunk_map_kernel(const int32_t *_
     if (tid == 0) {
         chunk_off[0] = 0;
         *err = bad ? ERR_CU_SEQLENS : 0;
+        if (bad && dev_err) atomicOr(dev_err, ERR_CU_SEQLENS);
     }
     if (in_lds) {
         for (int n = tid; n < N; n += MAP_THREADS) {
@@ -142,22 +143,6 @@ __device__ __forceinline__ void prep_one(const uint16_t *__restrict__ q, const u
     prep_chunk(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * Rec::BYTES);
 }
 
-// Global index of the idx-th chunk-head (heads fastest, sequences in input order) of the
-// segment [fb, fe), or -1 past its end. The whole range is the global chunk order itself;
-// for a part of it the sequences are walked in turn (segmented launches serve few).
-__device__ __forceinline__ int seg_chunk_of(const int32_t *__restrict__ chunk_off, int N, int H,
-                                            int fb, int fe, int64_t idx, int &h) {
-    h = (int)(idx % H);
-    int64_t c = idx / H;
-    if (fb == 0 && fe == SEG_ONE) return c < chunk_off[N] ? (int)c : -1;
-    for (int n = 0; n < N; ++n) {
-        const int len = chunk_off[n + 1] - chunk_off[n];
-        const int b = seg_chunk(len, fb), e = seg_chunk(len, fe);
-        if (c < e - b) return chunk_off[n] + b + (int)c;
-        c -= e - b;
-    }
-    return -1;
-}
 
 __global__ __launch_bounds__(64) void prep_kernel(const uint16_t *__restrict__ q,
                                                   const uint16_t *__restrict__ k,
@@ -195,22 +180,6 @@ struct Ring {
     static constexpr int loads_of(int w) { return (LOADS - w + NW - 1) / NW; }
 };
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt out of range");
-    // gfx9 s_waitcnt: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]; others left open
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-// vmcnt(N) and lgkmcnt(0) together: own global loads up to the N youngest, and
-// every own LDS access, complete
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_lgkm0() {
-    static_assert(N >= 0 && N < 64, "vmcnt out of range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
-}
-
-#define KDA_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // Issue this wave's share of the loads of one chunk (record + V tile) into an LDS slot.
 // (NSLOT only makes each ring shape its own specialization: clang's host pass rejects a
@@ -372,30 +341,20 @@ __global__ __launch_bounds__(64 * NW) void recur_kernel(
 template <int NW>
 constexpr int pair_nslot() { return NW == 1 ? 5 : 4; }
 
-template <int NW>
-struct PairLayout {
-    static_assert(NW == 1 || NW == 2, "one or two slices per block");
-    static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
-    static constexpr int SNAPS = 3;                      // snapshot buffers per slice
-    static constexpr int WAVES = NW == 1 ? 4 : 8;
-    static constexpr int LOADER = NW == 1 ? 3 : 4;
-    static constexpr int IDLE = NW == 1 ? -1 : 5;
-    // output wave of slice s, parity p
-    __device__ static constexpr int out_wave(int s, int p) { return NW == 1 ? 1 + p : (p ? 6 : 2) + s; }
-};
 
 // A launch covers the segment [fb, fe) of every sequence (seg_chunk; launches over
 // consecutive segments, in order on one stream, cover a batch). A sequence's state
 // enters from initial_state (or zeros) at its first chunk and from `carry` otherwise,
 // and leaves to final_state after its last chunk and to `carry` otherwise (carry may
 // be final_state itself). Sequences without chunks copy initial to final state in
-// the launch of the first segment.
+// the launch of the first segment. With zero_v the chain runs as if every v were 0 (the
+// part of the chain that is linear in the entry state alone; outputs are then not valid).
 template <int NW, int NSLOT>
 __device__ __forceinline__ void recur_pair_block(
     int bid, char *ring, const char *__restrict__ recs, const uint16_t *__restrict__ v,
     const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
     const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
-    float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
+    float *__restrict__ out, float *sfin, float *carry, int fb, int fe, bool zero_v = false) {
     using R = Ring<NW>;         // V tile geometry of NW slices
     using PL = PairLayout<NW>;
     constexpr int REC_LOADS = Rec::CHAIN / 1024;       // the chain's part of the record
@@ -515,7 +474,7 @@ __device__ __forceinline__ void recur_pair_block(
             x.tb = *(const bf16x8 *)(slot + Rec::TB + l * 16);
             const uint16_t *vt = (const uint16_t *)(slot + Rec::CHAIN);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x.vv[j] = vt[(4 * gq + j) * R::VCOLS + slice * 16 + c];
+            for (int j = 0; j < 4; ++j) x.vv[j] = zero_v ? (uint16_t)0 : vt[(4 * gq + j) * R::VCOLS + slice * 16 + c];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) x.wn[kb] = *(const bf16x8 *)(slot + Rec::WN + kb * 1024 + l * 16);
 #pragma unroll
@@ -790,296 +749,6 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_prep_kernel(
              *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
 
-// ---------------------------------------------------------------- direct-load paired recurrence
-// The paired recurrence without an LDS ring: every wave loads its own record
-// pieces from global memory (L2) straight into registers, one or two chunks
-// ahead of use, so that record traffic neither passes through LDS nor waits on
-// the LDS-DMA path (whose per-CU rate is a fraction of what plain vector loads
-// reach). LDS holds only the state snapshots the chain wave hands to the output
-// waves. The state decay arrives lane-permuted (two floats per lane) and is
-// broadcast within each 16-lane row by DPP inside the multiply.
-//   NW = 1: chain | output p0 | output p1
-//   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | idle, idle |
-//           output (slice 0, p1), (slice 1, p1)
-// (waves w and w+4 share a SIMD: each chain wave's partner does nothing.)
-template <int NW>
-struct DirectLayout {
-    static_assert(NW == 1 || NW == 2, "one or two slices per block");
-    static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
-    static constexpr int SNAPS = 3;
-    static constexpr int WAVES = NW == 1 ? 3 : 8;
-    static constexpr int BYTES = SNAPS * NW * SNAP;
-};
-
-template <int NW>
-__device__ __forceinline__ void recur_direct_block(
-    int bid, char *lds, const char *__restrict__ recs, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ cu, const int32_t *__restrict__ chunk_off,
-    const int32_t *__restrict__ order, int N, int T, int H, const float *s0,
-    float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
-    using DL = DirectLayout<NW>;
-    constexpr int PARTS = D / (16 * NW);
-    const int part = bid % PARTS;
-    const int sh = bid / PARTS;
-    const int h = sh % H;
-    const int n = order[sh / H];
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
-    const bool chain = w < NW;
-    const bool idle = NW == 2 && (w == 4 || w == 5);
-    const int parity = NW == 1 ? (w == 2) : (w >= 6);
-    const int slice = chain ? w : (NW == 1 ? 0 : (w & 1));
-    const int col = part * 16 * NW + slice * 16 + c;
-    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
-    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
-    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);   // this launch's chunks of the sequence
-    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
-    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
-    if (ci0 >= ci1) {
-        if (seq_c0 == seq_c1 && fb == 0 && chain && sfin) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
-                    sfin[o] = s0 ? s0[o] : 0.f;
-                }
-        }
-        return;
-    }
-    const int nch = ci1 - ci0;
-    const int64_t bos = seq_bos + (int64_t)C * (ci0 - seq_c0);
-    const float *sin = ci0 == seq_c0 ? s0 : carry;
-    float *sout = ci1 == seq_c1 ? sfin : carry;
-    auto snap_of = [&](int it) { return lds + ((it % DL::SNAPS) * NW + slice) * DL::SNAP; };
-    auto rec_of = [&](int k) { return recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES; };
-    auto sync = [] {
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const bf16x4 z4 = {};
-
-    if (idle) {
-        for (int it = 0; it < nch + 2; ++it) sync();
-        return;
-    }
-
-    if (chain) {
-        f32x4 S[8];
-        if (sin) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
-        } else {
-#pragma unroll
-            for (int b = 0; b < 8; ++b) S[b] = zero;
-        }
-        struct ChainIn {
-            bf16x8 wn[4], kt[8], tb;
-            f32x2 e;             // lane-permuted state decay
-            uint16_t vv[4];      // V[4g+j][col]; rows past the chunk end repeat its last
-                                 // row (finite, and T Diag(beta) is zero there)
-        };
-        auto load = [&](ChainIn &x, int k) {
-            const char *rec = rec_of(k);
-            x.tb = *(const bf16x8 *)(rec + Rec::TB + l * 16);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) x.wn[kb] = *(const bf16x8 *)(rec + Rec::WN + kb * 1024 + l * 16);
-            const int64_t t0 = bos + (int64_t)C * k;
-            const int nc = (int)min<int64_t>(C, eos - t0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 4 * gq + j < nc ? 4 * gq + j : nc - 1;
-                x.vv[j] = v[((t0 + t) * H + h) * D + col];
-            }
-#pragma unroll
-            for (int b = 0; b < 8; ++b) x.kt[b] = *(const bf16x8 *)(rec + Rec::KT + b * 1024 + l * 16);
-            x.e = *(const f32x2 *)(rec + Rec::EGP + l * 8);
-        };
-        auto step = [&](const ChainIn &x, int it) {
-            char *snap = snap_of(it);
-            bf16x8 shi[4];
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) shi[kb] = cat(to_bf16x4(S[2 * kb]), to_bf16x4(S[2 * kb + 1]));
-            const bf16x4 vin = __builtin_bit_cast(
-                bf16x4, (uint2{x.vv[0] | ((uint32_t)x.vv[1] << 16), x.vv[2] | ((uint32_t)x.vv[3] << 16)}));
-            // U - W S over four independent accumulators (plus T Diag(beta) V)
-            f32x4 a0 = mfma(x.wn[0], shi[0], zero), a1 = mfma(x.wn[1], shi[1], zero);
-            f32x4 a2 = mfma(x.wn[2], shi[2], zero), a3 = mfma(x.wn[3], shi[3], zero);
-            const f32x4 u = mfma(x.tb, cat(vin, vin), zero);
-            // the decayed state, formed while the products above run
-            f32x4 Sd[8];
-            Sd[0] = decay_block<0>(S[0], x.e);
-            Sd[1] = decay_block<1>(S[1], x.e);
-            Sd[2] = decay_block<2>(S[2], x.e);
-            Sd[3] = decay_block<3>(S[3], x.e);
-            Sd[4] = decay_block<4>(S[4], x.e);
-            Sd[5] = decay_block<5>(S[5], x.e);
-            Sd[6] = decay_block<6>(S[6], x.e);
-            Sd[7] = decay_block<7>(S[7], x.e);
-#pragma unroll
-            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + (b * 64 + l) * 16) = S[b];
-            bf16x4 vh, vl;
-            split4((a0 + a1) + (a2 + a3) + u, vh, vl);
-            *(bf16x8 *)(snap + 8 * 64 * 16 + l * 16) = cat(vh, vl);
-            const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
-#pragma unroll
-            for (int hb = 0; hb < 8; hb += 4) {
-                f32x4 tmp[4];
-#pragma unroll
-                for (int b = 0; b < 4; ++b) tmp[b] = mfma(x.kt[hb + b], vhh, Sd[hb + b]);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) S[hb + b] = mfma(x.kt[hb + b], vl0, tmp[b]);
-            }
-        };
-        ChainIn A, B;
-        load(A, 0);
-        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
-            sync();
-            if (it + 1 < nch) load(B, it + 1);
-            step(A, it);
-            if (it + 1 >= nch) break;
-            sync();
-            if (it + 2 < nch) load(A, it + 2);
-            step(B, it + 1);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
-        sync();
-        sync();
-        if (sout) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
-        }
-        return;
-    }
-
-    // ---- output wave: chunks m = parity, parity + 2, ...; the first half of chunk
-    // m's output after barrier m+1, the rest after barrier m+2
-    struct OutIn {
-        bf16x8 qh[4], ql[4], pp;
-    };
-    auto load = [&](OutIn &x, int m) {
-        const char *rec = rec_of(m);
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            x.qh[kb] = *(const bf16x8 *)(rec + Rec::QH + kb * 1024 + l * 16);
-            x.ql[kb] = *(const bf16x8 *)(rec + Rec::QL + kb * 1024 + l * 16);
-        }
-        x.pp = *(const bf16x8 *)(rec + Rec::PP + l * 16);
-    };
-    f32x4 oa = zero, ob = zero;
-    auto half_qs = [&](const OutIn &x, int m, int kb0) {
-        const char *snap = snap_of(m);
-#pragma unroll
-        for (int kb = kb0; kb < kb0 + 2; ++kb) {
-            const f32x4 a = *(const f32x4 *)(snap + ((2 * kb) * 64 + l) * 16);
-            const f32x4 b = *(const f32x4 *)(snap + ((2 * kb + 1) * 64 + l) * 16);
-            bf16x4 ah, al, bh, bl;
-            split4(a, ah, al);
-            split4(b, bh, bl);
-            const bf16x8 shi = cat(ah, bh), slo = cat(al, bl);
-            oa = mfma(x.qh[kb], shi, oa);
-            ob = mfma(x.qh[kb], slo, ob);
-            oa = mfma(x.ql[kb], shi, oa);
-        }
-    };
-    auto first = [&](const OutIn &x, int m) {
-        oa = zero;
-        ob = zero;
-        half_qs(x, m, 0);
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // snapshot reads done before the next barrier
-    };
-    auto finish = [&](const OutIn &x, int m) {
-        const char *snap = snap_of(m);
-        const bf16x8 vs = *(const bf16x8 *)(snap + 8 * 64 * 16 + l * 16);   // V_new hi | lo
-        half_qs(x, m, 2);
-        const bf16x4 vh = __builtin_shufflevector(vs, vs, 0, 1, 2, 3);
-        const bf16x4 vl = __builtin_shufflevector(vs, vs, 4, 5, 6, 7);
-        ob = mfma(x.pp, cat(vh, vh), ob);
-        ob = mfma(x.pp, cat(vl, z4), ob);
-        const f32x4 o = oa + ob;
-        const int64_t t0 = bos + (int64_t)C * m;
-        const int nc = (int)min<int64_t>(C, eos - t0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float *dst = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : store_sink + l;
-            *dst = o[j];
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-    };
-    OutIn X, Y;                      // chunks m = parity + 4i and parity + 4i + 2
-    // loads are issued unconditionally (past the end they repeat the last chunk), so
-    // that the compiler can count them exactly in its waits
-    auto cl = [&](int m) { return m < nch ? m : nch - 1; };
-    load(X, cl(parity));
-    load(Y, cl(parity + 2));
-    int nb = 0;
-    for (; nb < parity + 1; ++nb) sync();
-    for (int m = parity; m < nch; m += 4) {
-        sync(); ++nb;
-        first(X, m);
-        sync(); ++nb;
-        finish(X, m);
-        load(X, cl(m + 4));
-        if (m + 2 >= nch) break;
-        sync(); ++nb;
-        first(Y, m + 2);
-        sync(); ++nb;
-        finish(Y, m + 2);
-        load(Y, cl(m + 6));
-    }
-    for (; nb < nch + 2; ++nb) sync();
-}
-
-template <int NW>
-__global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_kernel(
-    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    recur_direct_block<NW>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), lds, recs, v, cu, chunk_off, order, N,
-                           T, H, s0, out, sfin, carry, fb, fe);
-}
-
-// recurrence over the segment [fb, fe) in blocks [0, RB), prep of [pb, pe) in the rest
-// (the LDS request, above half a CU's, keeps prep blocks off the recurrence's CUs)
-template <int NW>
-struct DirectPrep {
-    static constexpr int PREP_WAVES = DirectLayout<NW>::WAVES < 4 ? DirectLayout<NW>::WAVES : 4;
-    static constexpr int PREP_BYTES = PREP_WAVES * (int)sizeof(PrepLds);
-    static constexpr int LDS = (DirectLayout<NW>::BYTES > PREP_BYTES ? DirectLayout<NW>::BYTES : PREP_BYTES) >
-                                       80 * 1024
-                                   ? (DirectLayout<NW>::BYTES > PREP_BYTES ? DirectLayout<NW>::BYTES : PREP_BYTES)
-                                   : 80 * 1024 + 1024;
-};
-
-template <int NW>
-__global__ __launch_bounds__(64 * DirectLayout<NW>::WAVES) void recur_direct_prep_kernel(
-    const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
-    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
-    if ((int)blockIdx.x < RB) {
-        recur_direct_block<NW>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off, order, N,
-                               T, H, s0, out, sfin, carry, fb, fe);
-        return;
-    }
-    constexpr int PW = DirectPrep<NW>::PREP_WAVES;
-    const int w = threadIdx.x >> 6;
-    if (w >= PW) return;
-    const int64_t idx = (int64_t)(blockIdx.x - RB) * PW + w;
-    int h;
-    const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
-    if (ci < 0) return;
-    prep_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
-             *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
-}
-
 // ---------------------------------------------------------------- 32-token paired recurrence
 // The paired form (chain, two output waves per slice, loader) over 32-token chunks
 // built from two 16-token halves (Rec32). Per chunk step the chain wave converts
@@ -1106,9 +775,6 @@ struct Pair32 {
 };
 #ifndef KDA_PAIR32_NSLOT1
 #define KDA_PAIR32_NSLOT1 4
-#endif
-#ifndef KDA_PAIR32_NSLOT2
-#define KDA_PAIR32_NSLOT2 3
 #endif
 
 template <int NW, int NSLOT>
@@ -1510,200 +1176,11 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur32_prep_kerne
                *(PrepLds *)(lds + w * (int)sizeof(PrepLds)));
 }
 
-// ---------------------------------------------------------------- key-split recurrence
-// For few (sequence, head) chains: one block of 4 waves per (sequence, head,
-// 16-column slice), wave w owning key rows [32w, 32w+32) of the slice's state
-// (exactly k-block w of the state permutation, so its two 16-row blocks are the
-// B operand of its share of W.S). Per chunk, one barrier:
-//   before it: each wave computes its partial -W_w S_w (wave 0 adds U) and
-//     publishes it in LDS; waits for its own ring loads of the next chunk;
-//   after it: every wave sums the four partials in the same order (identical
-//     V_new everywhere), issues the ring load NSLOT chunks ahead, forms its
-//     partial of Q+S (wave 0 adds P V_new), publishes it, updates its own state
-//     rows; one wave (rotating) reduces and stores the previous chunk's output.
-// Partial buffers are double-buffered by chunk parity; all record pieces a wave
-// needs are read into registers before the barrier that releases their slot.
-constexpr int DK_WAVES = 4;
-#ifndef KDA_DK_NSLOT
-#define KDA_DK_NSLOT 4   // ring depth of the key-split recurrence (chunks in flight + 1)
-#endif
-
-template <int NSLOT>
-struct DkLayout {
-    static constexpr int SLOT = Rec::BYTES + 1024;                 // record + V tile (512 B used)
-    static constexpr int REC_LOADS = Rec::BYTES / 1024;            // 23
-    static constexpr int LOADS = REC_LOADS + 1;                    // + V tile
-    static constexpr int PER_WAVE = LOADS / DK_WAVES;              // 6
-    static constexpr int XCH = NSLOT * SLOT;                       // f32x4 [2][4][64]
-    static constexpr int XO = XCH + 2 * DK_WAVES * 64 * 16;        // f32x4 [2][4][64]
-    static constexpr int BYTES = XO + 2 * DK_WAVES * 64 * 16;
-};
-
-template <int NSLOT>
-__device__ __forceinline__ void dk_fill(char *slot, const char *rec, const uint16_t *v, int64_t t0,
-                                        int nc, int h, int H, int col0) {
-    using L = DkLayout<NSLOT>;
-    static_assert(L::LOADS % DK_WAVES == 0, "unbalanced ring loads");
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-    for (int u = 0; u < L::PER_WAVE; ++u) {
-        const int i = u * DK_WAVES + w;
-        if (i < L::REC_LOADS) {
-            __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
-                                             KDA_LDS(slot + i * 1024), 16, 0, 0);
-        } else if (l < 32) {
-            // V tile [16 tokens][16 columns] bf16: lane l -> token l/2, columns 8*(l%2)..+7
-            const int row = l >> 1;
-            const int64_t t = t0 + (row < nc ? row : nc - 1);
-            __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + col0 + (l & 1) * 8),
-                                             KDA_LDS(slot + Rec::BYTES), 16, 0, 0);
-        }
-    }
-}
-
-template <int NSLOT>
-__global__ __launch_bounds__(64 * DK_WAVES) void recur_dk_kernel(
-    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *__restrict__ s0, float *__restrict__ out, float *__restrict__ sfin) {
-    using L = DkLayout<NSLOT>;
-    static_assert(NSLOT >= 2, "ring needs two slots");
-    extern __shared__ __attribute__((aligned(16))) char ring[];
-    f32x4 *xch = (f32x4 *)(ring + L::XCH);
-    f32x4 *xo = (f32x4 *)(ring + L::XO);
-
-    const int bid = xcd_remap(blockIdx.x, gridDim.x, 8);
-    const int tile = bid % 8;
-    const int sh = bid / 8;
-    const int h = sh % H;
-    const int n = order[sh / H];
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
-    const int col0 = tile * 16, col = col0 + c;
-    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
-    const int ci0 = chunk_off[n], ci1 = chunk_off[n + 1];
-    const int nch = ci1 - ci0;
-
-    // this wave's state rows: blocks 2w and 2w+1 (key rows 32w + 4g + j and 32w + 16 + 4g + j)
-    f32x4 S0, S1;
-    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
-    if (s0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            S0[j] = s0[sbase + (int64_t)(32 * w + 4 * gq + j) * D];
-            S1[j] = s0[sbase + (int64_t)(32 * w + 16 + 4 * gq + j) * D];
-        }
-    } else {
-        S0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        S1 = S0;
-    }
-
-    auto fill = [&](int it) {
-        const int k = it < nch ? it : nch - 1;
-        const int64_t t0 = bos + (int64_t)C * k;
-        dk_fill<NSLOT>(ring + (it % NSLOT) * L::SLOT, recs + ((int64_t)(ci0 + k) * H + h) * Rec::BYTES,
-                       v, t0, (int)min<int64_t>(C, eos - t0), h, H, col0);
-    };
-    // reduce the four output partials of chunk it (published before the barrier of it+1)
-    auto emit = [&](int it) {
-        const f32x4 *xp = xo + (it & 1) * DK_WAVES * 64;
-        const f32x4 o = ((xp[l] + xp[64 + l]) + xp[128 + l]) + xp[192 + l];
-        const int64_t t0 = bos + (int64_t)C * it;
-        const int nc = (int)min<int64_t>(C, eos - t0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * gq + j < nc) out[((t0 + 4 * gq + j) * H + h) * D + col] = o[j];
-    };
-
-    if (nch > 0) {
-#pragma unroll
-        for (int it = 0; it < NSLOT; ++it) fill(it);
-        wait_vmcnt<(NSLOT - 1) * L::PER_WAVE>();
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-        const bf16x4 z4 = {};
-        for (int it = 0; it < nch; ++it) {
-            const char *slot = ring + (it % NSLOT) * L::SLOT;
-            // ---- record pieces of this wave (all read before the barrier)
-            const bf16x8 wn = *(const bf16x8 *)(slot + Rec::WN + w * 1024 + l * 16);
-            const bf16x8 qh = *(const bf16x8 *)(slot + Rec::QH + w * 1024 + l * 16);
-            const bf16x8 ql = *(const bf16x8 *)(slot + Rec::QL + w * 1024 + l * 16);
-            const bf16x8 kt0 = *(const bf16x8 *)(slot + Rec::KT + (2 * w) * 1024 + l * 16);
-            const bf16x8 kt1 = *(const bf16x8 *)(slot + Rec::KT + (2 * w + 1) * 1024 + l * 16);
-            const f32x4 eg0 = *(const f32x4 *)(slot + Rec::EG + (32 * w + 4 * gq) * 4);
-            const f32x4 eg1 = *(const f32x4 *)(slot + Rec::EG + (32 * w + 16 + 4 * gq) * 4);
-            bf16x8 tb = {}, vdup = {}, pp = {};
-            if (w == 0) {
-                tb = *(const bf16x8 *)(slot + Rec::TB + l * 16);
-                pp = *(const bf16x8 *)(slot + Rec::PP + l * 16);
-                const uint16_t *vt = (const uint16_t *)(slot + Rec::BYTES);
-                const bf16x4 vv = __builtin_bit_cast(
-                    bf16x4, (ushort4{vt[(4 * gq) * 16 + c], vt[(4 * gq + 1) * 16 + c],
-                                     vt[(4 * gq + 2) * 16 + c], vt[(4 * gq + 3) * 16 + c]}));
-                vdup = cat(vv, vv);
-            }
-            // ---- partial V_new: (wave 0: U) - W_w S_w
-            const bf16x8 shi = cat(to_bf16x4(S0), to_bf16x4(S1));
-            f32x4 part = w == 0 ? mfma(tb, vdup, zero) : zero;
-            part = mfma(wn, shi, part);
-            bf16x8 slo;
-            {
-                const uint2 h0 = __builtin_bit_cast(uint2, __builtin_shufflevector(shi, shi, 0, 1, 2, 3));
-                const uint2 h1 = __builtin_bit_cast(uint2, __builtin_shufflevector(shi, shi, 4, 5, 6, 7));
-                const uint32_t l0 = pack2(S0[0] - __uint_as_float(h0.x << 16), S0[1] - __uint_as_float(h0.x & 0xffff0000u));
-                const uint32_t l1 = pack2(S0[2] - __uint_as_float(h0.y << 16), S0[3] - __uint_as_float(h0.y & 0xffff0000u));
-                const uint32_t l2 = pack2(S1[0] - __uint_as_float(h1.x << 16), S1[1] - __uint_as_float(h1.x & 0xffff0000u));
-                const uint32_t l3 = pack2(S1[2] - __uint_as_float(h1.y << 16), S1[3] - __uint_as_float(h1.y & 0xffff0000u));
-                slo = __builtin_bit_cast(bf16x8, (uint4{l0, l1, l2, l3}));
-            }
-            if (KDA_SPLIT_S_WS) part = mfma(wn, slo, part);
-            xch[((it & 1) * DK_WAVES + w) * 64 + l] = part;
-            // own loads of chunk it+1 landed, own reads of this slot done (it is refilled next)
-            wait_vmcnt_lgkm0<(NSLOT - 2) * L::PER_WAVE>();
-            __builtin_amdgcn_s_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            fill(it + NSLOT);                           // slot of chunk it is released
-            __builtin_amdgcn_sched_barrier(0);
-            // ---- V_new (same summation order in every wave)
-            const f32x4 *xp = xch + (it & 1) * DK_WAVES * 64;
-            const f32x4 vn = ((xp[l] + xp[64 + l]) + xp[128 + l]) + xp[192 + l];
-            bf16x4 vh, vl;
-            split4(vn, vh, vl);
-            const bf16x8 vhh = cat(vh, vh), vl0 = cat(vl, z4);
-            // ---- partial outputs
-            f32x4 oa = mfma(qh, shi, zero);
-            f32x4 ob = KDA_SPLIT_S_QS ? mfma(qh, slo, zero) : zero;
-            oa = mfma(ql, shi, oa);
-            if (w == 0) {
-                ob = mfma(pp, vhh, ob);
-                ob = mfma(pp, vl0, ob);
-            }
-            xo[((it & 1) * DK_WAVES + w) * 64 + l] = oa + ob;
-            if (it > 0 && w == ((it - 1) & (DK_WAVES - 1))) emit(it - 1);
-            // ---- state update of this wave's rows
-            S0 = mfma(kt0, vhh, S0 * eg0);
-            S1 = mfma(kt1, vhh, S1 * eg1);
-            S0 = mfma(kt0, vl0, S0);
-            S1 = mfma(kt1, vl0, S1);
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);             // own LDS writes done
-        __builtin_amdgcn_s_barrier();
-        if (w == ((nch - 1) & (DK_WAVES - 1))) emit(nch - 1);
-    }
-    if (sfin) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sfin[sbase + (int64_t)(32 * w + 4 * gq + j) * D] = S0[j];
-            sfin[sbase + (int64_t)(32 * w + 16 + 4 * gq + j) * D] = S1[j];
-        }
-    }
-}
-
 // ---------------------------------------------------------------- launchers
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, int32_t *chunk_off,
                             int32_t *order, int32_t *err, int cl, hipStream_t st) {
     hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(MAP_THREADS), 0, st, cu, N, T, cu_safe, chunk_off,
-                       order, err, cl);
+                       order, err, device_error_word(), cl);
     return hipGetLastError();
 }
 
@@ -1728,20 +1205,6 @@ static hipError_t launch_recur_t(const char *recs, const uint16_t *v, const int3
     if (ensure_lds_limit((const void *)kern, (int)lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * NW), lds, st, recs, v, cu,
-                       chunk_off, order, N, T, H, s0, out, sfin);
-    return hipGetLastError();
-}
-
-template <int NSLOT>
-static hipError_t launch_recur_dk(const char *recs, const uint16_t *v, const int32_t *cu,
-                                  const int32_t *chunk_off, const int32_t *order, int N, int T,
-                                  int H, const float *s0, float *out, float *sfin, hipStream_t st) {
-    const size_t lds = (size_t)DkLayout<NSLOT>::BYTES;
-    auto kern = recur_dk_kernel<NSLOT>;
-    static std::atomic<uint64_t> lds_set{0};
-    if (ensure_lds_limit((const void *)kern, (int)lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    const int64_t blocks = (int64_t)N * H * 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DK_WAVES), lds, st, recs, v, cu,
                        chunk_off, order, N, T, H, s0, out, sfin);
     return hipGetLastError();
 }
@@ -1804,38 +1267,6 @@ static hipError_t launch_recur_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int NW>
-static hipError_t launch_recur_direct(const char *recs, const uint16_t *v, const int32_t *cu,
-                                      const int32_t *chunk_off, const int32_t *order, int N, int T,
-                                      int H, const float *s0, float *out, float *sfin, float *carry,
-                                      int fb, int fe, hipStream_t st) {
-    constexpr int lds = DirectLayout<NW>::BYTES;
-    auto kern = recur_direct_kernel<NW>;
-    static std::atomic<uint64_t> lds_set{0};
-    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
-    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
-                       recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
-    return hipGetLastError();
-}
-
-template <int NW>
-static hipError_t launch_recur_direct_prep(const RecurPrepArgs &a, hipStream_t st) {
-    constexpr int PW = DirectPrep<NW>::PREP_WAVES;
-    constexpr int lds = DirectPrep<NW>::LDS;
-    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
-    auto kern = recur_direct_prep_kernel<NW>;
-    static std::atomic<uint64_t> lds_set{0};
-    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
-    const int64_t pblocks = a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + PW - 1) / PW : 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * DirectLayout<NW>::WAVES), lds, st,
-                       a.recs, a.v, a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin,
-                       a.carry, a.fb, a.fe, (int)rb, a.q, a.k, a.g, a.beta, a.scale,
-                       a.recs, a.pb, a.pe);
-    return hipGetLastError();
-}
-
 hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                          const int32_t *cu, int N, int T, int H, float scale,
                          const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
@@ -1887,7 +1318,6 @@ hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32
                                 int waves, int fb, int fe, hipStream_t st) {
     switch (waves) {
     case 301: return launch_recur_pair32<1, KDA_PAIR32_NSLOT1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
-    case 302: return launch_recur_pair32<2, KDA_PAIR32_NSLOT2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1895,7 +1325,6 @@ hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32
 hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
     switch (waves) {
     case 301: return launch_recur32_prep_t<1, KDA_PAIR32_NSLOT1>(a, st);
-    case 302: return launch_recur32_prep_t<2, KDA_PAIR32_NSLOT2>(a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1907,8 +1336,6 @@ hipError_t launch_recur_range(const char *recs, const uint16_t *v, const int32_t
     switch (waves) {
     case 101: return launch_recur_pair<1, pair_nslot<1>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     case 102: return launch_recur_pair<2, pair_nslot<2>()>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
-    case 201: return launch_recur_direct<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
-    case 202: return launch_recur_direct<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
     case 9: {
         const RecurPrepArgs a{const_cast<char *>(recs), nullptr, nullptr, v, nullptr, nullptr, 0.f, cu, chunk_off,
                               order, N, T, H, s0, out, sfin, carry, fb, fe, 0, 0, 0};
@@ -1923,8 +1350,6 @@ hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st) 
     case 9: return launch_recur_hybrid(a, st);
     case 101: return launch_recur_prep_t<1, pair_nslot<1>()>(a, st);
     case 102: return launch_recur_prep_t<2, pair_nslot<2>()>(a, st);
-    case 201: return launch_recur_direct_prep<1>(a, st);
-    case 202: return launch_recur_direct_prep<2>(a, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1933,16 +1358,10 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st) {
     switch (waves) {
-    case 101: case 102: case 201: case 202: case 9:
+    case 101: case 102: case 9:
         return launch_recur_range(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, sfin,
                                   waves, 0, SEG_ONE, st);
-    case 0: return launch_recur_dk<KDA_DK_NSLOT>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 1: return launch_recur_t<1, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 2: return launch_recur_t<2, 4>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 4: return launch_recur_t<4, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 42: return launch_recur_t<4, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     case 8: return launch_recur_t<8, 2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
-    case 83: return launch_recur_t<8, 3>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1953,8 +1372,9 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
 // chains the paired recurrence leaves most CUs idle while each block walks thousands
 // of chunks, so every sequence is cut into P parts of about equal chunk count, each a
 // virtual sequence (contiguous in tokens and records). Pass 1 runs every part twice in
-// one launch, from S_in = 0 (final state B) and from S_in = I (final state M + B); the
-// composition kernel walks the parts of each sequence in order, S_{p+1} = M_p S_p + B_p
+// one launch, from S_in = 0 with the true v (final state B) and from S_in = I with v = 0
+// (final state M, the part's linear map itself, so no subtraction of two runs loses its
+// digits); the composition kernel walks the parts of each sequence in order, S_{p+1} = M_p S_p + B_p
 // from the sequence's initial state, and writes each part's entry state and the final
 // state; pass 2 re-runs every part from its entry state and writes the outputs. The
 // chain is then P times shorter for three passes of it, two of them side by side.
@@ -1985,9 +1405,9 @@ __global__ __launch_bounds__(256) void parts_setup_kernel(const int32_t *cu_safe
     }
 }
 
-// pass 1: blocks [0, G/2) run every part from a zero state, blocks [G/2, G) from the identity.
-// Both halves also write outputs (for entry states that are not the true ones) to `out`;
-// pass 2, a later launch on the same stream, overwrites every one of them.
+// pass 1: blocks [0, G/2) run every part from a zero state, blocks [G/2, G) from the identity
+// with v taken as 0. Both halves also write outputs (not the true ones) to `out`; pass 2, a
+// later launch on the same stream, overwrites every one of them.
 template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
@@ -1998,7 +1418,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel
     const bool id = (int)blockIdx.x >= RB;
     const int b = id ? (int)blockIdx.x - RB : (int)blockIdx.x;
     recur_pair_block<NW, NSLOT>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
-                                id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE);
+                                id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, id);
 }
 
 // composition over the parts of each sequence, one block per (sequence, head, 16 value
@@ -2019,7 +1439,7 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = rb[base + (int64_t)r * D + col0 + c0 + j];
         for (int k = 0; k < D; ++k) {
-            const float m = ri[base + (int64_t)r * D + k] - rb[base + (int64_t)r * D + k];
+            const float m = ri[base + (int64_t)r * D + k];
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] = fmaf(m, S[k][c0 + j], acc[j]);
         }

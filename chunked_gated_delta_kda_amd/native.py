@@ -17,7 +17,10 @@ VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 
 #: every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
-           "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_status_string", "kda_version")
+           "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_device_errors", "kda_status_string",
+           "kda_version")
+#: KDA_DEVERR_* bits of the device error word
+DEVERR = {1: "fused hand-off wait gave up (outputs invalid)", 2: "malformed cu_seqlens (sanitised)"}
 STATE_DTYPES = {"f32": 0, "bf16": 1}
 SEGMENT_ONE = 65536   # KDA_SEGMENT_ONE: unit of the launch plan's segment fractions
 KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent", 6: "parts"}
@@ -74,6 +77,8 @@ def load_library(path=LIB_PATH):
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode_ex.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, i32, i32, i32, vp, vp, f32p, vp, i32]
     lib.kda_decode_ex.restype = ctypes.c_int
+    lib.kda_device_errors.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
+    lib.kda_device_errors.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -89,6 +94,22 @@ def status_string(status):
 def check(status):
     if status != KDA_OK:
         raise KdaError(status, status_string(status))
+
+
+class KdaDeviceError(RuntimeError):
+    def __init__(self, bits):
+        names = [m for b, m in DEVERR.items() if bits & b]
+        super().__init__(f"device error bits {bits}: {'; '.join(names)}")
+        self.bits = bits
+
+
+def device_errors(stream_handle=None, clear=True):
+    """The device error word (KDA_DEVERR_* bits) of the current device, after
+    synchronising ``stream_handle`` (a hipStream_t as int, or None); cleared when
+    ``clear``."""
+    bits = ctypes.c_int32(0)
+    check(load_library().kda_device_errors(ctypes.c_void_p(stream_handle), ctypes.byref(bits), int(clear)))
+    return bits.value
 
 
 def error_word_offset(num_seqs):

@@ -55,6 +55,15 @@ typedef enum kda_variant {
 
 #define KDA_MAX_STAGE_EVENTS 64
 
+/* Error bits the kernels raise on the device (they cannot be returned by the call that
+ * enqueues them). Each call writes its own bits to the error word of its workspace (see
+ * kda_workspace_bytes) and ORs them into the device error word that kda_device_errors
+ * reads. */
+#define KDA_DEVERR_TIMEOUT 1      /* the fused variant's hand-off wait gave up: that
+                                     call's outputs and final_state are not valid        */
+#define KDA_DEVERR_CU_SEQLENS 2   /* cu_seqlens was not 0 = c_0 <= ... <= c_N = T; the
+                                     offsets were sanitised before use (see kda_fwd)     */
+
 /* Kernel kinds reported by kda_launch_plan (profiling). */
 #define KDA_KERNEL_CHUNK_MAP 0
 #define KDA_KERNEL_PREP 1
@@ -92,10 +101,10 @@ typedef struct kda_options {
  *               sequence of total_tokens tokens (then num_seqs must be 1).
  *               Monotonicity and c_N = total_tokens are preconditions checked on
  *               the device: malformed offsets are clamped to [0, T] and made
- *               non-decreasing before any kernel uses them (every access stays in
- *               bounds; rows outside the resulting ranges are not written), and the
- *               workspace's error word (see kda_workspace_bytes) is set to 2. The
- *               recurrent variant clamps each sequence's range the same way.
+ *               non-decreasing (each raised to the largest offset before it) before
+ *               any kernel uses them, by every variant (every access stays in bounds;
+ *               rows outside the resulting ranges are not written), and the error bit
+ *               KDA_DEVERR_CU_SEQLENS is raised (see kda_device_errors).
  *   num_seqs    N >= 1;  total_tokens T >= 0;  num_heads H >= 1;  head_dim == 128
  *   initial_state  fp32 [N, H, 128(key), 128(value)] or NULL (zeros)
  *   out         fp32 [T, H, 128]: o_t (written for every token)
@@ -121,8 +130,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
  * (0 for a variant that needs none). Returns 0 for invalid shapes too.
  * The workspace begins with int32 chunk offsets [N+1] and a sequence order [N],
  * each padded to a multiple of 256 bytes, followed by an int32 error word that a
- * call leaves at 0, or with bit 0 set (the fused variant's hand-off wait gave up:
- * outputs invalid) or bit 1 set (malformed cu_seqlens, see kda_fwd). */
+ * call leaves at 0 or at its KDA_DEVERR_* bits. */
 size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                            int32_t variant);
 
@@ -197,6 +205,17 @@ int kda_decode(const void *q, const void *k, const void *v, const float *g, cons
 int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, const float *beta,
                   float scale, int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                   const void *state_in, void *state_out, float *out, void *stream, int32_t state_dtype);
+
+/*
+ * kda_device_errors -- the device error word of the current device: the OR of the
+ * KDA_DEVERR_* bits that kernels of every call on this device (any variant, with or
+ * without a caller workspace, kda_fwd included) have raised since it was last cleared.
+ * Synchronises `stream` (hipStream_t or NULL) after reading, so *bits covers every call
+ * enqueued on that stream before this one; calls still running on other streams may
+ * raise bits later. clear != 0 resets the word to 0 (stream-ordered after the read).
+ * Returns KDA_OK, KDA_ERR_NULL (bits is NULL) or KDA_ERR_DEVICE.
+ */
+int kda_device_errors(void *stream, int32_t *bits, int32_t clear);
 
 /* Static, NUL-terminated description of a status code. */
 const char *kda_status_string(int status);

@@ -53,8 +53,9 @@ def _check_bf16(name, got, ref):
     assert synth.passes_bf16(m), (name, m)
 
 
-# the library picks 32 value columns per block below 1024 (sequence, head) chains and 64
-# from there; KDA_RECURRENT_TILE forces each of the three block shapes
+# the library picks the value-column tile per batch shape (128 columns per block for one
+# token per sequence, except 64 for an fp32 state from 16,384 chains); KDA_RECURRENT_TILE
+# forces each of the three block shapes
 @pytest.mark.parametrize("tile", [None, "128", "64", "32"])
 @pytest.mark.parametrize("N,H", [(1, 2), (7, 3), (300, 4)])
 @pytest.mark.parametrize("init", [True, False])

@@ -1,6 +1,7 @@
-"""Malformed cu_seqlens on the GPU: the chunk map sanitises the offsets (clamped to
-[0, T], made non-decreasing) before any other kernel reads them, sets the device error
-word to 2, and the call completes with every access in bounds. Ranges that were valid
+"""Malformed cu_seqlens on the GPU: every variant sanitises the offsets (clamped to
+[0, T], each raised to the largest offset before it) before using them, raises the device
+error bit 2 (in the device error word, and in the workspace's error word where there is a
+workspace), and the call completes with every access in bounds. Ranges that were valid
 keep correct outputs."""
 import sys
 
@@ -27,6 +28,8 @@ def _gpu():
 
 
 def _run(w, cu, variant):
+    """One call with the given offsets; returns (o, final state, workspace error word or
+    None for the variant without a workspace, device error word)."""
     import torch
     import chunked_gated_delta_kda_amd as kda
     from chunked_gated_delta_kda_amd import native
@@ -35,13 +38,17 @@ def _run(w, cu, variant):
     cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
     N = len(cu) - 1
     nbytes = kda.workspace_bytes(N, w.T, w.H, variant)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
     out = torch.full((w.T, w.H, 128), 7.0, device="cuda")
+    kda.device_errors(clear=True)
     o, f = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], cu_t, None, variant=variant,
                    workspace=ws, out=out)
-    torch.cuda.synchronize()
-    off = native.error_word_offset(N)
-    return o.cpu().numpy(), f.cpu().numpy(), int(ws[off:off + 4].view(torch.int32).item())
+    dev_err = kda.device_errors(clear=True)
+    word = None
+    if ws is not None:
+        off = native.error_word_offset(N)
+        word = int(ws[off:off + 4].view(torch.int32).item())
+    return o.cpu().numpy(), f.cpu().numpy(), word, dev_err
 
 
 # (offsets, T): decreasing, past T, negative start, nonzero start, short of T
@@ -49,14 +56,15 @@ CASES = [([0, 50, 30, 100], 100), ([0, 60, 140], 100), ([-5, 40, 100], 100), ([7
          ([0, 30, 70], 100), ([0, 100, 0, 100], 100)]
 
 
-@pytest.mark.parametrize("variant", ["split", "fused"])
+@pytest.mark.parametrize("variant", ["split", "fused", "recurrent"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "_".join(map(str, c[0])))
 def test_malformed_cu_seqlens(case, variant):
     cu, T = case
     w = synth.make_workload([T], 2, 5)
     _say(f"[robust] cu_seqlens={cu} T={T} variant={variant}")
-    o, f, err = _run(w, cu, variant)
-    assert err == ERR_CU_SEQLENS
+    o, f, word, dev_err = _run(w, cu, variant)
+    assert dev_err == ERR_CU_SEQLENS
+    assert word in (None, ERR_CU_SEQLENS)
     # sanitised offsets as the chunk map forms them
     cs = np.maximum.accumulate(np.clip(np.asarray(cu), 0, T))
     covered = np.zeros(T, dtype=bool)
@@ -76,7 +84,40 @@ def test_malformed_cu_seqlens(case, variant):
     assert synth.passes(mo) and synth.passes(mf)
 
 
-def test_wellformed_clears_error_word():
+@pytest.mark.parametrize("variant", ["split", "fused", "recurrent"])
+def test_wellformed_raises_nothing(variant):
     w = synth.make_workload([30, 70], 2, 6)
-    o, f, err = _run(w, [0, 30, 100], "split")
-    assert err == 0
+    o, f, word, dev_err = _run(w, [0, 30, 100], variant)
+    assert dev_err == 0 and word in (None, 0)
+
+
+def test_plain_kda_fwd_reports_malformed_offsets():
+    """kda_fwd without options (the library allocates and frees its own workspace): the
+    error is still visible through the device error word."""
+    import ctypes
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+    from chunked_gated_delta_kda_amd import native
+
+    lib = native.load_library()
+    w = synth.make_workload([100], 2, 8)
+    d = synth.to_device(w)
+    for cu, expect in (([0, 60, 30, 100], ERR_CU_SEQLENS), ([0, 30, 100], 0)):
+        cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+        out = torch.empty((w.T, w.H, 128), device="cuda")
+        fin = torch.empty((len(cu) - 1, w.H, 128, 128), device="cuda")
+        kda.device_errors(clear=True)
+        st = torch.cuda.current_stream()
+        p = lambda t: ctypes.c_void_p(t.data_ptr())
+        rc = lib.kda_fwd(p(d["q"]), p(d["k"]), p(d["v"]), p(d["g"]), p(d["beta"]), d["scale"], p(cu_t),
+                         len(cu) - 1, w.T, w.H, 128, None, p(out), p(fin), ctypes.c_void_p(st.cuda_stream))
+        assert rc == 0
+        bits = kda.device_errors(clear=True)
+        _say(f"[robust] plain kda_fwd cu={cu}: device error bits {bits}")
+        assert bits == expect
+        # Python fwd with check=True raises on the same offsets
+        if expect:
+            with pytest.raises(native.KdaDeviceError):
+                kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], cu_t, check=True)
+        else:
+            kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], cu_t, check=True)
