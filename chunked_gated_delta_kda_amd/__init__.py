@@ -9,7 +9,7 @@ import math
 
 from . import native
 
-__all__ = ["fwd", "decode", "workspace_bytes", "select_variant", "device_errors", "version", "native"]
+__all__ = ["fwd", "fwd_noalloc", "decode", "workspace_bytes", "select_variant", "device_errors", "version", "native"]
 
 HEAD_DIM = 128
 
@@ -160,6 +160,29 @@ def check_decode_args(q, k, v, g, beta, state=None, state_out="inplace", out=Non
     if out is not None:
         _expect("out", out, torch.float32, (N, H, Dk), dev)
     return N, H, state_dtype
+
+
+def fwd_noalloc(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None, *, out, final_state=None,
+                stream=None):
+    """KDA forward through kda_fwd_noalloc: the library allocates nothing (its kernels use a
+    fixed per-device scratch; at most native.NOALLOC_MAX_SEQS sequences). The caller passes
+    the outputs: ``out`` fp32 [T, H, 128] and, optionally, ``final_state`` fp32
+    [N, H, 128, 128]. Calls that overlap in time on one device race on the scratch.
+    Returns (out, final_state)."""
+    import torch
+
+    lib = native.load_library()
+    if q.device.type != "cuda":
+        raise ValueError("kda.fwd_noalloc needs device tensors")
+    T, H, N = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    if scale is None:
+        scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    rc = lib.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(cu_seqlens),
+                             N, T, H, HEAD_DIM, _ptr(initial_state), _ptr(out), _ptr(final_state),
+                             ctypes.c_void_p(st.cuda_stream))
+    native.check(rc)
+    return out, final_state
 
 
 def decode(q, k, v, g, beta, scale=None, state=None, *, out=None, state_out="inplace", state_dtype=None,

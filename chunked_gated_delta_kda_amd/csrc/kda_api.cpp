@@ -33,6 +33,29 @@ int32_t *device_error_word() {
     return (int32_t *)p;
 }
 
+// Scratch of kda_fwd_noalloc: every device the library runs on holds one copy. In host
+// code the array's name is only a stand-in for the symbol: its device address comes
+// from noalloc_scratch().
+static __device__ __align__(256) unsigned char noalloc_scratch_dev[KDA_NOALLOC_SCRATCH_BYTES];
+
+// Device address of the current device's scratch, resolved once per device
+// (hipGetSymbolAddress with that device current); nullptr on failure.
+static void *noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+    static std::atomic<void *> cache[64];
+    if (dev < 64) {
+        if (void *p = cache[dev].load(std::memory_order_acquire)) return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch_dev)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (dev < 64) cache[dev].store(p, std::memory_order_release);
+    return p;
+}
+
 }  // namespace kda
 
 namespace {
@@ -243,6 +266,7 @@ const char *kda_status_string(int s) {
     case KDA_ERR_LAUNCH: return "kernel launch failed";
     case KDA_ERR_DEVICE: return "HIP device error";
     case KDA_ERR_ALIAS: return "final_state partially overlaps initial_state";
+    case KDA_ERR_SCRATCH: return "kda_fwd_noalloc: more sequences than its fixed scratch holds (KDA_NOALLOC_MAX_SEQS)";
     default: return "unknown status";
     }
 }
@@ -472,6 +496,28 @@ int kda_fwd(const void *q, const void *k, const void *v, const float *g, const f
             float *final_state, void *stream) {
     return kda_fwd_ex(q, k, v, g, beta, scale, cu_seqlens, num_seqs, total_tokens, num_heads,
                       head_dim, initial_state, out, final_state, stream, nullptr);
+}
+
+int kda_fwd_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                    int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+                    float *final_state, void *stream) {
+    if (!shape_ok(num_seqs, total_tokens, num_heads)) return KDA_ERR_SHAPE;
+    const int picked = kda_select_variant(num_seqs, total_tokens, num_heads);
+    const int variant = picked == KDA_VARIANT_RECURRENT ? KDA_VARIANT_RECURRENT : KDA_VARIANT_FUSED;
+    kda_options opt{};
+    opt.variant = variant;
+    if (variant == KDA_VARIANT_FUSED) {
+        if (num_seqs > KDA_NOALLOC_MAX_SEQS) return KDA_ERR_SCRATCH;
+        const size_t need = ws_layout(num_seqs, total_tokens, num_heads, KDA_VARIANT_FUSED, 1, 0).total;
+        if (need > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+        void *ws = kda::noalloc_scratch();
+        if (!ws) return KDA_ERR_DEVICE;
+        opt.workspace = ws;
+        opt.workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+    }
+    return kda_fwd_ex(q, k, v, g, beta, scale, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim,
+                      initial_state, out, final_state, stream, &opt);
 }
 
 int kda_decode(const void *q, const void *k, const void *v, const float *g, const float *beta,

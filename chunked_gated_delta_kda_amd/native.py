@@ -12,17 +12,19 @@ LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(PKG, "libkda.so")
 
 KDA_OK = 0
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_UNSUPPORTED",
-          4: "KDA_ERR_ALLOC", 5: "KDA_ERR_LAUNCH", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_ALIAS"}
+          4: "KDA_ERR_ALLOC", 5: "KDA_ERR_LAUNCH", 6: "KDA_ERR_DEVICE", 7: "KDA_ERR_ALIAS",
+          8: "KDA_ERR_SCRATCH"}
 VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 
 #: every symbol include/kda.h declares
-EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_workspace_bytes", "kda_select_variant",
+EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_noalloc", "kda_workspace_bytes", "kda_select_variant",
            "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_device_errors", "kda_status_string",
            "kda_version")
 #: KDA_DEVERR_* bits of the device error word
 DEVERR = {1: "fused hand-off wait gave up (outputs invalid)", 2: "malformed cu_seqlens (sanitised)"}
 STATE_DTYPES = {"f32": 0, "bf16": 1}
 SEGMENT_ONE = 65536   # KDA_SEGMENT_ONE: unit of the launch plan's segment fractions
+NOALLOC_MAX_SEQS = 16384   # KDA_NOALLOC_MAX_SEQS
 KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent", 6: "parts"}
 
 
@@ -67,6 +69,8 @@ def load_library(path=LIB_PATH):
     lib.kda_fwd.restype = ctypes.c_int
     lib.kda_fwd_ex.argtypes = fwd_args + [ctypes.POINTER(KdaOptions)]
     lib.kda_fwd_ex.restype = ctypes.c_int
+    lib.kda_fwd_noalloc.argtypes = fwd_args
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.kda_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_select_variant.argtypes = [i32, i32, i32]

@@ -43,7 +43,8 @@ typedef enum kda_status {
     KDA_ERR_ALLOC = 4,       /* workspace allocation failed or caller workspace too small */
     KDA_ERR_LAUNCH = 5,      /* a kernel launch failed                                  */
     KDA_ERR_DEVICE = 6,      /* no usable gfx950 device, or a HIP runtime call failed   */
-    KDA_ERR_ALIAS = 7        /* final_state partially overlaps initial_state            */
+    KDA_ERR_ALIAS = 7,       /* final_state partially overlaps initial_state            */
+    KDA_ERR_SCRATCH = 8      /* kda_fwd_noalloc: the call needs more than its fixed scratch */
 } kda_status;
 
 typedef enum kda_variant {
@@ -133,6 +134,29 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
  * call leaves at 0 or at its KDA_DEVERR_* bits. */
 size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                            int32_t variant);
+
+/*
+ * kda_fwd_noalloc -- kda_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, outputs and errors as kda_fwd, but no allocation of any kind. The scratch
+ * its kernels need (chunk offsets, sequence order, sanitised offsets and an error word:
+ * about 12 bytes per sequence) lives in a fixed device array of KDA_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on until the process ends. It runs the
+ * token loop where KDA_VARIANT_AUTO would, and otherwise the fused variant (the split
+ * variant's chunk records do not fit a fixed buffer).
+ *   num_seqs at most KDA_NOALLOC_MAX_SEQS; beyond it the call returns KDA_ERR_SCRATCH
+ *   before anything is enqueued.
+ * Every call on one device shares that device's scratch and leaves its contents there;
+ * each call rewrites what it reads before reading it. Calls that overlap in time on one
+ * device (on different streams, or from different threads without ordering) race on the
+ * scratch: order them on one stream.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (256 * 1024)
+#define KDA_NOALLOC_MAX_SEQS 16384
+int kda_fwd_noalloc(const void *q, const void *k, const void *v, const float *g, const float *beta,
+                    float scale, const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens,
+                    int32_t num_heads, int32_t head_dim, const float *initial_state, float *out,
+                    float *final_state, void *stream);
 
 /* The variant KDA_VARIANT_AUTO resolves to for this shape. */
 int kda_select_variant(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
