@@ -70,8 +70,12 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 int64_t max_chunks(int64_t N, int64_t T, int cl = KDA_CHUNK) { return (T + cl - 1) / cl + N; }
 
 // The recurrence form 301 consumes 32-token chunk records; all others 16-token ones.
+// Forms 401/402 consume 32-token chunk records with fp16 operands (kda_h32.hip).
 int chunk_len(int waves) { return waves >= 300 ? 32 : KDA_CHUNK; }
-size_t rec_bytes(int waves) { return waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES; }
+bool fp16_form(int waves) { return waves == 401 || waves == 402; }
+size_t rec_bytes(int waves) {
+    return fp16_form(waves) ? kda::RECH_BYTES : waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES;
+}
 
 // Workspace: chunk offsets [N+1], sequence order [N], an error word, the sanitised
 // sequence offsets [N+1], and (split variant only) a state carry buffer [N, H, 128, 128]
@@ -96,12 +100,12 @@ constexpr size_t STATE_BYTES = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(floa
 // but 32768 x 16 1.21 | 1.41 (2). KDA_PARTS (1..MAX_PARTS) overrides, for the 16-token
 // forms.
 int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
-    if (waves >= 300) return 1;
+    if (waves == 301) return 1;
     if (const char *e = std::getenv("KDA_PARTS")) {
         const int p = std::atoi(e);
         if (p >= 1 && p <= MAX_PARTS) return p;
     }
-    if (waves != 101) return 1;
+    if (waves != 101 && waves != 401) return 1;
     int64_t p = 32 / (N * H);
     const int64_t by_len = max_chunks(N, T) / 64;
     if (by_len < p) p = by_len;
@@ -150,25 +154,29 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // (1 or 2 slices per block, a chain wave and two output waves per slice, one loader
 // wave). 301: the paired form over 32-token chunks. KDA_RECUR_WAVES overrides the
 // choice, for tuning.
-int recur_waves(int64_t N, int64_t H, const char *env = "KDA_RECUR_WAVES") {
+int recur_waves(int64_t N, int64_t T, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 8 || w == 9 || w == 101 || w == 102 || w == 301) return w;
+        if (w == 8 || w == 9 || w == 101 || w == 102 || w == 301 || w == 401 || w == 402) return w;
     }
-    // Measured on MI355X (ms, best segment count each; one slice per block 101 | two
-    // slices 102), one sequence of 8192 tokens: 20 heads 0.326 | 0.370; 24 heads 0.356 |
-    // 0.384; 28 heads 0.391 | 0.401; 32 heads 0.408 | 0.417; 40 heads 0.673 | 0.460 (101
-    // needs two rounds of blocks from 33 chains). Then (ms; paired 102 | eight-wave 8):
-    // 128 chains (8 x 1024 tokens, 16 heads) 0.181 | 0.205; 192 chains 0.476 | 0.478; 512
-    // chains of 2048 tokens 1.23 | 1.00; 8192 chains of 64 tokens 1.18 | 0.72; but 384
-    // chains of skewed lengths (12 sequences, 32768 tokens, 32 heads) 1.29 | 2.43, where
-    // the longest chain sets the end time. From 192 chains the hybrid (9) picks per chain
-    // on the device: paired for chains longer than a CU's balanced share, eight-wave
-    // otherwise.
+    // The 32-token fp16 forms (401: one 16-column slice per block, 402: two) take one
+    // serial step per 32 tokens. Measured on MI355X (ms per call; 401 | 402 | paired
+    // 16-token 101 or 102): one sequence of 8192 tokens x 32 heads 0.341 | 0.364 | 0.438;
+    // 8 x 1024 tokens x 16 heads 0.185 | 0.153 | 0.190; 65536 x 8 (over parts) 1.084 |
+    // 1.64 | 1.43; 4 x 4096 x 8 0.170 | 0.198; 2 x 8192 x 16 0.327 | 0.351. With many
+    // chains (ms; 402 | hybrid 9 | eight-wave 8 over 16-token records): 12 skewed
+    // sequences (32768 tokens) x 32 heads 0.991 | 1.238 | -; 24 x 1024 x 32 0.736 |
+    // 0.807 | 0.752; 16 x 2048 x 32 0.949 | 1.044 | 0.949; 8 x 2048 x 32 0.505 | 0.537 |
+    // 0.504; but 24 x 512 x 16 0.226 | 0.258 | 0.210; 256 x 256 x 32 2.22 | 2.30 | 2.09;
+    // 64 x 128 x 32 0.370 | 0.356 | 0.304; 256 x 16 x 32 0.672 | 0.431 | 0.336. So from
+    // 192 chains 402 where sequences average 1024 tokens or more, else the hybrid, which
+    // picks per chain on the device (paired blocks for chains longer than a CU's
+    // balanced share, one eight-wave block otherwise) and so keeps one long sequence in
+    // a batch of short ones off a slow eight-wave block.
     const int64_t chains = N * H;
-    if (chains <= 32) return 101;
-    if (chains < 192) return 102;
-    return 9;
+    if (chains <= 32) return 401;
+    if (chains < 192) return 402;
+    return T >= 1024 * N ? 402 : 9;
 }
 
 // Number of segments of the split variant. With S > 1 the launches are
@@ -296,7 +304,7 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
+    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, total_tokens, num_heads) : 0;
     const int cl = v == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
     kda_launch_info plan[2 + KDA_MAX_SEGMENTS];
     int n = 0;
@@ -332,7 +340,7 @@ size_t kda_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_h
     const int v = variant == KDA_VARIANT_AUTO
                       ? kda_select_variant(num_seqs, total_tokens, num_heads)
                       : variant;
-    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, num_heads) : 0;
+    const int waves = v == KDA_VARIANT_SPLIT ? recur_waves(num_seqs, total_tokens, num_heads) : 0;
     const int segs = v == KDA_VARIANT_SPLIT ? split_segments(num_seqs, total_tokens, num_heads, waves) : 1;
     const int parts = v == KDA_VARIANT_SPLIT ? split_parts(num_seqs, total_tokens, num_heads, waves) : 1;
     return ws_layout(num_seqs, total_tokens, num_heads, v, segs, waves, parts).total;
@@ -367,12 +375,13 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                            : variant;
     hipStream_t st = (hipStream_t)stream;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, H) : fused_waves(N, H);
+    const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, T, H) : fused_waves(N, H);
     const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, T, H, waves) : 1;
     const int parts = chosen == KDA_VARIANT_SPLIT ? split_parts(N, T, H, waves) : 1;
     const Layout lay = ws_layout(N, T, H, chosen, segs, waves, parts);
     const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
-    const bool c32 = cl == 32;
+    const bool c32 = cl == 32 && !fp16_form(waves);
+    const bool h32 = fp16_form(waves);
 
     // profiling events: [0] before the first kernel launch, [i] after the i-th (all on
     // the caller's stream, where every kernel runs in order)
@@ -418,10 +427,12 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
         auto prep = [&](int b, int e) {
+            if (h32) return kda::launch_prep_h32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
             return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st)
                        : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
         };
         auto recur_range = [&](float *carry, int b, int e) {
+            if (h32) return kda::launch_recur_h32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
             return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
                        : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
@@ -437,7 +448,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
                  around(st, [&] {
                      return kda::launch_parts(recs, v16, cus, chunk_off, order, N, T, H, parts, initial_state, out,
-                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, st);
+                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, h32, st);
                  });
         } else if (segs == 1) {
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
@@ -453,7 +464,11 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
                 a.fb = bound(sg), a.fe = bound(sg + 1), a.pb = bound(sg + 1), a.pe = bound(sg + 2);
-                ok = around(st, [&] { return c32 ? kda::launch_recur32_prep(a, waves, st) : kda::launch_recur_prep(a, waves, st); });
+                ok = around(st, [&] {
+                    return h32   ? kda::launch_recur_h32_prep(a, waves, st)
+                           : c32 ? kda::launch_recur32_prep(a, waves, st)
+                                 : kda::launch_recur_prep(a, waves, st);
+                });
             }
             ok = ok && around(st, [&] { return recur_range(a.carry, bound(segs - 1), kda::SEG_ONE); });
         }

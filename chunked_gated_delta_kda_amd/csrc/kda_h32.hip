@@ -1,0 +1,863 @@
+// kda_h32.hip -- the KDA forward over 32-token chunks with fp16 recurrence operands.
+//
+// A 32-token chunk is prepared as two 16-token halves a, b (each with the 16-token
+// chunked form of kda_device.hpp: gates, K+K-^T, Neumann inverse, W) and combined into
+// one 32-row WY form, so that one serial step of the recurrence covers 32 tokens:
+//
+//   V_new = U - W S,                 U = (T Diag(beta)) V           (32 x dv)
+//   O     = Q+ S + P V_new                                          (32 x dv)
+//   S    <- Diag(e^{G_C}) S + K~^T V_new                            (dk x dv)
+//
+// With D_a = Diag(e^{G_a}) the first half's total decay and every subscripted quantity
+// the 16-token one of its half (gates cumulated from the start of that half), T of the
+// whole chunk is block lower triangular, which gives
+//
+//   W rows a = W_a,  W rows b = W_b D_a - M W_a,        M = (W_b D_a) K-_a^T = W_b K~_a^T
+//   T Diag(beta) = [[TB_a, 0], [-M TB_a, TB_b]]
+//   P = [[P_aa, 0], [P_ba, P_bb]],                      P_ba = (Q+_b D_a) K-_a^T
+//   K~ rows a = K~_a e^{G_b},  Q+ rows b = Q+_b D_a,    e^{G_C} = e^{G_a + G_b}
+//
+// (this library's derivation from the per-token recurrence; every exponential stays
+// within the range of a 16-token chunk, so no anchor is needed). Every factor of the
+// serial chain (W, T Diag(beta), K~, the state as an operand, V_new) is bounded by the
+// key norms or the state, so it is rounded once to fp16 (11 significant bits) and
+// multiplied on v_mfma_f32_16x16x32_f16, where the 16-token path needed two bf16
+// pieces (hi + lo) and a second product for the same accuracy. The 32 tokens of a chunk
+// fill the 32-deep contraction of K~^T V_new and of P V_new exactly: the state update is
+// 8 products per 32 tokens instead of 32. The output's Q+ S, off the chain, keeps split
+// bf16 on both sides (three products): where the output is a decaying read-out of the
+// state (beta ~ 0), a few early tokens carry most of |o| and single fp16 rounding of Q+
+// and S there would reach the max-abs gate, which is relative to the RMS of all of o.
+//
+// fp16 holds magnitudes below 65504: the recurrence's operands are the state, V_new
+// (of the size of v) and quantities bounded by |k| and |q|, which the L2-normalised
+// keys and queries of KDA keep far inside that range.
+//
+// 32-deep token slots. The MFMA A operand lane l holds row l%16 and k-slots 8(l/16)+i;
+// here slot 8g+i (g = l/16) carries token tau(8g+i) = 4g+i (i < 4, half a) or
+// 16+4g+i-4 (i >= 4, half b), so that V_new, produced as two 16x16 D-layout blocks
+// (lane: rows 4g..4g+3 of each half), is the B operand of K~^T V_new and P V_new as it
+// stands in registers.
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+namespace kda {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int CH = 32;   // chunk length of this path
+
+__device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+__device__ __forceinline__ f16x8 cat16(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Write-only sink for output rows past a partial chunk's end (see the output waves).
+__device__ float h32_sink[64];
+
+// ---------------------------------------------------------------- chunk record
+// One (32-token chunk, head), fp16 MFMA operands in per-lane order (16 bytes per lane per
+// 1 KiB piece). The chain's pieces come first, one contiguous run of whole wave loads.
+struct RecH {
+    static constexpr int WN = 0;         // f16 [2 row blocks][4 kb][64][8]: -W, state-permuted A operand
+    static constexpr int KT = 8192;      // f16 [8 key blocks][64][8]: K~^T, token slots tau
+    static constexpr int TB = 16384;     // f16 [2][64][8]: T Diag(beta), token slots tau
+    static constexpr int EGP = 18432;    // f32 [128]: e^{G_C}, lane-permuted (egp_index); 512 B unused after
+    static constexpr int CHAIN = 19456;
+    static constexpr int QH = 19456;     // bf16 [2][4][64][8]: Q+ hi (scale folded in), state-permuted A operand
+    static constexpr int QL = 27648;     // bf16 [2][4][64][8]: Q+ lo
+    static constexpr int PP = 35840;     // f16 [2][64][8]: P = incl_lower(Q+ K-^T), token slots tau
+    static constexpr int BYTES = 37888;
+};
+static_assert(RecH::CHAIN % 1024 == 0 && RecH::BYTES % 1024 == 0, "record pieces in whole wave loads");
+static_assert(RecH::BYTES == RECH_BYTES, "record size mismatch");
+
+// ---------------------------------------------------------------- prep
+// LDS of one prep wave: the 16-token tiles of kda_device.hpp plus a 16x16 fp32 transpose.
+struct PrepHLds {
+    PrepLds t;
+    float tr[16][17];
+};
+
+// Transpose of a D-layout 16x16 matrix (lane (g, c) holds X[4g+j][c]): returns the
+// lane's values of X^T in D layout, i.e. X[c][4g+j].
+__device__ __forceinline__ f32x4 transpose16(f32x4 x, float (*tr)[17]) {
+    const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tr[4 * g + j][c] = x[j];
+    wave_sync();
+    f32x4 y;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = tr[c][4 * g + j];
+    wave_sync();
+    return y;
+}
+
+// Raw inputs of one 16-token half on this lane's channel pair: g, and q, k (bf16 pairs).
+// Loaded unconditionally (rows past the half's nc tokens reread row `fb`, a real token)
+// so that both halves' loads are issued together at the start of a chunk and one
+// memory latency is exposed instead of one per half; prep_half masks rows past nc.
+struct HalfIn {
+    f32x2 g[C];
+    uint32_t q[C], k[C];
+};
+__device__ __forceinline__ void load_half(HalfIn &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                          const float *__restrict__ g, int64_t t0, int nc, int64_t fb, int h,
+                                          int H, int c0) {
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const int64_t row = ((t < nc ? t0 + t : fb) * (int64_t)H + h) * D + c0;
+        x.g[t] = *(const f32x2 *)(g + row);
+        x.q[t] = *(const uint32_t *)(q + row);
+        x.k[t] = *(const uint32_t *)(k + row);
+    }
+}
+
+// One 16-token half of a 32-token chunk (HALF 0 = a, 1 = b), one wave. Rows past nc
+// carry k = q = 0, g = 0, beta = 0, which adds nothing. Writes the half's K~ token slots
+// (fp16) into the record's KT piece and its Q+ rows into QP; HALF 0 also writes its rows
+// of -W. Returns, per lane, with "R layout" meaning lane (g, c) holds X[c][4g+j]:
+//   Wt[b]  R layout of W[:, key block b] (HALF 1: scaled by D_a, i.e. W_b D_a)
+//   Wd[b]  (HALF 0) D layout of W[:, key block b]
+//   tbr    R layout of T Diag(beta);  pr  R layout of P (causal, diagonal kept)
+//   ec     e^{G_C} of this half on the lane's channel pair
+//   qh, ql hi and lo bf16 A operands of this half's Q+ rows (state permutation; HALF 1:
+//          Q+_b D_a), also written to the record
+// kts (HALF 0): K~ is further scaled per channel by e^{G_b}; ega (HALF 1): lane-permuted
+// e^{G_a}.
+template <int HALF>
+__device__ __forceinline__ void prep_half(const HalfIn &in, const float *__restrict__ beta,
+                                          int64_t t0, int nc, int h, int H, float scale, PrepLds &L,
+                                          char *rec, f32x2 kts, f32x2 ega, f32x4 (&Wt)[8], f32x4 (&Wd)[8],
+                                          f32x4 &tbr, f32x4 &pr, f32x2 &ec, bf16x8 (&qh)[4], bf16x8 (&ql)[4]) {
+    const int l = threadIdx.x & 63;
+    const int c0 = 2 * l;
+    const int r = l & 15, gq = l >> 4;
+
+    // ---- gates and scaled operands, lane = channel pair, loop over tokens (base-2 sums)
+    float G0[C], G1[C];
+    uint32_t qv[C], kv[C];
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        const bool in_range = t < nc;
+        const f32x2 gt = in_range ? in.g[t] : f32x2{0.f, 0.f};
+        const uint32_t qq = in_range ? in.q[t] : 0u, kk = in_range ? in.k[t] : 0u;
+        acc0 = __builtin_fmaf(fmaxf(gt.x, LOWER_BOUND), LOG2E, acc0);
+        acc1 = __builtin_fmaf(fmaxf(gt.y, LOWER_BOUND), LOG2E, acc1);
+        G0[t] = acc0;
+        G1[t] = acc1;
+        qv[t] = qq;
+        kv[t] = kk;
+    }
+    const float eC0 = __builtin_amdgcn_exp2f(acc0), eC1 = __builtin_amdgcn_exp2f(acc1);
+    ec = f32x2{eC0, eC1};
+    const float kt0 = HALF == 0 ? eC0 * kts.x : eC0, kt1 = HALF == 0 ? eC1 * kts.y : eC1;
+
+    uint32_t kpT[2][8], ktT[2][8];   // per channel, two tokens per dword: K+ (bf16), K~ (fp16)
+#pragma unroll
+    for (int t = 0; t < C; t += 2) {
+        float kpv[2][2], ktv[2][2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int tt = t + u;
+            const float ep0 = __builtin_amdgcn_exp2f(G0[tt]), ep1 = __builtin_amdgcn_exp2f(G1[tt]);
+            const float en0 = __builtin_amdgcn_exp2f(-G0[tt]), en1 = __builtin_amdgcn_exp2f(-G1[tt]);
+            const float k0 = bf_lo(kv[tt]), k1 = bf_hi(kv[tt]);
+            const float q0 = bf_lo(qv[tt]), q1 = bf_hi(qv[tt]);
+            const f32x2 kp = {k0 * ep0, k1 * ep1};
+            const f32x2 km = {k0 * en0, k1 * en1};
+            const f32x2 qp = {scale * q0 * ep0, scale * q1 * ep1};
+            const int rc = PrepLds::at(tt, c0);
+            *(uint32_t *)&L.kp[rc] = pack2(kp.x, kp.y);
+            bf16x2 hi, lo;
+            split2(km, hi, lo);
+            *(bf16x2 *)&L.kmh[rc] = hi;
+            *(bf16x2 *)&L.kml[rc] = lo;
+            split2(qp, hi, lo);
+            *(bf16x2 *)&L.qph[rc] = hi;
+            *(bf16x2 *)&L.qpl[rc] = lo;
+            kpv[u][0] = kp.x;
+            kpv[u][1] = kp.y;
+            ktv[u][0] = km.x * kt0;      // K~ = K e^{G_C - G} (times e^{G_b} for half a)
+            ktv[u][1] = km.y * kt1;
+        }
+#pragma unroll
+        for (int ch = 0; ch < 2; ++ch) {
+            kpT[ch][t / 2] = pack2(kpv[0][ch], kpv[1][ch]);
+            ktT[ch][t / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{ktv[0][ch], ktv[1][ch]}), f16x2));
+        }
+    }
+    // K+ transposed into LDS (operand of W); K~ straight into the record: channel c,
+    // half-local tokens 4e..4e+3 are token slots 8e + 4 HALF .. + 3 of lane 16e + c % 16
+    // of key block c / 16
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+        const int c = c0 + ch;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            *(uint2 *)&L.kpt[PrepLds::at_t(c, 4 * e)] = uint2{kpT[ch][2 * e], kpT[ch][2 * e + 1]};
+            *(uint2 *)(rec + RecH::KT + (c >> 4) * 1024 + (16 * e + (c & 15)) * 16 + HALF * 8) =
+                uint2{ktT[ch][2 * e], ktT[ch][2 * e + 1]};
+        }
+    }
+    float br = 0.f;
+    f32x4 bj = {0.f, 0.f, 0.f, 0.f};
+    if (r < nc) br = beta[(t0 + r) * (int64_t)H + h];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        if (4 * gq + j < nc) bj[j] = beta[(t0 + 4 * gq + j) * (int64_t)H + h];
+    wave_sync();
+
+    // ---- K+K-^T (both orientations) and the causal Q+K-^T, 128-deep
+    f32x4 akk = {0.f, 0.f, 0.f, 0.f}, akt = akk, pt = akk;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int off = PrepLds::at(r, 32 * kb + 8 * gq);
+        const bf16x8 kp = *(const bf16x8 *)&L.kp[off];
+        const bf16x8 kmh = *(const bf16x8 *)&L.kmh[off];
+        const bf16x8 kml = *(const bf16x8 *)&L.kml[off];
+        const bf16x8 qph = *(const bf16x8 *)&L.qph[off];
+        const bf16x8 qpl = *(const bf16x8 *)&L.qpl[off];
+        akk = mfma(kp, kmh, akk);   // (K+K-^T)[4g+j][r]
+        akt = mfma(kmh, kp, akt);   // (K+K-^T)[r][4g+j]
+        pt = mfma(kmh, qph, pt);    // (Q+K-^T)[r][4g+j], split 3-term
+        pt = mfma(kmh, qpl, pt);
+        pt = mfma(kml, qph, pt);
+    }
+    f32x4 Am, At;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = 4 * gq + j;
+        Am[j] = (r < row) ? bj[j] * akk[j] : 0.f;   // A[row][r]
+        At[j] = (row < r) ? br * akt[j] : 0.f;       // A^T[row][r] = A[r][row]
+        pr[j] = (row <= r) ? pt[j] : 0.f;            // P[r][row]
+    }
+
+    // ---- T^T = (I + A^T)^{-1} = (I - X)(I + X^2)(I + X^4)(I + X^8), X = A^T
+    const f32x4 X2 = mm16(Am, At);
+    const f32x4 A2 = mm16(At, Am);
+    const f32x4 X4 = mm16(A2, X2);
+    const f32x4 A4 = mm16(X2, A2);
+    const f32x4 X8 = mm16(A4, X4);
+    const f32x4 R1 = mm16(eye_plus(A4, l, 1.f), eye_plus(X8, l, 1.f));
+    const f32x4 R2 = mm16(eye_plus(A2, l, 1.f), R1);
+    const f32x4 Tt = mm16(eye_plus(Am, l, -1.f), R2);   // Tt[j] = T[r][4g+j]
+    tbr = Tt * bj;                                      // (T Diag(beta))[r][4g+j]
+    bf16x8 tb;
+    {
+        bf16x4 hi, lo;
+        split4(tbr, hi, lo);
+        tb = cat(hi, lo);
+    }
+
+    // ---- W = T Diag(beta) K+, one 16-column key block at a time, in both layouts
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bf16x4 a = *(const bf16x4 *)&L.kpt[PrepLds::at_t(16 * b + r, 4 * gq)];
+        Wt[b] = mfma(cat(a, a), tb, f32x4{0.f, 0.f, 0.f, 0.f});   // W[r][16b+4g+j]
+        if (HALF == 1) Wt[b] = decay_any(b, Wt[b], ega);
+        if (HALF == 0) Wd[b] = mfma(tb, cat(a, a), f32x4{0.f, 0.f, 0.f, 0.f});   // W[4g+j][16b+r]
+    }
+    // ---- Q+ rows of this half (fp16, scaled to the chunk start) and, for half a, -W rows
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int o0 = PrepLds::at(r, 32 * kb + 4 * gq), o1 = PrepLds::at(r, 32 * kb + 16 + 4 * gq);
+        const bf16x4 h0 = *(const bf16x4 *)&L.qph[o0], h1 = *(const bf16x4 *)&L.qph[o1];
+        const bf16x4 l0 = *(const bf16x4 *)&L.qpl[o0], l1 = *(const bf16x4 *)&L.qpl[o1];
+        if (HALF == 1) {
+            f32x4 x0, x1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x0[j] = (float)h0[j] + (float)l0[j];
+                x1[j] = (float)h1[j] + (float)l1[j];
+            }
+            x0 = decay_any(2 * kb, x0, ega);
+            x1 = decay_any(2 * kb + 1, x1, ega);
+            bf16x4 a0, b0, a1, b1;
+            split4(x0, a0, b0);
+            split4(x1, a1, b1);
+            qh[kb] = cat(a0, a1);
+            ql[kb] = cat(b0, b1);
+        } else {
+            qh[kb] = cat(h0, h1);
+            ql[kb] = cat(l0, l1);
+        }
+        *(bf16x8 *)(rec + RecH::QH + (HALF * 4 + kb) * 1024 + l * 16) = qh[kb];
+        *(bf16x8 *)(rec + RecH::QL + (HALF * 4 + kb) * 1024 + l * 16) = ql[kb];
+        if (HALF == 0)
+            *(f16x8 *)(rec + RecH::WN + kb * 1024 + l * 16) = cat16(to_f16x4(-Wt[2 * kb]), to_f16x4(-Wt[2 * kb + 1]));
+    }
+}
+
+// One wave turns one (32-token chunk, head) into a chunk record. t0: first token; nc:
+// its length (1..32).
+__device__ __forceinline__ void prep_h32(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                         const float *__restrict__ g, const float *__restrict__ beta, int64_t t0,
+                                         int nc, int h, int H, float scale, PrepHLds &LL, char *rec) {
+    PrepLds &L = LL.t;
+    const int l = threadIdx.x & 63, c0 = 2 * l, r = l & 15, gq = l >> 4;
+    const int nca = nc < C ? nc : C, ncb = nc > C ? nc - C : 0;
+    // every input load of the chunk issued at once
+    HalfIn ia, ib;
+    load_half(ia, q, k, g, t0, nca, t0, h, H, c0);
+    load_half(ib, q, k, g, t0 + C, ncb, t0, h, H, c0);
+    // gate total of the second half on this lane's channel pair (base 2)
+    float gb0 = 0.f, gb1 = 0.f;
+#pragma unroll
+    for (int t = 0; t < C; ++t) {
+        gb0 = __builtin_fmaf(t < ncb ? fmaxf(ib.g[t].x, LOWER_BOUND) : 0.f, LOG2E, gb0);
+        gb1 = __builtin_fmaf(t < ncb ? fmaxf(ib.g[t].y, LOWER_BOUND) : 0.f, LOG2E, gb1);
+    }
+    const f32x2 eb = {__builtin_amdgcn_exp2f(gb0), __builtin_amdgcn_exp2f(gb1)};
+
+    // ---- half a
+    f32x4 Wt[8], Wd[8], tba, pa, tbb, pb;
+    f32x2 ea, ebx;
+    bf16x8 qh[4], ql[4];
+    prep_half<0>(ia, beta, t0, nca, h, H, scale, L, rec, eb, f32x2{1.f, 1.f}, Wt, Wd, tba, pa, ea, qh, ql);
+    *(f32x2 *)(rec + RecH::EGP + egp_index(c0) * 4) = f32x2{ea.x * eb.x, ea.y * eb.y};
+    // K-_a as an MFMA operand (row = token of a, k-slots = keys in the state permutation)
+    bf16x8 kah[4], kal[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int o0 = PrepLds::at(r, 32 * kb + 4 * gq), o1 = PrepLds::at(r, 32 * kb + 16 + 4 * gq);
+        kah[kb] = cat(*(const bf16x4 *)&L.kmh[o0], *(const bf16x4 *)&L.kmh[o1]);
+        kal[kb] = cat(*(const bf16x4 *)&L.kml[o0], *(const bf16x4 *)&L.kml[o1]);
+    }
+    // e^{G_a} lane-permuted, through LDS
+    *(f32x2 *)&L.egs[egp_index(c0)] = ea;
+    wave_sync();
+    const f32x2 ega = *(const f32x2 *)&L.egs[2 * l];
+    wave_sync();
+
+    // ---- half b (W and Q+ scaled by D_a)
+    f32x4 Wb[8], unused[8];
+    prep_half<1>(ib, beta, t0 + C, ncb, h, H, scale, L, rec, f32x2{1.f, 1.f}, ega, Wb, unused, tbb, pb, ebx,
+                 qh, ql);
+
+    // ---- cross terms, transposed products so that the results land in R layout
+    // M = (W_b D_a) K-_a^T and P_ba = (Q+_b D_a) K-_a^T, 3-term split products
+    f32x4 mr = {0.f, 0.f, 0.f, 0.f}, pbr = mr;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        bf16x4 h0, l0, h1, l1;
+        split4(Wb[2 * kb], h0, l0);
+        split4(Wb[2 * kb + 1], h1, l1);
+        const bf16x8 wh = cat(h0, h1), wl = cat(l0, l1);
+        mr = mfma(kah[kb], wh, mr);
+        mr = mfma(kal[kb], wh, mr);
+        mr = mfma(kah[kb], wl, mr);
+        pbr = mfma(kah[kb], qh[kb], pbr);
+        pbr = mfma(kah[kb], ql[kb], pbr);
+        pbr = mfma(kal[kb], qh[kb], pbr);
+    }
+    // rows b of T Diag(beta), columns a: -M TB_a;  rows b of W: W_b D_a - M W_a
+    const f32x4 tbx = -mm16(transpose16(tba, LL.tr), mr);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) Wb[b] -= mm16(Wd[b], mr);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+        *(f16x8 *)(rec + RecH::WN + (4 + kb) * 1024 + l * 16) = cat16(to_f16x4(-Wb[2 * kb]), to_f16x4(-Wb[2 * kb + 1]));
+    const f16x4 z = {};
+    *(f16x8 *)(rec + RecH::TB + l * 16) = cat16(to_f16x4(tba), z);
+    *(f16x8 *)(rec + RecH::TB + 1024 + l * 16) = cat16(to_f16x4(tbx), to_f16x4(tbb));
+    *(f16x8 *)(rec + RecH::PP + l * 16) = cat16(to_f16x4(pa), z);
+    *(f16x8 *)(rec + RecH::PP + 1024 + l * 16) = cat16(to_f16x4(pbr), to_f16x4(pb));
+}
+
+// Record of chunk ci (global index, 32-token chunks), head h.
+__device__ __forceinline__ void prep_h32_one(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                             const float *__restrict__ g, const float *__restrict__ beta,
+                                             const int32_t *__restrict__ cu, int N, int T, int H, float scale,
+                                             const int32_t *__restrict__ chunk_off, char *__restrict__ recs, int ci,
+                                             int h, PrepHLds &L) {
+    int lo = 0, hi = N - 1;   // sequence owning chunk ci: largest n with chunk_off[n] <= ci
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= ci) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int64_t t0 = bos + (int64_t)CH * (ci - chunk_off[n]);
+    const int nc = (int)min<int64_t>(CH, eos - t0);
+    prep_h32(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * RecH::BYTES);
+}
+
+__global__ __launch_bounds__(64) void prep_h32_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                      const float *__restrict__ g, const float *__restrict__ beta,
+                                                      const int32_t *__restrict__ cu, int N, int T, int H, float scale,
+                                                      const int32_t *__restrict__ chunk_off, char *__restrict__ recs,
+                                                      int fb, int fe) {
+    __shared__ PrepHLds L;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, fb, fe, blockIdx.x, h);
+    if (ci < 0) return;
+    prep_h32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
+}
+
+// ---------------------------------------------------------------- recurrence
+// The paired recurrence over 32-token records: NW 16-column slices per block, per slice a
+// chain wave and two output waves (roles and SIMD placement as PairLayout), one loader
+// wave. The chain wave runs V_new = U - W S and S <- D S + K~^T V_new and publishes, per
+// chunk, the state it started from (fp32) and V_new; output wave parity p forms
+// O = Q+ S + P V_new of chunks m = p mod 2 over the two barriers after the chunk. One
+// barrier per chunk; snapshots rotate through three buffers; the loader fills an
+// NSLOT-deep LDS ring with the chain's pieces and the block's V tile by direct
+// global->LDS loads.
+template <int NW>
+struct PairH {
+    static constexpr int VCOLS = 16 * NW;
+    static constexpr int V_LPR = VCOLS * 2 / 16;     // lanes per V row (16 B each)
+    static constexpr int V_RPL = 64 / V_LPR;         // V rows per wave load
+    static constexpr int V_LOADS = CH / V_RPL;
+    static constexpr int REC_LOADS = RecH::CHAIN / 1024;
+    static constexpr int LOADS = REC_LOADS + V_LOADS;
+    static constexpr int SV = RecH::CHAIN;           // slot: V tile [32][VCOLS] bf16 after the chain pieces
+    static constexpr int SLOT = SV + V_LOADS * 1024;
+    static constexpr int SNAP = 8 * 1024 + 1024;     // fp32 state (8 key blocks of 16 rows) + V_new (fp16)
+    static constexpr int SNAPS = 3;
+    static_assert(V_RPL * V_LOADS == CH, "V tile geometry");
+};
+template <int NW>
+constexpr int pairh_nslot() { return NW == 1 ? 5 : 4; }
+template <int NW, int NSLOT>
+struct PairHLds {
+    static constexpr int BYTES = NSLOT * PairH<NW>::SLOT + PairH<NW>::SNAPS * NW * PairH<NW>::SNAP;
+    static_assert(BYTES <= 160 * 1024 && BYTES > 80 * 1024, "one block per CU");
+};
+
+// A launch covers the segment [fb, fe) of every sequence (seg_chunk over 32-token chunks).
+// The state enters from s0 (or zeros) at a sequence's first chunk and from `carry`
+// otherwise, and leaves to sfin after its last chunk and to `carry` otherwise. Sequences
+// without chunks copy s0 to sfin in the launch of the first segment. With zero_v the chain
+// runs as if every v were 0 (the part of the chain linear in the entry state; outputs then
+// not valid).
+template <int NW, int NSLOT>
+__device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char *__restrict__ recs,
+                                                const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+                                                const int32_t *__restrict__ chunk_off,
+                                                const int32_t *__restrict__ order, int N, int T, int H,
+                                                const float *s0, float *__restrict__ out, float *sfin, float *carry,
+                                                int fb, int fe, bool zero_v = false) {
+    using P = PairH<NW>;
+    using PL = PairLayout<NW>;
+    constexpr int LOADS = P::LOADS;
+    constexpr int SLOT = P::SLOT;
+    static_assert(NSLOT >= 3, "the chain reads one chunk ahead of the one it computes");
+    static_assert((NSLOT - 2) * LOADS < 64, "ring deeper than the vmcnt range");
+    char *snaps = ring + NSLOT * SLOT;
+
+    constexpr int PARTS = D / (16 * NW);
+    const int part = bid % PARTS;
+    const int sh = bid / PARTS;
+    const int h = sh % H;
+    const int n = order[sh / H];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63, c = l & 15, gq = l >> 4;
+    const bool chain = w < NW;
+    const bool loader = w == PL::LOADER;
+    const bool idle = w == PL::IDLE;
+    const int parity = (w == PL::out_wave(0, 1) || w == PL::out_wave(NW - 1, 1)) ? 1 : 0;
+    const int slice = chain ? w : ((loader || idle) ? 0 : (w == PL::out_wave(0, parity) ? 0 : 1));
+    const int vcol0 = part * P::VCOLS;
+    const int col = vcol0 + slice * 16 + c;
+    const int64_t seq_bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
+    const int seq_c0 = chunk_off[n], seq_c1 = chunk_off[n + 1];
+    const int ci0 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fb);
+    const int ci1 = seq_c0 + seg_chunk(seq_c1 - seq_c0, fe);
+    const int64_t sbase = ((int64_t)n * H + h) * D * D + col;
+    if (ci0 >= ci1) {
+        if (seq_c0 == seq_c1 && fb == 0 && chain && sfin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
+                    sfin[o] = s0 ? s0[o] : 0.f;
+                }
+        }
+        return;
+    }
+    const int nch = ci1 - ci0;
+    const int64_t bos = seq_bos + (int64_t)CH * (ci0 - seq_c0);
+    const float *sin = ci0 == seq_c0 ? s0 : carry;
+    float *sout = ci1 == seq_c1 ? sfin : carry;
+    auto snap_of = [&](int it) { return snaps + ((it % P::SNAPS) * NW + slice) * P::SNAP; };
+    auto rec_of = [&](int m) { return recs + ((int64_t)(ci0 + m) * H + h) * RecH::BYTES; };
+    auto sync = [] {
+        __builtin_amdgcn_s_barrier();      // slots it, it+1 ready; slot it-1 released
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    if (loader) {
+        auto fill = [&](int it) {
+            const int m = it < nch ? it : nch - 1;
+            const int64_t t0 = bos + (int64_t)CH * m;
+            const int nc = (int)min<int64_t>(CH, eos - t0);
+            char *slot = ring + (it % NSLOT) * SLOT;
+            const char *rec = rec_of(m);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                if (i < P::REC_LOADS) {
+                    __builtin_amdgcn_global_load_lds((const void *)(rec + i * 1024 + l * 16),
+                                                     KDA_LDS(slot + i * 1024), 16, 0, 0);
+                } else {
+                    const int j = i - P::REC_LOADS;
+                    const int row = j * P::V_RPL + l / P::V_LPR;
+                    const int cc = vcol0 + (l % P::V_LPR) * 8;
+                    const int64_t t = t0 + (row < nc ? row : nc - 1);   // rows past the end: finite filler
+                    __builtin_amdgcn_global_load_lds((const void *)(v + (t * H + h) * D + cc),
+                                                     KDA_LDS(slot + P::SV + j * 1024), 16, 0, 0);
+                }
+            }
+        };
+#pragma unroll
+        for (int it = 0; it < NSLOT - 1; ++it) fill(it);
+        for (int it = 0; it < nch; ++it) {
+            wait_vmcnt<(NSLOT - 3) * LOADS>();      // chunks it and it+1 have landed
+            sync();
+            fill(it + NSLOT - 1);
+        }
+        sync();
+        sync();
+        wait_vmcnt<0>();     // no ring write still in flight when the wave ends
+        return;
+    }
+
+    if (idle) {
+        for (int it = 0; it < nch + 2; ++it) sync();
+        return;
+    }
+
+    if (chain) {
+        f32x4 S[8];
+        if (sin) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+        } else {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = zero;
+        }
+        struct ChainIn {
+            f16x8 wn[8], kt[8], tb[2];
+            f32x2 e;              // lane-permuted decay of the whole chunk
+            uint16_t vv[8];       // V[tau(8g+i)][col]
+        };
+        auto chain_read = [&](ChainIn &x, int it) {
+            const char *slot = ring + (it % NSLOT) * SLOT;
+            x.tb[0] = *(const f16x8 *)(slot + RecH::TB + l * 16);
+            x.tb[1] = *(const f16x8 *)(slot + RecH::TB + 1024 + l * 16);
+            const uint16_t *vt = (const uint16_t *)(slot + P::SV);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x.vv[j] = zero_v ? (uint16_t)0 : vt[(4 * gq + j) * P::VCOLS + slice * 16 + c];
+                x.vv[4 + j] = zero_v ? (uint16_t)0 : vt[(C + 4 * gq + j) * P::VCOLS + slice * 16 + c];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x.wn[i] = *(const f16x8 *)(slot + RecH::WN + i * 1024 + l * 16);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) x.kt[b] = *(const f16x8 *)(slot + RecH::KT + b * 1024 + l * 16);
+            x.e = *(const f32x2 *)(slot + RecH::EGP + l * 8);
+        };
+        auto chain_step = [&](const ChainIn &x, int it) {
+            char *snap = snap_of(it);
+            f16x8 sh[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sh[kb] = cat16(to_f16x4(S[2 * kb]), to_f16x4(S[2 * kb + 1]));
+            // V (bf16) as an fp16 B operand; combined here, not where it was read (the
+            // compiler would otherwise wait for the read there)
+            f32x4 va, vb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t a = x.vv[j], b = x.vv[4 + j];
+                asm volatile("" : "+v"(a), "+v"(b));
+                va[j] = __uint_as_float(a << 16);
+                vb[j] = __uint_as_float(b << 16);
+            }
+            const f16x8 vin = cat16(to_f16x4(va), to_f16x4(vb));
+            // U - W S for both row blocks: six independent accumulators
+            f32x4 a0 = mfma16(x.wn[0], sh[0], zero), b0 = mfma16(x.wn[4], sh[0], zero);
+            f32x4 a1 = mfma16(x.wn[1], sh[1], zero), b1 = mfma16(x.wn[5], sh[1], zero);
+            const f32x4 ua = mfma16(x.tb[0], vin, zero), ub = mfma16(x.tb[1], vin, zero);
+            a0 = mfma16(x.wn[2], sh[2], a0);
+            b0 = mfma16(x.wn[6], sh[2], b0);
+            a1 = mfma16(x.wn[3], sh[3], a1);
+            b1 = mfma16(x.wn[7], sh[3], b1);
+            // the decayed state, formed while the products above run
+            f32x4 Sd[8];
+            Sd[0] = decay_block<0>(S[0], x.e);
+            Sd[1] = decay_block<1>(S[1], x.e);
+            Sd[2] = decay_block<2>(S[2], x.e);
+            Sd[3] = decay_block<3>(S[3], x.e);
+            Sd[4] = decay_block<4>(S[4], x.e);
+            Sd[5] = decay_block<5>(S[5], x.e);
+            Sd[6] = decay_block<6>(S[6], x.e);
+            Sd[7] = decay_block<7>(S[7], x.e);
+#pragma unroll
+            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + b * 1024 + l * 16) = S[b];
+            const f16x8 vn = cat16(to_f16x4((a0 + a1) + ua), to_f16x4((b0 + b1) + ub));
+            *(f16x8 *)(snap + 8192 + l * 16) = vn;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) S[b] = mfma16(x.kt[b], vn, Sd[b]);
+        };
+        // after each barrier every LDS access of the wave issued before it is waited for
+        auto sync_chain = [&] {
+            sync();
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+        };
+        ChainIn A, B;
+        sync();
+        chain_read(A, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        for (int it = 0; it < nch; it += 2) {   // unrolled by two: A and B alternate
+            if (it + 1 < nch) chain_read(B, it + 1);
+            chain_step(A, it);
+            if (it + 1 >= nch) break;
+            sync_chain();
+            if (it + 2 < nch) chain_read(A, it + 2);
+            chain_step(B, it + 1);
+            if (it + 2 >= nch) break;
+            sync_chain();
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
+        sync();
+        sync();
+        if (sout) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+        }
+        return;
+    }
+
+    // ---- output wave: chunks m = parity, parity + 2, ...; key blocks 0-1 of chunk m's
+    // output after barrier m+1, the rest and P V_new after barrier m+2. Its Q+ and P
+    // pieces come straight from global memory into registers, four chunks ahead.
+    struct OutIn {
+        bf16x8 qh[8], ql[8];
+        f16x8 pp[2];
+    };
+    auto load = [&](OutIn &x, int m) {
+        const char *rec = rec_of(m);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            x.qh[i] = *(const bf16x8 *)(rec + RecH::QH + i * 1024 + l * 16);
+            x.ql[i] = *(const bf16x8 *)(rec + RecH::QL + i * 1024 + l * 16);
+        }
+        x.pp[0] = *(const f16x8 *)(rec + RecH::PP + l * 16);
+        x.pp[1] = *(const f16x8 *)(rec + RecH::PP + 1024 + l * 16);
+    };
+    // two accumulators per row block, so that no product waits on the one before it
+    f32x4 oa = zero, ob = zero, oc = zero, od = zero;
+    auto half_qs = [&](const OutIn &x, int m, int kb0) {
+        const char *snap = snap_of(m);
+#pragma unroll
+        for (int kb = kb0; kb < kb0 + 2; ++kb) {
+            const f32x4 s0 = *(const f32x4 *)(snap + (2 * kb) * 1024 + l * 16);
+            const f32x4 s1 = *(const f32x4 *)(snap + (2 * kb + 1) * 1024 + l * 16);
+            bf16x4 h0, l0, h1, l1;
+            split4(s0, h0, l0);
+            split4(s1, h1, l1);
+            const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
+            oa = mfma(x.qh[kb], sh, oa);
+            ob = mfma(x.qh[4 + kb], sh, ob);
+            oc = mfma(x.qh[kb], sl, oc);
+            od = mfma(x.qh[4 + kb], sl, od);
+            oa = mfma(x.ql[kb], sh, oa);
+            ob = mfma(x.ql[4 + kb], sh, ob);
+        }
+    };
+    auto first = [&](const OutIn &x, int m) {
+        oa = zero;
+        ob = zero;
+        oc = zero;
+        od = zero;
+        half_qs(x, m, 0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // snapshot reads done before the next barrier
+    };
+    auto finish = [&](const OutIn &x, int m) {
+        const char *snap = snap_of(m);
+        const f16x8 vn = *(const f16x8 *)(snap + 8192 + l * 16);
+        half_qs(x, m, 2);
+        oc = mfma16(x.pp[0], vn, oc);
+        od = mfma16(x.pp[1], vn, od);
+        oa += oc;
+        ob += od;
+        const int64_t t0 = bos + (int64_t)CH * m;
+        const int nc = (int)min<int64_t>(CH, eos - t0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float *da = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : h32_sink + l;
+            float *db = C + 4 * gq + j < nc ? out + ((t0 + C + 4 * gq + j) * H + h) * D + col : h32_sink + l;
+            *da = oa[j];
+            *db = ob[j];
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+    };
+    OutIn X, Y;
+    // loads are issued unconditionally (past the end they repeat the last chunk), so
+    // that the compiler can count them exactly in its waits
+    auto cl = [&](int m) { return m < nch ? m : nch - 1; };
+    load(X, cl(parity));
+    load(Y, cl(parity + 2));
+    int nb = 0;
+    for (; nb < parity + 1; ++nb) sync();
+    for (int m = parity; m < nch; m += 4) {
+        sync(); ++nb;
+        first(X, m);
+        sync(); ++nb;
+        finish(X, m);
+        load(X, cl(m + 4));
+        if (m + 2 >= nch) break;
+        sync(); ++nb;
+        first(Y, m + 2);
+        sync(); ++nb;
+        finish(Y, m + 2);
+        load(Y, cl(m + 6));
+    }
+    for (; nb < nch + 2; ++nb) sync();
+}
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
+                               order, N, T, H, s0, out, sfin, carry, fb, fe);
+}
+
+// One launch: the recurrence over the segment [fb, fe) on blocks [0, RB) and the records
+// of the segment [pb, pe) on the blocks after them (PREP_WAVES chunk-heads per block).
+// The LDS request admits one block per CU, and workgroups are dispatched in index
+// order, so the prep blocks fill the CUs the recurrence leaves idle.
+constexpr int H32_PREP_WAVES = 4;
+
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_kernel(
+    const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    if ((int)blockIdx.x < RB) {
+        recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
+                                   order, N, T, H, s0, out, sfin, carry, fb, fe);
+        return;
+    }
+    const int w = threadIdx.x >> 6;
+    if (w >= H32_PREP_WAVES) return;
+    const int64_t idx = (int64_t)(blockIdx.x - RB) * H32_PREP_WAVES + w;
+    int h;
+    const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
+    if (ci < 0) return;
+    prep_h32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs_out, ci, h,
+                 *(PrepHLds *)(lds + w * (int)sizeof(PrepHLds)));
+}
+
+// Pass 1 of the recurrence over parts: blocks [0, G/2) run every part from a zero state,
+// blocks [G/2, G) from the identity with v taken as 0 (final state: the part's linear map).
+template <int NW, int NSLOT>
+__global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_kernel(
+    const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
+    const int32_t *__restrict__ vco, const int32_t *__restrict__ vorder, int NV, int T, int H,
+    const float *ident, float *out, float *rb, float *ri) {
+    extern __shared__ __attribute__((aligned(16))) char ring[];
+    const int RB = (int)(gridDim.x / 2);
+    const bool id = (int)blockIdx.x >= RB;
+    const int b = id ? (int)blockIdx.x - RB : (int)blockIdx.x;
+    recur_h32_block<NW, NSLOT>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
+                               id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, id);
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+                           const int32_t *cu, int N, int T, int H, float scale, const int32_t *chunk_off,
+                           char *recs, int fb, int fe, int64_t M, hipStream_t st) {
+    const int64_t blocks = seg_chunks_bound(M, N, fb, fe) * H;
+    if (blocks <= 0 || fe <= fb) return hipSuccess;
+    hipLaunchKernelGGL(prep_h32_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N, T, H, scale,
+                       chunk_off, recs, fb, fe);
+    return hipGetLastError();
+}
+
+template <int NW>
+static hipError_t launch_recur_h32_t(const char *recs, const uint16_t *v, const int32_t *cu,
+                                     const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
+                                     const float *s0, float *out, float *sfin, float *carry, int fb, int fe,
+                                     hipStream_t st) {
+    constexpr int NS = pairh_nslot<NW>();
+    constexpr int lds = PairHLds<NW, NS>::BYTES;
+    auto kern = recur_h32_kernel<NW, NS>;
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
+    const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st, recs, v, cu,
+                       chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_h32_range(const char *recs, const uint16_t *v, const int32_t *cu, const int32_t *chunk_off,
+                                  const int32_t *order, int N, int T, int H, const float *s0, float *out, float *sfin,
+                                  float *carry, int waves, int fb, int fe, hipStream_t st) {
+    switch (waves) {
+    case 401: return launch_recur_h32_t<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 402: return launch_recur_h32_t<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int NW>
+static hipError_t launch_recur_h32_prep_t(const RecurPrepArgs &a, hipStream_t st) {
+    constexpr int NS = pairh_nslot<NW>();
+    constexpr int pair = PairHLds<NW, NS>::BYTES;
+    constexpr int prep = H32_PREP_WAVES * (int)sizeof(PrepHLds);
+    constexpr int lds = pair > prep ? pair : prep;
+    static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
+    auto kern = recur_h32_prep_kernel<NW, NS>;
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
+    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
+    const int64_t pblocks =
+        a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + H32_PREP_WAVES - 1) / H32_PREP_WAVES : 0;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
+                       a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry, a.fb, a.fe, (int)rb,
+                       a.q, a.k, a.g, a.beta, a.scale, a.recs, a.pb, a.pe);
+    return hipGetLastError();
+}
+
+hipError_t launch_recur_h32_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
+    switch (waves) {
+    case 401: return launch_recur_h32_prep_t<1>(a, st);
+    case 402: return launch_recur_h32_prep_t<2>(a, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// pass 1 of the recurrence over parts on 32-token records (two-slice blocks, 2 x 4 NV H)
+hipError_t launch_h32_parts_pass1(const char *recs, const uint16_t *v, const int32_t *vcu, const int32_t *vco,
+                                  const int32_t *vorder, int NV, int T, int H, const float *ident, float *out,
+                                  float *rb, float *ri, hipStream_t st) {
+    constexpr int NW = 2, NS = pairh_nslot<2>();
+    constexpr int lds = PairHLds<NW, NS>::BYTES;
+    auto kern = recur_h32_parts_kernel<NW, NS>;
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
+    const int64_t rbk = (int64_t)NV * H * (D / (16 * NW));
+    hipLaunchKernelGGL(kern, dim3((unsigned)(2 * rbk)), dim3(64 * PairLayout<NW>::WAVES), lds, st, recs, v, vcu, vco,
+                       vorder, NV, T, H, ident, out, rb, ri);
+    return hipGetLastError();
+}
+
+}  // namespace kda

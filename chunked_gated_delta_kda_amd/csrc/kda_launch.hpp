@@ -29,6 +29,7 @@ int32_t *device_error_word();
 
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
 constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
+constexpr int RECH_BYTES = 37888;  // bytes of one 32-token chunk record of forms 401/402 (RecH::BYTES)
 
 // Segments of the split path. A launch over the segment [fb, fe) covers, of every
 // sequence with c chunks, its local chunks [seg_chunk(c, fb), seg_chunk(c, fe)): fb <= fe
@@ -90,6 +91,20 @@ hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32
                                 int waves, int fb, int fe, hipStream_t st);
 hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 
+// 32-token chunks with fp16 recurrence operands (kda_h32.hip): records of the segment
+// [fb, fe); recurrence forms 401 (one 16-column slice per block) and 402 (two), alone or
+// with the prep of [pb, pe); pass 1 of the recurrence over parts.
+hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+                           const int32_t *cu, int N, int T, int H, float scale, const int32_t *chunk_off,
+                           char *recs, int fb, int fe, int64_t M, hipStream_t st);
+hipError_t launch_recur_h32_range(const char *recs, const uint16_t *v, const int32_t *cu, const int32_t *chunk_off,
+                                  const int32_t *order, int N, int T, int H, const float *s0, float *out, float *sfin,
+                                  float *carry, int waves, int fb, int fe, hipStream_t st);
+hipError_t launch_recur_h32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
+hipError_t launch_h32_parts_pass1(const char *recs, const uint16_t *v, const int32_t *vcu, const int32_t *vco,
+                                  const int32_t *vorder, int NV, int T, int H, const float *ident, float *out,
+                                  float *rb, float *ri, hipStream_t st);
+
 hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
                         const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                         const float *s0, float *out, float *sfin, int waves, hipStream_t st);
@@ -111,9 +126,10 @@ hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int waves, hipStream_t st);
 
 // The recurrence over P parts of every sequence (few long chains); the buffers hold N P H
-// states each (ident, rb, ri, sin) and N P + 1 (vcu, vco) or N P (vorder) entries.
+// states each (ident, rb, ri, sin) and N P + 1 (vcu, vco) or N P (vorder) entries. h32:
+// over 32-token fp16 records (forms 401/402), else 16-token records.
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, hipStream_t st);
+                        float *ri, float *sin, bool h32, hipStream_t st);
 }  // namespace kda

@@ -1382,7 +1382,7 @@ hipError_t launch_recur(const char *recs, const uint16_t *v, const int32_t *cu,
 // virtual batch: part p of sequence n (at position n of `order`) is virtual sequence n P + p,
 // covering its chunks [seg(c, p/P), seg(c, (p+1)/P)); also fills the identity entry states
 __global__ __launch_bounds__(256) void parts_setup_kernel(const int32_t *cu_safe, const int32_t *chunk_off,
-                                                          const int32_t *order, int N, int P, int32_t *vcu,
+                                                          const int32_t *order, int N, int P, int cl, int32_t *vcu,
                                                           int32_t *vco, int32_t *vorder, float *ident,
                                                           int64_t nstates) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1392,7 +1392,7 @@ __global__ __launch_bounds__(256) void parts_setup_kernel(const int32_t *cu_safe
         const int c0 = chunk_off[n], c = chunk_off[n + 1] - c0;
         const int k = seg_chunk(c, (int)(((int64_t)p * SEG_ONE) / P));
         vco[v] = c0 + k;
-        vcu[v] = min(cu_safe[n + 1], cu_safe[n] + C * k);
+        vcu[v] = min(cu_safe[n + 1], cu_safe[n] + cl * k);
         vorder[v] = order[n] * P + p;
         if (v == (int64_t)N * P - 1) {
             vco[v + 1] = chunk_off[N];
@@ -1461,13 +1461,16 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, hipStream_t st) {
+                        float *ri, float *sin, bool h32, hipStream_t st) {
     const int NV = N * P;
     const int64_t ns = (int64_t)NV * H;
-    hipLaunchKernelGGL(parts_setup_kernel, dim3(512), dim3(256), 0, st, cu_safe, chunk_off, order, N, P, vcu, vco,
-                       vorder, ident, ns);
+    hipLaunchKernelGGL(parts_setup_kernel, dim3(512), dim3(256), 0, st, cu_safe, chunk_off, order, N, P,
+                       h32 ? 32 : C, vcu, vco, vorder, ident, ns);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    {
+    if (h32) {
+        if (launch_h32_parts_pass1(recs, v, vcu, vco, vorder, NV, T, H, ident, out, rb, ri, st) != hipSuccess)
+            return hipErrorLaunchFailure;
+    } else {
         constexpr int NW = 2, NS = pair_nslot<2>();
         constexpr int lds = PairLds<NW, NS>::BYTES;
         auto kern = recur_parts_kernel<NW, NS>;
@@ -1481,6 +1484,8 @@ hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_s
     hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), 0, st, s0, (const float *)rb,
                        (const float *)ri, N, P, H, sin, sfin);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 401, 0,
+                                           SEG_ONE, st);
     return launch_recur_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 101, 0, SEG_ONE, st);
 }
 

@@ -105,7 +105,7 @@ def test_decode_ex_validation_errors(lib):
 def test_workspace_bytes(lib):
     assert lib.kda_workspace_bytes(0, 16, 1, 1) == 0
     b = lib.kda_workspace_bytes(1, 8192, 32, 1)
-    assert b >= (8192 // 16) * 32 * 23552
+    assert b >= (8192 // 32) * 32 * 37888     # one 32-token record per chunk-head
     assert lib.kda_select_variant(1, 8192, 32) in (1, 2, 3)
     assert lib.kda_workspace_bytes(1, 8192, 32, 3) == 0    # the recurrent variant needs none
 
@@ -148,7 +148,7 @@ def test_launch_plan():
     assert [p[0] for p in nat.launch_plan(1, 8192, 8, "split")] == ["chunk_map", "prep", "parts"]
     assert [p[0] for p in nat.launch_plan(1, 2048, 8, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(1, 32768, 16, "split")][-1] != "parts"   # two parts do not pay
-    # the per-chain hybrid (from 192 chains) runs whole by default
+    # many chains (the two-slice 32-token form, or the per-chain hybrid) run whole by default
     assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []

@@ -18,7 +18,7 @@ from kda_check import compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-FORMS = [8, 9, 101, 102, 301]
+FORMS = [8, 9, 101, 102, 301, 401, 402]
 SEGMENTS = [1, 2, 3, 8]
 LENGTHS = [70, 0, 300, 16, 1, 129]
 
@@ -53,31 +53,36 @@ def test_form_and_segments(workload, form, segments, monkeypatch):
     assert ok
 
 
+@pytest.mark.parametrize("form", [101, 401])
 @pytest.mark.parametrize("parts", [2, 3, 5, 16])
-def test_parts(workload, parts, monkeypatch):
+def test_parts(workload, parts, form, monkeypatch):
     """The recurrence over parts of every sequence (pass 1 from zero and identity entry
-    states, composition, pass 2), forced on the varlen batch: some parts of the short
-    sequences hold no chunks, and the empty sequence passes its initial state through."""
+    states, composition, pass 2), forced on the varlen batch, over 16-token records (101)
+    and 32-token fp16 records (401): some parts of the short sequences hold no chunks, and
+    the empty sequence passes its initial state through."""
     monkeypatch.setenv("KDA_PARTS", str(parts))
+    monkeypatch.setenv("KDA_RECUR_WAVES", str(form))
     w, (ro, rf) = workload
-    _say(f"[forms] parts={parts} lengths={LENGTHS}")
+    _say(f"[forms] parts={parts} form={form} lengths={LENGTHS}")
     o, f = run_gpu(w, "split")
     ok, mo, mf = compare(w, o, f, ro, rf)
     _say(f"  o {mo}\n  S {mf}")
     assert ok
 
 
+@pytest.mark.parametrize("fp16", [False, True])
 @pytest.mark.parametrize("segments,parts", [(1, 1), (4, 1), (1, 3)])
-def test_no_final_state_and_in_place(workload, segments, parts, monkeypatch):
+def test_no_final_state_and_in_place(workload, segments, parts, fp16, monkeypatch):
     import torch
     import chunked_gated_delta_kda_amd as kda
 
-    monkeypatch.setenv("KDA_RECUR_WAVES", "102" if parts == 1 else "101")
+    form = (102 if parts == 1 else 101) + (300 if fp16 else 0)
+    monkeypatch.setenv("KDA_RECUR_WAVES", str(form))
     monkeypatch.setenv("KDA_SEGMENTS", str(segments))
     monkeypatch.setenv("KDA_PARTS", str(parts))
     w, (ro, rf) = workload
     d = synth.to_device(w)
-    _say(f"[forms] no final state, segments={segments}")
+    _say(f"[forms] no final state, form={form} segments={segments} parts={parts}")
     o, fin = kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["cu_seqlens"],
                      d["initial_state"], output_final_state=False, variant="split")
     torch.cuda.synchronize()

@@ -145,12 +145,18 @@ def test_linearity_config3(variant):
     two["v"] = (d["v"].float() * 2).to(torch.bfloat16)      # exact: a power of two
     two["initial_state"] = d["initial_state"] * 2
     o2, f2 = _fwd(two, variant)
+    # Doubling is exact in every rounding the kernels do, except for fp16 operands of the
+    # 32-token path below 2^-14 (fp16's subnormal range, where the rounding grid is an
+    # absolute 2^-24 rather than relative): there fp16(2x) and 2 fp16(x) may differ by one
+    # grid step. So: all but a small share of the values exactly doubled, the rest within
+    # a bound far below the parity gate.
     for got, ref in ((o2, o * 2), (f2, f * 2)):
         rms = float(ref.double().pow(2).mean().sqrt())
         err = float((got - ref).abs().max())
         exact = float((got != ref).double().mean())
         _say(f"  max err {err:.3e} (RMS {rms:.3e}), share of inexact values {exact:.2e}")
-        assert err <= 1e-6 * rms
+        assert exact <= 1e-3
+        assert err <= 1e-4 * rms
 
 
 def test_affine_composition_config4():
