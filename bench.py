@@ -48,10 +48,15 @@ HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 FLOP_PER_TOKEN_HEAD = 121856      # chunked method at C=16: 6 d^2 + 2C(3d + 2d) + 12 C^2, d = 128
 STATE_BYTES = 128 * 128 * 4       # one (sequence, head) state, fp32
-# algorithmic bytes per token-head that each kernel must move (inputs it reads,
-# outputs it writes); together they are q,k,v bf16 + g fp32 + beta fp32 + o fp32 = 1796 B
-KERNEL_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512, "fused": 1796,
-                               "recurrent": 1796}
+# Algorithmic bytes of the path per token-head (the unit): q, k, v bf16 (3 x 256) + g fp32
+# (512) + beta fp32 (4) + o fp32 (512) = 1796 B; with bf16 g, 1540 B. Plus 64 KiB per
+# (sequence, head) for each state read or written (32 KiB in bf16). A launch is credited
+# with the unit's bytes for every token-head it processes (the roofline's "achieved");
+# the bytes its own inputs and outputs amount to are reported beside ("own_bytes").
+BYTES_PER_TOKEN_HEAD = 1796
+KERNEL_OWN_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512}
+GATED_CONFIG = 3                  # the T=8192 varlen prefill the target sentence names
+GATED_BAR_US = 52.5               # 60% of the HBM roofline for its 252.2 MB
 DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128)"
 EVENT_EVERY = 4                   # timed steps per step that records kernel events
 COLD_STEPS = 20                   # extra steps timed after a cache-evicting device write each
@@ -105,7 +110,7 @@ class HipEvents:
 _COMMON_SOURCES = ("kda_api.cpp", "kda_launch.hpp")
 KIND_SOURCES = {"recurrent": _COMMON_SOURCES + ("kda_recurrent.hip",),
                 "fused": _COMMON_SOURCES + ("kda_device.hpp", "kda_fused.hip")}
-_CHUNKED_SOURCES = _COMMON_SOURCES + ("kda_device.hpp", "kda_split.hip")
+_CHUNKED_SOURCES = _COMMON_SOURCES + ("kda_device.hpp", "kda_split.hip", "kda_h32.hip")
 
 
 def _code_only(text):
@@ -188,8 +193,10 @@ def ingest_pmc(fetch_csv, write_csv, workload, command):
             continue
         base = m.group(1)      # e.g. prep, recur_pair, recur_prep, fused, chunk_map
         kind = ("recurrent" if base in ("recurrent", "decode") else
+                "parts" if base.startswith("parts") or base.endswith("_parts") else
                 "recur_prep" if base.startswith("recur") and base.endswith("_prep") else
-                "recur" if base.startswith("recur") else base)
+                "recur" if base.startswith("recur") else
+                "prep" if base.startswith("prep") else base)
         kinds[kind][0].extend(fetch[name])
         kinds[kind][1].extend(write[name])
     for kind, (fl, wl) in kinds.items():
@@ -222,7 +229,28 @@ def cpu_baseline(w, threads, gpu_o, gpu_f):
     dt = time.perf_counter() - t0
     par_o = synth.parity(gpu_o, ro)
     par_f = synth.parity(gpu_f, rf)
-    return dt, par_o, par_f
+    return dt, par_o, par_f, rf
+
+
+def cpu_one_thread(w, chains):
+    """The oracle on one thread over the first ``chains`` (sequence, head) chains: seconds."""
+    import oracle
+    inp = synth.oracle_inputs(w)
+    pairs = [(n, h) for n in range(w.N) for h in range(w.H)][:chains]
+    t0 = time.perf_counter()
+    oracle.kda_forward(**inp, pairs=pairs, threads=1)
+    return time.perf_counter() - t0, pairs
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def copy_calibration(args, dev):
@@ -333,7 +361,12 @@ def main():
                     help="benchmark the decode step over N sequences instead of a prefill config")
     ap.add_argument("--heads", type=int, default=32, help="heads of the --decode workload")
     ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
-                    help="state element type in HBM for --decode (bf16: the BF16-state form)")
+                    help="state element type in HBM (bf16: the BF16-state form; prefill initial/final "
+                         "state or the --decode state)")
+    ap.add_argument("--g-dtype", default="f32", choices=["f32", "bf16"],
+                    help="element type of g for the prefill (bf16: the input-byte diet form)")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="do not also time the T=8192 varlen workload (config 3) after the headline one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -346,7 +379,8 @@ def main():
 
     if args.ingest_pmc:
         workload = (f"decode{args.decode}x{args.heads}" + ("bf16" if args.state_dtype == "bf16" else "")
-                    if args.decode else f"config{args.config}")
+                    if args.decode else f"config{args.config}" + ("_bf16g" if args.g_dtype == "bf16" else "")
+                    + ("_bf16state" if args.state_dtype == "bf16" else ""))
         ingest_pmc(*args.ingest_pmc, workload, args.pmc_command)
         return
 
@@ -356,7 +390,6 @@ def main():
         sys.exit(2)
 
     import torch
-    import chunked_gated_delta_kda_amd as kda
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -365,20 +398,46 @@ def main():
     if args.decode:
         bench_decode(args, dev)
         return
-    log(f"[bench] generating config {args.config}: {synth.CONFIGS[args.config]['name']}")
-    w = synth.config_workload(args.config)
+    res = run_prefill(args.config, args, dev, cpu=not args.no_cpu_baseline)
+    if args.config != GATED_CONFIG and not args.no_gated:
+        g = run_prefill(GATED_CONFIG, args, dev, cpu=False)
+        res["gated_config"] = {k: g[k] for k in ("config", "value", "unit", "ms_per_step", "cold", "kernel_ms",
+                                                 "roofline", "path_hbm_frac")}
+        res["gated_config"]["bar_ms"] = GATED_BAR_US / 1e3
+    print(json.dumps(res), flush=True)
+
+
+def run_prefill(cfg, args, dev, cpu):
+    """Time one prefill workload (kda_fwd over the whole batch per step); returns the result dict."""
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+    from chunked_gated_delta_kda_amd import native
+
+    log(f"[bench] generating config {cfg}: {synth.CONFIGS[cfg]['name']}")
+    w = synth.config_workload(cfg)
+    g_bf16, s_bf16 = args.g_dtype == "bf16", args.state_dtype == "bf16"
+    if g_bf16:       # the input-byte diet forms run on the bf16-rounded values
+        w.g = synth.bf16_to_f32(synth.bf16_bits(w.g))
+    if s_bf16 and w.initial_state is not None:
+        w.initial_state = synth.bf16_to_f32(synth.bf16_bits(w.initial_state))
     d = synth.to_device(w, dev)
+    sdt = torch.bfloat16 if s_bf16 else torch.float32
+    if g_bf16:
+        d["g"] = d["g"].to(torch.bfloat16)
+    if s_bf16 and d["initial_state"] is not None:
+        d["initial_state"] = d["initial_state"].to(torch.bfloat16)
     N, T, H = w.N, w.T, w.H
     variant = args.variant if args.variant != "auto" else kda.select_variant(N, T, H)
     out = torch.empty((T, H, 128), dtype=torch.float32, device=dev)
-    fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+    fin = torch.empty((N, H, 128, 128), dtype=sdt, device=dev)
     nws = kda.workspace_bytes(N, T, H, variant)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
 
-    from chunked_gated_delta_kda_amd import native
     launch_info = native.launch_plan(N, T, H, variant)
     plan = [p[0] for p in launch_info]
     chunk_len = launch_info[0][3]
+    if (g_bf16 or s_bf16) and variant == "split" and chunk_len != 32:
+        log("[bench] note: bf16 inputs run the 32-token forms; the launch plan shown is the fp32 one")
     names = list(dict.fromkeys(plan))            # kinds, first-launch order
     ev = HipEvents()
     n_ev = len(plan) + 1
@@ -387,7 +446,7 @@ def main():
     def step(events=None):
         kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], d["cu_seqlens"],
                 d["initial_state"], variant=variant, out=out, final_state=fin, workspace=ws,
-                stage_events=events)
+                stage_events=events, state_dtype=sdt)
 
     log(f"[bench] variant={variant} warmup={args.warmup} steps={args.steps}")
     for _ in range(args.warmup):
@@ -423,8 +482,10 @@ def main():
         f"launches {launches}")
 
     TH = T * H
-    states = N * H * STATE_BYTES * ((1 if w.initial_state is not None else 0) + 1)
-    alg_bytes_total = TH * 1796 + states
+    unit = BYTES_PER_TOKEN_HEAD - (256 if g_bf16 else 0)
+    state_b = STATE_BYTES // (2 if s_bf16 else 1)
+    states = N * H * state_b * ((1 if w.initial_state is not None else 0) + 1)
+    alg_bytes_total = TH * unit + states
     alg_flops = TH * FLOP_PER_TOKEN_HEAD
     step_s = ms_per_step / 1e3
     tokens_per_s = T / step_s
@@ -443,68 +504,90 @@ def main():
             t += int(cs[b] - cs[a]) if b > a else 0
         return t
 
-    def launch_alg_bytes(kind, prep_r, recur_r):
-        """Bytes the algorithm must move in one launch: inputs read and outputs written
-        for the token-heads it prepares and runs; the batch's initial and final states
-        are counted once per step, with the last recurrence launch."""
+    def launch_bytes(kind, prep_r, recur_r):
+        """(algorithmic bytes credited to one launch, bytes of its own inputs and outputs):
+        the unit's bytes for every token-head the launch processes; the batch's states
+        with the last recurrence launch (or the one-launch kinds)."""
         if kind == "chunk_map":
-            return 4 * (N + 1) + 8 * N
-        if kind in ("fused", "recurrent"):
-            return TH * KERNEL_BYTES_PER_TOKEN_HEAD[kind] + states
-        b = (tokens_in(prep_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["prep"]
-             + tokens_in(recur_r) * H * KERNEL_BYTES_PER_TOKEN_HEAD["recur"])
+            b = 4 * (N + 1) + 8 * N
+            return b, b
+        if kind in ("fused", "recurrent", "parts"):
+            own = TH * (KERNEL_OWN_BYTES_PER_TOKEN_HEAD["recur"] if kind == "parts" else unit) + states
+            return TH * unit + states, own
+        tp, tr = tokens_in(prep_r) * H, tokens_in(recur_r) * H
+        own = (tp * (KERNEL_OWN_BYTES_PER_TOKEN_HEAD["prep"] - (256 if g_bf16 else 0))
+               + tr * KERNEL_OWN_BYTES_PER_TOKEN_HEAD["recur"])
+        alg = max(tp, tr) * unit
         if recur_r[1] == seg_one and recur_r[1] > recur_r[0]:
-            b += states
-        return b
+            alg += states
+            own += states
+        return alg, own
 
     kind_bytes = {nm: 0 for nm in names}
+    own_bytes = {nm: 0 for nm in names}
     for kind, pr, rr, _ in launch_info:
-        kind_bytes[kind] += launch_alg_bytes(kind, pr, rr)
+        a_b, o_b = launch_bytes(kind, pr, rr)
+        kind_bytes[kind] += a_b
+        own_bytes[kind] += o_b
 
     dom = max((nm for nm in names if nm != "chunk_map"), key=lambda nm: kern_ms[nm])
     dom_s = kern_ms[dom] / 1e3
     achieved = kind_bytes[dom] / dom_s / 1e9
-    workload = f"config{args.config}"
+    workload = f"config{cfg}" + ("_bf16g" if g_bf16 else "") + ("_bf16state" if s_bf16 else "")
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": measured_traffic(dom, workload),
                 "alg_bytes_per_launch": int(kind_bytes[dom] / launches[dom]),
+                "own_bytes_per_launch": int(own_bytes[dom] / launches[dom]),
                 "launches_per_step": launches[dom],
                 "avg_launch_ms": round(kern_ms[dom] / launches[dom], 5)}
 
     res = {"metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta)",
-           "config": {"workload": f"{synth.CONFIGS[args.config]['name']} (config {args.config})",
+           "data": "synthetic (seeded; bf16 q/k/v, " + ("bf16" if g_bf16 else "fp32") + " g, fp32 beta)",
+           "config": {"workload": f"{synth.CONFIGS[cfg]['name']} (config {cfg})",
                       "num_seqs": N, "total_tokens": T, "num_heads": H, "dk": 128, "dv": 128,
-                      "chunk": chunk_len, "variant": variant, "initial_state": w.initial_state is not None},
+                      "chunk": chunk_len, "variant": variant, "initial_state": w.initial_state is not None,
+                      "g_dtype": args.g_dtype, "state_dtype": args.state_dtype},
            "tflops": round(alg_flops / step_s / 1e12, 2),
            "mfma_bf16_peak_frac": round(alg_flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
            "path_hbm_frac": round(alg_bytes_total / step_s / 1e9 / HBM_PEAK_GBS, 4),
            "kernel_ms": {k: round(v, 5) for k, v in kern_ms.items()},
-           "cold": {"ms_per_step_median": round(float(np.median(cold)), 5), "steps": COLD_STEPS,
+           "cold": {"ms_per_step_median": round(float(np.median(cold)), 5),
+                    "tokens_per_s": round(T / (float(np.median(cold)) / 1e3), 1), "steps": COLD_STEPS,
                     "flush_bytes_before_each": COLD_FLUSH_BYTES},
            "kernel_launches": launches,
            "roofline": roofline, "cpu_baseline": None}
 
-    if not args.no_cpu_baseline:
+    if cpu:
         try:
-            cores = len(os.sched_getaffinity(0))
+            host = len(os.sched_getaffinity(0))
         except AttributeError:  # pragma: no cover
-            cores = os.cpu_count() or 1
-        threads = args.cpu_threads or min(16, cores)
+            host = os.cpu_count() or 1
+        # the box's CPU share for one GPU is 16 threads, whatever the host shows
+        threads = args.cpu_threads or min(16, host)
         log(f"[bench] oracle on the host: {N * H} chains, {threads} threads")
-        o_np, f_np = out.cpu().numpy(), fin.cpu().numpy()
-        dt, po, pf = cpu_baseline(w, threads, o_np, f_np)
+        o_np = out.cpu().numpy()
+        f_np = fin.float().cpu().numpy()
+        dt, po, pf, rf = cpu_baseline(w, threads, o_np, f_np)
+        one = min(4, N * H)
+        dt1, pairs1 = cpu_one_thread(w, one)
+        th1 = int(sum(w.lengths[n] for n, _ in pairs1))
         res["cpu_baseline"] = {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads,
                                "kind": "oracle",
                                "sample": f"the whole workload ({N * H} (sequence, head) chains, "
-                                         f"{TH} token-heads), fp64 token loop, {dt:.2f} s wall"}
+                                         f"{TH} token-heads), fp64 token loop, {dt:.2f} s wall",
+                               "cpu_model": cpu_model(), "host_cpus": host,
+                               "one_thread": {"token_heads_per_s": round(th1 / dt1, 1),
+                                              "sample": f"{one} chains ({th1} token-heads), {dt1:.2f} s"}}
+        if s_bf16:   # a bf16 final state: the bf16-result gate
+            pf = synth.parity_bf16(f_np, rf, synth.GATE_MAX_ABS_RMS)
+        ok_f = synth.passes_bf16(pf) if s_bf16 else synth.passes(pf)
         res["parity"] = {"o": {k: po[k] for k in ("rel_l2", "max_abs_rms")},
                          "final_state": {k: pf[k] for k in ("rel_l2", "max_abs_rms")},
-                         "pass": synth.passes(po) and synth.passes(pf)}
-    print(json.dumps(res), flush=True)
+                         "pass": synth.passes(po) and ok_f}
+    return res
 
 
 if __name__ == "__main__":

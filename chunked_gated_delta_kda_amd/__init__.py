@@ -50,9 +50,12 @@ def _expect(name, t, dtype, shape, dev):
                          f"{'' if t.is_contiguous() else ' (not contiguous)'}")
 
 
-def check_fwd_args(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None, final_state=None):
+def check_fwd_args(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=None, final_state=None,
+                   state_dtype=None):
     """Every check fwd makes on its tensors before anything is launched (dtype, shape,
-    contiguity, one device); returns (T, H, N)."""
+    contiguity, one device); returns (T, H, N, state dtype). g may be fp32 or bf16 (the
+    input-byte diet form); initial and final state share one dtype, fp32 or bf16 (by
+    default that of initial_state, else of final_state, else fp32)."""
     import torch
 
     dev = q.device
@@ -61,10 +64,16 @@ def check_fwd_args(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=No
     T, H, Dk = q.shape
     if Dk != HEAD_DIM:
         raise ValueError("head_dim must be 128")
+    gdt = g.dtype if g.dtype in (torch.float32, torch.bfloat16) else torch.float32
     for name, t, dt, shape in (("q", q, torch.bfloat16, (T, H, Dk)), ("k", k, torch.bfloat16, (T, H, Dk)),
-                               ("v", v, torch.bfloat16, (T, H, Dk)), ("g", g, torch.float32, (T, H, Dk)),
+                               ("v", v, torch.bfloat16, (T, H, Dk)), ("g", g, gdt, (T, H, Dk)),
                                ("beta", beta, torch.float32, (T, H))):
         _expect(name, t, dt, shape, dev)
+    if state_dtype is None:
+        state_dtype = (initial_state.dtype if initial_state is not None else
+                       final_state.dtype if final_state is not None else torch.float32)
+    if state_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"states: dtype {state_dtype}; initial_state and final_state must be fp32 or bf16")
     if cu_seqlens is not None:
         if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1 \
                 or not cu_seqlens.is_contiguous() or cu_seqlens.shape[0] < 2:
@@ -73,23 +82,26 @@ def check_fwd_args(q, k, v, g, beta, cu_seqlens=None, initial_state=None, out=No
     else:
         N = 1
     if initial_state is not None:
-        _expect("initial_state", initial_state, torch.float32, (N, H, Dk, Dk), dev)
+        _expect("initial_state", initial_state, state_dtype, (N, H, Dk, Dk), dev)
     if out is not None:
         _expect("out", out, torch.float32, (T, H, Dk), dev)
     if final_state is not None:
-        _expect("final_state", final_state, torch.float32, (N, H, Dk, Dk), dev)
-    return T, H, N
+        _expect("final_state", final_state, state_dtype, (N, H, Dk, Dk), dev)
+    return T, H, N, state_dtype
 
 
 def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         output_final_state=True, *, variant="auto", out=None, final_state=None,
-        workspace=None, stream=None, stage_events=None, check=False):
+        workspace=None, stream=None, stage_events=None, check=False, state_dtype=None):
     """KDA forward on the current HIP device.
 
-    q, k, v: bf16 [T, H, 128]; g: fp32 [T, H, 128] (log-decay, clamped at -5);
+    q, k, v: bf16 [T, H, 128]; g: fp32 or bf16 [T, H, 128] (log-decay, clamped at -5);
     beta: fp32 [T, H]; cu_seqlens: int32 [N+1] on the device or None (one sequence);
-    initial_state: fp32 [N, H, 128, 128] or None; out / final_state: caller buffers of the
-    result shapes (fp32, contiguous, on the device) or None.
+    initial_state: [N, H, 128, 128] fp32 or bf16, or None; out: fp32 [T, H, 128] caller
+    buffer or None; final_state: caller buffer of the state dtype or None. state_dtype
+    (torch.float32 or torch.bfloat16): the states' dtype, by default that of the given
+    states, else fp32. bf16 g or states run the split variant's 32-token forms or the
+    token loop (the fused variant rejects them).
     check: clear the device error word before the call and read it after (both
     synchronise the stream); raise native.KdaDeviceError if the kernels raised a bit
     (malformed cu_seqlens, a fused hand-off timeout).
@@ -101,7 +113,7 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("kda.fwd needs device tensors")
-    T, H, N = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    T, H, N, sdt = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state, state_dtype)
     Dk = HEAD_DIM
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
@@ -110,14 +122,17 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
     if not output_final_state:
         final_state = None
     elif final_state is None:
-        final_state = torch.empty((N, H, Dk, Dk), dtype=torch.float32, device=dev)
+        final_state = torch.empty((N, H, Dk, Dk), dtype=sdt, device=dev)
+    dtypes = {torch.float32: native.DTYPES["f32"], torch.bfloat16: native.DTYPES["bf16"]}
     var = native.VARIANTS[variant]
     if workspace is None:
         nbytes = lib.kda_workspace_bytes(N, T, H, var)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    opt = native.KdaOptions(var, 0, ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
-                            workspace.numel() if workspace is not None else 0, None, 0)
+    opt = native.KdaOptions(variant=var, n_stage_events=0,
+                            workspace=ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
+                            workspace_bytes=workspace.numel() if workspace is not None else 0,
+                            g_dtype=dtypes[g.dtype], state_dtype=dtypes[sdt])
     if stage_events is not None:   # profiling: a ctypes array of hipEvent_t handles
         opt.n_stage_events = len(stage_events)
         opt.stage_events = ctypes.cast(stage_events, ctypes.POINTER(ctypes.c_void_p))
@@ -174,7 +189,9 @@ def fwd_noalloc(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=Non
     lib = native.load_library()
     if q.device.type != "cuda":
         raise ValueError("kda.fwd_noalloc needs device tensors")
-    T, H, N = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    T, H, N, sdt = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, out, final_state)
+    if g.dtype != torch.float32 or sdt != torch.float32:
+        raise ValueError("fwd_noalloc: fp32 g and states only (it runs the fused variant)")
     if scale is None:
         scale = 1.0 / math.sqrt(HEAD_DIM)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)

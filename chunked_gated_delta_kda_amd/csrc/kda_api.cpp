@@ -355,6 +355,11 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     if (n_ev != 0 && (n_ev < 2 || n_ev > KDA_MAX_STAGE_EVENTS || !opt->stage_events))
         return KDA_ERR_UNSUPPORTED;
     if (opt && opt->reserved != 0) return KDA_ERR_UNSUPPORTED;
+    const int g_dtype = opt ? opt->g_dtype : KDA_DTYPE_F32;
+    const int s_dtype = opt ? opt->state_dtype : KDA_DTYPE_F32;
+    if ((g_dtype != KDA_DTYPE_F32 && g_dtype != KDA_DTYPE_BF16) || (s_dtype != KDA_DTYPE_F32 && s_dtype != KDA_DTYPE_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    const bool g_bf16 = g_dtype == KDA_DTYPE_BF16, s_bf16 = s_dtype == KDA_DTYPE_BF16;
     const int variant = opt ? opt->variant : KDA_VARIANT_AUTO;
     if (variant != KDA_VARIANT_AUTO && variant != KDA_VARIANT_SPLIT && variant != KDA_VARIANT_FUSED &&
         variant != KDA_VARIANT_RECURRENT)
@@ -365,7 +370,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     if (!cu_seqlens && num_seqs != 1) return KDA_ERR_SHAPE;
     if (!out && total_tokens > 0) return KDA_ERR_NULL;
     if (total_tokens > 0 && (!q || !k || !v || !g || !beta)) return KDA_ERR_NULL;
-    const size_t state_bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    const size_t state_bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * (s_bf16 ? 2 : 4);
     if (initial_state && final_state && (const void *)initial_state != (const void *)final_state &&
         overlaps(initial_state, state_bytes, final_state, state_bytes))
         return KDA_ERR_ALIAS;
@@ -373,9 +378,14 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int chosen = variant == KDA_VARIANT_AUTO
                            ? kda_select_variant(num_seqs, total_tokens, num_heads)
                            : variant;
+    // bf16 g or bf16 states: the 32-token forms and the token loop read them; the fused
+    // variant does not
+    if ((g_bf16 || s_bf16) && chosen == KDA_VARIANT_FUSED) return KDA_ERR_UNSUPPORTED;
     hipStream_t st = (hipStream_t)stream;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    const int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, T, H) : fused_waves(N, H);
+    int waves = chosen == KDA_VARIANT_SPLIT ? recur_waves(N, T, H) : fused_waves(N, H);
+    if (chosen == KDA_VARIANT_SPLIT && (g_bf16 || s_bf16) && !fp16_form(waves))
+        waves = (int64_t)N * H <= 32 ? 401 : 402;
     const int segs = chosen == KDA_VARIANT_SPLIT ? split_segments(N, T, H, waves) : 1;
     const int parts = chosen == KDA_VARIANT_SPLIT ? split_parts(N, T, H, waves) : 1;
     const Layout lay = ws_layout(N, T, H, chosen, segs, waves, parts);
@@ -399,8 +409,8 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     if (chosen == KDA_VARIANT_RECURRENT) {
         const int dvt = kda::recurrent_tile((int64_t)N * H, T, N, false);
         const bool ok = around(st, [&] {
-            return kda::launch_recurrent(q16, k16, v16, g, beta, scale, cu_seqlens, N, T, H, false, initial_state,
-                                         out, final_state, false, dvt, st);
+            return kda::launch_recurrent_fwd(q16, k16, v16, g, g_bf16, beta, scale, cu_seqlens, N, T, H,
+                                             initial_state, out, final_state, s_bf16, dvt, st);
         });
         return ok ? KDA_OK : KDA_ERR_LAUNCH;
     }
@@ -427,12 +437,12 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
         auto prep = [&](int b, int e) {
-            if (h32) return kda::launch_prep_h32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
+            if (h32) return kda::launch_prep_h32(q16, k16, g, g_bf16, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
             return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st)
                        : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
         };
         auto recur_range = [&](float *carry, int b, int e) {
-            if (h32) return kda::launch_recur_h32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
+            if (h32) return kda::launch_recur_h32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, s_bf16, st);
             return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
                        : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
@@ -448,7 +458,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
                  around(st, [&] {
                      return kda::launch_parts(recs, v16, cus, chunk_off, order, N, T, H, parts, initial_state, out,
-                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, h32, st);
+                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, h32, s_bf16, st);
                  });
         } else if (segs == 1) {
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
@@ -457,9 +467,12 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                                          : kda::launch_recur(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, waves, st);
                  });
         } else {
+            // the state crosses segment boundaries in fp32: through final_state where it is fp32,
+            // else through the workspace's carry buffer
             kda::RecurPrepArgs a{recs, q16, k16, v16, g, beta, scale, cus, chunk_off, order,
                                  N, T, H, initial_state, out, final_state,
-                                 final_state ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0, M};
+                                 final_state && !s_bf16 ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0, M,
+                                 g_bf16, s_bf16};
             auto bound = [&](int sg) { return segment_frac(sg, segs, (int64_t)N * H); };
             ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {

@@ -38,6 +38,8 @@
 // 16+4g+i-4 (i >= 4, half b), so that V_new, produced as two 16x16 D-layout blocks
 // (lane: rows 4g..4g+3 of each half), is the B operand of K~^T V_new and P V_new as it
 // stands in registers.
+#include <type_traits>
+
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -102,17 +104,26 @@ __device__ __forceinline__ f32x4 transpose16(f32x4 x, float (*tr)[17]) {
 // Loaded unconditionally (rows past the half's nc tokens reread row `fb`, a real token)
 // so that both halves' loads are issued together at the start of a chunk and one
 // memory latency is exposed instead of one per half; prep_half masks rows past nc.
+// GT: the element type of g, float or uint16_t (bf16 bits; the input-byte diet form:
+// half the bytes of the largest input).
+template <typename GT>
 struct HalfIn {
-    f32x2 g[C];
+    using GV = typename std::conditional<sizeof(GT) == 4, f32x2, uint32_t>::type;
+    GV g[C];
     uint32_t q[C], k[C];
+    __device__ f32x2 gval(int t) const {
+        if constexpr (sizeof(GT) == 4) return g[t];
+        else return f32x2{bf_lo(g[t]), bf_hi(g[t])};
+    }
 };
-__device__ __forceinline__ void load_half(HalfIn &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                          const float *__restrict__ g, int64_t t0, int nc, int64_t fb, int h,
-                                          int H, int c0) {
+template <typename GT>
+__device__ __forceinline__ void load_half(HalfIn<GT> &x, const uint16_t *__restrict__ q,
+                                          const uint16_t *__restrict__ k, const GT *__restrict__ g, int64_t t0,
+                                          int nc, int64_t fb, int h, int H, int c0) {
 #pragma unroll
     for (int t = 0; t < C; ++t) {
         const int64_t row = ((t < nc ? t0 + t : fb) * (int64_t)H + h) * D + c0;
-        x.g[t] = *(const f32x2 *)(g + row);
+        x.g[t] = *(const typename HalfIn<GT>::GV *)(g + row);
         x.q[t] = *(const uint32_t *)(q + row);
         x.k[t] = *(const uint32_t *)(k + row);
     }
@@ -130,8 +141,8 @@ __device__ __forceinline__ void load_half(HalfIn &x, const uint16_t *__restrict_
 //          Q+_b D_a), also written to the record
 // kts (HALF 0): K~ is further scaled per channel by e^{G_b}; ega (HALF 1): lane-permuted
 // e^{G_a}.
-template <int HALF>
-__device__ __forceinline__ void prep_half(const HalfIn &in, const float *__restrict__ beta,
+template <int HALF, typename GT>
+__device__ __forceinline__ void prep_half(const HalfIn<GT> &in, const float *__restrict__ beta,
                                           int64_t t0, int nc, int h, int H, float scale, PrepLds &L,
                                           char *rec, f32x2 kts, f32x2 ega, f32x4 (&Wt)[8], f32x4 (&Wd)[8],
                                           f32x4 &tbr, f32x4 &pr, f32x2 &ec, bf16x8 (&qh)[4], bf16x8 (&ql)[4]) {
@@ -146,7 +157,7 @@ __device__ __forceinline__ void prep_half(const HalfIn &in, const float *__restr
 #pragma unroll
     for (int t = 0; t < C; ++t) {
         const bool in_range = t < nc;
-        const f32x2 gt = in_range ? in.g[t] : f32x2{0.f, 0.f};
+        const f32x2 gt = in_range ? in.gval(t) : f32x2{0.f, 0.f};
         const uint32_t qq = in_range ? in.q[t] : 0u, kk = in_range ? in.k[t] : 0u;
         acc0 = __builtin_fmaf(fmaxf(gt.x, LOWER_BOUND), LOG2E, acc0);
         acc1 = __builtin_fmaf(fmaxf(gt.y, LOWER_BOUND), LOG2E, acc1);
@@ -297,22 +308,24 @@ __device__ __forceinline__ void prep_half(const HalfIn &in, const float *__restr
 
 // One wave turns one (32-token chunk, head) into a chunk record. t0: first token; nc:
 // its length (1..32).
+template <typename GT>
 __device__ __forceinline__ void prep_h32(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                         const float *__restrict__ g, const float *__restrict__ beta, int64_t t0,
+                                         const GT *__restrict__ g, const float *__restrict__ beta, int64_t t0,
                                          int nc, int h, int H, float scale, PrepHLds &LL, char *rec) {
     PrepLds &L = LL.t;
     const int l = threadIdx.x & 63, c0 = 2 * l, r = l & 15, gq = l >> 4;
     const int nca = nc < C ? nc : C, ncb = nc > C ? nc - C : 0;
     // every input load of the chunk issued at once
-    HalfIn ia, ib;
+    HalfIn<GT> ia, ib;
     load_half(ia, q, k, g, t0, nca, t0, h, H, c0);
     load_half(ib, q, k, g, t0 + C, ncb, t0, h, H, c0);
     // gate total of the second half on this lane's channel pair (base 2)
     float gb0 = 0.f, gb1 = 0.f;
 #pragma unroll
     for (int t = 0; t < C; ++t) {
-        gb0 = __builtin_fmaf(t < ncb ? fmaxf(ib.g[t].x, LOWER_BOUND) : 0.f, LOG2E, gb0);
-        gb1 = __builtin_fmaf(t < ncb ? fmaxf(ib.g[t].y, LOWER_BOUND) : 0.f, LOG2E, gb1);
+        const f32x2 gt = ib.gval(t);
+        gb0 = __builtin_fmaf(t < ncb ? fmaxf(gt.x, LOWER_BOUND) : 0.f, LOG2E, gb0);
+        gb1 = __builtin_fmaf(t < ncb ? fmaxf(gt.y, LOWER_BOUND) : 0.f, LOG2E, gb1);
     }
     const f32x2 eb = {__builtin_amdgcn_exp2f(gb0), __builtin_amdgcn_exp2f(gb1)};
 
@@ -372,8 +385,9 @@ __device__ __forceinline__ void prep_h32(const uint16_t *__restrict__ q, const u
 }
 
 // Record of chunk ci (global index, 32-token chunks), head h.
+template <typename GT>
 __device__ __forceinline__ void prep_h32_one(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                             const float *__restrict__ g, const float *__restrict__ beta,
+                                             const GT *__restrict__ g, const float *__restrict__ beta,
                                              const int32_t *__restrict__ cu, int N, int T, int H, float scale,
                                              const int32_t *__restrict__ chunk_off, char *__restrict__ recs, int ci,
                                              int h, PrepHLds &L) {
@@ -389,8 +403,9 @@ __device__ __forceinline__ void prep_h32_one(const uint16_t *__restrict__ q, con
     prep_h32(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * RecH::BYTES);
 }
 
+template <typename GT>
 __global__ __launch_bounds__(64) void prep_h32_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                      const float *__restrict__ g, const float *__restrict__ beta,
+                                                      const GT *__restrict__ g, const float *__restrict__ beta,
                                                       const int32_t *__restrict__ cu, int N, int T, int H, float scale,
                                                       const int32_t *__restrict__ chunk_off, char *__restrict__ recs,
                                                       int fb, int fe) {
@@ -402,6 +417,22 @@ __global__ __launch_bounds__(64) void prep_h32_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------- recurrence
+// Entry and exit states: fp32, or bf16 where the caller's states are (sbf: the input-byte
+// diet form, half the state bytes; rounded to nearest even on the way out). The chain
+// keeps an fp32 state; only the caller's s0 and sfin are bf16, the carry between
+// segments stays fp32.
+__device__ __forceinline__ float state_load(const float *p, bool bf, int64_t i) {
+    if (bf) return __uint_as_float((uint32_t)((const uint16_t *)p)[i] << 16);
+    return p[i];
+}
+__device__ __forceinline__ void state_store(float *p, bool bf, int64_t i, float x) {
+    if (bf) {
+        ((uint16_t *)p)[i] = (uint16_t)(pack2(x, 0.f) & 0xffffu);
+        return;
+    }
+    p[i] = x;
+}
+
 // The paired recurrence over 32-token records: NW 16-column slices per block, per slice a
 // chain wave and two output waves (roles and SIMD placement as PairLayout), one loader
 // wave. The chain wave runs V_new = U - W S and S <- D S + K~^T V_new and publishes, per
@@ -444,7 +475,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
                                                 const int32_t *__restrict__ chunk_off,
                                                 const int32_t *__restrict__ order, int N, int T, int H,
                                                 const float *s0, float *__restrict__ out, float *sfin, float *carry,
-                                                int fb, int fe, bool zero_v = false) {
+                                                int fb, int fe, bool sbf, bool zero_v = false) {
     using P = PairH<NW>;
     using PL = PairLayout<NW>;
     constexpr int LOADS = P::LOADS;
@@ -478,7 +509,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int64_t o = sbase + (int64_t)(16 * b + 4 * gq + j) * D;
-                    sfin[o] = s0 ? s0[o] : 0.f;
+                    state_store(sfin, sbf, o, s0 ? state_load(s0, sbf, o) : 0.f);
                 }
         }
         return;
@@ -487,6 +518,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
     const int64_t bos = seq_bos + (int64_t)CH * (ci0 - seq_c0);
     const float *sin = ci0 == seq_c0 ? s0 : carry;
     float *sout = ci1 == seq_c1 ? sfin : carry;
+    const bool sin_bf = sbf && ci0 == seq_c0, sout_bf = sbf && ci1 == seq_c1;
     auto snap_of = [&](int it) { return snaps + ((it % P::SNAPS) * NW + slice) * P::SNAP; };
     auto rec_of = [&](int m) { return recs + ((int64_t)(ci0 + m) * H + h) * RecH::BYTES; };
     auto sync = [] {
@@ -541,7 +573,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) S[b][j] = sin[sbase + (int64_t)(16 * b + 4 * gq + j) * D];
+                for (int j = 0; j < 4; ++j) S[b][j] = state_load(sin, sin_bf, sbase + (int64_t)(16 * b + 4 * gq + j) * D);
         } else {
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = zero;
@@ -634,7 +666,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
 #pragma unroll
             for (int b = 0; b < 8; ++b)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) sout[sbase + (int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+                for (int j = 0; j < 4; ++j) state_store(sout, sout_bf, sbase + (int64_t)(16 * b + 4 * gq + j) * D, S[b][j]);
         }
         return;
     }
@@ -731,10 +763,10 @@ template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe) {
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int sbf) {
     extern __shared__ __attribute__((aligned(16))) char ring[];
     recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, gridDim.x, D / (16 * NW)), ring, recs, v, cu, chunk_off,
-                               order, N, T, H, s0, out, sfin, carry, fb, fe);
+                               order, N, T, H, s0, out, sfin, carry, fb, fe, sbf != 0);
 }
 
 // One launch: the recurrence over the segment [fb, fe) on blocks [0, RB) and the records
@@ -743,17 +775,17 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_kernel(
 // order, so the prep blocks fill the CUs the recurrence leaves idle.
 constexpr int H32_PREP_WAVES = 4;
 
-template <int NW, int NSLOT>
+template <int NW, int NSLOT, typename GT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_kernel(
     const char *__restrict__ recs_in, const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
-    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB,
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const float *__restrict__ g,
+    const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB, int sbf,
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const GT *__restrict__ g,
     const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
     if ((int)blockIdx.x < RB) {
         recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
-                                   order, N, T, H, s0, out, sfin, carry, fb, fe);
+                                   order, N, T, H, s0, out, sfin, carry, fb, fe, sbf != 0);
         return;
     }
     const int w = threadIdx.x >> 6;
@@ -768,6 +800,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_ker
 
 // Pass 1 of the recurrence over parts: blocks [0, G/2) run every part from a zero state,
 // blocks [G/2, G) from the identity with v taken as 0 (final state: the part's linear map).
+// Its states are all fp32 (workspace).
 template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
@@ -778,17 +811,21 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_ke
     const bool id = (int)blockIdx.x >= RB;
     const int b = id ? (int)blockIdx.x - RB : (int)blockIdx.x;
     recur_h32_block<NW, NSLOT>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
-                               id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, id);
+                               id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, false, id);
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const void *g, bool g_bf16, const float *beta,
                            const int32_t *cu, int N, int T, int H, float scale, const int32_t *chunk_off,
                            char *recs, int fb, int fe, int64_t M, hipStream_t st) {
     const int64_t blocks = seg_chunks_bound(M, N, fb, fe) * H;
     if (blocks <= 0 || fe <= fb) return hipSuccess;
-    hipLaunchKernelGGL(prep_h32_kernel, dim3((unsigned)blocks), dim3(64), 0, st, q, k, g, beta, cu, N, T, H, scale,
-                       chunk_off, recs, fb, fe);
+    if (g_bf16)
+        hipLaunchKernelGGL(prep_h32_kernel<uint16_t>, dim3((unsigned)blocks), dim3(64), 0, st, q, k,
+                           (const uint16_t *)g, beta, cu, N, T, H, scale, chunk_off, recs, fb, fe);
+    else
+        hipLaunchKernelGGL(prep_h32_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, st, q, k, (const float *)g,
+                           beta, cu, N, T, H, scale, chunk_off, recs, fb, fe);
     return hipGetLastError();
 }
 
@@ -796,7 +833,7 @@ template <int NW>
 static hipError_t launch_recur_h32_t(const char *recs, const uint16_t *v, const int32_t *cu,
                                      const int32_t *chunk_off, const int32_t *order, int N, int T, int H,
                                      const float *s0, float *out, float *sfin, float *carry, int fb, int fe,
-                                     hipStream_t st) {
+                                     bool sbf, hipStream_t st) {
     constexpr int NS = pairh_nslot<NW>();
     constexpr int lds = PairHLds<NW, NS>::BYTES;
     auto kern = recur_h32_kernel<NW, NS>;
@@ -804,28 +841,28 @@ static hipError_t launch_recur_h32_t(const char *recs, const uint16_t *v, const 
     if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t blocks = (int64_t)N * H * (D / (16 * NW));
     hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(64 * PairLayout<NW>::WAVES), lds, st, recs, v, cu,
-                       chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe);
+                       chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, (int)sbf);
     return hipGetLastError();
 }
 
 hipError_t launch_recur_h32_range(const char *recs, const uint16_t *v, const int32_t *cu, const int32_t *chunk_off,
                                   const int32_t *order, int N, int T, int H, const float *s0, float *out, float *sfin,
-                                  float *carry, int waves, int fb, int fe, hipStream_t st) {
+                                  float *carry, int waves, int fb, int fe, bool sbf, hipStream_t st) {
     switch (waves) {
-    case 401: return launch_recur_h32_t<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
-    case 402: return launch_recur_h32_t<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, st);
+    case 401: return launch_recur_h32_t<1>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, sbf, st);
+    case 402: return launch_recur_h32_t<2>(recs, v, cu, chunk_off, order, N, T, H, s0, out, sfin, carry, fb, fe, sbf, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int NW>
+template <int NW, typename GT>
 static hipError_t launch_recur_h32_prep_t(const RecurPrepArgs &a, hipStream_t st) {
     constexpr int NS = pairh_nslot<NW>();
     constexpr int pair = PairHLds<NW, NS>::BYTES;
     constexpr int prep = H32_PREP_WAVES * (int)sizeof(PrepHLds);
     constexpr int lds = pair > prep ? pair : prep;
     static_assert(lds <= 160 * 1024 && lds > 80 * 1024, "LDS");
-    auto kern = recur_h32_prep_kernel<NW, NS>;
+    auto kern = recur_h32_prep_kernel<NW, NS, GT>;
     static std::atomic<uint64_t> lds_set{0};
     if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
     const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
@@ -833,14 +870,16 @@ static hipError_t launch_recur_h32_prep_t(const RecurPrepArgs &a, hipStream_t st
         a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + H32_PREP_WAVES - 1) / H32_PREP_WAVES : 0;
     hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
                        a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry, a.fb, a.fe, (int)rb,
-                       a.q, a.k, a.g, a.beta, a.scale, a.recs, a.pb, a.pe);
+                       (int)a.state_bf16, a.q, a.k, (const GT *)a.g, a.beta, a.scale, a.recs, a.pb, a.pe);
     return hipGetLastError();
 }
 
 hipError_t launch_recur_h32_prep(const RecurPrepArgs &a, int waves, hipStream_t st) {
-    switch (waves) {
-    case 401: return launch_recur_h32_prep_t<1>(a, st);
-    case 402: return launch_recur_h32_prep_t<2>(a, st);
+    switch (waves * 2 + (a.g_bf16 ? 1 : 0)) {
+    case 802: return launch_recur_h32_prep_t<1, float>(a, st);
+    case 803: return launch_recur_h32_prep_t<1, uint16_t>(a, st);
+    case 804: return launch_recur_h32_prep_t<2, float>(a, st);
+    case 805: return launch_recur_h32_prep_t<2, uint16_t>(a, st);
     default: return hipErrorInvalidValue;
     }
 }

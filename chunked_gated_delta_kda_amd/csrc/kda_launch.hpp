@@ -81,6 +81,8 @@ struct RecurPrepArgs {
     float *out, *sfin, *carry;
     int fb, fe, pb, pe;
     int64_t M;          // bound on the batch's chunk count
+    bool g_bf16 = false;      // g holds bf16 bits (forms 401/402 only)
+    bool state_bf16 = false;  // s0 and sfin hold bf16 bits (forms 401/402 only)
 };
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 // 32-token form (waves 301: one slice per block): recurrence over the segment
@@ -94,12 +96,13 @@ hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st
 // 32-token chunks with fp16 recurrence operands (kda_h32.hip): records of the segment
 // [fb, fe); recurrence forms 401 (one 16-column slice per block) and 402 (two), alone or
 // with the prep of [pb, pe); pass 1 of the recurrence over parts.
-hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
+// g_bf16: g holds bf16 bits; sbf: s0 and sfin hold bf16 bits (the carry stays fp32).
+hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const void *g, bool g_bf16, const float *beta,
                            const int32_t *cu, int N, int T, int H, float scale, const int32_t *chunk_off,
                            char *recs, int fb, int fe, int64_t M, hipStream_t st);
 hipError_t launch_recur_h32_range(const char *recs, const uint16_t *v, const int32_t *cu, const int32_t *chunk_off,
                                   const int32_t *order, int N, int T, int H, const float *s0, float *out, float *sfin,
-                                  float *carry, int waves, int fb, int fe, hipStream_t st);
+                                  float *carry, int waves, int fb, int fe, bool sbf, hipStream_t st);
 hipError_t launch_recur_h32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 hipError_t launch_h32_parts_pass1(const char *recs, const uint16_t *v, const int32_t *vcu, const int32_t *vco,
                                   const int32_t *vorder, int NV, int T, int H, const float *ident, float *out,
@@ -116,6 +119,11 @@ hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t
                             const float *beta, float scale, const int32_t *cu, int N, int T, int H,
                             bool one_token_per_seq, const void *s0, float *out, void *sfin, bool bf16_state,
                             int dvt, hipStream_t st);
+// The token loop over a packed batch (the recurrent variant of the forward), with g and the
+// initial/final states as fp32 or bf16 (g_bf16, s_bf16: bf16 bits).
+hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const void *g, bool g_bf16,
+                                const float *beta, float scale, const int32_t *cu, int N, int T, int H,
+                                const void *s0, float *out, void *sfin, bool s_bf16, int dvt, hipStream_t st);
 // value-column tile of launch_recurrent for this many (sequence, head) chains over a
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
@@ -131,5 +139,5 @@ hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, bool h32, hipStream_t st);
+                        float *ri, float *sin, bool h32, bool sbf, hipStream_t st);
 }  // namespace kda

@@ -72,6 +72,19 @@ __device__ __forceinline__ void store_state(float *base, int64_t i, const float 
     const f32x4v y = {x[0], x[1], x[2], x[3]};
     __builtin_nontemporal_store(y, (f32x4v *)(base + i));
 }
+// The same four columns of a bf16 state (the input-byte diet form of the prefill's
+// initial and final state): one 8-byte access, widened to fp32 / rounded to nearest even.
+__device__ __forceinline__ void load_state(const uint16_t *base, int64_t i, float (&x)[4]) {
+    const uint2 y = *(const uint2 *)(base + i);
+    x[0] = __uint_as_float(y.x << 16), x[1] = __uint_as_float(y.x & 0xffff0000u);
+    x[2] = __uint_as_float(y.y << 16), x[3] = __uint_as_float(y.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store_state(uint16_t *base, int64_t i, const float (&x)[4]) {
+    *(uint2 *)(base + i) = uint2{bf16_rne(x[0]) | (bf16_rne(x[1]) << 16), bf16_rne(x[2]) | (bf16_rne(x[3]) << 16)};
+}
+// g of one element: fp32, or bf16 bits
+__device__ __forceinline__ float g_val(const float *g, int64_t i) { return g[i]; }
+__device__ __forceinline__ float g_val(const uint16_t *g, int64_t i) { return __uint_as_float((uint32_t)g[i] << 16); }
 
 template <int DVT, int CPT>
 struct Tile {
@@ -91,16 +104,16 @@ struct TokIn {
     float beta;
 };
 
-template <int CPT>
+template <int CPT, typename GT>
 __device__ __forceinline__ TokIn<CPT> load_token(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                 const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                                 const uint16_t *__restrict__ v, const GT *__restrict__ g,
                                                  const float *__restrict__ beta, int64_t th, int tid, int col) {
     TokIn<CPT> r;
     const int64_t o = th * D;
     const int row = tid & (D - 1);  // threads >= 128 load a row they do not use: keeps the loads unconditional
     r.q = __uint_as_float((uint32_t)q[o + row] << 16);
     r.k = __uint_as_float((uint32_t)k[o + row] << 16);
-    r.g = g[o + row];
+    r.g = g_val(g, o + row);
     if constexpr (CPT == 8) {
         const uint4 x = *(const uint4 *)(v + o + col);
         r.v[0] = x.x, r.v[1] = x.y, r.v[2] = x.z, r.v[3] = x.w;
@@ -112,11 +125,13 @@ __device__ __forceinline__ TokIn<CPT> load_token(const uint16_t *__restrict__ q,
     return r;
 }
 
-template <int DVT>
+// GT: g's element type (float, or uint16_t for bf16 bits); ST: the states' element type
+// (float, or uint16_t for bf16 states, widened on load and rounded on store).
+template <int DVT, typename GT, typename ST>
 __global__ __launch_bounds__(NT) void recurrent_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
-    int N, int T, int H, int one_token_per_seq, const float *s0, float *__restrict__ out, float *sfin,
+    const GT *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
+    int N, int T, int H, int one_token_per_seq, const ST *s0, float *__restrict__ out, ST *sfin,
     int32_t *dev_err) {
     constexpr int CPT = 4;
     using TL = Tile<DVT, CPT>;
@@ -179,7 +194,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
     }
 
     TokIn<CPT> cur{};
-    if (t0 < t1) cur = load_token<CPT>(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
+    if (t0 < t1) cur = load_token<CPT, GT>(q, k, v, g, beta, (int64_t)t0 * H + h, tid, col);
     for (int t = t0; t < t1; ++t) {
         const int buf = (t - t0) & 1;
         const int64_t th = (int64_t)t * H + h;
@@ -199,7 +214,7 @@ __global__ __launch_bounds__(NT) void recurrent_kernel(
         const float bt = cur.beta;
         // next token's inputs (the last token reloads itself: loads stay unconditional)
         const int tn = t + 1 < t1 ? t + 1 : t;
-        cur = load_token<CPT>(q, k, v, g, beta, (int64_t)tn * H + h, tid, col);
+        cur = load_token<CPT, GT>(q, k, v, g, beta, (int64_t)tn * H + h, tid, col);
         __syncthreads();
 
         // decay, and this thread's part of u = S1^T k and w = S1^T q
@@ -310,7 +325,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(
             sp[m] = SV{};
     }
     const int64_t th = (int64_t)n * H + h;
-    const TokIn<CPT> cur = load_token<CPT>(q, k, v, g, beta, th, tid, col);
+    const TokIn<CPT> cur = load_token<CPT, float>(q, k, v, g, beta, th, tid, col);
     if (tid < D) {
         sq[tid] = cur.q;
         sk[tid] = cur.k;
@@ -426,8 +441,45 @@ static void launch_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         hipLaunchKernelGGL((decode_kernel<DVT, BF16S>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
                            scale, H, s0, out, sfin);
     else if constexpr (!BF16S)
-        hipLaunchKernelGGL((recurrent_kernel<DVT>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v, g, beta,
-                           scale, cu, N, T, H, 0, (const float *)s0, out, (float *)sfin, device_error_word());
+        hipLaunchKernelGGL((recurrent_kernel<DVT, float, float>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v,
+                           g, beta, scale, cu, N, T, H, 0, (const float *)s0, out, (float *)sfin, device_error_word());
+}
+
+template <int DVT, typename GT, typename ST>
+static void launch_fwd_tile(const uint16_t *q, const uint16_t *k, const uint16_t *v, const void *g,
+                            const float *beta, float scale, const int32_t *cu, int N, int T, int H, const void *s0,
+                            float *out, void *sfin, hipStream_t st) {
+    const int64_t blocks = (int64_t)N * H * (D / DVT);
+    hipLaunchKernelGGL((recurrent_kernel<DVT, GT, ST>), dim3((unsigned)blocks), dim3(NT), 0, st, q, k, v,
+                       (const GT *)g, beta, scale, cu, N, T, H, 0, (const ST *)s0, out, (ST *)sfin,
+                       device_error_word());
+}
+
+hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const void *g, bool g_bf16,
+                                const float *beta, float scale, const int32_t *cu, int N, int T, int H,
+                                const void *s0, float *out, void *sfin, bool s_bf16, int dvt, hipStream_t st) {
+    if (!g_bf16 && !s_bf16) {
+        return launch_recurrent(q, k, v, (const float *)g, beta, scale, cu, N, T, H, false, s0, out, sfin, false, dvt,
+                                st);
+    }
+#define KDA_FWD_TILE(W)                                                                                            \
+    case W:                                                                                                        \
+        if (g_bf16 && s_bf16)                                                                                      \
+            launch_fwd_tile<W, uint16_t, uint16_t>(q, k, v, g, beta, scale, cu, N, T, H, s0, out, sfin, st);       \
+        else if (g_bf16)                                                                                           \
+            launch_fwd_tile<W, uint16_t, float>(q, k, v, g, beta, scale, cu, N, T, H, s0, out, sfin, st);          \
+        else                                                                                                       \
+            launch_fwd_tile<W, float, uint16_t>(q, k, v, g, beta, scale, cu, N, T, H, s0, out, sfin, st);          \
+        break;
+    switch (dvt) {
+        KDA_FWD_TILE(128)
+        KDA_FWD_TILE(64)
+        KDA_FWD_TILE(32)
+    default:
+        return hipErrorInvalidValue;
+    }
+#undef KDA_FWD_TILE
+    return hipGetLastError();
 }
 
 hipError_t launch_recurrent(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

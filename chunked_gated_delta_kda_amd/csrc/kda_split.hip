@@ -1424,13 +1424,14 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel
 // composition over the parts of each sequence, one block per (sequence, head, 16 value
 // columns): the columns of a state evolve independently under M
 __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, const float *rb, const float *ri,
-                                                            int N, int P, int H, float *sin, float *sfin) {
+                                                            int N, int P, int H, float *sin, float *sfin, int sbf) {
     __shared__ float S[D][16];
     const int cs = blockIdx.x % 8, h = (blockIdx.x / 8) % H, n = blockIdx.x / (8 * H);
     const int t = threadIdx.x, r = t >> 1, c0 = (t & 1) * 8, col0 = cs * 16;
     for (int i = t; i < D * 16; i += 256) {
         const int rr = i / 16, cc = i % 16;
-        S[rr][cc] = s0 ? s0[((int64_t)n * H + h) * D * D + (int64_t)rr * D + col0 + cc] : 0.f;
+        const int64_t i0 = ((int64_t)n * H + h) * D * D + (int64_t)rr * D + col0 + cc;
+        S[rr][cc] = !s0 ? 0.f : sbf ? __uint_as_float((uint32_t)((const uint16_t *)s0)[i0] << 16) : s0[i0];
     }
     __syncthreads();
     for (int p = 0; p < P; ++p) {
@@ -1452,7 +1453,11 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
     }
     if (sfin) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sfin[((int64_t)n * H + h) * D * D + (int64_t)r * D + col0 + c0 + j] = S[r][c0 + j];
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i0 = ((int64_t)n * H + h) * D * D + (int64_t)r * D + col0 + c0 + j;
+            if (sbf) ((uint16_t *)sfin)[i0] = (uint16_t)(pack2(S[r][c0 + j], 0.f) & 0xffffu);   // round to nearest even
+            else sfin[i0] = S[r][c0 + j];
+        }
     }
 }
 
@@ -1461,7 +1466,7 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, bool h32, hipStream_t st) {
+                        float *ri, float *sin, bool h32, bool sbf, hipStream_t st) {
     const int NV = N * P;
     const int64_t ns = (int64_t)NV * H;
     hipLaunchKernelGGL(parts_setup_kernel, dim3(512), dim3(256), 0, st, cu_safe, chunk_off, order, N, P,
@@ -1482,10 +1487,10 @@ hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_s
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), 0, st, s0, (const float *)rb,
-                       (const float *)ri, N, P, H, sin, sfin);
+                       (const float *)ri, N, P, H, sin, sfin, (int)sbf);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 401, 0,
-                                           SEG_ONE, st);
+                                           SEG_ONE, false, st);
     return launch_recur_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 101, 0, SEG_ONE, st);
 }
 

@@ -23,6 +23,7 @@ EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_noalloc", "kda_workspace_bytes", "k
 #: KDA_DEVERR_* bits of the device error word
 DEVERR = {1: "fused hand-off wait gave up (outputs invalid)", 2: "malformed cu_seqlens (sanitised)"}
 STATE_DTYPES = {"f32": 0, "bf16": 1}
+DTYPES = STATE_DTYPES   # KDA_DTYPE_* of kda_options.g_dtype / state_dtype
 SEGMENT_ONE = 65536   # KDA_SEGMENT_ONE: unit of the launch plan's segment fractions
 NOALLOC_MAX_SEQS = 16384   # KDA_NOALLOC_MAX_SEQS
 KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_prep", 5: "recurrent", 6: "parts"}
@@ -31,7 +32,8 @@ KERNEL_KINDS = {0: "chunk_map", 1: "prep", 2: "recur", 3: "fused", 4: "recur_pre
 class KdaOptions(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("n_stage_events", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("reserved", ctypes.c_int32)]
+                ("stage_events", ctypes.POINTER(ctypes.c_void_p)), ("g_dtype", ctypes.c_int32),
+                ("state_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class KdaLaunchInfo(ctypes.Structure):

@@ -74,6 +74,10 @@ typedef enum kda_variant {
 #define KDA_KERNEL_RECURRENT 5    /* token-by-token recurrence (no chunk ranges)          */
 #define KDA_KERNEL_PARTS 6        /* recurrence over parts of each sequence: setup, two passes, composition */
 
+/* Element types of kda_options.g_dtype / state_dtype (and of kda_decode_ex). */
+#define KDA_DTYPE_F32 0
+#define KDA_DTYPE_BF16 1
+
 typedef struct kda_options {
     int32_t variant;        /* kda_variant                                              */
     int32_t n_stage_events; /* 0, or the length of stage_events (2..KDA_MAX_STAGE_EVENTS) */
@@ -85,8 +89,16 @@ typedef struct kda_options {
                             /* launch and [i] after the i-th (kda_launch_plan lists     */
                             /* them); slots past the last launch are left untouched.   */
                             /* NULL = no events.                                        */
+    int32_t g_dtype;        /* KDA_DTYPE_F32 (0) or KDA_DTYPE_BF16: g holds bf16 values */
+                            /* [T, H, 128] (the input-byte diet: half of g's bytes)     */
+    int32_t state_dtype;    /* KDA_DTYPE_F32 (0) or KDA_DTYPE_BF16: initial_state and   */
+                            /* final_state are bf16 [N, H, 128, 128] (stored in bf16,   */
+                            /* updated in fp32; final_state rounded to nearest even)    */
     int32_t reserved;       /* must be 0                                                */
 } kda_options;
+/* bf16 g or states are read by the split variant (its 32-token forms, which it then
+ * uses whatever the shape) and by the token loop; with the fused variant the call
+ * returns KDA_ERR_UNSUPPORTED. */
 
 /*
  * kda_fwd -- KDA forward (prefill) over a packed batch.

@@ -62,14 +62,25 @@ def test_validation_errors(lib):
     assert call(lib, q=None) == 1                     # KDA_ERR_NULL
     assert call(lib, beta=None) == 1
     assert call(lib, out=None) == 1
-    assert call(lib, opt=native.KdaOptions(7, 0, None, 0, None, 0)) == 3
-    assert call(lib, opt=native.KdaOptions(0, 1, None, 0, None, 0)) == 3      # 1 stage event
-    assert call(lib, opt=native.KdaOptions(0, 4, None, 0, None, 0)) == 3      # events NULL
-    small = native.KdaOptions(1, 0, ctypes.c_void_p(256), 10, None, 0)
-    assert call(lib, opt=native.KdaOptions(0, 0, None, 0, None, 1)) == 3   # reserved != 0
+    opts = lambda **kw: native.KdaOptions(**{"variant": 0, "n_stage_events": 0, **kw})
+    assert call(lib, opt=opts(variant=7)) == 3
+    assert call(lib, opt=opts(n_stage_events=1)) == 3                         # 1 stage event
+    assert call(lib, opt=opts(n_stage_events=4)) == 3                         # events NULL
+    assert call(lib, opt=opts(reserved=1)) == 3                               # reserved != 0
+    assert call(lib, opt=opts(g_dtype=2)) == 3                                # unknown g dtype
+    assert call(lib, opt=opts(state_dtype=-1)) == 3                           # unknown state dtype
+    # bf16 g or states: the fused variant does not read them
+    assert call(lib, opt=opts(variant=2, g_dtype=1)) == 3
+    assert call(lib, opt=opts(variant=2, state_dtype=1)) == 3
+    small = opts(variant=1, workspace=ctypes.c_void_p(256), workspace_bytes=10)
     assert call(lib, opt=small) == 4                  # KDA_ERR_ALLOC: workspace too small
-    # final_state partially overlapping initial_state
+    small.g_dtype = 1                                 # still too small with bf16 g (forms 401/402)
+    assert call(lib, opt=small) == 4
+    # final_state partially overlapping initial_state (as fp32, and as bf16 states)
     assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + 64)) == 7
+    n_bf16 = 2 * 128 * 128 * 2
+    assert call(lib, s0=ctypes.c_void_p(4096), fin=ctypes.c_void_p(4096 + n_bf16 - 64),
+                opt=opts(state_dtype=1, variant=1, workspace=ctypes.c_void_p(256), workspace_bytes=10)) == 7
 
 
 def decode_call(lib, **over):

@@ -23,20 +23,25 @@ def test_fwd_good_buffers():
     a = _inputs()
     out = torch.empty(T, H, D)
     fin = torch.empty(N, H, D, D)
-    assert check_fwd_args(**a, initial_state=torch.zeros(N, H, D, D), out=out, final_state=fin) == (T, H, N)
-    assert check_fwd_args(**a) == (T, H, N)
+    assert check_fwd_args(**a, initial_state=torch.zeros(N, H, D, D), out=out, final_state=fin) == \
+        (T, H, N, torch.float32)
+    assert check_fwd_args(**a) == (T, H, N, torch.float32)
+    # the input-byte diet forms: bf16 g, bf16 states
+    a["g"] = a["g"].to(torch.bfloat16)
+    sb = torch.zeros(N, H, D, D, dtype=torch.bfloat16)
+    assert check_fwd_args(**a, initial_state=sb, final_state=sb.clone()) == (T, H, N, torch.bfloat16)
 
 
 @pytest.mark.parametrize("name,bad", [
     ("out", lambda: torch.empty(T, H, D, dtype=torch.bfloat16)),          # half the bytes
     ("out", lambda: torch.empty(T - 1, H, D)),                            # one row short
     ("out", lambda: torch.empty(H, T, D).transpose(0, 1)),                # not contiguous
-    ("final_state", lambda: torch.empty(N, H, D, D, dtype=torch.bfloat16)),
     ("final_state", lambda: torch.empty(N - 1, H, D, D)),
     ("final_state", lambda: torch.empty(N, H, D, D).transpose(2, 3)),
     ("initial_state", lambda: torch.empty(N, H, D, 64)),
     ("beta", lambda: torch.empty(T, H, dtype=torch.float64)),
-    ("g", lambda: torch.empty(T, H, D, dtype=torch.bfloat16)),
+    ("g", lambda: torch.empty(T, H, D, dtype=torch.float16)),
+    ("final_state", lambda: torch.empty(N, H, D, D, dtype=torch.float16)),
     ("v", lambda: torch.empty(T, H, D)),
 ])
 def test_fwd_rejects(name, bad):
@@ -44,6 +49,13 @@ def test_fwd_rejects(name, bad):
     a[name] = bad()
     with pytest.raises(ValueError, match=name):
         check_fwd_args(**a)
+
+
+def test_fwd_rejects_mixed_state_dtypes():
+    a = _inputs()
+    with pytest.raises(ValueError, match="final_state"):
+        check_fwd_args(**a, initial_state=torch.zeros(N, H, D, D), final_state=torch.empty(N, H, D, D,
+                                                                                            dtype=torch.bfloat16))
 
 
 def test_fwd_rejects_bad_offsets_vector():

@@ -40,7 +40,7 @@ def _call(fn_name, w, variant=None):
     if fn_name == "kda_fwd_noalloc":
         rc = lib.kda_fwd_noalloc(*args)
     else:
-        opt = native.KdaOptions(native.VARIANTS[variant], 0, None, 0, None, 0)
+        opt = native.KdaOptions(variant=native.VARIANTS[variant])
         rc = lib.kda_fwd_ex(*args, ctypes.byref(opt))
     torch.cuda.synchronize()
     assert rc == 0, native.status_string(rc)
