@@ -15,7 +15,7 @@ import numpy as np
 
 from .build import LIB, build as _build
 
-__all__ = ["kda_forward", "LOWER_BOUND", "load_library"]
+__all__ = ["kda_forward", "kda_backward", "LOWER_BOUND", "load_library"]
 
 #: log-decay clamp the FlashKDA articles state (smzdm "KDA 内核到底难在哪").
 LOWER_BOUND = -5.0
@@ -39,6 +39,11 @@ def _bind(lib):
     lib.kda_oracle_fwd.argtypes = [dp, dp, dp, dp, dp, ctypes.c_double, ip,
                                    ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                    dp, ctypes.c_double, dp, dp, ip, ctypes.c_int64, ctypes.c_int]
+    if hasattr(lib, "kda_oracle_bwd"):
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        lib.kda_oracle_bwd.argtypes = [dp, dp, dp, dp, dp, ctypes.c_double, ip,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       dp, ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     return lib
 
 
@@ -98,3 +103,35 @@ def kda_forward(q, k, v, g, beta, scale, cu_seqlens=None, initial_state=None,
     if rc != 0:
         raise ValueError(f"kda_oracle_fwd failed with code {rc}")
     return out, fin
+
+
+def kda_backward(q, k, v, g, beta, scale, d_out, cu_seqlens=None, initial_state=None, d_final_state=None,
+                 lower_bound=LOWER_BOUND, threads=None, lib=None):
+    """Gradients of the forward oracle's outputs (fp64 reverse-mode token loop).
+
+    d_out: [T, H, dv] gradient of o; d_final_state: [N, H, dk, dv] or None (zero).
+    Returns dict(dq [T,H,dk], dk [T,H,dk], dv [T,H,dv], dg [T,H,dk], dbeta [T,H],
+    d_initial_state [N,H,dk,dv]) as float64 (d_initial_state is the gradient with respect
+    to the initial state, zeros standing in when none was given).
+    """
+    lib = lib or load_library()
+    q, k, v, g, beta, d_out = map(_f64, (q, k, v, g, beta, d_out))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    assert d_out.shape == (T, H, dv)
+    if cu_seqlens is None:
+        cu_seqlens = np.array([0, T], dtype=np.int64)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    N = cu.shape[0] - 1
+    s0 = None if initial_state is None else _f64(initial_state)
+    dfin = None if d_final_state is None else _f64(d_final_state)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dg=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)), d_initial_state=np.zeros((N, H, dk, dv)))
+    rc = lib.kda_oracle_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+                            _ptr(cu, ctypes.c_int64), N, H, dk, dv, _ptr(s0), float(lower_bound),
+                            _ptr(d_out), _ptr(dfin), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                            _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["d_initial_state"]),
+                            int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_bwd failed with code {rc}")
+    return out

@@ -8,23 +8,25 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "kda_oracle.c")
+SRC = os.path.join(HERE, "kda_oracle.c")          # forward
+SRC_BWD = os.path.join(HERE, "kda_oracle_bwd.c")  # backward (gradients of the forward)
 LIB = os.path.join(HERE, "libkda_oracle.so")
 
 
 def compile_oracle(src=SRC, out=LIB, cc=None, extra=(), strict=True):
-    """Compile ``src`` into the shared library ``out``; returns ``out``."""
+    """Compile ``src`` (a path or a list of paths) into the shared library ``out``; returns ``out``."""
     cc = cc or os.environ.get("CC", "gcc")
     tmp = out + ".tmp"
     warn = ["-Wall", "-Wextra", "-Werror"] if strict else ["-w"]
-    cmd = [cc, "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", *warn, *extra, src, "-o", tmp, "-lm"]
+    srcs = [src] if isinstance(src, str) else list(src)
+    cmd = [cc, "-O2", "-std=c99", "-fPIC", "-shared", "-pthread", *warn, *extra, *srcs, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
 
 
 def build():
-    return compile_oracle()
+    return compile_oracle([SRC, SRC_BWD])
 
 
 if __name__ == "__main__":
