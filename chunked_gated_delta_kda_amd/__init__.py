@@ -9,7 +9,7 @@ import math
 
 from . import native
 
-__all__ = ["fwd", "fwd_noalloc", "decode", "workspace_bytes", "select_variant", "device_errors", "version", "native"]
+__all__ = ["fwd", "fwd_noalloc", "bwd", "decode", "workspace_bytes", "select_variant", "device_errors", "version", "native"]
 
 HEAD_DIM = 128
 
@@ -148,6 +148,52 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         if bits:
             raise native.KdaDeviceError(bits)
     return out, final_state
+
+
+def check_bwd_args(q, k, v, g, beta, d_out, cu_seqlens=None, initial_state=None, d_final_state=None):
+    """Every check bwd makes on its inputs before anything is launched; returns (T, H, N).
+    The backward reads g, the states and the gradients in fp32."""
+    import torch
+
+    T, H, N, _ = check_fwd_args(q, k, v, g, beta, cu_seqlens, initial_state, state_dtype=torch.float32)
+    dev = q.device
+    _expect("g", g, torch.float32, (T, H, HEAD_DIM), dev)
+    _expect("d_out", d_out, torch.float32, (T, H, HEAD_DIM), dev)
+    if d_final_state is not None:
+        _expect("d_final_state", d_final_state, torch.float32, (N, H, HEAD_DIM, HEAD_DIM), dev)
+    return T, H, N
+
+
+def bwd(q, k, v, g, beta, d_out, scale=None, cu_seqlens=None, initial_state=None, d_final_state=None, *,
+        need_d_initial_state=True, workspace=None, stream=None):
+    """Gradients of fwd (kda_bwd): given d_out = dL/do (fp32 [T, H, 128]) and optionally
+    d_final_state = dL/dS_final (fp32 [N, H, 128, 128]), returns a dict of fp32 tensors dq,
+    dk, dv, dg ([T, H, 128]), dbeta ([T, H]) and d_initial_state ([N, H, 128, 128], or None
+    when need_d_initial_state is False). Inputs as for fwd, with g and initial_state fp32."""
+    import torch
+
+    lib = native.load_library()
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("kda.bwd needs device tensors")
+    T, H, N = check_bwd_args(q, k, v, g, beta, d_out, cu_seqlens, initial_state, d_final_state)
+    Dk = HEAD_DIM
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    f32 = dict(dtype=torch.float32, device=dev)
+    gr = dict(dq=torch.empty((T, H, Dk), **f32), dk=torch.empty((T, H, Dk), **f32),
+              dv=torch.empty((T, H, Dk), **f32), dg=torch.empty((T, H, Dk), **f32),
+              dbeta=torch.empty((T, H), **f32),
+              d_initial_state=torch.empty((N, H, Dk, Dk), **f32) if need_d_initial_state else None)
+    if workspace is None:
+        workspace = torch.empty(lib.kda_bwd_workspace_bytes(N, T, H), dtype=torch.uint8, device=dev)
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(cu_seqlens), N, T, H, Dk,
+                     _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(gr["dq"]), _ptr(gr["dk"]),
+                     _ptr(gr["dv"]), _ptr(gr["dg"]), _ptr(gr["dbeta"]), _ptr(gr["d_initial_state"]),
+                     ctypes.c_void_p(st.cuda_stream), _ptr(workspace), workspace.numel())
+    native.check(rc)
+    return gr
 
 
 def check_decode_args(q, k, v, g, beta, state=None, state_out="inplace", out=None, state_dtype=None):

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_split.hip", "kda_h32.hip", "kda_fused.hip", "kda_recurrent.hip"]
+SOURCES = ["kda_api.cpp", "kda_split.hip", "kda_h32.hip", "kda_fused.hip", "kda_recurrent.hip", "kda_bwd.hip"]
 
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Werror",
           "-Wno-unused-command-line-argument",

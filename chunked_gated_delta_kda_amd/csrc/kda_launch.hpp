@@ -128,6 +128,15 @@ hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
+// The backward (kda_bwd.hip): one workgroup per (sequence, head). chunk_off counts blocks of
+// bwd_block_tokens() tokens per sequence (the chunk map at that chunk length); ck holds a
+// state per block and head, buf bwd_block_tokens() states per (sequence, head).
+hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
+                      const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
+                      float *dg, float *dbeta, float *ds0, float *ck, float *buf, hipStream_t st);
+int bwd_block_tokens();
+
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                         const float *beta, const int32_t *cu, const int32_t *order, int N, int T,
                         int H, float scale, const float *s0, float *out, float *sfin, int *err,

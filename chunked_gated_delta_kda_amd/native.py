@@ -18,8 +18,8 @@ VARIANTS = {"auto": 0, "split": 1, "fused": 2, "recurrent": 3}
 
 #: every symbol include/kda.h declares
 EXPORTS = ("kda_fwd", "kda_fwd_ex", "kda_fwd_noalloc", "kda_workspace_bytes", "kda_select_variant",
-           "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_device_errors", "kda_status_string",
-           "kda_version")
+           "kda_launch_plan", "kda_decode", "kda_decode_ex", "kda_bwd", "kda_bwd_workspace_bytes",
+           "kda_device_errors", "kda_status_string", "kda_version")
 #: KDA_DEVERR_* bits of the device error word
 DEVERR = {1: "fused hand-off wait gave up (outputs invalid)", 2: "malformed cu_seqlens (sanitised)"}
 STATE_DTYPES = {"f32": 0, "bf16": 1}
@@ -83,6 +83,11 @@ def load_library(path=LIB_PATH):
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode_ex.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, i32, i32, i32, vp, vp, f32p, vp, i32]
     lib.kda_decode_ex.restype = ctypes.c_int
+    lib.kda_bwd.argtypes = [vp, vp, vp, f32p, f32p, ctypes.c_float, vp, i32, i32, i32, i32, f32p, f32p, f32p,
+                            f32p, f32p, f32p, f32p, f32p, f32p, vp, vp, ctypes.c_size_t]
+    lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.kda_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_device_errors.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32]
     lib.kda_device_errors.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]

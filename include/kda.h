@@ -243,6 +243,42 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
                   const void *state_in, void *state_out, float *out, void *stream, int32_t state_dtype);
 
 /*
+ * kda_bwd -- gradients of kda_fwd (training). The released FlashKDA kernels run the
+ * forward only, and training still goes through the Triton implementation (kucoin.com
+ * news flash on the FlashKDA release); this is the backward of the operation at the top
+ * of this file, derived by the chain rule through its token recurrence. Given the
+ * gradient d_out of a loss with respect to out and d_final_state with respect to
+ * final_state, it writes the gradients of that loss with respect to every input:
+ *
+ *   q, k, v, g, beta, scale, cu_seqlens, num_seqs, total_tokens, num_heads, head_dim,
+ *   initial_state   as for kda_fwd (g fp32 only; initial_state fp32 or NULL = zeros)
+ *   d_out           fp32 [T, H, 128] (required when T > 0)
+ *   d_final_state   fp32 [N, H, 128, 128] or NULL (zeros: the loss does not read the
+ *                   final state)
+ *   dq, dk, dv, dg  fp32 [T, H, 128] (required when T > 0; every row of a sequence is
+ *                   written). dg_t is 0 where g_t < -5: there the decay is the constant
+ *                   exp(-5); at g_t = -5 it is the derivative from above.
+ *   dbeta           fp32 [T, H] (required when T > 0)
+ *   d_initial_state fp32 [N, H, 128, 128] or NULL (not written). Written even where
+ *                   initial_state is NULL (the gradient with respect to a zero state).
+ *   workspace       device scratch of kda_bwd_workspace_bytes() bytes, or NULL: then the
+ *                   library allocates it stream-ordered on `stream`. It holds the state
+ *                   before every KDA_BWD_BLOCK-th token of each chain (64 KiB each) and,
+ *                   per (sequence, head), the states before each token of one block.
+ *
+ * The outputs must not overlap the inputs or each other. cu_seqlens is sanitised on the
+ * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). Returns KDA_OK or a kda_status code
+ * (host-side checks before anything is enqueued). Inputs are not modified.
+ */
+#define KDA_BWD_BLOCK 32
+size_t kda_bwd_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
+int kda_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
+            const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
+            int32_t head_dim, const float *initial_state, const float *d_out, const float *d_final_state,
+            float *dq, float *dk, float *dv, float *dg, float *dbeta, float *d_initial_state, void *stream,
+            void *workspace, size_t workspace_bytes);
+
+/*
  * kda_device_errors -- the device error word of the current device: the OR of the
  * KDA_DEVERR_* bits that kernels of every call on this device (any variant, with or
  * without a caller workspace, kda_fwd included) have raised since it was last cleared.

@@ -164,3 +164,33 @@ def test_launch_plan():
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "recurrent")] == ["recurrent"]
+
+
+def bwd_call(lib, **over):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, scale=0.088, cu=P, N=1, T=16, H=2, D=128, s0=None, do=P,
+             dsf=None, dq=P, dk=P, dv=P, dg=P, db=P, ds0=None, ws=ctypes.c_void_p(256), wsb=10)
+    a.update(over)
+    return lib.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["scale"], a["cu"], a["N"], a["T"],
+                       a["H"], a["D"], a["s0"], a["do"], a["dsf"], a["dq"], a["dk"], a["dv"], a["dg"],
+                       a["db"], a["ds0"], None, a["ws"], a["wsb"])
+
+
+def test_bwd_validation_errors(lib):
+    assert bwd_call(lib, D=64) == 3
+    assert bwd_call(lib, scale=float("nan")) == 3
+    assert bwd_call(lib, N=0) == 2
+    assert bwd_call(lib, T=-1) == 2
+    assert bwd_call(lib, cu=None, N=2) == 2
+    for name in ("q", "g", "beta", "do", "dq", "dk", "dv", "dg", "db"):
+        assert bwd_call(lib, **{name: None}) == 1, name
+    assert bwd_call(lib) == 4                         # workspace too small
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.kda_bwd_workspace_bytes(0, 16, 1) == 0
+    N, T, H = 8, 8192, 16
+    state = 128 * 128 * 4
+    b = lib.kda_bwd_workspace_bytes(N, T, H)
+    # a state per block of KDA_BWD_BLOCK tokens and head, and a block of states per chain
+    assert b >= (T // 32) * H * state + N * H * 32 * state
+    assert "#define KDA_BWD_BLOCK 32" in open(HEADER).read()
