@@ -27,6 +27,10 @@ reported as "cold".
 With --decode N a step is one kda_decode call: one token for each of N sequences,
 the fp32 state updated in place, as in a decode loop; that mode prints its own
 JSON line (decode tokens/s, roofline against HBM for the state traffic).
+
+With --backward a step is one kda_bwd call (all gradients) over the --config workload;
+that mode prints its own JSON line (backward tokens/s), with parity of sampled chains
+against the backward oracle.
 """
 import argparse
 import ctypes
@@ -349,6 +353,90 @@ def bench_decode(args, dev):
     print(json.dumps(res), flush=True)
 
 
+BWD_METRIC = "KDA backward (all gradients) tokens/s, 1 MI355X (dk=dv=128)"
+# Algorithmic bytes of the backward per token-head: q, k, v bf16 (3 x 256) + g, d_out fp32
+# (2 x 512) + beta (4) read; dq, dk, dv, dg fp32 (4 x 512) + dbeta (4) written. Plus 64 KiB
+# per (sequence, head) for the initial state, the final-state gradient and d_initial_state.
+BWD_BYTES_PER_TOKEN_HEAD = 3 * 256 + 2 * 512 + 4 + 4 * 512 + 4
+
+
+def bench_backward(args, dev):
+    """Backward step: kda_bwd over the whole --config workload per step."""
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+
+    cfg = args.config
+    log(f"[bench] backward, config {cfg}: {synth.CONFIGS[cfg]['name']}")
+    w = synth.config_workload(cfg)
+    d = synth.to_device(w, dev)
+    rng = np.random.Generator(np.random.PCG64(5000 + cfg))
+    do_h = rng.standard_normal((w.T, w.H, 128)).astype(np.float32)
+    dsf_h = rng.standard_normal((w.N, w.H, 128, 128)).astype(np.float32) * np.float32(0.1)
+    do, dsf = torch.from_numpy(do_h).to(dev), torch.from_numpy(dsf_h).to(dev)
+    ws = torch.empty(kda.native.load_library().kda_bwd_workspace_bytes(w.N, w.T, w.H), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        return kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], do, d["scale"], d["cu_seqlens"],
+                       d["initial_state"], dsf, workspace=ws)
+
+    for _ in range(args.warmup):
+        gr = step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record()
+        gr = step()
+        b.record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    alg = w.T * w.H * BWD_BYTES_PER_TOKEN_HEAD + w.N * w.H * STATE_BYTES * (3 if w.initial_state is not None else 2)
+    achieved = alg / (call_ms / 1e3) / 1e9
+    res = {"metric": BWD_METRIC, "value": round(w.T / (ms_per_step / 1e3), 1), "unit": "tokens/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+           "data": "synthetic (seeded; bf16 q/k/v, fp32 g/beta/d_out/final-state gradient)",
+           "config": {"workload": synth.CONFIGS[cfg]["name"] + ", backward", "num_seqs": w.N,
+                      "total_tokens": w.T, "num_heads": w.H, "dk": 128, "dv": 128},
+           "roofline": {"bound": "hbm", "kernel": "bwd", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                        "alg_bytes_per_launch": alg, "avg_call_ms": round(call_ms, 4)},
+           "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        import oracle
+        # the first two chains of the first sequence, on the oracle (one thread each)
+        n_tok = int(w.cu_seqlens[1])
+        heads = [0, 1] if w.H > 1 else [0]
+        sub = dict(q=w.q_f32()[:n_tok, heads].astype(np.float64), k=w.k_f32()[:n_tok, heads].astype(np.float64),
+                   v=w.v_f32()[:n_tok, heads].astype(np.float64), g=w.g[:n_tok, heads].astype(np.float64),
+                   beta=w.beta[:n_tok, heads].astype(np.float64), scale=float(w.scale),
+                   cu_seqlens=np.array([0, n_tok], dtype=np.int64),
+                   initial_state=None if w.initial_state is None else w.initial_state[:1, heads].astype(np.float64))
+        t0 = time.perf_counter()
+        ref = oracle.kda_backward(**sub, d_out=do_h[:n_tok, heads], d_final_state=dsf_h[:1, heads],
+                                  threads=len(heads))
+        dt = time.perf_counter() - t0
+        got = {n: gr[n].cpu().numpy() for n in ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")}
+        par = {}
+        ok = True
+        for n, v in got.items():
+            v = v[:1, heads] if n == "d_initial_state" else v[:n_tok, heads]
+            m = synth.parity(v, ref[n])
+            par[n] = {k: m[k] for k in ("rel_l2", "max_abs_rms")}
+            ok &= synth.passes(m)
+        par["pass"] = ok
+        res["parity"] = par
+        th = n_tok * len(heads)
+        res["cpu_baseline"] = {"value": round(th / dt / w.H, 1), "unit": "tokens/s", "cores": len(heads),
+                               "kind": "oracle",
+                               "sample": f"{len(heads)} of {w.N * w.H} chains ({th} token-heads), fp64, "
+                                         f"{dt:.2f} s wall, scaled to tokens of {w.H} heads"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -360,6 +448,8 @@ def main():
     ap.add_argument("--decode", type=int, default=0, metavar="N",
                     help="benchmark the decode step over N sequences instead of a prefill config")
     ap.add_argument("--heads", type=int, default=32, help="heads of the --decode workload")
+    ap.add_argument("--backward", action="store_true",
+                    help="benchmark the backward (kda_bwd) over the --config workload instead")
     ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"],
                     help="state element type in HBM (bf16: the BF16-state form; prefill initial/final "
                          "state or the --decode state)")
@@ -397,6 +487,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.decode:
         bench_decode(args, dev)
+        return
+    if args.backward:
+        bench_backward(args, dev)
         return
     res = run_prefill(args.config, args, dev, cpu=not args.no_cpu_baseline)
     if args.config != GATED_CONFIG and not args.no_gated:

@@ -502,20 +502,20 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
 }
 
 // Backward workspace: the head of the forward's (chunk offsets at KDA_BWD_BLOCK tokens,
-// order, error word, sanitised offsets), a state per block of KDA_BWD_BLOCK tokens and
-// head, and KDA_BWD_BLOCK states per (sequence, head).
-static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *buf, size_t *total) {
+// order, error word, sanitised offsets), then a state per block of KDA_BWD_BLOCK tokens
+// and head.
+static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *total) {
     if (!shape_ok(N, T, H)) return false;
+    if (max_chunks(N, T, KDA_BWD_BLOCK) * H > (int64_t)1 << 31) return false;
     const Layout L = ws_layout(N, T, H, KDA_VARIANT_FUSED, 1, 0);
     *ck = L.total;
-    *buf = *ck + align_up((size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES);
-    *total = *buf + (size_t)N * H * KDA_BWD_BLOCK * STATE_BYTES;
+    *total = *ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES;
     return true;
 }
 
 size_t kda_bwd_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads) {
-    size_t ck = 0, buf = 0, total = 0;
-    return bwd_layout(num_seqs, total_tokens, num_heads, &ck, &buf, &total) ? total : 0;
+    size_t ck = 0, total = 0;
+    return bwd_layout(num_seqs, total_tokens, num_heads, &ck, &total) ? total : 0;
 }
 
 int kda_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
@@ -523,12 +523,12 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
             int32_t head_dim, const float *initial_state, const float *d_out, const float *d_final_state,
             float *dq, float *dk, float *dv, float *dg, float *dbeta, float *d_initial_state, void *stream,
             void *workspace, size_t workspace_bytes) {
-    static_assert(KDA_BWD_BLOCK == 32, "block of the backward kernel");
+
     if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    size_t ck_at = 0, buf_at = 0, total = 0;
-    if (!bwd_layout(N, T, H, &ck_at, &buf_at, &total)) return KDA_ERR_SHAPE;
+    size_t ck_at = 0, total = 0;
+    if (!bwd_layout(N, T, H, &ck_at, &total)) return KDA_ERR_SHAPE;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (T > 0 && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg || !dbeta))
         return KDA_ERR_NULL;
@@ -553,7 +553,7 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     if (kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, KDA_BWD_BLOCK, st) != hipSuccess ||
         kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale, cus, chunk_off,
                         N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
-                        (float *)(ws + ck_at), (float *)(ws + buf_at), st) != hipSuccess)
+                        (float *)(ws + ck_at), st) != hipSuccess)
         rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;

@@ -14,215 +14,352 @@
 //   dS1 = dS + k du^T;          dk += S1 du;      dg_i = sum_j S1_ij dS1_ij (g_i >= -5)
 //   dS = Diag(a) dS1
 //
-// One workgroup per (sequence, head): the state and its gradient (fp32, 128 x 129:
-// one padding column makes both row and column walks free of LDS bank conflicts)
-// live in LDS; each step is a few elementwise passes and reductions over rows or
-// columns of the two tiles. The reverse walk needs the state before every token: a
-// forward pass stores a checkpoint every BLK tokens in the workspace, then, block by
-// block from the last, the tokens of a block are recomputed forward from their
-// checkpoint with the state before each token stored to a per-chain buffer of BLK
-// states, and walked backwards from it. Work per token is O(dk dv) on the vector
-// units: this kernel is correct and simple, not fast (no MFMA, one chain per CU).
+// Every value column j of the state evolves on its own (u_j, d_j, dd_j and du_j read
+// column j only); dq, dk, dg and dbeta sum over all columns. So a wave owns 16 value
+// columns of one (sequence, head) chain, its state and state gradient in registers (lane
+// l: key rows l and l + 64, 32 values each): sums over columns stay inside a lane, sums
+// over rows (u, dd) are one butterfly across the wave. Four waves make a block (64
+// columns), two blocks a chain; the waves of a block add their row gradients through
+// LDS, and the two blocks add theirs into zeroed outputs with one atomic add each (two
+// addends onto zero: the result does not depend on their order).
+//
+// The reverse walk needs the state before every token: a forward pass stores the state
+// every BLK tokens in the workspace, then, block by block from the last, the BLK states
+// of a block are recomputed from its checkpoint into registers and walked backwards.
+// Work per token is O(dk dv) on the vector units (no MFMA): a token loop, not the
+// chunked form; one chain occupies two CUs for the length of its sequence.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "kda.h"
-#include "kda_launch.hpp"
+#include "kda_device.hpp"
 
 namespace kda {
 namespace {
 
-constexpr int D = KDA_HEAD_DIM;
-constexpr int NT = 256;
-constexpr int LD = D + 1;        // padded row of the LDS tiles
+constexpr int BLK = KDA_BWD_BLOCK;      // tokens per checkpoint
+constexpr int WAVES = 4;                // waves per block: 64 value columns
+constexpr int HALVES = D / (16 * WAVES);
 constexpr float LB = KDA_LOWER_BOUND;
+static_assert(HALVES == 2, "two blocks per chain: the atomic sums have two addends");
 
-struct BwdLds {
-    float S[D * LD];     // the state (S_{t-1}, then S1 in place)
-    float dS[D * LD];    // dL/dS_t, then dS1, then dL/dS_{t-1}
-    float q[D], k[D], v[D], e[D], g[D], dout[D];
-    float u[D], r[D], d[D], dd[D], du[D];
-    float part[2][D];    // partial sums of the two halves of a reduction
-    float dot;           // d . do
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Sum over the 64 lanes of x[c] for 16 columns c: returns, in every lane l, the total of
+// column col_of_lane(l). A reduce-scatter in four halving steps, each pairing a lane with
+// one that keeps the other half of its columns (lanes l and l ^ 32 by a 32-lane swap, rows
+// of 16 lanes by a 16-lane swap, then within a row its mirror image and that of its
+// half), then two all-reduce steps within each quad. No step goes through LDS.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_QUAD_2301 = 0x4e, DPP_QUAD_1032 = 0xb1;   // quad_perm [2,3,0,1], [1,0,3,2]
+
+__device__ __forceinline__ float colsum16(const float (&x)[16], int lane) {
+    float y[8], z[4], w[2];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {   // lanes < 32 keep columns 0..7, the others 8..15
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[m]), __float_as_uint(x[8 + m]), false, false);
+        y[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {   // even rows of 16 lanes keep the lower four, odd rows the upper
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[m]), __float_as_uint(y[4 + m]), false, false);
+        z[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    const bool b3 = lane & 8, b2 = lane & 4;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {   // lane i of a row pairs with lane 15 - i
+        const float keep = b3 ? z[2 + m] : z[m], give = b3 ? z[m] : z[2 + m];
+        w[m] = keep + dpp<DPP_ROW_MIRROR>(give);
+    }
+    // lane i of a half-row pairs with lane 7 - i
+    float s = (b2 ? w[1] : w[0]) + dpp<DPP_ROW_HALF_MIRROR>(b2 ? w[0] : w[1]);
+    s += dpp<DPP_QUAD_2301>(s);
+    s += dpp<DPP_QUAD_1032>(s);
+    return s;
+}
+// the column whose total colsum16 leaves in lane l, and a lane that holds column c
+__device__ __forceinline__ int col_of_lane(int l) {
+    return ((l >> 5) & 1) * 8 + ((l >> 4) & 1) * 4 + ((l >> 3) & 1) * 2 + ((l >> 2) & 1);
+}
+__host__ __device__ constexpr int lane_of_col(int c) {
+    return ((c >> 3) & 1) << 5 | ((c >> 2) & 1) << 4 | ((c >> 1) & 1) << 3 | (c & 1) << 2;
+}
+// the 16 column totals, uniform across the wave
+__device__ __forceinline__ void broadcast16(float s, float (&out)[16]) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) out[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), lane_of_col(c)));
+}
+
+struct Tok {          // one token's inputs, as this lane needs them
+    float k[2], q[2], e[2], g[2];   // key rows l, l + 64
+    float v[16];                     // the wave's 16 value columns
     float beta;
 };
 
-// thread -> column tid % 128, rows [64 (tid / 128), +64): a wave's accesses to one row
-// are 64 consecutive words
-__device__ __forceinline__ int col_of(int tid) { return tid & (D - 1); }
-__device__ __forceinline__ int row0_of(int tid) { return (tid >> 7) * 64; }
-
-// sum over rows i of X[i][j] w[i], for column j = tid % 128 (both halves), into out[j]
-__device__ __forceinline__ void reduce_rows(const float *X, const float *w, float *out, BwdLds &L) {
-    const int tid = threadIdx.x, j = col_of(tid), i0 = row0_of(tid);
-    float acc = 0.f;
-    for (int i = i0; i < i0 + 64; ++i) acc = fmaf(X[i * LD + j], w[i], acc);
-    L.part[tid >> 7][j] = acc;
-    __syncthreads();
-    if (tid < D) out[tid] = L.part[0][tid] + L.part[1][tid];
-    __syncthreads();
-}
-
-// sum over columns j of X[i][j] w[j], for row i = tid % 128 (both halves of j): returns it
-// in threads 0..127
-__device__ __forceinline__ float reduce_cols(const float *X, const float *w, BwdLds &L) {
-    const int tid = threadIdx.x, i = tid & (D - 1), j0 = (tid >> 7) * 64;
-    float acc = 0.f;
-    for (int j = j0; j < j0 + 64; ++j) acc = fmaf(X[i * LD + j], w[j], acc);
-    L.part[tid >> 7][i] = acc;
-    __syncthreads();
-    const float s = tid < D ? L.part[0][tid] + L.part[1][tid] : 0.f;
-    __syncthreads();
-    return s;
-}
-
-__device__ __forceinline__ void load_tile(float *X, const float *src) {
-    const int tid = threadIdx.x, j = col_of(tid), i0 = row0_of(tid);
-    for (int i = i0; i < i0 + 64; ++i) X[i * LD + j] = src ? src[(int64_t)i * D + j] : 0.f;
-}
-__device__ __forceinline__ void store_tile(float *dst, const float *X) {
-    const int tid = threadIdx.x, j = col_of(tid), i0 = row0_of(tid);
-    for (int i = i0; i < i0 + 64; ++i) dst[(int64_t)i * D + j] = X[i * LD + j];
-}
-
-// inputs of token row th (= t H + h) into the LDS vectors
-__device__ __forceinline__ void load_token(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
-                                           const float *beta, const float *dout, int64_t th, BwdLds &L) {
-    const int tid = threadIdx.x;
-    if (tid < D) {
-        const int64_t o = th * D + tid;
-        L.q[tid] = __uint_as_float((uint32_t)q[o] << 16);
-        L.k[tid] = __uint_as_float((uint32_t)k[o] << 16);
-        L.v[tid] = __uint_as_float((uint32_t)v[o] << 16);
-        const float gi = g[o];
-        L.g[tid] = gi;
-        L.e[tid] = __expf(fmaxf(gi, LB));
-        if (dout) L.dout[tid] = dout[o];
+__device__ __forceinline__ void load_tok(Tok &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                         const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                         const float *__restrict__ beta, int64_t th, int c0, int lane) {
+    const int64_t o = th * D;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        x.k[r] = bf16f(k[o + lane + 64 * r]);
+        x.q[r] = bf16f(q[o + lane + 64 * r]);
+        x.g[r] = g[o + lane + 64 * r];
+        x.e[r] = __expf(fmaxf(x.g[r], LB));
     }
-    if (tid == 0) L.beta = beta[th];
-    __syncthreads();
-}
-
-// one token forward on the LDS state: S <- S1 + k d^T (u, r, d left in LDS)
-__device__ __forceinline__ void fwd_token(BwdLds &L) {
-    const int tid = threadIdx.x, j = col_of(tid), i0 = row0_of(tid);
-    for (int i = i0; i < i0 + 64; ++i) L.S[i * LD + j] *= L.e[i];
-    __syncthreads();
-    reduce_rows(L.S, L.k, L.u, L);
-    if (tid < D) {
-        L.r[tid] = L.v[tid] - L.u[tid];
-        L.d[tid] = L.beta * L.r[tid];
+    const uint4 *vp = (const uint4 *)(v + o + c0);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const uint4 w = vp[hh];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x.v[8 * hh + 2 * i] = __uint_as_float(u[i] << 16);
+            x.v[8 * hh + 2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
     }
-    __syncthreads();
-    for (int i = i0; i < i0 + 64; ++i) L.S[i * LD + j] = fmaf(L.k[i], L.d[j], L.S[i * LD + j]);
-    __syncthreads();
+    x.beta = beta[th];
 }
 
-// State checkpoints: chunk_off[n] (blocks of BLK tokens before sequence n) indexes ck,
-// [blocks, H, 128, 128]; buf holds BLK states per (sequence, head).
-constexpr int BLK = 32;
+// S <- S1 + k d^T with S1 = Diag(e) S: one token forward on this wave's columns
+__device__ __forceinline__ void fwd_step(float (&S)[2][16], const Tok &x, int lane) {
+    float p[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        S[0][c] *= x.e[0];
+        S[1][c] *= x.e[1];
+        p[c] = fmaf(S[1][c], x.k[1], S[0][c] * x.k[0]);
+    }
+    float u[16];
+    broadcast16(colsum16(p, lane), u);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const float d = x.beta * (x.v[c] - u[c]);
+        S[0][c] = fmaf(x.k[0], d, S[0][c]);
+        S[1][c] = fmaf(x.k[1], d, S[1][c]);
+    }
+}
 
-__global__ __launch_bounds__(NT) void bwd_kernel(
+// this lane's rows l, l + 64 of columns [c0, c0 + 16) of a 128 x 128 fp32 state (zeros
+// for a NULL source)
+__device__ __forceinline__ void load_slice(float (&S)[2][16], const float *src, int c0, int lane) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        if (!src) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) S[r][c] = 0.f;
+            continue;
+        }
+        const float4 *p = (const float4 *)(src + (int64_t)(lane + 64 * r) * D + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 f = p[i];
+            S[r][4 * i] = f.x, S[r][4 * i + 1] = f.y, S[r][4 * i + 2] = f.z, S[r][4 * i + 3] = f.w;
+        }
+    }
+}
+__device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][16], int c0, int lane) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        float4 *p = (float4 *)(dst + (int64_t)(lane + 64 * r) * D + c0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = make_float4(S[r][4 * i], S[r][4 * i + 1], S[r][4 * i + 2], S[r][4 * i + 3]);
+    }
+}
+
+struct BwdLds {
+    float part[2][WAVES][3][D];   // per-wave dq, dk, dg of a token (double-buffered by token)
+    float pb[2][WAVES];           // per-wave dbeta
+};
+
+// grid: 2 blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds a
+// state per block and head
+__global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ chunk_off, int N, int T, int H, const float *__restrict__ s0,
-    const float *__restrict__ dout, const float *__restrict__ dsf, float *__restrict__ dq,
-    float *__restrict__ dk, float *__restrict__ dv, float *__restrict__ dg, float *__restrict__ dbeta,
-    float *__restrict__ ds0, float *__restrict__ ck, float *__restrict__ buf) {
-    extern __shared__ __attribute__((aligned(16))) char lds_raw[];
-    BwdLds &L = *(BwdLds *)lds_raw;
-    const int h = blockIdx.x % H, n = blockIdx.x / H;
-    const int tid = threadIdx.x, j = col_of(tid), i0 = row0_of(tid);
-    const int64_t bos = cu ? cu[n] : 0, eos = cu ? cu[n + 1] : T;
-    const int64_t len = eos - bos;
-    const int nblk = (int)((len + BLK - 1) / BLK);
+    const int32_t *__restrict__ chunk_off, int H, const float *__restrict__ s0, const float *__restrict__ dout,
+    const float *__restrict__ dsf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
+    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck) {
+    __shared__ BwdLds L;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x, HALVES);
+    const int half = bid % HALVES, chain = bid / HALVES;
+    const int h = chain % H, n = chain / H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int c0 = 64 * half + 16 * wave;
+    const int64_t bos = cu[n], eos = cu[n + 1];
+    const int nblk = (int)((eos - bos + BLK - 1) / BLK);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
-    float *ckc = ck + ((int64_t)chunk_off[n] * H + h) * D * D;   // this chain's block b: ckc + b H D D
-    float *bufc = buf + ((int64_t)n * H + h) * BLK * D * D;
+    const int64_t ck_stride = (int64_t)H * D * D;
+    float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
+    auto tok = [&](Tok &x, int64_t t) { load_tok(x, q, k, v, g, beta, t * H + h, c0, lane); };
 
-    // ---- forward: a checkpoint before every block of BLK tokens
-    load_tile(L.S, s0 ? s0 + sbase : nullptr);
-    __syncthreads();
-    for (int64_t t = bos; t < eos; ++t) {
-        if ((t - bos) % BLK == 0) store_tile(ckc + ((t - bos) / BLK) * H * D * D, L.S);
-        load_token(q, k, v, g, beta, nullptr, t * H + h, L);
-        fwd_token(L);
+    // ---- forward: the state before every BLK-th token (inputs loaded one token ahead)
+    float S[2][16];
+    load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
+    if (bos < eos) {
+        Tok x;
+        tok(x, bos);
+        for (int64_t t = bos; t < eos; ++t) {
+            if ((t - bos) % BLK == 0) store_slice(ckc + ((t - bos) / BLK) * ck_stride, S, c0, lane);
+            Tok nx;
+            tok(nx, t + 1 < eos ? t + 1 : t);
+            fwd_step(S, x, lane);
+            x = nx;
+        }
     }
 
-    // ---- backward, block by block from the last
-    load_tile(L.dS, dsf ? dsf + sbase : nullptr);
-    __syncthreads();
+    // ---- backward, block by block from the last. The loads of a block, in order: the
+    // inputs of its first nin - 1 tokens (recomputing the states before each token), then
+    // those of its nin tokens from the last (the reverse walk); each is issued one step
+    // before it is used.
+    float dS[2][16];
+    load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
+    int par = 0;
     for (int b = nblk - 1; b >= 0; --b) {
-        const int64_t tb = bos + (int64_t)b * BLK, te = min(eos, tb + BLK);
-        load_tile(L.S, ckc + (int64_t)b * H * D * D);
-        __syncthreads();
-        for (int64_t t = tb; t < te; ++t) {      // the state before each token of the block
-            store_tile(bufc + (t - tb) * D * D, L.S);
-            load_token(q, k, v, g, beta, nullptr, t * H + h, L);
-            fwd_token(L);
+        const int64_t tb = bos + (int64_t)b * BLK;
+        const int nin = (int)std::min((int64_t)BLK, eos - tb);
+        const int nload = 2 * nin - 1;
+        auto tok_at = [&](int sidx) -> int64_t {
+            sidx = sidx < nload ? sidx : nload - 1;
+            return tb + (sidx < nin - 1 ? sidx : 2 * nin - 2 - sidx);
+        };
+        int sidx = 0;
+        Tok x;
+        tok(x, tok_at(0));
+        float Sb[BLK][2][16];   // the state before each token of the block
+        load_slice(S, ckc + b * ck_stride, c0, lane);
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) Sb[i][r][c] = S[r][c];
+            if (i + 1 < nin) {
+                Tok nx;
+                tok(nx, tok_at(++sidx));
+                fwd_step(S, x, lane);
+                x = nx;
+            }
         }
-        for (int64_t t = te - 1; t >= tb; --t) {
-            const int64_t th = t * H + h;
-            __syncthreads();                      // every thread's last reads of S are done
-            load_tile(L.S, bufc + (t - tb) * D * D);
-            load_token(q, k, v, g, beta, dout, th, L);
-            // S1 = Diag(a) S_{t-1}; u, r, d
-            for (int i = i0; i < i0 + 64; ++i) L.S[i * LD + j] *= L.e[i];
-            __syncthreads();
-            reduce_rows(L.S, L.k, L.u, L);
-            if (tid < D) {
-                L.r[tid] = L.v[tid] - L.u[tid];
-                L.d[tid] = L.beta * L.r[tid];
-            }
-            // o_t = scale S_t^T q
-            for (int i = i0; i < i0 + 64; ++i) L.dS[i * LD + j] = fmaf(scale * L.q[i], L.dout[j], L.dS[i * LD + j]);
-            __syncthreads();
-            if (tid < 64) {   // d . do, one wave
-                float p = L.d[tid] * L.dout[tid] + L.d[tid + 64] * L.dout[tid + 64];
 #pragma unroll
-                for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-                if (tid == 0) L.dot = p;
-            }
-            const float a_i = reduce_cols(L.S, L.dout, L);       // (S1 do)_i
-            const float b_i = reduce_cols(L.dS, L.d, L);         // (dS d)_i
-            reduce_rows(L.dS, L.k, L.dd, L);                     // dd = dS^T k
-            if (tid < D) dq[th * D + tid] = scale * (a_i + L.k[tid] * L.dot);
-            if (tid < D) {
-                const float ddj = L.dd[tid];
-                dv[th * D + tid] = L.beta * ddj;
-                L.du[tid] = -L.beta * ddj;
-            }
-            if (tid < 64) {   // dbeta = dd . r, one wave
-                float p = L.dd[tid] * L.r[tid] + L.dd[tid + 64] * L.r[tid + 64];
-#pragma unroll
-                for (int off = 32; off > 0; off >>= 1) p += __shfl_xor(p, off);
-                if (tid == 0) dbeta[th] = p;
-            }
-            __syncthreads();
-            // u = S1^T k:  dS1 = dS + k du^T,  dk += S1 du
-            for (int i = i0; i < i0 + 64; ++i) L.dS[i * LD + j] = fmaf(L.k[i], L.du[j], L.dS[i * LD + j]);
-            __syncthreads();
-            const float c_i = reduce_cols(L.S, L.du, L);         // (S1 du)_i
-            // dg_i = sum_j S1_ij dS1_ij
+        for (int i = BLK - 1; i >= 0; --i) {
+            if (i >= nin) continue;
+            const int64_t th = (tb + i) * H + h;
+            float dov[16];
             {
-                const int i = tid & (D - 1), jb = (tid >> 7) * 64;
-                float acc = 0.f;
-                for (int jj = jb; jj < jb + 64; ++jj) acc = fmaf(L.S[i * LD + jj], L.dS[i * LD + jj], acc);
-                L.part[tid >> 7][i] = acc;
+                const float4 *p = (const float4 *)(dout + th * D + c0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float4 f = p[j];
+                    dov[4 * j] = f.x, dov[4 * j + 1] = f.y, dov[4 * j + 2] = f.z, dov[4 * j + 3] = f.w;
+                }
             }
+            Tok nx;
+            tok(nx, tok_at(++sidx));
+            // S1, u, r, d
+            float S1[2][16], p[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                S1[0][c] = Sb[i][0][c] * x.e[0];
+                S1[1][c] = Sb[i][1][c] * x.e[1];
+                p[c] = fmaf(S1[1][c], x.k[1], S1[0][c] * x.k[0]);
+            }
+            float u[16], r[16], d[16];
+            broadcast16(colsum16(p, lane), u);
+            float d_do = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                r[c] = x.v[c] - u[c];
+                d[c] = x.beta * r[c];
+                d_do = fmaf(d[c], dov[c], d_do);
+            }
+            // o_t = scale S_t^T q: dq, and the output's term of dS
+            float gq[2], gk[2], gg[2];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                float a = 0.f;
+                const float sq = scale * x.q[rr];
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    a = fmaf(S1[rr][c], dov[c], a);
+                    dS[rr][c] = fmaf(sq, dov[c], dS[rr][c]);
+                }
+                gq[rr] = scale * fmaf(x.k[rr], d_do, a);
+            }
+            // dd = dS^T k; dv = beta dd; du = -beta dd; dbeta = dd . r
+#pragma unroll
+            for (int c = 0; c < 16; ++c) p[c] = fmaf(dS[1][c], x.k[1], dS[0][c] * x.k[0]);
+            const float ddl = colsum16(p, lane);
+            float dd[16];
+            broadcast16(ddl, dd);
+            if ((lane & 3) == 0) dv[th * D + c0 + col_of_lane(lane)] = x.beta * ddl;
+            float pbeta = 0.f, du[16];
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                pbeta = fmaf(dd[c], r[c], pbeta);
+                du[c] = -x.beta * dd[c];
+            }
+            // dk = dS d + S1 du; dS1 = dS + k du^T; dg = rows of S1 . dS1; dS_{t-1} = Diag(e) dS1
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                float a = 0.f, bs = 0.f, gs = 0.f;
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    a = fmaf(dS[rr][c], d[c], a);
+                    dS[rr][c] = fmaf(x.k[rr], du[c], dS[rr][c]);
+                    bs = fmaf(S1[rr][c], du[c], bs);
+                    gs = fmaf(S1[rr][c], dS[rr][c], gs);
+                    dS[rr][c] *= x.e[rr];
+                }
+                gk[rr] = a + bs;
+                gg[rr] = x.g[rr] >= LB ? gs : 0.f;
+            }
+            // the block's four waves add through LDS, then one atomic add per output
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                L.part[par][wave][0][lane + 64 * rr] = gq[rr];
+                L.part[par][wave][1][lane + 64 * rr] = gk[rr];
+                L.part[par][wave][2][lane + 64 * rr] = gg[rr];
+            }
+            if (lane == 0) L.pb[par][wave] = pbeta;
             __syncthreads();
-            if (tid < D) {
-                dk[th * D + tid] = b_i + c_i;
-                const float dgi = L.part[0][tid] + L.part[1][tid];
-                dg[th * D + tid] = L.g[tid] >= LB ? dgi : 0.f;
+            for (int o = tid; o < 3 * D + 1; o += 64 * WAVES) {
+                if (o == 3 * D) {
+                    const float sb = (L.pb[par][0] + L.pb[par][1]) + (L.pb[par][2] + L.pb[par][3]);
+                    unsafeAtomicAdd(dbeta + th, sb);
+                } else {
+                    const int a = o / D, row = o % D;
+                    const float sr = (L.part[par][0][a][row] + L.part[par][1][a][row]) +
+                                     (L.part[par][2][a][row] + L.part[par][3][a][row]);
+                    float *dst = a == 0 ? dq : a == 1 ? dk : dg;
+                    unsafeAtomicAdd(dst + th * D + row, sr);
+                }
             }
-            // S1 = Diag(a) S_{t-1}: dS_{t-1} = Diag(a) dS1
-            for (int i = i0; i < i0 + 64; ++i) L.dS[i * LD + j] *= L.e[i];
+            par ^= 1;   // the next token writes the other buffer: this barrier orders its reuse
+            x = nx;
         }
     }
-    __syncthreads();
-    if (ds0) store_tile(ds0 + sbase, L.dS);
+    if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
+}
+
+// zero dq, dk, dg ([n4] float4 each) and dbeta ([nb] floats): the backward adds into them
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *dq, float4 *dk, float4 *dg, int64_t n4, float *db,
+                                                       int64_t nb) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        dq[i] = z;
+        dk[i] = z;
+        dg[i] = z;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nb; i += stride) db[i] = 0.f;
 }
 
 }  // namespace
@@ -230,13 +367,17 @@ __global__ __launch_bounds__(NT) void bwd_kernel(
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                       float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
                       const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
-                      float *dg, float *dbeta, float *ds0, float *ck, float *buf, hipStream_t st) {
-    constexpr int lds = (int)sizeof(BwdLds);
-    static_assert(lds <= 160 * 1024, "LDS");
-    static std::atomic<uint64_t> lds_set{0};
-    if (ensure_lds_limit((const void *)bwd_kernel, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)((int64_t)N * H)), dim3(NT), lds, st, q, k, v, g, beta, scale,
-                       cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0, ck, buf);
+                      float *dg, float *dbeta, float *ds0, float *ck, hipStream_t st) {
+    const int64_t th = (int64_t)T * H;
+    if (th > 0) {
+        const int64_t n4 = th * D / 4;
+        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (float4 *)dq, (float4 *)dk,
+                           (float4 *)dg, n4, dbeta, th);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)((int64_t)N * H * HALVES)), dim3(64 * WAVES), 0, st, q, k, v, g,
+                       beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0, ck);
     return hipGetLastError();
 }
 

@@ -128,13 +128,13 @@ hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
-// The backward (kda_bwd.hip): one workgroup per (sequence, head). chunk_off counts blocks of
-// bwd_block_tokens() tokens per sequence (the chunk map at that chunk length); ck holds a
-// state per block and head, buf bwd_block_tokens() states per (sequence, head).
+// The backward (kda_bwd.hip): zeroes dq, dk, dg, dbeta, then two workgroups per (sequence,
+// head). chunk_off counts blocks of bwd_block_tokens() tokens per sequence (the chunk map
+// at that chunk length); ck holds a state per block and head.
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                       float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
                       const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
-                      float *dg, float *dbeta, float *ds0, float *ck, float *buf, hipStream_t st);
+                      float *dg, float *dbeta, float *ds0, float *ck, hipStream_t st);
 int bwd_block_tokens();
 
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

@@ -263,14 +263,16 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
  *                   initial_state is NULL (the gradient with respect to a zero state).
  *   workspace       device scratch of kda_bwd_workspace_bytes() bytes, or NULL: then the
  *                   library allocates it stream-ordered on `stream`. It holds the state
- *                   before every KDA_BWD_BLOCK-th token of each chain (64 KiB each) and,
- *                   per (sequence, head), the states before each token of one block.
+ *                   before every KDA_BWD_BLOCK-th token of each chain (64 KiB each: about
+ *                   16 KiB per token-head).
  *
  * The outputs must not overlap the inputs or each other. cu_seqlens is sanitised on the
- * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). Returns KDA_OK or a kda_status code
+ * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). dq, dk, dg and dbeta are sums of two
+ * halves over the value columns, added onto zero in either order: the results are the
+ * same from run to run. Returns KDA_OK or a kda_status code
  * (host-side checks before anything is enqueued). Inputs are not modified.
  */
-#define KDA_BWD_BLOCK 32
+#define KDA_BWD_BLOCK 4
 size_t kda_bwd_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads);
 int kda_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
             const int32_t *cu_seqlens, int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
