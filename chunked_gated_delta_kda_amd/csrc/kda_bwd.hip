@@ -15,19 +15,19 @@
 //   dS = Diag(a) dS1
 //
 // Every value column j of the state evolves on its own (u_j, d_j, dd_j and du_j read
-// column j only); dq, dk, dg and dbeta sum over all columns. So a wave owns 16 value
+// column j only); dq, dk, dg and dbeta sum over all columns. So a wave owns CW = 8 value
 // columns of one (sequence, head) chain, its state and state gradient in registers (lane
-// l: key rows l and l + 64, 32 values each): sums over columns stay inside a lane, sums
-// over rows (u, dd) are one butterfly across the wave. Four waves make a block (64
-// columns), two blocks a chain; the waves of a block add their row gradients through
-// LDS, and the two blocks add theirs into zeroed outputs with one atomic add each (two
-// addends onto zero: the result does not depend on their order).
+// l: key rows l and l + 64): sums over columns stay inside a lane, sums over rows (u, dd)
+// are one reduction across the wave. Eight waves make a block (64 columns), two blocks a
+// chain; the waves of a block add their row gradients through LDS, and the two blocks add
+// theirs into zeroed outputs with one atomic add each (two addends onto zero: the result
+// does not depend on their order).
 //
 // The reverse walk needs the state before every token: a forward pass stores the state
-// every BLK tokens in the workspace, then, block by block from the last, the BLK states
-// of a block are recomputed from its checkpoint into registers and walked backwards.
-// Work per token is O(dk dv) on the vector units (no MFMA): a token loop, not the
-// chunked form; one chain occupies two CUs for the length of its sequence.
+// every BLK tokens in the workspace, then, block by block from the last, the block's
+// tokens are recomputed from its checkpoint, keeping S1 and u of each in registers, and
+// walked backwards. Work per token is O(dk dv) on the vector units (no MFMA): a token
+// loop, not the chunked form; one chain occupies two CUs for the length of its sequence.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,18 +40,14 @@ namespace kda {
 namespace {
 
 constexpr int BLK = KDA_BWD_BLOCK;      // tokens per checkpoint
-constexpr int WAVES = 4;                // waves per block: 64 value columns
-constexpr int HALVES = D / (16 * WAVES);
+constexpr int CW = 8;                   // value columns per wave
+constexpr int WAVES = 8;                // waves per block: 64 value columns
+constexpr int HALVES = D / (CW * WAVES);
 constexpr float LB = KDA_LOWER_BOUND;
 static_assert(HALVES == 2, "two blocks per chain: the atomic sums have two addends");
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// Sum over the 64 lanes of x[c] for 16 columns c: returns, in every lane l, the total of
-// column col_of_lane(l). A reduce-scatter in four halving steps, each pairing a lane with
-// one that keeps the other half of its columns (lanes l and l ^ 32 by a 32-lane swap, rows
-// of 16 lanes by a 16-lane swap, then within a row its mirror image and that of its
-// half), then two all-reduce steps within each quad. No step goes through LDS.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
@@ -59,117 +55,147 @@ __device__ __forceinline__ float dpp(float x) {
 constexpr int DPP_ROW_MIRROR = 0x140, DPP_ROW_HALF_MIRROR = 0x141;
 constexpr int DPP_QUAD_2301 = 0x4e, DPP_QUAD_1032 = 0xb1;   // quad_perm [2,3,0,1], [1,0,3,2]
 
-__device__ __forceinline__ float colsum16(const float (&x)[16], int lane) {
-    float y[8], z[4], w[2];
+// Sum over the 64 lanes of x[c] for the wave's 8 columns: returns, in every lane l, the
+// total of column col_of_lane(l). Three halving steps pair each lane with one that keeps
+// the other half of its columns (lanes l and l ^ 32 by a 32-lane swap, rows of 16 lanes
+// by a 16-lane swap, lane i of a row with lane 15 - i), then an all-reduce over each half
+// row (its mirror image, then within quads). No step goes through LDS.
+__device__ __forceinline__ float colsum8(const float (&x)[CW], int lane) {
+    float y[4], z[2];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {   // lanes < 32 keep columns 0..7, the others 8..15
-        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[m]), __float_as_uint(x[8 + m]), false, false);
+    for (int m = 0; m < 4; ++m) {   // lanes < 32 keep columns 0..3, the others 4..7
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[m]), __float_as_uint(x[4 + m]), false, false);
         y[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {   // even rows of 16 lanes keep the lower four, odd rows the upper
-        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[m]), __float_as_uint(y[4 + m]), false, false);
+    for (int m = 0; m < 2; ++m) {   // even rows keep the lower two, odd rows the upper
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(y[m]), __float_as_uint(y[2 + m]), false, false);
         z[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     }
-    const bool b3 = lane & 8, b2 = lane & 4;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {   // lane i of a row pairs with lane 15 - i
-        const float keep = b3 ? z[2 + m] : z[m], give = b3 ? z[m] : z[2 + m];
-        w[m] = keep + dpp<DPP_ROW_MIRROR>(give);
-    }
-    // lane i of a half-row pairs with lane 7 - i
-    float s = (b2 ? w[1] : w[0]) + dpp<DPP_ROW_HALF_MIRROR>(b2 ? w[0] : w[1]);
+    const bool b3 = lane & 8;
+    float s = (b3 ? z[1] : z[0]) + dpp<DPP_ROW_MIRROR>(b3 ? z[0] : z[1]);
+    s += dpp<DPP_ROW_HALF_MIRROR>(s);
     s += dpp<DPP_QUAD_2301>(s);
     s += dpp<DPP_QUAD_1032>(s);
     return s;
 }
-// the column whose total colsum16 leaves in lane l, and a lane that holds column c
-__device__ __forceinline__ int col_of_lane(int l) {
-    return ((l >> 5) & 1) * 8 + ((l >> 4) & 1) * 4 + ((l >> 3) & 1) * 2 + ((l >> 2) & 1);
-}
-__host__ __device__ constexpr int lane_of_col(int c) {
-    return ((c >> 3) & 1) << 5 | ((c >> 2) & 1) << 4 | ((c >> 1) & 1) << 3 | (c & 1) << 2;
-}
-// the 16 column totals, uniform across the wave
-__device__ __forceinline__ void broadcast16(float s, float (&out)[16]) {
+// the column whose total colsum8 leaves in lane l, and a lane that holds column c
+__device__ __forceinline__ int col_of_lane(int l) { return ((l >> 5) & 1) * 4 + ((l >> 4) & 1) * 2 + ((l >> 3) & 1); }
+__host__ __device__ constexpr int lane_of_col(int c) { return ((c >> 2) & 1) << 5 | ((c >> 1) & 1) << 4 | (c & 1) << 3; }
+// the column totals, uniform across the wave
+__device__ __forceinline__ void broadcast8(float s, float (&out)[CW]) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) out[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), lane_of_col(c)));
+    for (int c = 0; c < CW; ++c) out[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), lane_of_col(c)));
 }
 
-struct Tok {          // one token's inputs, as this lane needs them
-    float k[2], q[2], e[2], g[2];   // key rows l, l + 64
-    float v[16];                     // the wave's 16 value columns
+// One token's inputs as this lane needs them, as loaded: bf16 bits of k and q and the
+// fp32 g of key rows l and l + 64, the wave's value columns of v (bf16 bits) and d_out,
+// and beta. A step converts them (ready) only where it uses them, so that the loads
+// issued a step ahead are waited for there and not at their issue.
+struct Raw {
+    uint16_t k[2], q[2];
+    float g[2];
+    uint4 v;
+    float4 dov[CW / 4];
+    float beta;
+};
+struct Tok {
+    float k[2], q[2], e[2], g[2];
+    float v[CW], dov[CW];
     float beta;
 };
 
-__device__ __forceinline__ void load_tok(Tok &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+__device__ __forceinline__ void load_raw(Raw &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                          const uint16_t *__restrict__ v, const float *__restrict__ g,
-                                         const float *__restrict__ beta, int64_t th, int c0, int lane) {
+                                         const float *__restrict__ beta, const float *__restrict__ dout, int64_t th,
+                                         int c0, int lane) {
     const int64_t o = th * D;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        x.k[r] = bf16f(k[o + lane + 64 * r]);
-        x.q[r] = bf16f(q[o + lane + 64 * r]);
+        x.k[r] = k[o + lane + 64 * r];
+        x.q[r] = q[o + lane + 64 * r];
         x.g[r] = g[o + lane + 64 * r];
-        x.e[r] = __expf(fmaxf(x.g[r], LB));
     }
-    const uint4 *vp = (const uint4 *)(v + o + c0);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-        const uint4 w = vp[hh];
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x.v[8 * hh + 2 * i] = __uint_as_float(u[i] << 16);
-            x.v[8 * hh + 2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
-    }
+    x.v = *(const uint4 *)(v + o + c0);
     x.beta = beta[th];
+    if (dout) {
+#pragma unroll
+        for (int j = 0; j < CW / 4; ++j) x.dov[j] = ((const float4 *)(dout + o + c0))[j];
+    }
 }
 
-// S <- S1 + k d^T with S1 = Diag(e) S: one token forward on this wave's columns
-__device__ __forceinline__ void fwd_step(float (&S)[2][16], const Tok &x, int lane) {
-    float p[16];
+__device__ __forceinline__ void ready(Tok &x, const Raw &r, bool with_dout) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int i = 0; i < 2; ++i) {
+        x.k[i] = bf16f(r.k[i]);
+        x.q[i] = bf16f(r.q[i]);
+        x.g[i] = r.g[i];
+        x.e[i] = __expf(fmaxf(r.g[i], LB));
+    }
+    const uint32_t u[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x.v[2 * i] = __uint_as_float(u[i] << 16);
+        x.v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+    x.beta = r.beta;
+    if (with_dout) {
+#pragma unroll
+        for (int j = 0; j < CW / 4; ++j) {
+            x.dov[4 * j] = r.dov[j].x, x.dov[4 * j + 1] = r.dov[j].y;
+            x.dov[4 * j + 2] = r.dov[j].z, x.dov[4 * j + 3] = r.dov[j].w;
+        }
+    }
+}
+
+// S1 = Diag(e) S in place; returns this lane's part of u = S1^T k (colsum8 layout)
+__device__ __forceinline__ float decay_u(float (&S)[2][CW], const Tok &x, int lane) {
+    float p[CW];
+#pragma unroll
+    for (int c = 0; c < CW; ++c) {
         S[0][c] *= x.e[0];
         S[1][c] *= x.e[1];
         p[c] = fmaf(S[1][c], x.k[1], S[0][c] * x.k[0]);
     }
-    float u[16];
-    broadcast16(colsum16(p, lane), u);
+    return colsum8(p, lane);
+}
+// S <- S1 + k d^T with d = beta (v - u)
+__device__ __forceinline__ void write_step(float (&S)[2][CW], const Tok &x, float ul) {
+    float u[CW];
+    broadcast8(ul, u);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
+    for (int c = 0; c < CW; ++c) {
         const float d = x.beta * (x.v[c] - u[c]);
         S[0][c] = fmaf(x.k[0], d, S[0][c]);
         S[1][c] = fmaf(x.k[1], d, S[1][c]);
     }
 }
 
-// this lane's rows l, l + 64 of columns [c0, c0 + 16) of a 128 x 128 fp32 state (zeros
+// this lane's rows l, l + 64 of columns [c0, c0 + CW) of a 128 x 128 fp32 state (zeros
 // for a NULL source)
-__device__ __forceinline__ void load_slice(float (&S)[2][16], const float *src, int c0, int lane) {
+__device__ __forceinline__ void load_slice(float (&S)[2][CW], const float *src, int c0, int lane) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         if (!src) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) S[r][c] = 0.f;
+            for (int c = 0; c < CW; ++c) S[r][c] = 0.f;
             continue;
         }
         const float4 *p = (const float4 *)(src + (int64_t)(lane + 64 * r) * D + c0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < CW / 4; ++i) {
             const float4 f = p[i];
             S[r][4 * i] = f.x, S[r][4 * i + 1] = f.y, S[r][4 * i + 2] = f.z, S[r][4 * i + 3] = f.w;
         }
     }
 }
-__device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][16], int c0, int lane) {
+__device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][CW], int c0, int lane) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         float4 *p = (float4 *)(dst + (int64_t)(lane + 64 * r) * D + c0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = make_float4(S[r][4 * i], S[r][4 * i + 1], S[r][4 * i + 2], S[r][4 * i + 3]);
+        for (int i = 0; i < CW / 4; ++i)
+            p[i] = make_float4(S[r][4 * i], S[r][4 * i + 1], S[r][4 * i + 2], S[r][4 * i + 3]);
     }
 }
 
@@ -177,6 +203,18 @@ struct BwdLds {
     float part[2][WAVES][3][D];   // per-wave dq, dk, dg of a token (double-buffered by token)
     float pb[2][WAVES];           // per-wave dbeta
 };
+
+// sum of the block's WAVES partials of one output (stride apart), in a fixed order
+__device__ __forceinline__ float sum_waves(const float *p, int stride) {
+    float s[WAVES];
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s[w] = p[w * stride];
+#pragma unroll
+    for (int m = WAVES / 2; m > 0; m >>= 1)
+#pragma unroll
+        for (int w = 0; w < m; ++w) s[w] += s[w + m];
+    return s[0];
+}
 
 // grid: 2 blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds a
 // state per block and head
@@ -192,90 +230,77 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const int h = chain % H, n = chain / H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
-    const int c0 = 64 * half + 16 * wave;
+    const int c0 = 64 * half + CW * wave;
     const int64_t bos = cu[n], eos = cu[n + 1];
     const int nblk = (int)((eos - bos + BLK - 1) / BLK);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
     const int64_t ck_stride = (int64_t)H * D * D;
     float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
-    auto tok = [&](Tok &x, int64_t t) { load_tok(x, q, k, v, g, beta, t * H + h, c0, lane); };
+    auto raw = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, nullptr, t * H + h, c0, lane); };
+    auto rawd = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, dout, t * H + h, c0, lane); };
 
     // ---- forward: the state before every BLK-th token (inputs loaded one token ahead)
-    float S[2][16];
+    float S[2][CW];
     load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
     if (bos < eos) {
-        Tok x;
-        tok(x, bos);
+        Raw xr;
+        raw(xr, bos);
         for (int64_t t = bos; t < eos; ++t) {
             if ((t - bos) % BLK == 0) store_slice(ckc + ((t - bos) / BLK) * ck_stride, S, c0, lane);
-            Tok nx;
-            tok(nx, t + 1 < eos ? t + 1 : t);
-            fwd_step(S, x, lane);
-            x = nx;
+            Tok x;
+            ready(x, xr, false);
+            raw(xr, t + 1 < eos ? t + 1 : t);
+            write_step(S, x, decay_u(S, x, lane));
         }
     }
 
     // ---- backward, block by block from the last. The loads of a block, in order: the
-    // inputs of its first nin - 1 tokens (recomputing the states before each token), then
-    // those of its nin tokens from the last (the reverse walk); each is issued one step
-    // before it is used.
-    float dS[2][16];
+    // inputs of its nin tokens (recomputing S1 and u of each), then the same from the last
+    // (the reverse walk); each is issued one step before it is used.
+    float dS[2][CW];
     load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
     int par = 0;
     for (int b = nblk - 1; b >= 0; --b) {
         const int64_t tb = bos + (int64_t)b * BLK;
         const int nin = (int)std::min((int64_t)BLK, eos - tb);
-        const int nload = 2 * nin - 1;
-        auto tok_at = [&](int sidx) -> int64_t {
-            sidx = sidx < nload ? sidx : nload - 1;
-            return tb + (sidx < nin - 1 ? sidx : 2 * nin - 2 - sidx);
+        const int nload = 2 * nin;
+        auto tok_at = [&](int sx) -> int64_t {
+            sx = sx < nload ? sx : nload - 1;
+            return tb + (sx < nin ? sx : 2 * nin - 1 - sx);
         };
         int sidx = 0;
-        Tok x;
-        tok(x, tok_at(0));
-        float Sb[BLK][2][16];   // the state before each token of the block
+        Raw xr;
+        rawd(xr, tok_at(0));
+        float S1s[BLK][2][CW], us[BLK];   // S1 and u of each token of the block
         load_slice(S, ckc + b * ck_stride, c0, lane);
 #pragma unroll
         for (int i = 0; i < BLK; ++i) {
+            if (i < nin) {
+                Tok x;
+                ready(x, xr, false);
+                rawd(xr, tok_at(++sidx));
+                us[i] = decay_u(S, x, lane);
 #pragma unroll
-            for (int r = 0; r < 2; ++r)
+                for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int c = 0; c < 16; ++c) Sb[i][r][c] = S[r][c];
-            if (i + 1 < nin) {
-                Tok nx;
-                tok(nx, tok_at(++sidx));
-                fwd_step(S, x, lane);
-                x = nx;
+                    for (int c = 0; c < CW; ++c) S1s[i][r][c] = S[r][c];
+                if (i + 1 < nin) write_step(S, x, us[i]);
             }
         }
 #pragma unroll
         for (int i = BLK - 1; i >= 0; --i) {
             if (i >= nin) continue;
             const int64_t th = (tb + i) * H + h;
-            float dov[16];
-            {
-                const float4 *p = (const float4 *)(dout + th * D + c0);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float4 f = p[j];
-                    dov[4 * j] = f.x, dov[4 * j + 1] = f.y, dov[4 * j + 2] = f.z, dov[4 * j + 3] = f.w;
-                }
-            }
-            Tok nx;
-            tok(nx, tok_at(++sidx));
-            // S1, u, r, d
-            float S1[2][16], p[16];
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                S1[0][c] = Sb[i][0][c] * x.e[0];
-                S1[1][c] = Sb[i][1][c] * x.e[1];
-                p[c] = fmaf(S1[1][c], x.k[1], S1[0][c] * x.k[0]);
-            }
-            float u[16], r[16], d[16];
-            broadcast16(colsum16(p, lane), u);
+            Tok x;
+            ready(x, xr, true);
+            const float(&dov)[CW] = x.dov;
+            rawd(xr, tok_at(++sidx));
+            const float(&S1)[2][CW] = S1s[i];
+            float u[CW], r[CW], d[CW];
+            broadcast8(us[i], u);
             float d_do = 0.f;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
+            for (int c = 0; c < CW; ++c) {
                 r[c] = x.v[c] - u[c];
                 d[c] = x.beta * r[c];
                 d_do = fmaf(d[c], dov[c], d_do);
@@ -287,22 +312,23 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                 float a = 0.f;
                 const float sq = scale * x.q[rr];
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
+                for (int c = 0; c < CW; ++c) {
                     a = fmaf(S1[rr][c], dov[c], a);
                     dS[rr][c] = fmaf(sq, dov[c], dS[rr][c]);
                 }
                 gq[rr] = scale * fmaf(x.k[rr], d_do, a);
             }
             // dd = dS^T k; dv = beta dd; du = -beta dd; dbeta = dd . r
+            float p[CW];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) p[c] = fmaf(dS[1][c], x.k[1], dS[0][c] * x.k[0]);
-            const float ddl = colsum16(p, lane);
-            float dd[16];
-            broadcast16(ddl, dd);
-            if ((lane & 3) == 0) dv[th * D + c0 + col_of_lane(lane)] = x.beta * ddl;
-            float pbeta = 0.f, du[16];
+            for (int c = 0; c < CW; ++c) p[c] = fmaf(dS[1][c], x.k[1], dS[0][c] * x.k[0]);
+            const float ddl = colsum8(p, lane);
+            float dd[CW];
+            broadcast8(ddl, dd);
+            dv[th * D + c0 + col_of_lane(lane)] = x.beta * ddl;   // eight lanes per column, one value
+            float pbeta = 0.f, du[CW];
 #pragma unroll
-            for (int c = 0; c < 16; ++c) {
+            for (int c = 0; c < CW; ++c) {
                 pbeta = fmaf(dd[c], r[c], pbeta);
                 du[c] = -x.beta * dd[c];
             }
@@ -311,7 +337,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             for (int rr = 0; rr < 2; ++rr) {
                 float a = 0.f, bs = 0.f, gs = 0.f;
 #pragma unroll
-                for (int c = 0; c < 16; ++c) {
+                for (int c = 0; c < CW; ++c) {
                     a = fmaf(dS[rr][c], d[c], a);
                     dS[rr][c] = fmaf(x.k[rr], du[c], dS[rr][c]);
                     bs = fmaf(S1[rr][c], du[c], bs);
@@ -321,7 +347,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                 gk[rr] = a + bs;
                 gg[rr] = x.g[rr] >= LB ? gs : 0.f;
             }
-            // the block's four waves add through LDS, then one atomic add per output
+            // the block's waves add through LDS, then one atomic add per output
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 L.part[par][wave][0][lane + 64 * rr] = gq[rr];
@@ -330,20 +356,14 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             }
             if (lane == 0) L.pb[par][wave] = pbeta;
             __syncthreads();
-            for (int o = tid; o < 3 * D + 1; o += 64 * WAVES) {
-                if (o == 3 * D) {
-                    const float sb = (L.pb[par][0] + L.pb[par][1]) + (L.pb[par][2] + L.pb[par][3]);
-                    unsafeAtomicAdd(dbeta + th, sb);
-                } else {
-                    const int a = o / D, row = o % D;
-                    const float sr = (L.part[par][0][a][row] + L.part[par][1][a][row]) +
-                                     (L.part[par][2][a][row] + L.part[par][3][a][row]);
-                    float *dst = a == 0 ? dq : a == 1 ? dk : dg;
-                    unsafeAtomicAdd(dst + th * D + row, sr);
-                }
+            if (tid < 3 * D) {
+                const int a = tid / D, row = tid % D;
+                float *dst = a == 0 ? dq : a == 1 ? dk : dg;
+                unsafeAtomicAdd(dst + th * D + row, sum_waves(&L.part[par][0][a][row], 3 * D));
+            } else if (tid == 3 * D) {
+                unsafeAtomicAdd(dbeta + th, sum_waves(&L.pb[par][0], 1));
             }
             par ^= 1;   // the next token writes the other buffer: this barrier orders its reuse
-            x = nx;
         }
     }
     if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
