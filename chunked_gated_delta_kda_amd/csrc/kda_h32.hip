@@ -432,6 +432,41 @@ __device__ __forceinline__ void state_store(float *p, bool bf, int64_t i, float 
     }
     p[i] = x;
 }
+// The chain wave's 32 state elements (rows 16 b + 4 gq + j of one column, at p + base):
+// the element type is chosen once for all of them, so that the loads issue back to back
+// (a choice per element puts each load in a branch of its own, and the compiler then
+// waits for every load before the next one issues).
+__device__ __forceinline__ void state_tile_load(f32x4 (&S)[8], const float *p, bool bf, int64_t base, int gq) {
+    if (bf) {
+        const uint16_t *q = (const uint16_t *)p + base;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[b][j] = __uint_as_float((uint32_t)q[(int64_t)(16 * b + 4 * gq + j) * D] << 16);
+    } else {
+        const float *q = p + base;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) S[b][j] = q[(int64_t)(16 * b + 4 * gq + j) * D];
+    }
+}
+__device__ __forceinline__ void state_tile_store(float *p, bool bf, int64_t base, int gq, const f32x4 (&S)[8]) {
+    if (bf) {
+        uint16_t *q = (uint16_t *)p + base;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                q[(int64_t)(16 * b + 4 * gq + j) * D] = (uint16_t)(pack2(S[b][j], 0.f) & 0xffffu);
+    } else {
+        float *q = p + base;
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) q[(int64_t)(16 * b + 4 * gq + j) * D] = S[b][j];
+    }
+}
 
 // The paired recurrence over 32-token records: NW 16-column slices per block, per slice a
 // chain wave and two output waves (roles and SIMD placement as PairLayout), one loader
@@ -570,10 +605,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
     if (chain) {
         f32x4 S[8];
         if (sin) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) S[b][j] = state_load(sin, sin_bf, sbase + (int64_t)(16 * b + 4 * gq + j) * D);
+            state_tile_load(S, sin, sin_bf, sbase, gq);
         } else {
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = zero;
@@ -662,12 +694,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
         __builtin_amdgcn_s_waitcnt(0xc07f);     // the last snapshot is written
         sync();
         sync();
-        if (sout) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) state_store(sout, sout_bf, sbase + (int64_t)(16 * b + 4 * gq + j) * D, S[b][j]);
-        }
+        if (sout) state_tile_store(sout, sout_bf, sbase, gq, S);
         return;
     }
 
