@@ -145,7 +145,8 @@ template <int HALF, typename GT>
 __device__ __forceinline__ void prep_half(const HalfIn<GT> &in, const float *__restrict__ beta,
                                           int64_t t0, int nc, int h, int H, float scale, PrepLds &L,
                                           char *rec, f32x2 kts, f32x2 ega, f32x4 (&Wt)[8], f32x4 (&Wd)[8],
-                                          f32x4 &tbr, f32x4 &pr, f32x2 &ec, bf16x8 (&qh)[4], bf16x8 (&ql)[4]) {
+                                          f32x4 &tbr, f32x4 &pr, f32x2 &ec, bf16x8 (&qh)[4], bf16x8 (&ql)[4],
+                                          uint32_t (&kta)[2][8]) {
     const int l = threadIdx.x & 63;
     const int c0 = 2 * l;
     const int r = l & 15, gq = l >> 4;
@@ -204,17 +205,23 @@ __device__ __forceinline__ void prep_half(const HalfIn<GT> &in, const float *__r
             ktT[ch][t / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{ktv[0][ch], ktv[1][ch]}), f16x2));
         }
     }
-    // K+ transposed into LDS (operand of W); K~ straight into the record: channel c,
-    // half-local tokens 4e..4e+3 are token slots 8e + 4 HALF .. + 3 of lane 16e + c % 16
-    // of key block c / 16
+    // K+ transposed into LDS (operand of W); K~ into the record: channel c, half-local
+    // tokens 4e..4e+3 are token slots 8e + 4 HALF .. + 3 of lane 16e + c % 16 of key block
+    // c / 16. Half a's K~ waits in kta for half b's, so that each 16-byte slot is stored
+    // whole (two 8-byte halves stored apart leave lines partly written in between).
 #pragma unroll
     for (int ch = 0; ch < 2; ++ch) {
         const int c = c0 + ch;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             *(uint2 *)&L.kpt[PrepLds::at_t(c, 4 * e)] = uint2{kpT[ch][2 * e], kpT[ch][2 * e + 1]};
-            *(uint2 *)(rec + RecH::KT + (c >> 4) * 1024 + (16 * e + (c & 15)) * 16 + HALF * 8) =
-                uint2{ktT[ch][2 * e], ktT[ch][2 * e + 1]};
+            if (HALF == 0) {
+                kta[ch][2 * e] = ktT[ch][2 * e];
+                kta[ch][2 * e + 1] = ktT[ch][2 * e + 1];
+            } else {
+                *(uint4 *)(rec + RecH::KT + (c >> 4) * 1024 + (16 * e + (c & 15)) * 16) =
+                    uint4{kta[ch][2 * e], kta[ch][2 * e + 1], ktT[ch][2 * e], ktT[ch][2 * e + 1]};
+            }
         }
     }
     float br = 0.f;
@@ -333,7 +340,8 @@ __device__ __forceinline__ void prep_h32(const uint16_t *__restrict__ q, const u
     f32x4 Wt[8], Wd[8], tba, pa, tbb, pb;
     f32x2 ea, ebx;
     bf16x8 qh[4], ql[4];
-    prep_half<0>(ia, beta, t0, nca, h, H, scale, L, rec, eb, f32x2{1.f, 1.f}, Wt, Wd, tba, pa, ea, qh, ql);
+    uint32_t kta[2][8];
+    prep_half<0>(ia, beta, t0, nca, h, H, scale, L, rec, eb, f32x2{1.f, 1.f}, Wt, Wd, tba, pa, ea, qh, ql, kta);
     *(f32x2 *)(rec + RecH::EGP + egp_index(c0) * 4) = f32x2{ea.x * eb.x, ea.y * eb.y};
     // K-_a as an MFMA operand (row = token of a, k-slots = keys in the state permutation)
     bf16x8 kah[4], kal[4];
@@ -352,7 +360,7 @@ __device__ __forceinline__ void prep_h32(const uint16_t *__restrict__ q, const u
     // ---- half b (W and Q+ scaled by D_a)
     f32x4 Wb[8], unused[8];
     prep_half<1>(ib, beta, t0 + C, ncb, h, H, scale, L, rec, f32x2{1.f, 1.f}, ega, Wb, unused, tbb, pb, ebx,
-                 qh, ql);
+                 qh, ql, kta);
 
     // ---- cross terms, transposed products so that the results land in R layout
     // M = (W_b D_a) K-_a^T and P_ba = (Q+_b D_a) K-_a^T, 3-term split products
