@@ -106,11 +106,34 @@ int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
         if (p >= 1 && p <= MAX_PARTS) return p;
     }
     if (waves != 101 && waves != 401) return 1;
+    // Over 32-token records, pass 2 can run the two-slice form (4 blocks per part), which
+    // fits twice the parts in one round: with chains of 128 such chunks or more per part
+    // that pays. Measured on MI355X (ms; P parts with pass 2 one-slice | P parts two-slice):
+    // 65536 tokens x 8 heads 0.964 (4) | 0.862 (8); 32768 x 8 0.520 (4) | 0.472 (8); but
+    // two sequences of 16384 x 4 0.262 (4) | 0.272 (8), 16384 x 4 0.178 (8) | 0.188 (8).
+    // With 16 chains (ms, whole | 4 parts two-slice): 2 x 65536 x 8 1.99 | 1.59; 2 x 32768 x 8
+    // 1.01 | 0.83; 4 x 16384 x 4 0.522 | 0.446; 65536 x 16 1.98 | 1.58; 32768 x 16 1.00 | 0.83.
+    if (waves == 401) {
+        const int64_t p2 = 64 / (N * H), per_seq = T / N / 32;
+        if (p2 >= 3 && per_seq / (p2 < MAX_PARTS ? p2 : MAX_PARTS) >= 128) return (int)(p2 < MAX_PARTS ? p2 : MAX_PARTS);
+    }
     int64_t p = 32 / (N * H);
     const int64_t by_len = max_chunks(N, T) / 64;
     if (by_len < p) p = by_len;
     if (p > MAX_PARTS) p = MAX_PARTS;
     return p >= 3 ? (int)p : 1;
+}
+
+// Recurrence form of pass 2 of the recurrence over parts (32-token records): 401 (one
+// 16-column slice per block, 8 blocks per part) while the parts fit one round of the
+// 256 CUs that way, else 402 (two slices, 4 blocks per part; see split_parts).
+// KDA_PARTS_FORM overrides, for tuning.
+int parts_pass2_waves(int64_t N, int64_t H, int P) {
+    if (const char *e = std::getenv("KDA_PARTS_FORM")) {
+        const int w = std::atoi(e);
+        if (w == 401 || w == 402) return w;
+    }
+    return N * H * P * 8 <= 256 ? 401 : 402;
 }
 
 Layout ws_layout(int64_t N, int64_t T, int64_t H, int variant, int segments, int waves, int parts = 1) {
@@ -458,7 +481,8 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&
                  around(st, [&] {
                      return kda::launch_parts(recs, v16, cus, chunk_off, order, N, T, H, parts, initial_state, out,
-                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, h32, s_bf16, st);
+                                              final_state, vcu, vco, vorder, ident, rb, ri, sin, h32, s_bf16,
+                                              parts_pass2_waves(N, H, parts), st);
                  });
         } else if (segs == 1) {
             ok = around(st, [&] { return prep(0, kda::SEG_ONE); }) &&

@@ -511,8 +511,9 @@ struct PairHLds {
 // otherwise, and leaves to sfin after its last chunk and to `carry` otherwise. Sequences
 // without chunks copy s0 to sfin in the launch of the first segment. With zero_v the chain
 // runs as if every v were 0 (the part of the chain linear in the entry state; outputs then
-// not valid).
-template <int NW, int NSLOT>
+// not valid). Without OUT only the states are produced: the output waves only keep the
+// barriers and the chain publishes no snapshots.
+template <int NW, int NSLOT, bool OUT = true>
 __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char *__restrict__ recs,
                                                 const uint16_t *__restrict__ v, const int32_t *__restrict__ cu,
                                                 const int32_t *__restrict__ chunk_off,
@@ -605,7 +606,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
         return;
     }
 
-    if (idle) {
+    if (idle || (!OUT && !chain)) {
         for (int it = 0; it < nch + 2; ++it) sync();
         return;
     }
@@ -673,10 +674,12 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
             Sd[5] = decay_block<5>(S[5], x.e);
             Sd[6] = decay_block<6>(S[6], x.e);
             Sd[7] = decay_block<7>(S[7], x.e);
+            if (OUT) {
 #pragma unroll
-            for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + b * 1024 + l * 16) = S[b];
+                for (int b = 0; b < 8; ++b) *(f32x4 *)(snap + b * 1024 + l * 16) = S[b];
+            }
             const f16x8 vn = cat16(to_f16x4((a0 + a1) + ua), to_f16x4((b0 + b1) + ub));
-            *(f16x8 *)(snap + 8192 + l * 16) = vn;
+            if (OUT) *(f16x8 *)(snap + 8192 + l * 16) = vn;
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = mfma16(x.kt[b], vn, Sd[b]);
         };
@@ -835,7 +838,7 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_ker
 
 // Pass 1 of the recurrence over parts: blocks [0, G/2) run every part from a zero state,
 // blocks [G/2, G) from the identity with v taken as 0 (final state: the part's linear map).
-// Its states are all fp32 (workspace).
+// Its states are all fp32 (workspace); it forms no outputs (pass 2 writes them all).
 template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
@@ -845,8 +848,8 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_ke
     const int RB = (int)(gridDim.x / 2);
     const bool id = (int)blockIdx.x >= RB;
     const int b = id ? (int)blockIdx.x - RB : (int)blockIdx.x;
-    recur_h32_block<NW, NSLOT>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
-                               id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, false, id);
+    recur_h32_block<NW, NSLOT, false>(xcd_remap(b, RB, D / (16 * NW)), ring, recs, v, vcu, vco, vorder, NV, T, H,
+                                      id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, false, id);
 }
 
 // ---------------------------------------------------------------- launchers

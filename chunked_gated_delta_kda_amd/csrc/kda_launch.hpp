@@ -148,5 +148,5 @@ hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v,
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, bool h32, bool sbf, hipStream_t st);
+                        float *ri, float *sin, bool h32, bool sbf, int pass2_waves, hipStream_t st);
 }  // namespace kda

@@ -1466,7 +1466,7 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,
                         const int32_t *order, int N, int T, int H, int P, const float *s0, float *out,
                         float *sfin, int32_t *vcu, int32_t *vco, int32_t *vorder, float *ident, float *rb,
-                        float *ri, float *sin, bool h32, bool sbf, hipStream_t st) {
+                        float *ri, float *sin, bool h32, bool sbf, int pass2_waves, hipStream_t st) {
     const int NV = N * P;
     const int64_t ns = (int64_t)NV * H;
     hipLaunchKernelGGL(parts_setup_kernel, dim3(512), dim3(256), 0, st, cu_safe, chunk_off, order, N, P,
@@ -1489,8 +1489,8 @@ hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_s
     hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), 0, st, s0, (const float *)rb,
                        (const float *)ri, N, P, H, sin, sfin, (int)sbf);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 401, 0,
-                                           SEG_ONE, false, st);
+    if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr,
+                                           pass2_waves, 0, SEG_ONE, false, st);
     return launch_recur_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr, 101, 0, SEG_ONE, st);
 }
 

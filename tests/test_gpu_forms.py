@@ -70,6 +70,22 @@ def test_parts(workload, parts, form, monkeypatch):
     assert ok
 
 
+@pytest.mark.parametrize("pass2", [401, 402])
+@pytest.mark.parametrize("parts", [2, 5])
+def test_parts_pass2_form(workload, parts, pass2, monkeypatch):
+    """Pass 2 of the recurrence over parts in either 32-token form (one or two 16-column
+    slices per block), whichever the part count would pick."""
+    monkeypatch.setenv("KDA_PARTS", str(parts))
+    monkeypatch.setenv("KDA_RECUR_WAVES", "401")
+    monkeypatch.setenv("KDA_PARTS_FORM", str(pass2))
+    w, (ro, rf) = workload
+    _say(f"[forms] parts={parts} pass 2 form={pass2} lengths={LENGTHS}")
+    o, f = run_gpu(w, "split")
+    ok, mo, mf = compare(w, o, f, ro, rf)
+    _say(f"  o {mo}\n  S {mf}")
+    assert ok
+
+
 @pytest.mark.parametrize("fp16", [False, True])
 @pytest.mark.parametrize("segments,parts", [(1, 1), (4, 1), (1, 3)])
 def test_no_final_state_and_in_place(workload, segments, parts, fp16, monkeypatch):
