@@ -106,16 +106,21 @@ int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
         if (p >= 1 && p <= MAX_PARTS) return p;
     }
     if (waves != 101 && waves != 401) return 1;
-    // Over 32-token records, pass 2 can run the two-slice form (4 blocks per part), which
-    // fits twice the parts in one round: with chains of 128 such chunks or more per part
-    // that pays. Measured on MI355X (ms; P parts with pass 2 one-slice | P parts two-slice):
-    // 65536 tokens x 8 heads 0.964 (4) | 0.862 (8); 32768 x 8 0.520 (4) | 0.472 (8); but
-    // two sequences of 16384 x 4 0.262 (4) | 0.272 (8), 16384 x 4 0.178 (8) | 0.188 (8).
-    // With 16 chains (ms, whole | 4 parts two-slice): 2 x 65536 x 8 1.99 | 1.59; 2 x 32768 x 8
-    // 1.01 | 0.83; 4 x 16384 x 4 0.522 | 0.446; 65536 x 16 1.98 | 1.58; 32768 x 16 1.00 | 0.83.
+    // Over 32-token records pass 1 runs four-slice blocks without outputs (2 per part and
+    // entry state) and pass 2 the two-slice form when the one-slice form would not fit one
+    // round: P = 64 / chains, with parts of 64 chunks or more. Measured on MI355X (ms for
+    // P = 1, 2, 4, 8, 16): 65536 tokens x 8 heads 1.75, 1.59, 0.970, 0.729, 0.840; 32768 x
+    // 8 0.885, 0.818, 0.523, 0.418, 0.474; 2 x 16384 x 4 0.389, 0.386, 0.270, 0.248, 0.307;
+    // 16384 x 4 0.336, 0.353, 0.224, 0.181, 0.207; 2 x 65536 x 8 1.99, 1.88, 1.34, 1.44,
+    // 1.53; 8192 x 16 (P = 1, 3, 4, 8) 0.236, 0.237, 0.221, 0.251; 2 x 8192 x 8 0.242, 0.238,
+    // 0.221, 0.255; but 8192 x 32 (P = 1, 2, 4, 8, 16) 0.359, 0.369, 0.395, 0.444, 0.539 and
+    // 4096 x 4 (P = 1, 3, 4, 8) 0.099, 0.103, 0.098, 0.108.
     if (waves == 401) {
-        const int64_t p2 = 64 / (N * H), per_seq = T / N / 32;
-        if (p2 >= 3 && per_seq / (p2 < MAX_PARTS ? p2 : MAX_PARTS) >= 128) return (int)(p2 < MAX_PARTS ? p2 : MAX_PARTS);
+        int64_t p = 64 / (N * H);
+        const int64_t by_len = T / N / 32 / 64;
+        if (by_len < p) p = by_len;
+        if (p > MAX_PARTS) p = MAX_PARTS;
+        return p >= 3 ? (int)p : 1;
     }
     int64_t p = 32 / (N * H);
     const int64_t by_len = max_chunks(N, T) / 64;

@@ -664,16 +664,20 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 //   NW = 2: chain 0, chain 1 | output (slice 0, p0), (slice 1, p0) | loader | idle |
 //           output (slice 0, p1), (slice 1, p1)
 // (the idle wave only keeps the barrier count, so that SIMD 1 hosts chain 1 alone).
+//   NW = 4: chain 0..3 | loader (states only, no output waves: the recurrence over
+//           parts' first pass)
 template <int NW>
 struct PairLayout {
-    static_assert(NW == 1 || NW == 2, "one or two slices per block");
+    static_assert(NW == 1 || NW == 2 || NW == 4, "one, two or four slices per block");
     static constexpr int SNAP = 64 * 32 * 4 + 64 * 16;   // state fp32 [64 lanes][32] + V_new hi|lo
     static constexpr int SNAPS = 3;                      // snapshot buffers per slice
-    static constexpr int WAVES = NW == 1 ? 4 : 8;
+    static constexpr int WAVES = NW == 1 ? 4 : NW == 2 ? 8 : 5;
     static constexpr int LOADER = NW == 1 ? 3 : 4;
-    static constexpr int IDLE = NW == 1 ? -1 : 5;
-    // output wave of slice s, parity p
-    __device__ static constexpr int out_wave(int s, int p) { return NW == 1 ? 1 + p : (p ? 6 : 2) + s; }
+    static constexpr int IDLE = NW == 2 ? 5 : -1;
+    // output wave of slice s, parity p (none with four slices)
+    __device__ static constexpr int out_wave(int s, int p) {
+        return NW == 1 ? 1 + p : NW == 2 ? (p ? 6 : 2) + s : -1;
+    }
 };
 
 // Global index of the idx-th chunk-head (heads fastest, sequences in input order) of the

@@ -500,9 +500,9 @@ struct PairH {
 };
 template <int NW>
 constexpr int pairh_nslot() { return NW == 1 ? 5 : 4; }
-template <int NW, int NSLOT>
+template <int NW, int NSLOT, bool OUT = true>
 struct PairHLds {
-    static constexpr int BYTES = NSLOT * PairH<NW>::SLOT + PairH<NW>::SNAPS * NW * PairH<NW>::SNAP;
+    static constexpr int BYTES = NSLOT * PairH<NW>::SLOT + (OUT ? PairH<NW>::SNAPS * NW * PairH<NW>::SNAP : 0);
     static_assert(BYTES <= 160 * 1024 && BYTES > 80 * 1024, "one block per CU");
 };
 
@@ -522,6 +522,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
                                                 int fb, int fe, bool sbf, bool zero_v = false) {
     using P = PairH<NW>;
     using PL = PairLayout<NW>;
+    static_assert(NW <= 2 || !OUT, "the four-slice block has no output waves");
     constexpr int LOADS = P::LOADS;
     constexpr int SLOT = P::SLOT;
     static_assert(NSLOT >= 3, "the chain reads one chunk ahead of the one it computes");
@@ -838,7 +839,8 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_ker
 
 // Pass 1 of the recurrence over parts: blocks [0, G/2) run every part from a zero state,
 // blocks [G/2, G) from the identity with v taken as 0 (final state: the part's linear map).
-// Its states are all fp32 (workspace); it forms no outputs (pass 2 writes them all).
+// Its states are all fp32 (workspace); it forms no outputs (pass 2 writes them all), so
+// its blocks are four chain waves (64 value columns) and the loader.
 template <int NW, int NSLOT>
 __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_parts_kernel(
     const char *__restrict__ recs, const uint16_t *__restrict__ v, const int32_t *__restrict__ vcu,
@@ -926,8 +928,8 @@ hipError_t launch_recur_h32_prep(const RecurPrepArgs &a, int waves, hipStream_t 
 hipError_t launch_h32_parts_pass1(const char *recs, const uint16_t *v, const int32_t *vcu, const int32_t *vco,
                                   const int32_t *vorder, int NV, int T, int H, const float *ident, float *out,
                                   float *rb, float *ri, hipStream_t st) {
-    constexpr int NW = 2, NS = pairh_nslot<2>();
-    constexpr int lds = PairHLds<NW, NS>::BYTES;
+    constexpr int NW = 4, NS = 4;
+    constexpr int lds = PairHLds<NW, NS, false>::BYTES;
     auto kern = recur_h32_parts_kernel<NW, NS>;
     static std::atomic<uint64_t> lds_set{0};
     if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;

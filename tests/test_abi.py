@@ -123,7 +123,7 @@ def test_workspace_bytes(lib):
 
 def test_launch_plan():
     from chunked_gated_delta_kda_amd import native as nat
-    for N, T, H in ((1, 8192, 32), (2, 16384, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32)):
+    for N, T, H in ((1, 8192, 32), (2, 4096, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32)):
         plan = nat.launch_plan(N, T, H, "split")
         kinds = [p[0] for p in plan]
         assert kinds[:2] == ["chunk_map", "prep"] and kinds[-1] == "recur"
@@ -161,7 +161,9 @@ def test_launch_plan():
     # 16 chains of 1,024 chunks (32 tokens) each: four parts, pass 2 with two slices per block
     assert [p[0] for p in nat.launch_plan(2, 65536, 8, "split")] == ["chunk_map", "prep", "parts"]
     assert [p[0] for p in nat.launch_plan(1, 32768, 16, "split")][-1] == "parts"   # four, two-slice pass 2
-    assert [p[0] for p in nat.launch_plan(1, 8192, 16, "split")][-1] != "parts"    # two parts do not pay
+    assert [p[0] for p in nat.launch_plan(1, 8192, 16, "split")][-1] == "parts"    # four parts of 64 chunks
+    assert [p[0] for p in nat.launch_plan(1, 8192, 32, "split")][-1] != "parts"    # two parts do not pay
+    assert [p[0] for p in nat.launch_plan(1, 4096, 4, "split")][-1] != "parts"     # parts under 64 chunks
     # many chains (the two-slice 32-token form, or the per-chain hybrid) run whole by default
     assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
