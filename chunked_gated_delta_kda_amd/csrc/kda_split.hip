@@ -1421,42 +1421,86 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel
                                 id ? ident : nullptr, out, id ? ri : rb, id ? ri : rb, 0, SEG_ONE, id);
 }
 
-// composition over the parts of each sequence, one block per (sequence, head, 16 value
-// columns): the columns of a state evolve independently under M
+// Composition over the parts of each sequence, one block per (sequence, head, 16 value
+// columns): the columns of a state evolve independently under M. Per part p, in order:
+// the entry state S is written out, then S <- M_p S + B_p in fp32, on the fp32 matrix
+// cores (v_mfma_f32_16x16x4_f32: A lane l holds M[row l % 16][k l / 16], B holds
+// S[k l / 16][col l % 16], the result rows 4 (l / 16) + j of column l % 16). Each of the
+// four waves owns 32 rows. M_p (64 KiB) goes through LDS with rows padded to 132 floats
+// (a wave's 16 rows x 4 k of an A operand fall in 64 distinct banks), loaded with whole
+// 16-byte accesses; the next part's M is loaded into registers during this part's product.
+constexpr int COMBINE_LD = D + 4;
+constexpr int COMBINE_LDS = (2 * D * COMBINE_LD + D * 16) * (int)sizeof(float);
+
 __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, const float *rb, const float *ri,
                                                             int N, int P, int H, float *sin, float *sfin, int sbf) {
-    __shared__ float S[D][16];
+    extern __shared__ __attribute__((aligned(16))) float combine_lds[];
+    float(*Ms)[D][COMBINE_LD] = (float(*)[D][COMBINE_LD])combine_lds;   // [2][D][D + 4]
+    float(*S)[16] = (float(*)[16])(combine_lds + 2 * D * COMBINE_LD);     // [D][16]
     const int cs = blockIdx.x % 8, h = (blockIdx.x / 8) % H, n = blockIdx.x / (8 * H);
-    const int t = threadIdx.x, r = t >> 1, c0 = (t & 1) * 8, col0 = cs * 16;
+    const int t = threadIdx.x, w = t >> 6, l = t & 63, col0 = cs * 16;
+    const int lc = l & 15, lk = l >> 4;    // MFMA: column (or row) l % 16, k slot l / 16
     for (int i = t; i < D * 16; i += 256) {
         const int rr = i / 16, cc = i % 16;
         const int64_t i0 = ((int64_t)n * H + h) * D * D + (int64_t)rr * D + col0 + cc;
         S[rr][cc] = !s0 ? 0.f : sbf ? __uint_as_float((uint32_t)((const uint16_t *)s0)[i0] << 16) : s0[i0];
     }
+    auto base_of = [&](int p) { return (((int64_t)n * P + p) * H + h) * D * D; };
+    float4 mreg[16];   // one part's M: 16 float4 per thread, element 4 (t + 256 j)
+    f32x4 breg[2];     // and its B at this lane's result positions
+    auto load_m = [&](int p) {
+        const float4 *src = (const float4 *)(ri + base_of(p));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) mreg[j] = src[t + 256 * j];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                breg[rt][j] = rb[base_of(p) + (int64_t)(32 * w + 16 * rt + 4 * lk + j) * D + col0 + lc];
+    };
+    auto store_m = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = 4 * (t + 256 * j), row = e / D, col = e % D;
+            *(float4 *)&Ms[buf][row][col] = mreg[j];
+        }
+    };
+    if (P > 0) {
+        load_m(0);
+        store_m(0);
+    }
     __syncthreads();
     for (int p = 0; p < P; ++p) {
-        const int64_t base = (((int64_t)n * P + p) * H + h) * D * D;
-        float acc[8];
+        const int64_t base = base_of(p);
+        f32x4 acc[2] = {breg[0], breg[1]};
+        if (p + 1 < P) load_m(p + 1);
+        const float(*M)[COMBINE_LD] = Ms[p & 1];
+#pragma unroll 8
+        for (int kk = 0; kk < D / 4; ++kk) {
+            const float b = S[4 * kk + lk][lc];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] = rb[base + (int64_t)r * D + col0 + c0 + j];
-        for (int k = 0; k < D; ++k) {
-            const float m = ri[base + (int64_t)r * D + k];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[j] = fmaf(m, S[k][c0 + j], acc[j]);
+            for (int rt = 0; rt < 2; ++rt)
+                acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(M[32 * w + 16 * rt + lc][4 * kk + lk], b, acc[rt], 0, 0, 0);
         }
+        // the entry state of part p, then (after every wave's reads of S) the new state
+        for (int i = t; i < D * 16 / 4; i += 256) {
+            const int rr = i / 4, c4 = (i % 4) * 4;
+            *(float4 *)(sin + base + (int64_t)rr * D + col0 + c4) = *(const float4 *)&S[rr][c4];
+        }
+        __syncthreads();   // every read of S and of this part's M is done
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sin[base + (int64_t)r * D + col0 + c0 + j] = S[r][c0 + j];
-        __syncthreads();
+        for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) S[r][c0 + j] = acc[j];
+            for (int j = 0; j < 4; ++j) S[32 * w + 16 * rt + 4 * lk + j][lc] = acc[rt][j];
+        if (p + 1 < P) store_m((p + 1) & 1);
         __syncthreads();
     }
     if (sfin) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t i0 = ((int64_t)n * H + h) * D * D + (int64_t)r * D + col0 + c0 + j;
-            if (sbf) ((uint16_t *)sfin)[i0] = (uint16_t)(pack2(S[r][c0 + j], 0.f) & 0xffffu);   // round to nearest even
-            else sfin[i0] = S[r][c0 + j];
+        for (int i = t; i < D * 16; i += 256) {
+            const int rr = i / 16, cc = i % 16;
+            const int64_t i0 = ((int64_t)n * H + h) * D * D + (int64_t)rr * D + col0 + cc;
+            if (sbf) ((uint16_t *)sfin)[i0] = (uint16_t)(pack2(S[rr][cc], 0.f) & 0xffffu);   // round to nearest even
+            else sfin[i0] = S[rr][cc];
         }
     }
 }
@@ -1486,8 +1530,11 @@ hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_s
                            vco, vorder, NV, T, H, (const float *)ident, out, rb, ri);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), 0, st, s0, (const float *)rb,
-                       (const float *)ri, N, P, H, sin, sfin, (int)sbf);
+    static std::atomic<uint64_t> combine_lds_set{0};
+    if (ensure_lds_limit((const void *)parts_combine_kernel, COMBINE_LDS, combine_lds_set) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), COMBINE_LDS, st, s0,
+                       (const float *)rb, (const float *)ri, N, P, H, sin, sfin, (int)sbf);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr,
                                            pass2_waves, 0, SEG_ONE, false, st);
