@@ -620,8 +620,12 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
 #pragma unroll
             for (int b = 0; b < 8; ++b) S[b] = zero;
         }
+        // The next chunk's pieces are read one step ahead, except with two slices per block
+        // the K~^T pieces (read in the step: the slot stays valid until the barrier after
+        // it), which keeps the two chain waves' registers within 256 without spills.
+        constexpr bool KT_AHEAD = NW == 1;
         struct ChainIn {
-            f16x8 wn[8], kt[8], tb[2];
+            f16x8 wn[8], kt[KT_AHEAD ? 8 : 1], tb[2];
             f32x2 e;              // lane-permuted decay of the whole chunk
             uint16_t vv[8];       // V[tau(8g+i)][col]
         };
@@ -637,12 +641,20 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) x.wn[i] = *(const f16x8 *)(slot + RecH::WN + i * 1024 + l * 16);
+            if constexpr (KT_AHEAD) {
 #pragma unroll
-            for (int b = 0; b < 8; ++b) x.kt[b] = *(const f16x8 *)(slot + RecH::KT + b * 1024 + l * 16);
+                for (int b = 0; b < 8; ++b) x.kt[b] = *(const f16x8 *)(slot + RecH::KT + b * 1024 + l * 16);
+            }
             x.e = *(const f32x2 *)(slot + RecH::EGP + l * 8);
         };
         auto chain_step = [&](const ChainIn &x, int it) {
             char *snap = snap_of(it);
+            f16x8 kt[8];
+            if constexpr (!KT_AHEAD) {
+                const char *slot = ring + (it % NSLOT) * SLOT;
+#pragma unroll
+                for (int b = 0; b < 8; ++b) kt[b] = *(const f16x8 *)(slot + RecH::KT + b * 1024 + l * 16);
+            }
             f16x8 sh[4];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) sh[kb] = cat16(to_f16x4(S[2 * kb]), to_f16x4(S[2 * kb + 1]));
@@ -682,7 +694,7 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
             const f16x8 vn = cat16(to_f16x4((a0 + a1) + ua), to_f16x4((b0 + b1) + ub));
             if (OUT) *(f16x8 *)(snap + 8192 + l * 16) = vn;
 #pragma unroll
-            for (int b = 0; b < 8; ++b) S[b] = mfma16(x.kt[b], vn, Sd[b]);
+            for (int b = 0; b < 8; ++b) S[b] = mfma16(KT_AHEAD ? x.kt[KT_AHEAD ? b : 0] : kt[b], vn, Sd[b]);
         };
         // after each barrier every LDS access of the wave issued before it is waited for
         auto sync_chain = [&] {
