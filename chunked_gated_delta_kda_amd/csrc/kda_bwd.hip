@@ -199,10 +199,14 @@ __device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][CW],
     }
 }
 
+// Per-wave row gradients of the BLK tokens of a block (double-buffered by block): the waves
+// add them once per block, behind one barrier.
 struct BwdLds {
-    float part[2][WAVES][3][D];   // per-wave dq, dk, dg of a token (double-buffered by token)
-    float pb[2][WAVES];           // per-wave dbeta
+    float part[2][BLK][WAVES][3][D];   // dq, dk, dg
+    float pb[2][BLK][WAVES];           // dbeta
 };
+constexpr int BWD_LDS = (int)sizeof(BwdLds);
+static_assert(BWD_LDS <= 160 * 1024, "LDS");
 
 // sum of the block's WAVES partials of one output (stride apart), in a fixed order
 __device__ __forceinline__ float sum_waves(const float *p, int stride) {
@@ -224,7 +228,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const int32_t *__restrict__ chunk_off, int H, const float *__restrict__ s0, const float *__restrict__ dout,
     const float *__restrict__ dsf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck) {
-    __shared__ BwdLds L;
+    extern __shared__ __attribute__((aligned(16))) char bwd_lds[];
+    BwdLds &L = *(BwdLds *)bwd_lds;
     const int bid = xcd_remap(blockIdx.x, gridDim.x, HALVES);
     const int half = bid % HALVES, chain = bid / HALVES;
     const int h = chain % H, n = chain / H;
@@ -256,10 +261,17 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
 
     // ---- backward, block by block from the last. The loads of a block, in order: the
     // inputs of its nin tokens (recomputing S1 and u of each), then the same from the last
-    // (the reverse walk); each is issued one step before it is used.
+    // (the reverse walk); each is issued one step before it is used, the next block's
+    // checkpoint and first inputs during this block's last token.
     float dS[2][CW];
     load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
     int par = 0;
+    Raw xr;            // the next inputs to use
+    float Sck[2][CW];  // the next block's checkpoint
+    if (nblk > 0) {
+        load_slice(Sck, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
+        rawd(xr, bos + (int64_t)(nblk - 1) * BLK);
+    }
     for (int b = nblk - 1; b >= 0; --b) {
         const int64_t tb = bos + (int64_t)b * BLK;
         const int nin = (int)std::min((int64_t)BLK, eos - tb);
@@ -269,10 +281,11 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             return tb + (sx < nin ? sx : 2 * nin - 1 - sx);
         };
         int sidx = 0;
-        Raw xr;
-        rawd(xr, tok_at(0));
         float S1s[BLK][2][CW], us[BLK];   // S1 and u of each token of the block
-        load_slice(S, ckc + b * ck_stride, c0, lane);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int c = 0; c < CW; ++c) S[r][c] = Sck[r][c];
 #pragma unroll
         for (int i = 0; i < BLK; ++i) {
             if (i < nin) {
@@ -294,7 +307,12 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             Tok x;
             ready(x, xr, true);
             const float(&dov)[CW] = x.dov;
-            rawd(xr, tok_at(++sidx));
+            if (i > 0) {
+                rawd(xr, tok_at(++sidx));
+            } else if (b > 0) {   // the block's last token: the next block's first loads
+                load_slice(Sck, ckc + (int64_t)(b - 1) * ck_stride, c0, lane);
+                rawd(xr, tb - BLK);
+            }
             const float(&S1)[2][CW] = S1s[i];
             float u[CW], r[CW], d[CW];
             broadcast8(us[i], u);
@@ -347,24 +365,39 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                 gk[rr] = a + bs;
                 gg[rr] = x.g[rr] >= LB ? gs : 0.f;
             }
-            // the block's waves add through LDS, then one atomic add per output
+            // this wave's row gradients of the token, added over the block's waves below
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
-                L.part[par][wave][0][lane + 64 * rr] = gq[rr];
-                L.part[par][wave][1][lane + 64 * rr] = gk[rr];
-                L.part[par][wave][2][lane + 64 * rr] = gg[rr];
+                L.part[par][i][wave][0][lane + 64 * rr] = gq[rr];
+                L.part[par][i][wave][1][lane + 64 * rr] = gk[rr];
+                L.part[par][i][wave][2][lane + 64 * rr] = gg[rr];
             }
-            if (lane == 0) L.pb[par][wave] = pbeta;
-            __syncthreads();
-            if (tid < 3 * D) {
-                const int a = tid / D, row = tid % D;
-                float *dst = a == 0 ? dq : a == 1 ? dk : dg;
-                unsafeAtomicAdd(dst + th * D + row, sum_waves(&L.part[par][0][a][row], 3 * D));
-            } else if (tid == 3 * D) {
-                unsafeAtomicAdd(dbeta + th, sum_waves(&L.pb[par][0], 1));
-            }
-            par ^= 1;   // the next token writes the other buffer: this barrier orders its reuse
+            if (lane == 0) L.pb[par][i][wave] = pbeta;
         }
+        // The next block's loads (issued during this block's last token) land before the
+        // atomic adds below are issued, so that waiting for them later does not also wait
+        // for the adds (loads, stores and atomics share one in-order counter).
+        asm volatile("" ::"v"(xr.k[0]), "v"(xr.k[1]), "v"(xr.q[0]), "v"(xr.q[1]), "v"(xr.g[0]), "v"(xr.g[1]),
+                     "v"(xr.v.x), "v"(xr.v.y), "v"(xr.v.z), "v"(xr.v.w), "v"(xr.dov[0].x), "v"(xr.dov[0].y),
+                     "v"(xr.dov[0].z), "v"(xr.dov[0].w), "v"(xr.dov[1].x), "v"(xr.dov[1].y), "v"(xr.dov[1].z),
+                     "v"(xr.dov[1].w));
+        asm volatile("" ::"v"(Sck[0][0]), "v"(Sck[0][1]), "v"(Sck[0][2]), "v"(Sck[0][3]), "v"(Sck[0][4]),
+                     "v"(Sck[0][5]), "v"(Sck[0][6]), "v"(Sck[0][7]), "v"(Sck[1][0]), "v"(Sck[1][1]), "v"(Sck[1][2]),
+                     "v"(Sck[1][3]), "v"(Sck[1][4]), "v"(Sck[1][5]), "v"(Sck[1][6]), "v"(Sck[1][7]));
+        __syncthreads();
+        // the block's waves add through LDS, then one atomic add per output and token
+        for (int o = tid; o < nin * (3 * D + 1); o += 64 * WAVES) {
+            const int i = o / (3 * D + 1), rem = o % (3 * D + 1);
+            const int64_t th = (tb + i) * H + h;
+            if (rem == 3 * D) {
+                unsafeAtomicAdd(dbeta + th, sum_waves(&L.pb[par][i][0], 1));
+            } else {
+                const int a = rem / D, row = rem % D;
+                float *dst = a == 0 ? dq : a == 1 ? dk : dg;
+                unsafeAtomicAdd(dst + th * D + row, sum_waves(&L.part[par][i][0][a][row], 3 * D));
+            }
+        }
+        par ^= 1;   // the next block writes the other buffer: the barrier above orders its reuse
     }
     if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
 }
@@ -396,8 +429,10 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                            (float4 *)dg, n4, dbeta, th);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)((int64_t)N * H * HALVES)), dim3(64 * WAVES), 0, st, q, k, v, g,
-                       beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0, ck);
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)bwd_kernel, BWD_LDS, lds_set) != hipSuccess) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)((int64_t)N * H * HALVES)), dim3(64 * WAVES), BWD_LDS, st, q, k,
+                       v, g, beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0, ck);
     return hipGetLastError();
 }
 
