@@ -108,7 +108,7 @@ struct Tok {
 __device__ __forceinline__ void load_raw(Raw &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                          const uint16_t *__restrict__ v, const float *__restrict__ g,
                                          const float *__restrict__ beta, const float *__restrict__ dout, int64_t th,
-                                         int c0, int lane) {
+                                         int c0, int lane, int vz) {
     const int64_t o = th * D;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
@@ -116,12 +116,23 @@ __device__ __forceinline__ void load_raw(Raw &x, const uint16_t *__restrict__ q,
         x.q[r] = q[o + lane + 64 * r];
         x.g[r] = g[o + lane + 64 * r];
     }
-    x.v = *(const uint4 *)(v + o + c0);
-    x.beta = beta[th];
+    // v, beta and dout are the same for every lane of the wave; vz (a zero the compiler
+    // cannot see through) keeps them vector loads, which complete in order, so that a use
+    // waits only for its own load. As scalar loads (out of order) every use would wait for
+    // all loads in flight, the prefetched ones included.
+    x.v = *(const uint4 *)(v + o + c0 + vz);
+    x.beta = beta[th + vz];
     if (dout) {
 #pragma unroll
-        for (int j = 0; j < CW / 4; ++j) x.dov[j] = ((const float4 *)(dout + o + c0))[j];
+        for (int j = 0; j < CW / 4; ++j) x.dov[j] = ((const float4 *)(dout + o + c0 + vz))[j];
     }
+}
+
+// Make the loads of r complete here (see the block combine in bwd_kernel).
+__device__ __forceinline__ void settle(const Raw &r) {
+    asm volatile("" ::"v"(r.k[0]), "v"(r.k[1]), "v"(r.q[0]), "v"(r.q[1]), "v"(r.g[0]), "v"(r.g[1]), "v"(r.v.x),
+                 "v"(r.v.y), "v"(r.v.z), "v"(r.v.w), "v"(r.dov[0].x), "v"(r.dov[0].y), "v"(r.dov[0].z),
+                 "v"(r.dov[0].w), "v"(r.dov[1].x), "v"(r.dov[1].y), "v"(r.dov[1].z), "v"(r.dov[1].w), "v"(r.beta));
 }
 
 __device__ __forceinline__ void ready(Tok &x, const Raw &r, bool with_dout) {
@@ -241,57 +252,86 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
     const int64_t ck_stride = (int64_t)H * D * D;
     float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
-    auto raw = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, nullptr, t * H + h, c0, lane); };
-    auto rawd = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, dout, t * H + h, c0, lane); };
+    int vz;   // 0, in a VGPR (see load_raw)
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    auto raw = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, nullptr, t * H + h, c0, lane, vz); };
+    auto rawd = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, dout, t * H + h, c0, lane, vz); };
 
-    // ---- forward: the state before every BLK-th token (inputs loaded one token ahead)
+    // ---- forward: the state before every BLK-th token. Inputs come through a ring of PF
+    // loads in registers, each issued PF tokens before it is used.
+    constexpr int PF = BLK;
     float S[2][CW];
     load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
     if (bos < eos) {
-        Raw xr;
-        raw(xr, bos);
-        for (int64_t t = bos; t < eos; ++t) {
-            if ((t - bos) % BLK == 0) store_slice(ckc + ((t - bos) / BLK) * ck_stride, S, c0, lane);
-            Tok x;
-            ready(x, xr, false);
-            raw(xr, t + 1 < eos ? t + 1 : t);
-            write_step(S, x, decay_u(S, x, lane));
+        Raw ring[PF];
+#pragma unroll
+        for (int j = 0; j < PF; ++j) raw(ring[j], bos + j < eos ? bos + j : eos - 1);
+        int64_t t0 = bos;
+        for (; t0 + PF <= eos; t0 += PF) {   // whole groups of PF tokens
+            store_slice(ckc + ((t0 - bos) / BLK) * ck_stride, S, c0, lane);
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                // Nothing here is conditional, and each slot is read before its refill is
+                // issued, so that the refill can take the slot's registers: else the loop's
+                // back edge copies the ring and so waits for every load in flight.
+                const int64_t t = t0 + j;
+                Tok x;
+                ready(x, ring[j], false);
+                __builtin_amdgcn_sched_barrier(0);
+                raw(ring[j], t + PF < eos ? t + PF : eos - 1);
+                write_step(S, x, decay_u(S, x, lane));
+            }
+        }
+        if (t0 < eos) {   // the last, partial group (already in the ring)
+            store_slice(ckc + ((t0 - bos) / BLK) * ck_stride, S, c0, lane);
+#pragma unroll
+            for (int j = 0; j < PF; ++j) {
+                if (t0 + j < eos) {
+                    Tok x;
+                    ready(x, ring[j], false);
+                    write_step(S, x, decay_u(S, x, lane));
+                }
+            }
         }
     }
 
-    // ---- backward, block by block from the last. The loads of a block, in order: the
-    // inputs of its nin tokens (recomputing S1 and u of each), then the same from the last
-    // (the reverse walk); each is issued one step before it is used, the next block's
-    // checkpoint and first inputs during this block's last token.
+    // ---- backward, block by block from the last. A block's loads take 2 BLK positions:
+    // position i < BLK the inputs of token i (recomputing S1 and u), position 2 BLK - 1 - i
+    // those of token i again (the reverse walk); positions past the block's tokens load a
+    // valid token and are skipped. They come through the same ring, each issued BLK
+    // positions before it is used: recompute token i uses slot i, reverse token i slot
+    // BLK - 1 - i, and each slot is refilled BLK positions on, in this block or the next.
     float dS[2][CW];
     load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
     int par = 0;
-    Raw xr;            // the next inputs to use
+    Raw ring[BLK];
     float Sck[2][CW];  // the next block's checkpoint
+    auto tok_pos = [&](int bb, int pos) -> int64_t {
+        const int64_t tbb = bos + (int64_t)bb * BLK;
+        const int nb = (int)std::min((int64_t)BLK, eos - tbb);
+        const int i = pos < BLK ? pos : 2 * BLK - 1 - pos;
+        return tbb + (i < nb ? i : nb - 1);
+    };
     if (nblk > 0) {
         load_slice(Sck, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
-        rawd(xr, bos + (int64_t)(nblk - 1) * BLK);
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) rawd(ring[j], tok_pos(nblk - 1, j));
     }
     for (int b = nblk - 1; b >= 0; --b) {
         const int64_t tb = bos + (int64_t)b * BLK;
         const int nin = (int)std::min((int64_t)BLK, eos - tb);
-        const int nload = 2 * nin;
-        auto tok_at = [&](int sx) -> int64_t {
-            sx = sx < nload ? sx : nload - 1;
-            return tb + (sx < nin ? sx : 2 * nin - 1 - sx);
-        };
-        int sidx = 0;
         float S1s[BLK][2][CW], us[BLK];   // S1 and u of each token of the block
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
             for (int c = 0; c < CW; ++c) S[r][c] = Sck[r][c];
 #pragma unroll
-        for (int i = 0; i < BLK; ++i) {
+        for (int i = 0; i < BLK; ++i) {   // positions 0 .. BLK - 1
+            Tok x;
+            ready(x, ring[i], false);
+            __builtin_amdgcn_sched_barrier(0);
+            rawd(ring[i], tok_pos(b, BLK + i));   // position BLK + i: reverse token BLK - 1 - i
             if (i < nin) {
-                Tok x;
-                ready(x, xr, false);
-                rawd(xr, tok_at(++sidx));
                 us[i] = decay_u(S, x, lane);
 #pragma unroll
                 for (int r = 0; r < 2; ++r)
@@ -301,18 +341,18 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             }
         }
 #pragma unroll
-        for (int i = BLK - 1; i >= 0; --i) {
-            if (i >= nin) continue;
-            const int64_t th = (tb + i) * H + h;
+        for (int i = BLK - 1; i >= 0; --i) {   // positions BLK .. 2 BLK - 1
+            const int slot = BLK - 1 - i;
             Tok x;
-            ready(x, xr, true);
+            ready(x, ring[slot], true);
+            __builtin_amdgcn_sched_barrier(0);
+            // the next block's position slot (block 0 reloads its own: unused)
+            rawd(ring[slot], tok_pos(b > 0 ? b - 1 : 0, slot));
+            if (i == 0) load_slice(Sck, ckc + (int64_t)(b > 0 ? b - 1 : 0) * ck_stride, c0, lane);
+            if (i >= nin) continue;
             const float(&dov)[CW] = x.dov;
-            if (i > 0) {
-                rawd(xr, tok_at(++sidx));
-            } else if (b > 0) {   // the block's last token: the next block's first loads
-                load_slice(Sck, ckc + (int64_t)(b - 1) * ck_stride, c0, lane);
-                rawd(xr, tb - BLK);
-            }
+            const int64_t th = (tb + i) * H + h;
+
             const float(&S1)[2][CW] = S1s[i];
             float u[CW], r[CW], d[CW];
             broadcast8(us[i], u);
@@ -374,13 +414,11 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             }
             if (lane == 0) L.pb[par][i][wave] = pbeta;
         }
-        // The next block's loads (issued during this block's last token) land before the
+        // The next block's loads (issued during this block's reverse walk) land before the
         // atomic adds below are issued, so that waiting for them later does not also wait
         // for the adds (loads, stores and atomics share one in-order counter).
-        asm volatile("" ::"v"(xr.k[0]), "v"(xr.k[1]), "v"(xr.q[0]), "v"(xr.q[1]), "v"(xr.g[0]), "v"(xr.g[1]),
-                     "v"(xr.v.x), "v"(xr.v.y), "v"(xr.v.z), "v"(xr.v.w), "v"(xr.dov[0].x), "v"(xr.dov[0].y),
-                     "v"(xr.dov[0].z), "v"(xr.dov[0].w), "v"(xr.dov[1].x), "v"(xr.dov[1].y), "v"(xr.dov[1].z),
-                     "v"(xr.dov[1].w));
+#pragma unroll
+        for (int j = 0; j < BLK; ++j) settle(ring[j]);
         asm volatile("" ::"v"(Sck[0][0]), "v"(Sck[0][1]), "v"(Sck[0][2]), "v"(Sck[0][3]), "v"(Sck[0][4]),
                      "v"(Sck[0][5]), "v"(Sck[0][6]), "v"(Sck[0][7]), "v"(Sck[1][0]), "v"(Sck[1][1]), "v"(Sck[1][2]),
                      "v"(Sck[1][3]), "v"(Sck[1][4]), "v"(Sck[1][5]), "v"(Sck[1][6]), "v"(Sck[1][7]));
