@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "kda.h"
 #include "kda_device.hpp"
@@ -88,73 +89,89 @@ __device__ __forceinline__ void broadcast8(float s, float (&out)[CW]) {
     for (int c = 0; c < CW; ++c) out[c] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), lane_of_col(c)));
 }
 
-// One token's inputs as this lane needs them, as loaded: bf16 bits of k and q and the
-// fp32 g of key rows l and l + 64, the wave's value columns of v (bf16 bits) and d_out,
-// and beta. A step converts them (ready) only where it uses them, so that the loads
-// issued a step ahead are waited for there and not at their issue.
-struct Raw {
-    uint16_t k[2], q[2];
-    float g[2];
-    uint4 v;
-    float4 dov[CW / 4];
-    float beta;
-};
+// One token's inputs as a lane uses them: k, q, g and e = exp(max(g, -5)) of its key rows
+// l and l + 64, the wave's CW value columns of v and d_out, and beta.
 struct Tok {
     float k[2], q[2], e[2], g[2];
     float v[CW], dov[CW];
     float beta;
 };
 
-__device__ __forceinline__ void load_raw(Raw &x, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                         const uint16_t *__restrict__ v, const float *__restrict__ g,
-                                         const float *__restrict__ beta, const float *__restrict__ dout, int64_t th,
-                                         int c0, int lane, int vz) {
-    const int64_t o = th * D;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        x.k[r] = k[o + lane + 64 * r];
-        x.q[r] = q[o + lane + 64 * r];
-        x.g[r] = g[o + lane + 64 * r];
+// The inputs reach the waves through LDS, a group of BLK tokens at a time: while the block
+// computes on one group, each thread has one 16-byte piece of the next group in flight,
+// and stores it at the end of the group, behind the group's barrier. So a load is only
+// waited for after a whole group of computation, in either direction of the walk, and the
+// waves issue no per-token loads. A staged token is the pieces below, in this order.
+constexpr int PK = 0, PG = 16, PV = 48, PQ = 56, PO = 72, PIECES = 88;
+struct InTok {
+    uint16_t k[D];      // pieces PK..: bf16 bits
+    float g[D];         // PG..
+    uint16_t v[64];     // PV..: the block's 64 value columns, bf16 bits
+    uint16_t q[D];      // PQ..
+    float dout[64];     // PO..: the block's 64 value columns
+    float beta[4];      // [0]
+};
+static_assert(sizeof(InTok) == 16 * PIECES + 16, "staged token: whole pieces, then beta");
+
+struct Stage {
+    uint4 x;      // this thread's piece
+    float beta;   // beta of token (tid mod BLK) of the group
+};
+
+// Load this thread's piece of the group of BLK tokens starting at t0 (tokens past last
+// repeat it: their pieces are loaded and stored but never read).
+__device__ __forceinline__ void stage_load(Stage &st, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                           const uint16_t *__restrict__ v, const float *__restrict__ g,
+                                           const float *__restrict__ beta, const float *__restrict__ dout,
+                                           int64_t t0, int64_t last, int half, int H, int h, int tid) {
+    const int idx = min(tid, PIECES * BLK - 1);
+    const int j = idx / PIECES, p = idx - j * PIECES;
+    const int64_t t = min(t0 + j, last);
+    const int64_t o = (t * H + h) * D;
+    const char *src;
+    if (p < PG)
+        src = (const char *)(k + o) + 16 * (p - PK);
+    else if (p < PV)
+        src = (const char *)(g + o) + 16 * (p - PG);
+    else if (p < PQ)
+        src = (const char *)(v + o + 64 * half) + 16 * (p - PV);
+    else if (p < PO)
+        src = (const char *)(q + o) + 16 * (p - PQ);
+    else
+        src = (const char *)(dout + o + 64 * half) + 16 * (p - PO);
+    st.x = *(const uint4 *)src;
+    st.beta = beta[min(t0 + (tid & (BLK - 1)), last) * H + h];
+}
+__device__ __forceinline__ void stage_store(InTok *grp, const Stage &st, int tid) {
+    if (tid < PIECES * BLK) {
+        const int j = tid / PIECES, p = tid - j * PIECES;
+        *(uint4 *)((char *)&grp[j] + 16 * p) = st.x;
     }
-    // v, beta and dout are the same for every lane of the wave; vz (a zero the compiler
-    // cannot see through) keeps them vector loads, which complete in order, so that a use
-    // waits only for its own load. As scalar loads (out of order) every use would wait for
-    // all loads in flight, the prefetched ones included.
-    x.v = *(const uint4 *)(v + o + c0 + vz);
-    x.beta = beta[th + vz];
-    if (dout) {
-#pragma unroll
-        for (int j = 0; j < CW / 4; ++j) x.dov[j] = ((const float4 *)(dout + o + c0 + vz))[j];
-    }
+    if (tid < BLK) grp[tid].beta[0] = st.beta;
 }
 
-// Make the loads of r complete here (see the block combine in bwd_kernel).
-__device__ __forceinline__ void settle(const Raw &r) {
-    asm volatile("" ::"v"(r.k[0]), "v"(r.k[1]), "v"(r.q[0]), "v"(r.q[1]), "v"(r.g[0]), "v"(r.g[1]), "v"(r.v.x),
-                 "v"(r.v.y), "v"(r.v.z), "v"(r.v.w), "v"(r.dov[0].x), "v"(r.dov[0].y), "v"(r.dov[0].z),
-                 "v"(r.dov[0].w), "v"(r.dov[1].x), "v"(r.dov[1].y), "v"(r.dov[1].z), "v"(r.dov[1].w), "v"(r.beta));
-}
-
-__device__ __forceinline__ void ready(Tok &x, const Raw &r, bool with_dout) {
+// token inputs from a staged token (q and d_out only for the reverse walk)
+__device__ __forceinline__ void tok_from(Tok &x, const InTok &in, int wave, int lane, bool reverse) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        x.k[i] = bf16f(r.k[i]);
-        x.q[i] = bf16f(r.q[i]);
-        x.g[i] = r.g[i];
-        x.e[i] = __expf(fmaxf(r.g[i], LB));
+        x.k[i] = bf16f(in.k[lane + 64 * i]);
+        x.g[i] = in.g[lane + 64 * i];
+        x.e[i] = __expf(fmaxf(x.g[i], LB));
+        x.q[i] = reverse ? bf16f(in.q[lane + 64 * i]) : 0.f;
     }
-    const uint32_t u[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+    const uint4 vv = *(const uint4 *)&in.v[CW * wave];
+    const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         x.v[2 * i] = __uint_as_float(u[i] << 16);
         x.v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
     }
-    x.beta = r.beta;
-    if (with_dout) {
+    x.beta = in.beta[0];
+    if (reverse) {
 #pragma unroll
         for (int j = 0; j < CW / 4; ++j) {
-            x.dov[4 * j] = r.dov[j].x, x.dov[4 * j + 1] = r.dov[j].y;
-            x.dov[4 * j + 2] = r.dov[j].z, x.dov[4 * j + 3] = r.dov[j].w;
+            const float4 f = *(const float4 *)&in.dout[CW * wave + 4 * j];
+            x.dov[4 * j] = f.x, x.dov[4 * j + 1] = f.y, x.dov[4 * j + 2] = f.z, x.dov[4 * j + 3] = f.w;
         }
     }
 }
@@ -211,10 +228,12 @@ __device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][CW],
 }
 
 // Per-wave row gradients of the BLK tokens of a block (double-buffered by block): the waves
-// add them once per block, behind one barrier.
+// add them once per block, behind one barrier. And the staged inputs, two groups.
 struct BwdLds {
     float part[2][BLK][WAVES][3][D];   // dq, dk, dg
     float pb[2][BLK][WAVES];           // dbeta
+    float dv[2][BLK][64];              // the block's value columns of dv
+    InTok in[2][BLK];
 };
 constexpr int BWD_LDS = (int)sizeof(BwdLds);
 static_assert(BWD_LDS <= 160 * 1024, "LDS");
@@ -252,107 +271,80 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
     const int64_t ck_stride = (int64_t)H * D * D;
     float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
-    int vz;   // 0, in a VGPR (see load_raw)
-    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
-    auto raw = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, nullptr, t * H + h, c0, lane, vz); };
-    auto rawd = [&](Raw &x, int64_t t) { load_raw(x, q, k, v, g, beta, dout, t * H + h, c0, lane, vz); };
+    Stage st;
+    auto stage = [&](int64_t t0) { stage_load(st, q, k, v, g, beta, dout, t0, eos - 1, half, H, h, tid); };
+    int buf = 0;   // the staged group in use
 
-    // ---- forward: the state before every BLK-th token. Inputs come through a ring of PF
-    // loads in registers, each issued PF tokens before it is used.
-    constexpr int PF = BLK;
+    // ---- forward: the state before every BLK-th token (the start of every block)
     float S[2][CW];
     load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
-    if (bos < eos) {
-        Raw ring[PF];
+    if (nblk > 0) {
+        stage(bos);
+        stage_store(L.in[0], st, tid);
+        __syncthreads();
+    }
+    // Nothing in flight as the loops start: a load pending from before a loop would be
+    // waited for (with everything issued after it) at its first use in every iteration.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int b = 0; b < nblk; ++b) {
+        const int64_t tb = bos + (int64_t)b * BLK;
+        // the next group: block b + 1, or after the last, the last again for the reverse walk
+        stage(b + 1 < nblk ? tb + BLK : tb);
+        store_slice(ckc + (int64_t)b * ck_stride, S, c0, lane);
+        const InTok *in = L.in[buf];
+        const int nin = (int)std::min((int64_t)BLK, eos - tb);
+        if (nin == BLK) {
 #pragma unroll
-        for (int j = 0; j < PF; ++j) raw(ring[j], bos + j < eos ? bos + j : eos - 1);
-        int64_t t0 = bos;
-        for (; t0 + PF <= eos; t0 += PF) {   // whole groups of PF tokens
-            store_slice(ckc + ((t0 - bos) / BLK) * ck_stride, S, c0, lane);
-#pragma unroll
-            for (int j = 0; j < PF; ++j) {
-                // Nothing here is conditional, and each slot is read before its refill is
-                // issued, so that the refill can take the slot's registers: else the loop's
-                // back edge copies the ring and so waits for every load in flight.
-                const int64_t t = t0 + j;
+            for (int i = 0; i < BLK; ++i) {
                 Tok x;
-                ready(x, ring[j], false);
-                __builtin_amdgcn_sched_barrier(0);
-                raw(ring[j], t + PF < eos ? t + PF : eos - 1);
+                tok_from(x, in[i], wave, lane, false);
                 write_step(S, x, decay_u(S, x, lane));
             }
-        }
-        if (t0 < eos) {   // the last, partial group (already in the ring)
-            store_slice(ckc + ((t0 - bos) / BLK) * ck_stride, S, c0, lane);
+        } else {
 #pragma unroll
-            for (int j = 0; j < PF; ++j) {
-                if (t0 + j < eos) {
+            for (int i = 0; i < BLK; ++i) {
+                if (i < nin) {
                     Tok x;
-                    ready(x, ring[j], false);
+                    tok_from(x, in[i], wave, lane, false);
                     write_step(S, x, decay_u(S, x, lane));
                 }
             }
         }
+        buf ^= 1;
+        stage_store(L.in[buf], st, tid);
+        __syncthreads();
     }
 
-    // ---- backward, block by block from the last. A block's loads take 2 BLK positions:
-    // position i < BLK the inputs of token i (recomputing S1 and u), position 2 BLK - 1 - i
-    // those of token i again (the reverse walk); positions past the block's tokens load a
-    // valid token and are skipped. They come through the same ring, each issued BLK
-    // positions before it is used: recompute token i uses slot i, reverse token i slot
-    // BLK - 1 - i, and each slot is refilled BLK positions on, in this block or the next.
+    // ---- backward, block by block from the last: recompute the block's tokens from its
+    // checkpoint (S1 and u of each kept in registers), then walk them backwards
     float dS[2][CW];
     load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
     int par = 0;
-    Raw ring[BLK];
-    float Sck[2][CW];  // the next block's checkpoint
-    auto tok_pos = [&](int bb, int pos) -> int64_t {
-        const int64_t tbb = bos + (int64_t)bb * BLK;
-        const int nb = (int)std::min((int64_t)BLK, eos - tbb);
-        const int i = pos < BLK ? pos : 2 * BLK - 1 - pos;
-        return tbb + (i < nb ? i : nb - 1);
-    };
-    if (nblk > 0) {
-        load_slice(Sck, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
-#pragma unroll
-        for (int j = 0; j < BLK; ++j) rawd(ring[j], tok_pos(nblk - 1, j));
-    }
-    for (int b = nblk - 1; b >= 0; --b) {
-        const int64_t tb = bos + (int64_t)b * BLK;
-        const int nin = (int)std::min((int64_t)BLK, eos - tb);
+    float Sck[2][CW];
+    if (nblk > 0) load_slice(S, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    auto block = [&](auto full, int64_t tb, int nin, const InTok *in) {
+        constexpr bool FULL = decltype(full)::value;
         float S1s[BLK][2][CW], us[BLK];   // S1 and u of each token of the block
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int c = 0; c < CW; ++c) S[r][c] = Sck[r][c];
-#pragma unroll
-        for (int i = 0; i < BLK; ++i) {   // positions 0 .. BLK - 1
-            Tok x;
-            ready(x, ring[i], false);
-            __builtin_amdgcn_sched_barrier(0);
-            rawd(ring[i], tok_pos(b, BLK + i));   // position BLK + i: reverse token BLK - 1 - i
-            if (i < nin) {
+        for (int i = 0; i < BLK; ++i) {
+            if (FULL || i < nin) {
+                Tok x;
+                tok_from(x, in[i], wave, lane, false);
                 us[i] = decay_u(S, x, lane);
 #pragma unroll
                 for (int r = 0; r < 2; ++r)
 #pragma unroll
                     for (int c = 0; c < CW; ++c) S1s[i][r][c] = S[r][c];
-                if (i + 1 < nin) write_step(S, x, us[i]);
+                if (i + 1 < BLK) write_step(S, x, us[i]);
             }
         }
 #pragma unroll
-        for (int i = BLK - 1; i >= 0; --i) {   // positions BLK .. 2 BLK - 1
-            const int slot = BLK - 1 - i;
+        for (int i = BLK - 1; i >= 0; --i) {
+            if (!FULL && i >= nin) continue;
             Tok x;
-            ready(x, ring[slot], true);
-            __builtin_amdgcn_sched_barrier(0);
-            // the next block's position slot (block 0 reloads its own: unused)
-            rawd(ring[slot], tok_pos(b > 0 ? b - 1 : 0, slot));
-            if (i == 0) load_slice(Sck, ckc + (int64_t)(b > 0 ? b - 1 : 0) * ck_stride, c0, lane);
-            if (i >= nin) continue;
+            tok_from(x, in[i], wave, lane, true);
             const float(&dov)[CW] = x.dov;
-            const int64_t th = (tb + i) * H + h;
-
             const float(&S1)[2][CW] = S1s[i];
             float u[CW], r[CW], d[CW];
             broadcast8(us[i], u);
@@ -383,7 +375,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             const float ddl = colsum8(p, lane);
             float dd[CW];
             broadcast8(ddl, dd);
-            dv[th * D + c0 + col_of_lane(lane)] = x.beta * ddl;   // eight lanes per column, one value
+            if ((lane & 7) == 0) L.dv[par][i][CW * wave + col_of_lane(lane)] = x.beta * ddl;
             float pbeta = 0.f, du[CW];
 #pragma unroll
             for (int c = 0; c < CW; ++c) {
@@ -414,28 +406,73 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             }
             if (lane == 0) L.pb[par][i][wave] = pbeta;
         }
-        // The next block's loads (issued during this block's reverse walk) land before the
-        // atomic adds below are issued, so that waiting for them later does not also wait
-        // for the adds (loads, stores and atomics share one in-order counter).
+    };
+    constexpr int KINDS = 7;   // combine tasks per token: dq, dk, dg (two 64-row pieces each), dv
+    constexpr int TASKS = BLK * KINDS + 1, ROUNDS = (TASKS + WAVES - 1) / WAVES;
+    float cval[ROUNDS] = {};   // the values of a wave's combine tasks (see there)
+    // One block of the walk, with the combine of its row gradients. Only the last block of
+    // a sequence (the first walked) can be partial; the others run the FULL form, whose
+    // combine has a fixed trip count.
+    auto step = [&](auto full, int b) {
+        constexpr bool FULL = decltype(full)::value;
+        const int64_t tb = bos + (int64_t)b * BLK;
+        const int nin = FULL ? BLK : (int)std::min((int64_t)BLK, eos - tb);
+        // the next block's inputs and checkpoint (block 0: its own again, unused)
+        const int bn = b > 0 ? b - 1 : 0;
+        stage(bos + (int64_t)bn * BLK);
+        load_slice(Sck, ckc + (int64_t)bn * ck_stride, c0, lane);
+        block(full, tb, nin, L.in[buf]);
+        // Take the next block's loads here, before this block's atomic adds are issued
+        // (loads, stores and atomics share one in-order counter: a wait for a load issued
+        // after the adds would wait for the adds too).
 #pragma unroll
-        for (int j = 0; j < BLK; ++j) settle(ring[j]);
-        asm volatile("" ::"v"(Sck[0][0]), "v"(Sck[0][1]), "v"(Sck[0][2]), "v"(Sck[0][3]), "v"(Sck[0][4]),
-                     "v"(Sck[0][5]), "v"(Sck[0][6]), "v"(Sck[0][7]), "v"(Sck[1][0]), "v"(Sck[1][1]), "v"(Sck[1][2]),
-                     "v"(Sck[1][3]), "v"(Sck[1][4]), "v"(Sck[1][5]), "v"(Sck[1][6]), "v"(Sck[1][7]));
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int c = 0; c < CW; ++c) S[r][c] = Sck[r][c];
+        buf ^= 1;
+        stage_store(L.in[buf], st, tid);
         __syncthreads();
-        // the block's waves add through LDS, then one atomic add per output and token
-        for (int o = tid; o < nin * (3 * D + 1); o += 64 * WAVES) {
-            const int i = o / (3 * D + 1), rem = o % (3 * D + 1);
-            const int64_t th = (tb + i) * H + h;
-            if (rem == 3 * D) {
-                unsafeAtomicAdd(dbeta + th, sum_waves(&L.pb[par][i][0], 1));
-            } else {
-                const int a = rem / D, row = rem % D;
-                float *dst = a == 0 ? dq : a == 1 ? dk : dg;
-                unsafeAtomicAdd(dst + th * D + row, sum_waves(&L.part[par][i][0][a][row], 3 * D));
+        // The block's waves add through LDS; then per token one atomic add per row of dq,
+        // dk and dg and one for dbeta, and the block's columns of dv (the reverse walk
+        // itself touches no global memory). Each wave takes whole 64-row pieces, so the
+        // output it writes is the same in all its lanes.
+        // Each store's value stays in a register of its own until the next block's combine:
+        // a register a store reads is rewritten only once the store is done (the compiler
+        // waits for that), and by then it long is.
+#pragma unroll
+        for (int it = 0; it < ROUNDS; ++it) {
+            asm volatile("" ::"v"(cval[it]));
+            const int task = wave + WAVES * it;
+            if (task < BLK * KINDS) {
+                const int i = task / KINDS, kind = task % KINDS;
+                if (!FULL && i >= nin) continue;
+                const int64_t th = (tb + i) * H + h;
+                if (kind < 6) {
+                    const int a = kind >> 1, row = 64 * (kind & 1) + lane;
+                    cval[it] = sum_waves(&L.part[par][i][0][a][row], 3 * D);
+                    if (a == 0)
+                        unsafeAtomicAdd(dq + th * D + row, cval[it]);
+                    else if (a == 1)
+                        unsafeAtomicAdd(dk + th * D + row, cval[it]);
+                    else
+                        unsafeAtomicAdd(dg + th * D + row, cval[it]);
+                } else {
+                    cval[it] = L.dv[par][i][lane];
+                    dv[th * D + 64 * half + lane] = cval[it];
+                }
+            } else if (task == BLK * KINDS && lane < nin) {
+                cval[it] = sum_waves(&L.pb[par][lane][0], 1);
+                unsafeAtomicAdd(dbeta + (tb + lane) * H + h, cval[it]);
             }
         }
         par ^= 1;   // the next block writes the other buffer: the barrier above orders its reuse
+    };
+    if (nblk > 0) {
+        if (eos - (bos + (int64_t)(nblk - 1) * BLK) == BLK)
+            step(std::true_type{}, nblk - 1);
+        else
+            step(std::false_type{}, nblk - 1);
+        for (int b = nblk - 2; b >= 0; --b) step(std::true_type{}, b);
     }
     if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
 }
