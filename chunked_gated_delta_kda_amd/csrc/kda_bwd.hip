@@ -250,6 +250,11 @@ __device__ __forceinline__ float sum_waves(const float *p, int stride) {
     return s[0];
 }
 
+// an atomic add and a store to global memory at an address held as an integer
+typedef __attribute__((address_space(1))) float gfloat;
+__device__ __forceinline__ void gadd(uint64_t a, float v) { __builtin_amdgcn_global_atomic_fadd_f32((gfloat *)a, v); }
+__device__ __forceinline__ void gstore(uint64_t a, float v) { *(gfloat *)a = v; }
+
 // grid: 2 blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds a
 // state per block and head
 __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
@@ -409,7 +414,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     };
     constexpr int KINDS = 7;   // combine tasks per token: dq, dk, dg (two 64-row pieces each), dv
     constexpr int TASKS = BLK * KINDS + 1, ROUNDS = (TASKS + WAVES - 1) / WAVES;
-    float cval[ROUNDS] = {};   // the values of a wave's combine tasks (see there)
+    float cval[ROUNDS] = {};      // the values of a wave's combine tasks (see there)
+    uint64_t cadr[ROUNDS] = {};   // and their addresses
     // One block of the walk, with the combine of its row gradients. Only the last block of
     // a sequence (the first walked) can be partial; the others run the FULL form, whose
     // combine has a fixed trip count.
@@ -424,11 +430,15 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
         block(full, tb, nin, L.in[buf]);
         // Take the next block's loads here, before this block's atomic adds are issued
         // (loads, stores and atomics share one in-order counter: a wait for a load issued
-        // after the adds would wait for the adds too).
+        // before the adds, if taken after them, waits for the adds too). The asm pins the
+        // copy here; else the compiler moves it to the loop's back edge.
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int c = 0; c < CW; ++c) S[r][c] = Sck[r][c];
+            for (int c = 0; c < CW; ++c) {
+                S[r][c] = Sck[r][c];
+                asm volatile("" : "+v"(S[r][c]));
+            }
         buf ^= 1;
         stage_store(L.in[buf], st, tid);
         __syncthreads();
@@ -436,12 +446,12 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
         // dk and dg and one for dbeta, and the block's columns of dv (the reverse walk
         // itself touches no global memory). Each wave takes whole 64-row pieces, so the
         // output it writes is the same in all its lanes.
-        // Each store's value stays in a register of its own until the next block's combine:
-        // a register a store reads is rewritten only once the store is done (the compiler
-        // waits for that), and by then it long is.
+        // Each store's address and value stay in registers of their own until the next
+        // block's combine: a register a store reads is rewritten only once the store is
+        // done (the compiler waits for that), and by then it long is.
 #pragma unroll
         for (int it = 0; it < ROUNDS; ++it) {
-            asm volatile("" ::"v"(cval[it]));
+            asm volatile("" ::"v"(cval[it]), "v"(cadr[it]));
             const int task = wave + WAVES * it;
             if (task < BLK * KINDS) {
                 const int i = task / KINDS, kind = task % KINDS;
@@ -451,18 +461,24 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                     const int a = kind >> 1, row = 64 * (kind & 1) + lane;
                     cval[it] = sum_waves(&L.part[par][i][0][a][row], 3 * D);
                     if (a == 0)
-                        unsafeAtomicAdd(dq + th * D + row, cval[it]);
+                        cadr[it] = (uint64_t)(dq + th * D + row);
                     else if (a == 1)
-                        unsafeAtomicAdd(dk + th * D + row, cval[it]);
+                        cadr[it] = (uint64_t)(dk + th * D + row);
                     else
-                        unsafeAtomicAdd(dg + th * D + row, cval[it]);
+                        cadr[it] = (uint64_t)(dg + th * D + row);
+                    asm volatile("" : "+v"(cadr[it]));
+                    gadd(cadr[it], cval[it]);
                 } else {
                     cval[it] = L.dv[par][i][lane];
-                    dv[th * D + 64 * half + lane] = cval[it];
+                    cadr[it] = (uint64_t)(dv + th * D + 64 * half + lane);
+                    asm volatile("" : "+v"(cadr[it]));
+                    gstore(cadr[it], cval[it]);
                 }
             } else if (task == BLK * KINDS && lane < nin) {
                 cval[it] = sum_waves(&L.pb[par][lane][0], 1);
-                unsafeAtomicAdd(dbeta + (tb + lane) * H + h, cval[it]);
+                cadr[it] = (uint64_t)(dbeta + (tb + lane) * H + h);
+                asm volatile("" : "+v"(cadr[it]));
+                gadd(cadr[it], cval[it]);
             }
         }
         par ^= 1;   // the next block writes the other buffer: the barrier above orders its reuse
