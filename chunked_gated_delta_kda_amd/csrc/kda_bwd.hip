@@ -90,10 +90,15 @@ __device__ __forceinline__ void broadcast8(float s, float (&out)[CW]) {
 }
 
 // One token's inputs as a lane uses them: k, q, g and e = exp(max(g, -5)) of its key rows
-// l and l + 64, the wave's CW value columns of v and d_out, and beta.
+// l and l + 64; v of the lane's column in the colsum8 layout (vl); the wave's CW value
+// columns of d_out; beta.
+//
+// Scalars per value column (u, d = beta (v - u), dd, du, and r = v - u) are kept in the
+// colsum8 layout, one column per lane, where each costs one operation; only what the
+// per-element updates use (d, du) is broadcast to the whole wave.
 struct Tok {
     float k[2], q[2], e[2], g[2];
-    float v[CW], dov[CW];
+    float vl, dov[CW];
     float beta;
 };
 
@@ -150,8 +155,10 @@ __device__ __forceinline__ void stage_store(InTok *grp, const Stage &st, int tid
     if (tid < BLK) grp[tid].beta[0] = st.beta;
 }
 
-// token inputs from a staged token (q and d_out only for the reverse walk)
-__device__ __forceinline__ void tok_from(Tok &x, const InTok &in, int wave, int lane, bool reverse) {
+// token inputs from a staged token (q and d_out only for the reverse walk); vz is a zero
+// the compiler cannot see through, which keeps d_out in vector registers (it meets the
+// broadcast d, held in scalar registers, in one operation)
+__device__ __forceinline__ void tok_from(Tok &x, const InTok &in, int wave, int lane, bool reverse, int vz) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         x.k[i] = bf16f(in.k[lane + 64 * i]);
@@ -159,18 +166,12 @@ __device__ __forceinline__ void tok_from(Tok &x, const InTok &in, int wave, int 
         x.e[i] = __expf(fmaxf(x.g[i], LB));
         x.q[i] = reverse ? bf16f(in.q[lane + 64 * i]) : 0.f;
     }
-    const uint4 vv = *(const uint4 *)&in.v[CW * wave];
-    const uint32_t u[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        x.v[2 * i] = __uint_as_float(u[i] << 16);
-        x.v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
+    x.vl = bf16f(in.v[CW * wave + col_of_lane(lane)]);
     x.beta = in.beta[0];
     if (reverse) {
 #pragma unroll
         for (int j = 0; j < CW / 4; ++j) {
-            const float4 f = *(const float4 *)&in.dout[CW * wave + 4 * j];
+            const float4 f = *(const float4 *)&in.dout[CW * wave + 4 * j + vz];
             x.dov[4 * j] = f.x, x.dov[4 * j + 1] = f.y, x.dov[4 * j + 2] = f.z, x.dov[4 * j + 3] = f.w;
         }
     }
@@ -187,16 +188,20 @@ __device__ __forceinline__ float decay_u(float (&S)[2][CW], const Tok &x, int la
     }
     return colsum8(p, lane);
 }
-// S <- S1 + k d^T with d = beta (v - u)
-__device__ __forceinline__ void write_step(float (&S)[2][CW], const Tok &x, float ul) {
-    float u[CW];
-    broadcast8(ul, u);
+// S <- S1 + k d^T, d given in the colsum8 layout
+__device__ __forceinline__ void write_d(float (&S)[2][CW], const Tok &x, float dl) {
+    float d[CW];
+    broadcast8(dl, d);
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
-        const float d = x.beta * (x.v[c] - u[c]);
-        S[0][c] = fmaf(x.k[0], d, S[0][c]);
-        S[1][c] = fmaf(x.k[1], d, S[1][c]);
+        S[0][c] = fmaf(x.k[0], d[c], S[0][c]);
+        S[1][c] = fmaf(x.k[1], d[c], S[1][c]);
     }
+}
+// one token forward: S <- Diag(e) S + k d^T, d = beta (v - S1^T k)
+__device__ __forceinline__ void fwd_step(float (&S)[2][CW], const Tok &x, int lane) {
+    const float ul = decay_u(S, x, lane);
+    write_d(S, x, x.beta * (x.vl - ul));
 }
 
 // this lane's rows l, l + 64 of columns [c0, c0 + CW) of a 128 x 128 fp32 state (zeros
@@ -231,7 +236,7 @@ __device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][CW],
 // add them once per block, behind one barrier. And the staged inputs, two groups.
 struct BwdLds {
     float part[2][BLK][WAVES][3][D];   // dq, dk, dg
-    float pb[2][BLK][WAVES];           // dbeta
+    float pb[2][BLK][WAVES][CW];       // dbeta, per value column
     float dv[2][BLK][64];              // the block's value columns of dv
     InTok in[2][BLK];
 };
@@ -255,6 +260,19 @@ typedef __attribute__((address_space(1))) float gfloat;
 __device__ __forceinline__ void gadd(uint64_t a, float v) { __builtin_amdgcn_global_atomic_fadd_f32((gfloat *)a, v); }
 __device__ __forceinline__ void gstore(uint64_t a, float v) { *(gfloat *)a = v; }
 
+// sum of n consecutive partials, in a fixed order
+template <int N>
+__device__ __forceinline__ float sum_fixed(const float *p) {
+    float s[N];
+#pragma unroll
+    for (int w = 0; w < N; ++w) s[w] = p[w];
+#pragma unroll
+    for (int m = N / 2; m > 0; m >>= 1)
+#pragma unroll
+        for (int w = 0; w < m; ++w) s[w] += s[w + m];
+    return s[0];
+}
+
 // grid: 2 blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds a
 // state per block and head
 __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
@@ -276,6 +294,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
     const int64_t ck_stride = (int64_t)H * D * D;
     float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
+    int vz;   // 0, in a vector register (see tok_from)
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
     Stage st;
     auto stage = [&](int64_t t0) { stage_load(st, q, k, v, g, beta, dout, t0, eos - 1, half, H, h, tid); };
     int buf = 0;   // the staged group in use
@@ -302,16 +322,16 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
 #pragma unroll
             for (int i = 0; i < BLK; ++i) {
                 Tok x;
-                tok_from(x, in[i], wave, lane, false);
-                write_step(S, x, decay_u(S, x, lane));
+                tok_from(x, in[i], wave, lane, false, vz);
+                fwd_step(S, x, lane);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < BLK; ++i) {
                 if (i < nin) {
                     Tok x;
-                    tok_from(x, in[i], wave, lane, false);
-                    write_step(S, x, decay_u(S, x, lane));
+                    tok_from(x, in[i], wave, lane, false, vz);
+                    fwd_step(S, x, lane);
                 }
             }
         }
@@ -330,36 +350,33 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     __builtin_amdgcn_s_waitcnt(0);
     auto block = [&](auto full, int64_t tb, int nin, const InTok *in) {
         constexpr bool FULL = decltype(full)::value;
-        float S1s[BLK][2][CW], us[BLK];   // S1 and u of each token of the block
+        float S1s[BLK][2][CW], rl[BLK], dl[BLK];   // S1, r = v - u and d of each token
 #pragma unroll
         for (int i = 0; i < BLK; ++i) {
             if (FULL || i < nin) {
                 Tok x;
-                tok_from(x, in[i], wave, lane, false);
-                us[i] = decay_u(S, x, lane);
+                tok_from(x, in[i], wave, lane, false, vz);
+                rl[i] = x.vl - decay_u(S, x, lane);
+                dl[i] = x.beta * rl[i];
 #pragma unroll
                 for (int r = 0; r < 2; ++r)
 #pragma unroll
                     for (int c = 0; c < CW; ++c) S1s[i][r][c] = S[r][c];
-                if (i + 1 < BLK) write_step(S, x, us[i]);
+                if (i + 1 < BLK) write_d(S, x, dl[i]);
             }
         }
 #pragma unroll
         for (int i = BLK - 1; i >= 0; --i) {
             if (!FULL && i >= nin) continue;
             Tok x;
-            tok_from(x, in[i], wave, lane, true);
+            tok_from(x, in[i], wave, lane, true, vz);
             const float(&dov)[CW] = x.dov;
             const float(&S1)[2][CW] = S1s[i];
-            float u[CW], r[CW], d[CW];
-            broadcast8(us[i], u);
+            float d[CW];
+            broadcast8(dl[i], d);
             float d_do = 0.f;
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                r[c] = x.v[c] - u[c];
-                d[c] = x.beta * r[c];
-                d_do = fmaf(d[c], dov[c], d_do);
-            }
+            for (int c = 0; c < CW; ++c) d_do = fmaf(d[c], dov[c], d_do);
             // o_t = scale S_t^T q: dq, and the output's term of dS
             float gq[2], gk[2], gg[2];
 #pragma unroll
@@ -378,15 +395,12 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
 #pragma unroll
             for (int c = 0; c < CW; ++c) p[c] = fmaf(dS[1][c], x.k[1], dS[0][c] * x.k[0]);
             const float ddl = colsum8(p, lane);
-            float dd[CW];
-            broadcast8(ddl, dd);
-            if ((lane & 7) == 0) L.dv[par][i][CW * wave + col_of_lane(lane)] = x.beta * ddl;
-            float pbeta = 0.f, du[CW];
-#pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                pbeta = fmaf(dd[c], r[c], pbeta);
-                du[c] = -x.beta * dd[c];
+            if ((lane & 7) == 0) {   // one lane per column
+                L.dv[par][i][CW * wave + col_of_lane(lane)] = x.beta * ddl;
+                L.pb[par][i][wave][col_of_lane(lane)] = ddl * rl[i];
             }
+            float du[CW];
+            broadcast8(-x.beta * ddl, du);
             // dk = dS d + S1 du; dS1 = dS + k du^T; dg = rows of S1 . dS1; dS_{t-1} = Diag(e) dS1
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
@@ -409,7 +423,6 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                 L.part[par][i][wave][1][lane + 64 * rr] = gk[rr];
                 L.part[par][i][wave][2][lane + 64 * rr] = gg[rr];
             }
-            if (lane == 0) L.pb[par][i][wave] = pbeta;
         }
     };
     constexpr int KINDS = 7;   // combine tasks per token: dq, dk, dg (two 64-row pieces each), dv
@@ -475,7 +488,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                     gstore(cadr[it], cval[it]);
                 }
             } else if (task == BLK * KINDS && lane < nin) {
-                cval[it] = sum_waves(&L.pb[par][lane][0], 1);
+                cval[it] = sum_fixed<WAVES * CW>(&L.pb[par][lane][0][0]);
                 cadr[it] = (uint64_t)(dbeta + (tb + lane) * H + h);
                 asm volatile("" : "+v"(cadr[it]));
                 gadd(cadr[it], cval[it]);
