@@ -61,6 +61,7 @@ BYTES_PER_TOKEN_HEAD = 1796
 KERNEL_OWN_BYTES_PER_TOKEN_HEAD = {"prep": 2 * 256 + 512 + 4, "recur": 256 + 512}
 GATED_CONFIG = 3                  # the T=8192 varlen prefill the target sentence names
 GATED_BAR_US = 52.5               # 60% of the HBM roofline for its 252.2 MB
+OTHER_CONFIGS = (1, 4, 5)         # timed after the headline line's two, unless --no-others
 DECODE_METRIC = "KDA decode step tokens/s, 1 MI355X (one token per sequence, dk=dv=128)"
 EVENT_EVERY = 4                   # timed steps per step that records kernel events
 COLD_STEPS = 20                   # extra steps timed after a cache-evicting device write each
@@ -360,12 +361,13 @@ BWD_METRIC = "KDA backward (all gradients) tokens/s, 1 MI355X (dk=dv=128)"
 BWD_BYTES_PER_TOKEN_HEAD = 3 * 256 + 2 * 512 + 4 + 4 * 512 + 4
 
 
-def bench_backward(args, dev):
-    """Backward step: kda_bwd over the whole --config workload per step."""
+def bench_backward(args, dev, cfg=None, cpu=True):
+    """Backward step: kda_bwd over the whole --config (or cfg) workload per step; returns the
+    result dict."""
     import torch
     import chunked_gated_delta_kda_amd as kda
 
-    cfg = args.config
+    cfg = args.config if cfg is None else cfg
     log(f"[bench] backward, config {cfg}: {synth.CONFIGS[cfg]['name']}")
     w = synth.config_workload(cfg)
     d = synth.to_device(w, dev)
@@ -405,7 +407,7 @@ def bench_backward(args, dev):
                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
                         "alg_bytes_per_launch": alg, "avg_call_ms": round(call_ms, 4)},
            "cpu_baseline": None}
-    if not args.no_cpu_baseline:
+    if cpu and not args.no_cpu_baseline:
         import oracle
         # the first two chains of the first sequence, on the oracle (one thread each)
         n_tok = int(w.cu_seqlens[1])
@@ -434,7 +436,7 @@ def bench_backward(args, dev):
                                "kind": "oracle",
                                "sample": f"{len(heads)} of {w.N * w.H} chains ({th} token-heads), fp64, "
                                          f"{dt:.2f} s wall, scaled to tokens of {w.H} heads"}
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def main():
@@ -457,6 +459,9 @@ def main():
                     help="element type of g for the prefill (bf16: the input-byte diet form)")
     ap.add_argument("--no-gated", action="store_true",
                     help="do not also time the T=8192 varlen workload (config 3) after the headline one")
+    ap.add_argument("--no-others", action="store_true",
+                    help="do not also time the other prefill workloads (configs 1, 4, 5) and the backward "
+                         "on config 3 after the headline one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (0: host cores, max 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -489,7 +494,7 @@ def main():
         bench_decode(args, dev)
         return
     if args.backward:
-        bench_backward(args, dev)
+        print(json.dumps(bench_backward(args, dev)), flush=True)
         return
     res = run_prefill(args.config, args, dev, cpu=not args.no_cpu_baseline)
     if args.config != GATED_CONFIG and not args.no_gated:
@@ -497,6 +502,18 @@ def main():
         res["gated_config"] = {k: g[k] for k in ("config", "value", "unit", "ms_per_step", "cold", "kernel_ms",
                                                  "roofline", "path_hbm_frac")}
         res["gated_config"]["bar_ms"] = GATED_BAR_US / 1e3
+    if not args.no_others:
+        # the other prefill workloads and the backward, each timed as above (no CPU leg)
+        others = {}
+        for cfg in OTHER_CONFIGS:
+            if cfg in (args.config, GATED_CONFIG):
+                continue
+            o = run_prefill(cfg, args, dev, cpu=False)
+            others[f"config{cfg}"] = {k: o[k] for k in ("config", "value", "unit", "ms_per_step", "cold")}
+        res["other_configs"] = others
+        b = bench_backward(args, dev, cfg=GATED_CONFIG, cpu=False)
+        res["backward"] = {k: b[k] for k in ("metric", "value", "unit", "ms_per_step", "config")}
+        res["backward"]["avg_call_ms"] = b["roofline"]["avg_call_ms"]
     print(json.dumps(res), flush=True)
 
 
