@@ -33,7 +33,9 @@ that mode prints its own JSON line (backward tokens/s), with parity of sampled c
 against the backward oracle.
 """
 import argparse
+import contextlib
 import ctypes
+import gc
 import json
 import math
 import os
@@ -46,6 +48,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from chunked_gated_delta_kda_amd import synth  # noqa: E402
+
+
+@contextlib.contextmanager
+def no_gc():
+    """No garbage-collector pause inside a timed region (collect before it)."""
+    gc.collect()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
 
 METRIC = "KDA prefill fwd tokens/s + % bf16 MFMA peak, 1 MI355X (T=8192, dk=dv=128)"
 HBM_PEAK_GBS = 8000.0             # MI355X HBM3E, published
@@ -306,13 +319,14 @@ def bench_decode(args, dev):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with no_gc():
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record()
+            step()
+            b.record()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     copy_calibration(args, dev)
@@ -387,13 +401,14 @@ def bench_backward(args, dev, cfg=None, cpu=True):
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for a, b in evs:
-        a.record()
-        gr = step()
-        b.record()
-    torch.cuda.synchronize()
-    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    with no_gc():
+        t0 = time.perf_counter()
+        for a, b in evs:
+            a.record()
+            gr = step()
+            b.record()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     alg = w.T * w.H * BWD_BYTES_PER_TOKEN_HEAD + w.N * w.H * STATE_BYTES * (3 if w.initial_state is not None else 2)
     achieved = alg / (call_ms / 1e3) / 1e9
@@ -562,11 +577,12 @@ def run_prefill(cfg, args, dev, cpu):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(step_events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    with no_gc():
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(step_events[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = {nm: 0.0 for nm in names}
     sampled = [e for e in step_events if e is not None]
