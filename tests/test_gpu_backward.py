@@ -120,20 +120,31 @@ def _sub_workload(w, seqs, heads):
                           cu_seqlens=cu, initial_state=s0, scale=w.scale), rows
 
 
-def test_bwd_config3_sampled_chains():
-    """8 x 1024 tokens x 16 heads with initial state, run whole on the GPU; six chains
-    compared with the oracle run on those chains alone."""
+@pytest.mark.parametrize("cfg", [3, 2])
+def test_bwd_config_every_chain(cfg):
+    """The full workloads, 8 x 1024 tokens x 16 heads with initial states (config 3) and
+    8192 tokens x 32 heads (config 2), run whole on the GPU: every chain compared with the
+    oracle, element by element."""
+    w = synth.config_workload(cfg)
+    _below_bound(w, cfg, frac=0.01)
+    do, dsf = _grads_in(w, cfg, True)
+    _say(f"[bwd] config {cfg} ({w.N} sequences, {w.T} tokens, {w.H} heads), every chain")
+    _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), f"config {cfg}")
+
+
+def test_bwd_chains_alone_match_the_batch():
+    """Chains are independent: two sequences x three heads of config 3 run as a batch of their
+    own give the same gradients as inside the whole batch (bit for bit)."""
     w = synth.config_workload(3)
     _below_bound(w, 3, frac=0.01)
     do, dsf = _grads_in(w, 3, True)
-    _say("[bwd] config 3 (8 x 1024 x 16), whole batch on the GPU")
     got = _run_gpu(w, do, dsf)
     seqs, heads = [0, 5], [0, 7, 15]
     sw, rows = _sub_workload(w, seqs, heads)
-    ref = _run_oracle(sw, np.ascontiguousarray(do[rows][:, heads]),
-                      np.ascontiguousarray(dsf[np.ix_(seqs, heads)]))
-    sub = {n: (got[n][np.ix_(seqs, heads)] if n == "d_initial_state" else got[n][rows][:, heads]) for n in NAMES}
-    _check(sub, ref, "config 3 chains")
+    alone = _run_gpu(sw, np.ascontiguousarray(do[rows][:, heads]), np.ascontiguousarray(dsf[np.ix_(seqs, heads)]))
+    for n in NAMES:
+        sub = got[n][np.ix_(seqs, heads)] if n == "d_initial_state" else got[n][rows][:, heads]
+        assert np.array_equal(sub, alone[n]), n
 
 
 def test_bwd_deterministic():
