@@ -25,9 +25,11 @@
 //
 // The reverse walk needs the state before every token: a forward pass stores the state
 // every BLK tokens in the workspace, then, block by block from the last, the block's
-// tokens are recomputed from its checkpoint, keeping S1 and u of each in registers, and
-// walked backwards. Work per token is O(dk dv) on the vector units (no MFMA): a token
-// loop, not the chunked form; one chain occupies two CUs for the length of its sequence.
+// tokens are recomputed from its checkpoint, keeping S1 and r of each in registers, and
+// walked backwards. The inputs of a block of tokens reach the waves through LDS, loaded
+// while the previous block computes. Work per token is O(dk dv) on the vector units (no
+// MFMA): a token loop, not the chunked form; one chain occupies two CUs for the length of
+// its sequence.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
