@@ -533,18 +533,37 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
 // Backward workspace: the head of the forward's (chunk offsets at KDA_BWD_BLOCK tokens,
 // order, error word, sanitised offsets), then a state per block of KDA_BWD_BLOCK tokens
 // and head.
-static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *total) {
+// Waves per backward workgroup: 8 (two workgroups per (sequence, head), their sums added
+// onto zeroed outputs) once the batch has 128 chains (256 workgroups, one per CU); for
+// fewer chains 4 or 2 (4 or 8 workgroups per chain, partial sums added by a last kernel),
+// so that the batch occupies more CUs, unless the partial sums would pass 8 GiB.
+// KDA_BWD_WAVES overrides the choice (for tests and tuning).
+static int bwd_waves(int64_t N, int64_t T, int64_t H) {
+    if (const char *e = std::getenv("KDA_BWD_WAVES")) {
+        const int w = std::atoi(e);
+        if (w == 8 || w == 4 || w == 2) return w;
+    }
+    const int64_t chains = N * H;
+    int w = chains >= 128 ? 8 : chains >= 64 ? 4 : 2;
+    while (w < 8 && kda::bwd_partial_floats(T, H, w) * 4 > ((int64_t)8 << 30)) w *= 2;
+    return w;
+}
+
+static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *psum, size_t *total, int *waves) {
     if (!shape_ok(N, T, H)) return false;
     if (max_chunks(N, T, KDA_BWD_BLOCK) * H > (int64_t)1 << 31) return false;
     const Layout L = ws_layout(N, T, H, KDA_VARIANT_FUSED, 1, 0);
+    *waves = bwd_waves(N, T, H);
     *ck = L.total;
-    *total = *ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES;
+    *psum = *ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES;
+    *total = *psum + (size_t)kda::bwd_partial_floats(T, H, *waves) * sizeof(float);
     return true;
 }
 
 size_t kda_bwd_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads) {
-    size_t ck = 0, total = 0;
-    return bwd_layout(num_seqs, total_tokens, num_heads, &ck, &total) ? total : 0;
+    size_t ck = 0, psum = 0, total = 0;
+    int waves = 0;
+    return bwd_layout(num_seqs, total_tokens, num_heads, &ck, &psum, &total, &waves) ? total : 0;
 }
 
 int kda_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
@@ -556,8 +575,9 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    size_t ck_at = 0, total = 0;
-    if (!bwd_layout(N, T, H, &ck_at, &total)) return KDA_ERR_SHAPE;
+    size_t ck_at = 0, psum_at = 0, total = 0;
+    int waves = 0;
+    if (!bwd_layout(N, T, H, &ck_at, &psum_at, &total, &waves)) return KDA_ERR_SHAPE;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (T > 0 && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg || !dbeta))
         return KDA_ERR_NULL;
@@ -582,7 +602,7 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     if (kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, KDA_BWD_BLOCK, st) != hipSuccess ||
         kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale, cus, chunk_off,
                         N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
-                        (float *)(ws + ck_at), st) != hipSuccess)
+                        (float *)(ws + ck_at), (float *)(ws + psum_at), waves, st) != hipSuccess)
         rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;

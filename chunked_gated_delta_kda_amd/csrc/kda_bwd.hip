@@ -44,10 +44,23 @@ namespace {
 
 constexpr int BLK = KDA_BWD_BLOCK;      // tokens per checkpoint
 constexpr int CW = 8;                   // value columns per wave
-constexpr int WAVES = 8;                // waves per block: 64 value columns
-constexpr int HALVES = D / (CW * WAVES);
 constexpr float LB = KDA_LOWER_BOUND;
-static_assert(HALVES == 2, "two blocks per chain: the atomic sums have two addends");
+
+// A block of NWV waves owns NCOL = 8 NWV value columns of one chain; PARTS blocks make the
+// chain. With 8 waves (two blocks per chain) the blocks add their row gradients straight
+// into the zeroed outputs (two addends onto zero: the result does not depend on their
+// order); with 4 or 2 waves (for batches of few chains, to occupy more CUs) each block
+// writes its partial sums and bwd_sum_kernel adds the PARTS of them in a fixed order.
+template <int NWV>
+struct Geo {
+    static constexpr int NCOL = CW * NWV, PARTS = D / NCOL, THREADS = 64 * NWV;
+    static constexpr bool ATOMIC = PARTS == 2;
+    // pieces of 16 bytes of a staged token, in this order: k, g, v (the block's columns), q,
+    // d_out (the block's columns); then beta
+    static constexpr int PK = 0, PG = 16, PV = 48, PQ = PV + NCOL * 2 / 16, PO = PQ + 16;
+    static constexpr int PIECES = PO + NCOL * 4 / 16;
+    static constexpr int PER_THREAD = (PIECES * BLK + THREADS - 1) / THREADS;
+};
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
@@ -105,62 +118,83 @@ struct Tok {
 };
 
 // The inputs reach the waves through LDS, a group of BLK tokens at a time: while the block
-// computes on one group, each thread has one 16-byte piece of the next group in flight,
-// and stores it at the end of the group, behind the group's barrier. So a load is only
-// waited for after a whole group of computation, in either direction of the walk, and the
-// waves issue no per-token loads. A staged token is the pieces below, in this order.
-constexpr int PK = 0, PG = 16, PV = 48, PQ = 56, PO = 72, PIECES = 88;
+// computes on one group, each thread has its pieces (16 bytes each) of the next group in
+// flight, and stores them at the end of the group, behind the group's barrier. So a load
+// is only waited for after a whole group of computation, in either direction of the walk,
+// and the waves issue no per-token loads. A staged token is the pieces of Geo, in order.
+template <int NCOL>
 struct InTok {
-    uint16_t k[D];      // pieces PK..: bf16 bits
-    float g[D];         // PG..
-    uint16_t v[64];     // PV..: the block's 64 value columns, bf16 bits
-    uint16_t q[D];      // PQ..
-    float dout[64];     // PO..: the block's 64 value columns
-    float beta[4];      // [0]
+    uint16_t k[D];        // bf16 bits
+    float g[D];
+    uint16_t v[NCOL];     // the block's value columns, bf16 bits
+    uint16_t q[D];
+    float dout[NCOL];     // the block's value columns
+    float beta[4];        // [0]
 };
-static_assert(sizeof(InTok) == 16 * PIECES + 16, "staged token: whole pieces, then beta");
 
+template <int NWV>
 struct Stage {
-    uint4 x;      // this thread's piece
-    float beta;   // beta of token (tid mod BLK) of the group
+    uint4 x0, x1, x2;   // this thread's pieces (Geo::PER_THREAD of them; kept as scalars, an
+                        // array here ended up in scratch memory)
+    float beta;         // beta of token (tid mod BLK) of the group
+    static_assert(Geo<NWV>::PER_THREAD <= 3, "pieces per thread");
 };
 
-// Load this thread's piece of the group of BLK tokens starting at t0 (tokens past last
-// repeat it: their pieces are loaded and stored but never read).
-__device__ __forceinline__ void stage_load(Stage &st, const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                           const uint16_t *__restrict__ v, const float *__restrict__ g,
-                                           const float *__restrict__ beta, const float *__restrict__ dout,
-                                           int64_t t0, int64_t last, int half, int H, int h, int tid) {
-    const int idx = min(tid, PIECES * BLK - 1);
-    const int j = idx / PIECES, p = idx - j * PIECES;
-    const int64_t t = min(t0 + j, last);
-    const int64_t o = (t * H + h) * D;
-    const char *src;
-    if (p < PG)
-        src = (const char *)(k + o) + 16 * (p - PK);
-    else if (p < PV)
-        src = (const char *)(g + o) + 16 * (p - PG);
-    else if (p < PQ)
-        src = (const char *)(v + o + 64 * half) + 16 * (p - PV);
-    else if (p < PO)
-        src = (const char *)(q + o) + 16 * (p - PQ);
-    else
-        src = (const char *)(dout + o + 64 * half) + 16 * (p - PO);
-    st.x = *(const uint4 *)src;
+// Load this thread's pieces of the group of BLK tokens starting at t0 (tokens past last
+// repeat it: their pieces are loaded and stored but never read; so are the repeats of the
+// last piece that fill the threads' share).
+template <int NWV>
+__device__ __forceinline__ void stage_load(Stage<NWV> &st, const uint16_t *__restrict__ q,
+                                           const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+                                           const float *__restrict__ g, const float *__restrict__ beta,
+                                           const float *__restrict__ dout, int64_t t0, int64_t last, int part,
+                                           int H, int h, int tid) {
+    using G = Geo<NWV>;
+    auto piece = [&](int m) -> uint4 {
+        const int idx = min(tid + G::THREADS * m, G::PIECES * BLK - 1);
+        const int j = idx / G::PIECES, p = idx - j * G::PIECES;
+        const int64_t t = min(t0 + j, last);
+        const int64_t o = (t * H + h) * D;
+        const int cb = G::NCOL * part;   // the block's first value column
+        const char *src;
+        if (p < G::PG)
+            src = (const char *)(k + o) + 16 * (p - G::PK);
+        else if (p < G::PV)
+            src = (const char *)(g + o) + 16 * (p - G::PG);
+        else if (p < G::PQ)
+            src = (const char *)(v + o + cb) + 16 * (p - G::PV);
+        else if (p < G::PO)
+            src = (const char *)(q + o) + 16 * (p - G::PQ);
+        else
+            src = (const char *)(dout + o + cb) + 16 * (p - G::PO);
+        return *(const uint4 *)src;
+    };
+    st.x0 = piece(0);
+    if constexpr (G::PER_THREAD > 1) st.x1 = piece(1);
+    if constexpr (G::PER_THREAD > 2) st.x2 = piece(2);
     st.beta = beta[min(t0 + (tid & (BLK - 1)), last) * H + h];
 }
-__device__ __forceinline__ void stage_store(InTok *grp, const Stage &st, int tid) {
-    if (tid < PIECES * BLK) {
-        const int j = tid / PIECES, p = tid - j * PIECES;
-        *(uint4 *)((char *)&grp[j] + 16 * p) = st.x;
-    }
+template <int NWV>
+__device__ __forceinline__ void stage_store(InTok<Geo<NWV>::NCOL> *grp, const Stage<NWV> &st, int tid) {
+    using G = Geo<NWV>;
+    auto put = [&](int m, const uint4 &x) {
+        const int idx = tid + G::THREADS * m;
+        if (idx < G::PIECES * BLK) {
+            const int j = idx / G::PIECES, p = idx - j * G::PIECES;
+            *(uint4 *)((char *)&grp[j] + 16 * p) = x;
+        }
+    };
+    put(0, st.x0);
+    if constexpr (G::PER_THREAD > 1) put(1, st.x1);
+    if constexpr (G::PER_THREAD > 2) put(2, st.x2);
     if (tid < BLK) grp[tid].beta[0] = st.beta;
 }
 
 // token inputs from a staged token (q and d_out only for the reverse walk); vz is a zero
 // the compiler cannot see through, which keeps d_out in vector registers (it meets the
 // broadcast d, held in scalar registers, in one operation)
-__device__ __forceinline__ void tok_from(Tok &x, const InTok &in, int wave, int lane, bool reverse, int vz) {
+template <int NCOL>
+__device__ __forceinline__ void tok_from(Tok &x, const InTok<NCOL> &in, int wave, int lane, bool reverse, int vz) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         x.k[i] = bf16f(in.k[lane + 64 * i]);
@@ -236,28 +270,36 @@ __device__ __forceinline__ void store_slice(float *dst, const float (&S)[2][CW],
 
 // Per-wave row gradients of the BLK tokens of a block (double-buffered by block): the waves
 // add them once per block, behind one barrier. And the staged inputs, two groups.
+template <int NWV>
 struct BwdLds {
-    float part[2][BLK][WAVES][3][D];   // dq, dk, dg
-    float pb[2][BLK][WAVES][CW];       // dbeta, per value column
-    float dv[2][BLK][64];              // the block's value columns of dv
-    InTok in[2][BLK];
+    float part[2][BLK][NWV][3][D];   // dq, dk, dg
+    float pb[2][BLK][NWV][CW];       // dbeta, per value column
+    float dv[2][BLK][Geo<NWV>::NCOL];
+    InTok<Geo<NWV>::NCOL> in[2][BLK];
 };
-constexpr int BWD_LDS = (int)sizeof(BwdLds);
-static_assert(BWD_LDS <= 160 * 1024, "LDS");
+template <int NWV>
+constexpr int bwd_lds() {
+    static_assert(sizeof(InTok<Geo<NWV>::NCOL>) == 16 * Geo<NWV>::PIECES + 16, "staged token: whole pieces, beta");
+    static_assert(sizeof(BwdLds<NWV>) <= 160 * 1024, "LDS");
+    return (int)sizeof(BwdLds<NWV>);
+}
 
-// sum of the block's WAVES partials of one output (stride apart), in a fixed order
+// sum of a block's NWV partials of one output (stride apart), in a fixed order
+template <int NWV>
 __device__ __forceinline__ float sum_waves(const float *p, int stride) {
-    float s[WAVES];
+    float s[NWV];
 #pragma unroll
-    for (int w = 0; w < WAVES; ++w) s[w] = p[w * stride];
+    for (int w = 0; w < NWV; ++w) s[w] = p[w * stride];
 #pragma unroll
-    for (int m = WAVES / 2; m > 0; m >>= 1)
+    for (int m = NWV / 2; m > 0; m >>= 1)
 #pragma unroll
         for (int w = 0; w < m; ++w) s[w] += s[w + m];
     return s[0];
 }
 
 // an atomic add and a store to global memory at an address held as an integer
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) f4v gf4v;
 typedef __attribute__((address_space(1))) float gfloat;
 __device__ __forceinline__ void gadd(uint64_t a, float v) { __builtin_amdgcn_global_atomic_fadd_f32((gfloat *)a, v); }
 __device__ __forceinline__ void gstore(uint64_t a, float v) { *(gfloat *)a = v; }
@@ -275,22 +317,27 @@ __device__ __forceinline__ float sum_fixed(const float *p) {
     return s[0];
 }
 
-// grid: 2 blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds a
-// state per block and head
-__global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
+// grid: PARTS blocks per (sequence, head); chunk_off counts blocks of BLK tokens; ck holds
+// a state per block of tokens and head. Without ATOMIC, the row gradients go to psum
+// ([PARTS][T H][3][128]: dq, dk, dg) and pbeta ([PARTS][T H]) instead of dq, dk, dg, dbeta.
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, float scale, const int32_t *__restrict__ cu,
     const int32_t *__restrict__ chunk_off, int H, const float *__restrict__ s0, const float *__restrict__ dout,
     const float *__restrict__ dsf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
-    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck) {
-    extern __shared__ __attribute__((aligned(16))) char bwd_lds[];
-    BwdLds &L = *(BwdLds *)bwd_lds;
-    const int bid = xcd_remap(blockIdx.x, gridDim.x, HALVES);
-    const int half = bid % HALVES, chain = bid / HALVES;
+    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck,
+    float *__restrict__ psum, float *__restrict__ pbeta, int64_t TH) {
+    using G = Geo<NWV>;
+    constexpr int NCOL = G::NCOL;
+    extern __shared__ __attribute__((aligned(16))) char bwd_smem[];
+    BwdLds<NWV> &L = *(BwdLds<NWV> *)bwd_smem;
+    const int bid = xcd_remap(blockIdx.x, gridDim.x, G::PARTS);
+    const int part = bid % G::PARTS, chain = bid / G::PARTS;
     const int h = chain % H, n = chain / H;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
-    const int c0 = 64 * half + CW * wave;
+    const int c0 = NCOL * part + CW * wave;
     const int64_t bos = cu[n], eos = cu[n + 1];
     const int nblk = (int)((eos - bos + BLK - 1) / BLK);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
@@ -298,8 +345,8 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     float *ckc = ck + (int64_t)chunk_off[n] * ck_stride + (int64_t)h * D * D;   // block b: ckc + b ck_stride
     int vz;   // 0, in a vector register (see tok_from)
     asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
-    Stage st;
-    auto stage = [&](int64_t t0) { stage_load(st, q, k, v, g, beta, dout, t0, eos - 1, half, H, h, tid); };
+    Stage<NWV> st;
+    auto stage = [&](int64_t t0) { stage_load<NWV>(st, q, k, v, g, beta, dout, t0, eos - 1, part, H, h, tid); };
     int buf = 0;   // the staged group in use
 
     // ---- forward: the state before every BLK-th token (the start of every block)
@@ -307,7 +354,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
     if (nblk > 0) {
         stage(bos);
-        stage_store(L.in[0], st, tid);
+        stage_store<NWV>(L.in[0], st, tid);
         __syncthreads();
     }
     // Nothing in flight as the loops start: a load pending from before a loop would be
@@ -318,7 +365,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
         // the next group: block b + 1, or after the last, the last again for the reverse walk
         stage(b + 1 < nblk ? tb + BLK : tb);
         store_slice(ckc + (int64_t)b * ck_stride, S, c0, lane);
-        const InTok *in = L.in[buf];
+        const InTok<NCOL> *in = L.in[buf];
         const int nin = (int)std::min((int64_t)BLK, eos - tb);
         if (nin == BLK) {
 #pragma unroll
@@ -338,7 +385,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
             }
         }
         buf ^= 1;
-        stage_store(L.in[buf], st, tid);
+        stage_store<NWV>(L.in[buf], st, tid);
         __syncthreads();
     }
 
@@ -350,7 +397,7 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
     float Sck[2][CW];
     if (nblk > 0) load_slice(S, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
     __builtin_amdgcn_s_waitcnt(0);
-    auto block = [&](auto full, int64_t tb, int nin, const InTok *in) {
+    auto block = [&](auto full, int64_t tb, int nin, const InTok<NCOL> *in) {
         constexpr bool FULL = decltype(full)::value;
         float S1s[BLK][2][CW], rl[BLK], dl[BLK];   // S1, r = v - u and d of each token
 #pragma unroll
@@ -428,9 +475,12 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
         }
     };
     constexpr int KINDS = 7;   // combine tasks per token: dq, dk, dg (two 64-row pieces each), dv
-    constexpr int TASKS = BLK * KINDS + 1, ROUNDS = (TASKS + WAVES - 1) / WAVES;
-    float cval[ROUNDS] = {};      // the values of a wave's combine tasks (see there)
-    uint64_t cadr[ROUNDS] = {};   // and their addresses
+    constexpr int TASKS = BLK * KINDS + 1, ROUNDS = (TASKS + NWV - 1) / NWV;
+    constexpr int CROUNDS = G::ATOMIC ? ROUNDS : 1, PROUNDS = G::ATOMIC ? 1 : (BLK * 3 * D / 4 + G::THREADS - 1) / G::THREADS;
+    float cval[CROUNDS] = {};      // the values of a wave's combine tasks (see there)
+    uint64_t cadr[CROUNDS] = {};   // and their addresses
+    f4v pval[PROUNDS] = {};        // without ATOMIC, the partial sums stored
+    uint64_t padr[PROUNDS] = {};
     // One block of the walk, with the combine of its row gradients. Only the last block of
     // a sequence (the first walked) can be partial; the others run the FULL form, whose
     // combine has a fixed trip count.
@@ -455,45 +505,101 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
                 asm volatile("" : "+v"(S[r][c]));
             }
         buf ^= 1;
-        stage_store(L.in[buf], st, tid);
+        stage_store<NWV>(L.in[buf], st, tid);
         __syncthreads();
-        // The block's waves add through LDS; then per token one atomic add per row of dq,
-        // dk and dg and one for dbeta, and the block's columns of dv (the reverse walk
-        // itself touches no global memory). Each wave takes whole 64-row pieces, so the
-        // output it writes is the same in all its lanes.
-        // Each store's address and value stay in registers of their own until the next
-        // block's combine: a register a store reads is rewritten only once the store is
-        // done (the compiler waits for that), and by then it long is.
-#pragma unroll
-        for (int it = 0; it < ROUNDS; ++it) {
-            asm volatile("" ::"v"(cval[it]), "v"(cadr[it]));
-            const int task = wave + WAVES * it;
-            if (task < BLK * KINDS) {
-                const int i = task / KINDS, kind = task % KINDS;
-                if (!FULL && i >= nin) continue;
-                const int64_t th = (tb + i) * H + h;
-                if (kind < 6) {
-                    const int a = kind >> 1, row = 64 * (kind & 1) + lane;
-                    cval[it] = sum_waves(&L.part[par][i][0][a][row], 3 * D);
-                    if (a == 0)
-                        cadr[it] = (uint64_t)(dq + th * D + row);
-                    else if (a == 1)
-                        cadr[it] = (uint64_t)(dk + th * D + row);
+        // The block's waves add through LDS; then per token one atomic add (or, without
+        // ATOMIC, one store of the partial sum) per row of dq, dk and dg and one for dbeta,
+        // and the block's columns of dv (the reverse walk itself touches no global
+        // memory). Each wave takes whole 64-row pieces, so the output it writes is the same
+        // in all its lanes.
+        if constexpr (G::ATOMIC) {
+            // Each store's address and value stay in registers of their own until the next
+            // block's combine: a register a store reads is rewritten only once the store is
+            // done (the compiler waits for that), and by then it long is.
+    #pragma unroll
+            for (int it = 0; it < ROUNDS; ++it) {
+                asm volatile("" ::"v"(cval[it]), "v"(cadr[it]));
+                const int task = wave + NWV * it;
+                if (task < BLK * KINDS) {
+                    const int i = task / KINDS, kind = task % KINDS;
+                    if (!FULL && i >= nin) continue;
+                    const int64_t th = (tb + i) * H + h;
+                    if (kind < 6) {
+                        const int a = kind >> 1, row = 64 * (kind & 1) + lane;
+                        cval[it] = sum_waves<NWV>(&L.part[par][i][0][a][row], 3 * D);
+                        if (!G::ATOMIC)
+                            cadr[it] = (uint64_t)(psum + (((int64_t)part * TH + th) * 3 + a) * D + row);
+                        else if (a == 0)
+                            cadr[it] = (uint64_t)(dq + th * D + row);
+                        else if (a == 1)
+                            cadr[it] = (uint64_t)(dk + th * D + row);
+                        else
+                            cadr[it] = (uint64_t)(dg + th * D + row);
+                        asm volatile("" : "+v"(cadr[it]));
+                        if (G::ATOMIC)
+                            gadd(cadr[it], cval[it]);
+                        else
+                            gstore(cadr[it], cval[it]);
+                    } else if (lane < NCOL) {
+                        cval[it] = L.dv[par][i][lane];
+                        cadr[it] = (uint64_t)(dv + th * D + NCOL * part + lane);
+                        asm volatile("" : "+v"(cadr[it]));
+                        gstore(cadr[it], cval[it]);
+                    }
+                } else if (task == BLK * KINDS && lane < nin) {
+                    cval[it] = sum_fixed<NWV * CW>(&L.pb[par][lane][0][0]);
+                    const int64_t th = (tb + lane) * H + h;
+                    cadr[it] = (uint64_t)(G::ATOMIC ? dbeta + th : pbeta + (int64_t)part * TH + th);
+                    asm volatile("" : "+v"(cadr[it]));
+                    if (G::ATOMIC)
+                        gadd(cadr[it], cval[it]);
                     else
-                        cadr[it] = (uint64_t)(dg + th * D + row);
-                    asm volatile("" : "+v"(cadr[it]));
-                    gadd(cadr[it], cval[it]);
-                } else {
-                    cval[it] = L.dv[par][i][lane];
-                    cadr[it] = (uint64_t)(dv + th * D + 64 * half + lane);
-                    asm volatile("" : "+v"(cadr[it]));
-                    gstore(cadr[it], cval[it]);
+                        gstore(cadr[it], cval[it]);
                 }
-            } else if (task == BLK * KINDS && lane < nin) {
-                cval[it] = sum_fixed<WAVES * CW>(&L.pb[par][lane][0][0]);
-                cadr[it] = (uint64_t)(dbeta + (tb + lane) * H + h);
-                asm volatile("" : "+v"(cadr[it]));
-                gadd(cadr[it], cval[it]);
+            }
+        } else {
+            // The partial sums, a float4 of 4 rows per thread and round (a token's 384 rows
+            // of dq, dk, dg are contiguous in psum), then dv and dbeta, one value per thread.
+            // As above, each store's value and address stay in registers of their own.
+#pragma unroll
+            for (int m = 0; m < PROUNDS; ++m) {
+                asm volatile("" ::"v"(pval[m]), "v"(padr[m]));
+                const int idx = tid + G::THREADS * m;
+                const int i = idx / (3 * D / 4), f = idx % (3 * D / 4);
+                if (idx < BLK * 3 * D / 4 && (FULL || i < nin)) {
+                    const int a = f / (D / 4), r4 = 4 * (f % (D / 4));
+                    const f4v *src = (const f4v *)&L.part[par][i][0][a][r4];
+                    f4v x[NWV];
+#pragma unroll
+                    for (int w = 0; w < NWV; ++w) x[w] = src[w * (3 * D / 4)];
+#pragma unroll
+                    for (int mm = NWV / 2; mm > 0; mm >>= 1)
+#pragma unroll
+                        for (int w = 0; w < mm; ++w) x[w] += x[w + mm];
+                    pval[m] = x[0];
+                    const int64_t th = (tb + i) * H + h;
+                    padr[m] = (uint64_t)(psum + (((int64_t)part * TH + th) * 3 + a) * D + r4);
+                    asm volatile("" : "+v"(padr[m]));
+                    *(gf4v *)padr[m] = pval[m];
+                }
+            }
+            asm volatile("" ::"v"(cval[0]), "v"(cadr[0]));
+            if (tid < BLK * NCOL) {
+                const int i = tid / NCOL, c = tid % NCOL;
+                if (FULL || i < nin) {
+                    cval[0] = L.dv[par][i][c];
+                    cadr[0] = (uint64_t)(dv + ((tb + i) * H + h) * D + NCOL * part + c);
+                    asm volatile("" : "+v"(cadr[0]));
+                    gstore(cadr[0], cval[0]);
+                }
+            } else if (tid < BLK * NCOL + BLK) {
+                const int i = tid - BLK * NCOL;
+                if (FULL || i < nin) {
+                    cval[0] = sum_fixed<NWV * CW>(&L.pb[par][i][0][0]);
+                    cadr[0] = (uint64_t)(pbeta + (int64_t)part * TH + (tb + i) * H + h);
+                    asm volatile("" : "+v"(cadr[0]));
+                    gstore(cadr[0], cval[0]);
+                }
             }
         }
         par ^= 1;   // the next block writes the other buffer: the barrier above orders its reuse
@@ -506,6 +612,46 @@ __global__ __launch_bounds__(64 * WAVES) void bwd_kernel(
         for (int b = nblk - 2; b >= 0; --b) step(std::true_type{}, b);
     }
     if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
+}
+
+// dq, dk, dg and dbeta as the fixed-order sums of the PARTS blocks' partials (psum
+// [PARTS][T H][3][128], pbeta [PARTS][T H]); zeros for tokens outside the sequences
+// (before cu[0] or from cu[N] on, possible only for offsets that were sanitised), which
+// no block writes
+template <int PARTS>
+__global__ __launch_bounds__(256) void bwd_sum_kernel(const float4 *__restrict__ psum, const float *__restrict__ pbeta,
+                                                      float4 *__restrict__ dq, float4 *__restrict__ dk,
+                                                      float4 *__restrict__ dg, float *__restrict__ dbeta, int64_t TH,
+                                                      int H, const int32_t *__restrict__ cu, int N) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t n4 = TH * 3 * D / 4;
+    const int64_t t_lo = cu[0], t_hi = cu[N];
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const int64_t th = i / (3 * D / 4), r = i % (3 * D / 4);
+        const int64_t t = th / H;
+        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t >= t_lo && t < t_hi) {
+            s = psum[i];
+#pragma unroll
+            for (int p = 1; p < PARTS; ++p) {
+                const float4 x = psum[(int64_t)p * n4 + i];
+                s.x += x.x, s.y += x.y, s.z += x.z, s.w += x.w;
+            }
+        }
+        const int a = (int)(r / (D / 4));
+        float4 *dst = a == 0 ? dq : a == 1 ? dk : dg;
+        dst[th * (D / 4) + r % (D / 4)] = s;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < TH; i += stride) {
+        const int64_t t = i / H;
+        float s = 0.f;
+        if (t >= t_lo && t < t_hi) {
+            s = pbeta[i];
+#pragma unroll
+            for (int p = 1; p < PARTS; ++p) s += pbeta[(int64_t)p * TH + i];
+        }
+        dbeta[i] = s;
+    }
 }
 
 // zero dq, dk, dg ([n4] float4 each) and dbeta ([nb] floats): the backward adds into them
@@ -523,23 +669,52 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *dq, float4 *dk, f
 
 }  // namespace
 
-hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
-                      const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
-                      float *dg, float *dbeta, float *ds0, float *ck, hipStream_t st) {
+template <int NWV>
+static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                                  const float *beta, float scale, const int32_t *cu_safe, const int32_t *chunk_off,
+                                  int N, int T, int H, const float *s0, const float *dout, const float *dsf, float *dq,
+                                  float *dk, float *dv, float *dg, float *dbeta, float *ds0, float *ck, float *psum,
+                                  hipStream_t st) {
+    using G = Geo<NWV>;
     const int64_t th = (int64_t)T * H;
-    if (th > 0) {
-        const int64_t n4 = th * D / 4;
-        const int64_t blocks = std::min<int64_t>((n4 + 255) / 256, 4096);
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, (float4 *)dq, (float4 *)dk,
-                           (float4 *)dg, n4, dbeta, th);
+    const int64_t n4 = th * D / 4;
+    const unsigned eblocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 4096));
+    float *pbeta = psum ? psum + (int64_t)G::PARTS * th * 3 * D : nullptr;
+    if (G::ATOMIC && th > 0) {
+        hipLaunchKernelGGL(bwd_zero_kernel, dim3(eblocks), dim3(256), 0, st, (float4 *)dq, (float4 *)dk, (float4 *)dg,
+                           n4, dbeta, th);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     static std::atomic<uint64_t> lds_set{0};
-    if (ensure_lds_limit((const void *)bwd_kernel, BWD_LDS, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(bwd_kernel, dim3((unsigned)((int64_t)N * H * HALVES)), dim3(64 * WAVES), BWD_LDS, st, q, k,
-                       v, g, beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0, ck);
+    if (ensure_lds_limit((const void *)bwd_kernel<NWV>, bwd_lds<NWV>(), lds_set) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(bwd_kernel<NWV>, dim3((unsigned)((int64_t)N * H * G::PARTS)), dim3(G::THREADS), bwd_lds<NWV>(),
+                       st, q, k, v, g, beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0,
+                       ck, psum, pbeta, th);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (!G::ATOMIC && th > 0)
+        hipLaunchKernelGGL(bwd_sum_kernel<G::PARTS>, dim3(eblocks), dim3(256), 0, st, (const float4 *)psum, pbeta,
+                           (float4 *)dq, (float4 *)dk, (float4 *)dg, dbeta, th, H, cu_safe, N);
     return hipGetLastError();
+}
+
+hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
+                      const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
+                      float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves, hipStream_t st) {
+    switch (waves) {
+    case 8:
+        return launch_bwd_form<8>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
+                                  dbeta, ds0, ck, nullptr, st);
+    case 4:
+        return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
+                                  dbeta, ds0, ck, psum, st);
+    case 2:
+        return launch_bwd_form<2>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
+                                  dbeta, ds0, ck, psum, st);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 int bwd_block_tokens() { return BLK; }

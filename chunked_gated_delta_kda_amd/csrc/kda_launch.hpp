@@ -128,13 +128,19 @@ hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
-// The backward (kda_bwd.hip): zeroes dq, dk, dg, dbeta, then two workgroups per (sequence,
-// head). chunk_off counts blocks of bwd_block_tokens() tokens per sequence (the chunk map
-// at that chunk length); ck holds a state per block and head.
+// The backward (kda_bwd.hip) with `waves` (8, 4 or 2) waves per workgroup, 128 / (8 waves)
+// workgroups per (sequence, head). With 8: zeroes dq, dk, dg, dbeta, which the two
+// workgroups of a chain add into; with 4 or 2: the workgroups write partial sums to psum
+// (bwd_partial_floats(T, H, waves) floats) and a last kernel adds them in a fixed order.
+// chunk_off counts blocks of bwd_block_tokens() tokens per sequence (the chunk map at that
+// chunk length); ck holds a state per block and head.
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                       float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
                       const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
-                      float *dg, float *dbeta, float *ds0, float *ck, hipStream_t st);
+                      float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves, hipStream_t st);
+inline int64_t bwd_partial_floats(int64_t T, int64_t H, int waves) {
+    return waves == 8 ? 0 : (int64_t)(16 / waves) * T * H * (3 * 128 + 1);
+}
 int bwd_block_tokens();
 
 hipError_t launch_fused(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,

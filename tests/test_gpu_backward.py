@@ -90,6 +90,21 @@ def test_bwd_small(name, lengths, H, seed, init, with_dsf):
     assert np.all(got["dg"][w.g < -5.0] == 0.0)
 
 
+@pytest.mark.parametrize("waves", [4, 2])
+@pytest.mark.parametrize("name,lengths,H,seed,init,with_dsf", CASES[:2], ids=[c[0] for c in CASES[:2]])
+def test_bwd_small_partial_forms(monkeypatch, waves, name, lengths, H, seed, init, with_dsf):
+    """The forms for batches of few chains: 4 or 8 workgroups per chain, partial sums added
+    by a last kernel (KDA_BWD_WAVES forces them here)."""
+    monkeypatch.setenv("KDA_BWD_WAVES", str(waves))
+    w = synth.make_workload(lengths, H, seed, with_initial_state=init, clamp_frac=0.1)
+    _below_bound(w, seed)
+    do, dsf = _grads_in(w, seed, with_dsf)
+    _say(f"[bwd] {name}, {waves} waves per workgroup")
+    got = _run_gpu(w, do, dsf)
+    _check(got, _run_oracle(w, do, dsf), f"{name} w{waves}")
+    assert np.all(got["dg"][w.g < -5.0] == 0.0)
+
+
 def test_bwd_single_sequence_without_offsets():
     w = synth.config_workload(1)
     do, dsf = _grads_in(w, 1, True)
@@ -132,9 +147,11 @@ def test_bwd_config_every_chain(cfg):
     _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), f"config {cfg}")
 
 
-def test_bwd_chains_alone_match_the_batch():
+def test_bwd_chains_alone_match_the_batch(monkeypatch):
     """Chains are independent: two sequences x three heads of config 3 run as a batch of their
-    own give the same gradients as inside the whole batch (bit for bit)."""
+    own give the same gradients as inside the whole batch (bit for bit, with the same form:
+    the forms add the column parts in different orders)."""
+    monkeypatch.setenv("KDA_BWD_WAVES", "8")
     w = synth.config_workload(3)
     _below_bound(w, 3, frac=0.01)
     do, dsf = _grads_in(w, 3, True)
@@ -147,12 +164,16 @@ def test_bwd_chains_alone_match_the_batch():
         assert np.array_equal(sub, alone[n]), n
 
 
-def test_bwd_deterministic():
-    """dq, dk, dg and dbeta are sums of two column halves added onto zero: two calls on the
-    same inputs give the same bits."""
+@pytest.mark.parametrize("waves", [8, 4, 2])
+def test_bwd_deterministic(monkeypatch, waves):
+    """dq, dk, dg and dbeta are sums of two column halves added onto zero (8 waves), or of 4
+    or 8 partial sums added in a fixed order: two calls on the same inputs give the same
+    bits. The forms differ only in the order of those sums."""
+    monkeypatch.setenv("KDA_BWD_WAVES", str(waves))
     w = synth.make_workload([300, 77], 3, 75, with_initial_state=True, clamp_frac=0.1)
     do, dsf = _grads_in(w, 75, True)
     a = _run_gpu(w, do, dsf)
     b = _run_gpu(w, do, dsf)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+    _check(a, _run_oracle(w, do, dsf), f"w{waves}")
