@@ -534,19 +534,20 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
 // order, error word, sanitised offsets), then a state per block of KDA_BWD_BLOCK tokens
 // and head.
 // Waves per backward workgroup: 8 (two workgroups per (sequence, head), their sums added
-// onto zeroed outputs) once the batch has 128 chains (256 workgroups, one per CU); for
-// fewer chains 4 or 2 (4 or 8 workgroups per chain, partial sums added by a last kernel),
-// so that the batch occupies more CUs, unless the partial sums would pass 8 GiB.
-// KDA_BWD_WAVES overrides the choice (for tests and tuning).
+// onto zeroed outputs) or 4 (four workgroups per chain, partial sums added by a last
+// kernel, so that a batch of few chains occupies more CUs). Measured on MI355X (ms per
+// call, 8 | 4 | 2 waves): 256 tokens x 2 heads 0.484 | 0.341 | 0.345; 8192 x 32 heads
+// 16.9 | 11.2 | 11.2; 8 x 1024 x 8 heads 2.22 | 1.55 | 2.13; 4 x 2048 x 24 heads 4.67 |
+// 4.71 | 5.37; 8 x 1024 x 16 heads 2.51 | 2.61 | 3.26. So 4 below 96 chains (unless its
+// partial sums would pass 8 GiB), else 8; two waves never paid. KDA_BWD_WAVES overrides
+// the choice (tests, tuning).
 static int bwd_waves(int64_t N, int64_t T, int64_t H) {
     if (const char *e = std::getenv("KDA_BWD_WAVES")) {
         const int w = std::atoi(e);
-        if (w == 8 || w == 4 || w == 2) return w;
+        if (w == 8 || w == 4) return w;
     }
-    const int64_t chains = N * H;
-    int w = chains >= 128 ? 8 : chains >= 64 ? 4 : 2;
-    while (w < 8 && kda::bwd_partial_floats(T, H, w) * 4 > ((int64_t)8 << 30)) w *= 2;
-    return w;
+    if (N * H >= 96) return 8;
+    return kda::bwd_partial_floats(T, H, 4) * 4 > ((int64_t)8 << 30) ? 8 : 4;
 }
 
 static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *psum, size_t *total, int *waves) {

@@ -49,8 +49,8 @@ constexpr float LB = KDA_LOWER_BOUND;
 // A block of NWV waves owns NCOL = 8 NWV value columns of one chain; PARTS blocks make the
 // chain. With 8 waves (two blocks per chain) the blocks add their row gradients straight
 // into the zeroed outputs (two addends onto zero: the result does not depend on their
-// order); with 4 or 2 waves (for batches of few chains, to occupy more CUs) each block
-// writes its partial sums and bwd_sum_kernel adds the PARTS of them in a fixed order.
+// order); with 4 waves (for batches of few chains, to occupy more CUs) each block writes
+// its partial sums and bwd_sum_kernel adds the PARTS of them in a fixed order.
 template <int NWV>
 struct Geo {
     static constexpr int NCOL = CW * NWV, PARTS = D / NCOL, THREADS = 64 * NWV;
@@ -708,9 +708,6 @@ hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, c
                                   dbeta, ds0, ck, nullptr, st);
     case 4:
         return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
-                                  dbeta, ds0, ck, psum, st);
-    case 2:
-        return launch_bwd_form<2>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
                                   dbeta, ds0, ck, psum, st);
     default:
         return hipErrorInvalidValue;

@@ -128,9 +128,9 @@ hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
-// The backward (kda_bwd.hip) with `waves` (8, 4 or 2) waves per workgroup, 128 / (8 waves)
+// The backward (kda_bwd.hip) with `waves` (8 or 4) waves per workgroup, 128 / (8 waves)
 // workgroups per (sequence, head). With 8: zeroes dq, dk, dg, dbeta, which the two
-// workgroups of a chain add into; with 4 or 2: the workgroups write partial sums to psum
+// workgroups of a chain add into; with 4: the workgroups write partial sums to psum
 // (bwd_partial_floats(T, H, waves) floats) and a last kernel adds them in a fixed order.
 // chunk_off counts blocks of bwd_block_tokens() tokens per sequence (the chunk map at that
 // chunk length); ck holds a state per block and head.

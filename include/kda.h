@@ -264,12 +264,15 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
  *   workspace       device scratch of kda_bwd_workspace_bytes() bytes, or NULL: then the
  *                   library allocates it stream-ordered on `stream`. It holds the state
  *                   before every KDA_BWD_BLOCK-th token of each chain (64 KiB each: about
- *                   16 KiB per token-head).
+ *                   16 KiB per token-head) and, for batches of fewer than 96 (sequence,
+ *                   head) chains, four partial sums of dq, dk, dg and dbeta (6,160 B per
+ *                   token-head).
  *
  * The outputs must not overlap the inputs or each other. cu_seqlens is sanitised on the
- * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). dq, dk, dg and dbeta are sums of two
- * halves over the value columns, added onto zero in either order: the results are the
- * same from run to run. Returns KDA_OK or a kda_status code
+ * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). dq, dk, dg and dbeta are sums over parts
+ * of the value columns: two halves added onto zero in either order, or (fewer than 96
+ * chains) four partial sums added in a fixed order. Either way the results are the same
+ * from run to run. Returns KDA_OK or a kda_status code
  * (host-side checks before anything is enqueued). Inputs are not modified.
  */
 #define KDA_BWD_BLOCK 4
