@@ -129,9 +129,12 @@ def fwd(q, k, v, g, beta, scale=None, cu_seqlens=None, initial_state=None,
         nbytes = lib.kda_workspace_bytes(N, T, H, var)
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     opt = native.KdaOptions(variant=var, n_stage_events=0,
                             workspace=ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else None,
-                            workspace_bytes=workspace.numel() if workspace is not None else 0,
+                            workspace_bytes=workspace.numel() * workspace.element_size() if workspace is not None
+                            else 0,
                             g_dtype=dtypes[g.dtype], state_dtype=dtypes[sdt])
     if stage_events is not None:   # profiling: a ctypes array of hipEvent_t handles
         opt.n_stage_events = len(stage_events)
@@ -187,11 +190,13 @@ def bwd(q, k, v, g, beta, d_out, scale=None, cu_seqlens=None, initial_state=None
               d_initial_state=torch.empty((N, H, Dk, Dk), **f32) if need_d_initial_state else None)
     if workspace is None:
         workspace = torch.empty(lib.kda_bwd_workspace_bytes(N, T, H), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
     st = stream if stream is not None else torch.cuda.current_stream(dev)
     rc = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(cu_seqlens), N, T, H, Dk,
                      _ptr(initial_state), _ptr(d_out), _ptr(d_final_state), _ptr(gr["dq"]), _ptr(gr["dk"]),
                      _ptr(gr["dv"]), _ptr(gr["dg"]), _ptr(gr["dbeta"]), _ptr(gr["d_initial_state"]),
-                     ctypes.c_void_p(st.cuda_stream), _ptr(workspace), workspace.numel())
+                     ctypes.c_void_p(st.cuda_stream), _ptr(workspace), workspace.numel() * workspace.element_size())
     native.check(rc)
     return gr
 

@@ -8,6 +8,7 @@ import sys
 import numpy as np
 import pytest
 
+import oracle
 from chunked_gated_delta_kda_amd import synth
 from kda_check import run_oracle
 
@@ -121,3 +122,45 @@ def test_plain_kda_fwd_reports_malformed_offsets():
                 kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], cu_t, check=True)
         else:
             kda.fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["scale"], cu_t, check=True)
+
+
+@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "_".join(map(str, c[0])))
+def test_bwd_malformed_cu_seqlens(monkeypatch, case, waves):
+    """The backward sanitises offsets as the forward does: the error bit is raised; every
+    sanitised sequence's gradients match the oracle on that sequence; rows of no sequence
+    get zero dq, dk, dg and dbeta. Both workgroup forms."""
+    import torch
+    import chunked_gated_delta_kda_amd as kda
+
+    monkeypatch.setenv("KDA_BWD_WAVES", waves)
+    cu, T = case
+    w = synth.make_workload([T], 2, 15, clamp_frac=0.1)
+    rng = np.random.Generator(np.random.PCG64(16))
+    do = rng.standard_normal((T, w.H, 128)).astype(np.float32)
+    _say(f"[robust] backward cu_seqlens={cu} T={T} waves={waves}")
+    d = synth.to_device(w)
+    cs = np.maximum.accumulate(np.clip(np.asarray(cu), 0, T))
+    N = len(cu) - 1
+    dsf = rng.standard_normal((N, w.H, 128, 128)).astype(np.float32) * np.float32(0.1)
+    kda.device_errors(clear=True)
+    gr = kda.bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], torch.from_numpy(do).cuda(), d["scale"],
+                 torch.tensor(cu, dtype=torch.int32, device="cuda"), None, torch.from_numpy(dsf).cuda())
+    torch.cuda.synchronize()
+    assert kda.device_errors(clear=True) == ERR_CU_SEQLENS
+    got = {n: gr[n].cpu().numpy() for n in ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")}
+    covered = np.zeros(T, dtype=bool)
+    for a, b in zip(cs[:-1], cs[1:]):
+        covered[a:b] = True
+    for n in ("dq", "dk", "dg", "dbeta"):
+        assert (got[n][~covered] == 0.0).all(), n
+    lens = np.diff(cs)
+    sub = synth.Workload(name="sub", q=w.q[cs[0]:cs[-1]], k=w.k[cs[0]:cs[-1]], v=w.v[cs[0]:cs[-1]],
+                         g=w.g[cs[0]:cs[-1]], beta=w.beta[cs[0]:cs[-1]],
+                         cu_seqlens=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    ref = oracle.kda_backward(**synth.oracle_inputs(sub), d_out=do[cs[0]:cs[-1]], d_final_state=dsf)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        m = synth.parity(got[n][cs[0]:cs[-1]], ref[n])
+        assert synth.passes(m), (n, m)
+    m = synth.parity(got["d_initial_state"], ref["d_initial_state"])
+    assert synth.passes(m), ("d_initial_state", m)
