@@ -21,7 +21,8 @@
 // are one reduction across the wave. Eight waves make a block (64 columns), two blocks a
 // chain; the waves of a block add their row gradients through LDS, and the two blocks add
 // theirs into zeroed outputs with one atomic add each (two addends onto zero: the result
-// does not depend on their order).
+// does not depend on their order). For batches of few chains, four blocks of four waves
+// per chain, whose partial sums a last kernel adds in a fixed order (see Geo).
 //
 // The reverse walk needs the state before every token: a forward pass stores the state
 // every BLK tokens in the workspace, then, block by block from the last, the block's
