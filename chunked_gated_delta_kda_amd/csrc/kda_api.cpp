@@ -550,21 +550,52 @@ static int bwd_waves(int64_t N, int64_t T, int64_t H) {
     return kda::bwd_partial_floats(T, H, 4) * 4 > ((int64_t)8 << 30) ? 8 : 4;
 }
 
-static bool bwd_layout(int64_t N, int64_t T, int64_t H, size_t *ck, size_t *psum, size_t *total, int *waves) {
+// Parts per sequence for the backward over parts (few long chains): doubled, up to 16, while
+// the blocks (two or four per (sequence, head) and part) stay within 1024 (four per CU) and
+// parts keep at least 1024 tokens on average; 1 = no parts. Each part costs a forward-state
+// and a gradient-state pass on top of its backward, and the composition. Measured on MI355X
+// (ms per call by parts): 65536 tokens x 8 heads 84.7 (1) | 34.3 (4) | 20.0 (8) | 17.6 (16);
+// 8192 x 32 heads 11.1 | 9.9 | 8.7 | 7.9 (1, 2, 4, 8); 12 skewed sequences (32768 tokens) x
+// 32 heads 40.7 | 49.0 (1, 2: 768 blocks already). KDA_BWD_PARTS overrides (1..16).
+static int bwd_parts(int64_t N, int64_t T, int64_t H, int waves) {
+    if (const char *e = std::getenv("KDA_BWD_PARTS")) {
+        const int p = std::atoi(e);
+        if (p >= 1 && p <= 16) return p;
+    }
+    const int64_t blocks = N * H * (waves == 8 ? 2 : 4);
+    int P = 1;
+    while (P < 16 && blocks * P * 2 <= 1024 && T / (N * P * 2) >= 1024) P *= 2;
+    return P;
+}
+
+struct BwdLayout {
+    size_t ck = 0, psum = 0, parts = 0, total = 0;
+    int waves = 8, P = 1;
+};
+
+static bool bwd_layout(int64_t N, int64_t T, int64_t H, BwdLayout *B) {
     if (!shape_ok(N, T, H)) return false;
     if (max_chunks(N, T, KDA_BWD_BLOCK) * H > (int64_t)1 << 31) return false;
     const Layout L = ws_layout(N, T, H, KDA_VARIANT_FUSED, 1, 0);
-    *waves = bwd_waves(N, T, H);
-    *ck = L.total;
-    *psum = *ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES;
-    *total = *psum + (size_t)kda::bwd_partial_floats(T, H, *waves) * sizeof(float);
+    B->waves = bwd_waves(N, T, H);
+    B->P = bwd_parts(N, T, H, B->waves);
+    if (N * B->P * H > (int64_t)1 << 24) B->P = 1;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    B->ck = L.total;
+    B->psum = up(B->ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES);
+    B->parts = up(B->psum + (size_t)kda::bwd_partial_floats(T, H, B->waves) * sizeof(float));
+    size_t parts_bytes = 0;
+    if (B->P > 1) {
+        const size_t nv = (size_t)N * B->P;
+        parts_bytes = up(3 * (nv + 1) * sizeof(int32_t)) + 4 * nv * (size_t)H * STATE_BYTES;
+    }
+    B->total = B->parts + parts_bytes;
     return true;
 }
 
 size_t kda_bwd_workspace_bytes(int32_t num_seqs, int32_t total_tokens, int32_t num_heads) {
-    size_t ck = 0, psum = 0, total = 0;
-    int waves = 0;
-    return bwd_layout(num_seqs, total_tokens, num_heads, &ck, &psum, &total, &waves) ? total : 0;
+    BwdLayout B;
+    return bwd_layout(num_seqs, total_tokens, num_heads, &B) ? B.total : 0;
 }
 
 int kda_bwd(const void *q, const void *k, const void *v, const float *g, const float *beta, float scale,
@@ -576,9 +607,9 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     if (head_dim != KDA_HEAD_DIM) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(scale)) return KDA_ERR_UNSUPPORTED;
     const int N = num_seqs, T = total_tokens, H = num_heads;
-    size_t ck_at = 0, psum_at = 0, total = 0;
-    int waves = 0;
-    if (!bwd_layout(N, T, H, &ck_at, &psum_at, &total, &waves)) return KDA_ERR_SHAPE;
+    BwdLayout B;
+    if (!bwd_layout(N, T, H, &B)) return KDA_ERR_SHAPE;
+    const size_t total = B.total;
     if (!cu_seqlens && N != 1) return KDA_ERR_SHAPE;
     if (T > 0 && (!q || !k || !v || !g || !beta || !d_out || !dq || !dk || !dv || !dg || !dbeta))
         return KDA_ERR_NULL;
@@ -600,10 +631,22 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     int32_t *chunk_off = (int32_t *)(ws + L.chunk_off), *order = (int32_t *)(ws + L.order);
     int32_t *err = (int32_t *)(ws + L.err), *cus = (int32_t *)(ws + L.cu);
     int rc = KDA_OK;
+    kda::BwdParts parts{};
+    parts.P = B.P;
+    if (B.P > 1) {
+        const size_t nv = (size_t)N * B.P;
+        char *pw = ws + B.parts;
+        parts.vcu = (int32_t *)pw;
+        parts.vco = parts.vcu + (nv + 1);
+        parts.vorder = parts.vco + (nv + 1);
+        float *f = (float *)(pw + ((3 * (nv + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
+        const size_t st1 = nv * (size_t)H * KDA_HEAD_DIM * KDA_HEAD_DIM;
+        parts.rb = f, parts.ri = f + st1, parts.sinf = f + 2 * st1, parts.sinb = f + 3 * st1;
+    }
     if (kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, KDA_BWD_BLOCK, st) != hipSuccess ||
         kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale, cus, chunk_off,
-                        N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
-                        (float *)(ws + ck_at), (float *)(ws + psum_at), waves, st) != hipSuccess)
+                        order, N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                        (float *)(ws + B.ck), (float *)(ws + B.psum), B.waves, parts, st) != hipSuccess)
         rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;
     return rc;

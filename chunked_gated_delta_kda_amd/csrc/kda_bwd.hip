@@ -328,7 +328,7 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     const int32_t *__restrict__ chunk_off, int H, const float *__restrict__ s0, const float *__restrict__ dout,
     const float *__restrict__ dsf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck,
-    float *__restrict__ psum, float *__restrict__ pbeta, int64_t TH) {
+    float *__restrict__ psum, float *__restrict__ pbeta, int64_t TH, int rev_parts) {
     using G = Geo<NWV>;
     constexpr int NCOL = G::NCOL;
     extern __shared__ __attribute__((aligned(16))) char bwd_smem[];
@@ -393,7 +393,10 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     // ---- backward, block by block from the last: recompute the block's tokens from its
     // checkpoint (S1 and u of each kept in registers), then walk them backwards
     float dS[2][CW];
-    load_slice(dS, dsf ? dsf + sbase : nullptr, c0, lane);
+    // over parts of sequences (rev_parts > 0 parts each), the exit gradient of part p of a
+    // sequence is at part index rev_parts - 1 - p (the composition walks them backwards)
+    const int nsrc = rev_parts > 0 ? n + rev_parts - 1 - 2 * (n % rev_parts) : n;
+    load_slice(dS, dsf ? dsf + ((int64_t)nsrc * H + h) * D * D : nullptr, c0, lane);
     int par = 0;
     float Sck[2][CW];
     if (nblk > 0) load_slice(S, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
@@ -615,6 +618,143 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
 }
 
+// ---- the backward over parts of each sequence (few long chains). Both maps of a part are
+// affine: its exit state is M S_in + B in its entry state, and the state gradient at its
+// start is Mg dS_out + Bg in the one at its end (Mg the product of the tokens' Diag(e)
+// (I - beta k k^T), applied to the key rows). Each is found by running the part twice:
+// from a zero entry with the real inputs (B, Bg), and from the identity with v = 0 (or
+// d_out = 0) (M, Mg). The composition then walks the parts, and the full backward runs
+// every part from its entry state and exit gradient.
+
+// Forward states only: grid 2 x (parts x H x PARTS); the first half from a zero state into
+// rb, the second from the identity with v = 0 into ri ([N P][H][128][128] each).
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void bwd_fstate_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dout,
+    const int32_t *__restrict__ cu, int H, float *__restrict__ rb, float *__restrict__ ri) {
+    using G = Geo<NWV>;
+    constexpr int NCOL = G::NCOL;
+    __shared__ InTok<NCOL> stg[2][BLK];
+    const int half_grid = gridDim.x / 2;
+    const bool ident = (int)blockIdx.x >= half_grid;
+    const int bid = xcd_remap((int)blockIdx.x - (ident ? half_grid : 0), half_grid, G::PARTS);
+    const int part = bid % G::PARTS, chain = bid / G::PARTS;
+    const int h = chain % H, n = chain / H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int c0 = NCOL * part + CW * wave;
+    const int64_t bos = cu[n], eos = cu[n + 1];
+    const int nblk = (int)((eos - bos + BLK - 1) / BLK);
+    int vz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    float S[2][CW];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) S[r][c] = ident && lane + 64 * r == c0 + c ? 1.f : 0.f;
+    Stage<NWV> st;
+    int buf = 0;
+    if (nblk > 0) {
+        stage_load<NWV>(st, q, k, v, g, beta, dout, bos, eos - 1, part, H, h, tid);
+        stage_store<NWV>(stg[0], st, tid);
+        __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int b = 0; b < nblk; ++b) {
+        const int64_t tb = bos + (int64_t)b * BLK;
+        stage_load<NWV>(st, q, k, v, g, beta, dout, b + 1 < nblk ? tb + BLK : tb, eos - 1, part, H, h, tid);
+        const int nin = (int)std::min((int64_t)BLK, eos - tb);
+#pragma unroll
+        for (int i = 0; i < BLK; ++i) {
+            if (i < nin) {
+                Tok x;
+                tok_from(x, stg[buf][i], wave, lane, false, vz);
+                if (ident) x.vl = 0.f;
+                fwd_step(S, x, lane);
+            }
+        }
+        buf ^= 1;
+        stage_store<NWV>(stg[buf], st, tid);
+        __syncthreads();
+    }
+    store_slice((ident ? ri : rb) + ((int64_t)n * H + h) * D * D, S, c0, lane);
+}
+
+// State gradients only, walking each part backwards: grid as above; the first half from a
+// zero gradient with the real d_out into rb, the second from the identity with d_out = 0
+// into ri, each at part index parts - 1 - p (part p of a sequence).
+template <int NWV>
+__global__ __launch_bounds__(64 * NWV) void bwd_rstate_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dout, float scale,
+    const int32_t *__restrict__ cu, int H, int parts, float *__restrict__ rb, float *__restrict__ ri) {
+    using G = Geo<NWV>;
+    constexpr int NCOL = G::NCOL;
+    __shared__ InTok<NCOL> stg[2][BLK];
+    const int half_grid = gridDim.x / 2;
+    const bool ident = (int)blockIdx.x >= half_grid;
+    const int bid = xcd_remap((int)blockIdx.x - (ident ? half_grid : 0), half_grid, G::PARTS);
+    const int part = bid % G::PARTS, chain = bid / G::PARTS;
+    const int h = chain % H, n = chain / H;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, tid = threadIdx.x;
+    const int c0 = NCOL * part + CW * wave;
+    const int64_t bos = cu[n], eos = cu[n + 1];
+    const int nblk = (int)((eos - bos + BLK - 1) / BLK);
+    int vz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(vz));
+    float dS[2][CW];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < CW; ++c) dS[r][c] = ident && lane + 64 * r == c0 + c ? 1.f : 0.f;
+    Stage<NWV> st;
+    int buf = 0;
+    if (nblk > 0) {
+        stage_load<NWV>(st, q, k, v, g, beta, dout, bos + (int64_t)(nblk - 1) * BLK, eos - 1, part, H, h, tid);
+        stage_store<NWV>(stg[0], st, tid);
+        __syncthreads();
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int64_t tb = bos + (int64_t)b * BLK;
+        stage_load<NWV>(st, q, k, v, g, beta, dout, bos + (int64_t)(b > 0 ? b - 1 : 0) * BLK, eos - 1, part, H, h,
+                        tid);
+        const int nin = (int)std::min((int64_t)BLK, eos - tb);
+#pragma unroll
+        for (int i = BLK - 1; i >= 0; --i) {
+            if (i < nin) {
+                Tok x;
+                tok_from(x, stg[buf][i], wave, lane, true, vz);
+                // dS += scale q do^T; dd = dS^T k; dS1 = dS - beta k dd^T; dS <- Diag(e) dS1
+                if (!ident) {
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const float sq = scale * x.q[rr];
+#pragma unroll
+                        for (int c = 0; c < CW; ++c) dS[rr][c] = fmaf(sq, x.dov[c], dS[rr][c]);
+                    }
+                }
+                float p[CW];
+#pragma unroll
+                for (int c = 0; c < CW; ++c) p[c] = fmaf(dS[1][c], x.k[1], dS[0][c] * x.k[0]);
+                float du[CW];
+                broadcast8(-x.beta * colsum8(p, lane), du);
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) dS[rr][c] = fmaf(x.k[rr], du[c], dS[rr][c]) * x.e[rr];
+            }
+        }
+        buf ^= 1;
+        stage_store<NWV>(stg[buf], st, tid);
+        __syncthreads();
+    }
+    const int nrev = n + parts - 1 - 2 * (n % parts);
+    store_slice((ident ? ri : rb) + ((int64_t)nrev * H + h) * D * D, dS, c0, lane);
+}
+
 // dq, dk, dg and dbeta as the fixed-order sums of the PARTS blocks' partials (psum
 // [PARTS][T H][3][128], pbeta [PARTS][T H]); zeros for tokens outside the sequences
 // (before cu[0] or from cu[N] on, possible only for offsets that were sanitised), which
@@ -673,14 +813,42 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *dq, float4 *dk, f
 template <int NWV>
 static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                                   const float *beta, float scale, const int32_t *cu_safe, const int32_t *chunk_off,
-                                  int N, int T, int H, const float *s0, const float *dout, const float *dsf, float *dq,
-                                  float *dk, float *dv, float *dg, float *dbeta, float *ds0, float *ck, float *psum,
-                                  hipStream_t st) {
+                                  const int32_t *order, int N, int T, int H, const float *s0, const float *dout,
+                                  const float *dsf, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
+                                  float *ck, float *psum, const BwdParts &parts, hipStream_t st) {
     using G = Geo<NWV>;
     const int64_t th = (int64_t)T * H;
     const int64_t n4 = th * D / 4;
     const unsigned eblocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 4096));
     float *pbeta = psum ? psum + (int64_t)G::PARTS * th * 3 * D : nullptr;
+    int rev_parts = 0;
+    if (parts.P > 1) {
+        // the parts as sequences; the state maps of every part (forward, then the gradient's),
+        // each composed over the parts; then the backward of every part from its entry state
+        // and exit gradient (the composition of the gradient maps writes d_initial_state)
+        const int P = parts.P, NV = N * P;
+        const unsigned sgrid = (unsigned)(2 * (int64_t)NV * H * G::PARTS);
+        if (launch_parts_setup(cu_safe, chunk_off, order, N, P, BLK, parts.vcu, parts.vco, parts.vorder, st) !=
+            hipSuccess)
+            return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(bwd_fstate_kernel<NWV>, dim3(sgrid), dim3(G::THREADS), 0, st, q, k, v, g, beta, dout,
+                           (const int32_t *)parts.vcu, H, parts.rb, parts.ri);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        if (launch_parts_compose(s0, parts.rb, parts.ri, N, P, H, parts.sinf, nullptr, st) != hipSuccess)
+            return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(bwd_rstate_kernel<NWV>, dim3(sgrid), dim3(G::THREADS), 0, st, q, k, v, g, beta, dout, scale,
+                           (const int32_t *)parts.vcu, H, P, parts.rb, parts.ri);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        if (launch_parts_compose(dsf, parts.rb, parts.ri, N, P, H, parts.sinb, ds0, st) != hipSuccess)
+            return hipErrorLaunchFailure;
+        cu_safe = parts.vcu;
+        chunk_off = parts.vco;
+        N = NV;
+        s0 = parts.sinf;
+        dsf = parts.sinb;
+        ds0 = nullptr;
+        rev_parts = P;
+    }
     if (G::ATOMIC && th > 0) {
         hipLaunchKernelGGL(bwd_zero_kernel, dim3(eblocks), dim3(256), 0, st, (float4 *)dq, (float4 *)dk, (float4 *)dg,
                            n4, dbeta, th);
@@ -691,7 +859,7 @@ static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const ui
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(bwd_kernel<NWV>, dim3((unsigned)((int64_t)N * H * G::PARTS)), dim3(G::THREADS), bwd_lds<NWV>(),
                        st, q, k, v, g, beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0,
-                       ck, psum, pbeta, th);
+                       ck, psum, pbeta, th, rev_parts);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (!G::ATOMIC && th > 0)
         hipLaunchKernelGGL(bwd_sum_kernel<G::PARTS>, dim3(eblocks), dim3(256), 0, st, (const float4 *)psum, pbeta,
@@ -700,16 +868,17 @@ static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const ui
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N, int T, int H,
-                      const float *s0, const float *dout, const float *dsf, float *dq, float *dk, float *dv,
-                      float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves, hipStream_t st) {
+                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N,
+                      int T, int H, const float *s0, const float *dout, const float *dsf, float *dq, float *dk,
+                      float *dv, float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves,
+                      const BwdParts &parts, hipStream_t st) {
     switch (waves) {
     case 8:
-        return launch_bwd_form<8>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
-                                  dbeta, ds0, ck, nullptr, st);
+        return launch_bwd_form<8>(q, k, v, g, beta, scale, cu_safe, chunk_off, order, N, T, H, s0, dout, dsf, dq, dk,
+                                  dv, dg, dbeta, ds0, ck, nullptr, parts, st);
     case 4:
-        return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk, dv, dg,
-                                  dbeta, ds0, ck, psum, st);
+        return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, order, N, T, H, s0, dout, dsf, dq, dk,
+                                  dv, dg, dbeta, ds0, ck, psum, parts, st);
     default:
         return hipErrorInvalidValue;
     }

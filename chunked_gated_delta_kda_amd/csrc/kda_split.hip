@@ -1505,6 +1505,24 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
     }
 }
 
+// the parts of every sequence as virtual sequences (cl-token chunks), and the composition
+// of their affine maps, for other users of the same scheme (the backward)
+hipError_t launch_parts_setup(const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N, int P,
+                              int cl, int32_t *vcu, int32_t *vco, int32_t *vorder, hipStream_t st) {
+    hipLaunchKernelGGL(parts_setup_kernel, dim3(64), dim3(256), 0, st, cu_safe, chunk_off, order, N, P, cl, vcu, vco,
+                       vorder, (float *)nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+hipError_t launch_parts_compose(const float *s0, const float *rb, const float *ri, int N, int P, int H, float *sin,
+                                float *sfin, hipStream_t st) {
+    static std::atomic<uint64_t> lds_set{0};
+    if (ensure_lds_limit((const void *)parts_combine_kernel, COMBINE_LDS, lds_set) != hipSuccess)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), COMBINE_LDS, st, s0, rb, ri, N, P,
+                       H, sin, sfin, 0);
+    return hipGetLastError();
+}
+
 // setup, pass 1 (two-slice paired blocks: 8 N P H of them), composition, pass 2 (one-slice
 // paired blocks, no state written: the composition wrote the final state)
 hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_safe, const int32_t *chunk_off,

@@ -177,3 +177,33 @@ def test_bwd_deterministic(monkeypatch, waves):
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
     _check(a, _run_oracle(w, do, dsf), f"w{waves}")
+
+
+@pytest.mark.parametrize("waves", [8, 4])
+@pytest.mark.parametrize("parts", [2, 3, 16])
+def test_bwd_parts(monkeypatch, waves, parts):
+    """The backward over parts of each sequence (KDA_BWD_PARTS forces it): state maps of
+    every part from zero and identity entries, composed forwards (entry states) and
+    backwards (exit gradients, d_initial_state), then every part's backward. Ragged lengths,
+    an empty sequence, parts with no tokens (16 parts of 5 tokens), initial state and
+    final-state gradient."""
+    monkeypatch.setenv("KDA_BWD_WAVES", str(waves))
+    monkeypatch.setenv("KDA_BWD_PARTS", str(parts))
+    w = synth.make_workload([300, 0, 77, 5], 2, 81, with_initial_state=True, clamp_frac=0.1)
+    _below_bound(w, 81)
+    do, dsf = _grads_in(w, 81, True)
+    _say(f"[bwd] parts={parts} waves={waves}")
+    _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), f"parts {parts} w{waves}")
+
+
+def test_bwd_parts_slow_decay(monkeypatch):
+    """Parts where the maps are far from zero: g = 0 (no decay) and small beta, so that a
+    part's state and gradient maps stay O(1) over its 256 tokens and the composition
+    carries real information from part to part."""
+    monkeypatch.setenv("KDA_BWD_PARTS", "4")
+    w = synth.make_workload([1024, 700], 2, 82, with_initial_state=True)
+    w.g[:] = np.float32(0.0)
+    w.beta[:] = np.float32(0.05)
+    do, dsf = _grads_in(w, 82, True)
+    _say("[bwd] parts=4, g = 0, beta = 0.05")
+    _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), "parts slow decay")
