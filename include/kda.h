@@ -266,7 +266,8 @@ int kda_decode_ex(const void *q, const void *k, const void *v, const float *g, c
  *                   before every KDA_BWD_BLOCK-th token of each chain (64 KiB each: about
  *                   16 KiB per token-head) and, for batches of fewer than 96 (sequence,
  *                   head) chains, four partial sums of dq, dk, dg and dbeta (6,160 B per
- *                   token-head).
+ *                   token-head); for few long sequences, cut into P parts, four states
+ *                   of 64 KiB per part and head.
  *
  * The outputs must not overlap the inputs or each other. cu_seqlens is sanitised on the
  * device as in kda_fwd (KDA_DEVERR_CU_SEQLENS). dq, dk, dg and dbeta are sums over parts
