@@ -550,27 +550,44 @@ static int bwd_waves(int64_t N, int64_t T, int64_t H) {
     return kda::bwd_partial_floats(T, H, 4) * 4 > ((int64_t)8 << 30) ? 8 : 4;
 }
 
-// Parts per sequence for the backward over parts (few long chains): doubled, up to 16, while
-// the blocks (two or four per (sequence, head) and part) stay within 1024 (four per CU) and
-// parts keep at least 1024 tokens on average; 1 = no parts. Each part costs a forward-state
-// and a gradient-state pass on top of its backward, and the composition. Measured on MI355X
-// (ms per call by parts): 65536 tokens x 8 heads 84.7 (1) | 34.3 (4) | 20.0 (8) | 17.6 (16);
-// 8192 x 32 heads 11.1 | 9.9 | 8.7 | 7.9 (1, 2, 4, 8); 12 skewed sequences (32768 tokens) x
-// 32 heads 40.7 | 49.0 (1, 2: 768 blocks already). KDA_BWD_PARTS overrides (1..16).
-static int bwd_parts(int64_t N, int64_t T, int64_t H, int waves) {
+// The backward over parts of each sequence (few or skewed long chains): slots for up to P
+// parts per sequence, a sequence taking one part per lstar tokens (rounded up, at least
+// one). lstar = 1024 tokens, or more where the batch alone fills 1024 blocks (two or four
+// per (sequence, head) and part): T H blocks / 1024. P = T / lstar as a power of two, at
+// most 16; P = 1: no parts. A part costs a forward-state and a gradient-state pass on top
+// of its backward, and the compositions; a sequence of one part costs neither. Measured
+// on MI355X (ms per call by uniform parts): 65536 tokens x 8 heads 84.7 (1) | 34.3 (4) |
+// 20.0 (8) | 17.6 (16); 8192 x 32 heads 11.1 | 9.9 | 8.7 | 7.9 (1, 2, 4, 8). KDA_BWD_PARTS
+// overrides P (1..16): then every sequence takes P parts, or with KDA_BWD_PART_TOKENS one
+// part per so many tokens (at most P).
+struct BwdSplit {
+    int P = 1, lstar = 0;   // lstar in blocks of KDA_BWD_BLOCK tokens
+};
+static BwdSplit bwd_parts(int64_t N, int64_t T, int64_t H, int waves) {
+    BwdSplit s;
+    const int64_t per_chain = waves == 8 ? 2 : 4;
+    int64_t lstar = std::max<int64_t>(1024, (T * H * per_chain + 1023) / 1024);
     if (const char *e = std::getenv("KDA_BWD_PARTS")) {
         const int p = std::atoi(e);
-        if (p >= 1 && p <= 16) return p;
+        if (p >= 1 && p <= 16) {
+            s.P = p;
+            s.lstar = 1;   // every sequence in p parts, or (KDA_BWD_PART_TOKENS) one per so many
+            if (const char *f = std::getenv("KDA_BWD_PART_TOKENS")) {
+                const int l = std::atoi(f);
+                if (l >= KDA_BWD_BLOCK) s.lstar = l / KDA_BWD_BLOCK;
+            }
+            return s;
+        }
     }
-    const int64_t blocks = N * H * (waves == 8 ? 2 : 4);
-    int P = 1;
-    while (P < 16 && blocks * P * 2 <= 1024 && T / (N * P * 2) >= 1024) P *= 2;
-    return P;
+    while (s.P < 16 && (int64_t)s.P * 2 * lstar <= T) s.P *= 2;
+    s.lstar = (int)((lstar + KDA_BWD_BLOCK - 1) / KDA_BWD_BLOCK);
+    (void)N;
+    return s;
 }
 
 struct BwdLayout {
     size_t ck = 0, psum = 0, parts = 0, total = 0;
-    int waves = 8, P = 1;
+    int waves = 8, P = 1, lstar = 0;
 };
 
 static bool bwd_layout(int64_t N, int64_t T, int64_t H, BwdLayout *B) {
@@ -578,7 +595,8 @@ static bool bwd_layout(int64_t N, int64_t T, int64_t H, BwdLayout *B) {
     if (max_chunks(N, T, KDA_BWD_BLOCK) * H > (int64_t)1 << 31) return false;
     const Layout L = ws_layout(N, T, H, KDA_VARIANT_FUSED, 1, 0);
     B->waves = bwd_waves(N, T, H);
-    B->P = bwd_parts(N, T, H, B->waves);
+    const BwdSplit sp = bwd_parts(N, T, H, B->waves);
+    B->P = sp.P, B->lstar = sp.lstar;
     if (N * B->P * H > (int64_t)1 << 24) B->P = 1;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     B->ck = L.total;
@@ -587,7 +605,7 @@ static bool bwd_layout(int64_t N, int64_t T, int64_t H, BwdLayout *B) {
     size_t parts_bytes = 0;
     if (B->P > 1) {
         const size_t nv = (size_t)N * B->P;
-        parts_bytes = up(3 * (nv + 1) * sizeof(int32_t)) + 4 * nv * (size_t)H * STATE_BYTES;
+        parts_bytes = up(2 * (nv + 1) * sizeof(int32_t)) + 4 * nv * (size_t)H * STATE_BYTES;
     }
     B->total = B->parts + parts_bytes;
     return true;
@@ -633,19 +651,19 @@ int kda_bwd(const void *q, const void *k, const void *v, const float *g, const f
     int rc = KDA_OK;
     kda::BwdParts parts{};
     parts.P = B.P;
+    parts.lstar = B.lstar;
     if (B.P > 1) {
         const size_t nv = (size_t)N * B.P;
         char *pw = ws + B.parts;
         parts.vcu = (int32_t *)pw;
         parts.vco = parts.vcu + (nv + 1);
-        parts.vorder = parts.vco + (nv + 1);
-        float *f = (float *)(pw + ((3 * (nv + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
+        float *f = (float *)(pw + ((2 * (nv + 1) * sizeof(int32_t) + 255) & ~(size_t)255));
         const size_t st1 = nv * (size_t)H * KDA_HEAD_DIM * KDA_HEAD_DIM;
         parts.rb = f, parts.ri = f + st1, parts.sinf = f + 2 * st1, parts.sinb = f + 3 * st1;
     }
     if (kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, KDA_BWD_BLOCK, st) != hipSuccess ||
         kda::launch_bwd((const uint16_t *)q, (const uint16_t *)k, (const uint16_t *)v, g, beta, scale, cus, chunk_off,
-                        order, N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
+                        N, T, H, initial_state, d_out, d_final_state, dq, dk, dv, dg, dbeta, d_initial_state,
                         (float *)(ws + B.ck), (float *)(ws + B.psum), B.waves, parts, st) != hipSuccess)
         rc = KDA_ERR_LAUNCH;
     if (owned && hipFreeAsync(ws, st) != hipSuccess && rc == KDA_OK) rc = KDA_ERR_DEVICE;

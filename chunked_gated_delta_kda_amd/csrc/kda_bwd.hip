@@ -328,7 +328,8 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     const int32_t *__restrict__ chunk_off, int H, const float *__restrict__ s0, const float *__restrict__ dout,
     const float *__restrict__ dsf, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv,
     float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ ds0, float *__restrict__ ck,
-    float *__restrict__ psum, float *__restrict__ pbeta, int64_t TH, int rev_parts) {
+    float *__restrict__ psum, float *__restrict__ pbeta, int64_t TH, int rev_parts,
+    const float *__restrict__ s0_seq, const float *__restrict__ dsf_seq) {
     using G = Geo<NWV>;
     constexpr int NCOL = G::NCOL;
     extern __shared__ __attribute__((aligned(16))) char bwd_smem[];
@@ -340,6 +341,9 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int c0 = NCOL * part + CW * wave;
     const int64_t bos = cu[n], eos = cu[n + 1];
+    // over parts, an empty part after the first of its sequence has nothing to do (the
+    // first writes d_initial_state, even for an empty sequence)
+    if (rev_parts > 0 && n % rev_parts != 0 && bos >= eos) return;
     const int nblk = (int)((eos - bos + BLK - 1) / BLK);
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
     const int64_t ck_stride = (int64_t)H * D * D;
@@ -350,9 +354,21 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     auto stage = [&](int64_t t0) { stage_load<NWV>(st, q, k, v, g, beta, dout, t0, eos - 1, part, H, h, tid); };
     int buf = 0;   // the staged group in use
 
+    // Over parts (rev_parts > 0): the entry state of a sequence's first part is the
+    // sequence's (s0_seq), of the others the composition's (s0); the exit gradient of its
+    // last part with tokens is the sequence's (dsf_seq), of the others the composition's
+    // (dsf, the part at index rev_parts - 1 - p).
+    const int pidx = rev_parts > 0 ? n % rev_parts : 0;
+    const int64_t seqbase = rev_parts > 0 ? ((int64_t)(n / rev_parts) * H + h) * D * D : sbase;
+    const bool first_part = rev_parts == 0 || pidx == 0;
+    const bool last_part = rev_parts == 0 || pidx + 1 == rev_parts || cu[n + 1] >= cu[n + 2];
+
     // ---- forward: the state before every BLK-th token (the start of every block)
     float S[2][CW];
-    load_slice(S, s0 ? s0 + sbase : nullptr, c0, lane);
+    {
+        const float *src = first_part ? (rev_parts > 0 ? s0_seq : s0) : s0;
+        load_slice(S, src ? src + (first_part ? seqbase : sbase) : nullptr, c0, lane);
+    }
     if (nblk > 0) {
         stage(bos);
         stage_store<NWV>(L.in[0], st, tid);
@@ -393,10 +409,11 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
     // ---- backward, block by block from the last: recompute the block's tokens from its
     // checkpoint (S1 and u of each kept in registers), then walk them backwards
     float dS[2][CW];
-    // over parts of sequences (rev_parts > 0 parts each), the exit gradient of part p of a
-    // sequence is at part index rev_parts - 1 - p (the composition walks them backwards)
-    const int nsrc = rev_parts > 0 ? n + rev_parts - 1 - 2 * (n % rev_parts) : n;
-    load_slice(dS, dsf ? dsf + ((int64_t)nsrc * H + h) * D * D : nullptr, c0, lane);
+    {
+        const int nsrc = rev_parts > 0 ? n + rev_parts - 1 - 2 * pidx : n;
+        const float *src = last_part ? (rev_parts > 0 ? dsf_seq : dsf) : dsf;
+        load_slice(dS, src ? src + (last_part ? seqbase : ((int64_t)nsrc * H + h) * D * D) : nullptr, c0, lane);
+    }
     int par = 0;
     float Sck[2][CW];
     if (nblk > 0) load_slice(S, ckc + (int64_t)(nblk - 1) * ck_stride, c0, lane);
@@ -615,7 +632,7 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
             step(std::false_type{}, nblk - 1);
         for (int b = nblk - 2; b >= 0; --b) step(std::true_type{}, b);
     }
-    if (ds0) store_slice(ds0 + sbase, dS, c0, lane);
+    if (ds0 && first_part) store_slice(ds0 + seqbase, dS, c0, lane);   // over parts: the first part's
 }
 
 // ---- the backward over parts of each sequence (few long chains). Both maps of a part are
@@ -626,13 +643,37 @@ __global__ __launch_bounds__(64 * NWV) void bwd_kernel(
 // d_out = 0) (M, Mg). The composition then walks the parts, and the full backward runs
 // every part from its entry state and exit gradient.
 
+// The parts as virtual sequences: sequence n of c blocks takes Pn = min(P, ceil(c / lstar))
+// parts of c / Pn blocks (rounded), in slots n P .. n P + Pn - 1; its other slots are empty
+// (at its end). vcu, vco: token and block offsets, N P + 1 each.
+__global__ __launch_bounds__(256) void bwd_parts_setup_kernel(const int32_t *__restrict__ cu_safe,
+                                                              const int32_t *__restrict__ chunk_off, int N, int P,
+                                                              int lstar, int32_t *__restrict__ vcu,
+                                                              int32_t *__restrict__ vco) {
+    const int64_t nv = (int64_t)N * P;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v <= nv; v += (int64_t)gridDim.x * blockDim.x) {
+        if (v == nv) {
+            vco[v] = chunk_off[N];
+            vcu[v] = cu_safe[N];
+            continue;
+        }
+        const int n = (int)(v / P), p = (int)(v % P);
+        const int c0 = chunk_off[n], c = chunk_off[n + 1] - c0;
+        const int pn = max(1, min(P, (c + lstar - 1) / lstar));
+        const int k = p < pn ? (int)(((int64_t)c * p) / pn) : c;
+        vco[v] = c0 + k;
+        vcu[v] = min(cu_safe[n + 1], cu_safe[n] + BLK * k);
+    }
+}
+
 // Forward states only: grid 2 x (parts x H x PARTS); the first half from a zero state into
-// rb, the second from the identity with v = 0 into ri ([N P][H][128][128] each).
+// rb, the second from the identity with v = 0 into ri ([N P][H][128][128] each). The last
+// part of a sequence (the last with tokens) needs no map: no part follows it.
 template <int NWV>
 __global__ __launch_bounds__(64 * NWV) void bwd_fstate_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ dout,
-    const int32_t *__restrict__ cu, int H, float *__restrict__ rb, float *__restrict__ ri) {
+    const int32_t *__restrict__ cu, int H, int parts, float *__restrict__ rb, float *__restrict__ ri) {
     using G = Geo<NWV>;
     constexpr int NCOL = G::NCOL;
     __shared__ InTok<NCOL> stg[2][BLK];
@@ -641,6 +682,8 @@ __global__ __launch_bounds__(64 * NWV) void bwd_fstate_kernel(
     const int bid = xcd_remap((int)blockIdx.x - (ident ? half_grid : 0), half_grid, G::PARTS);
     const int part = bid % G::PARTS, chain = bid / G::PARTS;
     const int h = chain % H, n = chain / H;
+    // only a part followed by another of its sequence needs its map
+    if (n % parts + 1 >= parts || cu[n + 1] >= cu[n + 2]) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int c0 = NCOL * part + CW * wave;
@@ -683,7 +726,8 @@ __global__ __launch_bounds__(64 * NWV) void bwd_fstate_kernel(
 
 // State gradients only, walking each part backwards: grid as above; the first half from a
 // zero gradient with the real d_out into rb, the second from the identity with d_out = 0
-// into ri, each at part index parts - 1 - p (part p of a sequence).
+// into ri, each at part index parts - 1 - p (part p of a sequence). The first part's map
+// is not needed: the backward of that part writes d_initial_state itself.
 template <int NWV>
 __global__ __launch_bounds__(64 * NWV) void bwd_rstate_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
@@ -697,6 +741,8 @@ __global__ __launch_bounds__(64 * NWV) void bwd_rstate_kernel(
     const int bid = xcd_remap((int)blockIdx.x - (ident ? half_grid : 0), half_grid, G::PARTS);
     const int part = bid % G::PARTS, chain = bid / G::PARTS;
     const int h = chain % H, n = chain / H;
+    // only a part with tokens after the first of its sequence needs its map
+    if (n % parts == 0 || cu[n] >= cu[n + 1]) return;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, tid = threadIdx.x;
     const int c0 = NCOL * part + CW * wave;
@@ -813,7 +859,7 @@ __global__ __launch_bounds__(256) void bwd_zero_kernel(float4 *dq, float4 *dk, f
 template <int NWV>
 static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
                                   const float *beta, float scale, const int32_t *cu_safe, const int32_t *chunk_off,
-                                  const int32_t *order, int N, int T, int H, const float *s0, const float *dout,
+                                  int N, int T, int H, const float *s0, const float *dout,
                                   const float *dsf, float *dq, float *dk, float *dv, float *dg, float *dbeta, float *ds0,
                                   float *ck, float *psum, const BwdParts &parts, hipStream_t st) {
     using G = Geo<NWV>;
@@ -822,31 +868,32 @@ static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const ui
     const unsigned eblocks = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n4 + 255) / 256, 4096));
     float *pbeta = psum ? psum + (int64_t)G::PARTS * th * 3 * D : nullptr;
     int rev_parts = 0;
+    const float *s0_seq = s0, *dsf_seq = dsf;
     if (parts.P > 1) {
         // the parts as sequences; the state maps of every part (forward, then the gradient's),
         // each composed over the parts; then the backward of every part from its entry state
         // and exit gradient (the composition of the gradient maps writes d_initial_state)
         const int P = parts.P, NV = N * P;
         const unsigned sgrid = (unsigned)(2 * (int64_t)NV * H * G::PARTS);
-        if (launch_parts_setup(cu_safe, chunk_off, order, N, P, BLK, parts.vcu, parts.vco, parts.vorder, st) !=
-            hipSuccess)
-            return hipErrorLaunchFailure;
-        hipLaunchKernelGGL(bwd_fstate_kernel<NWV>, dim3(sgrid), dim3(G::THREADS), 0, st, q, k, v, g, beta, dout,
-                           (const int32_t *)parts.vcu, H, parts.rb, parts.ri);
+        hipLaunchKernelGGL(bwd_parts_setup_kernel, dim3((unsigned)std::min<int64_t>((NV + 256) / 256, 1024)), dim3(256),
+                           0, st, cu_safe, chunk_off, N, P, parts.lstar, parts.vcu, parts.vco);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        if (launch_parts_compose(s0, parts.rb, parts.ri, N, P, H, parts.sinf, nullptr, st) != hipSuccess)
+        const int32_t *vcu = parts.vcu;
+        hipLaunchKernelGGL(bwd_fstate_kernel<NWV>, dim3(sgrid), dim3(G::THREADS), 0, st, q, k, v, g, beta, dout, vcu, H,
+                           P, parts.rb, parts.ri);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        if (launch_parts_compose(s0, parts.rb, parts.ri, N, P, H, parts.sinf, nullptr, vcu, false, st) != hipSuccess)
             return hipErrorLaunchFailure;
         hipLaunchKernelGGL(bwd_rstate_kernel<NWV>, dim3(sgrid), dim3(G::THREADS), 0, st, q, k, v, g, beta, dout, scale,
-                           (const int32_t *)parts.vcu, H, P, parts.rb, parts.ri);
+                           vcu, H, P, parts.rb, parts.ri);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-        if (launch_parts_compose(dsf, parts.rb, parts.ri, N, P, H, parts.sinb, ds0, st) != hipSuccess)
+        if (launch_parts_compose(dsf, parts.rb, parts.ri, N, P, H, parts.sinb, nullptr, vcu, true, st) != hipSuccess)
             return hipErrorLaunchFailure;
         cu_safe = parts.vcu;
         chunk_off = parts.vco;
         N = NV;
         s0 = parts.sinf;
         dsf = parts.sinb;
-        ds0 = nullptr;
         rev_parts = P;
     }
     if (G::ATOMIC && th > 0) {
@@ -859,7 +906,7 @@ static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const ui
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(bwd_kernel<NWV>, dim3((unsigned)((int64_t)N * H * G::PARTS)), dim3(G::THREADS), bwd_lds<NWV>(),
                        st, q, k, v, g, beta, scale, cu_safe, chunk_off, H, s0, dout, dsf, dq, dk, dv, dg, dbeta, ds0,
-                       ck, psum, pbeta, th, rev_parts);
+                       ck, psum, pbeta, th, rev_parts, s0_seq, dsf_seq);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (!G::ATOMIC && th > 0)
         hipLaunchKernelGGL(bwd_sum_kernel<G::PARTS>, dim3(eblocks), dim3(256), 0, st, (const float4 *)psum, pbeta,
@@ -868,16 +915,16 @@ static hipError_t launch_bwd_form(const uint16_t *q, const uint16_t *k, const ui
 }
 
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N,
+                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N,
                       int T, int H, const float *s0, const float *dout, const float *dsf, float *dq, float *dk,
                       float *dv, float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves,
                       const BwdParts &parts, hipStream_t st) {
     switch (waves) {
     case 8:
-        return launch_bwd_form<8>(q, k, v, g, beta, scale, cu_safe, chunk_off, order, N, T, H, s0, dout, dsf, dq, dk,
+        return launch_bwd_form<8>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk,
                                   dv, dg, dbeta, ds0, ck, nullptr, parts, st);
     case 4:
-        return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, order, N, T, H, s0, dout, dsf, dq, dk,
+        return launch_bwd_form<4>(q, k, v, g, beta, scale, cu_safe, chunk_off, N, T, H, s0, dout, dsf, dq, dk,
                                   dv, dg, dbeta, ds0, ck, psum, parts, st);
     default:
         return hipErrorInvalidValue;

@@ -128,21 +128,21 @@ hipError_t launch_recurrent_fwd(const uint16_t *q, const uint16_t *k, const uint
 // batch of `tokens` tokens in `seqs` sequences, with an fp32 or a bf16 state
 int recurrent_tile(int64_t chains, int64_t tokens, int64_t seqs, bool bf16_state);
 
-// The parts of every sequence as virtual sequences of cl-token chunks (vcu, vco, vorder:
-// N P + 1, N P + 1, N P), and the composition over parts of affine maps S <- M S + B (ri,
-// rb: [N P][H][128][128] fp32): sin receives each part's entry state, sfin (or NULL) the
-// last exit state, s0 (or NULL: zeros) entering part 0.
-hipError_t launch_parts_setup(const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N, int P,
-                              int cl, int32_t *vcu, int32_t *vco, int32_t *vorder, hipStream_t st);
+// The composition over parts of affine maps S <- M S + B (ri, rb: [N P][H][128][128] fp32):
+// sin receives each part's entry state, sfin (or NULL) the last exit state, s0 (or NULL:
+// zeros) entering part 0. With vcu (the parts' token offsets) only the maps that are needed
+// apply (see parts_combine_kernel); rev: the arrays hold the parts in reverse order.
 hipError_t launch_parts_compose(const float *s0, const float *rb, const float *ri, int N, int P, int H, float *sin,
-                                float *sfin, hipStream_t st);
+                                float *sfin, const int32_t *vcu, bool rev, hipStream_t st);
 
-// Workspace of the backward over P parts per sequence (P > 1): the virtual sequences, and
-// four [N P][H][128][128] fp32 arrays (rb and ri hold the forward maps, then the gradient
-// maps; sinf and sinb the entry states and the exit gradients of the parts).
+// Workspace of the backward over up to P parts per sequence (P > 1): the parts as virtual
+// sequences (vcu, vco: N P + 1 offsets each), and four [N P][H][128][128] fp32 arrays (rb and
+// ri hold the forward maps, then the gradient maps; sinf and sinb the entry states and the
+// exit gradients of the parts). A sequence of c blocks of tokens takes ceil(c / lstar)
+// parts (at most P), the slots after them being empty.
 struct BwdParts {
-    int P;
-    int32_t *vcu, *vco, *vorder;
+    int P, lstar;
+    int32_t *vcu, *vco;
     float *rb, *ri, *sinf, *sinb;
 };
 
@@ -154,7 +154,7 @@ struct BwdParts {
 // chunk length); ck holds a state per block and head. With parts (parts.P > 1) each
 // sequence is cut into P parts of whole blocks, run as sequences of their own.
 hipError_t launch_bwd(const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
-                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N,
+                      float scale, const int32_t *cu_safe, const int32_t *chunk_off, int N,
                       int T, int H, const float *s0, const float *dout, const float *dsf, float *dq, float *dk,
                       float *dv, float *dg, float *dbeta, float *ds0, float *ck, float *psum, int waves,
                       const BwdParts &parts, hipStream_t st);

@@ -1432,12 +1432,20 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_parts_kernel
 constexpr int COMBINE_LD = D + 4;
 constexpr int COMBINE_LDS = (2 * D * COMBINE_LD + D * 16) * (int)sizeof(float);
 
+// With vcu (the parts' token offsets; NULL: every map applies), a part's map is applied only
+// where it is needed: forwards (rev = 0) that of part p while part p + 1 has tokens;
+// backwards (rev = 1: the arrays hold part p at index P - 1 - p) that of part p, p >= 1,
+// while part p has tokens. The parts with tokens of a sequence come first.
 __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, const float *rb, const float *ri,
-                                                            int N, int P, int H, float *sin, float *sfin, int sbf) {
+                                                            int N, int P, int H, float *sin, float *sfin, int sbf,
+                                                            const int32_t *vcu, int rev) {
     extern __shared__ __attribute__((aligned(16))) float combine_lds[];
     float(*Ms)[D][COMBINE_LD] = (float(*)[D][COMBINE_LD])combine_lds;   // [2][D][D + 4]
     float(*S)[16] = (float(*)[16])(combine_lds + 2 * D * COMBINE_LD);     // [D][16]
     const int cs = blockIdx.x % 8, h = (blockIdx.x / 8) % H, n = blockIdx.x / (8 * H);
+    // with vcu, a sequence of one part (or none) has nothing to compose: its part reads the
+    // sequence's own entry state and exit gradient
+    if (vcu && (P < 2 || vcu[n * P + 1] >= vcu[n * P + 2])) return;
     const int t = threadIdx.x, w = t >> 6, l = t & 63, col0 = cs * 16;
     const int lc = l & 15, lk = l >> 4;    // MFMA: column (or row) l % 16, k slot l / 16
     for (int i = t; i < D * 16; i += 256) {
@@ -1446,9 +1454,20 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
         S[rr][cc] = !s0 ? 0.f : sbf ? __uint_as_float((uint32_t)((const uint16_t *)s0)[i0] << 16) : s0[i0];
     }
     auto base_of = [&](int p) { return (((int64_t)n * P + p) * H + h) * D * D; };
+    // with vcu: whether step p applies its map, and whether its entry state is read later
+    auto has_tokens = [&](int part) { return vcu[n * P + part] < vcu[n * P + part + 1]; };
+    auto applies = [&](int p) {
+        const int pp = rev ? P - 1 - p : p;   // the part whose map step p applies
+        return !vcu || (rev ? pp >= 1 && has_tokens(pp) : pp + 1 < P && has_tokens(pp + 1));
+    };
+    auto entry_read = [&](int p) {
+        const int pp = rev ? P - 1 - p : p;
+        return !vcu || pp == 0 || has_tokens(pp);
+    };
     float4 mreg[16];   // one part's M: 16 float4 per thread, element 4 (t + 256 j)
     f32x4 breg[2];     // and its B at this lane's result positions
     auto load_m = [&](int p) {
+        if (!applies(p)) return;
         const float4 *src = (const float4 *)(ri + base_of(p));
 #pragma unroll
         for (int j = 0; j < 16; ++j) mreg[j] = src[t + 256 * j];
@@ -1472,26 +1491,34 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
     __syncthreads();
     for (int p = 0; p < P; ++p) {
         const int64_t base = base_of(p);
+        const bool apply = applies(p);
         f32x4 acc[2] = {breg[0], breg[1]};
         if (p + 1 < P) load_m(p + 1);
         const float(*M)[COMBINE_LD] = Ms[p & 1];
+        if (apply) {
 #pragma unroll 8
-        for (int kk = 0; kk < D / 4; ++kk) {
-            const float b = S[4 * kk + lk][lc];
+            for (int kk = 0; kk < D / 4; ++kk) {
+                const float b = S[4 * kk + lk][lc];
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-                acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(M[32 * w + 16 * rt + lc][4 * kk + lk], b, acc[rt], 0, 0, 0);
+                for (int rt = 0; rt < 2; ++rt)
+                    acc[rt] =
+                        __builtin_amdgcn_mfma_f32_16x16x4f32(M[32 * w + 16 * rt + lc][4 * kk + lk], b, acc[rt], 0, 0, 0);
+            }
         }
         // the entry state of part p, then (after every wave's reads of S) the new state
-        for (int i = t; i < D * 16 / 4; i += 256) {
-            const int rr = i / 4, c4 = (i % 4) * 4;
-            *(float4 *)(sin + base + (int64_t)rr * D + col0 + c4) = *(const float4 *)&S[rr][c4];
+        if (entry_read(p)) {
+            for (int i = t; i < D * 16 / 4; i += 256) {
+                const int rr = i / 4, c4 = (i % 4) * 4;
+                *(float4 *)(sin + base + (int64_t)rr * D + col0 + c4) = *(const float4 *)&S[rr][c4];
+            }
         }
         __syncthreads();   // every read of S and of this part's M is done
+        if (apply) {
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) S[32 * w + 16 * rt + 4 * lk + j][lc] = acc[rt][j];
+                for (int j = 0; j < 4; ++j) S[32 * w + 16 * rt + 4 * lk + j][lc] = acc[rt][j];
+        }
         if (p + 1 < P) store_m((p + 1) & 1);
         __syncthreads();
     }
@@ -1505,21 +1532,14 @@ __global__ __launch_bounds__(256) void parts_combine_kernel(const float *s0, con
     }
 }
 
-// the parts of every sequence as virtual sequences (cl-token chunks), and the composition
-// of their affine maps, for other users of the same scheme (the backward)
-hipError_t launch_parts_setup(const int32_t *cu_safe, const int32_t *chunk_off, const int32_t *order, int N, int P,
-                              int cl, int32_t *vcu, int32_t *vco, int32_t *vorder, hipStream_t st) {
-    hipLaunchKernelGGL(parts_setup_kernel, dim3(64), dim3(256), 0, st, cu_safe, chunk_off, order, N, P, cl, vcu, vco,
-                       vorder, (float *)nullptr, (int64_t)0);
-    return hipGetLastError();
-}
+// the composition of the parts' affine maps, for other users of the same scheme (the backward)
 hipError_t launch_parts_compose(const float *s0, const float *rb, const float *ri, int N, int P, int H, float *sin,
-                                float *sfin, hipStream_t st) {
+                                float *sfin, const int32_t *vcu, bool rev, hipStream_t st) {
     static std::atomic<uint64_t> lds_set{0};
     if (ensure_lds_limit((const void *)parts_combine_kernel, COMBINE_LDS, lds_set) != hipSuccess)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), COMBINE_LDS, st, s0, rb, ri, N, P,
-                       H, sin, sfin, 0);
+                       H, sin, sfin, 0, vcu, (int)rev);
     return hipGetLastError();
 }
 
@@ -1552,7 +1572,7 @@ hipError_t launch_parts(const char *recs, const uint16_t *v, const int32_t *cu_s
     if (ensure_lds_limit((const void *)parts_combine_kernel, COMBINE_LDS, combine_lds_set) != hipSuccess)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(parts_combine_kernel, dim3((unsigned)(N * H * 8)), dim3(256), COMBINE_LDS, st, s0,
-                       (const float *)rb, (const float *)ri, N, P, H, sin, sfin, (int)sbf);
+                       (const float *)rb, (const float *)ri, N, P, H, sin, sfin, (int)sbf, (const int32_t *)nullptr, 0);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (h32) return launch_recur_h32_range(recs, v, vcu, vco, vorder, NV, T, H, sin, out, nullptr, nullptr,
                                            pass2_waves, 0, SEG_ONE, false, st);

@@ -207,3 +207,18 @@ def test_bwd_parts_slow_decay(monkeypatch):
     do, dsf = _grads_in(w, 82, True)
     _say("[bwd] parts=4, g = 0, beta = 0.05")
     _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), "parts slow decay")
+
+
+@pytest.mark.parametrize("waves", [8, 4])
+def test_bwd_parts_by_length(monkeypatch, waves):
+    """Parts in proportion to each sequence's length (one per 128 tokens here, at most 8):
+    700 tokens in 6 parts, 300 in 3, the short and the empty sequences in one (no state
+    passes for them), the other slots empty."""
+    monkeypatch.setenv("KDA_BWD_WAVES", str(waves))
+    monkeypatch.setenv("KDA_BWD_PARTS", "8")
+    monkeypatch.setenv("KDA_BWD_PART_TOKENS", "128")
+    w = synth.make_workload([700, 40, 0, 300, 5], 2, 83, with_initial_state=True, clamp_frac=0.1)
+    _below_bound(w, 83)
+    do, dsf = _grads_in(w, 83, True)
+    _say(f"[bwd] parts by length, waves={waves}")
+    _check(_run_gpu(w, do, dsf), _run_oracle(w, do, dsf), f"parts by length w{waves}")
