@@ -597,7 +597,8 @@ static bool bwd_layout(int64_t N, int64_t T, int64_t H, BwdLayout *B) {
     B->waves = bwd_waves(N, T, H);
     const BwdSplit sp = bwd_parts(N, T, H, B->waves);
     B->P = sp.P, B->lstar = sp.lstar;
-    if (N * B->P * H > (int64_t)1 << 24) B->P = 1;
+    // the parts' four state arrays stay within 8 GiB
+    if (N * B->P * H > (int64_t)1 << 24 || 4 * N * B->P * H * (int64_t)STATE_BYTES > ((int64_t)8 << 30)) B->P = 1;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     B->ck = L.total;
     B->psum = up(B->ck + (size_t)max_chunks(N, T, KDA_BWD_BLOCK) * (size_t)H * STATE_BYTES);

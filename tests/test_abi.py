@@ -199,3 +199,28 @@ def test_bwd_workspace_bytes(lib):
     # a state per block of KDA_BWD_BLOCK tokens and head
     assert b >= (T // 4) * H * state
     assert "#define KDA_BWD_BLOCK 4" in open(HEADER).read()
+
+
+def test_bwd_workspace_forms(lib, monkeypatch):
+    """The workspace covers each backward form: the checkpoints alone (two 8-wave blocks per
+    chain, no parts); plus four partial sums of 385 floats per token-head (four 4-wave
+    blocks per chain, below 96 chains); plus four states per part slot and head and the
+    parts' offsets (over parts)."""
+    state = 128 * 128 * 4
+    N, T, H = 1, 8192, 32
+    for var in ("KDA_BWD_WAVES", "KDA_BWD_PARTS", "KDA_BWD_PART_TOKENS"):
+        monkeypatch.delenv(var, raising=False)
+    monkeypatch.setenv("KDA_BWD_WAVES", "8")
+    monkeypatch.setenv("KDA_BWD_PARTS", "1")
+    base = lib.kda_bwd_workspace_bytes(N, T, H)
+    assert base >= (T // 4) * H * state
+    monkeypatch.setenv("KDA_BWD_WAVES", "4")
+    partial = lib.kda_bwd_workspace_bytes(N, T, H)
+    assert partial - base >= 4 * T * H * 385 * 4
+    monkeypatch.setenv("KDA_BWD_PARTS", "8")
+    parts = lib.kda_bwd_workspace_bytes(N, T, H)
+    assert parts - partial >= 4 * N * 8 * H * state + 2 * (N * 8 + 1) * 4
+    # the default for one long sequence of 32 heads: four-wave blocks over parts
+    monkeypatch.delenv("KDA_BWD_WAVES")
+    monkeypatch.delenv("KDA_BWD_PARTS")
+    assert lib.kda_bwd_workspace_bytes(N, T, H) == parts
