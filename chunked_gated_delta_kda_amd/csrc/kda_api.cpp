@@ -69,13 +69,11 @@ size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 // chunks of cl tokens: an upper bound over any split of T tokens into N sequences
 int64_t max_chunks(int64_t N, int64_t T, int cl = KDA_CHUNK) { return (T + cl - 1) / cl + N; }
 
-// The recurrence form 301 consumes 32-token chunk records; all others 16-token ones.
-// Forms 401/402 consume 32-token chunk records with fp16 operands (kda_h32.hip).
-int chunk_len(int waves) { return waves >= 300 ? 32 : KDA_CHUNK; }
+// Forms 401/402 consume 32-token chunk records with fp16 operands (kda_h32.hip); all
+// others 16-token ones.
 bool fp16_form(int waves) { return waves == 401 || waves == 402; }
-size_t rec_bytes(int waves) {
-    return fp16_form(waves) ? kda::RECH_BYTES : waves >= 300 ? kda::REC32_BYTES : kda::REC_BYTES;
-}
+int chunk_len(int waves) { return fp16_form(waves) ? 32 : KDA_CHUNK; }
+size_t rec_bytes(int waves) { return fp16_form(waves) ? kda::RECH_BYTES : kda::REC_BYTES; }
 
 // Workspace: chunk offsets [N+1], sequence order [N], an error word, the sanitised
 // sequence offsets [N+1], and (split variant only) a state carry buffer [N, H, 128, 128]
@@ -100,7 +98,6 @@ constexpr size_t STATE_BYTES = (size_t)KDA_HEAD_DIM * KDA_HEAD_DIM * sizeof(floa
 // but 32768 x 16 1.21 | 1.41 (2). KDA_PARTS (1..MAX_PARTS) overrides, for the 16-token
 // forms.
 int split_parts(int64_t N, int64_t T, int64_t H, int waves) {
-    if (waves == 301) return 1;
     if (const char *e = std::getenv("KDA_PARTS")) {
         const int p = std::atoi(e);
         if (p >= 1 && p <= MAX_PARTS) return p;
@@ -180,12 +177,12 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 // per block, each owning 16 value columns and forming its own outputs; the block's waves
 // share each chunk record through one LDS ring 2 chunks deep. 101, 102: the paired form
 // (1 or 2 slices per block, a chain wave and two output waves per slice, one loader
-// wave). 301: the paired form over 32-token chunks. KDA_RECUR_WAVES overrides the
-// choice, for tuning.
+// wave). 401, 402: the paired form over 32-token chunks with fp16 operands (kda_h32.hip).
+// KDA_RECUR_WAVES overrides the choice, for tuning.
 int recur_waves(int64_t N, int64_t T, int64_t H, const char *env = "KDA_RECUR_WAVES") {
     if (const char *e = std::getenv(env)) {
         const int w = std::atoi(e);
-        if (w == 8 || w == 9 || w == 101 || w == 102 || w == 301 || w == 401 || w == 402) return w;
+        if (w == 8 || w == 9 || w == 101 || w == 102 || w == 401 || w == 402) return w;
     }
     // The 32-token fp16 forms (401: one 16-column slice per block, 402: two) take one
     // serial step per 32 tokens. Measured on MI355X (ms per call; 401 | 402 | paired
@@ -418,7 +415,6 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     const int parts = chosen == KDA_VARIANT_SPLIT ? split_parts(N, T, H, waves) : 1;
     const Layout lay = ws_layout(N, T, H, chosen, segs, waves, parts);
     const int cl = chosen == KDA_VARIANT_SPLIT ? chunk_len(waves) : KDA_CHUNK;
-    const bool c32 = cl == 32 && !fp16_form(waves);
     const bool h32 = fp16_form(waves);
 
     // profiling events: [0] before the first kernel launch, [i] after the i-th (all on
@@ -466,13 +462,11 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
         const int64_t M = max_chunks(N, T, cl);
         auto prep = [&](int b, int e) {
             if (h32) return kda::launch_prep_h32(q16, k16, g, g_bf16, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
-            return c32 ? kda::launch_prep32(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st)
-                       : kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
+            return kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
         };
         auto recur_range = [&](float *carry, int b, int e) {
             if (h32) return kda::launch_recur_h32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, s_bf16, st);
-            return c32 ? kda::launch_recur32_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st)
-                       : kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
+            return kda::launch_recur_range(recs, v16, cus, chunk_off, order, N, T, H, initial_state, out, final_state, carry, waves, b, e, st);
         };
         if (parts > 1) {
             const int NV = N * parts;
@@ -507,9 +501,7 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
                 a.fb = bound(sg), a.fe = bound(sg + 1), a.pb = bound(sg + 1), a.pe = bound(sg + 2);
                 ok = around(st, [&] {
-                    return h32   ? kda::launch_recur_h32_prep(a, waves, st)
-                           : c32 ? kda::launch_recur32_prep(a, waves, st)
-                                 : kda::launch_recur_prep(a, waves, st);
+                    return h32 ? kda::launch_recur_h32_prep(a, waves, st) : kda::launch_recur_prep(a, waves, st);
                 });
             }
             ok = ok && around(st, [&] { return recur_range(a.carry, bound(segs - 1), kda::SEG_ONE); });

@@ -28,7 +28,6 @@ inline hipError_t ensure_lds_limit(const void *kern, int bytes, std::atomic<uint
 int32_t *device_error_word();
 
 constexpr int REC_BYTES = 23552;   // bytes of one 16-token chunk record (Rec::BYTES)
-constexpr int REC32_BYTES = 50176; // bytes of one 32-token chunk record (Rec32::BYTES)
 constexpr int RECH_BYTES = 37888;  // bytes of one 32-token chunk record of forms 401/402 (RecH::BYTES)
 
 // Segments of the split path. A launch over the segment [fb, fe) covers, of every
@@ -50,12 +49,7 @@ inline int64_t seg_chunks_bound(int64_t M, int N, int fb, int fe) {
 hipError_t launch_chunk_map(const int32_t *cu, int N, int T, int32_t *cu_safe, int32_t *chunk_off,
                             int32_t *order, int32_t *err, int cl, hipStream_t st);
 
-// Records (16-token chunks; 32-token with prep32) of the segment [fb, fe); M bounds the
-// batch's chunk count.
-hipError_t launch_prep32(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
-                         const int32_t *cu, int N, int T, int H, float scale,
-                         const int32_t *chunk_off, char *recs, int fb, int fe, int64_t M,
-                         hipStream_t st);
+// Records (16-token chunks) of the segment [fb, fe); M bounds the batch's chunk count.
 
 hipError_t launch_prep(const uint16_t *q, const uint16_t *k, const float *g, const float *beta,
                        const int32_t *cu, int N, int T, int H, float scale,
@@ -85,13 +79,6 @@ struct RecurPrepArgs {
     bool state_bf16 = false;  // s0 and sfin hold bf16 bits (forms 401/402 only)
 };
 hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
-// 32-token form (waves 301: one slice per block): recurrence over the segment
-// [fb, fe), alone or with the prep of [pb, pe) on the idle CUs
-hipError_t launch_recur32_range(const char *recs, const uint16_t *v, const int32_t *cu,
-                                const int32_t *chunk_off, const int32_t *order, int N, int T,
-                                int H, const float *s0, float *out, float *sfin, float *carry,
-                                int waves, int fb, int fe, hipStream_t st);
-hipError_t launch_recur32_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 
 // 32-token chunks with fp16 recurrence operands (kda_h32.hip): records of the segment
 // [fb, fe); recurrence forms 401 (one 16-column slice per block) and 402 (two), alone or

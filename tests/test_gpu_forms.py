@@ -18,7 +18,7 @@ from kda_check import compare, run_gpu, run_oracle
 
 pytestmark = pytest.mark.gpu
 
-FORMS = [8, 9, 101, 102, 301, 401, 402]
+FORMS = [8, 9, 101, 102, 401, 402]
 SEGMENTS = [1, 2, 3, 8]
 LENGTHS = [70, 0, 300, 16, 1, 129]
 

@@ -32,7 +32,7 @@ CASES = [
     ("split", {"KDA_RECUR_WAVES": "9"}),
     ("split", {"KDA_RECUR_WAVES": "9", "KDA_SEGMENTS": "3"}),
     ("split", {"KDA_PARTS": "3"}),
-    ("split", {"KDA_RECUR_WAVES": "301", "KDA_SEGMENTS": "2"}),
+    ("split", {"KDA_RECUR_WAVES": "401", "KDA_SEGMENTS": "2"}),
     ("fused", {}),
     ("recurrent", {}),
 ]
