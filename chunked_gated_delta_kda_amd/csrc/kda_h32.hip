@@ -725,65 +725,97 @@ __device__ __forceinline__ void recur_h32_block(int bid, char *ring, const char 
     // ---- output wave: chunks m = parity, parity + 2, ...; key blocks 0-1 of chunk m's
     // output after barrier m+1, the rest and P V_new after barrier m+2. Its Q+ and P
     // pieces come straight from global memory into registers, four chunks ahead.
+    // One slice per block: the wave forms both 16-row blocks of its slice. Two slices:
+    // output wave `slice` of a parity forms row block `slice` of both slices, so that the
+    // block reads each chunk's Q+ and P pieces once (each wave the half of its rows), not
+    // once per slice.
+    constexpr int NR = NW == 1 ? 2 : 1;     // row blocks per output wave
+    constexpr int NSL = NW;                  // slices per output wave
+    auto row_block = [&](int r) { return NW == 1 ? r : slice; };
+    auto slice_of = [&](int s) { return NW == 1 ? slice : s; };
     struct OutIn {
-        bf16x8 qh[8], ql[8];
-        f16x8 pp[2];
+        bf16x8 qh[4 * NR], ql[4 * NR];
+        f16x8 pp[NR];
     };
     auto load = [&](OutIn &x, int m) {
         const char *rec = rec_of(m);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            x.qh[i] = *(const bf16x8 *)(rec + RecH::QH + i * 1024 + l * 16);
-            x.ql[i] = *(const bf16x8 *)(rec + RecH::QL + i * 1024 + l * 16);
+        for (int r = 0; r < NR; ++r) {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int piece = (4 * row_block(r) + kb) * 1024;
+                x.qh[4 * r + kb] = *(const bf16x8 *)(rec + RecH::QH + piece + l * 16);
+                x.ql[4 * r + kb] = *(const bf16x8 *)(rec + RecH::QL + piece + l * 16);
+            }
+            x.pp[r] = *(const f16x8 *)(rec + RecH::PP + row_block(r) * 1024 + l * 16);
         }
-        x.pp[0] = *(const f16x8 *)(rec + RecH::PP + l * 16);
-        x.pp[1] = *(const f16x8 *)(rec + RecH::PP + 1024 + l * 16);
     };
-    // two accumulators per row block, so that no product waits on the one before it
-    f32x4 oa = zero, ob = zero, oc = zero, od = zero;
+    auto snap_sl = [&](int m, int s) { return snaps + ((m % P::SNAPS) * NW + slice_of(s)) * P::SNAP; };
+    // two accumulators per (row block, slice): Q+hi S_hi and Q+lo S_hi in oa, Q+hi S_lo
+    // and P V_new in oc, so that no product waits on the one before it
+    f32x4 oa[NR][NSL], oc[NR][NSL];
     auto half_qs = [&](const OutIn &x, int m, int kb0) {
-        const char *snap = snap_of(m);
 #pragma unroll
         for (int kb = kb0; kb < kb0 + 2; ++kb) {
-            const f32x4 s0 = *(const f32x4 *)(snap + (2 * kb) * 1024 + l * 16);
-            const f32x4 s1 = *(const f32x4 *)(snap + (2 * kb + 1) * 1024 + l * 16);
-            bf16x4 h0, l0, h1, l1;
-            split4(s0, h0, l0);
-            split4(s1, h1, l1);
-            const bf16x8 sh = cat(h0, h1), sl = cat(l0, l1);
-            oa = mfma(x.qh[kb], sh, oa);
-            ob = mfma(x.qh[4 + kb], sh, ob);
-            oc = mfma(x.qh[kb], sl, oc);
-            od = mfma(x.qh[4 + kb], sl, od);
-            oa = mfma(x.ql[kb], sh, oa);
-            ob = mfma(x.ql[4 + kb], sh, ob);
+            bf16x8 sh[NSL], sl[NSL];
+#pragma unroll
+            for (int s = 0; s < NSL; ++s) {
+                const char *snap = snap_sl(m, s);
+                const f32x4 s0 = *(const f32x4 *)(snap + (2 * kb) * 1024 + l * 16);
+                const f32x4 s1 = *(const f32x4 *)(snap + (2 * kb + 1) * 1024 + l * 16);
+                bf16x4 h0, l0, h1, l1;
+                split4(s0, h0, l0);
+                split4(s1, h1, l1);
+                sh[s] = cat(h0, h1);
+                sl[s] = cat(l0, l1);
+            }
+#pragma unroll
+            for (int s = 0; s < NSL; ++s)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) oa[r][s] = mfma(x.qh[4 * r + kb], sh[s], oa[r][s]);
+#pragma unroll
+            for (int s = 0; s < NSL; ++s)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) oc[r][s] = mfma(x.qh[4 * r + kb], sl[s], oc[r][s]);
+#pragma unroll
+            for (int s = 0; s < NSL; ++s)
+#pragma unroll
+                for (int r = 0; r < NR; ++r) oa[r][s] = mfma(x.ql[4 * r + kb], sh[s], oa[r][s]);
         }
     };
     auto first = [&](const OutIn &x, int m) {
-        oa = zero;
-        ob = zero;
-        oc = zero;
-        od = zero;
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int s = 0; s < NSL; ++s) oa[r][s] = zero, oc[r][s] = zero;
         half_qs(x, m, 0);
         __builtin_amdgcn_s_waitcnt(0xc07f);   // snapshot reads done before the next barrier
     };
     auto finish = [&](const OutIn &x, int m) {
-        const char *snap = snap_of(m);
-        const f16x8 vn = *(const f16x8 *)(snap + 8192 + l * 16);
+        f16x8 vn[NSL];
+#pragma unroll
+        for (int s = 0; s < NSL; ++s) vn[s] = *(const f16x8 *)(snap_sl(m, s) + 8192 + l * 16);
         half_qs(x, m, 2);
-        oc = mfma16(x.pp[0], vn, oc);
-        od = mfma16(x.pp[1], vn, od);
-        oa += oc;
-        ob += od;
         const int64_t t0 = bos + (int64_t)CH * m;
         const int nc = (int)min<int64_t>(CH, eos - t0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float *da = 4 * gq + j < nc ? out + ((t0 + 4 * gq + j) * H + h) * D + col : h32_sink + l;
-            float *db = C + 4 * gq + j < nc ? out + ((t0 + C + 4 * gq + j) * H + h) * D + col : h32_sink + l;
-            *da = oa[j];
-            *db = ob[j];
-        }
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int s = 0; s < NSL; ++s) {
+                oc[r][s] = mfma16(x.pp[r], vn[s], oc[r][s]);
+                oa[r][s] += oc[r][s];
+            }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < NR; ++r)
+#pragma unroll
+                for (int s = 0; s < NSL; ++s) {
+                    const int row = C * row_block(r) + 4 * gq + j;
+                    const int cs = vcol0 + slice_of(s) * 16 + c;
+                    float *d = row < nc ? out + ((t0 + row) * H + h) * D + cs : h32_sink + l;
+                    *d = oa[r][s][j];
+                }
         __builtin_amdgcn_s_waitcnt(0xc07f);
     };
     OutIn X, Y;
