@@ -199,6 +199,16 @@ int recur_waves(int64_t N, int64_t T, int64_t H, const char *env = "KDA_RECUR_WA
     // balanced share, one eight-wave block otherwise) and so keeps one long sequence in
     // a batch of short ones off a slow eight-wave block.
     const int64_t chains = N * H;
+    // 25-32 chains of 8192 tokens or more: the two-slice form on half the CUs, with the
+    // prep of the next segment on the other half (split_segments), beats the one-slice
+    // form on all of them. Measured on MI355X (ms; 401 | 402 over 3, 4, 5 segments): 8192
+    // tokens x 32 heads 0.361 | 0.356, 0.344, 0.345; 16384 x 32 0.681 | 0.660, 0.654,
+    // 0.665; but 8192 x 24 0.305 | 0.313, 0.310, 0.313; 2 x 4096 x 16 0.177 | 0.191,
+    // 0.195, 0.204; 4096 x 32 0.173 | 0.188, 0.194, 0.202; 8192 x 16 0.222 | 0.283. With
+    // 4 segments (segment ratio 1.0 | 1.25 | 1.6): 8192 x 32 0.355 | 0.346 | 0.361 (401:
+    // 0.360); 8192 x 28 0.337 | 0.325 | 0.340 (401: 0.348); 32768 x 32 1.277 | 1.262 |
+    // 1.275 (401: 1.326).
+    if (chains > 24 && chains <= 32 && T >= 8192 * N) return 402;
     if (chains <= 32) return 401;
     if (chains < 192) return 402;
     return T >= 1024 * N ? 402 : 9;
@@ -224,6 +234,9 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     // 1.023 | 1.052 | 1.075; 16 x 2048 x 32 1.032 | 1.084 | 1.124; 16 x 1024 x 16 0.263 |
     // 0.299 | 0.322. KDA_SEGMENTS selects segments for it (parity-tested).
     if (waves == 9) return 1;
+    // the two-slice 32-token form on 25-32 long chains (recur_waves): 4 segments, measured
+    // best of 3-5 (above)
+    if (waves == 402 && N * H <= 32) return 4;
     // The prep of a segment (work ~ the chain count) runs on the CUs the recurrence
     // leaves idle and must fit under its time: segments only with at least 2.5 idle CUs
     // per chain. Measured on MI355X (ms, 8192 tokens; unsegmented | segmented): 101 with
