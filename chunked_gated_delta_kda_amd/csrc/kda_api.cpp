@@ -214,6 +214,12 @@ int recur_waves(int64_t N, int64_t T, int64_t H, const char *env = "KDA_RECUR_WA
     return T >= 1024 * N ? 402 : 9;
 }
 
+// The split path's first prep forms the chunk map itself (no chunk-map launch) for the
+// 32-token forms the shape picks by itself and batches of at most 63 sequences.
+bool map_in_prep(int64_t N, int64_t T, int64_t H) {
+    return fp16_form(recur_waves(N, T, H)) && kda::prep_h32_maps((int)N);
+}
+
 // Number of segments of the split variant. With S > 1 the launches are
 // prep(segment 0), then recurrence(s) fused with prep(s+1) for s < S-1, then
 // recurrence(S-1): the prep of later segments runs on the CUs the recurrence leaves
@@ -351,7 +357,8 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
         for (int i = 0; info && i < n && i < max_launches; ++i) info[i] = plan[i];
         return n;
     }
-    plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
+    if (v != KDA_VARIANT_SPLIT || !map_in_prep(num_seqs, total_tokens, num_heads))
+        plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
         auto bound = [&](int sg) { return (int32_t)segment_frac(sg, segs, (int64_t)num_seqs * num_heads); };
@@ -470,10 +477,16 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
     int32_t *cus = (int32_t *)(ws + lay.cu);   // sanitised cu_seqlens, written by the chunk map
     char *recs = ws + lay.recs;
 
-    bool ok = around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, cl, st); });
+    // the chunk map: a launch of its own, or formed by the first prep (map_in_prep)
+    const bool mapped = chosen == KDA_VARIANT_SPLIT && h32 && map_in_prep(N, T, H);
+    bool ok = mapped ||
+              around(st, [&] { return kda::launch_chunk_map(cu_seqlens, N, T, cus, chunk_off, order, err, cl, st); });
     if (ok && chosen == KDA_VARIANT_SPLIT) {
         const int64_t M = max_chunks(N, T, cl);
         auto prep = [&](int b, int e) {
+            if (mapped && b == 0)
+                return kda::launch_prep_h32_map(q16, k16, g, g_bf16, beta, cu_seqlens, N, T, H, scale, recs, e, M,
+                                                cus, chunk_off, order, err, st);
             if (h32) return kda::launch_prep_h32(q16, k16, g, g_bf16, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
             return kda::launch_prep(q16, k16, g, beta, cus, N, T, H, scale, chunk_off, recs, b, e, M, st);
         };

@@ -40,6 +40,7 @@
 // stands in registers.
 #include <type_traits>
 
+#include "kda.h"
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -422,6 +423,119 @@ __global__ __launch_bounds__(64) void prep_h32_kernel(const uint16_t *__restrict
     const int ci = seg_chunk_of(chunk_off, N, H, fb, fe, blockIdx.x, h);
     if (ci < 0) return;
     prep_h32_one(q, k, g, beta, cu, N, T, H, scale, chunk_off, recs, ci, h, L);
+}
+
+// ---------------------------------------------------------------- chunk map in the prep
+// For batches of at most MAP_WAVE_MAX sequences the first prep launch forms the chunk map
+// itself instead of a launch of its own before it: each wave derives it from the caller's
+// offsets in registers (lane n: offset n and the chunks before sequence n), with the
+// sanitising of the chunk-map kernel (every offset clamped to [0, T] and raised to the
+// largest offset before it; the error bit when the offsets were not 0 = c_0 <= c_1 <= ...
+// <= c_N = T), and block 0 stores it (sanitised offsets, chunk offsets, longest-first
+// order, error word) for the kernels after it.
+constexpr int MAP_WAVE_MAX = 63;   // N + 1 offsets in one wave's lanes
+constexpr int MAP_ERR_CU_SEQLENS = KDA_DEVERR_CU_SEQLENS;
+
+struct WaveMap {
+    int32_t cs;   // lane n <= N: sanitised offset n
+    int32_t co;   // lane n <= N: chunks (of CH tokens) before sequence n
+    bool bad;     // the offsets were malformed (the same in every lane)
+};
+
+__device__ __forceinline__ WaveMap wave_map(const int32_t *__restrict__ cu, int N, int T) {
+    const int l = threadIdx.x & 63;
+    int32_t raw = 0;
+    if (l <= N) raw = cu ? cu[l] : (l == 0 ? 0 : T);
+    const int32_t prev = __shfl_up(raw, 1);
+    const bool bad = l <= N && ((l == 0 && raw != 0) || (l > 0 && raw < prev) || (l == N && raw != T));
+    int32_t x = l <= N ? min(max(raw, 0), T) : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {       // running maximum (lanes past N: the last offset)
+        const int32_t y = __shfl_up(x, d);
+        if (l >= d) x = max(x, y);
+    }
+    const int32_t nxt = __shfl_down(x, 1);
+    int32_t c = l < N ? (nxt - x + CH - 1) / CH : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {       // inclusive sum of the chunk counts
+        const int32_t y = __shfl_up(c, d);
+        if (l >= d) c += y;
+    }
+    int32_t co = __shfl_up(c, 1);
+    if (l == 0) co = 0;
+    WaveMap m;
+    m.cs = x;
+    m.co = co;
+    m.bad = __ballot(bad) != 0;
+    return m;
+}
+
+// value of lane i (i uniform across the wave)
+__device__ __forceinline__ int32_t lane_val(int32_t x, int i) {
+    return __builtin_amdgcn_readlane(x, i);
+}
+
+// The map's outputs for the later kernels (one wave).
+__device__ __forceinline__ void wave_map_store(const WaveMap &m, int N, int32_t *__restrict__ cu_safe,
+                                               int32_t *__restrict__ chunk_off, int32_t *__restrict__ order,
+                                               int32_t *__restrict__ err, int32_t *dev_err) {
+    const int l = threadIdx.x & 63;
+    if (l <= N) {
+        cu_safe[l] = m.cs;
+        chunk_off[l] = m.co;
+    }
+    const int32_t len = __shfl_down(m.cs, 1) - m.cs;   // lane n < N: length of sequence n
+    int rank = 0;
+    for (int j = 0; j < N; ++j) {
+        const int32_t lj = lane_val(len, j);
+        rank += (lj > len) || (lj == len && j < l);
+    }
+    if (l < N) order[rank] = l;
+    if (l == 0) {
+        *err = m.bad ? MAP_ERR_CU_SEQLENS : 0;
+        if (m.bad && dev_err) atomicOr(dev_err, MAP_ERR_CU_SEQLENS);
+    }
+}
+
+// The prep of the segment [0, fe) with the chunk map formed in the launch (N <= MAP_WAVE_MAX):
+// cu is the caller's offsets; block 0 also stores the map.
+template <typename GT>
+__global__ __launch_bounds__(64) void prep_h32_map_kernel(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                          const GT *__restrict__ g, const float *__restrict__ beta,
+                                                          const int32_t *__restrict__ cu, int N, int T, int H,
+                                                          float scale, char *__restrict__ recs, int fe,
+                                                          int32_t *__restrict__ cu_safe, int32_t *__restrict__ chunk_off,
+                                                          int32_t *__restrict__ order, int32_t *__restrict__ err,
+                                                          int32_t *dev_err) {
+    __shared__ PrepHLds L;
+    const WaveMap m = wave_map(cu, N, T);
+    if (blockIdx.x == 0) wave_map_store(m, N, cu_safe, chunk_off, order, err, dev_err);
+    // chunk and head of this wave (as seg_chunk_of over [0, fe))
+    const int h = (int)(blockIdx.x % H);
+    int c = (int)(blockIdx.x / H), ci = -1;
+    if (fe == SEG_ONE) {
+        ci = c < lane_val(m.co, N) ? c : -1;
+    } else {
+        for (int n = 0; n < N; ++n) {
+            const int c0 = lane_val(m.co, n), e = seg_chunk(lane_val(m.co, n + 1) - c0, fe);
+            if (c < e) {
+                ci = c0 + c;
+                break;
+            }
+            c -= e;
+        }
+    }
+    if (ci < 0) return;
+    int lo = 0, hi = N - 1;   // sequence owning chunk ci: largest n with co[n] <= ci
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (lane_val(m.co, mid) <= ci) lo = mid; else hi = mid - 1;
+    }
+    const int n = lo;
+    const int64_t bos = lane_val(m.cs, n), eos = lane_val(m.cs, n + 1);
+    const int64_t t0 = bos + (int64_t)CH * (ci - lane_val(m.co, n));
+    const int nc = (int)min<int64_t>(CH, eos - t0);
+    prep_h32(q, k, g, beta, t0, nc, h, H, scale, L, recs + ((int64_t)ci * H + h) * RecH::BYTES);
 }
 
 // ---------------------------------------------------------------- recurrence
@@ -910,6 +1024,26 @@ hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const void *g, 
     else
         hipLaunchKernelGGL(prep_h32_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, st, q, k, (const float *)g,
                            beta, cu, N, T, H, scale, chunk_off, recs, fb, fe);
+    return hipGetLastError();
+}
+
+bool prep_h32_maps(int N) { return N >= 1 && N <= MAP_WAVE_MAX; }
+
+hipError_t launch_prep_h32_map(const uint16_t *q, const uint16_t *k, const void *g, bool g_bf16, const float *beta,
+                               const int32_t *cu, int N, int T, int H, float scale, char *recs, int fe, int64_t M,
+                               int32_t *cu_safe, int32_t *chunk_off, int32_t *order, int32_t *err, hipStream_t st) {
+    if (!prep_h32_maps(N) || fe <= 0 || fe > SEG_ONE) return hipErrorInvalidValue;
+    // at least one block: block 0 stores the map even when there are no chunks
+    int64_t blocks = seg_chunks_bound(M, N, 0, fe) * H;
+    if (blocks < 1) blocks = 1;
+    if (g_bf16)
+        hipLaunchKernelGGL(prep_h32_map_kernel<uint16_t>, dim3((unsigned)blocks), dim3(64), 0, st, q, k,
+                           (const uint16_t *)g, beta, cu, N, T, H, scale, recs, fe, cu_safe, chunk_off, order, err,
+                           device_error_word());
+    else
+        hipLaunchKernelGGL(prep_h32_map_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, st, q, k,
+                           (const float *)g, beta, cu, N, T, H, scale, recs, fe, cu_safe, chunk_off, order, err,
+                           device_error_word());
     return hipGetLastError();
 }
 

@@ -87,6 +87,14 @@ hipError_t launch_recur_prep(const RecurPrepArgs &a, int waves, hipStream_t st);
 hipError_t launch_prep_h32(const uint16_t *q, const uint16_t *k, const void *g, bool g_bf16, const float *beta,
                            const int32_t *cu, int N, int T, int H, float scale, const int32_t *chunk_off,
                            char *recs, int fb, int fe, int64_t M, hipStream_t st);
+// The same for the first segment [0, fe) with the chunk map formed in the launch (no
+// chunk-map launch before it): cu is the caller's offsets, and the launch stores cu_safe,
+// chunk_off, order and the error word as launch_chunk_map does (32-token chunks). Only for
+// prep_h32_maps(N), batches of at most 63 sequences.
+bool prep_h32_maps(int N);
+hipError_t launch_prep_h32_map(const uint16_t *q, const uint16_t *k, const void *g, bool g_bf16, const float *beta,
+                               const int32_t *cu, int N, int T, int H, float scale, char *recs, int fe, int64_t M,
+                               int32_t *cu_safe, int32_t *chunk_off, int32_t *order, int32_t *err, hipStream_t st);
 hipError_t launch_recur_h32_range(const char *recs, const uint16_t *v, const int32_t *cu, const int32_t *chunk_off,
                                   const int32_t *order, int N, int T, int H, const float *s0, float *out, float *sfin,
                                   float *carry, int waves, int fb, int fe, bool sbf, hipStream_t st);

@@ -123,11 +123,15 @@ def test_workspace_bytes(lib):
 
 def test_launch_plan():
     from chunked_gated_delta_kda_amd import native as nat
-    for N, T, H in ((1, 8192, 32), (2, 4096, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32)):
+    for N, T, H in ((1, 8192, 32), (2, 4096, 8), (8, 8192, 16), (64, 100000, 32), (12, 32768, 32),
+                    (200, 51200, 8)):
         plan = nat.launch_plan(N, T, H, "split")
         kinds = [p[0] for p in plan]
-        assert kinds[:2] == ["chunk_map", "prep"] and kinds[-1] == "recur"
-        assert set(kinds[2:-1]) <= {"recur_prep"}
+        # the 32-token forms form the chunk map in their first prep for up to 63
+        # sequences; otherwise it is a launch of its own
+        head = ["prep"] if N <= 63 and plan[0][3] == 32 else ["chunk_map", "prep"]
+        assert kinds[:len(head)] == head and kinds[-1] == "recur"
+        assert set(kinds[len(head):-1]) <= {"recur_prep"}
         cl = plan[0][3]
         assert cl in (16, 32) and all(p[3] == cl for p in plan)
         one = nat.SEGMENT_ONE
@@ -135,8 +139,9 @@ def test_launch_plan():
         # the prep segments and the recurrence segments each tile [0, SEGMENT_ONE) in
         # order, and a segment's records are prepared in an earlier launch than its
         # recurrence
-        preps = [p[1] for p in plan[1:] if p[1] != (0, 0)]
-        recs = [p[2] for p in plan[1:] if p[2] != (0, 0)]
+        work = plan[len(head) - 1:]      # the launches after the chunk map, if any
+        preps = [p[1] for p in work if p[1] != (0, 0)]
+        recs = [p[2] for p in work if p[2] != (0, 0)]
         for ranges in (preps, recs):
             assert ranges[0][0] == 0 and ranges[-1][1] == one
             assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
@@ -154,18 +159,20 @@ def test_launch_plan():
             assert got == list(range(c))
     # few long chains: the recurrence runs over parts of each sequence, in one launch
     # entry after the prep of all chunks
-    assert [p[0] for p in nat.launch_plan(1, 65536, 8, "split")] == ["chunk_map", "prep", "parts"]
-    assert [p[0] for p in nat.launch_plan(1, 65536, 4, "split")] == ["chunk_map", "prep", "parts"]
-    assert [p[0] for p in nat.launch_plan(1, 8192, 8, "split")] == ["chunk_map", "prep", "parts"]
-    assert [p[0] for p in nat.launch_plan(1, 2048, 8, "split")] == ["chunk_map", "prep", "recur"]
+    assert [p[0] for p in nat.launch_plan(1, 65536, 8, "split")] == ["prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 65536, 4, "split")] == ["prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 8192, 8, "split")] == ["prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(1, 2048, 8, "split")] == ["prep", "recur"]
     # 16 chains of 1,024 chunks (32 tokens) each: four parts, pass 2 with two slices per block
-    assert [p[0] for p in nat.launch_plan(2, 65536, 8, "split")] == ["chunk_map", "prep", "parts"]
+    assert [p[0] for p in nat.launch_plan(2, 65536, 8, "split")] == ["prep", "parts"]
     assert [p[0] for p in nat.launch_plan(1, 32768, 16, "split")][-1] == "parts"   # four, two-slice pass 2
     assert [p[0] for p in nat.launch_plan(1, 8192, 16, "split")][-1] == "parts"    # four parts of 64 chunks
     assert [p[0] for p in nat.launch_plan(1, 8192, 32, "split")][-1] != "parts"    # two parts do not pay
     assert [p[0] for p in nat.launch_plan(1, 4096, 4, "split")][-1] != "parts"     # parts under 64 chunks
     # many chains (the two-slice 32-token form, or the per-chain hybrid) run whole by default
-    assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["chunk_map", "prep", "recur"]
+    assert [p[0] for p in nat.launch_plan(12, 32768, 32, "split")] == ["prep", "recur"]
+    # the per-chain hybrid (16-token records) of many short sequences keeps the chunk-map launch
+    assert [p[0] for p in nat.launch_plan(200, 51200, 8, "split")] == ["chunk_map", "prep", "recur"]
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "fused")] == ["chunk_map", "fused"]
     assert nat.launch_plan(0, 16, 1, "split") == []
     assert [p[0] for p in nat.launch_plan(8, 8192, 16, "recurrent")] == ["recurrent"]
