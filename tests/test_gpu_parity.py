@@ -143,3 +143,24 @@ def test_many_sequences(N, maxlen, variant):
     ok, mo, mf = compare(w, o, f, ro, rf)
     _say(f"  o {mo}\n  S {mf}")
     assert ok
+
+
+@pytest.mark.parametrize("N", [63, 64])
+def test_chunk_map_boundary(N):
+    """Up to 63 sequences (32-token forms) the first prep launch forms the chunk map, one
+    wave holding the offsets; from 64 a chunk-map launch does. Both sides of the boundary,
+    with empty and one-token sequences, every chain compared."""
+    from chunked_gated_delta_kda_amd import native
+    rng = np.random.Generator(np.random.PCG64(6300 + N))
+    lengths = rng.integers(2, 90, size=N)
+    lengths[::9] = 0
+    lengths[1::13] = 1
+    w = synth.make_workload(lengths, 1, 6300 + N, with_initial_state=True, clamp_frac=0.1)
+    plan = [p[0] for p in native.launch_plan(N, w.T, 1, "split")]
+    assert plan[-1] == "recur" and (plan[0] == "chunk_map") == (N > 63), plan
+    _say(f"[parity] chunk map boundary N={N} T={w.T} plan={plan}")
+    o, f = run_gpu(w, "split")
+    ro, rf = run_oracle(w)
+    ok, mo, mf = compare(w, o, f, ro, rf)
+    _say(f"  o {mo}\n  S {mf}")
+    assert ok

@@ -57,8 +57,23 @@ CASES = [([0, 50, 30, 100], 100), ([0, 60, 140], 100), ([-5, 40, 100], 100), ([7
          ([0, 30, 70], 100), ([0, 100, 0, 100], 100)]
 
 
+def _many(n):
+    """n sequences over 100 tokens (many empty), one offset decreasing and one past T:
+    63 is the most the first prep's wave-held chunk map takes, 64 the fewest the
+    chunk-map launch does."""
+    rng = np.random.Generator(np.random.PCG64(n))
+    cu = np.sort(rng.integers(0, 101, size=n + 1))
+    cu[0], cu[-1] = 0, 100
+    cu[10] = cu[9] - 5
+    cu[40] = 140
+    return [int(x) for x in cu], 100
+
+
+CASES += [_many(63), _many(64)]
+
+
 @pytest.mark.parametrize("variant", ["split", "fused", "recurrent"])
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "_".join(map(str, c[0])))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "_".join(map(str, c[0])) if len(c[0]) < 8 else f"N{len(c[0]) - 1}")
 def test_malformed_cu_seqlens(case, variant):
     cu, T = case
     w = synth.make_workload([T], 2, 5)
