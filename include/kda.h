@@ -192,7 +192,10 @@ typedef struct kda_launch_info {
  * writes up to max_launches entries to info (may be NULL) and returns the count
  * (0 for an invalid shape). When the recurrence of a shape leaves CUs idle,
  * the split variant cuts the sequences into segments and prepares the records of
- * segment s+1 inside the launch that runs the recurrence of segment s. */
+ * segment s+1 inside the launch that runs the recurrence of segment s. For batches of
+ * at most 63 sequences on the 32-token chunks, the first prep launch also forms the
+ * chunk map (no KDA_KERNEL_CHUNK_MAP entry). The plan is that of fp32 g and states:
+ * bf16 ones move a shape that would run 16-token chunks onto the 32-token ones. */
 int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_heads,
                         int32_t variant, kda_launch_info *info, int32_t max_launches);
 
