@@ -240,9 +240,10 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
     // 1.023 | 1.052 | 1.075; 16 x 2048 x 32 1.032 | 1.084 | 1.124; 16 x 1024 x 16 0.263 |
     // 0.299 | 0.322. KDA_SEGMENTS selects segments for it (parity-tested).
     if (waves == 9) return 1;
-    // the two-slice 32-token form on 25-32 long chains (recur_waves): 4 segments, measured
-    // best of 3-5 (above)
-    if (waves == 402 && N * H <= 32) return 4;
+    // the two-slice 32-token form on 25-32 long chains (recur_waves): 5 segments (with
+    // segment_ratio's r = 1.05; 4 with r = 1.25 before the last segment ran the one-slice
+    // form, measured best of 3-5 then)
+    if (waves == 402 && N * H <= 32) return 5;
     // The prep of a segment (work ~ the chain count) runs on the CUs the recurrence
     // leaves idle and must fit under its time: segments only with at least 2.5 idle CUs
     // per chain. Measured on MI355X (ms, 8192 tokens; unsegmented | segmented): 101 with
@@ -270,19 +271,25 @@ int split_segments(int64_t N, int64_t T, int64_t H, int waves) {
 // segment's recurrence (time per chunk independent of the chain count).
 // r = min(2, 1 + 8 / chains); measured on MI355X (ms for r = 1, 1.3, 1.6, 2): 8192 tokens x
 // 32 heads 0.433, 0.428, 0.435, 0.454; 65536 x 8 2.307, 2.293, 2.280, 2.277.
+// The two-slice 32-token form on 25-32 chains (five segments, the last one in the
+// one-slice form on all CUs): r = 1.05. Measured on MI355X (ms warm, cold; 4 segments with
+// r = 1.25 -> 5 with r = 1.05; alternating builds, 2 rounds): 8192 tokens x 32 heads
+// 0.346 -> 0.338, 0.388 -> 0.377; 2 x 16384 x 16 0.357 -> 0.347, 0.398 -> 0.389; 8192 x
+// 28 0.316 -> 0.316, 0.358 -> 0.359; 16384 x 32 0.646 -> 0.656, 0.694 -> 0.703.
 // KDA_SEGMENT_RATIO overrides r, for tuning.
-double segment_ratio(int64_t chains) {
+double segment_ratio(int64_t chains, int waves) {
     if (const char *e = std::getenv("KDA_SEGMENT_RATIO")) {
         const double r = std::atof(e);
         if (r >= 1.0 && r <= 4.0) return r;
     }
+    if (waves == 402 && chains <= 32) return 1.05;
     const double r = 1.0 + 8.0 / (double)(chains > 0 ? chains : 1);
     return r > 2.0 ? 2.0 : r;
 }
-int segment_frac(int sg, int S, int64_t chains) {
+int segment_frac(int sg, int S, int64_t chains, int waves) {
     if (sg <= 0) return 0;
     if (sg >= S) return kda::SEG_ONE;
-    const double r = segment_ratio(chains);
+    const double r = segment_ratio(chains, waves);
     const double f = r == 1.0 ? (double)sg / S : (std::pow(r, sg) - 1.0) / (std::pow(r, S) - 1.0);
     return (int)std::lround(f * kda::SEG_ONE);
 }
@@ -361,7 +368,7 @@ int32_t kda_launch_plan(int32_t num_seqs, int32_t total_tokens, int32_t num_head
         plan[n++] = {KDA_KERNEL_CHUNK_MAP, 0, 0, 0, 0, cl};
     if (v == KDA_VARIANT_SPLIT) {
         const int segs = split_segments(num_seqs, total_tokens, num_heads, waves);
-        auto bound = [&](int sg) { return (int32_t)segment_frac(sg, segs, (int64_t)num_seqs * num_heads); };
+        auto bound = [&](int sg) { return (int32_t)segment_frac(sg, segs, (int64_t)num_seqs * num_heads, waves); };
         if (split_parts(num_seqs, total_tokens, num_heads, waves) > 1) {
             plan[n++] = {KDA_KERNEL_PREP, 0, KDA_SEGMENT_ONE, 0, 0, cl};
             plan[n++] = {KDA_KERNEL_PARTS, 0, 0, 0, KDA_SEGMENT_ONE, cl};
@@ -522,7 +529,9 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                                  N, T, H, initial_state, out, final_state,
                                  final_state && !s_bf16 ? final_state : (float *)(ws + lay.carry), 0, 0, 0, 0, M,
                                  g_bf16, s_bf16};
-            auto bound = [&](int sg) { return segment_frac(sg, segs, (int64_t)N * H); };
+            // the form chosen for the segments (waves changes for the last one below)
+            const int seg_waves = waves;
+            auto bound = [&](int sg) { return segment_frac(sg, segs, (int64_t)N * H, seg_waves); };
             ok = around(st, [&] { return prep(0, bound(1)); });
             for (int sg = 0; ok && sg + 1 < segs; ++sg) {
                 a.fb = bound(sg), a.fe = bound(sg + 1), a.pb = bound(sg + 1), a.pe = bound(sg + 2);
@@ -530,6 +539,11 @@ int kda_fwd_ex(const void *q, const void *k, const void *v, const float *g, cons
                     return h32 ? kda::launch_recur_h32_prep(a, waves, st) : kda::launch_recur_prep(a, waves, st);
                 });
             }
+            // The last segment has no prep beside it: with at most 32 chains the one-slice
+            // form takes all CUs (same state layout as the two-slice form's carry).
+            // Measured on MI355X, 8192 tokens x 32 heads: 0.3539 -> 0.3499 ms (alternating
+            // builds in one process, 4 rounds each).
+            if (waves == 402 && (int64_t)N * H <= 32) waves = 401;
             ok = ok && around(st, [&] { return recur_range(a.carry, bound(segs - 1), kda::SEG_ONE); });
         }
     } else if (ok) {
