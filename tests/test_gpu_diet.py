@@ -107,6 +107,20 @@ def test_diet_config3():
     _check(w2, o, f, True, "config 3")
 
 
+def test_diet_config2_with_initial_state():
+    """8192 tokens x 32 heads with bf16 g and bf16 initial and final states: the default
+    schedule of five segments, the carry in fp32 between them and the last segment in the
+    one-slice form writing the bf16 final state; every chain compared."""
+    w = synth.config_workload(2)
+    rng = np.random.Generator(np.random.PCG64(2002))
+    s0 = (rng.standard_normal((w.N, w.H, 128, 128)) * 0.05).astype(np.float32)
+    w = synth.Workload(name=w.name, q=w.q, k=w.k, v=w.v, g=w.g, beta=w.beta, cu_seqlens=w.cu_seqlens,
+                       initial_state=s0, scale=w.scale)
+    _say("[diet] config 2 with an initial state, bf16 g and states")
+    w2, o, f = _run(w, True, True, "auto")
+    _check(w2, o, f, True, "config 2")
+
+
 def test_fused_rejects_diet():
     import torch
     import chunked_gated_delta_kda_amd as kda
