@@ -543,7 +543,7 @@ def main():
             others[f"config{cfg}"] = {k: o[k] for k in ("config", "value", "unit", "ms_per_step", "cold")}
         res["other_configs"] = others
         b = bench_backward(args, dev, cfg=GATED_CONFIG, cpu=False)
-        res["backward"] = {k: b[k] for k in ("metric", "value", "unit", "ms_per_step", "config")}
+        res["backward"] = {k: b[k] for k in ("metric", "value", "unit", "ms_per_step", "config", "roofline")}
         res["backward"]["avg_call_ms"] = b["roofline"]["avg_call_ms"]
     print(json.dumps(res), flush=True)
 
