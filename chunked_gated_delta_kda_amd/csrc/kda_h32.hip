@@ -978,16 +978,35 @@ __global__ __launch_bounds__(64 * PairLayout<NW>::WAVES) void recur_h32_prep_ker
     const int32_t *__restrict__ chunk_off, const int32_t *__restrict__ order, int N, int T, int H,
     const float *s0, float *__restrict__ out, float *sfin, float *carry, int fb, int fe, int RB, int sbf,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const GT *__restrict__ g,
-    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe) {
+    const float *__restrict__ beta, float scale, char *__restrict__ recs_out, int pb, int pe, int xsplit) {
     extern __shared__ __attribute__((aligned(16))) char lds[];
-    if ((int)blockIdx.x < RB) {
-        recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
-                                   order, N, T, H, s0, out, sfin, carry, fb, fe, sbf != 0);
-        return;
+    int prep_block;
+    if (xsplit) {
+        // Workgroups are dealt to the eight XCDs in turn (block b to XCD b mod 8). XCDs 0-3
+        // run the recurrence, each chain whole on one of them (XCD x, k = b / 8: chain
+        // 4 (k / P) + x, column block k mod P); XCDs 4-7 prepare the next segment, so that its
+        // HBM reads and record writes stay out of the L2s the recurrence reads its records from.
+        constexpr int P = D / (16 * NW);
+        const int x = (int)blockIdx.x & 7, kk = (int)blockIdx.x >> 3;
+        if (x < 4) {
+            const int chain = 4 * (kk / P) + x;
+            if (chain * P < RB)
+                recur_h32_block<NW, NSLOT>(chain * P + kk % P, lds, recs_in, v, cu, chunk_off, order, N, T, H, s0,
+                                           out, sfin, carry, fb, fe, sbf != 0);
+            return;
+        }
+        prep_block = 4 * kk + x - 4;
+    } else {
+        if ((int)blockIdx.x < RB) {
+            recur_h32_block<NW, NSLOT>(xcd_remap(blockIdx.x, RB, D / (16 * NW)), lds, recs_in, v, cu, chunk_off,
+                                       order, N, T, H, s0, out, sfin, carry, fb, fe, sbf != 0);
+            return;
+        }
+        prep_block = (int)blockIdx.x - RB;
     }
     const int w = threadIdx.x >> 6;
     if (w >= H32_PREP_WAVES) return;
-    const int64_t idx = (int64_t)(blockIdx.x - RB) * H32_PREP_WAVES + w;
+    const int64_t idx = (int64_t)prep_block * H32_PREP_WAVES + w;
     int h;
     const int ci = seg_chunk_of(chunk_off, N, H, pb, pe, idx, h);
     if (ci < 0) return;
@@ -1083,12 +1102,22 @@ static hipError_t launch_recur_h32_prep_t(const RecurPrepArgs &a, hipStream_t st
     auto kern = recur_h32_prep_kernel<NW, NS, GT>;
     static std::atomic<uint64_t> lds_set{0};
     if (ensure_lds_limit((const void *)kern, lds, lds_set) != hipSuccess) return hipErrorInvalidValue;
-    const int64_t rb = (int64_t)a.N * a.H * (D / (16 * NW));
+    constexpr int P = D / (16 * NW);
+    const int64_t chains = (int64_t)a.N * a.H;
+    const int64_t rb = chains * P;
     const int64_t pblocks =
         a.pe > a.pb ? (seg_chunks_bound(a.M, a.N, a.pb, a.pe) * a.H + H32_PREP_WAVES - 1) / H32_PREP_WAVES : 0;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(rb + pblocks)), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
+    // two-slice blocks of at most 32 chains: the recurrence on XCDs 0-3 (eight chains of
+    // four blocks fill an XCD's 32 CUs), the prep on XCDs 4-7 (see the kernel)
+    const bool xsplit = NW == 2 && chains <= 32;
+    int64_t grid = rb + pblocks;
+    if (xsplit) {
+        const int64_t krec = (chains + 3) / 4 * P, kprep = (pblocks + 3) / 4;
+        grid = 8 * (krec > kprep ? krec : kprep);
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * PairLayout<NW>::WAVES), lds, st, a.recs, a.v,
                        a.cu, a.chunk_off, a.order, a.N, a.T, a.H, a.s0, a.out, a.sfin, a.carry, a.fb, a.fe, (int)rb,
-                       (int)a.state_bf16, a.q, a.k, (const GT *)a.g, a.beta, a.scale, a.recs, a.pb, a.pe);
+                       (int)a.state_bf16, a.q, a.k, (const GT *)a.g, a.beta, a.scale, a.recs, a.pb, a.pe, (int)xsplit);
     return hipGetLastError();
 }
 
